@@ -1,0 +1,173 @@
+"""Pins of the oracle's index step (row statistics, v/s scores, top-p selection)."""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+from oracle import index as oi
+from synth import config_by_name, generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_lse_matches_library_logsumexp():
+    q = _rand((3, 64, 16), 1)
+    k = _rand((1, 256, 16), 2)
+    zs, lse = oi.row_stats(q, k, 0.25, 256)
+    for h in range(3):
+        for r in range(64):
+            n = 256 - 64 + r
+            z = q[h, r] @ k[0, : n + 1].T * 0.25
+            assert abs(lse[h, r] - logsumexp(z)) < 1e-12
+
+
+def test_scores_closed_form_equal_keys():
+    # every key equal -> each causal row is uniform: A[n, m] = 1/(n+1)
+    N, L = 256, 64
+    q = _rand((2, L, 8), 3)
+    k = np.tile(_rand((1, 1, 8), 4), (1, N, 1))
+    v, s, _ = oi.scores(q, k, 0.3, N)
+    for m in range(N):
+        exact = sum(Fraction(1, n + 1) for n in range(max(m, N - L), N)) / L
+        assert abs(v[0, m] - float(exact)) <= 2e-7 * float(exact)
+    T = N // 64
+    for j in range(T):
+        blk = T - 1 - j
+        exact = sum(sum(Fraction(1, n + 1) for n in range(max(m, N - L), N)) for m in range(64 * blk, 64 * blk + 64)) / L
+        assert abs(s[0, j] - float(exact)) <= 2e-7 * float(exact)
+
+
+def test_scores_bruteforce_loops():
+    N, L, D = 128, 64, 4
+    q = _rand((1, L, D), 5)
+    k = _rand((1, N, D), 6)
+    scale = 0.5
+    v, s, _ = oi.scores(q, k, scale, N)
+    vb = [0.0] * N
+    sb = [0.0] * (N // 64)
+    for r in range(L):
+        n = N - L + r
+        zs = [sum(q[0, r, d] * k[0, m, d] for d in range(D)) * scale for m in range(n + 1)]
+        mx = max(zs)
+        tot = sum(math.exp(z - mx) for z in zs)
+        for m in range(n + 1):
+            a = math.exp(zs[m] - mx) / tot
+            vb[m] += a / L
+            sb[n // 64 - m // 64] += a / L
+    assert np.allclose(v[0], np.float32(vb), rtol=1e-6, atol=0)
+    assert np.allclose(s[0], np.float32(sb), rtol=1e-6, atol=0)
+
+
+def test_scores_invariants():
+    N = 1024
+    q = _rand((4, 64, 16), 7)
+    k = _rand((2, N, 16), 8) * 2
+    v, s, _ = oi.scores(q, k, 0.25, N)
+    assert (v >= 0).all() and (s >= 0).all()
+    assert np.allclose(v.astype(np.float64).sum(1), 1.0, atol=1e-5)
+    assert np.allclose(s.astype(np.float64).sum(1), 1.0, atol=1e-5)
+    # with last_q = 64 rows in the final block, s(j) is the mass of key block T-1-j
+    T = N // 64
+    blocks = v.astype(np.float64).reshape(4, T, 64).sum(2)[:, ::-1]
+    assert np.allclose(s, blocks, rtol=1e-5, atol=1e-9)
+
+
+def _read_golden_select():
+    cases = []
+    for line in open(os.path.join(GOLDEN, "select_top_p.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        xs, p, sel = line.split(";")
+        cases.append((np.array([float(t) for t in xs.split()], dtype=np.float32), float(p),
+                      [int(t) for t in sel.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("x,p,expected", _read_golden_select())
+def test_select_golden(x, p, expected):
+    assert list(oi.select_top_p(x, p)) == expected
+
+
+def _brute_select(x_units, p_num, p_den):
+    """Exact rational brute force: smallest subset reaching p * total, then the
+    largest-mass such subset, then lexicographically smallest sorted indices."""
+    n = len(x_units)
+    total = sum(x_units)
+    tgt = Fraction(p_num, p_den) * total
+    for k in range(n + 1):
+        best = None
+        for comb in itertools.combinations(range(n), k):
+            mass = sum(x_units[i] for i in comb)
+            if mass >= tgt:
+                key = (-mass, comb)
+                if best is None or key < best:
+                    best = key
+        if best is not None:
+            return list(best[1])
+    return list(range(n))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_select_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 11))
+    units = rng.integers(0, 6, size=n)           # dyadic scores: units * 2^-20, many ties
+    if units.sum() == 0:
+        units[0] = 1
+    x = (units * 2.0 ** -20).astype(np.float32)
+    p_num = int(rng.integers(1, 256))
+    got = list(oi.select_top_p(x, p_num / 256.0))
+    assert got == _brute_select([int(u) for u in units], p_num, 256)
+
+
+def test_select_edges_and_monotone():
+    x = np.random.default_rng(0).random(500).astype(np.float32)
+    assert len(oi.select_top_p(x, 1.0)) == 500
+    assert len(oi.select_top_p(x, 1.5)) == 500
+    assert len(oi.select_top_p(x, 0.0)) == 0
+    assert len(oi.select_top_p(x, -0.2)) == 0
+    prev = set()
+    for p in np.linspace(0.05, 0.99, 25):
+        cur = set(oi.select_top_p(x, p).tolist())
+        assert prev <= cur
+        prev = cur
+
+
+def _index_for(cfg):
+    t = generate(cfg, tensors=("q", "k"), rows=None)
+    q_last = t["q"][:, cfg.N - cfg.last_q:]
+    return oi.build_index(q_last, t["k"], cfg.scale, cfg.N, cfg.top_p), t["outliers"]
+
+
+@pytest.mark.parametrize("seed", [1001, 7, 8, 9])
+def test_planted_outliers_are_top_verticals_literal_inputs(seed):
+    # literal tiny workload: N(0,1) inputs, 8 keys scaled x8
+    cfg = config_by_name("tiny", seed=seed)
+    idx, outl = _index_for(cfg)
+    top8 = np.sort(np.argsort(-idx["v"][0].astype(np.float64), kind="stable")[:8])
+    assert list(top8) == list(outl)
+    assert set(outl.tolist()) <= set(idx["vert"][0].tolist())
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_planted_vertical_and_slash_band(seed):
+    # shared mean (slash band) plus moderate outliers (vertical lines)
+    cfg = config_by_name("tiny", seed=seed, c=6.0, f_out=3.0)
+    idx, outl = _index_for(cfg)
+    assert set(outl.tolist()) <= set(idx["vert"][0].tolist())
+    assert {0, 1} <= set(idx["slash"][0].tolist())
+
+
+def test_negative_control_no_structure():
+    cfg = config_by_name("tiny", seed=5, n_out=0)
+    idx, _ = _index_for(cfg)
+    # with no mean and no outliers the mass is spread: most columns are needed
+    assert len(idx["vert"][0]) > 0.5 * cfg.N
