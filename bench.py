@@ -1,0 +1,225 @@
+"""Benchmark of the vertical-slash sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input that is
+already resident in HBM: sparse-index build (scores + top-p) -> active region
+-> sparse attention forward -> backward (delta, dQ, dK, dV).
+
+Default workload: the Qwen2.5-3B-shaped layer at 131072 tokens (16 q heads,
+2 kv heads, head dim 128, bf16, top-p 0.95), forward + backward.
+
+Prints one JSON line with the effective sparse-attention TFLOP/s of the whole
+step (effective FLOPs = 4*d*A forward + 10*d*A backward, A = active entries
+summed over q heads), tokens/s, per-stage times, the roofline of the sparse
+forward kernel and the fp64 oracle timed on the host as a CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective sparse-attn TFLOP/s fwd+bwd + tokens/s at 128K, 1 MI355X"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen128k")
+    ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the sparse path is built and timed on a single "
+              "MI355X; multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dynamic_sparse_attention_index_amd as vs
+    from synth import config_by_name, generate
+
+    cfg = config_by_name(args.workload)
+    if args.top_p is not None:
+        cfg = config_by_name(args.workload, top_p=args.top_p)
+    if cfg.P != 1:
+        print("ring-simulation workloads are timed by bench_ring mode (not in this line)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    T = N // 64
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    t0 = time.time()
+    host = generate(cfg)
+    q = torch.tensor(host["q"]).to(dev, tdt)
+    k = torch.tensor(host["k"]).to(dev, tdt)
+    v = torch.tensor(host["v"]).to(dev, tdt)
+    do = torch.tensor(host["do"]).to(dev, tdt)
+    gen_s = time.time() - t0
+
+    lay = vs.layout("contig", 1, N)
+    vert_s = torch.empty(Hq, N, device=dev)
+    slash_s = torch.empty(Hq, T, device=dev)
+    vidx = torch.empty(Hq, N, dtype=torch.int32, device=dev)
+    vcnt = torch.empty(Hq, dtype=torch.int32, device=dev)
+    sidx = torch.empty(Hq, T, dtype=torch.int32, device=dev)
+    scnt = torch.empty(Hq, dtype=torch.int32, device=dev)
+    ws = torch.empty(vs.index_workspace_size(Hq, Hkv, N, D), dtype=torch.uint8, device=dev)
+    q_last = q[:, N - cfg.last_q:]
+    vs.vs_index_build(q_last, k, lay, cfg.scale, cfg.top_p, vert_s, slash_s, vidx, vcnt, sidx, scnt, ws)
+    torch.cuda.synchronize()
+    max_s = int(scnt.max().item())
+    mask = vs.Mask(Hq, Hkv, lay, tile_cap=Hq * T * (max_s + 1))
+    o = torch.empty(Hq, N, D, device=dev)
+    lse = torch.empty(Hq, N, device=dev)
+    delta = torch.empty(Hq, N, device=dev)
+    dq = torch.zeros(Hq, N, D, device=dev)
+    dk = torch.zeros(Hkv, N, D, device=dev)
+    dv = torch.zeros(Hkv, N, D, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = {name: [] for name in ("index", "mask", "fwd", "bwd")}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record: marks[0].record(stream)
+        vs.vs_index_build(q_last, k, lay, cfg.scale, cfg.top_p, vert_s, slash_s, vidx, vcnt, sidx, scnt, ws, stream)
+        if record: marks[1].record(stream)
+        vs.vs_block_mask(vidx, vcnt, sidx, scnt, 0, 0, mask, stream)
+        if record: marks[2].record(stream)
+        vs.vs_attn_fwd(q, k, v, mask, cfg.scale, o, lse, 0, stream)
+        if record: marks[3].record(stream)
+        if cfg.backward:
+            vs.vs_attn_bwd_prep(o, do, delta, stream)
+            dq.zero_()
+            dk.zero_()
+            dv.zero_()
+            vs.vs_attn_bwd(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, stream)
+        if record:
+            marks[4].record(stream)
+            ev["index"].append((marks[0], marks[1]))
+            ev["mask"].append((marks[1], marks[2]))
+            ev["fwd"].append((marks[2], marks[3]))
+            ev["bwd"].append((marks[3], marks[4]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    status = int(mask.arrays()["status"].item())
+    if status != 0:
+        raise RuntimeError(f"mask status {status}")
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {kname: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for kname, pairs in ev.items()}
+
+    A = int(mask.arrays()["n_active"].sum().item())
+    total_causal = Hq * N * (N + 1) // 2
+    sparsity = 1.0 - A / total_causal
+    eff_flops = (4 + (10 if cfg.backward else 0)) * D * A
+    tflops = eff_flops / (ms_per_step * 1e-3) / 1e12
+    attn_ms = stage_ms["fwd"] + stage_ms["bwd"]
+    attn_tflops = eff_flops / (attn_ms * 1e-3) / 1e12
+
+    # roofline of the sparse forward kernel (one kernel per vs_attn_fwd call)
+    fwd_flops = 4 * D * A
+    fwd_tf = fwd_flops / (stage_ms["fwd"] * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    roofline = {"kernel": "attn_fwd_kernel", "bound": "mfma", "achieved": round(fwd_tf, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(fwd_tf / peak, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, host, vidx, vcnt, sidx, scnt, args.cpu_seconds, tflops_unit=True)
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "seq_len": N, "head_dim": D,
+                   "top_p": cfg.top_p, "last_q": cfg.last_q, "backward": cfg.backward, "mean_c": cfg.c,
+                   "seed": cfg.seed},
+        "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
+        "attn_only_tflops": round(attn_tflops, 3),
+        "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
+        "active_entries": A, "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
+        "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, host, vidx, vcnt, sidx, scnt, seconds, tflops_unit=True):
+    """Time the fp64 oracle on a bounded sample of the same workload on host cores.
+
+    Sample: the index step for a subset of q heads, and forward+backward of a
+    seeded set of (head, query block) items, extrapolated linearly to the whole
+    step by head count and by active entries.
+    """
+    import torch  # noqa: F401  (for .cpu())
+    from oracle import index as oi
+    from oracle import attention as oa
+    from oracle import mask as om
+
+    N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    cores = len(os.sched_getaffinity(0))
+    vc, sc = vcnt.cpu().numpy(), scnt.cpu().numpy()
+    vert = [vidx[h, :vc[h]].cpu().numpy().astype(np.int64) for h in range(Hq)]
+    slash = [sidx[h, :sc[h]].cpu().numpy().astype(np.int64) for h in range(Hq)]
+    # index: one head
+    t0 = time.perf_counter()
+    oi.build_index(host["q"][:1, N - cfg.last_q:], host["k"][:1], cfg.scale, N, cfg.top_p)
+    t_index = (time.perf_counter() - t0) * Hq
+    # attention fwd+bwd on random blocks until the time budget is used
+    rng = np.random.default_rng(0)
+    pos = np.arange(N)
+    done_active, t_attn = 0, 0.0
+    items = 0
+    while t_attn < seconds and items < 4096:
+        h = int(rng.integers(Hq))
+        I = int(rng.integers(N // 64))
+        g = h * Hkv // Hq
+        rows = pos[64 * I:64 * I + 64]
+        t0 = time.perf_counter()
+        M, _, _ = om.active(rows, pos, vert[h], slash[h])
+        used = M.any(axis=0)
+        kk, vv = host["k"][g, used], host["v"][g, used]
+        oa.forward_rows(host["q"][h, rows], kk, vv, M[:, used], cfg.scale)
+        if cfg.backward:
+            oa.backward_rows(host["q"][h, rows], kk, vv, M[:, used], cfg.scale, host["do"][h, rows])
+        t_attn += time.perf_counter() - t0
+        done_active += int(M.sum())
+        items += 1
+    A_total = sum(om.active_count(N, vert[h], slash[h]) for h in range(Hq))
+    t_attn_full = t_attn * A_total / max(done_active, 1)
+    t_total = t_index + t_attn_full
+    eff = (4 + (10 if cfg.backward else 0)) * D * A_total
+    return {"value": round(eff / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "tokens_per_s": round(N / t_total, 3), "seconds_measured": round(t_attn + t_index / Hq, 1),
+            "sample": f"index step of 1 of {Hq} q heads (x{Hq}); fwd+bwd of {items} random (head, 64-row "
+                      f"block) items = {done_active} of {A_total} active entries, extrapolated linearly "
+                      f"in active entries; numpy fp64"}
+
+
+if __name__ == "__main__":
+    main()

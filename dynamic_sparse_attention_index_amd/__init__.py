@@ -1,0 +1,210 @@
+"""Python binding of the vertical-slash sparse attention library (libvsattn.so).
+
+Argument marshalling only: every step of the path runs in the gfx950 HIP
+kernels behind the C ABI declared in include/vs_attn.h. PyTorch provides device
+memory and streams. If the library has not been built, calling any entry point
+raises; there is no fallback implementation.
+
+Entry points (same names and meaning as the C ABI):
+    vs_index_build, vs_block_mask, vs_attn_fwd, vs_merge_lse,
+    vs_attn_bwd_prep, vs_attn_bwd
+plus helpers to size workspaces and hold a mask buffer (``Mask``).
+"""
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+LIB_PATH = _build.LIB
+
+VS_OK, VS_ERR_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_CAPACITY, VS_ERR_HIP = 0, -1, -2, -3, -4, -5
+VS_F32, VS_BF16 = 0, 1
+LAYOUTS = {"contig": 0, "striped": 1, "zigzag": 2}
+TILE_DIAG = 0x40000000
+TILE_MASK = 0x3FFFFFFF
+
+EXPORTED = [
+    "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_mask_bytes", "vs_mask_init",
+    "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd",
+]
+
+
+class VsTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("D", ctypes.c_int32), ("stride_h", ctypes.c_int64),
+                ("stride_n", ctypes.c_int64)]
+
+
+class VsLayout(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("P", ctypes.c_int32), ("n_global", ctypes.c_int64)]
+
+
+_P32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class VsMask(ctypes.Structure):
+    _fields_ = [("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("QB", ctypes.c_int32), ("KB", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("W", ctypes.c_int32), ("lay", VsLayout), ("tile_cap", ctypes.c_int64),
+                ("rank", ctypes.c_int32), ("src", ctypes.c_int32),
+                ("tile_ptr", ctypes.c_void_p), ("tile_col", ctypes.c_void_p), ("csc_ptr", ctypes.c_void_p),
+                ("csc_row", ctypes.c_void_p), ("vloc", ctypes.c_void_p), ("vloc_cnt", ctypes.c_void_p),
+                ("vcum", ctypes.c_void_p), ("vert_end", ctypes.c_void_p), ("slash_bits", ctypes.c_void_p),
+                ("n_active", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+
+
+class VsError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libvsattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.vs_status_string.restype = ctypes.c_char_p
+        L.vs_status_string.argtypes = [i32]
+        L.vs_index_workspace_size.restype = sz
+        L.vs_index_workspace_size.argtypes = [i32, i32, i64, i32, i32]
+        L.vs_index_build.restype = i32
+        L.vs_index_build.argtypes = [VsTensor, VsTensor, VsLayout, f32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.vs_mask_bytes.restype = sz
+        L.vs_mask_bytes.argtypes = [i32, i32, VsLayout, i64]
+        L.vs_mask_init.restype = i32
+        L.vs_mask_init.argtypes = [ctypes.POINTER(VsMask), vp, sz, i32, i32, VsLayout, i64]
+        L.vs_block_mask.restype = i32
+        L.vs_block_mask.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, ctypes.POINTER(VsMask), vp]
+        L.vs_attn_fwd.restype = i32
+        L.vs_attn_fwd.argtypes = [VsTensor, VsTensor, VsTensor, ctypes.POINTER(VsMask), f32, vp, vp, i32, vp]
+        L.vs_merge_lse.restype = i32
+        L.vs_merge_lse.argtypes = [vp, vp, vp, vp, i32, i64, i32, vp]
+        L.vs_attn_bwd_prep.restype = i32
+        L.vs_attn_bwd_prep.argtypes = [vp, VsTensor, vp, vp]
+        L.vs_attn_bwd.restype = i32
+        L.vs_attn_bwd.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask), f32,
+                                  vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(code):
+    try:
+        return lib().vs_status_string(code).decode()
+    except RuntimeError:
+        return str(code)
+
+
+def _check(code, what):
+    if code != VS_OK:
+        raise VsError(code, what)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def as_vs_tensor(t: torch.Tensor) -> VsTensor:
+    """[H, N, D] torch view -> vs_tensor (no copy)."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("expected a [H, N, D] tensor with contiguous D")
+    if t.dtype == torch.bfloat16:
+        dt = VS_BF16
+    elif t.dtype == torch.float32:
+        dt = VS_F32
+    else:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return VsTensor(t.data_ptr(), dt, t.shape[0], t.shape[1], t.shape[2], t.stride(0), t.stride(1))
+
+
+def layout(kind: str = "contig", P: int = 1, n_global: int = 0) -> VsLayout:
+    return VsLayout(LAYOUTS[kind], P, n_global)
+
+
+def index_workspace_size(Hq, Hkv, n_global, D, last_q=64) -> int:
+    return int(lib().vs_index_workspace_size(Hq, Hkv, n_global, D, last_q))
+
+
+def vs_index_build(q_last, k, lay: VsLayout, scale, top_p, vert_score, slash_score, vert_idx, vert_cnt,
+                   slash_idx, slash_cnt, ws, stream=None):
+    _check(lib().vs_index_build(as_vs_tensor(q_last), as_vs_tensor(k), lay, scale, top_p, _ptr(vert_score),
+                                _ptr(slash_score), _ptr(vert_idx), _ptr(vert_cnt), _ptr(slash_idx),
+                                _ptr(slash_cnt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "vs_index_build")
+
+
+class Mask:
+    """A caller-owned device buffer carved into a vs_mask descriptor."""
+
+    def __init__(self, Hq, Hkv, lay: VsLayout, tile_cap, device="cuda"):
+        nbytes = int(lib().vs_mask_bytes(Hq, Hkv, lay, tile_cap))
+        if nbytes == 0:
+            raise VsError(VS_ERR_ARG, "vs_mask_bytes")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.desc = VsMask()
+        _check(lib().vs_mask_init(ctypes.byref(self.desc), _ptr(self.buf), nbytes, Hq, Hkv, lay, tile_cap),
+               "vs_mask_init")
+
+    def _view(self, name, n, dtype):
+        off = getattr(self.desc, name) - self.buf.data_ptr()
+        esz = torch.empty((), dtype=dtype).element_size()
+        return self.buf[off:off + n * esz].view(dtype)
+
+    def arrays(self):
+        d = self.desc
+        n_csr, n_col = d.Hq * d.QB, d.tile_cap
+        return {
+            "tile_ptr": self._view("tile_ptr", n_csr + 1, torch.int32),
+            "tile_col": self._view("tile_col", n_col, torch.int32),
+            "csc_ptr": self._view("csc_ptr", d.Hq * d.KB + 1, torch.int32),
+            "csc_row": self._view("csc_row", n_col, torch.int32),
+            "vloc": self._view("vloc", d.Hq * d.KB * 64, torch.int32),
+            "vloc_cnt": self._view("vloc_cnt", d.Hq, torch.int32),
+            "vcum": self._view("vcum", d.Hq * (d.KB + 1), torch.int32),
+            "vert_end": self._view("vert_end", d.Hq * d.QB, torch.int32),
+            "slash_bits": self._view("slash_bits", d.Hq * d.W, torch.int32),
+            "n_active": self._view("n_active", d.Hq * d.QB, torch.int64),
+            "status": self._view("status", 1, torch.int32),
+        }
+
+
+def vs_block_mask(vert_idx, vert_cnt, slash_idx, slash_cnt, rank, step, mask: Mask, stream=None):
+    _check(lib().vs_block_mask(_ptr(vert_idx), _ptr(vert_cnt), vert_idx.stride(0), _ptr(slash_idx),
+                               _ptr(slash_cnt), slash_idx.stride(0), rank, step, ctypes.byref(mask.desc),
+                               _stream(stream)), "vs_block_mask")
+
+
+def vs_attn_fwd(q, k, v, mask: Mask, scale, o, lse, accumulate=0, stream=None):
+    _check(lib().vs_attn_fwd(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), ctypes.byref(mask.desc), scale,
+                             _ptr(o), _ptr(lse), int(accumulate), _stream(stream)), "vs_attn_fwd")
+
+
+def vs_merge_lse(o_acc, lse_acc, o_step, lse_step, stream=None):
+    Hq, Nq, D = o_acc.shape
+    _check(lib().vs_merge_lse(_ptr(o_acc), _ptr(lse_acc), _ptr(o_step), _ptr(lse_step), Hq, Nq, D,
+                              _stream(stream)), "vs_merge_lse")
+
+
+def vs_attn_bwd_prep(o, dout, delta, stream=None):
+    _check(lib().vs_attn_bwd_prep(_ptr(o), as_vs_tensor(dout), _ptr(delta), _stream(stream)), "vs_attn_bwd_prep")
+
+
+def vs_attn_bwd(q, k, v, dout, lse, delta, mask: Mask, scale, dq, dk, dv, stream=None):
+    _check(lib().vs_attn_bwd(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), as_vs_tensor(dout), _ptr(lse),
+                             _ptr(delta), ctypes.byref(mask.desc), scale, _ptr(dq), _ptr(dk), _ptr(dv),
+                             _stream(stream)), "vs_attn_bwd")

@@ -1,0 +1,222 @@
+// The C ABI: host-side validation, workspace sizing and kernel launches.
+// No device memory is allocated here; every buffer comes from the caller.
+#include <string.h>
+
+#include "vs_common.h"
+#include "vs_internal.h"
+
+using namespace vs;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == VS_BF16 ? 2 : 4; }
+
+// Checks every property the kernels rely on for a [H, N, D] view.
+int check_tensor(const vs_tensor& t, int H, int64_t N, int D) {
+  if (!t.ptr) return VS_ERR_ARG;
+  if (t.dtype != VS_F32 && t.dtype != VS_BF16) return VS_ERR_ARG;
+  if (t.H != H || t.N != N || t.D != D) return VS_ERR_ARG;
+  if (t.stride_n < D || t.stride_h < 0) return VS_ERR_ARG;
+  const int eb = elem_bytes(t.dtype);
+  if (!aligned16(t.ptr) || (t.stride_n * eb) % 16 || (t.stride_h * eb) % 16) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
+int check_layout(const vs_layout& lay) {
+  if (lay.P < 1 || lay.n_global <= 0) return VS_ERR_ARG;
+  if (lay.kind != VS_CONTIG && lay.kind != VS_STRIPED && lay.kind != VS_ZIGZAG) return VS_ERR_ARG;
+  const int64_t unit = (lay.kind == VS_ZIGZAG ? 128 : 64) * (int64_t)lay.P;
+  if (lay.n_global % unit) return VS_ERR_UNSUPPORTED;
+  if (lay.n_global / 64 > (int64_t)1 << 24) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
+bool supported_dtype_dim(int dtype, int D) {
+  return (dtype == VS_BF16 && (D == 64 || D == 128)) || (dtype == VS_F32 && D == 64);
+}
+
+TView view(const vs_tensor& t) { return TView{t.ptr, t.stride_h, t.stride_n}; }
+
+struct MaskLayout {
+  size_t off[12];
+  size_t total;
+};
+
+MaskLayout mask_layout(int Hq, const vs_layout& lay, int64_t tile_cap) {
+  const int64_t T = lay.n_global / 64, QB = T / lay.P, W = (T + 31) / 32;
+  const size_t sizes[12] = {
+      (size_t)(Hq * QB + 1) * 4,        // tile_ptr
+      (size_t)tile_cap * 4,             // tile_col
+      (size_t)(Hq * QB + 1) * 4,        // csc_ptr
+      (size_t)tile_cap * 4,             // csc_row
+      (size_t)(Hq * QB * 64) * 4,       // vloc
+      (size_t)Hq * 4,                   // vloc_cnt
+      (size_t)(Hq * (QB + 1)) * 4,      // vcum
+      (size_t)(Hq * QB) * 4,            // vert_end
+      (size_t)(Hq * W) * 4,             // slash_bits
+      (size_t)(Hq * QB) * 8,            // n_active
+      (size_t)4,                        // status
+      0};
+  MaskLayout L;
+  size_t o = 0;
+  for (int i = 0; i < 12; ++i) {
+    L.off[i] = o;
+    o += (sizes[i] + 255) & ~(size_t)255;
+  }
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vs_status_string(int s) {
+  switch (s) {
+    case VS_OK: return "ok";
+    case VS_ERR_ARG: return "invalid argument";
+    case VS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VS_ERR_WORKSPACE: return "workspace or buffer too small";
+    case VS_ERR_CAPACITY: return "tile list capacity exceeded";
+    case VS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t vs_index_workspace_size(int Hq, int Hkv, int64_t n_global, int D, int last_q) {
+  if (Hq <= 0 || Hkv <= 0 || n_global < 64) return 0;
+  return index_workspace_bytes(Hq, Hkv, n_global, D, last_q);
+}
+
+int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, float top_p,
+                   float* vert_score, float* slash_score, int32_t* vert_idx, int32_t* vert_cnt,
+                   int32_t* slash_idx, int32_t* slash_cnt, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_layout(lay)) != VS_OK) return st;
+  const int Hq = q_last.H, Hkv = k.H, D = q_last.D, last_q = (int)q_last.N;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return VS_ERR_ARG;
+  if (Hq / Hkv > 8) return VS_ERR_UNSUPPORTED;
+  if (last_q < 1 || last_q > 64) return VS_ERR_UNSUPPORTED;
+  if ((st = check_tensor(q_last, Hq, last_q, D)) != VS_OK) return st;
+  if ((st = check_tensor(k, Hkv, lay.n_global, D)) != VS_OK) return st;
+  if (q_last.dtype != k.dtype || !supported_dtype_dim(k.dtype, D)) return VS_ERR_UNSUPPORTED;
+  if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || !ws)
+    return VS_ERR_ARG;
+  if (!(scale > 0.f) || top_p != top_p) return VS_ERR_ARG;
+  if (ws_bytes < vs_index_workspace_size(Hq, Hkv, lay.n_global, D, last_q)) return VS_ERR_WORKSPACE;
+  return launch_index_build(k.dtype, D, view(q_last), Hq, last_q, view(k), Hkv, lay, scale, top_p, vert_score,
+                            slash_score, vert_idx, vert_cnt, slash_idx, slash_cnt, ws, ws_bytes,
+                            (hipStream_t)stream);
+}
+
+size_t vs_mask_bytes(int Hq, int Hkv, vs_layout lay, int64_t tile_cap) {
+  if (Hq <= 0 || Hkv <= 0 || tile_cap < 0 || check_layout(lay) != VS_OK) return 0;
+  return mask_layout(Hq, lay, tile_cap).total;
+}
+
+int vs_mask_init(vs_mask* m, void* buf, size_t bytes, int Hq, int Hkv, vs_layout lay, int64_t tile_cap) {
+  int st;
+  if (!m || !buf) return VS_ERR_ARG;
+  if ((st = check_layout(lay)) != VS_OK) return st;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || tile_cap < 0 || tile_cap > 0x7FFFFFFF) return VS_ERR_ARG;
+  if (!aligned16(buf)) return VS_ERR_UNSUPPORTED;
+  const MaskLayout L = mask_layout(Hq, lay, tile_cap);
+  if (bytes < L.total) return VS_ERR_WORKSPACE;
+  memset(m, 0, sizeof(*m));
+  char* b = (char*)buf;
+  m->Hq = Hq;
+  m->Hkv = Hkv;
+  m->T = (int32_t)(lay.n_global / 64);
+  m->QB = m->KB = m->T / lay.P;
+  m->W = (m->T + 31) / 32;
+  m->lay = lay;
+  m->tile_cap = tile_cap;
+  m->rank = m->src = -1;
+  m->tile_ptr = (int32_t*)(b + L.off[0]);
+  m->tile_col = (int32_t*)(b + L.off[1]);
+  m->csc_ptr = (int32_t*)(b + L.off[2]);
+  m->csc_row = (int32_t*)(b + L.off[3]);
+  m->vloc = (int32_t*)(b + L.off[4]);
+  m->vloc_cnt = (int32_t*)(b + L.off[5]);
+  m->vcum = (int32_t*)(b + L.off[6]);
+  m->vert_end = (int32_t*)(b + L.off[7]);
+  m->slash_bits = (uint32_t*)(b + L.off[8]);
+  m->n_active = (int64_t*)(b + L.off[9]);
+  m->status = (int32_t*)(b + L.off[10]);
+  return VS_OK;
+}
+
+int vs_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
+                  const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
+                  int rank, int step, vs_mask* m, void* stream) {
+  if (!m || !m->tile_ptr || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt) return VS_ERR_ARG;
+  if (check_layout(m->lay) != VS_OK) return VS_ERR_ARG;
+  const int P = m->lay.P;
+  if (rank < 0 || rank >= P || step < 0 || step >= P) return VS_ERR_ARG;
+  if (vert_stride < 0 || slash_stride < 0) return VS_ERR_ARG;
+  const int src = ((rank - step) % P + P) % P;
+  m->rank = rank;
+  m->src = src;
+  return launch_block_mask(vert_idx, vert_cnt, vert_stride, slash_idx, slash_cnt, slash_stride, rank, src, m,
+                           (hipStream_t)stream);
+}
+
+static int check_attn(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v, const vs_mask* m) {
+  int st;
+  if (!m || !m->tile_ptr || m->rank < 0) return VS_ERR_ARG;
+  const int D = q.D;
+  const int64_t Nq = (int64_t)m->QB * 64, Nk = (int64_t)m->KB * 64;
+  if ((st = check_tensor(q, m->Hq, Nq, D)) != VS_OK) return st;
+  if ((st = check_tensor(k, m->Hkv, Nk, D)) != VS_OK) return st;
+  if ((st = check_tensor(v, m->Hkv, Nk, D)) != VS_OK) return st;
+  if (q.dtype != k.dtype || q.dtype != v.dtype) return VS_ERR_ARG;
+  if (!supported_dtype_dim(q.dtype, D)) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
+int vs_attn_fwd(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float scale, float* o, float* lse,
+                int accumulate, void* stream) {
+  int st;
+  if ((st = check_attn(q, k, v, m)) != VS_OK) return st;
+  if (!o || !lse || !aligned16(o)) return VS_ERR_ARG;
+  if (accumulate != 0 && accumulate != 1) return VS_ERR_ARG;
+  if (!(scale > 0.f)) return VS_ERR_ARG;
+  return launch_attn_fwd(q.dtype, q.D, view(q), view(k), view(v), m, scale, o, lse, accumulate,
+                         (hipStream_t)stream);
+}
+
+int vs_merge_lse(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step, int Hq, int64_t Nq,
+                 int D, void* stream) {
+  if (!o_acc || !lse_acc || !o_step || !lse_step || Hq <= 0 || Nq < 0) return VS_ERR_ARG;
+  if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
+  if (!aligned16(o_acc) || !aligned16(o_step)) return VS_ERR_UNSUPPORTED;
+  if (Nq == 0) return VS_OK;
+  return launch_merge(o_acc, lse_acc, o_step, lse_step, Hq, Nq, D, (hipStream_t)stream);
+}
+
+int vs_attn_bwd_prep(const float* o, vs_tensor dout, float* delta, void* stream) {
+  if (!o || !delta || !dout.ptr) return VS_ERR_ARG;
+  int st;
+  if ((st = check_tensor(dout, dout.H, dout.N, dout.D)) != VS_OK) return st;
+  if (dout.D != 64 && dout.D != 128) return VS_ERR_UNSUPPORTED;
+  if (!aligned16(o)) return VS_ERR_UNSUPPORTED;
+  if (dout.H <= 0 || dout.N <= 0) return VS_ERR_ARG;
+  return launch_bwd_prep(o, dout.dtype, view(dout), dout.H, dout.N, dout.D, delta, (hipStream_t)stream);
+}
+
+int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, const float* lse, const float* delta,
+                const vs_mask* m, float scale, float* dq, float* dk, float* dv, void* stream) {
+  int st;
+  if ((st = check_attn(q, k, v, m)) != VS_OK) return st;
+  if ((st = check_tensor(dout, m->Hq, (int64_t)m->QB * 64, q.D)) != VS_OK) return st;
+  if (dout.dtype != q.dtype) return VS_ERR_ARG;
+  if (!lse || !delta || !dq || !dk || !dv) return VS_ERR_ARG;
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return VS_ERR_UNSUPPORTED;
+  if (!(scale > 0.f)) return VS_ERR_ARG;
+  return launch_attn_bwd(q.dtype, q.D, view(q), view(k), view(v), view(dout), lse, delta, m, scale, dq, dk, dv,
+                         (hipStream_t)stream);
+}
+
+}  // extern "C"

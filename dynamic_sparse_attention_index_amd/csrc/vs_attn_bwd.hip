@@ -1,0 +1,480 @@
+// Backward of the block-sparse vertical-slash attention over one ring step.
+//
+// The pages describe the sparse forward (MTraining review, page 1, section
+// 三.2 item 3) and train with it, so the gradient is the exact gradient of
+// softmax attention restricted to the same active set, the index being held
+// fixed: with the final row statistics LSE and delta = rowsum(dO * O),
+//   P = exp(z - LSE), dV += P^T dO, dS = P * (dO.V - delta),
+//   dQ += dS K * scale, dK += dS^T Q * scale.
+//
+// Three kernels, no atomics except for vertical columns:
+//   * dq_kernel     -- query-major like the forward: one workgroup per
+//                      (q head, query block) recomputes P and dP over the same
+//                      tiles and gathered vertical chunks and owns its dQ rows;
+//   * dkdv_kernel   -- key-major over slash tiles: one workgroup per (kv head,
+//                      key block) walks the CSC lists of every q head of the
+//                      group and owns the key block's dK/dV rows;
+//   * dkdv_vert_kernel -- the shard's vertical columns, 64 gathered columns per
+//                      work item against a range of query blocks, added to
+//                      dK/dV with fp32 atomics (a column can belong to several
+//                      q heads of the group).
+#include <type_traits>
+
+#include "vs_common.h"
+#include "vs_internal.h"
+
+namespace vs {
+
+constexpr int BWD_THREADS = 256;
+constexpr int VERT_SEG = 256;          // query blocks per vertical work item
+constexpr int VERT_GRID = 2048;        // persistent workgroups for vertical columns
+
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  int64_t qsh, qsn, ksh, ksn, vsh, vsn, dsh, dsn;
+  const float *lse, *delta;
+  const int32_t *tile_ptr, *tile_col, *csc_ptr, *csc_row, *vloc, *vloc_cnt, *vert_end;
+  const uint32_t* slash_bits;
+  float *dq, *dk, *dv;
+  int Hq, Hkv, QB, KB, W, kind, P, rank, src;
+  float scale, scale_log2;
+};
+
+// Row/key permutation inside a 64-wide tile (see the forward kernel): value i
+// of subtile t in lane group g is position 32*(t/2) + 8*g + 4*(t%2) + i.
+__device__ __forceinline__ int pos_of(int t, int g, int i) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i; }
+__device__ __forceinline__ int pos_row(int t, int m) { return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3); }
+
+template <typename T, int D>
+struct BwdTile {
+  static constexpr int KP = D + (sizeof(T) == 2 ? 8 : 4);
+  static constexpr int CPR = D * (int)sizeof(T) / 16;
+  static constexpr int CPT = BLK * CPR / BWD_THREADS;
+  static constexpr int NK = (sizeof(T) == 2) ? D / 32 : D / 4;   // contraction steps over D
+  using Frag = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
+};
+
+// Load a lane's fragment of row `row` (contraction slots of lane group g) from global.
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frag(const T* row, int g, typename BwdTile<T, D>::Frag* f) {
+  constexpr int NK = BwdTile<T, D>::NK;
+  if constexpr (sizeof(T) == 2) {
+    #pragma unroll
+    for (int ks = 0; ks < NK; ++ks) f[ks] = *(const bf16x8*)(row + 32 * ks + 8 * g);
+  } else {
+    #pragma unroll
+    for (int ks = 0; ks < NK; ++ks) f[ks] = row[4 * ks + g];
+  }
+}
+
+// acc[t] = X_lds[pos_row(t, m)] . frag  (a 16x16 block of (X F^T)^T per subtile)
+template <typename T, int D>
+__device__ __forceinline__ void rows_dot_frag(const T* X, int n16, int g4,
+                                              const typename BwdTile<T, D>::Frag* f, f32x4* acc) {
+  constexpr int KP = BwdTile<T, D>::KP, NK = BwdTile<T, D>::NK;
+  #pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const T* xr = X + pos_row(t, n16) * KP;
+    if constexpr (sizeof(T) == 2) {
+      #pragma unroll
+      for (int ks = 0; ks < NK; ++ks) acc[t] = mfma_bf16(*(const bf16x8*)(xr + 32 * ks + 8 * g4), f[ks], acc[t]);
+    } else {
+      #pragma unroll
+      for (int ks = 0; ks < NK; ++ks) acc[t] = mfma_f32(xr[4 * ks + g4], f[ks], acc[t]);
+    }
+  }
+}
+
+// out[dt] += X_lds^T(d, slots) * w  where w[t][i] weights position pos_of(t, g4, i)
+// (contraction over the 64 tile positions; X row-major [64][KP]).
+// For bf16 inputs the fp32 weights (P or dS) are carried as a pair of bf16
+// values w = hi + lo (hi = bf16(w), lo = bf16(w - hi)), two MFMAs sharing the
+// X operand: the gradient sums run over up to a whole sequence of rows, and a
+// single bf16 rounding of every weight (relative 2^-9) would dominate their
+// error; the pair leaves about 2^-17.
+template <typename T, int D>
+__device__ __forceinline__ void colsT_times(const T* X, int n16, int g4, const f32x4* w, f32x4* out) {
+  constexpr int KP = BwdTile<T, D>::KP;
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 wh[2], wl[2];
+    #pragma unroll
+    for (int c = 0; c < 2; ++c)
+      #pragma unroll
+      for (int e = 0; e < 2; ++e)
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = w[2 * c + e][i];
+          const bf16 hi = (bf16)x;
+          wh[c][4 * e + i] = hi;
+          wl[c][4 * e + i] = (bf16)(x - (float)hi);
+        }
+    #pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      #pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const T* base = X + (32 * c + 8 * g4 + (n16 >> 2)) * KP + 16 * dt + 4 * (n16 & 3);
+        const bf16x8 xa = lds_read_tr16_x2(base, KP);
+        out[dt] = mfma_bf16(xa, wh[c], out[dt]);
+        out[dt] = mfma_bf16(xa, wl[c], out[dt]);
+      }
+  } else {
+    #pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      #pragma unroll
+      for (int t = 0; t < 4; ++t)
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) out[dt] = mfma_f32(X[pos_of(t, g4, i) * KP + 16 * dt + n16], w[t][i], out[dt]);
+  }
+}
+
+// Stage 64 rows (given per thread chunk) of a [*, D] tensor into an LDS tile.
+template <typename T, int D>
+__device__ __forceinline__ void stage_rows(T* dst, const T* base, int64_t sn, const int* rows, int tid) {
+  constexpr int KP = BwdTile<T, D>::KP, CPR = BwdTile<T, D>::CPR, CPT = BwdTile<T, D>::CPT;
+  #pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + c * BWD_THREADS;
+    const int r = ch / CPR, col = (ch % CPR) * (16 / (int)sizeof(T));
+    *(i32x4*)(dst + r * KP + col) = *(const i32x4*)(base + (int64_t)rows[c] * sn + col);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query-major. Wave w owns query rows 16w..16w+15 of block I.
+template <typename T, int D>
+__global__ void __launch_bounds__(BWD_THREADS) dq_kernel(BwdArgs a) {
+  using Tl = BwdTile<T, D>;
+  constexpr int KP = Tl::KP, CPR = Tl::CPR, CPT = Tl::CPT, NK = Tl::NK;
+  __shared__ __attribute__((aligned(16))) T Ks[BLK * KP];
+  __shared__ __attribute__((aligned(16))) T Vs[BLK * KP];
+  __shared__ int thr_sh[BLK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int nitems = a.Hq * a.QB;
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int I = a.QB - 1 - item / a.Hq;
+  const int h = item % a.Hq;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int64_t u = (int64_t)h * a.QB + I;
+  const int rowoff = wave * 16 + n16;
+  const int64_t grow = (int64_t)I * BLK + rowoff;
+  const int t0 = a.tile_ptr[u];
+  const int nt = a.tile_ptr[u + 1] - t0;
+  const int ve = a.vert_end[u];
+  const int total = nt + (ve + BLK - 1) / BLK;
+  if (total == 0) return;
+
+  typename Tl::Frag qf[NK], df[NK];
+  load_row_frag<T, D>((const T*)a.q + h * a.qsh + grow * a.qsn, g4, qf);
+  load_row_frag<T, D>((const T*)a.dout + h * a.dsh + grow * a.dsn, g4, df);
+  const float lse2 = a.lse[(int64_t)h * a.QB * BLK + grow] * LOG2E;
+  const float dl = a.delta[(int64_t)h * a.QB * BLK + grow];
+  const bool row_live = lse2 > -INFINITY;
+  const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I);
+  const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
+  const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
+  const T* kbase = (const T*)a.k + kvh * a.ksh;
+  const T* vbase = (const T*)a.v + kvh * a.vsh;
+
+  f32x4 acc[D / 16];
+  #pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int it = 0; it < total; ++it) {
+    int rows[CPT];
+    int mode;
+    if (it < nt) {
+      const int e = a.tile_col[t0 + it];
+      const int J = e & VS_TILE_MASK;
+      mode = (e & VS_TILE_DIAG) ? 1 : 0;
+      #pragma unroll
+      for (int c = 0; c < CPT; ++c) rows[c] = J * BLK + (tid + c * BWD_THREADS) / CPR;
+      if (tid < BLK) thr_sh[tid] = tid;
+    } else {
+      const int base = (it - nt) * BLK;
+      mode = 1;
+      #pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int idx = base + (tid + c * BWD_THREADS) / CPR;
+        rows[c] = idx < ve ? vl[idx] : vl[base];
+      }
+      if (tid < BLK) {
+        const int idx = base + tid;
+        int thr = BLK;
+        if (idx < ve) {
+          const int m = vl[idx];
+          const int64_t j = G - global_block(a.kind, a.P, a.KB, a.src, m / BLK);
+          if (!((sb[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
+        }
+        thr_sh[tid] = thr;
+      }
+    }
+    stage_rows<T, D>(Ks, kbase, a.ksn, rows, tid);
+    stage_rows<T, D>(Vs, vbase, a.vsn, rows, tid);
+    __syncthreads();
+    f32x4 s[4], dp[4];
+    rows_dot_frag<T, D>(Ks, n16, g4, qf, s);    // S^T: [key][row]
+    rows_dot_frag<T, D>(Vs, n16, g4, df, dp);   // dP^T
+    #pragma unroll
+    for (int t = 0; t < 4; ++t)
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool act = row_live && !(mode && thr_sh[pos_of(t, g4, i)] > rowoff);
+        const float p = act ? __builtin_amdgcn_exp2f(s[t][i] * a.scale_log2 - lse2) : 0.f;
+        s[t][i] = p * (dp[t][i] - dl);          // dS
+      }
+    colsT_times<T, D>(Ks, n16, g4, s, acc);      // dQ^T += K^T dS^T
+    __syncthreads();
+  }
+  float* out = a.dq + ((int64_t)h * a.QB * BLK + grow) * D;
+  #pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 r = *(f32x4*)(out + 16 * dt + 4 * g4);
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] += acc[dt][i] * a.scale;
+    *(f32x4*)(out + 16 * dt + 4 * g4) = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared core of the key-major kernels: wave w owns 16 keys (kf/vf fragments);
+// the staged query block (Qs, dOs, per-row lse2/delta) is processed against
+// them. thr[lane]: rows with row offset < thr are inactive for this lane's key
+// (key-side causal / vertical threshold); BLK = inactive everywhere.
+template <typename T, int D>
+__device__ __forceinline__ void key_block_step(const T* Qs, const T* dOs, const float* lse_sh, const float* dl_sh,
+                                               const typename BwdTile<T, D>::Frag* kf,
+                                               const typename BwdTile<T, D>::Frag* vf, int thr, int n16, int g4,
+                                               float scale_log2, f32x4* acc_dk, f32x4* acc_dv) {
+  f32x4 s[4], dp[4];
+  rows_dot_frag<T, D>(Qs, n16, g4, kf, s);     // S: [row][key], rows permuted
+  rows_dot_frag<T, D>(dOs, n16, g4, vf, dp);   // dP
+  f32x4 ds[4];
+  #pragma unroll
+  for (int t = 0; t < 4; ++t)
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = pos_of(t, g4, i);
+      const float l2 = lse_sh[r];
+      const bool act = r >= thr && l2 > -INFINITY;
+      const float p = act ? __builtin_amdgcn_exp2f(s[t][i] * scale_log2 - l2) : 0.f;
+      s[t][i] = p;
+      ds[t][i] = p * (dp[t][i] - dl_sh[r]);
+    }
+  colsT_times<T, D>(dOs, n16, g4, s, acc_dv);   // dV^T += dO^T P
+  colsT_times<T, D>(Qs, n16, g4, ds, acc_dk);   // dK^T += Q^T dS
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void stage_query_block(T* Qs, T* dOs, float* lse_sh, float* dl_sh, const BwdArgs& a,
+                                                  int h, int I, int tid) {
+  constexpr int CPR = BwdTile<T, D>::CPR, CPT = BwdTile<T, D>::CPT;
+  int rows[CPT];
+  #pragma unroll
+  for (int c = 0; c < CPT; ++c) rows[c] = I * BLK + (tid + c * BWD_THREADS) / CPR;
+  stage_rows<T, D>(Qs, (const T*)a.q + h * a.qsh, a.qsn, rows, tid);
+  stage_rows<T, D>(dOs, (const T*)a.dout + h * a.dsh, a.dsn, rows, tid);
+  if (tid < BLK) {
+    const int64_t r = (int64_t)h * a.QB * BLK + (int64_t)I * BLK + tid;
+    lse_sh[tid] = a.lse[r] * LOG2E;
+    dl_sh[tid] = a.delta[r];
+  }
+}
+
+// dK/dV over slash tiles: grid = Hkv * KB, item -> (kv head, key block J).
+template <typename T, int D>
+__global__ void __launch_bounds__(BWD_THREADS) dkdv_kernel(BwdArgs a) {
+  using Tl = BwdTile<T, D>;
+  constexpr int KP = Tl::KP, NK = Tl::NK;
+  __shared__ __attribute__((aligned(16))) T Qs[BLK * KP];
+  __shared__ __attribute__((aligned(16))) T dOs[BLK * KP];
+  __shared__ float lse_sh[BLK], dl_sh[BLK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int nitems = a.Hkv * a.KB;
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int J = item % a.KB, kvh = item / a.KB;
+  const int grp = a.Hq / a.Hkv;
+  const int keyoff = wave * 16 + n16;
+  const int64_t krow = (int64_t)J * BLK + keyoff;
+  typename Tl::Frag kf[NK], vf[NK];
+  load_row_frag<T, D>((const T*)a.k + kvh * a.ksh + krow * a.ksn, g4, kf);
+  load_row_frag<T, D>((const T*)a.v + kvh * a.vsh + krow * a.vsn, g4, vf);
+  f32x4 acc_dk[D / 16], acc_dv[D / 16];
+  #pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc_dk[dt] = acc_dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool any = false;
+  for (int hh = 0; hh < grp; ++hh) {
+    const int h = kvh * grp + hh;
+    const int64_t cu = (int64_t)h * a.KB + J;
+    const int c0 = a.csc_ptr[cu], c1 = a.csc_ptr[cu + 1];
+    for (int e = c0; e < c1; ++e) {
+      const int ent = a.csc_row[e];
+      const int I = ent & VS_TILE_MASK;
+      stage_query_block<T, D>(Qs, dOs, lse_sh, dl_sh, a, h, I, tid);
+      __syncthreads();
+      // diagonal tile: key k is active for rows >= k
+      const int thr = (ent & VS_TILE_DIAG) ? keyoff : 0;
+      key_block_step<T, D>(Qs, dOs, lse_sh, dl_sh, kf, vf, thr, n16, g4, a.scale_log2, acc_dk, acc_dv);
+      any = true;
+      __syncthreads();
+    }
+  }
+  if (!any) return;
+  float* dkr = a.dk + ((int64_t)kvh * a.KB * BLK + krow) * D;
+  float* dvr = a.dv + ((int64_t)kvh * a.KB * BLK + krow) * D;
+  #pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 x = *(f32x4*)(dkr + 16 * dt + 4 * g4);
+    f32x4 y = *(f32x4*)(dvr + 16 * dt + 4 * g4);
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] += acc_dk[dt][i] * a.scale;
+      y[i] += acc_dv[dt][i];
+    }
+    *(f32x4*)(dkr + 16 * dt + 4 * g4) = x;
+    *(f32x4*)(dvr + 16 * dt + 4 * g4) = y;
+  }
+}
+
+// dK/dV of vertical columns. Work items (h, chunk of 64 columns, query-block
+// segment) are enumerated from the device-side vertical counts; a fixed grid
+// strides over them and every workgroup exits after the last item.
+template <typename T, int D>
+__global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
+  using Tl = BwdTile<T, D>;
+  constexpr int KP = Tl::KP, NK = Tl::NK;
+  __shared__ __attribute__((aligned(16))) T Qs[BLK * KP];
+  __shared__ __attribute__((aligned(16))) T dOs[BLK * KP];
+  __shared__ float lse_sh[BLK], dl_sh[BLK];
+  __shared__ int any_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int nseg = (a.QB + VERT_SEG - 1) / VERT_SEG;
+  int64_t total = 0;
+  for (int h = 0; h < a.Hq; ++h) total += (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+  const int grp = a.Hq / a.Hkv;
+  for (int64_t w = blockIdx.x; w < total; w += gridDim.x) {
+    // decode (h, chunk, seg)
+    int64_t r = w;
+    int h = 0;
+    for (; h < a.Hq; ++h) {
+      const int64_t n = (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+      if (r < n) break;
+      r -= n;
+    }
+    const int chunk = (int)(r / nseg), seg = (int)(r % nseg);
+    const int kvh = h / grp;
+    const int cnt = a.vloc_cnt[h];
+    const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
+    const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
+    const int slot = chunk * BLK + wave * 16 + n16;
+    const bool valid = slot < cnt;
+    const int m = vl[valid ? slot : chunk * BLK];
+    const int64_t gb = global_block(a.kind, a.P, a.KB, a.src, m / BLK);
+    typename Tl::Frag kf[NK], vf[NK];
+    load_row_frag<T, D>((const T*)a.k + kvh * a.ksh + (int64_t)m * a.ksn, g4, kf);
+    load_row_frag<T, D>((const T*)a.v + kvh * a.vsh + (int64_t)m * a.vsn, g4, vf);
+    f32x4 acc_dk[D / 16], acc_dv[D / 16];
+    #pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc_dk[dt] = acc_dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int I0 = seg * VERT_SEG, I1 = min(a.QB, I0 + VERT_SEG);
+    bool touched = false;
+    for (int I = I0; I < I1; ++I) {
+      const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I);
+      const int64_t j = G - gb;
+      int thr = BLK;
+      if (valid && j >= 0 && !((sb[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
+      if (tid == 0) any_sh = 0;
+      __syncthreads();
+      if (thr < BLK) any_sh = 1;
+      __syncthreads();
+      if (!any_sh) continue;
+      stage_query_block<T, D>(Qs, dOs, lse_sh, dl_sh, a, h, I, tid);
+      __syncthreads();
+      key_block_step<T, D>(Qs, dOs, lse_sh, dl_sh, kf, vf, thr, n16, g4, a.scale_log2, acc_dk, acc_dv);
+      touched = true;
+      __syncthreads();
+    }
+    if (touched && valid) {
+      float* dkr = a.dk + ((int64_t)kvh * a.KB * BLK + m) * D;
+      float* dvr = a.dv + ((int64_t)kvh * a.KB * BLK + m) * D;
+      #pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          atomicAdd(dkr + 16 * dt + 4 * g4 + i, acc_dk[dt][i] * a.scale);
+          atomicAdd(dvr + 16 * dt + 4 * g4 + i, acc_dv[dt][i]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// delta[row] = dO[row] . O[row]; D/4 threads per row.
+template <typename T>
+__global__ void bwd_prep_kernel(const float* o, const T* dout, int64_t dsh, int64_t dsn, int64_t Nq, int64_t rows,
+                                int D, float* delta) {
+  const int per = D / 4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = t / per;
+  const int c = (int)(t % per) * 4;
+  float x = 0.f;
+  if (r < rows) {
+    const int64_t h = r / Nq, n = r % Nq;
+    const f32x4 ov = *(const f32x4*)(o + r * D + c);
+    const T* dr = dout + h * dsh + n * dsn + c;
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) x += ov[i] * to_f32(dr[i]);
+  }
+    for (int off = per / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  if (r < rows && c == 0) delta[r] = x;
+}
+
+int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, int D, float* delta,
+                    hipStream_t stream) {
+  const int64_t rows = (int64_t)Hq * Nq;
+  const int64_t n = rows * (D / 4);
+  const int tpb = 256;
+  const dim3 grid((unsigned)((n + tpb - 1) / tpb));
+  if (dtype == VS_BF16)
+    hipLaunchKernelGGL(bwd_prep_kernel<bf16>, grid, dim3(tpb), 0, stream, o, (const bf16*)dout.ptr, dout.sh, dout.sn,
+                       Nq, rows, D, delta);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, dim3(tpb), 0, stream, o, (const float*)dout.ptr, dout.sh,
+                       dout.sn, Nq, rows, D, delta);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+template <typename T, int D>
+static void launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((dkdv_vert_kernel<T, D>), dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
+}
+
+int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, const float* lse,
+                    const float* delta, const vs_mask* m, float scale, float* dq, float* dk, float* dv,
+                    hipStream_t stream) {
+  BwdArgs a;
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.dout = dout.ptr;
+  a.qsh = q.sh; a.qsn = q.sn; a.ksh = k.sh; a.ksn = k.sn; a.vsh = v.sh; a.vsn = v.sn;
+  a.dsh = dout.sh; a.dsn = dout.sn;
+  a.lse = lse; a.delta = delta;
+  a.tile_ptr = m->tile_ptr; a.tile_col = m->tile_col; a.csc_ptr = m->csc_ptr; a.csc_row = m->csc_row;
+  a.vloc = m->vloc; a.vloc_cnt = m->vloc_cnt; a.vert_end = m->vert_end; a.slash_bits = m->slash_bits;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
+  a.P = m->lay.P; a.rank = m->rank; a.src = m->src;
+  a.scale = scale; a.scale_log2 = scale * LOG2E;
+  if (dtype == VS_BF16 && D == 128) launch_bwd_typed<bf16, 128>(a, stream);
+  else if (dtype == VS_BF16 && D == 64) launch_bwd_typed<bf16, 64>(a, stream);
+  else if (dtype == VS_F32 && D == 64) launch_bwd_typed<float, 64>(a, stream);
+  else return VS_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+}  // namespace vs

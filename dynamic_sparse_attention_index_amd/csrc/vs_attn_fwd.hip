@@ -1,0 +1,327 @@
+// Block-sparse attention forward over the active region of one ring step,
+// and the log-sum-exp merge of partial results.
+//
+// Computes, for every query row, softmax attention restricted to the active
+// entries of the vertical-slash set (MTraining review, page 1, section 三.2
+// item 3: only the active entries of the local sub-matrix are computed; item 2:
+// slashes at 64x64 block granularity, verticals at token granularity). The
+// incremental-softmax merge follows the Ring Attention overview page, section
+// 2.1.
+//
+// One workgroup = one (q head, 64-row query block); four waves of 16 rows.
+// Work per block: the listed slash tiles (dense 64x64 on MFMA, causal predicate
+// only on the block's own diagonal tile), then the shard's vertical columns
+// gathered 64 at a time into a dense tile (columns already inside a listed tile
+// or beyond the causal edge are masked). S^T = K Q^T keeps one query row per
+// lane, so the online-softmax state is per lane and O^T = V^T P^T consumes P
+// straight from registers; V^T fragments come from the row-major V tile via
+// the gfx950 LDS transpose read.
+#include <type_traits>
+
+#include "vs_common.h"
+#include "vs_internal.h"
+
+namespace vs {
+
+constexpr int FWD_THREADS = 256;  // 4 waves x 16 query rows
+
+struct FwdArgs {
+  const void* q; const void* k; const void* v;
+  int64_t qsh, qsn, ksh, ksn, vsh, vsn;
+  const int32_t* tile_ptr; const int32_t* tile_col;
+  const int32_t* vloc; const int32_t* vert_end; const uint32_t* slash_bits;
+  float* o; float* lse;
+  int Hq, Hkv, QB, KB, W, kind, P, rank, src, accumulate;
+  float scale_log2;
+};
+
+// Physical key (0..63) held by S^T output value i of 16-key subtile t in lane
+// group g: subtile t covers keys 32*(t/2) + 8*g + 4*(t%2) + i, so each lane
+// group later supplies 8 consecutive keys to the P.V contraction.
+__device__ __forceinline__ int key_of(int t, int g, int i) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i; }
+// Key row read by lane row m (0..15) of subtile t for the A operand of S^T.
+__device__ __forceinline__ int key_row(int t, int m) { return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3); }
+
+template <typename T, int D>
+struct FwdTile {
+  static constexpr int KP = D + (sizeof(T) == 2 ? 8 : 4);       // LDS row pitch (elements)
+  static constexpr int CPR = D * (int)sizeof(T) / 16;            // 16-byte chunks per row
+  static constexpr int CPT = BLK * CPR / FWD_THREADS;            // chunks per thread
+  static_assert(CPT >= 1 && BLK * CPR % FWD_THREADS == 0, "tile split");
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
+  using Tl = FwdTile<T, D>;
+  constexpr int KP = Tl::KP, CPR = Tl::CPR, CPT = Tl::CPT;
+  __shared__ __attribute__((aligned(16))) T Ks[BLK * KP];
+  __shared__ __attribute__((aligned(16))) T Vs[BLK * KP];
+  __shared__ int thr_sh[BLK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  // work item: heavy (late) query blocks first; contiguous item ranges per XCD
+  const int nitems = a.Hq * a.QB;
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int I = a.QB - 1 - item / a.Hq;
+  const int h = item % a.Hq;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int64_t u = (int64_t)h * a.QB + I;
+  const int rowoff = wave * 16 + n16;  // this lane's query row within the block
+  const int64_t grow = (int64_t)I * BLK + rowoff;
+
+  const T* qrow = (const T*)a.q + h * a.qsh + grow * a.qsn;
+  const T* kbase = (const T*)a.k + kvh * a.ksh;
+  const T* vbase = (const T*)a.v + kvh * a.vsh;
+
+  // Q fragment (B operand of S^T): this lane's row, contraction slots of group g4
+  constexpr int NQ = (sizeof(T) == 2) ? D / 32 : D / 4;
+  typedef typename std::conditional<sizeof(T) == 2, bf16x8, float>::type QFrag;
+  QFrag qf[NQ];
+  if constexpr (sizeof(T) == 2) {
+    #pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks + 8 * g4);
+  } else {
+    #pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) qf[ks] = qrow[4 * ks + g4];
+  }
+
+  const int t0 = a.tile_ptr[u];
+  const int nt = a.tile_ptr[u + 1] - t0;
+  const int ve = a.vert_end[u];
+  const int total = nt + (ve + BLK - 1) / BLK;
+  const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I);
+  const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
+  const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
+
+  f32x4 acc[D / 16];
+  #pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // staging registers for the next tile
+  i32x4 kreg[CPT], vreg[CPT];
+  int mode_next = 0, thr_next = 0;
+
+  auto fetch = [&](int it) {
+    int src_rows[CPT];
+    if (it < nt) {
+      const int e = a.tile_col[t0 + it];
+      const int J = e & VS_TILE_MASK;
+      mode_next = (e & VS_TILE_DIAG) ? 1 : 0;
+      #pragma unroll
+      for (int c = 0; c < CPT; ++c) src_rows[c] = J * BLK + (tid + c * FWD_THREADS) / CPR;
+      thr_next = tid < BLK ? tid : 0;  // causal threshold inside the diagonal tile
+    } else {
+      const int base = (it - nt) * BLK;
+      mode_next = 1;
+      #pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int slot = (tid + c * FWD_THREADS) / CPR;
+        const int idx = base + slot;
+        src_rows[c] = idx < ve ? vl[idx] : vl[base];
+      }
+      if (tid < BLK) {
+        const int idx = base + tid;
+        int thr = BLK;  // never active
+        if (idx < ve) {
+          const int m = vl[idx];
+          const int64_t gb = global_block(a.kind, a.P, a.KB, a.src, m / BLK);
+          const int64_t j = G - gb;
+          const bool covered = (sb[j >> 5] >> (j & 31)) & 1u;
+          if (!covered) thr = (j == 0) ? (m % BLK) : 0;
+        }
+        thr_next = thr;
+      }
+    }
+    #pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int col = ((tid + c * FWD_THREADS) % CPR) * (16 / (int)sizeof(T));
+      kreg[c] = *(const i32x4*)(kbase + src_rows[c] * a.ksn + col);
+      vreg[c] = *(const i32x4*)(vbase + src_rows[c] * a.vsn + col);
+    }
+  };
+
+  if (total > 0) fetch(0);
+  for (int it = 0; it < total; ++it) {
+    #pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * FWD_THREADS;
+      const int r = ch / CPR, col = (ch % CPR) * (16 / (int)sizeof(T));
+      *(i32x4*)(Ks + r * KP + col) = kreg[c];
+      *(i32x4*)(Vs + r * KP + col) = vreg[c];
+    }
+    if (tid < BLK) thr_sh[tid] = thr_next;
+    const int mode = mode_next;
+    __syncthreads();
+    if (it + 1 < total) fetch(it + 1);
+
+    // ---- S^T = K Q^T for this wave's 16 rows x 64 keys
+    f32x4 s[4];
+    #pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T* krow = Ks + key_row(t, n16) * KP;
+      if constexpr (sizeof(T) == 2) {
+        #pragma unroll
+        for (int ks = 0; ks < NQ; ++ks)
+          s[t] = mfma_bf16(*(const bf16x8*)(krow + 32 * ks + 8 * g4), qf[ks], s[t]);
+      } else {
+        #pragma unroll
+        for (int ks = 0; ks < NQ; ++ks) s[t] = mfma_f32(krow[4 * ks + g4], qf[ks], s[t]);
+      }
+    }
+    // ---- scale, mask, online softmax (log2 domain)
+    float mx = -INFINITY;
+    #pragma unroll
+    for (int t = 0; t < 4; ++t)
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[t][i] * a.scale_log2;
+        if (mode && thr_sh[key_of(t, g4, i)] > rowoff) x = -INFINITY;
+        s[t][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+    #pragma unroll
+    for (int t = 0; t < 4; ++t)
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[t][i] - m_use);
+        s[t][i] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    #pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) acc[dt][i] *= alpha;
+
+    // ---- O^T += V^T P^T
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 pf[2];
+      #pragma unroll
+      for (int c = 0; c < 2; ++c)
+        #pragma unroll
+        for (int e = 0; e < 2; ++e)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) pf[c][4 * e + i] = (bf16)s[2 * c + e][i];
+      #pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const T* base = Vs + (32 * c + 8 * g4 + (n16 >> 2)) * KP + 16 * dt + 4 * (n16 & 3);
+          acc[dt] = mfma_bf16(lds_read_tr16_x2(base, KP), pf[c], acc[dt]);
+        }
+    } else {
+      #pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        #pragma unroll
+        for (int t = 0; t < 4; ++t)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[dt] = mfma_f32(Vs[key_of(t, g4, i) * KP + 16 * dt + n16], s[t][i], acc[dt]);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write or merge
+  float l_tot = l_run + wave_shfl_xor(l_run, 16);
+  l_tot = l_tot + wave_shfl_xor(l_tot, 32);
+  const bool nonempty = l_tot > 0.f;
+  const float inv = nonempty ? 1.f / l_tot : 0.f;
+  const float lse_new = nonempty ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
+  float* orow = a.o + ((int64_t)h * a.QB * BLK + grow) * D;
+  float* lrow = a.lse + (int64_t)h * a.QB * BLK + grow;
+  if (!a.accumulate) {
+    #pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4 r;
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = acc[dt][i] * inv;
+      *(f32x4*)(orow + 16 * dt + 4 * g4) = r;
+    }
+    if (g4 == 0) *lrow = lse_new;
+  } else {
+    const float lse_old = *lrow;
+    const float mxl = fmaxf(lse_old, lse_new);
+    const float base = (mxl == -INFINITY) ? 0.f : mxl;
+    const float wa = expf(lse_old - base), wb = expf(lse_new - base);
+    const float tot = wa + wb;
+    const float ca = tot > 0.f ? wa / tot : 0.f;
+    const float cb = tot > 0.f ? wb / tot * inv : 0.f;
+    #pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4 old = *(f32x4*)(orow + 16 * dt + 4 * g4);
+      f32x4 r;
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = ca * old[i] + cb * acc[dt][i];
+      *(f32x4*)(orow + 16 * dt + 4 * g4) = r;
+    }
+    // every lane of the row has read lse_old before the wave writes it
+    if (g4 == 0) *lrow = tot > 0.f ? base + logf(tot) : -INFINITY;
+  }
+}
+
+int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* m, float scale,
+                    float* o, float* lse, int accumulate, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr;
+  a.qsh = q.sh; a.qsn = q.sn; a.ksh = k.sh; a.ksn = k.sn; a.vsh = v.sh; a.vsn = v.sn;
+  a.tile_ptr = m->tile_ptr; a.tile_col = m->tile_col; a.vloc = m->vloc; a.vert_end = m->vert_end;
+  a.slash_bits = m->slash_bits; a.o = o; a.lse = lse;
+  a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
+  a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
+  a.scale_log2 = scale * LOG2E;
+  const dim3 grid((unsigned)(m->Hq * m->QB)), block(FWD_THREADS);
+  if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 128>), grid, block, 0, stream, a);
+  else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
+  else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);
+  else return VS_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+// ---- log-sum-exp merge ------------------------------------------------------
+// One thread per (row, 4 consecutive features).
+__global__ void merge_kernel(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
+                             int64_t rows, int D) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = D / 4;
+  if (t >= rows * per) return;
+  const int64_t r = t / per;
+  const int c = (int)(t % per) * 4;
+  const float la = lse_acc[r], lb = lse_step[r];
+  const float mx = fmaxf(la, lb);
+  const float base = (mx == -INFINITY) ? 0.f : mx;
+  const float wa = expf(la - base), wb = expf(lb - base);
+  const float tot = wa + wb;
+  const float ca = tot > 0.f ? wa / tot : 0.f, cb = tot > 0.f ? wb / tot : 0.f;
+  f32x4 x = *(const f32x4*)(o_acc + r * D + c);
+  const f32x4 y = *(const f32x4*)(o_step + r * D + c);
+  #pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = ca * x[i] + cb * y[i];
+  *(f32x4*)(o_acc + r * D + c) = x;
+  // the row's LSE is written by the thread of its first feature group after
+  // the other groups of the same row have read it: rows never straddle a
+  // wave boundary (D/4 divides 64), and a wave's loads complete before its stores
+  if (c == 0) lse_acc[r] = tot > 0.f ? base + logf(tot) : -INFINITY;
+}
+
+int launch_merge(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
+                 int Hq, int64_t Nq, int D, hipStream_t stream) {
+  const int64_t rows = (int64_t)Hq * Nq;
+  const int64_t n = rows * (D / 4);
+  const int tpb = 256;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0, stream,
+                     o_acc, lse_acc, o_step, lse_step, rows, D);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+}  // namespace vs

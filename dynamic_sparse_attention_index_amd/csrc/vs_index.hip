@@ -1,0 +1,433 @@
+// Online sparse-index approximation on the GPU.
+//
+// MTraining review, page 1, section 三.2 item 1: the last queries are scored
+// against the keys, cumulative attention statistics are formed along the
+// vertical (column) and slash (diagonal) directions, and the minimum number of
+// verticals and slashes that recall the target attention mass is estimated;
+// item 2: verticals at token level, slashes aggregated over 64x64 blocks.
+// The budget is the "online top-p" of section 五.
+//
+// Passes:
+//   1. rowstat  -- per kv head and key range, the (max, sum exp) of every scored
+//                  row of every q head of the group (one K read, MFMA, exp);
+//   2. combine  -- the row log-sum-exp;
+//   3. colsum   -- recompute the logits, P = exp(z - LSE), column sums per q
+//                  head = vertical mass v(m); block sums of v = slash mass s(j)
+//                  (the scored rows lie in the last 64-block, so diagonal j
+//                  collects exactly key block T-1-j);
+//   4. select   -- per head, exact top-p by radix select on the fp32 bit
+//                  patterns with fixed-point mass histograms, then ascending
+//                  compaction.
+#include <algorithm>
+#include <type_traits>
+
+#include "vs_common.h"
+#include "vs_internal.h"
+
+namespace vs {
+
+constexpr int IDX_SPLIT_TARGET = 1024;   // workgroups per pass (over all kv heads)
+
+struct IndexArgs {
+  const void* q; const void* k;
+  int64_t qsh, qsn, ksh, ksn;
+  int Hq, Hkv, last_q, kind, P, NB, T, nsplit, tiles_per;
+  int64_t n_global;
+  float scale_log2;
+  float* part;       // [Hq, 64, nsplit, 2]
+  float* lse2;       // [Hq, 64] (log2 domain)
+  float* vert; float* slash;
+};
+
+template <typename T, int D>
+struct IdxTile {
+  static constexpr int KP = D + (sizeof(T) == 2 ? 8 : 4);
+  static constexpr int CPR = D * (int)sizeof(T) / 16;
+  static constexpr int NK = (sizeof(T) == 2) ? D / 32 : D / 4;
+  using Frag = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
+};
+
+// One wave holds the 64 scored rows of its q head as A operands (4 subtiles of
+// 16 rows) and multiplies them with the staged 64-key tile: acc[rs][kt] lane
+// (g, n) = S[row 16 rs + 4 g + i][key 16 kt + n].
+template <typename T, int D>
+__device__ __forceinline__ void score_tile(const T* Ks, const typename IdxTile<T, D>::Frag (*qa)[IdxTile<T, D>::NK],
+                                           int n16, int g4, f32x4 (*acc)[4]) {
+  constexpr int KP = IdxTile<T, D>::KP, NK = IdxTile<T, D>::NK;
+  #pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const T* kr = Ks + (16 * kt + n16) * KP;
+    typename IdxTile<T, D>::Frag kb[NK];
+    if constexpr (sizeof(T) == 2) {
+      #pragma unroll
+      for (int ks = 0; ks < NK; ++ks) kb[ks] = *(const bf16x8*)(kr + 32 * ks + 8 * g4);
+    } else {
+      #pragma unroll
+      for (int ks = 0; ks < NK; ++ks) kb[ks] = kr[4 * ks + g4];
+    }
+    #pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {
+      acc[rs][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      #pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        if constexpr (sizeof(T) == 2) acc[rs][kt] = mfma_bf16(qa[rs][ks], kb[ks], acc[rs][kt]);
+        else acc[rs][kt] = mfma_f32(qa[rs][ks], kb[ks], acc[rs][kt]);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_q_rows(const IndexArgs& a, int h, int n16, int g4,
+                                            typename IdxTile<T, D>::Frag (*qa)[IdxTile<T, D>::NK]) {
+  constexpr int NK = IdxTile<T, D>::NK;
+  #pragma unroll
+  for (int rs = 0; rs < 4; ++rs) {
+    const int r = 16 * rs + n16;
+    const T* qr = (const T*)a.q + h * a.qsh + (int64_t)r * a.qsn;
+    #pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      if constexpr (sizeof(T) == 2) {
+        qa[rs][ks] = r < a.last_q ? *(const bf16x8*)(qr + 32 * ks + 8 * g4) : bf16x8{};
+      } else {
+        qa[rs][ks] = r < a.last_q ? qr[4 * ks + g4] : 0.f;
+      }
+    }
+  }
+}
+
+// Stage key tile `tau` (storage order) of kv head `kvh` into LDS; returns its global block.
+template <typename T, int D>
+__device__ __forceinline__ int64_t stage_key_tile(T* Ks, const IndexArgs& a, int kvh, int tau, int tid, int nthr) {
+  constexpr int KP = IdxTile<T, D>::KP, CPR = IdxTile<T, D>::CPR;
+  const T* kb = (const T*)a.k + kvh * a.ksh + (int64_t)tau * BLK * a.ksn;
+  for (int ch = tid; ch < BLK * CPR; ch += nthr) {
+    const int r = ch / CPR, col = (ch % CPR) * (16 / (int)sizeof(T));
+    *(i32x4*)(Ks + r * KP + col) = *(const i32x4*)(kb + (int64_t)r * a.ksn + col);
+  }
+  return global_block(a.kind, a.P, a.NB, tau / a.NB, tau % a.NB);
+}
+
+// Pass 1: grid (nsplit, Hkv), 64 * group threads (one wave per q head).
+template <typename T, int D>
+__global__ void __launch_bounds__(512) index_rowstat_kernel(IndexArgs a) {
+  using Tl = IdxTile<T, D>;
+  __shared__ __attribute__((aligned(16))) T Ks[BLK * Tl::KP];
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int kvh = blockIdx.y, grp = a.Hq / a.Hkv, h = kvh * grp + wave;
+  typename Tl::Frag qa[4][Tl::NK];
+  load_q_rows<T, D>(a, h, n16, g4, qa);
+  const int row0 = BLK - a.last_q;          // row offset of scored row 0 in the last block
+  float m[4][4], l[4][4];
+  #pragma unroll
+  for (int rs = 0; rs < 4; ++rs)
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) { m[rs][i] = -INFINITY; l[rs][i] = 0.f; }
+  const int tau0 = blockIdx.x * a.tiles_per;
+  const int tau1 = min(a.T, tau0 + a.tiles_per);
+  for (int tau = tau0; tau < tau1; ++tau) {
+    const int64_t G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
+    __syncthreads();
+    f32x4 acc[4][4];
+    score_tile<T, D>(Ks, qa, n16, g4, acc);
+    const bool last = G == a.T - 1;
+    #pragma unroll
+    for (int rs = 0; rs < 4; ++rs)
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rs + 4 * g4 + i;
+        float x[4], tmax = -INFINITY;
+        #pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          float z = acc[rs][kt][i] * a.scale_log2;
+          if (r >= a.last_q || (last && 16 * kt + n16 > row0 + r)) z = -INFINITY;
+          x[kt] = z;
+          tmax = fmaxf(tmax, z);
+        }
+        if (tmax > m[rs][i]) {
+          l[rs][i] *= __builtin_amdgcn_exp2f(m[rs][i] - tmax);
+          m[rs][i] = tmax;
+        }
+        if (m[rs][i] > -INFINITY)
+          #pragma unroll
+          for (int kt = 0; kt < 4; ++kt) l[rs][i] += __builtin_amdgcn_exp2f(x[kt] - m[rs][i]);
+      }
+    __syncthreads();
+  }
+  // combine the 16 key lanes of each row
+  #pragma unroll
+  for (int rs = 0; rs < 4; ++rs)
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mm = m[rs][i], ll = l[rs][i];
+      #pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float mo = __shfl_xor(mm, off, 64), lo = __shfl_xor(ll, off, 64);
+        const float mn = fmaxf(mm, mo);
+        const float base = mn == -INFINITY ? 0.f : mn;
+        ll = ll * __builtin_amdgcn_exp2f(mm - base) + lo * __builtin_amdgcn_exp2f(mo - base);
+        mm = mn;
+      }
+      if (n16 == 0) {
+        const int r = 16 * rs + 4 * g4 + i;
+        float* p = a.part + (((int64_t)h * BLK + r) * a.nsplit + blockIdx.x) * 2;
+        p[0] = mm;
+        p[1] = ll;
+      }
+    }
+}
+
+// Pass 2: one thread per (q head, row).
+__global__ void index_combine_kernel(IndexArgs a) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.Hq * BLK) return;
+  const float* p = a.part + (int64_t)t * a.nsplit * 2;
+  float mm = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, p[2 * s]);
+  float ll = 0.f;
+  if (mm > -INFINITY)
+    for (int s = 0; s < a.nsplit; ++s) ll += p[2 * s + 1] * __builtin_amdgcn_exp2f(p[2 * s] - mm);
+  a.lse2[t] = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+}
+
+// Pass 3: grid (nsplit, Hkv); vertical mass per key and slash mass per block.
+template <typename T, int D>
+__global__ void __launch_bounds__(512) index_colsum_kernel(IndexArgs a) {
+  using Tl = IdxTile<T, D>;
+  __shared__ __attribute__((aligned(16))) T Ks[BLK * Tl::KP];
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int kvh = blockIdx.y, grp = a.Hq / a.Hkv, h = kvh * grp + wave;
+  typename Tl::Frag qa[4][Tl::NK];
+  load_q_rows<T, D>(a, h, n16, g4, qa);
+  float lse[4][4];
+  #pragma unroll
+  for (int rs = 0; rs < 4; ++rs)
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rs + 4 * g4 + i;
+      lse[rs][i] = r < a.last_q ? a.lse2[h * BLK + r] : -INFINITY;
+    }
+  const int row0 = BLK - a.last_q;
+  const float inv_rows = 1.f / (float)a.last_q;
+  const int tau0 = blockIdx.x * a.tiles_per;
+  const int tau1 = min(a.T, tau0 + a.tiles_per);
+  for (int tau = tau0; tau < tau1; ++tau) {
+    const int64_t G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
+    __syncthreads();
+    f32x4 acc[4][4];
+    score_tile<T, D>(Ks, qa, n16, g4, acc);
+    const bool last = G == a.T - 1;
+    float col[4];
+    #pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      float c = 0.f;
+      #pragma unroll
+      for (int rs = 0; rs < 4; ++rs)
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rs + 4 * g4 + i;
+          const bool act = lse[rs][i] > -INFINITY && !(last && 16 * kt + n16 > row0 + r);
+          if (act) c += __builtin_amdgcn_exp2f(acc[rs][kt][i] * a.scale_log2 - lse[rs][i]);
+        }
+      c += __shfl_xor(c, 16, 64);
+      c += __shfl_xor(c, 32, 64);
+      col[kt] = c * inv_rows;
+    }
+    if (g4 == 0)
+      #pragma unroll
+      for (int kt = 0; kt < 4; ++kt) a.vert[(int64_t)h * a.n_global + G * BLK + 16 * kt + n16] = col[kt];
+    float bs = col[0] + col[1] + col[2] + col[3];
+    #pragma unroll
+    for (int off = 1; off < 16; off <<= 1) bs += __shfl_xor(bs, off, 64);
+    if (lane == 0) a.slash[(int64_t)h * a.T + (a.T - 1 - G)] = bs;
+    __syncthreads();
+  }
+}
+
+// ---- exact top-p selection ---------------------------------------------------
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+
+struct SelectArgs {
+  const float* vert; const float* slash;
+  int32_t *vert_idx, *vert_cnt, *slash_idx, *slash_cnt;
+  int64_t n_vert; int n_slash;
+  float top_p;
+};
+
+__device__ __forceinline__ uint64_t fixed_mass(float x) {
+  return (uint64_t)__builtin_rint((double)x * 1099511627776.0);  // x * 2^40, exact for fp32 x
+}
+
+// Block-wide exclusive scan (SEL_THREADS threads), returns the block total.
+__device__ __forceinline__ int sel_scan(int x, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+  #pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) { const int t = sh[w]; sh[w] = run; run += t; }
+    sh[SEL_WAVES] = run;
+  }
+  __syncthreads();
+  const int res = sh[wave] + incl - x;
+  *total = sh[SEL_WAVES];
+  __syncthreads();
+  return res;
+}
+
+// grid (Hq, 2): y = 0 vertical scores, y = 1 slash scores.
+__global__ void __launch_bounds__(SEL_THREADS) topp_select_kernel(SelectArgs a) {
+  __shared__ unsigned long long hist[SEL_WAVES][256];
+  __shared__ unsigned long long red[SEL_WAVES];
+  __shared__ int scan_sh[SEL_WAVES + 1];
+  __shared__ unsigned long long sel_rem;
+  __shared__ uint32_t sel_prefix;
+  const int h = blockIdx.x;
+  const bool is_vert = blockIdx.y == 0;
+  const int64_t n = is_vert ? a.n_vert : a.n_slash;
+  const float* x = is_vert ? a.vert + h * a.n_vert : a.slash + (int64_t)h * a.n_slash;
+  int32_t* out = is_vert ? a.vert_idx + h * a.n_vert : a.slash_idx + (int64_t)h * a.n_slash;
+  int32_t* cnt = is_vert ? a.vert_cnt + h : a.slash_cnt + h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if (a.top_p >= 1.f) {
+    for (int64_t i = tid; i < n; i += SEL_THREADS) out[i] = (int32_t)i;
+    if (tid == 0) *cnt = (int32_t)n;
+    return;
+  }
+  if (!(a.top_p > 0.f)) {
+    if (tid == 0) *cnt = 0;
+    return;
+  }
+  // total fixed-point mass
+  unsigned long long s = 0;
+  for (int64_t i = tid; i < n; i += SEL_THREADS) s += fixed_mass(x[i]);
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long tot = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) tot += red[w];
+    const unsigned long long pq = (unsigned long long)__builtin_rint((double)a.top_p * 4294967296.0);
+    const unsigned __int128 prod = (unsigned __int128)pq * tot;
+    sel_rem = (unsigned long long)((prod + 0xFFFFFFFFull) >> 32);   // ceil(pq * tot / 2^32)
+    sel_prefix = 0;
+  }
+  __syncthreads();
+  if (sel_rem == 0) {
+    if (tid == 0) *cnt = 0;
+    return;
+  }
+  // radix select on the fp32 bit pattern (non-negative: bit order = value order)
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int b = lane; b < 256; b += 64) hist[wave][b] = 0;
+    __syncthreads();
+    const uint32_t prefix = sel_prefix;
+    for (int64_t i = tid; i < n; i += SEL_THREADS) {
+      const float xv = x[i];
+      const uint32_t bits = __float_as_uint(xv);
+      if ((bits & hi_mask) == prefix) atomicAdd(&hist[wave][(bits >> shift) & 255u], fixed_mass(xv));
+    }
+    __syncthreads();
+    if (tid < 256) {
+      unsigned long long t = 0;
+      for (int w = 0; w < SEL_WAVES; ++w) t += hist[w][tid];
+      hist[0][tid] = t;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long rem = sel_rem, above = 0;
+      int b = 255;
+      for (; b > 0; --b) {
+        if (above + hist[0][b] >= rem) break;
+        above += hist[0][b];
+      }
+      sel_rem = rem - above;
+      sel_prefix = prefix | ((uint32_t)b << shift);
+    }
+    __syncthreads();
+  }
+  const uint32_t xstar = sel_prefix;
+  const unsigned long long qstar = fixed_mass(__uint_as_float(xstar));
+  const unsigned long long k_tie = qstar ? (sel_rem + qstar - 1) / qstar : 0;
+  // ascending compaction: x > x*, or x == x* among the first k_tie ties
+  int base = 0;
+  unsigned long long ties_before = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += SEL_THREADS) {
+    const int64_t i = c0 + tid;
+    uint32_t bits = 0;
+    if (i < n) bits = __float_as_uint(x[i]);
+    const int is_tie = (i < n) && bits == xstar;
+    int tie_tot;
+    const int tie_pos = sel_scan(is_tie, &tie_tot, scan_sh);
+    const int keep = (i < n) && (bits > xstar || (is_tie && ties_before + tie_pos < k_tie));
+    int tot;
+    const int pos = sel_scan(keep, &tot, scan_sh);
+    if (keep) out[base + pos] = (int32_t)i;
+    base += tot;
+    ties_before += tie_tot;
+  }
+  if (tid == 0) *cnt = base;
+}
+
+size_t index_workspace_bytes(int Hq, int Hkv, int64_t n_global, int D, int last_q) {
+  (void)D; (void)last_q;
+  const int64_t T = n_global / BLK;
+  const int64_t nsplit = std::min<int64_t>(T, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
+  return (size_t)(Hq * BLK * nsplit * 2 + Hq * BLK) * sizeof(float) + 256;
+}
+
+int launch_index_build(int dtype, int D, TView q_last, int Hq, int last_q, TView k, int Hkv,
+                       const vs_layout& lay, float scale, float top_p, float* vert_score,
+                       float* slash_score, int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx,
+                       int32_t* slash_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  IndexArgs a;
+  a.q = q_last.ptr; a.k = k.ptr;
+  a.qsh = q_last.sh; a.qsn = q_last.sn; a.ksh = k.sh; a.ksn = k.sn;
+  a.Hq = Hq; a.Hkv = Hkv; a.last_q = last_q; a.kind = lay.kind; a.P = lay.P;
+  a.n_global = lay.n_global;
+  a.T = (int)(lay.n_global / BLK);
+  a.NB = a.T / lay.P;
+  a.nsplit = (int)std::min<int64_t>(a.T, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
+  a.tiles_per = (a.T + a.nsplit - 1) / a.nsplit;
+  a.nsplit = (a.T + a.tiles_per - 1) / a.tiles_per;
+  a.scale_log2 = scale * LOG2E;
+  if (ws_bytes < index_workspace_bytes(Hq, Hkv, lay.n_global, D, last_q)) return VS_ERR_WORKSPACE;
+  a.part = (float*)ws;
+  a.lse2 = a.part + (int64_t)Hq * BLK * a.nsplit * 2;
+  a.vert = vert_score; a.slash = slash_score;
+  const int grp = Hq / Hkv;
+  const dim3 grid(a.nsplit, Hkv), block(64 * grp);
+  if (dtype == VS_BF16 && D == 128) {
+    hipLaunchKernelGGL((index_rowstat_kernel<bf16, 128>), grid, block, 0, stream, a);
+  } else if (dtype == VS_BF16 && D == 64) {
+    hipLaunchKernelGGL((index_rowstat_kernel<bf16, 64>), grid, block, 0, stream, a);
+  } else if (dtype == VS_F32 && D == 64) {
+    hipLaunchKernelGGL((index_rowstat_kernel<float, 64>), grid, block, 0, stream, a);
+  } else {
+    return VS_ERR_UNSUPPORTED;
+  }
+  hipLaunchKernelGGL(index_combine_kernel, dim3((Hq * BLK + 255) / 256), dim3(256), 0, stream, a);
+  if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL((index_colsum_kernel<bf16, 128>), grid, block, 0, stream, a);
+  else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((index_colsum_kernel<bf16, 64>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((index_colsum_kernel<float, 64>), grid, block, 0, stream, a);
+  SelectArgs s;
+  s.vert = vert_score; s.slash = slash_score; s.vert_idx = vert_idx; s.vert_cnt = vert_cnt;
+  s.slash_idx = slash_idx; s.slash_cnt = slash_cnt; s.n_vert = lay.n_global; s.n_slash = a.T; s.top_p = top_p;
+  hipLaunchKernelGGL(topp_select_kernel, dim3(Hq, 2), dim3(SEL_THREADS), 0, stream, s);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+}  // namespace vs

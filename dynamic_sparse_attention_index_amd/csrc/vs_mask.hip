@@ -1,0 +1,237 @@
+// Active-region compaction: from the shared vertical/slash index to the
+// per-(head, query block) tile lists, their transpose, the shard's vertical
+// columns and exact active-entry counts of one (rank, ring step).
+//
+// Follows the MTraining review, page 1, section 三.2 item 3: after the index is
+// shared, each worker determines the active region of its local attention
+// sub-matrix from the indices of the active verticals and slashes. The review
+// times a 2.08 ms host step next to the index build (section 五, latency
+// breakdown); here the whole conversion is integer work on the GPU.
+//
+// Four launches: per-head setup (slash bitmap, the shard's vertical columns and
+// their per-block prefix counts), list lengths, one exclusive scan, list fill.
+#include "vs_common.h"
+#include "vs_internal.h"
+
+namespace vs {
+
+struct MaskArgs {
+  const int32_t* vert_idx; const int32_t* vert_cnt; int64_t vert_stride;
+  const int32_t* slash_idx; const int32_t* slash_cnt; int64_t slash_stride;
+  int kind, P, NB, T, W, Hq, rank, src;
+  int64_t tile_cap;
+  int32_t *tile_ptr, *tile_col, *csc_ptr, *csc_row, *vloc, *vloc_cnt, *vcum, *vert_end;
+  uint32_t* slash_bits;
+  int64_t* n_active;
+  int32_t* status;
+};
+
+constexpr int MASK_THREADS = 1024;
+
+// Block-wide exclusive scan of one int per thread (1024 threads = 16 waves).
+__device__ __forceinline__ int block_exclusive_scan(int x, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < MASK_THREADS / 64; ++w) { int t = sh[w]; sh[w] = run; run += t; }
+    sh[MASK_THREADS / 64] = run;
+  }
+  __syncthreads();
+  int res = sh[wave] + incl - x;
+  *total = sh[MASK_THREADS / 64];
+  __syncthreads();
+  return res;
+}
+
+// Launch 1: grid = Hq, one workgroup per head.
+__global__ void __launch_bounds__(MASK_THREADS) mask_head_kernel(MaskArgs a) {
+  __shared__ int sh[MASK_THREADS / 64 + 1];
+  const int h = blockIdx.x;
+  const int32_t* S = a.slash_idx + (int64_t)h * a.slash_stride;
+  const int ns = a.slash_cnt[h];
+  if (h == 0 && threadIdx.x == 0) a.status[0] = VS_OK;
+  // slash bitmap
+  for (int w = threadIdx.x; w < a.W; w += MASK_THREADS) {
+    int lo = lower_bound_i32(S, ns, (int64_t)w * 32);
+    int hi = lower_bound_i32(S, ns, (int64_t)w * 32 + 32);
+    uint32_t bits = 0;
+    for (int e = lo; e < hi; ++e) {
+      const int d = S[e] - w * 32;
+      if (d >= 0 && d < 32) bits |= 1u << d;
+    }
+    a.slash_bits[(int64_t)h * a.W + w] = bits;
+  }
+  // vertical columns of the visible shard, order-preserving compaction
+  const int32_t* V = a.vert_idx + (int64_t)h * a.vert_stride;
+  const int nv = a.vert_cnt[h];
+  int32_t* out = a.vloc + (int64_t)h * a.NB * BLK;
+  int base = 0;
+  for (int c0 = 0; c0 < nv; c0 += MASK_THREADS) {
+    const int e = c0 + threadIdx.x;
+    int keep = 0, local = 0;
+    if (e < nv) {
+      const int64_t m = V[e];
+      if (m >= 0 && m < (int64_t)a.T * BLK) {
+        int J;
+        keep = owner_of_block(a.kind, a.P, a.NB, m / BLK, &J) == a.src;
+        local = J * BLK + (int)(m % BLK);
+      }
+    }
+    int tot;
+    const int pos = block_exclusive_scan(keep, &tot, sh);
+    if (keep && base + pos < a.NB * BLK) out[base + pos] = local;
+    base += tot;
+  }
+  base = min(base, a.NB * BLK);  // only reachable with repeated positions in the input
+  if (threadIdx.x == 0) a.vloc_cnt[h] = base;
+  __syncthreads();
+  // vcum[J] = number of shard verticals in local blocks < J
+  for (int J = threadIdx.x; J <= a.NB; J += MASK_THREADS)
+    a.vcum[(int64_t)h * (a.NB + 1) + J] = lower_bound_i32(out, base, (int64_t)J * BLK);
+}
+
+// Launch 2: list lengths. Threads [0, Hq*NB) handle (h, I) rows of the CSR,
+// threads [Hq*NB, 2*Hq*NB) handle (h, J) columns of the CSC.
+__global__ void mask_count_kernel(MaskArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nrow = (int64_t)a.Hq * a.NB;
+  if (t >= 2 * nrow) return;
+  const bool csr = t < nrow;
+  const int64_t u = csr ? t : t - nrow;
+  const int h = (int)(u / a.NB), B = (int)(u % a.NB);
+  const int32_t* S = a.slash_idx + (int64_t)h * a.slash_stride;
+  const int ns = a.slash_cnt[h];
+  int cnt = 0;
+  if (csr) {  // key blocks G - j of the visible shard
+    const int64_t G = global_block(a.kind, a.P, a.NB, a.rank, B);
+    for (int e = 0; e < ns; ++e) {
+      const int j = S[e];
+      if (j < 0 || j > G) continue;
+      int J;
+      if (owner_of_block(a.kind, a.P, a.NB, G - j, &J) == a.src) ++cnt;
+    }
+    a.tile_ptr[1 + u] = cnt;
+  } else {    // query blocks G' + j of this rank
+    const int64_t Gp = global_block(a.kind, a.P, a.NB, a.src, B);
+    for (int e = 0; e < ns; ++e) {
+      const int j = S[e];
+      if (j < 0 || Gp + j >= a.T) continue;
+      int I;
+      if (owner_of_block(a.kind, a.P, a.NB, Gp + j, &I) == a.rank) ++cnt;
+    }
+    a.csc_ptr[1 + u] = cnt;
+  }
+}
+
+// Launch 3: one workgroup; in-place inclusive scan of both length arrays.
+__device__ void scan_inplace(int32_t* p, int64_t n, int* sh) {
+  int run = 0;
+  if (threadIdx.x == 0) p[0] = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += MASK_THREADS) {
+    const int64_t e = c0 + threadIdx.x;
+    const int x = e < n ? p[1 + e] : 0;
+    int tot;
+    const int pos = block_exclusive_scan(x, &tot, sh);
+    if (e < n) p[1 + e] = run + pos + x;
+    run += tot;
+  }
+}
+
+__global__ void __launch_bounds__(MASK_THREADS) mask_scan_kernel(MaskArgs a) {
+  __shared__ int sh[MASK_THREADS / 64 + 1];
+  const int64_t n = (int64_t)a.Hq * a.NB;
+  scan_inplace(a.tile_ptr, n, sh);
+  scan_inplace(a.csc_ptr, n, sh);
+  __syncthreads();
+  if (threadIdx.x == 0 && ((int64_t)a.tile_ptr[n] > a.tile_cap || (int64_t)a.csc_ptr[n] > a.tile_cap))
+    a.status[0] = VS_ERR_CAPACITY;
+}
+
+// Launch 4: fill the lists; the CSR half also writes vert_end and n_active.
+__global__ void mask_fill_kernel(MaskArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nrow = (int64_t)a.Hq * a.NB;
+  if (t >= 2 * nrow) return;
+  const bool csr = t < nrow;
+  const int64_t u = csr ? t : t - nrow;
+  const int h = (int)(u / a.NB), B = (int)(u % a.NB);
+  const int32_t* S = a.slash_idx + (int64_t)h * a.slash_stride;
+  const int ns = a.slash_cnt[h];
+  const bool fits = a.status[0] == VS_OK;
+  if (csr) {
+    const int64_t G = global_block(a.kind, a.P, a.NB, a.rank, B);
+    const int32_t* vc = a.vcum + (int64_t)h * (a.NB + 1);
+    int32_t* dst = a.tile_col + a.tile_ptr[u];
+    int n = 0;
+    int64_t act = 0, covered = 0;
+    // descending j gives ascending key blocks (same predicate as the count)
+    for (int e = ns - 1; e >= 0; --e) {
+      const int j = S[e];
+      if (j < 0 || j > G) continue;
+      int J;
+      if (owner_of_block(a.kind, a.P, a.NB, G - j, &J) != a.src) continue;
+      if (fits) dst[n] = J | (j == 0 ? VS_TILE_DIAG : 0);
+      ++n;
+      if (j == 0) {
+        act += BLK * (BLK + 1) / 2;
+      } else {
+        act += BLK * BLK;
+        covered += vc[J + 1] - vc[J];
+      }
+    }
+    const int J_le = blocks_upto(a.kind, a.P, a.NB, a.src, G);
+    const int J_lt = blocks_upto(a.kind, a.P, a.NB, a.src, G - 1);
+    a.vert_end[u] = vc[J_le];
+    act += (int64_t)BLK * (vc[J_lt] - covered);
+    if (J_le > J_lt) {  // the shard holds the query block's own global block
+      const bool diag_sel = (a.slash_bits[(int64_t)h * a.W] & 1u) != 0;
+      if (!diag_sel) {
+        const int32_t* vl = a.vloc + (int64_t)h * a.NB * BLK;
+        for (int e = vc[J_lt]; e < vc[J_le]; ++e) act += BLK - (vl[e] % BLK);
+      }
+    }
+    a.n_active[u] = act;
+  } else {
+    if (!fits) return;
+    const int64_t Gp = global_block(a.kind, a.P, a.NB, a.src, B);
+    int32_t* dst = a.csc_row + a.csc_ptr[u];
+    int n = 0;
+    for (int e = 0; e < ns; ++e) {
+      const int j = S[e];
+      if (j < 0 || Gp + j >= a.T) continue;
+      int I;
+      if (owner_of_block(a.kind, a.P, a.NB, Gp + j, &I) != a.rank) continue;
+      dst[n++] = I | (j == 0 ? VS_TILE_DIAG : 0);
+    }
+  }
+}
+
+int launch_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
+                      const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
+                      int rank, int src, vs_mask* m, hipStream_t stream) {
+  MaskArgs a;
+  a.vert_idx = vert_idx; a.vert_cnt = vert_cnt; a.vert_stride = vert_stride;
+  a.slash_idx = slash_idx; a.slash_cnt = slash_cnt; a.slash_stride = slash_stride;
+  a.kind = m->lay.kind; a.P = m->lay.P; a.NB = m->QB; a.T = m->T; a.W = m->W; a.Hq = m->Hq;
+  a.rank = rank; a.src = src; a.tile_cap = m->tile_cap;
+  a.tile_ptr = m->tile_ptr; a.tile_col = m->tile_col; a.csc_ptr = m->csc_ptr; a.csc_row = m->csc_row;
+  a.vloc = m->vloc; a.vloc_cnt = m->vloc_cnt; a.vcum = m->vcum; a.vert_end = m->vert_end;
+  a.slash_bits = m->slash_bits; a.n_active = m->n_active; a.status = m->status;
+  const int64_t nthr = 2 * (int64_t)m->Hq * m->QB;
+  const int tpb = 256;
+  const unsigned nblk = (unsigned)((nthr + tpb - 1) / tpb);
+  hipLaunchKernelGGL(mask_head_kernel, dim3(m->Hq), dim3(MASK_THREADS), 0, stream, a);
+  hipLaunchKernelGGL(mask_count_kernel, dim3(nblk), dim3(tpb), 0, stream, a);
+  hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(MASK_THREADS), 0, stream, a);
+  hipLaunchKernelGGL(mask_fill_kernel, dim3(nblk), dim3(tpb), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+}  // namespace vs

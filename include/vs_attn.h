@@ -1,0 +1,218 @@
+/*
+ * vs_attn.h -- C ABI of the vertical-slash (VS) dynamic sparse attention path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The path is the per-rank hot path of MTraining (review page "MTraining:
+ * 分布式动态稀疏注意力高效超长上下文训练", xllm-io paper-review):
+ *   1. vs_index_build  -- online sparse-index approximation (section 三.2 item 1
+ *                         and 2): score the last queries against every key, take
+ *                         the attention mass of token-level vertical columns and
+ *                         of 64x64 block-level slash diagonals, and keep the
+ *                         fewest of each that reach the top-p budget;
+ *   2. vs_block_mask   -- each worker derives the active region of its local
+ *                         attention sub-matrix from the shared index (section
+ *                         三.2 item 3);
+ *   3. vs_attn_fwd     -- block-sparse flash attention over only the active
+ *                         entries of one ring step (same item);
+ *   4. vs_merge_lse    -- incremental-softmax merge of partial results across
+ *                         ring steps (Ring Attention overview page,
+ *                         intelliparadigm, section 2.1);
+ *   5. vs_attn_bwd_prep / vs_attn_bwd -- gradient of the same sparse attention.
+ *
+ * Conventions shared by every call:
+ *   - All data pointers are DEVICE pointers unless stated otherwise. The
+ *     library never allocates, frees or retains device memory: every buffer,
+ *     including scratch, is owned by the caller.
+ *   - Every compute call is asynchronous on `stream` (a hipStream_t; NULL is
+ *     the default stream). Host-side validation errors are returned
+ *     synchronously; a kernel launch failure returns VS_ERR_HIP. Conditions
+ *     found on the device (list capacity overflow) are written to a device
+ *     status word that the caller reads after synchronising the stream.
+ *   - A token position is "global" when it indexes the whole sequence and
+ *     "local" when it indexes one rank's shard in storage order.
+ *   - Attention uses natural-log LSE, logits q.k * scale (scale = 1/sqrt(D)),
+ *     query head h reads kv head h / (Hq / Hkv). Empty rows give O = 0 and
+ *     LSE = -inf and contribute no gradient.
+ *   - The active set of query head h with vertical set V_h (global positions)
+ *     and slash set S_h (block-diagonal ids, block = 64 tokens) is
+ *       M_h[n, m] = [m <= n] and ([m in V_h] or [n/64 - m/64 in S_h]).
+ * Supported: D in {64, 128}; dtype f32 or bf16 (q, k, v, dout alike); every
+ * local length a multiple of 64; Hq a multiple of Hkv; last_q in [1, 64].
+ */
+#ifndef VS_ATTN_H
+#define VS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VS_OK = 0,
+  VS_ERR_ARG = -1,          /* null pointer, inconsistent shape or bad value   */
+  VS_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head dim, alignment) */
+  VS_ERR_WORKSPACE = -3,    /* workspace or mask buffer too small              */
+  VS_ERR_CAPACITY = -4,     /* device-side list capacity exceeded (status word) */
+  VS_ERR_HIP = -5           /* a HIP runtime call or kernel launch failed      */
+} vs_status;
+
+typedef enum { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
+
+/* How global positions are dealt to the P ranks of the context-parallel ring
+ * (review page 1, section 三.3):
+ *   VS_CONTIG  -- rank r holds [r*N/P, (r+1)*N/P);
+ *   VS_STRIPED -- 64-token stripes round-robin: rank r holds global blocks
+ *                 G with G mod P == r (the balanced layout);
+ *   VS_ZIGZAG  -- 2P equal chunks, rank r holds chunks r and 2P-1-r.
+ * A shard is stored in ascending global order. P = 1 is the plain sequence. */
+typedef enum { VS_CONTIG = 0, VS_STRIPED = 1, VS_ZIGZAG = 2 } vs_layout_kind;
+
+typedef struct {
+  int32_t kind;      /* vs_layout_kind */
+  int32_t P;         /* ranks, >= 1 */
+  int64_t n_global;  /* whole sequence length, a multiple of 64*P (128*P for zigzag) */
+} vs_layout;
+
+/* A [H, N, D] tensor view; D is contiguous, strides are in elements. */
+typedef struct {
+  const void* ptr;
+  int32_t dtype;     /* vs_dtype */
+  int32_t H;
+  int64_t N;
+  int32_t D;
+  int64_t stride_h;
+  int64_t stride_n;
+} vs_tensor;
+
+/* Flag bit on tile_col / csc_row entries: the tile is the query block's own
+ * global block, so the causal predicate applies inside it. */
+#define VS_TILE_DIAG 0x40000000
+#define VS_TILE_MASK 0x3FFFFFFF
+
+/* Host-side descriptor of the active region of one (rank, ring step), with
+ * device arrays carved from one caller-owned device buffer by vs_mask_init.
+ * QB = local query blocks, KB = local key blocks (= QB), T = global blocks.
+ *   tile_ptr[Hq*QB+1], tile_col[tile_cap]: per (head h, query block I) the
+ *       ascending local key blocks J of the visible shard whose 64x64 tile
+ *       holds a slash-active entry (CSR), ORed with VS_TILE_DIAG;
+ *   csc_ptr[Hq*KB+1], csc_row[tile_cap]: the same pairs per (h, J), listing
+ *       ascending I (CSC), ORed with VS_TILE_DIAG;
+ *   vloc[Hq*KB*64] (head h at h*KB*64), vloc_cnt[Hq]: ascending local
+ *       positions of the visible shard's vertical columns;
+ *   vcum[Hq*(KB+1)]: vertical columns of the shard before local block J;
+ *   vert_end[Hq*QB]: the first vert_end entries of vloc have an active entry
+ *       in query block I (those in a listed tile are covered by it and are
+ *       skipped by the kernels);
+ *   slash_bits[Hq*W], W = ceil(T/32): bit j set iff j in S_h;
+ *   n_active[Hq*QB]: active entries of query block I in this shard (exact);
+ *   status[1]: VS_OK or VS_ERR_CAPACITY after vs_block_mask. */
+typedef struct {
+  int32_t Hq, Hkv, QB, KB, T, W;
+  vs_layout lay;
+  int64_t tile_cap;
+  int32_t rank, src;          /* set by vs_block_mask */
+  int32_t* tile_ptr;
+  int32_t* tile_col;
+  int32_t* csc_ptr;
+  int32_t* csc_row;
+  int32_t* vloc;
+  int32_t* vloc_cnt;
+  int32_t* vcum;
+  int32_t* vert_end;
+  uint32_t* slash_bits;
+  int64_t* n_active;
+  int32_t* status;
+} vs_mask;
+
+/* Human-readable name of a status code (static string). */
+const char* vs_status_string(int status);
+
+/* ---- 1. sparse index -------------------------------------------------- */
+
+/* Workspace bytes vs_index_build needs (device memory). */
+size_t vs_index_workspace_size(int Hq, int Hkv, int64_t n_global, int D, int last_q);
+
+/* Online sparse-index approximation (review page 1, section 三.2 items 1-2).
+ *   q_last: [Hq, last_q, D], the queries at global rows n_global-last_q ..
+ *           n_global-1;
+ *   k:      [Hkv, n_global, D], every key, shards concatenated in rank order
+ *           under `lay` (for P = 1: global order);
+ *   scale:  logit scale (1/sqrt(D));
+ *   top_p:  target mass; >= 1 keeps every element, <= 0 keeps none.
+ * Outputs (device, caller-owned):
+ *   vert_score[Hq, n_global]  fp32: v_h(m) = (1/last_q) sum over the scored
+ *       rows n >= m of softmax_n(m), indexed by global position;
+ *   slash_score[Hq, n_global/64] fp32: s_h(j) = mass on block-diagonal j;
+ *   vert_idx[Hq, n_global], vert_cnt[Hq]: per head the selected global
+ *       positions, ascending (row stride n_global);
+ *   slash_idx[Hq, n_global/64], slash_cnt[Hq]: selected diagonals, ascending.
+ * Selection: per head and separately for v and s, the fewest elements in
+ * descending score order (ties: lower index first) whose fixed-point mass
+ * sum_i round(x_i * 2^40) reaches ceil(round(p * 2^32) * total / 2^32). */
+int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, float top_p,
+                   float* vert_score, float* slash_score,
+                   int32_t* vert_idx, int32_t* vert_cnt,
+                   int32_t* slash_idx, int32_t* slash_cnt,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---- 2. active region ------------------------------------------------- */
+
+/* Device bytes of one mask buffer able to hold `tile_cap` (h, I, J) tiles. */
+size_t vs_mask_bytes(int Hq, int Hkv, vs_layout lay, int64_t tile_cap);
+
+/* Carve a caller-owned device buffer into the arrays of `m` (host call, no
+ * device work). Returns VS_ERR_WORKSPACE if `bytes` is too small. */
+int vs_mask_init(vs_mask* m, void* buf, size_t bytes, int Hq, int Hkv, vs_layout lay, int64_t tile_cap);
+
+/* Derive the active region of rank `rank` at ring step `step` (visible KV
+ * shard src = (rank - step) mod P) from the shared index (review page 1,
+ * section 三.2 item 3). vert_idx/slash_idx rows have strides vert_stride /
+ * slash_stride (elements) and hold vert_cnt[h] / slash_cnt[h] ascending
+ * entries. Fills every array of `m`; on tile-list overflow writes
+ * VS_ERR_CAPACITY to m->status and leaves the lists unspecified. */
+int vs_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
+                  const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
+                  int rank, int step, vs_mask* m, void* stream);
+
+/* ---- 3./4. forward and merge ----------------------------------------- */
+
+/* Sparse attention of the rank's queries against one visible KV shard,
+ * computing only the tiles and vertical columns listed in `m`.
+ *   q: [Hq, QB*64, D] (rank's shard), k, v: [Hkv, KB*64, D] (shard m->src);
+ *   o: [Hq, QB*64, D] fp32 contiguous, lse: [Hq, QB*64] fp32.
+ * accumulate = 0: o, lse receive this step's normalised output and LSE.
+ * accumulate = 1: (o, lse) hold a running merge (start: o = 0, lse = -inf)
+ *   and this step's result is merged into them in place (same formula as
+ *   vs_merge_lse), without writing the step's own output. */
+int vs_attn_fwd(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float scale,
+                float* o, float* lse, int accumulate, void* stream);
+
+/* In-place log-sum-exp merge (Ring Attention overview, section 2.1):
+ *   L = log(e^La + e^Lb), O = e^(La-L) Oa + e^(Lb-L) Ob, (0, -inf) = identity.
+ * o_acc/o_step: [Hq, Nq, D] fp32 contiguous; lse_acc/lse_step: [Hq, Nq]. */
+int vs_merge_lse(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
+                 int Hq, int64_t Nq, int D, void* stream);
+
+/* ---- 5. backward ------------------------------------------------------ */
+
+/* delta[h, n] = sum_d dout[h, n, d] * o[h, n, d] (the row term of the
+ * softmax gradient), from the FINAL output o [Hq, Nq, D] fp32 contiguous. */
+int vs_attn_bwd_prep(const float* o, vs_tensor dout, float* delta, void* stream);
+
+/* Gradient contribution of the active entries of `m` (one ring step), using
+ * the final lse [Hq, Nq] and delta [Hq, Nq] of the rank's rows:
+ *   P = exp(q.k*scale - lse), dV += P^T dO, dS = P (dO.v - delta),
+ *   dQ += dS K scale, dK += dS^T Q scale, summed over the q heads of a kv head.
+ * dq [Hq, Nq, D], dk/dv [Hkv, Nk, D]: fp32 contiguous, accumulated (+=); the
+ * caller zeroes them before the first step. dk/dv contributions of vertical
+ * columns are added with fp32 atomics, so their low bits may vary run to run. */
+int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout,
+                const float* lse, const float* delta, const vs_mask* m, float scale,
+                float* dq, float* dk, float* dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VS_ATTN_H */

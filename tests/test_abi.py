@@ -1,0 +1,133 @@
+"""The C ABI library: exported symbols and host-side validation (no GPU needed).
+
+Only calls that return before any device work are made here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_attention_index_amd as vs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vs_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vs_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(vs.LIB_PATH):
+        pytest.skip("library not built")
+    return vs.lib()
+
+
+def test_header_symbols_exported(L):
+    names = _declared()
+    assert set(names) == set(vs.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert vs.status_string(code) and vs.status_string(code) != "unknown status"
+    assert vs.status_string(123) == "unknown status"
+
+
+def _fake_tensor(addr, H, N, D, dtype=vs.VS_BF16):
+    return vs.VsTensor(addr, dtype, H, N, D, N * D, D)
+
+
+def _mask(L, Hq=4, Hkv=2, N=1024, kind="contig", P=1, cap=100):
+    lay = vs.layout(kind, P, N)
+    nbytes = L.vs_mask_bytes(Hq, Hkv, lay, cap)
+    assert nbytes > 0
+    m = vs.VsMask()
+    fake = 0x10000000  # never dereferenced: vs_mask_init only computes addresses
+    assert L.vs_mask_init(ctypes.byref(m), fake, nbytes, Hq, Hkv, lay, cap) == 0
+    return m, lay, nbytes, fake
+
+
+def test_mask_init_layout(L):
+    m, lay, nbytes, base = _mask(L)
+    ptrs = [m.tile_ptr, m.tile_col, m.csc_ptr, m.csc_row, m.vloc, m.vloc_cnt, m.vcum, m.vert_end,
+            m.slash_bits, m.n_active, m.status]
+    assert all(base <= p < base + nbytes and (p - base) % 256 == 0 for p in ptrs)
+    assert ptrs == sorted(ptrs) and len(set(ptrs)) == len(ptrs)
+    assert (m.QB, m.KB, m.T, m.W) == (16, 16, 16, 1)
+    m2 = vs.VsMask()
+    assert L.vs_mask_init(ctypes.byref(m2), base, nbytes - 1, 4, 2, lay, 100) == vs.VS_ERR_WORKSPACE
+
+
+def test_layout_validation(L):
+    assert L.vs_mask_bytes(4, 2, vs.layout("striped", 3, 64 * 10), 10) == 0      # N % (64 P) != 0
+    assert L.vs_mask_bytes(4, 2, vs.layout("zigzag", 2, 64 * 6), 10) == 0        # N % (128 P) != 0
+    assert L.vs_mask_bytes(4, 2, vs.layout("zigzag", 2, 64 * 8), 10) > 0
+    m = vs.VsMask()
+    assert L.vs_mask_init(ctypes.byref(m), 0x10000000, 1 << 20, 3, 2, vs.layout("contig", 1, 1024), 10) \
+        == vs.VS_ERR_ARG                                                           # Hq % Hkv != 0
+
+
+def test_fwd_validation_before_device_work(L):
+    m, lay, _, _ = _mask(L)
+    m.rank = 0
+    m.src = 0
+    q = _fake_tensor(0x20000000, 4, 1024, 128)
+    k = _fake_tensor(0x30000000, 2, 1024, 128)
+    o, lse = ctypes.c_void_p(0x40000000), ctypes.c_void_p(0x50000000)
+    null = _fake_tensor(None, 4, 1024, 128)
+    assert L.vs_attn_fwd(null, k, k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_ARG
+    bad_n = _fake_tensor(0x20000000, 4, 1000, 128)
+    assert L.vs_attn_fwd(bad_n, k, k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_ARG
+    d96q, d96k = _fake_tensor(0x20000000, 4, 1024, 96), _fake_tensor(0x30000000, 2, 1024, 96)
+    assert L.vs_attn_fwd(d96q, d96k, d96k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_UNSUPPORTED
+    mis = _fake_tensor(0x20000002, 4, 1024, 128)
+    assert L.vs_attn_fwd(mis, k, k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_UNSUPPORTED
+    f32k = _fake_tensor(0x30000000, 2, 1024, 128, vs.VS_F32)
+    assert L.vs_attn_fwd(q, f32k, f32k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_ARG
+    assert L.vs_attn_fwd(q, k, k, ctypes.byref(m), -1.0, o, lse, 0, None) == vs.VS_ERR_ARG
+    assert L.vs_attn_fwd(q, k, k, ctypes.byref(m), 0.1, o, lse, 2, None) == vs.VS_ERR_ARG
+    assert L.vs_attn_fwd(q, k, k, ctypes.byref(m), 0.1, None, lse, 0, None) == vs.VS_ERR_ARG
+    m.rank = -1                                            # mask never built
+    assert L.vs_attn_fwd(q, k, k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_ARG
+
+
+def test_block_mask_and_index_validation(L):
+    m, lay, _, _ = _mask(L, kind="striped", P=4, N=1024)
+    p = ctypes.c_void_p(0x60000000)
+    assert L.vs_block_mask(p, p, 1024, p, p, 16, 4, 0, ctypes.byref(m), None) == vs.VS_ERR_ARG   # rank >= P
+    assert L.vs_block_mask(p, p, 1024, p, p, 16, 0, -1, ctypes.byref(m), None) == vs.VS_ERR_ARG
+    assert L.vs_block_mask(None, p, 1024, p, p, 16, 0, 0, ctypes.byref(m), None) == vs.VS_ERR_ARG
+    q = _fake_tensor(0x20000000, 16, 64, 128)
+    k = _fake_tensor(0x30000000, 2, 4096, 128)
+    lay = vs.layout("contig", 1, 4096)
+    ws = L.vs_index_workspace_size(16, 2, 4096, 128, 64)
+    assert ws > 0
+    args = [p] * 6
+    assert L.vs_index_build(q, k, lay, 0.1, 0.9, *args, p, ws - 1, None) == vs.VS_ERR_WORKSPACE
+    q65 = _fake_tensor(0x20000000, 16, 65, 128)
+    assert L.vs_index_build(q65, k, lay, 0.1, 0.9, *args, p, ws, None) == vs.VS_ERR_UNSUPPORTED
+    k3 = _fake_tensor(0x30000000, 3, 4096, 128)
+    assert L.vs_index_build(q, k3, lay, 0.1, 0.9, *args, p, ws, None) == vs.VS_ERR_ARG
+    kshort = _fake_tensor(0x30000000, 2, 2048, 128)
+    assert L.vs_index_build(q, kshort, lay, 0.1, 0.9, *args, p, ws, None) == vs.VS_ERR_ARG
+
+
+def test_bwd_and_merge_validation(L):
+    m, lay, _, _ = _mask(L)
+    m.rank = m.src = 0
+    q = _fake_tensor(0x20000000, 4, 1024, 128)
+    k = _fake_tensor(0x30000000, 2, 1024, 128)
+    p = ctypes.c_void_p(0x40000000)
+    dq_mis = ctypes.c_void_p(0x40000004)
+    assert L.vs_attn_bwd(q, k, k, q, p, p, ctypes.byref(m), 0.1, dq_mis, p, p, None) == vs.VS_ERR_UNSUPPORTED
+    assert L.vs_attn_bwd(q, k, k, q, None, p, ctypes.byref(m), 0.1, p, p, p, None) == vs.VS_ERR_ARG
+    assert L.vs_merge_lse(p, p, p, p, 4, 1024, 96, None) == vs.VS_ERR_UNSUPPORTED
+    assert L.vs_merge_lse(None, p, p, p, 4, 1024, 128, None) == vs.VS_ERR_ARG
+    assert L.vs_merge_lse(p, p, p, p, 4, 0, 128, None) == vs.VS_OK          # nothing to do

@@ -1,0 +1,203 @@
+"""GPU sparse forward / merge / backward vs the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oa
+from oracle import layout as ol
+from oracle import mask as om
+from synth import config_by_name, generate
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _index(rng, N, Hq, nv, ns, band=3):
+    T = N // 64
+    vert = [np.sort(rng.choice(N, nv, replace=False)) for _ in range(Hq)]
+    slash = [np.sort(np.unique(np.concatenate([np.arange(band), rng.choice(T, ns, replace=False)])))
+             for _ in range(Hq)]
+    return vert, slash
+
+
+def _fwd_case(cfg, vert, slash, kind="contig", P=1, accumulate_steps=False):
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    t = generate(cfg, tensors=("q", "k", "v"))
+    N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    lay = vs.layout(kind, P, N)
+    QB = N // 64 // P
+    lists = H.upload_lists(vert, slash, N)
+    cap = H.tile_cap_for(slash, Hq, QB)
+    worst = 0.0
+    for rank in range(P):
+        q = H.to_dev(H.shard(t["q"], kind, P, rank), cfg.dtype)
+        o_acc = torch.zeros(Hq, QB * 64, D, device="cuda")
+        l_acc = torch.full((Hq, QB * 64), -math.inf, device="cuda")
+        ref_o = np.zeros((Hq, QB * 64, D))
+        ref_l = np.full((Hq, QB * 64), -np.inf)
+        for step in range(P):
+            src = ol.ring_source(rank, step, P)
+            k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
+            v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+            m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+            if accumulate_steps:
+                vs.vs_attn_fwd(q, k, v, m, cfg.scale, o_acc, l_acc, accumulate=1)
+            else:
+                o = torch.empty(Hq, QB * 64, D, device="cuda")
+                lse = torch.empty(Hq, QB * 64, device="cuda")
+                vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse)
+                vs.vs_merge_lse(o_acc, l_acc, o, lse)
+            ref = H.oracle_step_forward(t["q"], t["k"], t["v"], vert, slash, kind, P, rank, step, cfg.scale)
+            for (h, I), (o_r, l_r) in ref.items():
+                sl = slice(64 * I, 64 * I + 64)
+                ref_o[h, sl], ref_l[h, sl] = oa.merge(ref_o[h, sl], ref_l[h, sl], o_r, l_r)
+        torch.cuda.synchronize()
+        go, gl = o_acc.cpu().numpy(), l_acc.cpu().numpy()
+        err = np.abs(go - ref_o).max()
+        fin = np.isfinite(ref_l)
+        assert (gl[~fin] == -np.inf).all() and (go[~fin] == 0).all()
+        lerr = np.abs(gl[fin] - ref_l[fin]).max() if fin.any() else 0.0
+        worst = max(worst, err, lerr)
+        assert err <= TOL[cfg.dtype] and lerr <= TOL[cfg.dtype], (rank, err, lerr)
+    return worst
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_fwd_random_index_contig(dtype, D):
+    rng = np.random.default_rng(1)
+    cfg = config_by_name("qwen32k", N=64 * 24, Hq=4, Hkv=2, D=D, dtype=dtype, n_out=5, c=2.0)
+    vert, slash = _index(rng, cfg.N, cfg.Hq, 150, 5)
+    slash[1] = slash[1][slash[1] != 0]        # a head without the diagonal block: causal verticals + empty rows
+    vert[2] = np.zeros(0, dtype=np.int64)     # a head without verticals
+    _fwd_case(cfg, vert, slash)
+
+
+@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2), ("contig", 2)])
+def test_fwd_ring_merge(kind, P):
+    rng = np.random.default_rng(2)
+    cfg = config_by_name("qwen32k", N=64 * 32, Hq=4, Hkv=1, n_out=4, c=2.0)
+    vert, slash = _index(rng, cfg.N, cfg.Hq, 100, 6)
+    _fwd_case(cfg, vert, slash, kind, P, accumulate_steps=False)
+    _fwd_case(cfg, vert, slash, kind, P, accumulate_steps=True)
+
+
+def test_fwd_full_budget_is_dense_causal_sdpa():
+    """All verticals and slashes selected -> dense causal attention (torch SDPA on the GPU, fp32)."""
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    cfg = config_by_name("qwen32k", N=64 * 20, Hq=2, Hkv=1, n_out=3, c=1.0)
+    t = generate(cfg, tensors=("q", "k", "v"))
+    N, Hq, D = cfg.N, cfg.Hq, cfg.D
+    vert = [np.arange(N)] * Hq
+    slash = [np.arange(N // 64)] * Hq
+    lay = vs.layout("contig", 1, N)
+    m = H.gpu_mask(H.upload_lists(vert, slash, N), Hq, 1, lay, 0, 0, H.tile_cap_for(slash, Hq, N // 64))
+    q, k, v = (H.to_dev(t[x], "bf16") for x in ("q", "k", "v"))
+    o = torch.empty(Hq, N, D, device="cuda")
+    lse = torch.empty(Hq, N, device="cuda")
+    vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse)
+    kk = k.float().expand(Hq, N, D).contiguous()
+    vv = v.float().expand(Hq, N, D).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(q.float(), kk, vv, is_causal=True)
+    torch.cuda.synchronize()
+    assert (o - ref).abs().max().item() < 2e-2
+
+
+def _bwd_case(cfg, vert, slash, kind="contig", P=1):
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    t = generate(cfg)
+    N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    lay = vs.layout(kind, P, N)
+    QB = N // 64 // P
+    lists = H.upload_lists(vert, slash, N)
+    cap = H.tile_cap_for(slash, Hq, QB)
+    # oracle: full gradients over the global active set
+    ref_dq = np.zeros((Hq, N, D))
+    ref_dk = np.zeros((Hkv, N, D))
+    ref_dv = np.zeros((Hkv, N, D))
+    pos = np.arange(N)
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        M, _, _ = om.active(pos, pos, vert[h], slash[h])
+        dq, dk, dv = oa.backward_rows(t["q"][h], t["k"][g], t["v"][g], M, cfg.scale, t["do"][h])
+        ref_dq[h] += dq
+        ref_dk[g] += dk
+        ref_dv[g] += dv
+    dk_all = {r: torch.zeros(Hkv, QB * 64, D, device="cuda") for r in range(P)}
+    dv_all = {r: torch.zeros(Hkv, QB * 64, D, device="cuda") for r in range(P)}
+    errs = []
+    for rank in range(P):
+        q = H.to_dev(H.shard(t["q"], kind, P, rank), cfg.dtype)
+        do = H.to_dev(H.shard(t["do"], kind, P, rank), cfg.dtype)
+        o = torch.zeros(Hq, QB * 64, D, device="cuda")
+        lse = torch.full((Hq, QB * 64), -math.inf, device="cuda")
+        for step in range(P):
+            src = ol.ring_source(rank, step, P)
+            k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
+            v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+            m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+            vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse, accumulate=1)
+        delta = torch.empty(Hq, QB * 64, device="cuda")
+        vs.vs_attn_bwd_prep(o, do, delta)
+        dq = torch.zeros(Hq, QB * 64, D, device="cuda")
+        for step in range(P):
+            src = ol.ring_source(rank, step, P)
+            k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
+            v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+            m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+            vs.vs_attn_bwd(q, k, v, do, lse, delta, m, cfg.scale, dq, dk_all[src], dv_all[src])
+        torch.cuda.synchronize()
+        rows = ol.shard_positions(kind, N, P, rank)
+        errs.append(np.abs(dq.cpu().numpy() - ref_dq[:, rows]).max())
+    for r in range(P):
+        cols = ol.shard_positions(kind, N, P, r)
+        errs.append(np.abs(dk_all[r].cpu().numpy() - ref_dk[:, cols]).max())
+        errs.append(np.abs(dv_all[r].cpu().numpy() - ref_dv[:, cols]).max())
+    assert max(errs) <= TOL[cfg.dtype], errs
+    return errs
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_bwd_random_index(dtype, D):
+    rng = np.random.default_rng(3)
+    cfg = config_by_name("qwen32k", N=64 * 16, Hq=4, Hkv=2, D=D, dtype=dtype, n_out=4, c=2.0)
+    vert, slash = _index(rng, cfg.N, cfg.Hq, 90, 4)
+    slash[3] = slash[3][slash[3] != 0]
+    _bwd_case(cfg, vert, slash)
+
+
+@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2)])
+def test_bwd_ring(kind, P):
+    rng = np.random.default_rng(4)
+    cfg = config_by_name("qwen32k", N=64 * 16, Hq=2, Hkv=1, n_out=4, c=2.0)
+    vert, slash = _index(rng, cfg.N, cfg.Hq, 60, 4)
+    _bwd_case(cfg, vert, slash, kind, P)
+
+
+def test_merge_kernel_matches_formula():
+    import dynamic_sparse_attention_index_amd as vs
+    rng = np.random.default_rng(0)
+    Hq, Nq, D = 3, 256, 128
+    oa_ = rng.standard_normal((Hq, Nq, D)).astype(np.float32)
+    ob_ = rng.standard_normal((Hq, Nq, D)).astype(np.float32)
+    la = rng.standard_normal((Hq, Nq)).astype(np.float32) * 3
+    lb = rng.standard_normal((Hq, Nq)).astype(np.float32) * 3
+    la[0, :10] = -np.inf
+    lb[0, 5:15] = -np.inf
+    oa_[0, :10] = 0
+    ob_[0, 5:15] = 0
+    ref_o, ref_l = oa.merge(oa_.astype(np.float64), la.astype(np.float64), ob_.astype(np.float64),
+                            lb.astype(np.float64))
+    to = torch.tensor(oa_, device="cuda")
+    tl = torch.tensor(la, device="cuda")
+    vs.vs_merge_lse(to, tl, torch.tensor(ob_, device="cuda"), torch.tensor(lb, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.abs(to.cpu().numpy() - ref_o).max() < 1e-5
+    fin = np.isfinite(ref_l)
+    assert np.abs(tl.cpu().numpy()[fin] - ref_l[fin]).max() < 1e-5
+    assert (tl.cpu().numpy()[~fin] == -np.inf).all()

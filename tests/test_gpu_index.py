@@ -1,0 +1,65 @@
+"""GPU sparse-index build vs the fp64 oracle."""
+import numpy as np
+import pytest
+
+from oracle import index as oi
+from synth import config_by_name, generate
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_index(cfg, kind="contig", P=1, last_q=64):
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    t = generate(cfg, tensors=("q", "k"), rows=None)
+    N = cfg.N
+    q_last = t["q"][:, N - last_q:]
+    k_store = H.storage_order(t["k"], kind, P)
+    lay = vs.layout(kind, P, N)
+    out = H.gpu_index(H.to_dev(q_last, cfg.dtype), H.to_dev(k_store, cfg.dtype), lay, cfg.scale, cfg.top_p)
+    ref = oi.build_index(q_last, t["k"], cfg.scale, N, cfg.top_p)
+    gv, gs = out["v"].cpu().numpy(), out["s"].cpu().numpy()
+    for g, o in ((gv, ref["v"]), (gs, ref["s"])):
+        o64 = o.astype(np.float64)
+        tol = 1e-4 * np.abs(o64) + 1e-7 * o64.max(axis=1, keepdims=True)
+        assert (np.abs(g - o64) <= tol).all(), np.abs(g - o64).max()
+    vert, slash = H.lists_from_gpu(out)
+    for h in range(cfg.Hq):
+        # bit-exact given identical scores: the oracle's rule on the GPU's own scores
+        assert np.array_equal(vert[h], oi.select_top_p(gv[h], cfg.top_p)), h
+        assert np.array_equal(slash[h], oi.select_top_p(gs[h], cfg.top_p)), h
+        # against the oracle's scores: differences only within 1e-5 of the cutoff score
+        for got, exp, x in ((vert[h], ref["vert"][h], ref["v"][h]), (slash[h], ref["slash"][h], ref["s"][h])):
+            diff = np.setxor1d(got, exp)
+            if len(diff) and len(exp):
+                cut = x[exp].min()
+                assert (np.abs(x[diff].astype(np.float64) - cut) <= 1e-5).all(), (h, diff)
+    return out, ref
+
+
+def test_index_tiny_fp32():
+    _check_index(config_by_name("tiny"))
+
+
+@pytest.mark.parametrize("last_q", [64, 40])
+def test_index_gqa_bf16(last_q):
+    _check_index(config_by_name("qwen32k", N=8192, c=5.0), last_q=last_q)
+
+
+@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2)])
+def test_index_layout_storage_order(kind, P):
+    _check_index(config_by_name("qwen32k", N=8192, Hq=8, Hkv=2, c=5.0), kind, P)
+
+
+def test_index_llama_group4_and_budget_edges():
+    cfg = config_by_name("llama256k", N=4096, Hq=8, Hkv=2, c=3.0, yarn_scale=32.0)
+    _check_index(cfg)
+    out, _ = _check_index(config_by_name("llama256k", N=4096, Hq=8, Hkv=2, top_p=1.0))
+    assert (out["vcnt"].cpu().numpy() == 4096).all() and (out["scnt"].cpu().numpy() == 64).all()
+    out, _ = _check_index(config_by_name("llama256k", N=4096, Hq=8, Hkv=2, top_p=0.0))
+    assert (out["vcnt"].cpu().numpy() == 0).all() and (out["scnt"].cpu().numpy() == 0).all()
+
+
+def test_index_qwen32k_full_size():
+    from synth.inputs import CONFIGS
+    _check_index(CONFIGS["qwen32k"])
