@@ -270,6 +270,262 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, head dim 128: each wave owns 32 query rows and one half (32 keys) of
+// every staged 64-key tile, so a K/V fragment read from LDS feeds two MFMAs and
+// a wave reads only its half of the tile. The two key halves keep separate
+// online-softmax states that are merged through LDS at the end (the same
+// log-sum-exp merge as across ring steps). Tiles are stored unpadded with an
+// XOR swizzle of 16-byte chunks: K rows so that the 16 rows read by one lane
+// group hit distinct chunks, V rows so that the transpose reads of two lane
+// groups cover all 64 banks.
+namespace fwd2 {
+
+constexpr int D = 128;
+constexpr int CH = D / 8;              // 16-byte chunks per row
+constexpr int TILE = BLK * D;          // elements per staged tile
+constexpr int CPT = BLK * CH / FWD_THREADS;  // chunks per thread per tile (4)
+
+__device__ __forceinline__ int swz_k(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
+__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 1) | (((r >> 3) & 1) << 3); }
+// element offset of logical (row, chunk) in a staged tile
+__device__ __forceinline__ int k_off(int r, int lc) { return r * D + ((lc ^ swz_k(r)) << 3); }
+__device__ __forceinline__ int v_off(int r, int lc) { return r * D + ((lc ^ swz_v(r)) << 3); }
+
+}  // namespace fwd2
+
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
+  using namespace fwd2;
+  // K tile, V tile; after the loop the same 32 KiB carry the key-half exchange
+  __shared__ __attribute__((aligned(16))) bf16 KVs[2 * TILE];
+  __shared__ float xs[2 * 2 * 64 * 2];
+  __shared__ int thr_sh[BLK];
+  bf16* Ks = KVs;
+  bf16* Vs = KVs + TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int rh = wave & 1, kh = wave >> 1;   // row half, key half
+  const int nitems = a.Hq * a.QB;
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int I = a.QB - 1 - item / a.Hq;
+  const int h = item % a.Hq;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int64_t u = (int64_t)h * a.QB + I;
+  const int64_t row_base = (int64_t)I * BLK + 32 * rh;   // this wave's first query row
+
+  const bf16* qb = (const bf16*)a.q + h * a.qsh;
+  const bf16* kbase = (const bf16*)a.k + kvh * a.ksh;
+  const bf16* vbase = (const bf16*)a.v + kvh * a.vsh;
+
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[rs][ks] = *(const bf16x8*)(qb + (row_base + 16 * rs + n16) * a.qsn + 32 * ks + 8 * g4);
+
+  const int t0 = a.tile_ptr[u];
+  const int nt = a.tile_ptr[u + 1] - t0;
+  const int ve = a.vert_end[u];
+  const int total = nt + (ve + BLK - 1) / BLK;
+  const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I);
+  const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
+  const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
+
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[rs][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  i32x4 kreg[CPT], vreg[CPT];
+  int mode_next = 0, thr_next = 0;
+  auto fetch = [&](int it) {
+    int src_rows[CPT];
+    if (it < nt) {
+      const int e = a.tile_col[t0 + it];
+      const int J = e & VS_TILE_MASK;
+      mode_next = (e & VS_TILE_DIAG) ? 1 : 0;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) src_rows[c] = J * BLK + (tid + c * FWD_THREADS) / CH;
+      thr_next = tid < BLK ? tid : 0;
+    } else {
+      const int base = (it - nt) * BLK;
+      mode_next = 1;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int idx = base + (tid + c * FWD_THREADS) / CH;
+        src_rows[c] = idx < ve ? vl[idx] : vl[base];
+      }
+      if (tid < BLK) {
+        const int idx = base + tid;
+        int thr = BLK;
+        if (idx < ve) {
+          const int m = vl[idx];
+          const int64_t j = G - global_block(a.kind, a.P, a.KB, a.src, m / BLK);
+          if (!((sb[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
+        }
+        thr_next = thr;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int col = ((tid + c * FWD_THREADS) % CH) * 8;
+      kreg[c] = *(const i32x4*)(kbase + (int64_t)src_rows[c] * a.ksn + col);
+      vreg[c] = *(const i32x4*)(vbase + (int64_t)src_rows[c] * a.vsn + col);
+    }
+  };
+
+  const float sl2 = a.scale_log2;
+  if (total > 0) fetch(0);
+  for (int it = 0; it < total; ++it) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * FWD_THREADS;
+      const int r = ch / CH, lc = ch % CH;
+      *(i32x4*)(Ks + k_off(r, lc)) = kreg[c];
+      *(i32x4*)(Vs + v_off(r, lc)) = vreg[c];
+    }
+    if (tid < BLK) thr_sh[tid] = thr_next;
+    const int mode = mode_next;
+    __syncthreads();
+    if (it + 1 < total) fetch(it + 1);
+
+    // S^T for 32 keys (this wave's half) x 32 rows: s[rs][t] lane (g, n):
+    // S[row 16 rs + n][key 32 kh + 8 g + 4 t + i]
+    f32x4 s[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kr = 32 * kh + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) s[rs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(Ks + k_off(kr, 4 * ks + g4));
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) s[rs][t] = mfma_bf16(kf, qf[rs][ks], s[rs][t]);
+      }
+    }
+    bf16x8 pf[2];
+    bool rescale = false;
+    float alpha[2];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      const int rowoff = 32 * rh + 16 * rs + n16;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[rs][t][i];
+          if (mode && thr_sh[32 * kh + 8 * g4 + 4 * t + i] > rowoff) x = -INFINITY;
+          s[rs][t][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[rs], mx * sl2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha[rs] = __builtin_amdgcn_exp2f(m_run[rs] - m_use);
+      rescale |= m_new != m_run[rs];
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -m_use));
+          psum += p;
+          pf[rs][4 * t + i] = (bf16)p;
+        }
+      l_run[rs] = l_run[rs] * alpha[rs] + psum;
+      m_run[rs] = m_new;
+    }
+    if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rs][dt][i] *= alpha[rs];
+    }
+    // O^T += V^T P^T over this wave's 32 keys (one 32-deep contraction)
+    const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int lc = 2 * dt + ((n16 & 3) >> 1);
+      const bf16x8 va = lds_read_tr16_x2(Vs + v_off(vr, lc) + 4 * (n16 & 1), D);
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) acc[rs][dt] = mfma_bf16(va, pf[rs], acc[rs][dt]);
+    }
+    __syncthreads();
+  }
+
+  // ---- merge the two key halves (kh = 1 hands its state to kh = 0 via LDS);
+  // the loop ended on a barrier, so the tile buffers are free.
+  float* xo = (float*)KVs;                       // [2 rh][2 rs][8 dt][64 lanes] f32x4 = 32 KiB
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs) {
+    float l = l_run[rs] + wave_shfl_xor(l_run[rs], 16);
+    l_run[rs] = l + wave_shfl_xor(l, 32);
+  }
+  if (kh == 1) {
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(xo + (((rh * 2 + rs) * 8 + dt) * 64 + lane) * 4) = acc[rs][dt];
+      xs[((rh * 2 + rs) * 64 + lane) * 2 + 0] = m_run[rs];
+      xs[((rh * 2 + rs) * 64 + lane) * 2 + 1] = l_run[rs];
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs) {
+    const float m1 = xs[((rh * 2 + rs) * 64 + lane) * 2 + 0];
+    const float l1 = xs[((rh * 2 + rs) * 64 + lane) * 2 + 1];
+    const float m0 = m_run[rs];
+    const float mm = fmaxf(m0, m1);
+    const float mb = (mm == -INFINITY) ? 0.f : mm;
+    const float w0 = __builtin_amdgcn_exp2f(m0 - mb), w1 = __builtin_amdgcn_exp2f(m1 - mb);
+    const float l_tot = l_run[rs] * w0 + l1 * w1;
+    const bool nonempty = l_tot > 0.f;
+    const float inv = nonempty ? 1.f / l_tot : 0.f;
+    const float lse_new = nonempty ? (mm + log2f(l_tot)) * LN2 : -INFINITY;
+    const int64_t grow = row_base + 16 * rs + n16;
+    float* orow = a.o + ((int64_t)h * a.QB * BLK + grow) * D;
+    float* lrow = a.lse + (int64_t)h * a.QB * BLK + grow;
+    float ca = 0.f, cb = inv;
+    if (a.accumulate) {
+      const float lse_old = *lrow;
+      const float mxl = fmaxf(lse_old, lse_new);
+      const float base = (mxl == -INFINITY) ? 0.f : mxl;
+      const float wa = expf(lse_old - base), wb = expf(lse_new - base);
+      const float tot = wa + wb;
+      ca = tot > 0.f ? wa / tot : 0.f;
+      cb = tot > 0.f ? wb / tot * inv : 0.f;
+      if (g4 == 0) *lrow = tot > 0.f ? base + logf(tot) : -INFINITY;
+    } else if (g4 == 0) {
+      *lrow = lse_new;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o1 = *(const f32x4*)(xo + (((rh * 2 + rs) * 8 + dt) * 64 + lane) * 4);
+      f32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (acc[rs][dt][i] * w0 + o1[i] * w1) * cb;
+      if (a.accumulate) {
+        const f32x4 old = *(const f32x4*)(orow + 16 * dt + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] += ca * old[i];
+      }
+      *(f32x4*)(orow + 16 * dt + 4 * g4) = r;
+    }
+  }
+}
+
 int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* m, float scale,
                     float* o, float* lse, int accumulate, hipStream_t stream) {
   FwdArgs a;
@@ -281,7 +537,7 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
   const dim3 grid((unsigned)(m->Hq * m->QB)), block(FWD_THREADS);
-  if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 128>), grid, block, 0, stream, a);
+  if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);
   else return VS_ERR_UNSUPPORTED;
