@@ -23,7 +23,8 @@
 
 namespace vs {
 
-constexpr int FWD_THREADS = 256;  // 4 waves x 16 query rows
+constexpr int FWD_THREADS = 256;  // 4 waves
+constexpr int FWD_MAX_W = 512;    // slash-bitmap words held in LDS (sequences up to 2^20 tokens)
 
 struct FwdArgs {
   const void* q; const void* k; const void* v;
@@ -271,37 +272,28 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16, head dim 128: each wave owns 32 query rows and one half (32 keys) of
-// every staged 64-key tile, so a K/V fragment read from LDS feeds two MFMAs and
-// a wave reads only its half of the tile. The two key halves keep separate
-// online-softmax states that are merged through LDS at the end (the same
-// log-sum-exp merge as across ring steps). Tiles are stored unpadded with an
-// XOR swizzle of 16-byte chunks: K rows so that the 16 rows read by one lane
-// group hit distinct chunks, V rows so that the transpose reads of two lane
-// groups cover all 64 banks.
-namespace fwd2 {
-
-constexpr int D = 128;
-constexpr int CH = D / 8;              // 16-byte chunks per row
-constexpr int TILE = BLK * D;          // elements per staged tile
-constexpr int CPT = BLK * CH / FWD_THREADS;  // chunks per thread per tile (4)
-
-__device__ __forceinline__ int swz_k(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
-__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 1) | (((r >> 3) & 1) << 3); }
-// element offset of logical (row, chunk) in a staged tile
-__device__ __forceinline__ int k_off(int r, int lc) { return r * D + ((lc ^ swz_k(r)) << 3); }
-__device__ __forceinline__ int v_off(int r, int lc) { return r * D + ((lc ^ swz_v(r)) << 3); }
-
-}  // namespace fwd2
-
+// bf16, head dim 128 (the production path). Each wave owns 32 query rows and
+// one half (32 keys) of every 64-key tile, so a K/V fragment read from LDS
+// feeds two MFMAs and a wave reads only its half of the tile; the two key
+// halves keep separate online-softmax states, merged through LDS at the end
+// (the same log-sum-exp merge as across ring steps). Tiles stream into two
+// LDS stages with asynchronous global->LDS copies issued one tile ahead, so
+// each tile costs one barrier. Row indices of gathered vertical chunks and
+// list entries are loaded one more tile ahead.
 __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
-  using namespace fwd2;
-  // K tile, V tile; after the loop the same 32 KiB carry the key-half exchange
-  __shared__ __attribute__((aligned(16))) bf16 KVs[2 * TILE];
+  constexpr int D = TD;
+  // Two LDS stages of (K tile, V tile) as distinct arrays, and the loop is
+  // unrolled by two, so the compiler can tell the stage being read from the
+  // stage being filled and lets the copy run under the compute. After the
+  // loop the K and V arrays of stage 0 carry the key-half exchange.
+  __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 V1[TILE_ELEMS];
   __shared__ float xs[2 * 2 * 64 * 2];
-  __shared__ int thr_sh[BLK];
-  bf16* Ks = KVs;
-  bf16* Vs = KVs + TILE;
+  __shared__ int thr0_sh[BLK], thr1_sh[BLK];
+  __shared__ int desc0_sh[BLK], desc1_sh[BLK];
+  __shared__ uint32_t sbits[FWD_MAX_W];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
@@ -319,13 +311,6 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
   const bf16* kbase = (const bf16*)a.k + kvh * a.ksh;
   const bf16* vbase = (const bf16*)a.v + kvh * a.vsh;
 
-  bf16x8 qf[2][4];
-#pragma unroll
-  for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[rs][ks] = *(const bf16x8*)(qb + (row_base + 16 * rs + n16) * a.qsn + 32 * ks + 8 * g4);
-
   const int t0 = a.tile_ptr[u];
   const int nt = a.tile_ptr[u + 1] - t0;
   const int ve = a.vert_end[u];
@@ -334,66 +319,76 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
   const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
   const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
 
+  // Tile descriptors travel through LDS as well: wave 0 copies the list entry
+  // (slash tile) or the 64 column positions (vertical chunk) of tile it+2
+  // while tile it is computed; after the next barrier every wave decodes them
+  // into copy rows, the tile mode (0 = full, 1 = thresholds apply) and the
+  // key thresholds (query rows below a key's threshold are inactive). No
+  // register ever waits on an outstanding copy.
+  for (int w = tid; w < a.W; w += FWD_THREADS) sbits[w] = sb[w];
+  auto desc_copy = [&](int it, int* desc) {
+    if (wave != 0) return;
+    const int32_t* src = (it < nt) ? a.tile_col + t0 + it : vl + min((it - nt) * BLK + lane, ve - 1);
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)(
+                                         (__attribute__((address_space(3))) int*)(desc)),
+                                     4, 0, 0);
+  };
+  auto desc_decode = [&](int it, const int* desc, int* rows, int& mode, int& thr) {
+    if (it < nt) {
+      const int e = desc[0];
+      const int J = e & VS_TILE_MASK;
+      mode = (e & VS_TILE_DIAG) ? 1 : 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rows[c] = J * BLK + dma_local_row(wave, c, lane);
+      thr = tid;
+    } else {
+      const int base = (it - nt) * BLK;
+      mode = 1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rows[c] = desc[dma_local_row(wave, c, lane)];
+      thr = BLK;
+      if (tid < BLK && base + tid < ve) {
+        const int m = desc[tid];
+        const int64_t j = G - global_block(a.kind, a.P, a.KB, a.src, m / BLK);
+        if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
+      }
+    }
+  };
+
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[rs][ks] = *(const bf16x8*)(qb + (row_base + 16 * rs + n16) * a.qsn + 32 * ks + 8 * g4);
+
   f32x4 acc[2][8];
 #pragma unroll
   for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[rs][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-  i32x4 kreg[CPT], vreg[CPT];
-  int mode_next = 0, thr_next = 0;
-  auto fetch = [&](int it) {
-    int src_rows[CPT];
-    if (it < nt) {
-      const int e = a.tile_col[t0 + it];
-      const int J = e & VS_TILE_MASK;
-      mode_next = (e & VS_TILE_DIAG) ? 1 : 0;
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) src_rows[c] = J * BLK + (tid + c * FWD_THREADS) / CH;
-      thr_next = tid < BLK ? tid : 0;
-    } else {
-      const int base = (it - nt) * BLK;
-      mode_next = 1;
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int idx = base + (tid + c * FWD_THREADS) / CH;
-        src_rows[c] = idx < ve ? vl[idx] : vl[base];
-      }
-      if (tid < BLK) {
-        const int idx = base + tid;
-        int thr = BLK;
-        if (idx < ve) {
-          const int m = vl[idx];
-          const int64_t j = G - global_block(a.kind, a.P, a.KB, a.src, m / BLK);
-          if (!((sb[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
-        }
-        thr_next = thr;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int col = ((tid + c * FWD_THREADS) % CH) * 8;
-      kreg[c] = *(const i32x4*)(kbase + (int64_t)src_rows[c] * a.ksn + col);
-      vreg[c] = *(const i32x4*)(vbase + (int64_t)src_rows[c] * a.vsn + col);
-    }
-  };
-
   const float sl2 = a.scale_log2;
-  if (total > 0) fetch(0);
-  for (int it = 0; it < total; ++it) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * FWD_THREADS;
-      const int r = ch / CH, lc = ch % CH;
-      *(i32x4*)(Ks + k_off(r, lc)) = kreg[c];
-      *(i32x4*)(Vs + v_off(r, lc)) = vreg[c];
-    }
-    if (tid < BLK) thr_sh[tid] = thr_next;
-    const int mode = mode_next;
-    __syncthreads();
-    if (it + 1 < total) fetch(it + 1);
+  int mode_c = 0;
 
+  // One tile: wait for its copy, start the next copy, compute. Ks/Vs/thr/desc
+  // of the stage being read, Kn/Vn/thn/dn of the other stage.
+  auto step = [&](int it, const bf16* Ks, const bf16* Vs, const int* thc, bf16* Kn, bf16* Vn, int* thn,
+                  int* dn_next, const int* dn_cur) {
+    wait_all_mem();
+    __syncthreads();  // tile `it` and descriptor it+1 have landed; tile it-1 is done
+    const int mode = mode_c;
+    if (it + 1 < total) {
+      int rows_n[4], thr_n, mode_n;
+      desc_decode(it + 1, dn_cur, rows_n, mode_n, thr_n);
+      dma_tile(Kn, kbase, a.ksn, rows_n, wave, lane);
+      dma_tile(Vn, vbase, a.vsn, rows_n, wave, lane);
+      if (tid < BLK) thn[tid] = thr_n;
+      mode_c = mode_n;
+      // the other descriptor slot held descriptor `it`, decoded before the barrier
+      if (it + 2 < total) desc_copy(it + 2, dn_next);
+    }
     // S^T for 32 keys (this wave's half) x 32 rows: s[rs][t] lane (g, n):
     // S[row 16 rs + n][key 32 kh + 8 g + 4 t + i]
     f32x4 s[2][2];
@@ -404,29 +399,31 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
       for (int rs = 0; rs < 2; ++rs) s[rs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(Ks + k_off(kr, 4 * ks + g4));
+        const bf16x8 kf = *(const bf16x8*)(Ks + tile_off(kr, 4 * ks + g4));
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) s[rs][t] = mfma_bf16(kf, qf[rs][ks], s[rs][t]);
       }
+    }
+    if (mode) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int th = thc[32 * kh + 8 * g4 + 4 * t + i];
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs)
+            if (th > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
+        }
     }
     bf16x8 pf[2];
     bool rescale = false;
     float alpha[2];
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
-      const int rowoff = 32 * rh + 16 * rs + n16;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[rs][t][i];
-          if (mode && thr_sh[32 * kh + 8 * g4 + 4 * t + i] > rowoff) x = -INFINITY;
-          s[rs][t][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+      float mx = fmaxf(fmaxf(fmaxf(s[rs][0][0], s[rs][0][1]), fmaxf(s[rs][0][2], s[rs][0][3])),
+                       fmaxf(fmaxf(s[rs][1][0], s[rs][1][1]), fmaxf(s[rs][1][2], s[rs][1][3])));
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
       const float m_new = fmaxf(m_run[rs], mx * sl2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       alpha[rs] = __builtin_amdgcn_exp2f(m_run[rs] - m_use);
@@ -456,26 +453,43 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int lc = 2 * dt + ((n16 & 3) >> 1);
-      const bf16x8 va = lds_read_tr16_x2(Vs + v_off(vr, lc) + 4 * (n16 & 1), D);
+      const bf16x8 va = lds_read_tr16_x2(Vs + tile_off(vr, lc) + 4 * (n16 & 1), D);
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) acc[rs][dt] = mfma_bf16(va, pf[rs], acc[rs][dt]);
     }
+  };
+
+  if (total > 0) {
+    desc_copy(0, desc0_sh);
+    if (total > 1) desc_copy(1, desc1_sh);
+    wait_all_mem();
     __syncthreads();
+    int rows0[4], thr0;
+    desc_decode(0, desc0_sh, rows0, mode_c, thr0);
+    dma_tile(K0, kbase, a.ksn, rows0, wave, lane);
+    dma_tile(V0, vbase, a.vsn, rows0, wave, lane);
+    if (tid < BLK) thr0_sh[tid] = thr0;
+  }
+  for (int it = 0; it < total; it += 2) {
+    // even tiles live in stage 0 (descriptor of it+1 in slot 1), odd in stage 1
+    step(it, K0, V0, thr0_sh, K1, V1, thr1_sh, desc0_sh, desc1_sh);
+    if (it + 1 < total) step(it + 1, K1, V1, thr1_sh, K0, V0, thr0_sh, desc1_sh, desc0_sh);
   }
 
-  // ---- merge the two key halves (kh = 1 hands its state to kh = 0 via LDS);
-  // the loop ended on a barrier, so the tile buffers are free.
-  float* xo = (float*)KVs;                       // [2 rh][2 rs][8 dt][64 lanes] f32x4 = 32 KiB
+  // ---- merge the two key halves (kh = 1 hands its state to kh = 0 via LDS)
 #pragma unroll
   for (int rs = 0; rs < 2; ++rs) {
-    float l = l_run[rs] + wave_shfl_xor(l_run[rs], 16);
-    l_run[rs] = l + wave_shfl_xor(l, 32);
+    const float l = l_run[rs] + xor16(l_run[rs]);
+    l_run[rs] = l + xor32(l);
   }
+  __syncthreads();  // every wave is past its last read of the stages
+  // [2 rh][2 rs][8 dt][64 lanes] f32x4: row half 0 in K0, row half 1 in V0 (16 KiB each)
+  float* xo = (float*)(rh == 0 ? K0 : V0);
   if (kh == 1) {
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(xo + (((rh * 2 + rs) * 8 + dt) * 64 + lane) * 4) = acc[rs][dt];
+      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(xo + ((rs * 8 + dt) * 64 + lane) * 4) = acc[rs][dt];
       xs[((rh * 2 + rs) * 64 + lane) * 2 + 0] = m_run[rs];
       xs[((rh * 2 + rs) * 64 + lane) * 2 + 1] = l_run[rs];
     }
@@ -512,7 +526,7 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const f32x4 o1 = *(const f32x4*)(xo + (((rh * 2 + rs) * 8 + dt) * 64 + lane) * 4);
+      const f32x4 o1 = *(const f32x4*)(xo + ((rs * 8 + dt) * 64 + lane) * 4);
       f32x4 r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = (acc[rs][dt][i] * w0 + o1[i] * w1) * cb;
@@ -537,7 +551,10 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
   const dim3 grid((unsigned)(m->Hq * m->QB)), block(FWD_THREADS);
-  if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
+  if (dtype == VS_BF16 && D == 128) {
+    if (m->W > FWD_MAX_W) return VS_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
+  }
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);
   else return VS_ERR_UNSUPPORTED;

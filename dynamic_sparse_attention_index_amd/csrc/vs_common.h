@@ -96,3 +96,53 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int64_t 
 }
 
 }  // namespace vs
+
+namespace vs {
+
+// --- staged 64 x 128 bf16 tiles -----------------------------------------------
+// A tile holds 64 rows of 128 bf16 (256 B = 16 chunks of 16 B), unpadded, with
+// the 16-byte chunks of row r permuted by an XOR swizzle. The swizzle makes the
+// two access patterns of the attention kernels conflict-free on the 64 LDS
+// banks: (a) 16 lanes reading one chunk from the 16 rows {8q + 4t + i} (MFMA
+// operand rows), and (b) the transpose reads, where 16 lanes read two chunks
+// from 4 consecutive rows and two lane groups read rows 8 apart.
+constexpr int TD = 128;                 // head dim of the staged tiles
+constexpr int TCH = TD / 8;             // chunks per row
+constexpr int TILE_ELEMS = BLK * TD;    // 8192 bf16 = 16 KiB
+__device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 1) | (((r >> 3) & 1) << 3) | ((r >> 4) & 1); }
+__device__ __forceinline__ int tile_off(int r, int lc) { return r * TD + ((lc ^ tile_swz(r)) << 3); }
+
+// Asynchronous global -> LDS copy of one tile by a 256-thread workgroup
+// (gfx950 global_load_lds_dwordx4: lane L of a wave writes 16 B at the
+// wave-uniform LDS address + 16 L). Wave w copies the 1 KiB segments
+// s = w + 4 c (rows 4 s .. 4 s + 3); lane L carries local row 4 s + L / 16,
+// physical chunk L % 16. src_row[c] is the global row for that local row.
+__device__ __forceinline__ int dma_local_row(int wave, int c, int lane) { return 4 * (wave + 4 * c) + (lane >> 4); }
+__device__ __forceinline__ void dma_tile(bf16* lds_tile, const bf16* gbase, int64_t row_stride, const int* src_row,
+                                         int wave, int lane) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int s = wave + 4 * c;
+    const int r = 4 * s + (lane >> 4);
+    const int lc = (lane & 15) ^ tile_swz(r);
+    const bf16* g = gbase + (int64_t)src_row[c] * row_stride + lc * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g,
+                                     (__attribute__((address_space(3))) void*)(
+                                         (__attribute__((address_space(3))) bf16*)(lds_tile + s * 512)),
+                                     16, 0, 0);
+  }
+}
+// Wait for this wave's outstanding memory operations (incl. LDS copies).
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Cross-lane exchange between the four 16-lane groups of a wave.
+__device__ __forceinline__ float xor16(float v) { return __shfl_xor(v, 16, 64); }
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// Round 8 fp32 weights to a bf16 pair (hi = bf16(w), lo = bf16(w - hi)).
+__device__ __forceinline__ void split_bf16(float w, bf16& hi, bf16& lo) {
+  hi = (bf16)w;
+  lo = (bf16)(w - (float)hi);
+}
+
+}  // namespace vs
