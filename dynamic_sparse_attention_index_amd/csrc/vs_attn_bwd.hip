@@ -414,6 +414,515 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16, head dim 128 (the production path). Same tiling as the forward: 64-row
+// query blocks and 64-key tiles staged in swizzled LDS tiles by asynchronous
+// copies, two stages, one barrier per tile; each wave covers 32 rows x 32 keys.
+
+// Split 8 fp32 weights into a bf16 hi/lo pair of MFMA operands.
+__device__ __forceinline__ void split8(const f32x4& w0, const f32x4& w1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16 h0, l0, h1, l1;
+    split_bf16(w0[i], h0, l0);
+    split_bf16(w1[i], h1, l1);
+    hi[i] = h0; lo[i] = l0; hi[4 + i] = h1; lo[4 + i] = l1;
+  }
+}
+
+// dQ, query-major. Wave (rh, kh) = rows 32 rh.. of the block, keys 32 kh.. of
+// every tile; the two key halves' partial dQ are added through LDS at the end.
+__global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a) {
+  constexpr int D = TD;
+  __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 V1[TILE_ELEMS];
+  __shared__ int thr0_sh[BLK], thr1_sh[BLK], desc0_sh[BLK], desc1_sh[BLK];
+  __shared__ uint32_t sbits[MAX_LDS_W];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int rh = wave & 1, kh = wave >> 1;
+  const int nitems = a.Hq * a.QB;
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int I = a.QB - 1 - item / a.Hq;
+  const int h = item % a.Hq;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int64_t u = (int64_t)h * a.QB + I;
+  const int64_t row_base = (int64_t)I * BLK + 32 * rh;
+
+  BlockTiles bt;
+  bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
+  bt.t0 = a.tile_ptr[u]; bt.nt = a.tile_ptr[u + 1] - bt.t0; bt.ve = a.vert_end[u];
+  bt.total = bt.nt + (bt.ve + BLK - 1) / BLK;
+  bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
+  bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+  const int total = bt.total;
+  if (total == 0) return;
+  const uint32_t* sbg = a.slash_bits + (int64_t)h * a.W;
+  for (int w = tid; w < a.W; w += BWD_THREADS) sbits[w] = sbg[w];
+
+  const bf16* kbase = (const bf16*)a.k + kvh * a.ksh;
+  const bf16* vbase = (const bf16*)a.v + kvh * a.vsh;
+  bf16x8 qf[2][4], df[2][4];
+  float lse2[2], dl[2];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs) {
+    const int64_t grow = row_base + 16 * rs + n16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[rs][ks] = *(const bf16x8*)((const bf16*)a.q + h * a.qsh + grow * a.qsn + 32 * ks + 8 * g4);
+      df[rs][ks] = *(const bf16x8*)((const bf16*)a.dout + h * a.dsh + grow * a.dsn + 32 * ks + 8 * g4);
+    }
+    lse2[rs] = a.lse[(int64_t)h * a.QB * BLK + grow] * LOG2E;
+    dl[rs] = a.delta[(int64_t)h * a.QB * BLK + grow];
+  }
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[rs][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.scale_log2;
+  int mode_c = 0;
+
+  auto step = [&](int it, const bf16* Ks, const bf16* Vs, const int* thc, bf16* Kn, bf16* Vn, int* thn,
+                  int* dn_next, const int* dn_cur) {
+    wait_all_mem();
+    __syncthreads();
+    const int mode = mode_c;
+    if (it + 1 < total) {
+      int rows_n[4], thr_n, mode_n;
+      bt.desc_decode(it + 1, dn_cur, rows_n, mode_n, thr_n, wave, lane, tid);
+      dma_tile(Kn, kbase, a.ksn, rows_n, wave, lane);
+      dma_tile(Vn, vbase, a.vsn, rows_n, wave, lane);
+      if (tid < BLK) thn[tid] = thr_n;
+      mode_c = mode_n;
+      if (it + 2 < total) bt.desc_copy(it + 2, dn_next, wave, lane);
+    }
+    // S^T and dP^T for keys 32 kh + 8 g + 4 t + i, rows 16 rs + n of the wave
+    f32x4 s[2][2], dp[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kr = 32 * kh + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) s[rs][t] = dp[rs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(Ks + tile_off(kr, 4 * ks + g4));
+        const bf16x8 vf = *(const bf16x8*)(Vs + tile_off(kr, 4 * ks + g4));
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          s[rs][t] = mfma_bf16(kf, qf[rs][ks], s[rs][t]);
+          dp[rs][t] = mfma_bf16(vf, df[rs][ks], dp[rs][t]);
+        }
+      }
+    }
+    bf16x8 dsh[2], dsl[2];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      const int rowoff = 32 * rh + 16 * rs + n16;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bool act = lse2[rs] > -INFINITY;
+          if (mode) act = act && thc[32 * kh + 8 * g4 + 4 * t + i] <= rowoff;
+          const float p = act ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs])) : 0.f;
+          s[rs][t][i] = p * (dp[rs][t][i] - dl[rs]);
+        }
+      split8(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
+    }
+    // dQ^T += K^T dS^T over this wave's 32 keys
+    const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int lc = 2 * dt + ((n16 & 3) >> 1);
+      const bf16x8 ka = lds_read_tr16_x2(Ks + tile_off(vr, lc) + 4 * (n16 & 1), D);
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        acc[rs][dt] = mfma_bf16(ka, dsh[rs], acc[rs][dt]);
+        acc[rs][dt] = mfma_bf16(ka, dsl[rs], acc[rs][dt]);
+      }
+    }
+  };
+
+  bt.desc_copy(0, desc0_sh, wave, lane);
+  if (total > 1) bt.desc_copy(1, desc1_sh, wave, lane);
+  wait_all_mem();
+  __syncthreads();
+  {
+    int rows0[4], thr0;
+    bt.desc_decode(0, desc0_sh, rows0, mode_c, thr0, wave, lane, tid);
+    dma_tile(K0, kbase, a.ksn, rows0, wave, lane);
+    dma_tile(V0, vbase, a.vsn, rows0, wave, lane);
+    if (tid < BLK) thr0_sh[tid] = thr0;
+  }
+  for (int it = 0; it < total; it += 2) {
+    step(it, K0, V0, thr0_sh, K1, V1, thr1_sh, desc0_sh, desc1_sh);
+    if (it + 1 < total) step(it + 1, K1, V1, thr1_sh, K0, V0, thr0_sh, desc1_sh, desc0_sh);
+  }
+  __syncthreads();
+  float* xo = (float*)(rh == 0 ? K0 : V0);   // [2 rs][8 dt][64 lanes] f32x4 per row half
+  if (kh == 1) {
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(xo + ((rs * 8 + dt) * 64 + lane) * 4) = acc[rs][dt];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs) {
+    float* out = a.dq + ((int64_t)h * a.QB * BLK + row_base + 16 * rs + n16) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o1 = *(const f32x4*)(xo + ((rs * 8 + dt) * 64 + lane) * 4);
+      f32x4 r = *(f32x4*)(out + 16 * dt + 4 * g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] += (acc[rs][dt][i] + o1[i]) * a.scale;
+      *(f32x4*)(out + 16 * dt + 4 * g4) = r;
+    }
+  }
+}
+
+// Key-major core: wave (kh, rh) holds keys 32 kh + 16 kt + n (kt = 0, 1) as
+// K/V fragments and processes rows 32 rh .. 32 rh + 31 of a staged query block
+// (Q, dO tiles; per-row lse in log2 units and delta). thr[kt]: rows with
+// offset below it are inactive for key kt of this lane.
+__device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const float* lsh, const float* dsh_,
+                                         const bf16x8 (*kf)[4], const bf16x8 (*vf)[4], const int* thr,
+                                         int kh, int rh, int g4, int n16, float sl2, f32x4 (*acc_dk)[8],
+                                         f32x4 (*acc_dv)[8]) {
+  (void)kh;
+  constexpr int D = TD;
+  // S and dP, rows 32 rh + 8 g + 4 t + i (lane's column = key n)
+  f32x4 s[2][2], dp[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int qr = 32 * rh + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt][t] = dp[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 qa = *(const bf16x8*)(Qs + tile_off(qr, 4 * ks + g4));
+      const bf16x8 oa = *(const bf16x8*)(Os + tile_off(qr, 4 * ks + g4));
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt][t] = mfma_bf16(qa, kf[kt][ks], s[kt][t]);
+        dp[kt][t] = mfma_bf16(oa, vf[kt][ks], dp[kt][t]);
+      }
+    }
+  }
+  const int r0 = 32 * rh + 8 * g4;
+  f32x4 l2[2] = {*(const f32x4*)(lsh + r0), *(const f32x4*)(lsh + r0 + 4)};   // natural log
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l2[t][i] *= LOG2E;
+  const f32x4 dd[2] = {*(const f32x4*)(dsh_ + r0), *(const f32x4*)(dsh_ + r0 + 4)};
+  bf16x8 ph[2], pl[2], dh[2], dl[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x4 ds[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * t + i;
+        const bool act = r >= thr[kt] && l2[t][i] > -INFINITY;
+        const float p = act ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][t][i], sl2, -l2[t][i])) : 0.f;
+        s[kt][t][i] = p;
+        ds[t][i] = p * (dp[kt][t][i] - dd[t][i]);
+      }
+    split8(s[kt][0], s[kt][1], ph[kt], pl[kt]);
+    split8(ds[0], ds[1], dh[kt], dl[kt]);
+  }
+  // dV^T += dO^T P, dK^T += Q^T dS over the wave's 32 rows
+  const int rr = 32 * rh + 8 * g4 + (n16 >> 2);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int lc = 2 * dt + ((n16 & 3) >> 1);
+    const bf16x8 oT = lds_read_tr16_x2(Os + tile_off(rr, lc) + 4 * (n16 & 1), D);
+    const bf16x8 qT = lds_read_tr16_x2(Qs + tile_off(rr, lc) + 4 * (n16 & 1), D);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      acc_dv[kt][dt] = mfma_bf16(oT, ph[kt], acc_dv[kt][dt]);
+      acc_dv[kt][dt] = mfma_bf16(oT, pl[kt], acc_dv[kt][dt]);
+      acc_dk[kt][dt] = mfma_bf16(qT, dh[kt], acc_dk[kt][dt]);
+      acc_dk[kt][dt] = mfma_bf16(qT, dl[kt], acc_dk[kt][dt]);
+    }
+  }
+}
+
+// Copy the Q and dO rows of query block I of head h and its lse/delta.
+__device__ __forceinline__ void stage_qblock(bf16* Qn, bf16* On, float* ln, const BwdArgs& a, int h, int I, int wave,
+                                             int lane) {
+  int rows[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) rows[c] = I * BLK + dma_local_row(wave, c, lane);
+  dma_tile(Qn, (const bf16*)a.q + h * a.qsh, a.qsn, rows, wave, lane);
+  dma_tile(On, (const bf16*)a.dout + h * a.dsh, a.dsn, rows, wave, lane);
+  if (wave < 2) {
+    const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)h * a.QB * BLK + (int64_t)I * BLK + lane;
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)(
+                                         (__attribute__((address_space(3))) float*)(ln + wave * BLK)),
+                                     4, 0, 0);
+  }
+}
+
+// Combine the two row halves' dK/dV partials (rh = 1 -> rh = 0 through LDS)
+// and add them to dk/dv (plain stores when `atomic` is 0, fp32 atomics
+// otherwise). keys[kt]: output row of this lane's key kt (-1 = none).
+__device__ __forceinline__ void kv_finish(float* xbuf_dk, float* xbuf_dv, f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8],
+                                          float* dk, float* dv, const int64_t* keys, int kh, int rh, int lane, int g4,
+                                          float scale, bool atomic) {
+  constexpr int D = TD;
+  float* xk = xbuf_dk + kh * (2 * 8 * 64 * 4);
+  float* xv = xbuf_dv + kh * (2 * 8 * 64 * 4);
+  __syncthreads();
+  if (rh == 1) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        *(f32x4*)(xk + ((kt * 8 + dt) * 64 + lane) * 4) = acc_dk[kt][dt];
+        *(f32x4*)(xv + ((kt * 8 + dt) * 64 + lane) * 4) = acc_dv[kt][dt];
+      }
+  }
+  __syncthreads();
+  if (rh == 1) return;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    if (keys[kt] < 0) continue;
+    float* kr = dk + keys[kt] * D;
+    float* vr = dv + keys[kt] * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 k1 = *(const f32x4*)(xk + ((kt * 8 + dt) * 64 + lane) * 4);
+      const f32x4 v1 = *(const f32x4*)(xv + ((kt * 8 + dt) * 64 + lane) * 4);
+      if (atomic) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          atomicAdd(kr + 16 * dt + 4 * g4 + i, (acc_dk[kt][dt][i] + k1[i]) * scale);
+          atomicAdd(vr + 16 * dt + 4 * g4 + i, acc_dv[kt][dt][i] + v1[i]);
+        }
+      } else {
+        f32x4 x = *(f32x4*)(kr + 16 * dt + 4 * g4);
+        f32x4 y = *(f32x4*)(vr + 16 * dt + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] += (acc_dk[kt][dt][i] + k1[i]) * scale;
+          y[i] += acc_dv[kt][dt][i] + v1[i];
+        }
+        *(f32x4*)(kr + 16 * dt + 4 * g4) = x;
+        *(f32x4*)(vr + 16 * dt + 4 * g4) = y;
+      }
+    }
+  }
+}
+
+// dK/dV over slash tiles: one workgroup per (kv head, key block J); walks the
+// CSC lists of every q head of the group (entries staged through LDS like the
+// forward's descriptors) and owns the key block's dK/dV rows.
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs a) {
+  // stage s = (Q tile, dO tile) in QOs; after the loop QO0 / QO1 (32 KiB each)
+  // carry the dK / dV exchange
+  __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
+  bf16* Q0 = QO0;
+  bf16* O0 = QO0 + TILE_ELEMS;
+  bf16* Q1 = QO1;
+  bf16* O1 = QO1 + TILE_ELEMS;
+  __shared__ __attribute__((aligned(16))) float L0[2 * BLK];
+  __shared__ __attribute__((aligned(16))) float L1[2 * BLK];
+  __shared__ int desc0_sh[BLK], desc1_sh[BLK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int kh = wave >> 1, rh = wave & 1;
+  const int nitems = a.Hkv * a.KB;
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int J = item % a.KB, kvh = item / a.KB;
+  const int grp = a.Hq / a.Hkv;
+  // flattened (head, CSC entry) sequence of the group
+  int cstart[8], cnt[8], total = 0;
+  for (int hh = 0; hh < grp; ++hh) {
+    const int64_t cu = (int64_t)(kvh * grp + hh) * a.KB + J;
+    cstart[hh] = a.csc_ptr[cu];
+    cnt[hh] = a.csc_ptr[cu + 1] - cstart[hh];
+    total += cnt[hh];
+  }
+  if (total == 0) return;
+  auto entry_of = [&](int it, int& hh) {   // position in csc_row of step `it`
+    hh = 0;
+    while (it >= cnt[hh]) { it -= cnt[hh]; ++hh; }
+    return cstart[hh] + it;
+  };
+  auto desc_copy = [&](int it, int* slot) {
+    if (wave != 0) return;
+    int hh;
+    const int e = entry_of(it, hh);
+    __builtin_amdgcn_global_load_lds((const void*)(a.csc_row + e),
+                                     (__attribute__((address_space(3))) void*)(
+                                         (__attribute__((address_space(3))) int*)(slot)),
+                                     4, 0, 0);
+  };
+
+  bf16x8 kf[2][4], vf[2][4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int64_t krow = (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[kt][ks] = *(const bf16x8*)((const bf16*)a.k + kvh * a.ksh + krow * a.ksn + 32 * ks + 8 * g4);
+      vf[kt][ks] = *(const bf16x8*)((const bf16*)a.v + kvh * a.vsh + krow * a.vsn + 32 * ks + 8 * g4);
+    }
+  }
+  f32x4 acc_dk[2][8], acc_dv[2][8];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc_dk[kt][dt] = acc_dv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.scale_log2;
+  int diag_c = 0;
+
+  auto step = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, bf16* Qn, bf16* On, float* Ln,
+                  int* dn_next, const int* dn_cur) {
+    wait_all_mem();
+    __syncthreads();
+    const int diag = diag_c;
+    if (it + 1 < total) {
+      int hh;
+      entry_of(it + 1, hh);
+      const int e = dn_cur[0];
+      stage_qblock(Qn, On, Ln, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane);
+      diag_c = (e & VS_TILE_DIAG) ? 1 : 0;
+      if (it + 2 < total) desc_copy(it + 2, dn_next);
+    }
+    int thr[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) thr[kt] = diag ? 32 * kh + 16 * kt + n16 : 0;
+    kv_block(Qs, Os, Ls, Ls + BLK, kf, vf, thr, kh, rh, g4, n16, sl2, acc_dk, acc_dv);
+  };
+
+  desc_copy(0, desc0_sh);
+  if (total > 1) desc_copy(1, desc1_sh);
+  wait_all_mem();
+  __syncthreads();
+  {
+    int hh;
+    entry_of(0, hh);
+    const int e = desc0_sh[0];
+    stage_qblock(Q0, O0, L0, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane);
+    diag_c = (e & VS_TILE_DIAG) ? 1 : 0;
+  }
+  for (int it = 0; it < total; it += 2) {
+    step(it, Q0, O0, L0, Q1, O1, L1, desc0_sh, desc1_sh);
+    if (it + 1 < total) step(it + 1, Q1, O1, L1, Q0, O0, L0, desc1_sh, desc0_sh);
+  }
+  int64_t keys[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) keys[kt] = (int64_t)kvh * a.KB * BLK + (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
+  kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, false);
+}
+
+// dK/dV of vertical columns: work items (head, 64-column chunk of the shard's
+// verticals, range of VERT_SEG query blocks) enumerated from the device-side
+// counts; a fixed grid strides over them. Query blocks before the chunk's
+// first column are skipped; within the range every block is processed with
+// per-key thresholds (causal edge, columns covered by a listed tile).
+// Results are added with fp32 atomics (a column can be a vertical of several
+// q heads of the group).
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) float L0[2 * BLK];
+  __shared__ __attribute__((aligned(16))) float L1[2 * BLK];
+  __shared__ uint32_t sbits[MAX_LDS_W];
+  bf16* Q0 = QO0;
+  bf16* O0 = QO0 + TILE_ELEMS;
+  bf16* Q1 = QO1;
+  bf16* O1 = QO1 + TILE_ELEMS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int kh = wave >> 1, rh = wave & 1;
+  const int nseg = (a.QB + VERT_SEG - 1) / VERT_SEG;
+  int64_t nwork = 0;
+  for (int h = 0; h < a.Hq; ++h) nwork += (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+  const int grp = a.Hq / a.Hkv;
+  const float sl2 = a.scale_log2;
+  for (int64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
+    int64_t r = w;
+    int h = 0;
+    for (; h < a.Hq; ++h) {
+      const int64_t n = (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+      if (r < n) break;
+      r -= n;
+    }
+    const int chunk = (int)(r / nseg), seg = (int)(r % nseg);
+    const int kvh = h / grp;
+    const int cnt = a.vloc_cnt[h];
+    const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
+    const int64_t gb_min = global_block(a.kind, a.P, a.KB, a.src, vl[chunk * BLK] / BLK);
+    const int I_lo = max(seg * VERT_SEG, blocks_upto(a.kind, a.P, a.QB, a.rank, gb_min - 1));
+    const int I_hi = min(a.QB, (seg + 1) * VERT_SEG);
+    const int total = I_hi - I_lo;
+    if (total <= 0) continue;
+    __syncthreads();  // the previous item's exchange has been read
+    const uint32_t* sbg = a.slash_bits + (int64_t)h * a.W;
+    for (int x = tid; x < a.W; x += BWD_THREADS) sbits[x] = sbg[x];
+    int m[2];
+    int64_t gbk[2];
+    bool valid[2];
+    bf16x8 kf[2][4], vf[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int slot = chunk * BLK + 32 * kh + 16 * kt + n16;
+      valid[kt] = slot < cnt;
+      m[kt] = vl[valid[kt] ? slot : chunk * BLK];
+      gbk[kt] = global_block(a.kind, a.P, a.KB, a.src, m[kt] / BLK);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kf[kt][ks] = *(const bf16x8*)((const bf16*)a.k + kvh * a.ksh + (int64_t)m[kt] * a.ksn + 32 * ks + 8 * g4);
+        vf[kt][ks] = *(const bf16x8*)((const bf16*)a.v + kvh * a.vsh + (int64_t)m[kt] * a.vsn + 32 * ks + 8 * g4);
+      }
+    }
+    f32x4 acc_dk[2][8], acc_dv[2][8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc_dk[kt][dt] = acc_dv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, bf16* Qn, bf16* On, float* Ln) {
+      wait_all_mem();
+      __syncthreads();
+      if (it + 1 < total) stage_qblock(Qn, On, Ln, a, h, I_lo + it + 1, wave, lane);
+      const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I_lo + it);
+      int thr[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int64_t j = G - gbk[kt];
+        thr[kt] = BLK;
+        if (valid[kt] && j >= 0 && !((sbits[j >> 5] >> (j & 31)) & 1u)) thr[kt] = (j == 0) ? (m[kt] % BLK) : 0;
+      }
+      kv_block(Qs, Os, Ls, Ls + BLK, kf, vf, thr, kh, rh, g4, n16, sl2, acc_dk, acc_dv);
+    };
+    stage_qblock(Q0, O0, L0, a, h, I_lo, wave, lane);
+    for (int it = 0; it < total; it += 2) {
+      step(it, Q0, O0, L0, Q1, O1, L1);
+      if (it + 1 < total) step(it + 1, Q1, O1, L1, Q0, O0, L0);
+    }
+    int64_t keys[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) keys[kt] = valid[kt] ? (int64_t)kvh * a.KB * BLK + m[kt] : -1;
+    kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, true);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // delta[row] = dO[row] . O[row]; D/4 threads per row.
 template <typename T>
 __global__ void bwd_prep_kernel(const float* o, const T* dout, int64_t dsh, int64_t dsn, int64_t Nq, int64_t rows,
@@ -470,7 +979,12 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src;
   a.scale = scale; a.scale_log2 = scale * LOG2E;
-  if (dtype == VS_BF16 && D == 128) launch_bwd_typed<bf16, 128>(a, stream);
+  if (dtype == VS_BF16 && D == 128) {
+    if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
+  }
   else if (dtype == VS_BF16 && D == 64) launch_bwd_typed<bf16, 64>(a, stream);
   else if (dtype == VS_F32 && D == 64) launch_bwd_typed<float, 64>(a, stream);
   else return VS_ERR_UNSUPPORTED;

@@ -146,3 +146,58 @@ __device__ __forceinline__ void split_bf16(float w, bf16& hi, bf16& lo) {
 }
 
 }  // namespace vs
+
+namespace vs {
+
+constexpr int MAX_LDS_W = 512;   // slash-bitmap words kept in LDS (sequences up to 2^20 tokens)
+
+// The tile sequence of one (q head, local query block) against the visible
+// shard: its listed slash tiles, then its vertical columns gathered 64 at a
+// time. Descriptors are staged through LDS by asynchronous copies (wave 0
+// copies the list entry or the 64 column positions of a tile into a 64-int
+// slot) and decoded by every wave after a barrier into the four copy rows of
+// the lane, the tile mode (0 = full tile, 1 = per-key thresholds apply) and,
+// for tid < 64, the threshold of key row tid: query rows with offset below it
+// are inactive for that key (causal edge or a column already covered by a
+// listed tile).
+struct BlockTiles {
+  const int32_t* tile_col;
+  const int32_t* vl;          // the shard's vertical columns of this head
+  const uint32_t* sbits;      // LDS copy of the head's slash bitmap
+  int t0, nt, ve, total;
+  int64_t G;                  // global block of the query block
+  int kind, P, KB, src;
+
+  __device__ __forceinline__ void desc_copy(int it, int* slot, int wave, int lane) const {
+    if (wave != 0) return;
+    const int32_t* s = (it < nt) ? tile_col + t0 + it : vl + min((it - nt) * BLK + lane, ve - 1);
+    __builtin_amdgcn_global_load_lds((const void*)s,
+                                     (__attribute__((address_space(3))) void*)(
+                                         (__attribute__((address_space(3))) int*)(slot)),
+                                     4, 0, 0);
+  }
+  __device__ __forceinline__ void desc_decode(int it, const int* slot, int* rows, int& mode, int& thr, int wave,
+                                              int lane, int tid) const {
+    if (it < nt) {
+      const int e = slot[0];
+      const int J = e & VS_TILE_MASK;
+      mode = (e & VS_TILE_DIAG) ? 1 : 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rows[c] = J * BLK + dma_local_row(wave, c, lane);
+      thr = tid;
+    } else {
+      const int base = (it - nt) * BLK;
+      mode = 1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+      thr = BLK;
+      if (tid < BLK && base + tid < ve) {
+        const int m = slot[tid];
+        const int64_t j = G - global_block(kind, P, KB, src, m / BLK);
+        if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
+      }
+    }
+  }
+};
+
+}  // namespace vs
