@@ -42,11 +42,15 @@ def parse():
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--copy-probe", action="store_true", help="run only a 1 GiB device copy (counter scaling)")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the sparse path is built and timed on a single "
               "MI355X; multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
@@ -96,29 +100,40 @@ def main():
     dv = torch.zeros(Hkv, N, D, device=dev)
     stream = torch.cuda.current_stream()
 
-    ev = {name: [] for name in ("index", "mask", "fwd", "bwd")}
+    stages = ("index", "mask", "fwd", "bwd_prep_zero", "dq", "dkdv", "dkdv_vert")
+    ev = {name: [] for name in stages}
 
     def step(record):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
-        if record: marks[0].record(stream)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
+
+        def mark(i):
+            if record:
+                marks[i].record(stream)
+        mark(0)
         vs.vs_index_build(q_last, k, lay, cfg.scale, cfg.top_p, vert_s, slash_s, vidx, vcnt, sidx, scnt, ws, stream)
-        if record: marks[1].record(stream)
+        mark(1)
         vs.vs_block_mask(vidx, vcnt, sidx, scnt, 0, 0, mask, stream)
-        if record: marks[2].record(stream)
+        mark(2)
         vs.vs_attn_fwd(q, k, v, mask, cfg.scale, o, lse, 0, stream)
-        if record: marks[3].record(stream)
+        mark(3)
         if cfg.backward:
             vs.vs_attn_bwd_prep(o, do, delta, stream)
             dq.zero_()
             dk.zero_()
             dv.zero_()
-            vs.vs_attn_bwd(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, stream)
+            mark(4)
+            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DQ, stream)
+            mark(5)
+            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DKDV, stream)
+            mark(6)
+            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DKDV_VERT, stream)
+        else:
+            for i in (4, 5, 6):
+                mark(i)
+        mark(7)
         if record:
-            marks[4].record(stream)
-            ev["index"].append((marks[0], marks[1]))
-            ev["mask"].append((marks[1], marks[2]))
-            ev["fwd"].append((marks[2], marks[3]))
-            ev["bwd"].append((marks[3], marks[4]))
+            for i, name in enumerate(stages):
+                ev[name].append((marks[i], marks[i + 1]))
 
     for _ in range(args.warmup):
         step(False)
@@ -134,20 +149,42 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     stage_ms = {kname: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for kname, pairs in ev.items()}
 
-    A = int(mask.arrays()["n_active"].sum().item())
+    arrs = mask.arrays()
+    n_active = arrs["n_active"]
+    A = int(n_active.sum().item())
+    tp = arrs["tile_ptr"].cpu().numpy()
+    tcol = arrs["tile_col"][: int(tp[-1])].cpu().numpy()
+    n_diag = int(((tcol & vs.TILE_DIAG) != 0).sum())
+    A_slash = 4096 * (len(tcol) - n_diag) + 2080 * n_diag     # entries inside listed slash tiles
+    A_vert = A - A_slash                                       # vertical entries outside them
     total_causal = Hq * N * (N + 1) // 2
     sparsity = 1.0 - A / total_causal
     eff_flops = (4 + (10 if cfg.backward else 0)) * D * A
     tflops = eff_flops / (ms_per_step * 1e-3) / 1e12
-    attn_ms = stage_ms["fwd"] + stage_ms["bwd"]
+    attn_ms = sum(stage_ms[x] for x in ("fwd", "bwd_prep_zero", "dq", "dkdv", "dkdv_vert"))
     attn_tflops = eff_flops / (attn_ms * 1e-3) / 1e12
 
-    # roofline of the sparse forward kernel (one kernel per vs_attn_fwd call)
-    fwd_flops = 4 * D * A
-    fwd_tf = fwd_flops / (stage_ms["fwd"] * 1e-3) / 1e12
+    # Roofline of the dominant kernel. Each timed stage below is exactly one
+    # kernel launch. Algorithmic FLOPs per active entry (FlashAttention-2
+    # convention, 14 d in total): forward 4 d; dK/dV kernels 8 d (recompute S,
+    # dP, dV, dK) over their entries; dQ kernel 2 d.
     peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    roofline = {"kernel": "attn_fwd_kernel", "bound": "mfma", "achieved": round(fwd_tf, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(fwd_tf / peak, 4), "traffic": None}
+    kernels = {"fwd": ("attn_fwd_bf16_d128_kernel", 4 * D * A)}
+    if cfg.backward:
+        kernels.update({"dq": ("dq_bf16_d128_kernel", 2 * D * A),
+                        "dkdv": ("dkdv_bf16_d128_kernel", 8 * D * A_slash),
+                        "dkdv_vert": ("dkdv_vert_bf16_d128_kernel", 8 * D * A_vert)})
+    per_kernel = {}
+    for st, (kname, flops) in kernels.items():
+        tf = flops / (stage_ms[st] * 1e-3) / 1e12
+        per_kernel[st] = {"kernel": kname, "ms": round(stage_ms[st], 4), "tflops": round(tf, 2),
+                          "frac_mfma_peak": round(tf / peak, 4)}
+    dom = max(per_kernel, key=lambda x: per_kernel[x]["ms"])
+    dk_name, dk_flops = kernels[dom]
+    roofline = {"kernel": dk_name, "bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": peak,
+                "unit": "TFLOP/s", "frac": per_kernel[dom]["frac_mfma_peak"],
+                "traffic": stored_traffic(dk_name), "algorithmic_flops_per_launch": dk_flops,
+                "mean_launch_ms": round(stage_ms[dom], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -163,10 +200,44 @@ def main():
         "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
         "attn_only_tflops": round(attn_tflops, 3),
         "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
-        "active_entries": A, "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
+        "kernels": per_kernel,
+        "active_entries": A, "active_slash_tiles": A_slash, "active_vertical": A_vert,
+        "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/counters.json: FETCH_SIZE and WRITE_SIZE runs scaled by the
+    same counters' reading for a copy of known size), or None when absent or
+    when the kernel's source file has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def copy_probe():
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
 
 
 def cpu_baseline(cfg, host, vidx, vcnt, sidx, scnt, seconds, tflops_unit=True):

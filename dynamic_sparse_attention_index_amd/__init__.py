@@ -27,8 +27,9 @@ TILE_MASK = 0x3FFFFFFF
 
 EXPORTED = [
     "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_mask_bytes", "vs_mask_init",
-    "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd",
+    "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
 ]
+VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL = 1, 2, 4, 7
 
 
 class VsTensor(ctypes.Structure):
@@ -93,6 +94,9 @@ def lib():
         L.vs_attn_bwd.restype = i32
         L.vs_attn_bwd.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask), f32,
                                   vp, vp, vp, vp]
+        L.vs_attn_bwd_parts.restype = i32
+        L.vs_attn_bwd_parts.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask),
+                                        f32, vp, vp, vp, i32, vp]
         _lib = L
     return _lib
 
@@ -208,3 +212,9 @@ def vs_attn_bwd(q, k, v, dout, lse, delta, mask: Mask, scale, dq, dk, dv, stream
     _check(lib().vs_attn_bwd(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), as_vs_tensor(dout), _ptr(lse),
                              _ptr(delta), ctypes.byref(mask.desc), scale, _ptr(dq), _ptr(dk), _ptr(dv),
                              _stream(stream)), "vs_attn_bwd")
+
+
+def vs_attn_bwd_parts(q, k, v, dout, lse, delta, mask: Mask, scale, dq, dk, dv, parts, stream=None):
+    _check(lib().vs_attn_bwd_parts(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), as_vs_tensor(dout),
+                                   _ptr(lse), _ptr(delta), ctypes.byref(mask.desc), scale, _ptr(dq), _ptr(dk),
+                                   _ptr(dv), int(parts), _stream(stream)), "vs_attn_bwd_parts")

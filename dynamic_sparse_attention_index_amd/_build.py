@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "libvsattn.so")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics",

@@ -206,17 +206,23 @@ int vs_attn_bwd_prep(const float* o, vs_tensor dout, float* delta, void* stream)
   return launch_bwd_prep(o, dout.dtype, view(dout), dout.H, dout.N, dout.D, delta, (hipStream_t)stream);
 }
 
-int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, const float* lse, const float* delta,
-                const vs_mask* m, float scale, float* dq, float* dk, float* dv, void* stream) {
+int vs_attn_bwd_parts(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, const float* lse, const float* delta,
+                      const vs_mask* m, float scale, float* dq, float* dk, float* dv, int parts, void* stream) {
   int st;
   if ((st = check_attn(q, k, v, m)) != VS_OK) return st;
   if ((st = check_tensor(dout, m->Hq, (int64_t)m->QB * 64, q.D)) != VS_OK) return st;
   if (dout.dtype != q.dtype) return VS_ERR_ARG;
+  if (parts <= 0 || (parts & ~VS_BWD_ALL)) return VS_ERR_ARG;
   if (!lse || !delta || !dq || !dk || !dv) return VS_ERR_ARG;
   if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return VS_ERR_UNSUPPORTED;
   if (!(scale > 0.f)) return VS_ERR_ARG;
   return launch_attn_bwd(q.dtype, q.D, view(q), view(k), view(v), view(dout), lse, delta, m, scale, dq, dk, dv,
-                         (hipStream_t)stream);
+                         parts, (hipStream_t)stream);
+}
+
+int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, const float* lse, const float* delta,
+                const vs_mask* m, float scale, float* dq, float* dk, float* dv, void* stream) {
+  return vs_attn_bwd_parts(q, k, v, dout, lse, delta, m, scale, dq, dk, dv, VS_BWD_ALL, stream);
 }
 
 }  // extern "C"

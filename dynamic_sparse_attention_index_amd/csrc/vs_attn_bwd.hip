@@ -959,15 +959,18 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
 }
 
 template <typename T, int D>
-static void launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
-  hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
-  hipLaunchKernelGGL((dkdv_vert_kernel<T, D>), dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
+static void launch_bwd_typed(const BwdArgs& a, int parts, hipStream_t stream) {
+  if (parts & VS_BWD_DQ)
+    hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
+  if (parts & VS_BWD_DKDV)
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
+  if (parts & VS_BWD_DKDV_VERT)
+    hipLaunchKernelGGL((dkdv_vert_kernel<T, D>), dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
 }
 
 int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, const float* lse,
                     const float* delta, const vs_mask* m, float scale, float* dq, float* dk, float* dv,
-                    hipStream_t stream) {
+                    int parts, hipStream_t stream) {
   BwdArgs a;
   a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.dout = dout.ptr;
   a.qsh = q.sh; a.qsn = q.sn; a.ksh = k.sh; a.ksn = k.sn; a.vsh = v.sh; a.vsn = v.sn;
@@ -981,12 +984,16 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   a.scale = scale; a.scale_log2 = scale * LOG2E;
   if (dtype == VS_BF16 && D == 128) {
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
-    hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
-    hipLaunchKernelGGL(dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
+    if (a.Hq / a.Hkv > 8) return VS_ERR_UNSUPPORTED;
+    if (parts & VS_BWD_DQ)
+      hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
+    if (parts & VS_BWD_DKDV)
+      hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
+    if (parts & VS_BWD_DKDV_VERT)
+      hipLaunchKernelGGL(dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
   }
-  else if (dtype == VS_BF16 && D == 64) launch_bwd_typed<bf16, 64>(a, stream);
-  else if (dtype == VS_F32 && D == 64) launch_bwd_typed<float, 64>(a, stream);
+  else if (dtype == VS_BF16 && D == 64) launch_bwd_typed<bf16, 64>(a, parts, stream);
+  else if (dtype == VS_F32 && D == 64) launch_bwd_typed<float, 64>(a, parts, stream);
   else return VS_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }

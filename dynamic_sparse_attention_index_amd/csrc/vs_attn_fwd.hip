@@ -17,6 +17,7 @@
 // straight from registers; V^T fragments come from the row-major V tile via
 // the gfx950 LDS transpose read.
 #include <type_traits>
+#include <utility>
 
 #include "vs_common.h"
 #include "vs_internal.h"
@@ -24,7 +25,10 @@
 namespace vs {
 
 constexpr int FWD_THREADS = 256;  // 4 waves
-constexpr int FWD_MAX_W = 512;    // slash-bitmap words held in LDS (sequences up to 2^20 tokens)
+#ifndef VS_FWD_STAGES
+#define VS_FWD_STAGES 2
+#endif
+constexpr int FWD_STAGES = VS_FWD_STAGES;   // LDS pipeline depth of the bf16 forward
 
 struct FwdArgs {
   const void* q; const void* k; const void* v;
@@ -280,20 +284,27 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 // LDS stages with asynchronous global->LDS copies issued one tile ahead, so
 // each tile costs one barrier. Row indices of gathered vertical chunks and
 // list entries are loaded one more tile ahead.
-__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
+template <int NS>
+__global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
   constexpr int D = TD;
-  // Two LDS stages of (K tile, V tile) as distinct arrays, and the loop is
-  // unrolled by two, so the compiler can tell the stage being read from the
-  // stage being filled and lets the copy run under the compute. After the
-  // loop the K and V arrays of stage 0 carry the key-half exchange.
-  __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 V1[TILE_ELEMS];
+  // NS LDS stages, each (K tile, V tile) in an array of its own, and the loop
+  // unrolled by NS, so the compiler can tell the stage being read from the
+  // stages being filled and lets the copies run under the compute; NS - 1
+  // tiles are in flight. After the loop stage 0 carries the key-half exchange.
+  __shared__ __attribute__((aligned(16))) bf16 KV0[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 KV1[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 KV2[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 KV3[2 * TILE_ELEMS];
   __shared__ float xs[2 * 2 * 64 * 2];
-  __shared__ int thr0_sh[BLK], thr1_sh[BLK];
-  __shared__ int desc0_sh[BLK], desc1_sh[BLK];
-  __shared__ uint32_t sbits[FWD_MAX_W];
+  __shared__ int thr_sh[NS][BLK];
+  __shared__ int desc_sh[NS][BLK];
+  __shared__ uint32_t sbits[MAX_LDS_W];
+  auto stage = [&]<int k>() -> bf16* {
+    if constexpr (k == 0) return KV0;
+    else if constexpr (k == 1) return KV1;
+    else if constexpr (k == 2) return KV2;
+    else return KV3;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
@@ -311,50 +322,15 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
   const bf16* kbase = (const bf16*)a.k + kvh * a.ksh;
   const bf16* vbase = (const bf16*)a.v + kvh * a.vsh;
 
-  const int t0 = a.tile_ptr[u];
-  const int nt = a.tile_ptr[u + 1] - t0;
-  const int ve = a.vert_end[u];
-  const int total = nt + (ve + BLK - 1) / BLK;
-  const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I);
-  const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
-  const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
-
-  // Tile descriptors travel through LDS as well: wave 0 copies the list entry
-  // (slash tile) or the 64 column positions (vertical chunk) of tile it+2
-  // while tile it is computed; after the next barrier every wave decodes them
-  // into copy rows, the tile mode (0 = full, 1 = thresholds apply) and the
-  // key thresholds (query rows below a key's threshold are inactive). No
-  // register ever waits on an outstanding copy.
-  for (int w = tid; w < a.W; w += FWD_THREADS) sbits[w] = sb[w];
-  auto desc_copy = [&](int it, int* desc) {
-    if (wave != 0) return;
-    const int32_t* src = (it < nt) ? a.tile_col + t0 + it : vl + min((it - nt) * BLK + lane, ve - 1);
-    __builtin_amdgcn_global_load_lds((const void*)src,
-                                     (__attribute__((address_space(3))) void*)(
-                                         (__attribute__((address_space(3))) int*)(desc)),
-                                     4, 0, 0);
-  };
-  auto desc_decode = [&](int it, const int* desc, int* rows, int& mode, int& thr) {
-    if (it < nt) {
-      const int e = desc[0];
-      const int J = e & VS_TILE_MASK;
-      mode = (e & VS_TILE_DIAG) ? 1 : 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) rows[c] = J * BLK + dma_local_row(wave, c, lane);
-      thr = tid;
-    } else {
-      const int base = (it - nt) * BLK;
-      mode = 1;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) rows[c] = desc[dma_local_row(wave, c, lane)];
-      thr = BLK;
-      if (tid < BLK && base + tid < ve) {
-        const int m = desc[tid];
-        const int64_t j = G - global_block(a.kind, a.P, a.KB, a.src, m / BLK);
-        if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
-      }
-    }
-  };
+  BlockTiles bt;
+  bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
+  bt.t0 = a.tile_ptr[u]; bt.nt = a.tile_ptr[u + 1] - bt.t0; bt.ve = a.vert_end[u];
+  bt.total = bt.nt + (bt.ve + BLK - 1) / BLK;
+  bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
+  bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+  const int total = bt.total;
+  const uint32_t* sbg = a.slash_bits + (int64_t)h * a.W;
+  for (int w = tid; w < a.W; w += FWD_THREADS) sbits[w] = sbg[w];
 
   bf16x8 qf[2][4];
 #pragma unroll
@@ -370,25 +346,32 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
     for (int dt = 0; dt < 8; ++dt) acc[rs][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float sl2 = a.scale_log2;
-  int mode_c = 0;
+  int mode_st[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) mode_st[k] = 0;
 
-  // One tile: wait for its copy, start the next copy, compute. Ks/Vs/thr/desc
-  // of the stage being read, Kn/Vn/thn/dn of the other stage.
-  auto step = [&](int it, const bf16* Ks, const bf16* Vs, const int* thc, bf16* Kn, bf16* Vn, int* thn,
-                  int* dn_next, const int* dn_cur) {
+  // decode the descriptor of tile t (slot t % NS) and start its copy into stage nk
+  auto issue = [&]<int nk>(int t) {
+    int rows[4], thr, mode;
+    bt.desc_decode(t, desc_sh[nk], rows, mode, thr, wave, lane, tid);
+    bf16* st = stage.template operator()<nk>();
+    dma_tile(st, kbase, a.ksn, rows, wave, lane);
+    dma_tile(st + TILE_ELEMS, vbase, a.vsn, rows, wave, lane);
+    if (tid < BLK) thr_sh[nk][tid] = thr;
+    mode_st[nk] = mode;
+  };
+
+  // One tile in stage k: wait for its copy, start the copy of tile it+NS-1
+  // and the descriptor copy of tile it+NS, compute.
+  auto step = [&]<int k>(int it) {
+    constexpr int nk = (k + NS - 1) % NS;
     wait_all_mem();
-    __syncthreads();  // tile `it` and descriptor it+1 have landed; tile it-1 is done
-    const int mode = mode_c;
-    if (it + 1 < total) {
-      int rows_n[4], thr_n, mode_n;
-      desc_decode(it + 1, dn_cur, rows_n, mode_n, thr_n);
-      dma_tile(Kn, kbase, a.ksn, rows_n, wave, lane);
-      dma_tile(Vn, vbase, a.vsn, rows_n, wave, lane);
-      if (tid < BLK) thn[tid] = thr_n;
-      mode_c = mode_n;
-      // the other descriptor slot held descriptor `it`, decoded before the barrier
-      if (it + 2 < total) desc_copy(it + 2, dn_next);
-    }
+    __syncthreads();  // tile `it` and descriptor it+NS-1 have landed; tile it-1 is done
+    if (it + NS - 1 < total) issue.template operator()<nk>(it + NS - 1);
+    if (it + NS < total) bt.desc_copy(it + NS, desc_sh[k], wave, lane);
+    const bf16* Ks = stage.template operator()<k>();
+    const bf16* Vs = Ks + TILE_ELEMS;
+    const int mode = mode_st[k];
     // S^T for 32 keys (this wave's half) x 32 rows: s[rs][t] lane (g, n):
     // S[row 16 rs + n][key 32 kh + 8 g + 4 t + i]
     f32x4 s[2][2];
@@ -409,7 +392,7 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int th = thc[32 * kh + 8 * g4 + 4 * t + i];
+          const int th = thr_sh[k][32 * kh + 8 * g4 + 4 * t + i];
 #pragma unroll
           for (int rs = 0; rs < 2; ++rs)
             if (th > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
@@ -424,10 +407,15 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
                        fmaxf(fmaxf(s[rs][1][0], s[rs][1][1]), fmaxf(s[rs][1][2], s[rs][1][3])));
       mx = fmaxf(mx, xor16(mx));
       mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run[rs], mx * sl2);
+      // Exact running max: the largest probability of the row is then exactly
+      // 1 in bf16, which keeps the dominant term of O free of rounding (a
+      // stale reference doubles the O error on peaked rows).
+      const float mt = mx * sl2;
+      const bool up = mt > m_run[rs];
+      const float m_new = up ? mt : m_run[rs];
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha[rs] = __builtin_amdgcn_exp2f(m_run[rs] - m_use);
-      rescale |= m_new != m_run[rs];
+      alpha[rs] = up ? __builtin_amdgcn_exp2f(m_run[rs] - m_use) : 1.f;
+      rescale |= up;
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -450,30 +438,34 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
     }
     // O^T += V^T P^T over this wave's 32 keys (one 32-deep contraction)
     const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
+    const int vb = (n16 & 3) >> 1, vo = 4 * (n16 & 1);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int lc = 2 * dt + ((n16 & 3) >> 1);
-      const bf16x8 va = lds_read_tr16_x2(Vs + tile_off(vr, lc) + 4 * (n16 & 1), D);
+    for (int q = 0; q < 2; ++q) {
+      bf16x8 va[4];
+      lds_read_tr16_x2_4(Vs + tile_off(vr, 8 * q + vb) + vo, Vs + tile_off(vr, 8 * q + 2 + vb) + vo,
+                         Vs + tile_off(vr, 8 * q + 4 + vb) + vo, Vs + tile_off(vr, 8 * q + 6 + vb) + vo, va);
 #pragma unroll
-      for (int rs = 0; rs < 2; ++rs) acc[rs][dt] = mfma_bf16(va, pf[rs], acc[rs][dt]);
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) acc[rs][4 * q + d4] = mfma_bf16(va[d4], pf[rs], acc[rs][4 * q + d4]);
     }
   };
 
   if (total > 0) {
-    desc_copy(0, desc0_sh);
-    if (total > 1) desc_copy(1, desc1_sh);
+    // descriptors of tiles 0 .. NS-1, then the copies of tiles 0 .. NS-2
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+      if (t < total) bt.desc_copy(t, desc_sh[t], wave, lane);
     wait_all_mem();
     __syncthreads();
-    int rows0[4], thr0;
-    desc_decode(0, desc0_sh, rows0, mode_c, thr0);
-    dma_tile(K0, kbase, a.ksn, rows0, wave, lane);
-    dma_tile(V0, vbase, a.vsn, rows0, wave, lane);
-    if (tid < BLK) thr0_sh[tid] = thr0;
+    [&]<int... ks>(std::integer_sequence<int, ks...>) {
+      ((ks < total ? (issue.template operator()<ks>(ks), 0) : 0), ...);
+    }(std::make_integer_sequence<int, NS - 1>{});
   }
-  for (int it = 0; it < total; it += 2) {
-    // even tiles live in stage 0 (descriptor of it+1 in slot 1), odd in stage 1
-    step(it, K0, V0, thr0_sh, K1, V1, thr1_sh, desc0_sh, desc1_sh);
-    if (it + 1 < total) step(it + 1, K1, V1, thr1_sh, K0, V0, thr0_sh, desc1_sh, desc0_sh);
+  for (int it0 = 0; it0 < total; it0 += NS) {
+    [&]<int... ks>(std::integer_sequence<int, ks...>) {
+      ((it0 + ks < total ? (step.template operator()<ks>(it0 + ks), 0) : 0), ...);
+    }(std::make_integer_sequence<int, NS>{});
   }
 
   // ---- merge the two key halves (kh = 1 hands its state to kh = 0 via LDS)
@@ -483,8 +475,8 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
     l_run[rs] = l + xor32(l);
   }
   __syncthreads();  // every wave is past its last read of the stages
-  // [2 rh][2 rs][8 dt][64 lanes] f32x4: row half 0 in K0, row half 1 in V0 (16 KiB each)
-  float* xo = (float*)(rh == 0 ? K0 : V0);
+  // [2 rh][2 rs][8 dt][64 lanes] f32x4: 16 KiB per row half, in stage 0
+  float* xo = (float*)KV0 + rh * (2 * 8 * 64 * 4);
   if (kh == 1) {
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
@@ -552,8 +544,8 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.scale_log2 = scale * LOG2E;
   const dim3 grid((unsigned)(m->Hq * m->QB)), block(FWD_THREADS);
   if (dtype == VS_BF16 && D == 128) {
-    if (m->W > FWD_MAX_W) return VS_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
+    if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel<FWD_STAGES>, grid, block, 0, stream, a);
   }
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);

@@ -201,3 +201,39 @@ struct BlockTiles {
 };
 
 }  // namespace vs
+
+namespace vs {
+
+// Four transpose-read pairs (eight ds_read_b64_tr_b16, each pair 4 rows apart)
+// issued back to back with one LDS wait at the end. Issued as one asm block
+// so the compiler does not hold them behind outstanding global->LDS copies
+// into other stages (it cannot prove the intrinsic form does not alias them);
+// the block waits for its own results before returning them.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+// (p + 4 rows of a 256-byte-pitch tile = p + 1024 bytes)
+__device__ __forceinline__ void lds_read_tr16_x2_4(const bf16* p0, const bf16* p1, const bf16* p2, const bf16* p3,
+                                                   bf16x8* out) {
+  typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+  i32x2 r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2)), "v"(lds_addr(p3))
+      : "memory");
+  out[0] = __builtin_bit_cast(bf16x8, i32x4{r0[0], r0[1], r1[0], r1[1]});
+  out[1] = __builtin_bit_cast(bf16x8, i32x4{r2[0], r2[1], r3[0], r3[1]});
+  out[2] = __builtin_bit_cast(bf16x8, i32x4{r4[0], r4[1], r5[0], r5[1]});
+  out[3] = __builtin_bit_cast(bf16x8, i32x4{r6[0], r6[1], r7[0], r7[1]});
+}
+
+}  // namespace vs

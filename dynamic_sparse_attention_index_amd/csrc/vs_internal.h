@@ -29,7 +29,7 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
 
 int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, const float* lse,
                     const float* delta, const vs_mask* m, float scale, float* dq, float* dk, float* dv,
-                    hipStream_t stream);
+                    int parts, hipStream_t stream);
 
 size_t index_workspace_bytes(int Hq, int Hkv, int64_t n_global, int D, int last_q);
 

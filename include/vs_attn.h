@@ -212,6 +212,22 @@ int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout,
                 const float* lse, const float* delta, const vs_mask* m, float scale,
                 float* dq, float* dk, float* dv, void* stream);
 
+/* The same gradient in separately launchable parts (each one kernel), for
+ * callers that schedule them on different streams or time them apart:
+ *   VS_BWD_DQ    -- dq of the rank's rows (query-major over the tile lists);
+ *   VS_BWD_DKDV  -- dk/dv of the keys inside listed slash tiles (key-major
+ *                   over the CSC lists; plain read-modify-write);
+ *   VS_BWD_DKDV_VERT -- dk/dv of the vertical columns (fp32 atomics).
+ * `parts` is an OR of these; VS_BWD_ALL is vs_attn_bwd. Parts that write the
+ * same array (the two dk/dv parts) must not run concurrently. */
+#define VS_BWD_DQ 1
+#define VS_BWD_DKDV 2
+#define VS_BWD_DKDV_VERT 4
+#define VS_BWD_ALL 7
+int vs_attn_bwd_parts(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout,
+                      const float* lse, const float* delta, const vs_mask* m, float scale,
+                      float* dq, float* dk, float* dv, int parts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,7 @@ def _fwd_case(cfg, vert, slash, kind="contig", P=1, accumulate_steps=False):
         assert (gl[~fin] == -np.inf).all() and (go[~fin] == 0).all()
         lerr = np.abs(gl[fin] - ref_l[fin]).max() if fin.any() else 0.0
         worst = max(worst, err, lerr)
+        print(f"fwd {cfg.dtype} D={cfg.D} {kind} P={P} rank={rank}: max|dO|={err:.3e} max|dLSE|={lerr:.3e}")
         assert err <= TOL[cfg.dtype] and lerr <= TOL[cfg.dtype], (rank, err, lerr)
     return worst
 
@@ -158,6 +159,7 @@ def _bwd_case(cfg, vert, slash, kind="contig", P=1):
         cols = ol.shard_positions(kind, N, P, r)
         errs.append(np.abs(dk_all[r].cpu().numpy() - ref_dk[:, cols]).max())
         errs.append(np.abs(dv_all[r].cpu().numpy() - ref_dv[:, cols]).max())
+    print(f"bwd {cfg.dtype} D={cfg.D} {kind} P={P}: max errors (dq per rank, then dk, dv per shard) {errs}")
     assert max(errs) <= TOL[cfg.dtype], errs
     return errs
 
