@@ -58,7 +58,7 @@ class WorkloadConfig:
 # Shared-mean strengths calibrated per workload so that the oracle's mean
 # per-head sparsity is ~95% (python -m oracle.calibrate --config NAME).
 # Sparsity depends strongly on N at fixed c, hence one value per workload.
-C_STAR = {"qwen32k": 6.75, "qwen128k": 3.64, "qwen512k_cp32": 3.64, "llama256k": 3.64}
+C_STAR = {"qwen32k": 7.27, "qwen128k": 3.64, "qwen512k_cp32": 0.0, "llama256k": 0.0}
 
 CONFIGS = {
     "tiny": WorkloadConfig("tiny", 1, 1, 2048, 64, "f32", 8, 8.0, 0.0, 0.9, 1001),
