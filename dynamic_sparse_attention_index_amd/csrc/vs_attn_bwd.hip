@@ -152,8 +152,8 @@ __global__ void __launch_bounds__(BWD_THREADS) dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
   const int nitems = a.Hq * a.QB;
-  int item = blockIdx.x;
-  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
+  if (item < 0) return;
   const int I = a.QB - 1 - item / a.Hq;
   const int h = item % a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
@@ -294,9 +294,9 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
   const int nitems = a.Hkv * a.KB;
-  int item = blockIdx.x;
-  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
-  const int J = item % a.KB, kvh = item / a.KB;
+  const int item = xcd_cluster_item(blockIdx.x, nitems, kmajor_csize(a.Hkv));
+  if (item < 0) return;
+  const int J = item / a.Hkv, kvh = item % a.Hkv;
   const int grp = a.Hq / a.Hkv;
   const int keyoff = wave * 16 + n16;
   const int64_t krow = (int64_t)J * BLK + keyoff;
@@ -444,8 +444,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   const int g4 = lane >> 4, n16 = lane & 15;
   const int rh = wave & 1, kh = wave >> 1;
   const int nitems = a.Hq * a.QB;
-  int item = blockIdx.x;
-  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
+  if (item < 0) return;
   const int I = a.QB - 1 - item / a.Hq;
   const int h = item % a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
@@ -743,9 +743,9 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   const int g4 = lane >> 4, n16 = lane & 15;
   const int kh = wave >> 1, rh = wave & 1;
   const int nitems = a.Hkv * a.KB;
-  int item = blockIdx.x;
-  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
-  const int J = item % a.KB, kvh = item / a.KB;
+  const int item = xcd_cluster_item(blockIdx.x, nitems, kmajor_csize(a.Hkv));
+  if (item < 0) return;
+  const int J = item / a.Hkv, kvh = item % a.Hkv;
   const int grp = a.Hq / a.Hkv;
   // flattened (head, CSC entry) sequence of the group
   int cstart[8], cnt[8], total = 0;
@@ -961,9 +961,9 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
 template <typename T, int D>
 static void launch_bwd_typed(const BwdArgs& a, int parts, hipStream_t stream) {
   if (parts & VS_BWD_DQ)
-    hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<T, D>), dim3(xcd_cluster_grid(a.Hq * a.QB, qmajor_csize(a.Hq))), dim3(BWD_THREADS), 0, stream, a);
   if (parts & VS_BWD_DKDV)
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(xcd_cluster_grid(a.Hkv * a.KB, kmajor_csize(a.Hkv))), dim3(BWD_THREADS), 0, stream, a);
   if (parts & VS_BWD_DKDV_VERT)
     hipLaunchKernelGGL((dkdv_vert_kernel<T, D>), dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
 }
@@ -986,9 +986,9 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     if (a.Hq / a.Hkv > 8) return VS_ERR_UNSUPPORTED;
     if (parts & VS_BWD_DQ)
-      hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3((unsigned)(a.Hq * a.QB)), dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3(xcd_cluster_grid(a.Hq * a.QB, qmajor_csize(a.Hq))), dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV)
-      hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3((unsigned)(a.Hkv * a.KB)), dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3(xcd_cluster_grid(a.Hkv * a.KB, kmajor_csize(a.Hkv))), dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV_VERT)
       hipLaunchKernelGGL(dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
   }

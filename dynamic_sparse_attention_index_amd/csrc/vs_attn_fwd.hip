@@ -65,10 +65,10 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
-  // work item: heavy (late) query blocks first; contiguous item ranges per XCD
+  // work item: heavy (late) query blocks first, clustered per XCD
   const int nitems = a.Hq * a.QB;
-  int item = blockIdx.x;
-  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
+  if (item < 0) return;
   const int I = a.QB - 1 - item / a.Hq;
   const int h = item % a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
@@ -310,8 +310,8 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
   const int g4 = lane >> 4, n16 = lane & 15;
   const int rh = wave & 1, kh = wave >> 1;   // row half, key half
   const int nitems = a.Hq * a.QB;
-  int item = blockIdx.x;
-  if ((nitems & 7) == 0) item = (blockIdx.x & 7) * (nitems >> 3) + (blockIdx.x >> 3);
+  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
+  if (item < 0) return;
   const int I = a.QB - 1 - item / a.Hq;
   const int h = item % a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
@@ -542,7 +542,7 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
-  const dim3 grid((unsigned)(m->Hq * m->QB)), block(FWD_THREADS);
+  const dim3 grid(xcd_cluster_grid(m->Hq * m->QB, qmajor_csize(m->Hq))), block(FWD_THREADS);
   if (dtype == VS_BF16 && D == 128) {
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel<FWD_STAGES>, grid, block, 0, stream, a);

@@ -54,6 +54,28 @@ __device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// --- work order across XCDs ---------------------------------------------------
+// Callers number their work items heavy-first (causal work shrinks along the
+// item order). Items are taken in clusters of `csize` consecutive items and
+// cluster k runs on XCD k % 8 (the dispatcher deals blocks to the 8 XCDs
+// round-robin), so every XCD gets an even share of heavy and light clusters and
+// the blocks resident on one XCD at a time work on neighbouring items, whose
+// tiles its L2 then serves more than once. The grid is rounded up to whole
+// rounds of 8 clusters; blocks past the last item get -1 and return at once.
+__device__ __forceinline__ int xcd_cluster_item(int b, int nitems, int csize) {
+  const int x = b & 7, j = b >> 3;
+  const int item = ((j / csize) * 8 + x) * csize + j % csize;
+  return item < nitems ? item : -1;
+}
+__host__ inline unsigned xcd_cluster_grid(int nitems, int csize) {
+  const int nclusters = (nitems + csize - 1) / csize;
+  return (unsigned)(((nclusters + 7) / 8) * 8 * csize);
+}
+// Query-major kernels: 8 query blocks x all heads per cluster.
+__host__ __device__ __forceinline__ int qmajor_csize(int Hq) { return 8 * Hq; }
+// Key-major kernels: 8 key blocks x all kv heads per cluster.
+__host__ __device__ __forceinline__ int kmajor_csize(int Hkv) { return 8 * Hkv; }
+
 // --- layout maps -------------------------------------------------------------
 // Global 64-block of local block J of rank `rank` (NB = local blocks per shard).
 __device__ __host__ __forceinline__ int64_t global_block(int kind, int P, int NB, int rank, int J) {
