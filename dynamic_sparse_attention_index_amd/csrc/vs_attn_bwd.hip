@@ -440,7 +440,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   __shared__ int thr0_sh[BLK], thr1_sh[BLK], desc0_sh[BLK], desc1_sh[BLK];
   __shared__ uint32_t sbits[MAX_LDS_W];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int rh = wave & 1, kh = wave >> 1;
   const int nitems = a.Hq * a.QB;
@@ -454,8 +455,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
 
   BlockTiles bt;
   bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
-  bt.t0 = a.tile_ptr[u]; bt.nt = a.tile_ptr[u + 1] - bt.t0; bt.ve = a.vert_end[u];
-  bt.total = bt.nt + (bt.ve + BLK - 1) / BLK;
+  bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
   bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
   bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
   const int total = bt.total;
@@ -463,8 +463,26 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   const uint32_t* sbg = a.slash_bits + (int64_t)h * a.W;
   for (int w = tid; w < a.W; w += BWD_THREADS) sbits[w] = sbg[w];
 
-  const bf16* kbase = (const bf16*)a.k + kvh * a.ksh;
-  const bf16* vbase = (const bf16*)a.v + kvh * a.vsh;
+  const char* kbase = (const char*)((const bf16*)a.k + kvh * a.ksh);
+  const char* vbase = (const char*)((const bf16*)a.v + kvh * a.vsh);
+  const uint32_t krb = (uint32_t)a.ksn * 2, vrb = (uint32_t)a.vsn * 2;   // row pitch in bytes
+  const DmaLane dlane = dma_lane(wave, lane);
+  // start the copy of tile t into (Kn, Vn); its row thresholds go to thn
+  auto issue = [&](int t, const int* slot, bf16* Kn, bf16* Vn, int* thn) -> int {
+    int thr = tid, mode = 1;
+    if (!bt.vert(t)) {
+      const int r0 = bt.tile_row(slot, mode);
+      dma_tile_rows(Kn, kbase + (int64_t)r0 * krb, krb, dlane, wave);
+      dma_tile_rows(Vn, vbase + (int64_t)r0 * vrb, vrb, dlane, wave);
+    } else {
+      int rows[4];
+      bt.vert_rows(t, slot, rows, thr, wave, lane, tid);
+      dma_tile_gather(Kn, kbase, rows, krb, dlane, wave);
+      dma_tile_gather(Vn, vbase, rows, vrb, dlane, wave);
+    }
+    if (tid < BLK) thn[tid] = thr;
+    return mode;
+  };
   bf16x8 qf[2][4], df[2][4];
   float lse2[2], dl[2];
 #pragma unroll
@@ -492,12 +510,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
     __syncthreads();
     const int mode = mode_c;
     if (it + 1 < total) {
-      int rows_n[4], thr_n, mode_n;
-      bt.desc_decode(it + 1, dn_cur, rows_n, mode_n, thr_n, wave, lane, tid);
-      dma_tile(Kn, kbase, a.ksn, rows_n, wave, lane);
-      dma_tile(Vn, vbase, a.vsn, rows_n, wave, lane);
-      if (tid < BLK) thn[tid] = thr_n;
-      mode_c = mode_n;
+      mode_c = issue(it + 1, dn_cur, Kn, Vn, thn);
       if (it + 2 < total) bt.desc_copy(it + 2, dn_next, wave, lane);
     }
     // S^T and dP^T for keys 32 kh + 8 g + 4 t + i, rows 16 rs + n of the wave
@@ -551,13 +564,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   if (total > 1) bt.desc_copy(1, desc1_sh, wave, lane);
   wait_all_mem();
   __syncthreads();
-  {
-    int rows0[4], thr0;
-    bt.desc_decode(0, desc0_sh, rows0, mode_c, thr0, wave, lane, tid);
-    dma_tile(K0, kbase, a.ksn, rows0, wave, lane);
-    dma_tile(V0, vbase, a.vsn, rows0, wave, lane);
-    if (tid < BLK) thr0_sh[tid] = thr0;
-  }
+  mode_c = issue(0, desc0_sh, K0, V0, thr0_sh);
   for (int it = 0; it < total; it += 2) {
     step(it, K0, V0, thr0_sh, K1, V1, thr1_sh, desc0_sh, desc1_sh);
     if (it + 1 < total) step(it + 1, K1, V1, thr1_sh, K0, V0, thr0_sh, desc1_sh, desc0_sh);
@@ -657,12 +664,11 @@ __device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const f
 
 // Copy the Q and dO rows of query block I of head h and its lse/delta.
 __device__ __forceinline__ void stage_qblock(bf16* Qn, bf16* On, float* ln, const BwdArgs& a, int h, int I, int wave,
-                                             int lane) {
-  int rows[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) rows[c] = I * BLK + dma_local_row(wave, c, lane);
-  dma_tile(Qn, (const bf16*)a.q + h * a.qsh, a.qsn, rows, wave, lane);
-  dma_tile(On, (const bf16*)a.dout + h * a.dsh, a.dsn, rows, wave, lane);
+                                             int lane, const DmaLane& dl) {
+  const int64_t r0 = (int64_t)I * BLK;
+  const uint32_t qrb = (uint32_t)a.qsn * 2, orb = (uint32_t)a.dsn * 2;
+  dma_tile_rows(Qn, (const char*)((const bf16*)a.q + h * a.qsh + r0 * a.qsn), qrb, dl, wave);
+  dma_tile_rows(On, (const char*)((const bf16*)a.dout + h * a.dsh + r0 * a.dsn), orb, dl, wave);
   if (wave < 2) {
     const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)h * a.QB * BLK + (int64_t)I * BLK + lane;
     __builtin_amdgcn_global_load_lds((const void*)src,
@@ -739,7 +745,9 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   __shared__ __attribute__((aligned(16))) float L1[2 * BLK];
   __shared__ int desc0_sh[BLK], desc1_sh[BLK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const DmaLane dlane = dma_lane(wave, lane);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int kh = wave >> 1, rh = wave & 1;
   const int nitems = a.Hkv * a.KB;
@@ -798,7 +806,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
       int hh;
       entry_of(it + 1, hh);
       const int e = dn_cur[0];
-      stage_qblock(Qn, On, Ln, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane);
+      stage_qblock(Qn, On, Ln, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane, dlane);
       diag_c = (e & VS_TILE_DIAG) ? 1 : 0;
       if (it + 2 < total) desc_copy(it + 2, dn_next);
     }
@@ -816,7 +824,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
     int hh;
     entry_of(0, hh);
     const int e = desc0_sh[0];
-    stage_qblock(Q0, O0, L0, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane);
+    stage_qblock(Q0, O0, L0, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane, dlane);
     diag_c = (e & VS_TILE_DIAG) ? 1 : 0;
   }
   for (int it = 0; it < total; it += 2) {
@@ -846,7 +854,9 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
   bf16* O0 = QO0 + TILE_ELEMS;
   bf16* Q1 = QO1;
   bf16* O1 = QO1 + TILE_ELEMS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const DmaLane dlane = dma_lane(wave, lane);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int kh = wave >> 1, rh = wave & 1;
   const int nseg = (a.QB + VERT_SEG - 1) / VERT_SEG;
@@ -899,7 +909,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
     auto step = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, bf16* Qn, bf16* On, float* Ln) {
       wait_all_mem();
       __syncthreads();
-      if (it + 1 < total) stage_qblock(Qn, On, Ln, a, h, I_lo + it + 1, wave, lane);
+      if (it + 1 < total) stage_qblock(Qn, On, Ln, a, h, I_lo + it + 1, wave, lane, dlane);
       const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I_lo + it);
       int thr[2];
 #pragma unroll
@@ -910,7 +920,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
       }
       kv_block(Qs, Os, Ls, Ls + BLK, kf, vf, thr, kh, rh, g4, n16, sl2, acc_dk, acc_dv);
     };
-    stage_qblock(Q0, O0, L0, a, h, I_lo, wave, lane);
+    stage_qblock(Q0, O0, L0, a, h, I_lo, wave, lane, dlane);
     for (int it = 0; it < total; it += 2) {
       step(it, Q0, O0, L0, Q1, O1, L1);
       if (it + 1 < total) step(it + 1, Q1, O1, L1, Q0, O0, L0);
@@ -984,6 +994,10 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   a.scale = scale; a.scale_log2 = scale * LOG2E;
   if (dtype == VS_BF16 && D == 128) {
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
+    const int64_t krows = (int64_t)m->KB * BLK, qrows = (int64_t)m->QB * BLK;
+    if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn) || !dma_offsets_fit(qrows, q.sn) ||
+        !dma_offsets_fit(qrows, dout.sn))
+      return VS_ERR_UNSUPPORTED;
     if (a.Hq / a.Hkv > 8) return VS_ERR_UNSUPPORTED;
     if (parts & VS_BWD_DQ)
       hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3(xcd_cluster_grid(a.Hq * a.QB, qmajor_csize(a.Hq))), dim3(BWD_THREADS), 0, stream, a);

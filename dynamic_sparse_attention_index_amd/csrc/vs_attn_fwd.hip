@@ -306,7 +306,8 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
     else return KV3;
   };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int rh = wave & 1, kh = wave >> 1;   // row half, key half
   const int nitems = a.Hq * a.QB;
@@ -319,13 +320,14 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
   const int64_t row_base = (int64_t)I * BLK + 32 * rh;   // this wave's first query row
 
   const bf16* qb = (const bf16*)a.q + h * a.qsh;
-  const bf16* kbase = (const bf16*)a.k + kvh * a.ksh;
-  const bf16* vbase = (const bf16*)a.v + kvh * a.vsh;
+  const char* kbase = (const char*)((const bf16*)a.k + kvh * a.ksh);
+  const char* vbase = (const char*)((const bf16*)a.v + kvh * a.vsh);
+  const uint32_t krb = (uint32_t)a.ksn * 2, vrb = (uint32_t)a.vsn * 2;   // row pitch in bytes
+  const DmaLane dl = dma_lane(wave, lane);
 
   BlockTiles bt;
   bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
-  bt.t0 = a.tile_ptr[u]; bt.nt = a.tile_ptr[u + 1] - bt.t0; bt.ve = a.vert_end[u];
-  bt.total = bt.nt + (bt.ve + BLK - 1) / BLK;
+  bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
   bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
   bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
   const int total = bt.total;
@@ -352,11 +354,18 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
 
   // decode the descriptor of tile t (slot t % NS) and start its copy into stage nk
   auto issue = [&]<int nk>(int t) {
-    int rows[4], thr, mode;
-    bt.desc_decode(t, desc_sh[nk], rows, mode, thr, wave, lane, tid);
     bf16* st = stage.template operator()<nk>();
-    dma_tile(st, kbase, a.ksn, rows, wave, lane);
-    dma_tile(st + TILE_ELEMS, vbase, a.vsn, rows, wave, lane);
+    int thr = tid, mode = 1;
+    if (!bt.vert(t)) {
+      const int r0 = bt.tile_row(desc_sh[nk], mode);
+      dma_tile_rows(st, kbase + (int64_t)r0 * krb, krb, dl, wave);
+      dma_tile_rows(st + TILE_ELEMS, vbase + (int64_t)r0 * vrb, vrb, dl, wave);
+    } else {
+      int rows[4];
+      bt.vert_rows(t, desc_sh[nk], rows, thr, wave, lane, tid);
+      dma_tile_gather(st, kbase, rows, krb, dl, wave);
+      dma_tile_gather(st + TILE_ELEMS, vbase, rows, vrb, dl, wave);
+    }
     if (tid < BLK) thr_sh[nk][tid] = thr;
     mode_st[nk] = mode;
   };
@@ -405,8 +414,7 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
     for (int rs = 0; rs < 2; ++rs) {
       float mx = fmaxf(fmaxf(fmaxf(s[rs][0][0], s[rs][0][1]), fmaxf(s[rs][0][2], s[rs][0][3])),
                        fmaxf(fmaxf(s[rs][1][0], s[rs][1][1]), fmaxf(s[rs][1][2], s[rs][1][3])));
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
+      mx = group4_max(mx);
       // Exact running max: the largest probability of the row is then exactly
       // 1 in bf16, which keeps the dominant term of O free of rounding (a
       // stale reference doubles the O error on peaked rows).
@@ -471,8 +479,7 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
   // ---- merge the two key halves (kh = 1 hands its state to kh = 0 via LDS)
 #pragma unroll
   for (int rs = 0; rs < 2; ++rs) {
-    const float l = l_run[rs] + xor16(l_run[rs]);
-    l_run[rs] = l + xor32(l);
+    l_run[rs] = group4_sum(l_run[rs]);
   }
   __syncthreads();  // every wave is past its last read of the stages
   // [2 rh][2 rs][8 dt][64 lanes] f32x4: 16 KiB per row half, in stage 0
@@ -545,6 +552,8 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   const dim3 grid(xcd_cluster_grid(m->Hq * m->QB, qmajor_csize(m->Hq))), block(FWD_THREADS);
   if (dtype == VS_BF16 && D == 128) {
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
+    const int64_t krows = (int64_t)m->KB * BLK;
+    if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel<FWD_STAGES>, grid, block, 0, stream, a);
   }
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);

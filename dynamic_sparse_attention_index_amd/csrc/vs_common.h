@@ -154,12 +154,76 @@ __device__ __forceinline__ void dma_tile(bf16* lds_tile, const bf16* gbase, int6
                                      16, 0, 0);
   }
 }
+// The same copy with the address split into a wave-uniform part (tile base,
+// 64-bit, scalar registers) and a 32-bit per-lane part, so no per-piece
+// 64-bit multiply is spent on it. Lane L of wave w carries local rows
+// r_c = r0 + 16 c with r0 = 4 w + L / 16 < 16; the swizzle of r_c is that of
+// r0 with bit 0 set to c & 1, so a lane needs two column offsets only.
+// `wave` must be wave-uniform (readfirstlane) for the LDS side to stay scalar.
+struct DmaLane {
+  uint32_t r0;          // local row of the c = 0 piece
+  uint32_t col[2];      // byte offset of the swizzled 16-byte column, c even / odd
+};
+__device__ __forceinline__ DmaLane dma_lane(int wave, int lane) {
+  DmaLane d;
+  d.r0 = 4 * wave + (lane >> 4);
+  const int sw = tile_swz((int)d.r0);
+  d.col[0] = (((lane & 15) ^ sw) << 4);
+  d.col[1] = (((lane & 15) ^ sw ^ 1) << 4);
+  return d;
+}
+__device__ __forceinline__ void dma_copy16(const char* g, bf16* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)g,
+                                   (__attribute__((address_space(3))) void*)(
+                                       (__attribute__((address_space(3))) bf16*)(lds)),
+                                   16, 0, 0);
+}
+// 64 consecutive rows starting at `tile` (wave-uniform), row pitch row_bytes.
+__device__ __forceinline__ void dma_tile_rows(bf16* lds_tile, const char* tile, uint32_t row_bytes, const DmaLane& d,
+                                              int wave) {
+  const uint32_t lo = d.r0 * row_bytes;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    dma_copy16(tile + (size_t)(16 * c) * row_bytes + (lo + d.col[c & 1]), lds_tile + (wave + 4 * c) * 512);
+}
+// 64 gathered rows of `base` (wave-uniform): this lane's pieces come from rows
+// src_row[c]. Offsets are 32-bit and the row product 24-bit: the caller keeps
+// rows and row_bytes below 2^24 and rows * row_bytes below 2^32.
+__device__ __forceinline__ void dma_tile_gather(bf16* lds_tile, const char* base, const int* src_row,
+                                                uint32_t row_bytes, const DmaLane& d, int wave) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    dma_copy16(base + (__umul24((uint32_t)src_row[c], row_bytes) + d.col[c & 1]), lds_tile + (wave + 4 * c) * 512);
+}
+// Host check for the 32-bit tile-copy offsets: a bf16 view of `rows` rows
+// with row pitch `row_stride` elements keeps rows and the pitch in bytes
+// below 2^24 and their product below 2^32.
+__host__ inline bool dma_offsets_fit(int64_t rows, int64_t row_stride) {
+  const int64_t rb = row_stride * 2;
+  return rows < (1 << 24) && rb < (1 << 24) && rows * rb < (int64_t(1) << 32);
+}
 // Wait for this wave's outstanding memory operations (incl. LDS copies).
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Cross-lane exchange between the four 16-lane groups of a wave.
 __device__ __forceinline__ float xor16(float v) { return __shfl_xor(v, 16, 64); }
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Max / sum over lanes n, n + 16, n + 32, n + 48 (result in all four), with
+// the gfx950 row swaps: swapping 16-lane rows (then 32-lane halves) between
+// two copies of a value leaves each lane holding its own value and its
+// partner's, in one order or the other, so a symmetric op needs no select.
+__device__ __forceinline__ float group4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // Round 8 fp32 weights to a bf16 pair (hi = bf16(w), lo = bf16(w - hi)).
 __device__ __forceinline__ void split_bf16(float w, bf16& hi, bf16& lo) {
@@ -186,38 +250,48 @@ struct BlockTiles {
   const int32_t* tile_col;
   const int32_t* vl;          // the shard's vertical columns of this head
   const uint32_t* sbits;      // LDS copy of the head's slash bitmap
-  int t0, nt, ve, total;
+  int t0, nt, ve, nvc, total;
   int64_t G;                  // global block of the query block
   int kind, P, KB, src;
 
+  // Tile order: the nvc vertical chunks first, then the listed tiles from the
+  // query block's own diagonal outwards (the list holds them far to near).
+  // The largest scores of a row usually sit in the sink / outlier columns or
+  // next to the diagonal, so the online-softmax reference is set by the first
+  // tiles and the O rescale is rarely needed afterwards.
+  __device__ __forceinline__ void init(int t0_, int t1_, int ve_) {
+    t0 = t0_; nt = t1_ - t0_; ve = ve_;
+    nvc = (ve + BLK - 1) / BLK;
+    total = nt + nvc;
+  }
+  __device__ __forceinline__ bool vert(int it) const { return it < nvc; }
   __device__ __forceinline__ void desc_copy(int it, int* slot, int wave, int lane) const {
     if (wave != 0) return;
-    const int32_t* s = (it < nt) ? tile_col + t0 + it : vl + min((it - nt) * BLK + lane, ve - 1);
+    const int32_t* s = vert(it) ? vl + min(it * BLK + lane, ve - 1) : tile_col + t0 + (nt - 1 - (it - nvc));
     __builtin_amdgcn_global_load_lds((const void*)s,
                                      (__attribute__((address_space(3))) void*)(
                                          (__attribute__((address_space(3))) int*)(slot)),
                                      4, 0, 0);
   }
-  __device__ __forceinline__ void desc_decode(int it, const int* slot, int* rows, int& mode, int& thr, int wave,
-                                              int lane, int tid) const {
-    if (it < nt) {
-      const int e = slot[0];
-      const int J = e & VS_TILE_MASK;
-      mode = (e & VS_TILE_DIAG) ? 1 : 0;
+  // Listed tile: its first key row (wave-uniform) and whether it is the
+  // diagonal tile (mode 1: key k active for rows >= k).
+  __device__ __forceinline__ int tile_row(const int* slot, int& mode) const {
+    const int e = __builtin_amdgcn_readfirstlane(slot[0]);
+    mode = (e & VS_TILE_DIAG) ? 1 : 0;
+    return (e & VS_TILE_MASK) * BLK;
+  }
+  // Vertical chunk `it`: the key rows of this lane's copy pieces and, for
+  // tid < BLK, the key's row threshold (rows below it are inactive: the causal
+  // edge, and columns already covered by a listed tile of this block).
+  __device__ __forceinline__ void vert_rows(int it, const int* slot, int* rows, int& thr, int wave, int lane,
+                                            int tid) const {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) rows[c] = J * BLK + dma_local_row(wave, c, lane);
-      thr = tid;
-    } else {
-      const int base = (it - nt) * BLK;
-      mode = 1;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
-      thr = BLK;
-      if (tid < BLK && base + tid < ve) {
-        const int m = slot[tid];
-        const int64_t j = G - global_block(kind, P, KB, src, m / BLK);
-        if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
-      }
+    for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+    thr = BLK;
+    if (tid < BLK && it * BLK + tid < ve) {
+      const int m = slot[tid];
+      const int64_t j = G - global_block(kind, P, KB, src, m / BLK);
+      if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
     }
   }
 };
