@@ -25,10 +25,6 @@
 namespace vs {
 
 constexpr int FWD_THREADS = 256;  // 4 waves
-#ifndef VS_FWD_STAGES
-#define VS_FWD_STAGES 2
-#endif
-constexpr int FWD_STAGES = VS_FWD_STAGES;   // LDS pipeline depth of the bf16 forward
 
 struct FwdArgs {
   const void* q; const void* k; const void* v;
@@ -280,30 +276,38 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 // one half (32 keys) of every 64-key tile, so a K/V fragment read from LDS
 // feeds two MFMAs and a wave reads only its half of the tile; the two key
 // halves keep separate online-softmax states, merged through LDS at the end
-// (the same log-sum-exp merge as across ring steps). Tiles stream into two
-// LDS stages with asynchronous global->LDS copies issued one tile ahead, so
-// each tile costs one barrier. Row indices of gathered vertical chunks and
-// list entries are loaded one more tile ahead.
-template <int NS>
-__global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
+// (the same log-sum-exp merge as across ring steps).
+//
+// Software pipeline: step i computes S for tile i + 1 (an MFMA chain that
+// does not depend on the softmax) together with the softmax and P.V of tile
+// i, so the matrix cores and the vector ALU work at the same time. K tiles
+// are therefore staged one tile ahead of V tiles: during step i LDS holds
+// K[i+1] (being read), V[i] (being read), and receives K[i+2] and V[i+1]
+// through asynchronous global->LDS copies, in two K and two V stages (64 KiB,
+// two workgroups per CU). Descriptors (list entries or gathered vertical
+// rows) arrive one step before the K copy that needs them; what the V copy
+// needs (the same descriptor, read again) stays in LDS in between.
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
   constexpr int D = TD;
-  // NS LDS stages, each (K tile, V tile) in an array of its own, and the loop
-  // unrolled by NS, so the compiler can tell the stage being read from the
-  // stages being filled and lets the copies run under the compute; NS - 1
-  // tiles are in flight. After the loop stage 0 carries the key-half exchange.
-  __shared__ __attribute__((aligned(16))) bf16 KV0[2 * TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 KV1[2 * TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 KV2[2 * TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 KV3[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 V1[TILE_ELEMS];
   __shared__ float xs[2 * 2 * 64 * 2];
-  __shared__ int thr_sh[NS][BLK];
-  __shared__ int desc_sh[NS][BLK];
+  // descriptor and row thresholds of tile t live in slot t % 3 from the
+  // descriptor copy (step t - 3) to the softmax (step t)
+  __shared__ int thr_sh[3][BLK];
+  __shared__ int desc_sh[3][BLK];
   __shared__ uint32_t sbits[MAX_LDS_W];
-  auto stage = [&]<int k>() -> bf16* {
-    if constexpr (k == 0) return KV0;
-    else if constexpr (k == 1) return KV1;
-    else if constexpr (k == 2) return KV2;
-    else return KV3;
+  // stages are chosen at compile time (the loop is unrolled by two) so the
+  // compiler can tell the stages being read from the ones being filled
+  auto Kst = [&]<int p>() -> bf16* {
+    if constexpr (p == 0) return K0;
+    else return K1;
+  };
+  auto Vst = [&]<int p>() -> bf16* {
+    if constexpr (p == 0) return V0;
+    else return V1;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -348,42 +352,44 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
     for (int dt = 0; dt < 8; ++dt) acc[rs][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float sl2 = a.scale_log2;
-  int mode_st[NS];
-#pragma unroll
-  for (int k = 0; k < NS; ++k) mode_st[k] = 0;
 
-  // decode the descriptor of tile t (slot t % NS) and start its copy into stage nk
-  auto issue = [&]<int nk>(int t) {
-    bf16* st = stage.template operator()<nk>();
-    int thr = tid, mode = 1;
+  int mode_pend = 0;   // mode of the tile whose V copy was started last
+
+  // start the K copy of tile t into K stage p and record its row thresholds
+  auto issue_k = [&]<int p>(int t) {
+    bf16* ks = Kst.template operator()<p>();
+    const int* slot = desc_sh[t % 3];
+    int thr = tid;
     if (!bt.vert(t)) {
-      const int r0 = bt.tile_row(desc_sh[nk], mode);
-      dma_tile_rows(st, kbase + (int64_t)r0 * krb, krb, dl, wave);
-      dma_tile_rows(st + TILE_ELEMS, vbase + (int64_t)r0 * vrb, vrb, dl, wave);
+      int mode;
+      const int r0 = bt.tile_row(slot, mode);
+      dma_tile_rows(ks, kbase + (int64_t)r0 * krb, krb, dl, wave);
     } else {
       int rows[4];
-      bt.vert_rows(t, desc_sh[nk], rows, thr, wave, lane, tid);
-      dma_tile_gather(st, kbase, rows, krb, dl, wave);
-      dma_tile_gather(st + TILE_ELEMS, vbase, rows, vrb, dl, wave);
+      bt.vert_rows(t, slot, rows, thr, wave, lane, tid);
+      dma_tile_gather(ks, kbase, rows, krb, dl, wave);
     }
-    if (tid < BLK) thr_sh[nk][tid] = thr;
-    mode_st[nk] = mode;
+    if (tid < BLK) thr_sh[t % 3][tid] = thr;
   };
-
-  // One tile in stage k: wait for its copy, start the copy of tile it+NS-1
-  // and the descriptor copy of tile it+NS, compute.
-  auto step = [&]<int k>(int it) {
-    constexpr int nk = (k + NS - 1) % NS;
-    wait_all_mem();
-    __syncthreads();  // tile `it` and descriptor it+NS-1 have landed; tile it-1 is done
-    if (it + NS - 1 < total) issue.template operator()<nk>(it + NS - 1);
-    if (it + NS < total) bt.desc_copy(it + NS, desc_sh[k], wave, lane);
-    const bf16* Ks = stage.template operator()<k>();
-    const bf16* Vs = Ks + TILE_ELEMS;
-    const int mode = mode_st[k];
-    // S^T for 32 keys (this wave's half) x 32 rows: s[rs][t] lane (g, n):
-    // S[row 16 rs + n][key 32 kh + 8 g + 4 t + i]
-    f32x4 s[2][2];
+  // start the V copy of tile t into V stage p (descriptor read again)
+  auto issue_v = [&]<int p>(int t) {
+    bf16* vs_ = Vst.template operator()<p>();
+    const int* slot = desc_sh[t % 3];
+    if (!bt.vert(t)) {
+      const int r0 = bt.tile_row(slot, mode_pend);
+      dma_tile_rows(vs_, vbase + (int64_t)r0 * vrb, vrb, dl, wave);
+    } else {
+      int rows[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+      dma_tile_gather(vs_, vbase, rows, vrb, dl, wave);
+      mode_pend = 1;
+    }
+  };
+  // S^T for 32 keys (this wave's half) x 32 rows from K stage p: s[rs][t]
+  // lane (g, n) = S[row 16 rs + n][key 32 kh + 8 g + 4 t + i]
+  auto qk = [&]<int p>(f32x4 (&s)[2][2]) {
+    const bf16* Ks = Kst.template operator()<p>();
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int kr = 32 * kh + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
@@ -396,12 +402,18 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
         for (int rs = 0; rs < 2; ++rs) s[rs][t] = mfma_bf16(kf, qf[rs][ks], s[rs][t]);
       }
     }
+  };
+  // online softmax of S (thresholds in slot p when mode is set) and
+  // O^T += V^T P^T from V stage p
+  // S of the next tile (from K stage pk) is computed inside the branch-free
+  // exponential section so its MFMAs interleave with the vector work.
+  auto softmax_pv = [&]<int p, int pk>(f32x4 (&s)[2][2], int mode, const int* thr, f32x4 (&s_next)[2][2]) {
     if (mode) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int th = thr_sh[k][32 * kh + 8 * g4 + 4 * t + i];
+          const int th = thr[32 * kh + 8 * g4 + 4 * t + i];
 #pragma unroll
           for (int rs = 0; rs < 2; ++rs)
             if (th > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
@@ -409,7 +421,7 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
     }
     bf16x8 pf[2];
     bool rescale = false;
-    float alpha[2];
+    float alpha[2], m_use[2];
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
       float mx = fmaxf(fmaxf(fmaxf(s[rs][0][0], s[rs][0][1]), fmaxf(s[rs][0][2], s[rs][0][3])),
@@ -421,19 +433,9 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
       const float mt = mx * sl2;
       const bool up = mt > m_run[rs];
       const float m_new = up ? mt : m_run[rs];
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha[rs] = up ? __builtin_amdgcn_exp2f(m_run[rs] - m_use) : 1.f;
+      m_use[rs] = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha[rs] = up ? __builtin_amdgcn_exp2f(m_run[rs] - m_use[rs]) : 1.f;
       rescale |= up;
-      float psum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -m_use));
-          psum += p;
-          pf[rs][4 * t + i] = (bf16)p;
-        }
-      l_run[rs] = l_run[rs] * alpha[rs] + psum;
       m_run[rs] = m_new;
     }
     if (__builtin_amdgcn_ballot_w64(rescale)) {
@@ -444,7 +446,28 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[rs][dt][i] *= alpha[rs];
     }
-    // O^T += V^T P^T over this wave's 32 keys (one 32-deep contraction)
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -m_use[rs]));
+          psum += pr;
+          pf[rs][4 * t + i] = (bf16)pr;
+        }
+      l_run[rs] = l_run[rs] * alpha[rs] + psum;
+    }
+    qk.template operator()<pk>(s_next);
+    // 8 K-fragment reads, then one MFMA of the next S per three vector ops
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    const bf16* Vs = Vst.template operator()<p>();
     const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
     const int vb = (n16 & 3) >> 1, vo = 4 * (n16 & 1);
 #pragma unroll
@@ -459,31 +482,50 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
     }
   };
 
-  if (total > 0) {
-    // descriptors of tiles 0 .. NS-1, then the copies of tiles 0 .. NS-2
+  f32x4 s_cur[2][2];
+  // step i (stage parity p = i % 2): S of tile i is in s_cur, K[i+1] in K
+  // stage 1-p, V[i] in V stage p, descriptor i+2 in slot (i+2) % 3.
+  auto step = [&]<int p>(int i) {
+    constexpr int q = 1 - p;
+    wait_all_mem();
+    __syncthreads();   // copies issued in step i-1 have landed; step i-1 is done everywhere
+    const int mode_i = mode_pend;
+    if (i + 1 < total) issue_v.template operator()<q>(i + 1);
+    if (i + 2 < total) issue_k.template operator()<p>(i + 2);
+    if (i + 3 < total) bt.desc_copy(i + 3, desc_sh[i % 3], wave, lane);
+    // (the last step computes a next S from a stale stage and drops it)
+    f32x4 s_next[2][2];
+    softmax_pv.template operator()<p, q>(s_cur, mode_i, thr_sh[i % 3], s_next);
 #pragma unroll
-    for (int t = 0; t < NS; ++t)
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s_cur[rs][t] = s_next[rs][t];
+  };
+
+  if (total > 0) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
       if (t < total) bt.desc_copy(t, desc_sh[t], wave, lane);
     wait_all_mem();
     __syncthreads();
-    [&]<int... ks>(std::integer_sequence<int, ks...>) {
-      ((ks < total ? (issue.template operator()<ks>(ks), 0) : 0), ...);
-    }(std::make_integer_sequence<int, NS - 1>{});
+    issue_k.template operator()<0>(0);
+    issue_v.template operator()<0>(0);
+    if (total > 1) issue_k.template operator()<1>(1);
+    wait_all_mem();
+    __syncthreads();
+    qk.template operator()<0>(s_cur);
   }
-  for (int it0 = 0; it0 < total; it0 += NS) {
-    [&]<int... ks>(std::integer_sequence<int, ks...>) {
-      ((it0 + ks < total ? (step.template operator()<ks>(it0 + ks), 0) : 0), ...);
-    }(std::make_integer_sequence<int, NS>{});
+  for (int i0 = 0; i0 < total; i0 += 2) {
+    step.template operator()<0>(i0);
+    if (i0 + 1 < total) step.template operator()<1>(i0 + 1);
   }
 
   // ---- merge the two key halves (kh = 1 hands its state to kh = 0 via LDS)
 #pragma unroll
-  for (int rs = 0; rs < 2; ++rs) {
-    l_run[rs] = group4_sum(l_run[rs]);
-  }
+  for (int rs = 0; rs < 2; ++rs) l_run[rs] = group4_sum(l_run[rs]);
   __syncthreads();  // every wave is past its last read of the stages
-  // [2 rh][2 rs][8 dt][64 lanes] f32x4: 16 KiB per row half, in stage 0
-  float* xo = (float*)KV0 + rh * (2 * 8 * 64 * 4);
+  // [2 rs][8 dt][64 lanes] f32x4 = 16 KiB per row half: K stage 0 / V stage 0
+  float* xo = (float*)(rh == 0 ? K0 : V0);
   if (kh == 1) {
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
@@ -510,6 +552,8 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
     const int64_t grow = row_base + 16 * rs + n16;
     float* orow = a.o + ((int64_t)h * a.QB * BLK + grow) * D;
     float* lrow = a.lse + (int64_t)h * a.QB * BLK + grow;
+    // O and LSE are written once and not read again by this kernel: stream
+    // them past the caches (non-temporal) so they do not evict K/V tiles
     float ca = 0.f, cb = inv;
     if (a.accumulate) {
       const float lse_old = *lrow;
@@ -534,7 +578,7 @@ __global__ void __launch_bounds__(FWD_THREADS, NS >= 3 ? 1 : 2) attn_fwd_bf16_d1
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[i] += ca * old[i];
       }
-      *(f32x4*)(orow + 16 * dt + 4 * g4) = r;
+      __builtin_nontemporal_store(r, (f32x4*)(orow + 16 * dt + 4 * g4));
     }
   }
 }
@@ -554,7 +598,7 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     const int64_t krows = (int64_t)m->KB * BLK;
     if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel<FWD_STAGES>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
   }
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);
