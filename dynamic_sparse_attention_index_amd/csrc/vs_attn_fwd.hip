@@ -419,7 +419,10 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
             if (th > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
         }
     }
-    bf16x8 pf[2];
+    // P as a hi + lo bf16 pair (two MFMAs per product): with bf16 P alone the
+    // O error (a few 1e-3) passes into delta = rowsum(dO * O) and from there,
+    // scaled by large outlier keys, into dQ beyond the 2e-2 bound
+    bf16x8 pf[2], pl[2];
     bool rescale = false;
     float alpha[2], m_use[2];
 #pragma unroll
@@ -455,7 +458,10 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
         for (int i = 0; i < 4; ++i) {
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -m_use[rs]));
           psum += pr;
-          pf[rs][4 * t + i] = (bf16)pr;
+          bf16 hi, lo;
+          split_bf16(pr, hi, lo);
+          pf[rs][4 * t + i] = hi;
+          pl[rs][4 * t + i] = lo;
         }
       l_run[rs] = l_run[rs] * alpha[rs] + psum;
     }
@@ -478,7 +484,10 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-        for (int rs = 0; rs < 2; ++rs) acc[rs][4 * q + d4] = mfma_bf16(va[d4], pf[rs], acc[rs][4 * q + d4]);
+        for (int rs = 0; rs < 2; ++rs) {
+          acc[rs][4 * q + d4] = mfma_bf16(va[d4], pf[rs], acc[rs][4 * q + d4]);
+          acc[rs][4 * q + d4] = mfma_bf16(va[d4], pl[rs], acc[rs][4 * q + d4]);
+        }
     }
   };
 

@@ -1,0 +1,273 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times, checked on sampled outputs against the fp64 oracle.
+
+Both sides use the oracle's index (computed here from the synthetic inputs),
+so the attention comparison does not depend on ties at the top-p budget edge;
+the GPU index itself is compared with the oracle's separately (same rule as
+the small index tests). Checked per workload:
+  * O, LSE and dQ of seeded query blocks (first, last, random) against the
+    oracle's attention over each row's whole active key set;
+  * dK and dV of the last key blocks: keys there are attended only by rows
+    at or after them, so the oracle gets their exact gradients from those
+    few rows (slash tiles and vertical columns both contribute).
+The ring case runs one rank's full ring (every step) at P = 32.
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oa
+from oracle import index as oi
+from oracle import layout as ol
+from oracle import mask as om
+from synth import config_by_name, generate
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2   # bf16 inputs, fp32 outputs (absolute)
+
+
+def _log(msg):
+    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def _oracle_index(t, cfg):
+    N = cfg.N
+    ref = oi.build_index(t["q"][:, N - cfg.last_q:], t["k"], cfg.scale, N, cfg.top_p)
+    return ref
+
+
+def _candidate_cols(rows, vert_h, slash_h):
+    """A superset of the keys the rows can attend (their verticals and the key
+    blocks on their selected block diagonals, up to the last row); the oracle's
+    active() is then evaluated on these columns only (exact: every other
+    column is inactive by definition)."""
+    qb = np.unique(rows // 64)
+    kb = np.unique((qb[:, None] - np.asarray(slash_h, dtype=np.int64)[None, :]).ravel())
+    kb = kb[kb >= 0]
+    cols = np.concatenate([np.asarray(vert_h, dtype=np.int64), (kb[:, None] * 64 + np.arange(64)[None, :]).ravel()])
+    cols = np.unique(cols)
+    return cols[cols <= rows.max()]
+
+
+def _rows_check(t, cfg, vert, slash, rows_of, got, heads, blocks):
+    """O / LSE / dQ of query blocks `blocks` (rows_of(I) -> global rows) of `heads`."""
+    Hq, Hkv = cfg.Hq, cfg.Hkv
+    worst = {"o": 0.0, "lse": 0.0, "dq": 0.0}
+    for h in heads:
+        g = h * Hkv // Hq
+        for I in blocks:
+            rows = rows_of(I)
+            cand = _candidate_cols(rows, vert[h], slash[h])
+            M, _, _ = om.active(rows, cand, vert[h], slash[h])
+            used = cand[M.any(axis=0)]
+            M = M[:, M.any(axis=0)]
+            q, do = t["q"][h, rows], t["do"][h, rows]
+            k, v = t["k"][g, used], t["v"][g, used]
+            o, lse = oa.forward_rows(q, k, v, M, cfg.scale)
+            dq, _, _ = oa.backward_rows(q, k, v, M, cfg.scale, do)
+            fin = np.isfinite(lse)
+            sl = slice(64 * I, 64 * I + 64)
+            worst["o"] = max(worst["o"], float(np.abs(got["o"][h, sl] - o).max()))
+            worst["lse"] = max(worst["lse"], float(np.abs(got["lse"][h, sl][fin] - lse[fin]).max()) if fin.any() else 0.0)
+            worst["dq"] = max(worst["dq"], float(np.abs(got["dq"][h, sl] - dq).max()))
+    return worst
+
+
+def _tail_active(cfg, vert, slash, row_lo, rows_filter=None):
+    """Estimate of the active (row, key) pairs with both at or after row_lo:
+    slash tiles of the window's row blocks plus vertical columns in it (rows
+    filtered block by block; the layouts keep 64-row blocks whole)."""
+    N = cfg.N
+    J0, QB = row_lo // 64, N // 64
+    Ib = np.arange(J0, QB)
+    w = np.ones(len(Ib)) if rows_filter is None else rows_filter(Ib * 64).astype(float)
+    total = 0.0
+    for h in range(cfg.Hq):
+        sh = np.sort(np.asarray(slash[h]))
+        total += 4096.0 * (w * np.searchsorted(sh, Ib - J0, side="right")).sum()
+        vm = np.asarray(vert[h])
+        vm = vm[vm >= row_lo]
+        total += float((N - vm).sum()) * w.mean()
+    return int(total)
+
+
+def _tail_start(cfg, vert, slash, first_blocks, rows_filter=None, need=4096, max_blocks=512):
+    """Start of the tail window: the last `first_blocks` key blocks, doubled
+    until the window holds at least `need` active entries (so the dK/dV check
+    is not vacuous when the last blocks are attended by nobody)."""
+    nb = first_blocks
+    while True:
+        row_lo = cfg.N - 64 * nb
+        cnt = _tail_active(cfg, vert, slash, row_lo, rows_filter)
+        if cnt >= need or nb >= max_blocks:
+            return row_lo, cnt
+        nb *= 2
+
+
+def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None):
+    """dK / dV of keys at global positions >= row_lo: exact contributions of the
+    rows at or after row_lo (optionally only those passing rows_filter)."""
+    Hq, Hkv, N = cfg.Hq, cfg.Hkv, cfg.N
+    rows = np.arange(row_lo, N)
+    if rows_filter is not None:
+        rows = rows[rows_filter(rows)]
+    keys = np.arange(row_lo, N)
+    ref_dk = np.zeros((Hkv, len(keys), cfg.D))
+    ref_dv = np.zeros((Hkv, len(keys), cfg.D))
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        if len(rows) == 0:
+            continue
+        cand = _candidate_cols(rows, vert[h], slash[h])
+        M, _, _ = om.active(rows, cand, vert[h], slash[h])
+        used = cand[M.any(axis=0)]
+        _, dk, dv = oa.backward_rows(t["q"][h, rows], t["k"][g, used], t["v"][g, used], M[:, M.any(axis=0)],
+                                     cfg.scale, t["do"][h, rows])
+        sel = used >= row_lo
+        ref_dk[g, used[sel] - row_lo] += dk[sel]
+        ref_dv[g, used[sel] - row_lo] += dv[sel]
+    return (float(np.abs(dk_of(keys) - ref_dk).max()), float(np.abs(dv_of(keys) - ref_dv).max()))
+
+
+def _contig_case(name):
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    cfg = config_by_name(name)
+    N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    T = N // 64
+    _log(f"{name}: generating N={N} Hq={Hq} Hkv={Hkv}")
+    t = generate(cfg)
+    _log(f"{name}: oracle index")
+    ref = _oracle_index(t, cfg)
+    dev = "cuda"
+    q, k, v, do = (H.to_dev(t[x], cfg.dtype) for x in ("q", "k", "v", "do"))
+    lay = vs.layout("contig", 1, N)
+    _log(f"{name}: GPU index vs oracle index")
+    H.check_index(H.gpu_index(q[:, N - cfg.last_q:], k, lay, cfg.scale, cfg.top_p), ref, cfg.top_p)
+    vert, slash = ref["vert"], ref["slash"]
+    _log(f"{name}: GPU mask + forward + backward (oracle index)")
+    m = H.gpu_mask(H.upload_lists(vert, slash, N), Hq, Hkv, lay, 0, 0, H.tile_cap_for(slash, Hq, T))
+    assert int(m.arrays()["status"].item()) == 0
+    o = torch.empty(Hq, N, D, device=dev)
+    lse = torch.empty(Hq, N, device=dev)
+    delta = torch.empty(Hq, N, device=dev)
+    dq = torch.zeros(Hq, N, D, device=dev)
+    dk = torch.zeros(Hkv, N, D, device=dev)
+    dv = torch.zeros(Hkv, N, D, device=dev)
+    vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse)
+    vs.vs_attn_bwd_prep(o, do, delta)
+    vs.vs_attn_bwd(q, k, v, do, lse, delta, m, cfg.scale, dq, dk, dv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg.seed + 77)
+    heads = sorted(set([0, Hq - 1] + rng.choice(Hq, 2, replace=False).tolist()))
+    blocks = sorted(set([0, T - 1, T // 2] + rng.choice(T, 3, replace=False).tolist()))
+    _log(f"{name}: oracle rows heads={heads} blocks={blocks}")
+    got = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
+    w = _rows_check(t, cfg, vert, slash, lambda I: np.arange(64 * I, 64 * I + 64), got, heads, blocks)
+    row_lo, n_tail = _tail_start(cfg, vert, slash, 3)
+    _log(f"{name}: oracle dK/dV of the last {(N - row_lo) // 64} key blocks ({n_tail} active entries)")
+    assert n_tail > 0
+    dk_h, dv_h = dk.cpu().numpy(), dv.cpu().numpy()
+    ek, ev = _tail_kv_check(t, cfg, vert, slash, row_lo, lambda keys: dk_h[:, keys], lambda keys: dv_h[:, keys])
+    _log(f"{name}: max errors O {w['o']:.3e} LSE {w['lse']:.3e} dQ {w['dq']:.3e} dK {ek:.3e} dV {ev:.3e}")
+    assert max(w["o"], w["lse"], w["dq"], ek, ev) <= TOL, (w, ek, ev)
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_qwen128k_step():
+    """The benchmarked step: 16/2 heads, 131072 tokens, d 128, bf16, fwd + bwd."""
+    _contig_case("qwen128k")
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_llama256k_step():
+    """32/8 heads, 262144 tokens with Yarn x32 positions, fwd + bwd."""
+    _contig_case("llama256k")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("kind,rank", [("striped", 7), ("zigzag", 20)])
+def test_fullsize_qwen512k_ring_rank(kind, rank):
+    """One rank of a 524288-token sequence at P = 32: the whole ring (32 steps,
+    accumulated forward, per-step backward into each source shard's dK/dV)."""
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    cfg = config_by_name("qwen512k_cp32")
+    N, Hq, Hkv, D, P = cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P
+    T = N // 64
+    QB = T // P
+    _log(f"512k {kind} rank {rank}: generating")
+    t = generate(cfg)
+    _log("512k: oracle index")
+    ref = _oracle_index(t, cfg)
+    lay = vs.layout(kind, P, N)
+    _log("512k: GPU index (whole sequence, storage order) vs oracle")
+    k_store = H.storage_order(t["k"], kind, P)
+    H.check_index(H.gpu_index(H.to_dev(t["q"][:, N - cfg.last_q:], cfg.dtype), H.to_dev(k_store, cfg.dtype), lay,
+                              cfg.scale, cfg.top_p), ref, cfg.top_p)
+    del k_store
+    vert, slash = ref["vert"], ref["slash"]
+    lists = H.upload_lists(vert, slash, N)
+    cap = H.tile_cap_for(slash, Hq, QB)
+    dev = "cuda"
+    rows_r = ol.shard_positions(kind, N, P, rank)
+    q = H.to_dev(t["q"][:, rows_r], cfg.dtype)
+    do = H.to_dev(t["do"][:, rows_r], cfg.dtype)
+    o = torch.zeros(Hq, QB * 64, D, device=dev)
+    lse = torch.full((Hq, QB * 64), -math.inf, device=dev)
+    _log("512k: forward over 32 ring steps")
+    kv = {}
+    for step in range(P):
+        src = ol.ring_source(rank, step, P)
+        cols = ol.shard_positions(kind, N, P, src)
+        kv[src] = (H.to_dev(t["k"][:, cols], cfg.dtype), H.to_dev(t["v"][:, cols], cfg.dtype))
+        m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+        assert int(m.arrays()["status"].item()) == 0
+        vs.vs_attn_fwd(q, kv[src][0], kv[src][1], m, cfg.scale, o, lse, accumulate=1)
+    delta = torch.empty(Hq, QB * 64, device=dev)
+    vs.vs_attn_bwd_prep(o, do, delta)
+    dq = torch.zeros(Hq, QB * 64, D, device=dev)
+    dk = {s: torch.zeros(Hkv, QB * 64, D, device=dev) for s in range(P)}
+    dv = {s: torch.zeros(Hkv, QB * 64, D, device=dev) for s in range(P)}
+    _log("512k: backward over 32 ring steps")
+    for step in range(P):
+        src = ol.ring_source(rank, step, P)
+        m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+        vs.vs_attn_bwd(q, kv[src][0], kv[src][1], do, lse, delta, m, cfg.scale, dq, dk[src], dv[src])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg.seed + 11 * rank)
+    heads = sorted(set([0, Hq - 1] + rng.choice(Hq, 1).tolist()))
+    blocks = sorted(set([0, QB - 1] + rng.choice(QB, 3, replace=False).tolist()))
+    _log(f"512k: oracle rows heads={heads} local blocks={blocks}")
+    got = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
+    w = _rows_check(t, cfg, vert, slash, lambda I: rows_r[64 * I:64 * I + 64], got, heads, blocks)
+    # dK/dV of the last global key blocks (at least 64), from this rank's rows only
+    owner = np.empty(N, dtype=np.int64)
+    local = np.empty(N, dtype=np.int64)
+    for s in range(P):
+        c = ol.shard_positions(kind, N, P, s)
+        owner[c] = s
+        local[c] = np.arange(len(c))
+    dk_h = {s: dk[s].cpu().numpy() for s in range(P)}
+    dv_h = {s: dv[s].cpu().numpy() for s in range(P)}
+
+    def gather(store, keys):
+        out = np.empty((Hkv, len(keys), D), dtype=np.float32)
+        for s in np.unique(owner[keys]):
+            sel = owner[keys] == s
+            out[:, sel] = store[s][:, local[keys[sel]]]
+        return out
+    mine = np.zeros(N, dtype=bool)
+    mine[rows_r] = True
+    row_lo, n_tail = _tail_start(cfg, vert, slash, 64, rows_filter=lambda rows: mine[rows], max_blocks=1024)
+    _log(f"512k: oracle dK/dV of the last {(N - row_lo) // 64} key blocks, this rank's rows ({n_tail} active)")
+    assert n_tail > 0
+    ek, ev = _tail_kv_check(t, cfg, vert, slash, row_lo, lambda keys: gather(dk_h, keys),
+                            lambda keys: gather(dv_h, keys), rows_filter=lambda rows: mine[rows])
+    _log(f"512k {kind} rank {rank}: max errors O {w['o']:.3e} LSE {w['lse']:.3e} dQ {w['dq']:.3e} "
+         f"dK {ek:.3e} dV {ev:.3e}")
+    assert max(w["o"], w["lse"], w["dq"], ek, ev) <= TOL, (w, ek, ev)

@@ -18,22 +18,7 @@ def _check_index(cfg, kind="contig", P=1, last_q=64):
     lay = vs.layout(kind, P, N)
     out = H.gpu_index(H.to_dev(q_last, cfg.dtype), H.to_dev(k_store, cfg.dtype), lay, cfg.scale, cfg.top_p)
     ref = oi.build_index(q_last, t["k"], cfg.scale, N, cfg.top_p)
-    gv, gs = out["v"].cpu().numpy(), out["s"].cpu().numpy()
-    for g, o in ((gv, ref["v"]), (gs, ref["s"])):
-        o64 = o.astype(np.float64)
-        tol = 1e-4 * np.abs(o64) + 1e-7 * o64.max(axis=1, keepdims=True)
-        assert (np.abs(g - o64) <= tol).all(), np.abs(g - o64).max()
-    vert, slash = H.lists_from_gpu(out)
-    for h in range(cfg.Hq):
-        # bit-exact given identical scores: the oracle's rule on the GPU's own scores
-        assert np.array_equal(vert[h], oi.select_top_p(gv[h], cfg.top_p)), h
-        assert np.array_equal(slash[h], oi.select_top_p(gs[h], cfg.top_p)), h
-        # against the oracle's scores: differences only within 1e-5 of the cutoff score
-        for got, exp, x in ((vert[h], ref["vert"][h], ref["v"][h]), (slash[h], ref["slash"][h], ref["s"][h])):
-            diff = np.setxor1d(got, exp)
-            if len(diff) and len(exp):
-                cut = x[exp].min()
-                assert (np.abs(x[diff].astype(np.float64) - cut) <= 1e-5).all(), (h, diff)
+    H.check_index(out, ref, cfg.top_p)
     return out, ref
 
 

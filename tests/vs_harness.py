@@ -98,3 +98,27 @@ def oracle_step_forward(q, k, v, vert, slash, kind, P, rank, step, scale, heads=
             o, lse = oa.forward_rows(q[h, rows], k[g, cols[used]], v[g, cols[used]], M[:, used], scale)
             out[(h, I)] = (o, lse)
     return out
+
+
+def check_index(out, ref, top_p):
+    """GPU index (gpu_index output) against the oracle's build_index result:
+    scores within 1e-4 relative (+1e-7 of the row max); the selection equals
+    the oracle's top-p rule applied to the GPU's own scores (bit-exact); and
+    against the oracle's selection it differs only in positions whose oracle
+    score lies within 1e-5 of the cutoff score (ties at the budget edge)."""
+    from oracle import index as oi
+    gv, gs = out["v"].cpu().numpy(), out["s"].cpu().numpy()
+    for g, o in ((gv, ref["v"]), (gs, ref["s"])):
+        o64 = o.astype(np.float64)
+        tol = 1e-4 * np.abs(o64) + 1e-7 * o64.max(axis=1, keepdims=True)
+        assert (np.abs(g - o64) <= tol).all(), np.abs(g - o64).max()
+    vert, slash = lists_from_gpu(out)
+    for h in range(gv.shape[0]):
+        assert np.array_equal(vert[h], oi.select_top_p(gv[h], top_p)), h
+        assert np.array_equal(slash[h], oi.select_top_p(gs[h], top_p)), h
+        for got, exp, x in ((vert[h], ref["vert"][h], ref["v"][h]), (slash[h], ref["slash"][h], ref["s"][h])):
+            diff = np.setxor1d(got, exp)
+            if len(diff) and len(exp):
+                cut = x[exp].min()
+                assert (np.abs(x[diff].astype(np.float64) - cut) <= 1e-5).all(), (h, diff)
+    return vert, slash
