@@ -14,6 +14,11 @@ forward kernel and the fp64 oracle timed on the host as a CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline]
+
+Ring simulation (a workload with P > 1, e.g. --workload qwen512k_cp32): every
+rank's steps of the ring run one after another on the one GPU, each timed
+alone; prints a separate report line (per-step times and load imbalance,
+striped vs zigzag, fused vs separate merge), not the headline line.
 """
 import argparse
 import json
@@ -43,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-probe", action="store_true", help="run only a 1 GiB device copy (counter scaling)")
+    ap.add_argument("--layouts", default="striped,zigzag", help="ring simulation: layouts to compare")
+    ap.add_argument("--ring-reps", type=int, default=3, help="ring simulation: timed repetitions (median)")
+    ap.add_argument("--report-md", default=None, help="ring simulation: also write a markdown summary here")
     return ap.parse_args()
 
 
@@ -64,8 +72,8 @@ def main():
     if args.top_p is not None:
         cfg = config_by_name(args.workload, top_p=args.top_p)
     if cfg.P != 1:
-        print("ring-simulation workloads are timed by bench_ring mode (not in this line)", file=sys.stderr)
-        sys.exit(2)
+        ring_report(args, cfg)
+        return
     dev = torch.device("cuda:0")
     N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
     T = N // 64
@@ -206,6 +214,184 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def ring_report(args, cfg):
+    """Ring simulation of one sequence at P ranks on one GPU.
+
+    All shards stay resident in storage order (rank r's rows are rows
+    r*N/P .. of the storage-order tensors). For each layout: the global index
+    over the storage-order keys, then for every rank r and ring step s
+    (source shard (r - s) mod P) the step's active region, the forward with
+    the merge fused into its epilogue, and after the forward of all steps the
+    backward of every step. Each (r, s) kernel group is timed alone with HIP
+    events on the launch stream; reported times are medians over repetitions.
+    Communication between ranks is not part of it (one GPU).
+    """
+    import torch
+    import dynamic_sparse_attention_index_amd as vs
+    from synth import generate
+    from synth.inputs import layout_permutation
+
+    dev = torch.device("cuda:0")
+    N, Hq, Hkv, D, P = cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P
+    T, QB = N // 64, N // 64 // P
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    t0 = time.time()
+    host = generate(cfg)
+    gen_s = time.time() - t0
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        return a, b
+
+    out = {"metric": f"ring simulation: one rank's sparse fwd+bwd ring steps, {N} tokens at P={P}, 1 MI355X",
+           "unit": "ms", "workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "seq_len": N, "P": P, "head_dim": D,
+           "dtype": cfg.dtype, "data": "synthetic", "reps": args.ring_reps, "gen_s": round(gen_s, 1),
+           "communication": "excluded (one GPU; every rank's steps run in turn)", "layouts": {}}
+    for kind in args.layouts.split(","):
+        perm = np.concatenate([layout_permutation(kind, N, P, r) for r in range(P)])
+        q = torch.tensor(host["q"][:, perm]).to(dev, tdt)
+        k = torch.tensor(host["k"][:, perm]).to(dev, tdt)
+        v = torch.tensor(host["v"][:, perm]).to(dev, tdt)
+        do = torch.tensor(host["do"][:, perm]).to(dev, tdt)
+        lay = vs.layout(kind, P, N)
+        # global index over the storage-order keys; the last rows are global
+        # rows N - last_q .. N - 1, wherever they are stored
+        last_rows = np.nonzero(np.isin(perm, np.arange(N - cfg.last_q, N)))[0]
+        order = np.argsort(perm[last_rows])
+        q_last = q[:, torch.tensor(last_rows[order], device=dev)].contiguous()
+        vert_s = torch.empty(Hq, N, device=dev)
+        slash_s = torch.empty(Hq, T, device=dev)
+        vidx = torch.empty(Hq, N, dtype=torch.int32, device=dev)
+        vcnt = torch.empty(Hq, dtype=torch.int32, device=dev)
+        sidx = torch.empty(Hq, T, dtype=torch.int32, device=dev)
+        scnt = torch.empty(Hq, dtype=torch.int32, device=dev)
+        ws = torch.empty(vs.index_workspace_size(Hq, Hkv, N, D), dtype=torch.uint8, device=dev)
+
+        def index():
+            vs.vs_index_build(q_last, k, lay, cfg.scale, cfg.top_p, vert_s, slash_s, vidx, vcnt, sidx, scnt, ws,
+                              stream)
+        index()
+        torch.cuda.synchronize()
+        t_index = []
+        for _ in range(args.ring_reps):
+            ev = timed(index)
+            torch.cuda.synchronize()
+            t_index.append(ev[0].elapsed_time(ev[1]))
+        cap = Hq * QB * (int(scnt.max().item()) + 1)
+        t_mask = np.zeros((args.ring_reps, P, P))
+        t_fwd = np.zeros((args.ring_reps, P, P))
+        t_bwd = np.zeros((args.ring_reps, P, P))
+        act = np.zeros((P, P), dtype=np.int64)
+        o = torch.empty(Hq, QB * 64, D, device=dev)
+        lse = torch.empty(Hq, QB * 64, device=dev)
+        delta = torch.empty(Hq, QB * 64, device=dev)
+        dq = torch.empty(Hq, QB * 64, D, device=dev)
+        dk = torch.zeros(P, Hkv, QB * 64, D, device=dev)   # per source shard
+        dv = torch.zeros(P, Hkv, QB * 64, D, device=dev)
+        for rep in range(-1, args.ring_reps):       # rep -1: warm-up
+            dk.zero_()
+            dv.zero_()
+            for r in range(P):
+                rows = slice(r * QB * 64, (r + 1) * QB * 64)
+                qr, dor = q[:, rows], do[:, rows]
+                o.zero_()
+                lse.fill_(-math.inf)
+                dq.zero_()
+                masks, evs = [], []
+                for st in range(P):
+                    src = (r - st) % P
+                    cols = slice(src * QB * 64, (src + 1) * QB * 64)
+                    m = vs.Mask(Hq, Hkv, lay, cap)
+                    e_m = timed(lambda: vs.vs_block_mask(vidx, vcnt, sidx, scnt, r, st, m, stream))
+                    e_f = timed(lambda: vs.vs_attn_fwd(qr, k[:, cols], v[:, cols], m, cfg.scale, o, lse, 1, stream))
+                    masks.append(m)
+                    evs.append((e_m, e_f))
+                vs.vs_attn_bwd_prep(o, dor, delta, stream)
+                ebs = []
+                for st in range(P):
+                    src = (r - st) % P
+                    cols = slice(src * QB * 64, (src + 1) * QB * 64)
+                    ebs.append(timed(lambda: vs.vs_attn_bwd(qr, k[:, cols], v[:, cols], dor, lse, delta, masks[st],
+                                                            cfg.scale, dq, dk[src], dv[src], stream)))
+                torch.cuda.synchronize()
+                if rep >= 0:
+                    for st in range(P):
+                        (a, b), (c, d) = evs[st]
+                        t_mask[rep, r, st] = a.elapsed_time(b)
+                        t_fwd[rep, r, st] = c.elapsed_time(d)
+                        t_bwd[rep, r, st] = ebs[st][0].elapsed_time(ebs[st][1])
+                else:
+                    for st, m in enumerate(masks):
+                        arr = m.arrays()
+                        if int(arr["status"].item()) != 0:
+                            raise RuntimeError(f"mask status {int(arr['status'].item())} at rank {r} step {st}")
+                        act[r, st] = int(arr["n_active"].sum().item())
+                del masks
+        tm, tf, tb = (np.median(x, axis=0) for x in (t_mask, t_fwd, t_bwd))
+        t = tf + tb                                    # attention time of step s on rank r
+        mean_r = t.mean(axis=0)
+        max_r = t.max(axis=0)
+        cmean, cmax = act.mean(axis=0), act.max(axis=0)
+        ring_ms = float(max_r.sum())                   # the ring waits for the slowest rank each step
+        A_total = int(act.sum())
+        # merge: separate kernel vs fused into the forward, rank 0's steps
+        o_step = torch.empty_like(o)
+        l_step = torch.empty_like(lse)
+        fused, split = [], []
+        r = 0
+        qr = q[:, 0:QB * 64]
+        for st in range(P):
+            src = (r - st) % P
+            cols = slice(src * QB * 64, (src + 1) * QB * 64)
+            m = vs.Mask(Hq, Hkv, lay, cap)
+            vs.vs_block_mask(vidx, vcnt, sidx, scnt, r, st, m, stream)
+            ef = timed(lambda: vs.vs_attn_fwd(qr, k[:, cols], v[:, cols], m, cfg.scale, o, lse, 1, stream))
+            es1 = timed(lambda: vs.vs_attn_fwd(qr, k[:, cols], v[:, cols], m, cfg.scale, o_step, l_step, 0, stream))
+            es2 = timed(lambda: vs.vs_merge_lse(o, lse, o_step, l_step, stream))
+            torch.cuda.synchronize()
+            fused.append(ef[0].elapsed_time(ef[1]))
+            split.append(es1[0].elapsed_time(es1[1]) + es2[0].elapsed_time(es2[1]))
+            del m
+        out["layouts"][kind] = {
+            "index_ms": round(float(np.median(t_index)), 4),
+            "mask_ms_per_step_mean": round(float(tm.mean()), 4),
+            "fwd_ms_per_step_mean": round(float(tf.mean()), 4),
+            "bwd_ms_per_step_mean": round(float(tb.mean()), 4),
+            "step_time_imbalance_mean": round(float((max_r / mean_r).mean()), 4),
+            "step_time_imbalance_max": round(float((max_r / mean_r).max()), 4),
+            "step_count_imbalance_mean": round(float((cmax / np.maximum(cmean, 1)).mean()), 4),
+            "step_count_imbalance_max": round(float((cmax / np.maximum(cmean, 1)).max()), 4),
+            "ring_time_imbalance": round(float(max_r.sum() / mean_r.sum()), 4),
+            "worker_total_imbalance": round(float(t.sum(axis=1).max() / t.sum(axis=1).mean()), 4),
+            "ring_ms_fwd_bwd": round(ring_ms, 3),
+            "per_gpu_tokens_per_s": round((N / P) / (ring_ms * 1e-3), 1),
+            "per_gpu_effective_tflops": round(14 * D * A_total / P / (ring_ms * 1e-3) / 1e12, 2),
+            "active_entries": A_total,
+            "merge_fused_ms_per_step": round(float(np.mean(fused)), 4),
+            "merge_separate_ms_per_step": round(float(np.mean(split)), 4),
+        }
+        del q, k, v, do, dk, dv
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+    if args.report_md:
+        with open(args.report_md, "w") as f:
+            f.write(f"# Ring simulation report: {cfg.name} ({N} tokens, P = {P}, {Hq}/{Hkv} heads, d {D}, "
+                    f"{cfg.dtype})\n\n")
+            f.write("Command (repository root, one MI355X): `python bench.py --workload " + cfg.name +
+                    f" --layouts {args.layouts} --ring-reps {args.ring_reps}"
+                    f" --report-md <path>`\n\n")
+            f.write("Every rank's ring steps run one after another on the one GPU (communication excluded); "
+                    "times are medians over repetitions of each (rank, step) kernel group timed alone.\n\n")
+            keys = list(next(iter(out["layouts"].values())).keys())
+            f.write("| quantity | " + " | ".join(out["layouts"]) + " |\n|---|" + "---|" * len(out["layouts"]) + "\n")
+            for kk in keys:
+                f.write(f"| {kk} | " + " | ".join(str(out["layouts"][L][kk]) for L in out["layouts"]) + " |\n")
 
 
 def stored_traffic(kernel):

@@ -123,6 +123,14 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _cptr(t):
+    """Pointer of a dense buffer argument (the ABI's plain float* arrays are
+    contiguous [H, N(, D)]); a strided view would be read or written wrongly."""
+    if not t.is_contiguous():
+        raise VsError(VS_ERR_ARG, "non-contiguous buffer passed where the ABI takes a dense array")
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def as_vs_tensor(t: torch.Tensor) -> VsTensor:
     """[H, N, D] torch view -> vs_tensor (no copy)."""
     if t.dim() != 3 or t.stride(2) != 1:
@@ -195,26 +203,26 @@ def vs_block_mask(vert_idx, vert_cnt, slash_idx, slash_cnt, rank, step, mask: Ma
 
 def vs_attn_fwd(q, k, v, mask: Mask, scale, o, lse, accumulate=0, stream=None):
     _check(lib().vs_attn_fwd(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), ctypes.byref(mask.desc), scale,
-                             _ptr(o), _ptr(lse), int(accumulate), _stream(stream)), "vs_attn_fwd")
+                             _cptr(o), _cptr(lse), int(accumulate), _stream(stream)), "vs_attn_fwd")
 
 
 def vs_merge_lse(o_acc, lse_acc, o_step, lse_step, stream=None):
     Hq, Nq, D = o_acc.shape
-    _check(lib().vs_merge_lse(_ptr(o_acc), _ptr(lse_acc), _ptr(o_step), _ptr(lse_step), Hq, Nq, D,
+    _check(lib().vs_merge_lse(_cptr(o_acc), _cptr(lse_acc), _cptr(o_step), _cptr(lse_step), Hq, Nq, D,
                               _stream(stream)), "vs_merge_lse")
 
 
 def vs_attn_bwd_prep(o, dout, delta, stream=None):
-    _check(lib().vs_attn_bwd_prep(_ptr(o), as_vs_tensor(dout), _ptr(delta), _stream(stream)), "vs_attn_bwd_prep")
+    _check(lib().vs_attn_bwd_prep(_cptr(o), as_vs_tensor(dout), _cptr(delta), _stream(stream)), "vs_attn_bwd_prep")
 
 
 def vs_attn_bwd(q, k, v, dout, lse, delta, mask: Mask, scale, dq, dk, dv, stream=None):
-    _check(lib().vs_attn_bwd(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), as_vs_tensor(dout), _ptr(lse),
-                             _ptr(delta), ctypes.byref(mask.desc), scale, _ptr(dq), _ptr(dk), _ptr(dv),
+    _check(lib().vs_attn_bwd(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), as_vs_tensor(dout), _cptr(lse),
+                             _cptr(delta), ctypes.byref(mask.desc), scale, _cptr(dq), _cptr(dk), _cptr(dv),
                              _stream(stream)), "vs_attn_bwd")
 
 
 def vs_attn_bwd_parts(q, k, v, dout, lse, delta, mask: Mask, scale, dq, dk, dv, parts, stream=None):
     _check(lib().vs_attn_bwd_parts(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), as_vs_tensor(dout),
-                                   _ptr(lse), _ptr(delta), ctypes.byref(mask.desc), scale, _ptr(dq), _ptr(dk),
-                                   _ptr(dv), int(parts), _stream(stream)), "vs_attn_bwd_parts")
+                                   _cptr(lse), _cptr(delta), ctypes.byref(mask.desc), scale, _cptr(dq), _cptr(dk),
+                                   _cptr(dv), int(parts), _stream(stream)), "vs_attn_bwd_parts")

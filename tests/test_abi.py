@@ -131,3 +131,12 @@ def test_bwd_and_merge_validation(L):
     assert L.vs_merge_lse(p, p, p, p, 4, 1024, 96, None) == vs.VS_ERR_UNSUPPORTED
     assert L.vs_merge_lse(None, p, p, p, 4, 1024, 128, None) == vs.VS_ERR_ARG
     assert L.vs_merge_lse(p, p, p, p, 4, 0, 128, None) == vs.VS_OK          # nothing to do
+
+
+def test_dense_buffer_arguments_must_be_contiguous():
+    """The ABI's plain float* arrays are dense; the binding refuses a strided view
+    before anything is launched."""
+    import torch
+    with pytest.raises(vs.VsError):
+        vs._cptr(torch.zeros(4, 8)[:, :4])
+    assert vs._cptr(torch.zeros(4, 8)).value is not None
