@@ -194,6 +194,19 @@ def main():
                 "traffic": stored_traffic(dk_name), "algorithmic_flops_per_launch": dk_flops,
                 "mean_launch_ms": round(stage_ms[dom], 4)}
 
+    # Index pass (scores + top-p): algorithmic bytes = K read once + the last
+    # query rows + vertical and slash scores written; FLOPs = two passes of
+    # 2 * last_q * N * d per q head (row statistics, then the masses).
+    esz = 2 if cfg.dtype == "bf16" else 4
+    idx_bytes = Hkv * N * D * esz + Hq * cfg.last_q * D * esz + 4 * Hq * N + 4 * Hq * T
+    idx_flops = 2 * 2 * cfg.last_q * N * D * Hq
+    index_pass = {"ms": round(stage_ms["index"], 4), "algorithmic_bytes": idx_bytes,
+                  "gbs": round(idx_bytes / (stage_ms["index"] * 1e-3) / 1e9, 1),
+                  "frac_hbm_peak": round(idx_bytes / (stage_ms["index"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tflops": round(idx_flops / (stage_ms["index"] * 1e-3) / 1e12, 2),
+                  "frac_mfma_peak": round(idx_flops / (stage_ms["index"] * 1e-3) / 1e12 / peak, 4)}
+    strict_tflops = (4 + (8 if cfg.backward else 0)) * D * A / (ms_per_step * 1e-3) / 1e12
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, host, vidx, vcnt, sidx, scnt, args.cpu_seconds, tflops_unit=True)
@@ -211,6 +224,7 @@ def main():
         "kernels": per_kernel,
         "active_entries": A, "active_slash_tiles": A_slash, "active_vertical": A_vert,
         "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
+        "strict_algorithmic_tflops": round(strict_tflops, 3), "index_pass": index_pass,
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
