@@ -17,9 +17,6 @@ FLAGS = [
     # packed fp32 VALU forms are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics",
-    # MFMA results in VGPRs: the default keeps the dK/dV accumulators in
-    # AGPRs and copies them through VGPRs around every MFMA group
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # scores are never NaN: plain v_max without the NaN-quieting duplicate
     "-fno-honor-nans",
 ]

@@ -662,6 +662,90 @@ __device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const f
   }
 }
 
+// The two halves of kv_block, for the software-pipelined dK/dV kernel:
+// kv_sdp computes S and dP of a staged tile (MFMA only); kv_grad turns them
+// into P and dS (hi + lo pairs) and adds dV^T += dO^T P, dK^T += Q^T dS.
+__device__ __forceinline__ void kv_frag(const bf16* Qs, const bf16* Os, int rh, int g4, int n16, bf16x8 (*qa)[4],
+                                        bf16x8 (*oa)[4]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int qr = 32 * rh + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qa[t][ks] = *(const bf16x8*)(Qs + tile_off(qr, 4 * ks + g4));
+      oa[t][ks] = *(const bf16x8*)(Os + tile_off(qr, 4 * ks + g4));
+    }
+  }
+}
+__device__ __forceinline__ void kv_sdp(const bf16x8 (*qa)[4], const bf16x8 (*oa)[4], const bf16x8 (*kf)[4],
+                                       const bf16x8 (*vf)[4], f32x4 (*s)[2], f32x4 (*dp)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt][t] = dp[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt][t] = mfma_bf16(qa[t][ks], kf[kt][ks], s[kt][t]);
+        dp[kt][t] = mfma_bf16(oa[t][ks], vf[kt][ks], dp[kt][t]);
+      }
+  }
+}
+// per-row lse (log2 units) and delta of the wave's rows 32 rh + 8 g + 4 t + i
+__device__ __forceinline__ void kv_rowstats(const float* lsh, const float* dsh_, int rh, int g4, f32x4* l2,
+                                            f32x4* dd) {
+  const int r0 = 32 * rh + 8 * g4;
+  l2[0] = *(const f32x4*)(lsh + r0);
+  l2[1] = *(const f32x4*)(lsh + r0 + 4);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l2[t][i] *= LOG2E;
+  dd[0] = *(const f32x4*)(dsh_ + r0);
+  dd[1] = *(const f32x4*)(dsh_ + r0 + 4);
+}
+__device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], const f32x4* l2, const f32x4* dd,
+                                       const int* thr, int rh, int g4, float sl2, bf16x8* ph, bf16x8* pl,
+                                       bf16x8* dh, bf16x8* dl) {
+  const int r0 = 32 * rh + 8 * g4;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x4 ds[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * t + i;
+        const bool act = r >= thr[kt] && l2[t][i] > -INFINITY;
+        const float pr = act ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][t][i], sl2, -l2[t][i])) : 0.f;
+        s[kt][t][i] = pr;
+        ds[t][i] = pr * (dp[kt][t][i] - dd[t][i]);
+      }
+    split8(s[kt][0], s[kt][1], ph[kt], pl[kt]);
+    split8(ds[0], ds[1], dh[kt], dl[kt]);
+  }
+}
+__device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf16x8* ph, const bf16x8* pl,
+                                        const bf16x8* dh, const bf16x8* dl, int rh, int g4, int n16,
+                                        f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8]) {
+  constexpr int D = TD;
+  const int rr = 32 * rh + 8 * g4 + (n16 >> 2);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int lc = 2 * dt + ((n16 & 3) >> 1);
+    const bf16x8 oT = lds_read_tr16_x2(Os + tile_off(rr, lc) + 4 * (n16 & 1), D);
+    const bf16x8 qT = lds_read_tr16_x2(Qs + tile_off(rr, lc) + 4 * (n16 & 1), D);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      acc_dv[kt][dt] = mfma_bf16(oT, ph[kt], acc_dv[kt][dt]);
+      acc_dv[kt][dt] = mfma_bf16(oT, pl[kt], acc_dv[kt][dt]);
+      acc_dk[kt][dt] = mfma_bf16(qT, dh[kt], acc_dk[kt][dt]);
+      acc_dk[kt][dt] = mfma_bf16(qT, dl[kt], acc_dk[kt][dt]);
+    }
+  }
+}
+
 // Copy the Q and dO rows of query block I of head h and its lse/delta.
 __device__ __forceinline__ void stage_qblock(bf16* Qn, bf16* On, float* ln, const BwdArgs& a, int h, int I, int wave,
                                              int lane, const DmaLane& dl) {
@@ -730,20 +814,31 @@ __device__ __forceinline__ void kv_finish(float* xbuf_dk, float* xbuf_dv, f32x4 
 }
 
 // dK/dV over slash tiles: one workgroup per (kv head, key block J); walks the
-// CSC lists of every q head of the group (entries staged through LDS like the
-// forward's descriptors) and owns the key block's dK/dV rows.
+// CSC lists of every q head of the group and owns the key block's dK/dV rows.
+// Software pipeline over the (q head, query block) tiles of the walk: step i
+// computes S and dP of tile i + 1 on the matrix cores while the vector ALU
+// turns S and dP of tile i into P and dS, then adds tile i's dV and dK. Three
+// (Q, dO) stages: tile i (gradient products), tile i + 1 (S, dP), tile i + 2
+// (being copied). One workgroup per CU (the accumulators and K/V fragments
+// take more than half the registers), so LDS has room for the third stage.
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs a) {
-  // stage s = (Q tile, dO tile) in QOs; after the loop QO0 / QO1 (32 KiB each)
-  // carry the dK / dV exchange
   __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
-  bf16* Q0 = QO0;
-  bf16* O0 = QO0 + TILE_ELEMS;
-  bf16* Q1 = QO1;
-  bf16* O1 = QO1 + TILE_ELEMS;
+  __shared__ __attribute__((aligned(16))) bf16 QO2[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) float L0[2 * BLK];
   __shared__ __attribute__((aligned(16))) float L1[2 * BLK];
-  __shared__ int desc0_sh[BLK], desc1_sh[BLK];
+  __shared__ __attribute__((aligned(16))) float L2[2 * BLK];
+  __shared__ int desc_sh[3][BLK];   // CSC entry of tile t in slot t % 3
+  auto QOst = [&]<int p>() -> bf16* {
+    if constexpr (p == 0) return QO0;
+    else if constexpr (p == 1) return QO1;
+    else return QO2;
+  };
+  auto Lst = [&]<int p>() -> float* {
+    if constexpr (p == 0) return L0;
+    else if constexpr (p == 1) return L1;
+    else return L2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -769,14 +864,24 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
     while (it >= cnt[hh]) { it -= cnt[hh]; ++hh; }
     return cstart[hh] + it;
   };
-  auto desc_copy = [&](int it, int* slot) {
+  auto desc_copy = [&](int it) {
     if (wave != 0) return;
     int hh;
     const int e = entry_of(it, hh);
     __builtin_amdgcn_global_load_lds((const void*)(a.csc_row + e),
                                      (__attribute__((address_space(3))) void*)(
-                                         (__attribute__((address_space(3))) int*)(slot)),
+                                         (__attribute__((address_space(3))) int*)(desc_sh[it % 3])),
                                      4, 0, 0);
+  };
+  // start the copy of tile t into stage p; returns its diagonal flag
+  auto issue = [&]<int p>(int t) -> int {
+    int hh;
+    entry_of(t, hh);
+    const int e = __builtin_amdgcn_readfirstlane(desc_sh[t % 3][0]);
+    bf16* qo = QOst.template operator()<p>();
+    stage_qblock(qo, qo + TILE_ELEMS, Lst.template operator()<p>(), a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane,
+                 dlane);
+    return (e & VS_TILE_DIAG) ? 1 : 0;
   };
 
   bf16x8 kf[2][4], vf[2][4];
@@ -795,45 +900,79 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc_dk[kt][dt] = acc_dv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale_log2;
-  int diag_c = 0;
+  f32x4 s_c[2][2], dp_c[2][2];
+  int diag_c = 0, diag_n1 = 0;
 
-  auto step = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, bf16* Qn, bf16* On, float* Ln,
-                  int* dn_next, const int* dn_cur) {
+  // step i (stage p = i % 3): S/dP of tile i in (s_c, dp_c); tile i + 1 is
+  // in stage p + 1, tile i + 2's descriptor in slot (i + 2) % 3.
+  auto step = [&]<int p>(int i) {
+    constexpr int p1 = (p + 1) % 3, p2 = (p + 2) % 3;
     wait_all_mem();
-    __syncthreads();
-    const int diag = diag_c;
-    if (it + 1 < total) {
-      int hh;
-      entry_of(it + 1, hh);
-      const int e = dn_cur[0];
-      stage_qblock(Qn, On, Ln, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane, dlane);
-      diag_c = (e & VS_TILE_DIAG) ? 1 : 0;
-      if (it + 2 < total) desc_copy(it + 2, dn_next);
-    }
+    __syncthreads();   // tile i + 1 and descriptor i + 2 have landed; step i - 1 is done everywhere
+    const int diag_i = diag_c;
+    int diag_n2 = 0;
+    if (i + 2 < total) diag_n2 = issue.template operator()<p2>(i + 2);
+    if (i + 3 < total) desc_copy(i + 3);
+    // S, dP of tile i + 1 (the last step computes them from a stale stage and
+    // drops them): fragments and this tile's row statistics are read first, so
+    // the region below holds only MFMAs and vector ops, interleaved one MFMA
+    // per six vector ops
+    const bf16* Qn = QOst.template operator()<p1>();
+    bf16x8 qa[2][4], oa[2][4];
+    kv_frag(Qn, Qn + TILE_ELEMS, rh, g4, n16, qa, oa);
+    f32x4 l2[2], dd[2];
+    const float* Lc = Lst.template operator()<p>();
+    kv_rowstats(Lc, Lc + BLK, rh, g4, l2, dd);
     int thr[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) thr[kt] = diag ? 32 * kh + 16 * kt + n16 : 0;
-    kv_block(Qs, Os, Ls, Ls + BLK, kf, vf, thr, kh, rh, g4, n16, sl2, acc_dk, acc_dv);
+    for (int kt = 0; kt < 2; ++kt) thr[kt] = diag_i ? 32 * kh + 16 * kt + n16 : 0;
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s_n[2][2], dp_n[2][2];
+    kv_sdp(qa, oa, kf, vf, s_n, dp_n);
+    bf16x8 ph[2], pl[2], dh[2], dl[2];
+    kv_pds(s_c, dp_c, l2, dd, thr, rh, g4, sl2, ph, pl, dh, dl);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16* Qc = QOst.template operator()<p>();
+    kv_grad(Qc, Qc + TILE_ELEMS, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s_c[kt][t] = s_n[kt][t];
+        dp_c[kt][t] = dp_n[kt][t];
+      }
+    diag_c = diag_n1;
+    diag_n1 = diag_n2;
   };
 
-  desc_copy(0, desc0_sh);
-  if (total > 1) desc_copy(1, desc1_sh);
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (t < total) desc_copy(t);
+  wait_all_mem();
+  __syncthreads();
+  diag_c = issue.template operator()<0>(0);
+  if (total > 1) diag_n1 = issue.template operator()<1>(1);
   wait_all_mem();
   __syncthreads();
   {
-    int hh;
-    entry_of(0, hh);
-    const int e = desc0_sh[0];
-    stage_qblock(Q0, O0, L0, a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane, dlane);
-    diag_c = (e & VS_TILE_DIAG) ? 1 : 0;
+    bf16x8 qa[2][4], oa[2][4];
+    kv_frag(QO0, QO0 + TILE_ELEMS, rh, g4, n16, qa, oa);
+    kv_sdp(qa, oa, kf, vf, s_c, dp_c);
   }
-  for (int it = 0; it < total; it += 2) {
-    step(it, Q0, O0, L0, Q1, O1, L1, desc0_sh, desc1_sh);
-    if (it + 1 < total) step(it + 1, Q1, O1, L1, Q0, O0, L0, desc1_sh, desc0_sh);
+  for (int i0 = 0; i0 < total; i0 += 3) {
+    step.template operator()<0>(i0);
+    if (i0 + 1 < total) step.template operator()<1>(i0 + 1);
+    if (i0 + 2 < total) step.template operator()<2>(i0 + 2);
   }
   int64_t keys[2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) keys[kt] = (int64_t)kvh * a.KB * BLK + (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
+  wait_all_mem();
   kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, false);
 }
 
