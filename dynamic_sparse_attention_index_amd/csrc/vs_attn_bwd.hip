@@ -437,7 +437,9 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 V1[TILE_ELEMS];
-  __shared__ int thr0_sh[BLK], thr1_sh[BLK], desc0_sh[BLK], desc1_sh[BLK];
+  __shared__ __attribute__((aligned(16))) int thr0_sh[BLK];
+  __shared__ __attribute__((aligned(16))) int thr1_sh[BLK];
+  __shared__ int desc0_sh[BLK], desc1_sh[BLK];
   __shared__ uint32_t sbits[MAX_LDS_W];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -532,16 +534,23 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
       }
     }
     bf16x8 dsh[2], dsl[2];
+    // row thresholds of this lane's 8 keys, read unconditionally (two 16-byte
+    // reads) and applied with selects: a conditional read per element made the
+    // compiler branch around every exponential
+    const i32x4 th0 = *(const i32x4*)(thc + 32 * kh + 8 * g4);
+    const i32x4 th1 = *(const i32x4*)(thc + 32 * kh + 8 * g4 + 4);
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
       const int rowoff = 32 * rh + 16 * rs + n16;
+      const bool row_ok = lse2[rs] > -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          bool act = lse2[rs] > -INFINITY;
-          if (mode) act = act && thc[32 * kh + 8 * g4 + 4 * t + i] <= rowoff;
-          const float p = act ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs])) : 0.f;
+          const int th = t == 0 ? th0[i] : th1[i];
+          const bool act = row_ok && (!mode || th <= rowoff);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs]));
+          const float p = act ? e : 0.f;
           s[rs][t][i] = p * (dp[rs][t][i] - dl[rs]);
         }
       split8(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
