@@ -837,7 +837,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   __shared__ __attribute__((aligned(16))) float L0[2 * BLK];
   __shared__ __attribute__((aligned(16))) float L1[2 * BLK];
   __shared__ __attribute__((aligned(16))) float L2[2 * BLK];
-  __shared__ int desc_sh[3][BLK];   // CSC entry of tile t in slot t % 3
+  __shared__ int desc_sh[3][BLK];   // CSC entry of tile t in slot t % 3 (the copy fills all 64 words)
+  __shared__ int head_sh[3];        // q head (within the group) of tile t in slot t % 3
   auto QOst = [&]<int p>() -> bf16* {
     if constexpr (p == 0) return QO0;
     else if constexpr (p == 1) return QO1;
@@ -859,37 +860,67 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   if (item < 0) return;
   const int J = item / a.Hkv, kvh = item % a.Hkv;
   const int grp = a.Hq / a.Hkv;
-  // flattened (head, CSC entry) sequence of the group
-  int cstart[8], cnt[8], total = 0;
-  for (int hh = 0; hh < grp; ++hh) {
-    const int64_t cu = (int64_t)(kvh * grp + hh) * a.KB + J;
-    cstart[hh] = a.csc_ptr[cu];
-    cnt[hh] = a.csc_ptr[cu + 1] - cstart[hh];
-    total += cnt[hh];
+  // The walk is the concatenation of the group's q heads' CSC lists for this
+  // key block. Per-head ranges sit in lanes 0 .. grp-1 and are read back with
+  // readlane by a wave-uniform head index (an SGPR array indexed at run time
+  // compiles into compare/select chains).
+  int cst_l = 0, cnt_l = 0;
+  if (lane < grp) {
+    const int64_t cu = (int64_t)(kvh * grp + lane) * a.KB + J;
+    cst_l = a.csc_ptr[cu];
+    cnt_l = a.csc_ptr[cu + 1] - cst_l;
   }
+  int total = 0;
+  for (int hh = 0; hh < grp; ++hh) total += __builtin_amdgcn_readlane(cnt_l, hh);
   if (total == 0) return;
-  auto entry_of = [&](int it, int& hh) {   // position in csc_row of step `it`
-    hh = 0;
-    while (it >= cnt[hh]) { it -= cnt[hh]; ++hh; }
-    return cstart[hh] + it;
+  // per-head row-0 offsets (bytes) of Q and dO, and of the head's lse / delta rows
+  const int64_t q_off_l = lane < grp ? (int64_t)(kvh * grp + lane) * a.qsh * 2 : 0;
+  const int64_t o_off_l = lane < grp ? (int64_t)(kvh * grp + lane) * a.dsh * 2 : 0;
+  auto rl64 = [&](int64_t v, int hh) -> int64_t {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)v, hh);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), hh);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
   };
+  // cursor (head, position) of the next descriptor copy; copies are issued
+  // for walk positions 0, 1, 2, ... in order
+  int cur_h = 0, cur_p = 0;
+  auto cur_skip = [&]() {
+    while (cur_h < grp && cur_p >= __builtin_amdgcn_readlane(cnt_l, cur_h)) {
+      ++cur_h;
+      cur_p = 0;
+    }
+  };
+  cur_skip();
   auto desc_copy = [&](int it) {
-    if (wave != 0) return;
-    int hh;
-    const int e = entry_of(it, hh);
-    __builtin_amdgcn_global_load_lds((const void*)(a.csc_row + e),
-                                     (__attribute__((address_space(3))) void*)(
-                                         (__attribute__((address_space(3))) int*)(desc_sh[it % 3])),
-                                     4, 0, 0);
+    if (wave == 0) {
+      const int e = __builtin_amdgcn_readlane(cst_l, cur_h) + cur_p;
+      __builtin_amdgcn_global_load_lds((const void*)(a.csc_row + e),
+                                       (__attribute__((address_space(3))) void*)(
+                                           (__attribute__((address_space(3))) int*)(desc_sh[it % 3])),
+                                       4, 0, 0);
+      if (lane == 0) head_sh[it % 3] = cur_h;   // the walk position's q head
+    }
+    ++cur_p;
+    cur_skip();
   };
   // start the copy of tile t into stage p; returns its diagonal flag
   auto issue = [&]<int p>(int t) -> int {
-    int hh;
-    entry_of(t, hh);
     const int e = __builtin_amdgcn_readfirstlane(desc_sh[t % 3][0]);
+    const int hh = __builtin_amdgcn_readfirstlane(head_sh[t % 3]);
+    const int I = e & VS_TILE_MASK;
     bf16* qo = QOst.template operator()<p>();
-    stage_qblock(qo, qo + TILE_ELEMS, Lst.template operator()<p>(), a, kvh * grp + hh, e & VS_TILE_MASK, wave, lane,
-                 dlane);
+    float* ls = Lst.template operator()<p>();
+    const int64_t r0 = (int64_t)I * BLK;
+    const uint32_t qrb = (uint32_t)a.qsn * 2, orb = (uint32_t)a.dsn * 2;
+    dma_tile_rows(qo, (const char*)a.q + rl64(q_off_l, hh) + r0 * qrb, qrb, dlane, wave);
+    dma_tile_rows(qo + TILE_ELEMS, (const char*)a.dout + rl64(o_off_l, hh) + r0 * orb, orb, dlane, wave);
+    if (wave < 2) {
+      const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)(kvh * grp + hh) * a.QB * BLK + r0 + lane;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)(
+                                           (__attribute__((address_space(3))) float*)(ls + wave * BLK)),
+                                       4, 0, 0);
+    }
     return (e & VS_TILE_DIAG) ? 1 : 0;
   };
 
