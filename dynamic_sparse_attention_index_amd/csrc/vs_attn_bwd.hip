@@ -495,7 +495,10 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
       qf[rs][ks] = *(const bf16x8*)((const bf16*)a.q + h * a.qsh + grow * a.qsn + 32 * ks + 8 * g4);
       df[rs][ks] = *(const bf16x8*)((const bf16*)a.dout + h * a.dsh + grow * a.dsn + 32 * ks + 8 * g4);
     }
-    lse2[rs] = a.lse[(int64_t)h * a.QB * BLK + grow] * LOG2E;
+    // an empty row (LSE = -inf) gets +inf, so exp2(S * scale - LSE) is 0
+    // for it without a per-element select
+    const float lr = a.lse[(int64_t)h * a.QB * BLK + grow];
+    lse2[rs] = lr == -INFINITY ? INFINITY : lr * LOG2E;
     dl[rs] = a.delta[(int64_t)h * a.QB * BLK + grow];
   }
   f32x4 acc[2][8];
@@ -534,23 +537,25 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
       }
     }
     bf16x8 dsh[2], dsl[2];
-    // row thresholds of this lane's 8 keys, read unconditionally (two 16-byte
-    // reads) and applied with selects: a conditional read per element made the
-    // compiler branch around every exponential
-    const i32x4 th0 = *(const i32x4*)(thc + 32 * kh + 8 * g4);
-    const i32x4 th1 = *(const i32x4*)(thc + 32 * kh + 8 * g4 + 4);
+    if (mode) {   // wave-uniform: diagonal tile or vertical chunk
+      // row thresholds of this lane's 8 keys (two 16-byte reads)
+      const i32x4 th0 = *(const i32x4*)(thc + 32 * kh + 8 * g4);
+      const i32x4 th1 = *(const i32x4*)(thc + 32 * kh + 8 * g4 + 4);
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((t == 0 ? th0[i] : th1[i]) > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
+    }
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
-      const int rowoff = 32 * rh + 16 * rs + n16;
-      const bool row_ok = lse2[rs] > -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int th = t == 0 ? th0[i] : th1[i];
-          const bool act = row_ok && (!mode || th <= rowoff);
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs]));
-          const float p = act ? e : 0.f;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs]));
           s[rs][t][i] = p * (dp[rs][t][i] - dl[rs]);
         }
       split8(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
@@ -710,14 +715,26 @@ __device__ __forceinline__ void kv_rowstats(const float* lsh, const float* dsh_,
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l2[t][i] *= LOG2E;
+    for (int i = 0; i < 4; ++i) l2[t][i] = l2[t][i] == -INFINITY ? INFINITY : l2[t][i] * LOG2E;
   dd[0] = *(const f32x4*)(dsh_ + r0);
   dd[1] = *(const f32x4*)(dsh_ + r0 + 4);
 }
+// l2: row LSE in log2 units, +inf for an empty row (kv_rowstats); on the
+// diagonal tile (wave-uniform `diag`) key kt of this lane is active for rows
+// >= thr[kt].
 __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], const f32x4* l2, const f32x4* dd,
-                                       const int* thr, int rh, int g4, float sl2, bf16x8* ph, bf16x8* pl,
-                                       bf16x8* dh, bf16x8* dl) {
+                                       int diag, const int* thr, int rh, int g4, float sl2, bf16x8* ph,
+                                       bf16x8* pl, bf16x8* dh, bf16x8* dl) {
   const int r0 = 32 * rh + 8 * g4;
+  if (diag) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r0 + 4 * t + i < thr[kt]) s[kt][t][i] = -INFINITY;
+  }
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     f32x4 ds[2];
@@ -725,9 +742,7 @@ __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], cons
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + 4 * t + i;
-        const bool act = r >= thr[kt] && l2[t][i] > -INFINITY;
-        const float pr = act ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][t][i], sl2, -l2[t][i])) : 0.f;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][t][i], sl2, -l2[t][i]));
         s[kt][t][i] = pr;
         ds[t][i] = pr * (dp[kt][t][i] - dd[t][i]);
       }
@@ -965,12 +980,12 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
     kv_rowstats(Lc, Lc + BLK, rh, g4, l2, dd);
     int thr[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) thr[kt] = diag_i ? 32 * kh + 16 * kt + n16 : 0;
+    for (int kt = 0; kt < 2; ++kt) thr[kt] = 32 * kh + 16 * kt + n16;
     __builtin_amdgcn_sched_barrier(0);
     f32x4 s_n[2][2], dp_n[2][2];
     kv_sdp(qa, oa, kf, vf, s_n, dp_n);
     bf16x8 ph[2], pl[2], dh[2], dl[2];
-    kv_pds(s_c, dp_c, l2, dd, thr, rh, g4, sl2, ph, pl, dh, dl);
+    kv_pds(s_c, dp_c, l2, dd, diag_i, thr, rh, g4, sl2, ph, pl, dh, dl);
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);

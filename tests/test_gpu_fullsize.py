@@ -78,30 +78,39 @@ def _rows_check(t, cfg, vert, slash, rows_of, got, heads, blocks):
 
 
 def _tail_active(cfg, vert, slash, row_lo, rows_filter=None):
-    """Estimate of the active (row, key) pairs with both at or after row_lo:
-    slash tiles of the window's row blocks plus vertical columns in it (rows
-    filtered block by block; the layouts keep 64-row blocks whole)."""
+    """Active (row, key) pairs with row and key at or after row_lo (rows
+    filtered; the layouts keep 64-row blocks whole): per row block I, its
+    slash tiles inside the window (2080 entries on the diagonal, 4096 off it)
+    plus the entries of its verticals in the window that no such tile covers."""
     N = cfg.N
     J0, QB = row_lo // 64, N // 64
     Ib = np.arange(J0, QB)
-    w = np.ones(len(Ib)) if rows_filter is None else rows_filter(Ib * 64).astype(float)
-    total = 0.0
+    if rows_filter is not None:
+        Ib = Ib[rows_filter(Ib * 64)]
+    total = 0
     for h in range(cfg.Hq):
         sh = np.sort(np.asarray(slash[h]))
-        total += 4096.0 * (w * np.searchsorted(sh, Ib - J0, side="right")).sum()
-        vm = np.asarray(vert[h])
+        vm = np.sort(np.asarray(vert[h]))
         vm = vm[vm >= row_lo]
-        total += float((N - vm).sum()) * w.mean()
-    return int(total)
+        for I in Ib:
+            ss = sh[sh <= I - J0]
+            total += 4096 * int((ss > 0).sum()) + 2080 * int((ss == 0).sum())
+            m = vm[vm < 64 * (I + 1)]
+            if len(m):
+                covered = np.isin(I - m // 64, ss)
+                total += int(np.minimum(64, 64 * (I + 1) - m)[~covered].sum())
+    return total
 
 
-def _tail_start(cfg, vert, slash, first_blocks, rows_filter=None, need=4096, max_blocks=512):
-    """Start of the tail window: the last `first_blocks` key blocks, doubled
-    until the window holds at least `need` active entries (so the dK/dV check
-    is not vacuous when the last blocks are attended by nobody)."""
+def _tail_start(cfg, vert, slash, first_blocks, rows_filter=None, need=4096, max_blocks=512, end_row=None):
+    """Start of the tail window: `first_blocks` key blocks before end_row (the
+    sequence end, or a ring rank's last row), doubled until the window holds
+    at least `need` active entries (so the dK/dV check is not vacuous when the
+    last blocks are attended by nobody)."""
+    end_row = cfg.N if end_row is None else end_row
     nb = first_blocks
     while True:
-        row_lo = cfg.N - 64 * nb
+        row_lo = max(0, end_row - 64 * nb)
         cnt = _tail_active(cfg, vert, slash, row_lo, rows_filter)
         if cnt >= need or nb >= max_blocks:
             return row_lo, cnt
@@ -245,7 +254,9 @@ def test_fullsize_qwen512k_ring_rank(kind, rank):
     _log(f"512k: oracle rows heads={heads} local blocks={blocks}")
     got = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
     w = _rows_check(t, cfg, vert, slash, lambda I: rows_r[64 * I:64 * I + 64], got, heads, blocks)
-    # dK/dV of the last global key blocks (at least 64), from this rank's rows only
+    # dK/dV of the key blocks from 64 (or more) blocks before this rank's last
+    # row to the end, from this rank's rows only (keys past its last row get
+    # nothing from it)
     owner = np.empty(N, dtype=np.int64)
     local = np.empty(N, dtype=np.int64)
     for s in range(P):
@@ -263,7 +274,10 @@ def test_fullsize_qwen512k_ring_rank(kind, rank):
         return out
     mine = np.zeros(N, dtype=bool)
     mine[rows_r] = True
-    row_lo, n_tail = _tail_start(cfg, vert, slash, 64, rows_filter=lambda rows: mine[rows], max_blocks=1024)
+    # (striped: the rank holds every P-th block, so start 2P blocks back)
+    row_lo, n_tail = _tail_start(cfg, vert, slash, 2 * P if kind == "striped" else 3,
+                                 rows_filter=lambda rows: mine[rows], max_blocks=1024,
+                                 end_row=int(rows_r.max()) + 1)
     _log(f"512k: oracle dK/dV of the last {(N - row_lo) // 64} key blocks, this rank's rows ({n_tail} active)")
     assert n_tail > 0
     ek, ev = _tail_kv_check(t, cfg, vert, slash, row_lo, lambda keys: gather(dk_h, keys),
