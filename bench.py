@@ -177,11 +177,18 @@ def main():
     # convention, 14 d in total): forward 4 d; dK/dV kernels 8 d (recompute S,
     # dP, dV, dK) over their entries; dQ kernel 2 d.
     peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    kernels = {"fwd": ("attn_fwd_bf16_d128_kernel", 4 * D * A)}
+    if cfg.dtype == "bf16" and D == 128:
+        kn = {"fwd": "attn_fwd_bf16_d128_kernel", "dq": "dq_bf16_d128_kernel",
+              "dkdv": "dkdv_bf16_d128_kernel", "dkdv_vert": "dkdv_vert_bf16_d128_kernel"}
+    else:
+        tn = "bf16" if cfg.dtype == "bf16" else "float"
+        kn = {"fwd": f"attn_fwd_kernel<{tn}, {D}>", "dq": f"dq_kernel<{tn}, {D}>",
+              "dkdv": f"dkdv_kernel<{tn}, {D}>", "dkdv_vert": f"dkdv_vert_kernel<{tn}, {D}>"}
+    kernels = {"fwd": (kn["fwd"], 4 * D * A)}
     if cfg.backward:
-        kernels.update({"dq": ("dq_bf16_d128_kernel", 2 * D * A),
-                        "dkdv": ("dkdv_bf16_d128_kernel", 8 * D * A_slash),
-                        "dkdv_vert": ("dkdv_vert_bf16_d128_kernel", 8 * D * A_vert)})
+        kernels.update({"dq": (kn["dq"], 2 * D * A),
+                        "dkdv": (kn["dkdv"], 8 * D * A_slash),
+                        "dkdv_vert": (kn["dkdv_vert"], 8 * D * A_vert)})
     per_kernel = {}
     for st, (kname, flops) in kernels.items():
         tf = flops / (stage_ms[st] * 1e-3) / 1e12
