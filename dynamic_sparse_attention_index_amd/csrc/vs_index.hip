@@ -178,17 +178,23 @@ __global__ void __launch_bounds__(512) index_rowstat_kernel(IndexArgs a) {
     }
 }
 
-// Pass 2: one thread per (q head, row).
-__global__ void index_combine_kernel(IndexArgs a) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+// Pass 2: one wave per (q head, row); lanes stride over the key-range splits.
+constexpr int COMB_THREADS = 256;
+__global__ void __launch_bounds__(COMB_THREADS) index_combine_kernel(IndexArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (COMB_THREADS / 64) + (threadIdx.x >> 6);
   if (t >= a.Hq * BLK) return;
   const float* p = a.part + (int64_t)t * a.nsplit * 2;
   float mm = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, p[2 * s]);
+  for (int s = lane; s < a.nsplit; s += 64) mm = fmaxf(mm, p[2 * s]);
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
   float ll = 0.f;
   if (mm > -INFINITY)
-    for (int s = 0; s < a.nsplit; ++s) ll += p[2 * s + 1] * __builtin_amdgcn_exp2f(p[2 * s] - mm);
-  a.lse2[t] = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+    for (int s = lane; s < a.nsplit; s += 64) ll += p[2 * s + 1] * __builtin_amdgcn_exp2f(p[2 * s] - mm);
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ll += __shfl_xor(ll, off, 64);
+  if (lane == 0) a.lse2[t] = ll > 0.f ? mm + log2f(ll) : -INFINITY;
 }
 
 // Pass 3: grid (nsplit, Hkv); vertical mass per key and slash mass per block.
@@ -261,34 +267,10 @@ __device__ __forceinline__ uint64_t fixed_mass(float x) {
   return (uint64_t)__builtin_rint((double)x * 1099511627776.0);  // x * 2^40, exact for fp32 x
 }
 
-// Block-wide exclusive scan (SEL_THREADS threads), returns the block total.
-__device__ __forceinline__ int sel_scan(int x, int* total, int* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = x;
-  #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) sh[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < SEL_WAVES; ++w) { const int t = sh[w]; sh[w] = run; run += t; }
-    sh[SEL_WAVES] = run;
-  }
-  __syncthreads();
-  const int res = sh[wave] + incl - x;
-  *total = sh[SEL_WAVES];
-  __syncthreads();
-  return res;
-}
-
 // grid (Hq, 2): y = 0 vertical scores, y = 1 slash scores.
 __global__ void __launch_bounds__(SEL_THREADS) topp_select_kernel(SelectArgs a) {
   __shared__ unsigned long long hist[SEL_WAVES][256];
   __shared__ unsigned long long red[SEL_WAVES];
-  __shared__ int scan_sh[SEL_WAVES + 1];
   __shared__ unsigned long long sel_rem;
   __shared__ uint32_t sel_prefix;
   const int h = blockIdx.x;
@@ -362,24 +344,54 @@ __global__ void __launch_bounds__(SEL_THREADS) topp_select_kernel(SelectArgs a) 
   const uint32_t xstar = sel_prefix;
   const unsigned long long qstar = fixed_mass(__uint_as_float(xstar));
   const unsigned long long k_tie = qstar ? (sel_rem + qstar - 1) / qstar : 0;
-  // ascending compaction: x > x*, or x == x* among the first k_tie ties
-  int base = 0;
-  unsigned long long ties_before = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += SEL_THREADS) {
-    const int64_t i = c0 + tid;
-    uint32_t bits = 0;
-    if (i < n) bits = __float_as_uint(x[i]);
-    const int is_tie = (i < n) && bits == xstar;
-    int tie_tot;
-    const int tie_pos = sel_scan(is_tie, &tie_tot, scan_sh);
-    const int keep = (i < n) && (bits > xstar || (is_tie && ties_before + tie_pos < k_tie));
-    int tot;
-    const int pos = sel_scan(keep, &tot, scan_sh);
-    if (keep) out[base + pos] = (int32_t)i;
-    base += tot;
-    ties_before += tie_tot;
+  // ascending compaction: x > x*, or x == x* among the first k_tie ties (in
+  // index order). Each wave owns a contiguous index range; pass A counts its
+  // keeps and ties, one barrier, then pass B writes positions from ballots.
+  __shared__ int wave_gt[SEL_WAVES], wave_tie[SEL_WAVES];
+  const int64_t per = (n + SEL_WAVES - 1) / SEL_WAVES;
+  const int64_t w0 = min(n, (int64_t)wave * per), w1 = min(n, w0 + per);
+  int n_gt = 0, n_tie = 0;
+  for (int64_t i = w0 + lane; i < w1; i += 64) {
+    const uint32_t bits = __float_as_uint(x[i]);
+    n_gt += bits > xstar;
+    n_tie += bits == xstar;
   }
-  if (tid == 0) *cnt = base;
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    n_gt += __shfl_xor(n_gt, off, 64);
+    n_tie += __shfl_xor(n_tie, off, 64);
+  }
+  if (lane == 0) {
+    wave_gt[wave] = n_gt;
+    wave_tie[wave] = n_tie;
+  }
+  __syncthreads();
+  // this wave's output base, and the ties before its range
+  unsigned long long ties_before = 0, run_ties = 0;
+  int base = 0, total_kept = 0;
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const unsigned long long room = k_tie > run_ties ? k_tie - run_ties : 0;
+    const int kept_w = wave_gt[w] + (int)min((unsigned long long)wave_tie[w], room);
+    if (w < wave) base += kept_w;
+    if (w == wave) ties_before = run_ties;
+    total_kept += kept_w;
+    run_ties += (unsigned long long)wave_tie[w];
+  }
+  unsigned long long ties_seen = ties_before;
+  for (int64_t c0 = w0; c0 < w1; c0 += 64) {
+    const int64_t i = c0 + lane;
+    const uint32_t bits = i < w1 ? __float_as_uint(x[i]) : 0u;
+    const bool is_tie = i < w1 && bits == xstar;
+    const unsigned long long tmask = __ballot(is_tie);
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const unsigned long long tie_rank = ties_seen + __popcll(tmask & below);
+    const bool keep = i < w1 && (bits > xstar || (is_tie && tie_rank < k_tie));
+    const unsigned long long kmask = __ballot(keep);
+    if (keep) out[base + __popcll(kmask & below)] = (int32_t)i;
+    base += __popcll(kmask);
+    ties_seen += __popcll(tmask);
+  }
+  if (tid == 0) *cnt = total_kept;
 }
 
 size_t index_workspace_bytes(int Hq, int Hkv, int64_t n_global, int D, int last_q) {
@@ -419,7 +431,8 @@ int launch_index_build(int dtype, int D, TView q_last, int Hq, int last_q, TView
   } else {
     return VS_ERR_UNSUPPORTED;
   }
-  hipLaunchKernelGGL(index_combine_kernel, dim3((Hq * BLK + 255) / 256), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(index_combine_kernel, dim3((Hq * BLK + COMB_THREADS / 64 - 1) / (COMB_THREADS / 64)),
+                     dim3(COMB_THREADS), 0, stream, a);
   if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL((index_colsum_kernel<bf16, 128>), grid, block, 0, stream, a);
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((index_colsum_kernel<bf16, 64>), grid, block, 0, stream, a);
   else hipLaunchKernelGGL((index_colsum_kernel<float, 64>), grid, block, 0, stream, a);

@@ -48,3 +48,29 @@ def test_index_llama_group4_and_budget_edges():
 def test_index_qwen32k_full_size():
     from synth.inputs import CONFIGS
     _check_index(CONFIGS["qwen32k"])
+
+
+@pytest.mark.parametrize("p", [0.3, 0.55, 0.8, 0.95])
+def test_index_ties_at_cutoff(p):
+    """Identical key rows give bit-identical vertical scores; with them carrying
+    most of the mass, the top-p cutoff falls inside the tie group and the
+    selection must keep the lowest-indexed ties first (the oracle's rule
+    applied to the GPU's own scores, bit-exact)."""
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    cfg = config_by_name("tiny", top_p=p)
+    t = generate(cfg, tensors=("q", "k"))
+    k = t["k"].copy()
+    k[:, 300:420] = 3.0 * k[:, 300:301]     # 120 identical, dominant columns
+    k[:, 900:940] = k[:, 900:901]           # 40 more identical ones
+    N = cfg.N
+    q_last = t["q"][:, N - 64:]
+    lay = vs.layout("contig", 1, N)
+    out = H.gpu_index(H.to_dev(q_last, cfg.dtype), H.to_dev(k, cfg.dtype), lay, cfg.scale, p)
+    ref = oi.build_index(q_last, k, cfg.scale, N, p)
+    vert, _ = H.check_index(out, ref, p)
+    gv = out["v"].cpu().numpy()[0]
+    assert len(np.unique(gv[300:420])) == 1          # the group really ties
+    sel = set(vert[0].tolist())
+    inside = [i for i in range(300, 420) if i in sel]
+    assert inside == list(range(300, 300 + len(inside)))   # a prefix of the tie group
