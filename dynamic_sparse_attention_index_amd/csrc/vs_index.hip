@@ -263,8 +263,21 @@ struct SelectArgs {
   float top_p;
 };
 
+// round_half_even(x * 2^40) for a non-negative fp32 x <= 2^23, in integers:
+// x = m * 2^(E - 150) with the 24-bit significand m (E = 1 for subnormals),
+// so x * 2^40 = m * 2^(E - 110): a left shift, or a right shift rounded half
+// to even. Equal to rint((double)x * 2^40) for every such x (checked
+// exhaustively on the host); no fp64 arithmetic or f64 -> u64 conversion.
 __device__ __forceinline__ uint64_t fixed_mass(float x) {
-  return (uint64_t)__builtin_rint((double)x * 1099511627776.0);  // x * 2^40, exact for fp32 x
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t e = b >> 23, f = b & 0x7FFFFFu;
+  const uint64_t m = e ? (uint64_t)(f | 0x800000u) : (uint64_t)f;
+  const int sh = (e ? (int)e : 1) - 110;
+  if (sh >= 0) return m << sh;
+  const int r = -sh;
+  if (r >= 64) return 0;
+  const uint64_t q = m >> r, rem = m & ((1ull << r) - 1), half = 1ull << (r - 1);
+  return q + ((rem > half || (rem == half && (q & 1))) ? 1u : 0u);
 }
 
 // grid (Hq, 2): y = 0 vertical scores, y = 1 slash scores.
