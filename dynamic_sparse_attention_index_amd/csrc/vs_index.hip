@@ -255,6 +255,7 @@ __global__ void __launch_bounds__(512) index_colsum_kernel(IndexArgs a) {
 // ---- exact top-p selection ---------------------------------------------------
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_UNROLL = 8;   // loads in flight per thread in each sweep
 
 struct SelectArgs {
   const float* vert; const float* slash;
@@ -280,79 +281,131 @@ __device__ __forceinline__ uint64_t fixed_mass(float x) {
   return q + ((rem > half || (rem == half && (q & 1))) ? 1u : 0u);
 }
 
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave over a 256-digit mass histogram h (lane l holds digits 4l..4l+3).
+// With the suffix mass S(b) = sum of h[b'] for b' >= b, returns the digit
+// b* = the largest b >= 1 with S(b) >= rem (0 when there is none) and stores
+// S(b* + 1), the mass of the digits above it, in *above. The histogram total
+// goes to *total.
+__device__ __forceinline__ int sel_digit(const unsigned long long* h, unsigned long long rem, int lane,
+                                         unsigned long long* above, unsigned long long* total) {
+  unsigned long long v[4];
+  #pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = h[4 * lane + j];
+  const unsigned long long loc = v[0] + v[1] + v[2] + v[3];
+  unsigned long long suf = loc;   // inclusive suffix over lanes
+  #pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long t = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += t;
+  }
+  *total = __shfl(suf, 0, 64);
+  unsigned long long s = suf - loc;
+  int cnt = 0;
+  #pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    s += v[j];   // S(4 lane + j)
+    cnt += (4 * lane + j >= 1 && s >= rem) ? 1 : 0;
+  }
+  const int b = wave_sum_i32(cnt);
+  unsigned long long ab = 0;
+  #pragma unroll
+  for (int j = 0; j < 4; ++j) ab += (4 * lane + j > b) ? v[j] : 0ull;
+  *above = wave_sum_u64(ab);
+  return b;
+}
+
 // grid (Hq, 2): y = 0 vertical scores, y = 1 slash scores.
 __global__ void __launch_bounds__(SEL_THREADS) topp_select_kernel(SelectArgs a) {
   __shared__ unsigned long long hist[SEL_WAVES][256];
-  __shared__ unsigned long long red[SEL_WAVES];
   __shared__ unsigned long long sel_rem;
   __shared__ uint32_t sel_prefix;
+  __shared__ int sel_empty;
   const int h = blockIdx.x;
   const bool is_vert = blockIdx.y == 0;
-  const int64_t n = is_vert ? a.n_vert : a.n_slash;
+  const int n = is_vert ? (int)a.n_vert : a.n_slash;
   const float* x = is_vert ? a.vert + h * a.n_vert : a.slash + (int64_t)h * a.n_slash;
   int32_t* out = is_vert ? a.vert_idx + h * a.n_vert : a.slash_idx + (int64_t)h * a.n_slash;
   int32_t* cnt = is_vert ? a.vert_cnt + h : a.slash_cnt + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   if (a.top_p >= 1.f) {
-    for (int64_t i = tid; i < n; i += SEL_THREADS) out[i] = (int32_t)i;
-    if (tid == 0) *cnt = (int32_t)n;
+    for (int i = tid; i < n; i += SEL_THREADS) out[i] = i;
+    if (tid == 0) *cnt = n;
     return;
   }
   if (!(a.top_p > 0.f)) {
     if (tid == 0) *cnt = 0;
     return;
   }
-  // total fixed-point mass
-  unsigned long long s = 0;
-  for (int64_t i = tid; i < n; i += SEL_THREADS) s += fixed_mass(x[i]);
-  #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (lane == 0) red[wave] = s;
-  __syncthreads();
-  if (tid == 0) {
-    unsigned long long tot = 0;
-    for (int w = 0; w < SEL_WAVES; ++w) tot += red[w];
-    const unsigned long long pq = (unsigned long long)__builtin_rint((double)a.top_p * 4294967296.0);
-    const unsigned __int128 prod = (unsigned __int128)pq * tot;
-    sel_rem = (unsigned long long)((prod + 0xFFFFFFFFull) >> 32);   // ceil(pq * tot / 2^32)
-    sel_prefix = 0;
-  }
-  __syncthreads();
-  if (sel_rem == 0) {
-    if (tid == 0) *cnt = 0;
-    return;
-  }
-  // radix select on the fp32 bit pattern (non-negative: bit order = value order)
+  // Radix select on the fp32 bit pattern (non-negative: bit order = value
+  // order), 8 bits a pass, each digit weighted by its fixed-point mass. The
+  // first pass sees every score, so its histogram total is the whole mass
+  // and sets the target ceil(p * total).
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int b = lane; b < 256; b += 64) hist[wave][b] = 0;
-    __syncthreads();
-    const uint32_t prefix = sel_prefix;
-    for (int64_t i = tid; i < n; i += SEL_THREADS) {
-      const float xv = x[i];
-      const uint32_t bits = __float_as_uint(xv);
-      if ((bits & hi_mask) == prefix) atomicAdd(&hist[wave][(bits >> shift) & 255u], fixed_mass(xv));
+    const uint32_t prefix = pass == 0 ? 0u : sel_prefix;
+    unsigned long long* hw = hist[wave];
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) hw[lane + 64 * j] = 0;
+    for (int c0 = 0; c0 < n; c0 += SEL_THREADS * SEL_UNROLL) {
+      uint32_t bits[SEL_UNROLL];
+      #pragma unroll
+      for (int k = 0; k < SEL_UNROLL; ++k) {
+        const int i = c0 + tid + k * SEL_THREADS;
+        bits[k] = i < n ? __float_as_uint(x[i]) : 0u;
+      }
+      #pragma unroll
+      for (int k = 0; k < SEL_UNROLL; ++k) {
+        const int i = c0 + tid + k * SEL_THREADS;
+        if (i < n && (bits[k] & hi_mask) == prefix)
+          atomicAdd(&hw[(bits[k] >> shift) & 255u], fixed_mass(__uint_as_float(bits[k])));
+      }
     }
     __syncthreads();
     if (tid < 256) {
       unsigned long long t = 0;
+      #pragma unroll
       for (int w = 0; w < SEL_WAVES; ++w) t += hist[w][tid];
       hist[0][tid] = t;
     }
     __syncthreads();
-    if (tid == 0) {
-      unsigned long long rem = sel_rem, above = 0;
-      int b = 255;
-      for (; b > 0; --b) {
-        if (above + hist[0][b] >= rem) break;
-        above += hist[0][b];
+    if (wave == 0) {
+      unsigned long long rem = pass == 0 ? 0ull : sel_rem, above, total;
+      if (pass == 0) {
+        // the target needs the total first: a second wave-wide sum
+        unsigned long long loc = 0;
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) loc += hist[0][4 * lane + j];
+        const unsigned long long tot = wave_sum_u64(loc);
+        const unsigned long long pq = (unsigned long long)__builtin_rint((double)a.top_p * 4294967296.0);
+        const unsigned __int128 prod = (unsigned __int128)pq * tot;
+        rem = (unsigned long long)((prod + 0xFFFFFFFFull) >> 32);   // ceil(pq * tot / 2^32)
       }
-      sel_rem = rem - above;
-      sel_prefix = prefix | ((uint32_t)b << shift);
+      const int b = sel_digit(hist[0], rem, lane, &above, &total);
+      if (lane == 0) {
+        sel_empty = rem == 0;
+        sel_rem = rem - above;
+        sel_prefix = prefix | ((uint32_t)b << shift);
+      }
     }
     __syncthreads();
+    if (sel_empty) {
+      if (tid == 0) *cnt = 0;
+      return;
+    }
   }
   const uint32_t xstar = sel_prefix;
   const unsigned long long qstar = fixed_mass(__uint_as_float(xstar));
@@ -361,19 +414,25 @@ __global__ void __launch_bounds__(SEL_THREADS) topp_select_kernel(SelectArgs a) 
   // index order). Each wave owns a contiguous index range; pass A counts its
   // keeps and ties, one barrier, then pass B writes positions from ballots.
   __shared__ int wave_gt[SEL_WAVES], wave_tie[SEL_WAVES];
-  const int64_t per = (n + SEL_WAVES - 1) / SEL_WAVES;
-  const int64_t w0 = min(n, (int64_t)wave * per), w1 = min(n, w0 + per);
+  const int per = (n + SEL_WAVES - 1) / SEL_WAVES;
+  const int w0 = min(n, wave * per), w1 = min(n, w0 + per);
   int n_gt = 0, n_tie = 0;
-  for (int64_t i = w0 + lane; i < w1; i += 64) {
-    const uint32_t bits = __float_as_uint(x[i]);
-    n_gt += bits > xstar;
-    n_tie += bits == xstar;
+  for (int c0 = w0; c0 < w1; c0 += 64 * SEL_UNROLL) {
+    uint32_t bits[SEL_UNROLL];
+    #pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int i = c0 + lane + 64 * k;
+      bits[k] = i < w1 ? __float_as_uint(x[i]) : 0u;
+    }
+    #pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const bool ok = c0 + lane + 64 * k < w1;
+      n_gt += (ok && bits[k] > xstar) ? 1 : 0;
+      n_tie += (ok && bits[k] == xstar) ? 1 : 0;
+    }
   }
-  #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    n_gt += __shfl_xor(n_gt, off, 64);
-    n_tie += __shfl_xor(n_tie, off, 64);
-  }
+  n_gt = wave_sum_i32(n_gt);
+  n_tie = wave_sum_i32(n_tie);
   if (lane == 0) {
     wave_gt[wave] = n_gt;
     wave_tie[wave] = n_tie;
@@ -391,18 +450,27 @@ __global__ void __launch_bounds__(SEL_THREADS) topp_select_kernel(SelectArgs a) 
     run_ties += (unsigned long long)wave_tie[w];
   }
   unsigned long long ties_seen = ties_before;
-  for (int64_t c0 = w0; c0 < w1; c0 += 64) {
-    const int64_t i = c0 + lane;
-    const uint32_t bits = i < w1 ? __float_as_uint(x[i]) : 0u;
-    const bool is_tie = i < w1 && bits == xstar;
-    const unsigned long long tmask = __ballot(is_tie);
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const unsigned long long tie_rank = ties_seen + __popcll(tmask & below);
-    const bool keep = i < w1 && (bits > xstar || (is_tie && tie_rank < k_tie));
-    const unsigned long long kmask = __ballot(keep);
-    if (keep) out[base + __popcll(kmask & below)] = (int32_t)i;
-    base += __popcll(kmask);
-    ties_seen += __popcll(tmask);
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = w0; c0 < w1; c0 += 64 * SEL_UNROLL) {
+    uint32_t bits[SEL_UNROLL];
+    #pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int i = c0 + lane + 64 * k;
+      bits[k] = i < w1 ? __float_as_uint(x[i]) : 0u;
+    }
+    #pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int i = c0 + lane + 64 * k;
+      const bool ok = i < w1;
+      const bool is_tie = ok && bits[k] == xstar;
+      const unsigned long long tmask = __ballot(is_tie);
+      const unsigned long long tie_rank = ties_seen + __popcll(tmask & below);
+      const bool keep = ok && (bits[k] > xstar || (is_tie && tie_rank < k_tie));
+      const unsigned long long kmask = __ballot(keep);
+      if (keep) out[base + __popcll(kmask & below)] = i;
+      base += __popcll(kmask);
+      ties_seen += __popcll(tmask);
+    }
   }
   if (tid == 0) *cnt = total_kept;
 }
