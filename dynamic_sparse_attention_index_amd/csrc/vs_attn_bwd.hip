@@ -26,7 +26,7 @@
 namespace vs {
 
 constexpr int BWD_THREADS = 256;
-constexpr int VERT_SEG = 256;          // query blocks per vertical work item
+constexpr int VERT_SEG = 128;          // query blocks per vertical work item
 constexpr int VERT_GRID = 2048;        // persistent workgroups for vertical columns
 
 struct BwdArgs {
@@ -366,7 +366,10 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
       if (r < n) break;
       r -= n;
     }
-    const int chunk = (int)(r / nseg), seg = (int)(r % nseg);
+    // segments rotate with the chunk: the dispatcher deals workgroups to the
+    // eight XCDs in turn, and without the rotation one XCD would get every
+    // chunk's last (always full) segment
+    const int chunk = (int)(r / nseg), seg = (int)((r % nseg + chunk) % nseg);
     const int kvh = h / grp;
     const int cnt = a.vloc_cnt[h];
     const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
@@ -1066,7 +1069,10 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
       if (r < n) break;
       r -= n;
     }
-    const int chunk = (int)(r / nseg), seg = (int)(r % nseg);
+    // segments rotate with the chunk: the dispatcher deals workgroups to the
+    // eight XCDs in turn, and without the rotation one XCD would get every
+    // chunk's last (always full) segment
+    const int chunk = (int)(r / nseg), seg = (int)((r % nseg + chunk) % nseg);
     const int kvh = h / grp;
     const int cnt = a.vloc_cnt[h];
     const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
