@@ -151,11 +151,10 @@ __global__ void __launch_bounds__(BWD_THREADS) dq_kernel(BwdArgs a) {
   __shared__ int thr_sh[BLK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
-  const int nitems = a.Hq * a.QB;
-  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
-  if (item < 0) return;
-  const int I = a.QB - 1 - item / a.Hq;
-  const int h = item % a.Hq;
+  int rank_i, hh_i, g_i;
+  if (!xcd_group_item(blockIdx.x, a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv, &rank_i, &hh_i, &g_i)) return;
+  const int I = a.QB - 1 - rank_i;
+  const int h = g_i * (a.Hq / a.Hkv) + hh_i;
   const int kvh = h / (a.Hq / a.Hkv);
   const int64_t u = (int64_t)h * a.QB + I;
   const int rowoff = wave * 16 + n16;
@@ -293,10 +292,8 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_kernel(BwdArgs a) {
   __shared__ float lse_sh[BLK], dl_sh[BLK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
-  const int nitems = a.Hkv * a.KB;
-  const int item = xcd_cluster_item(blockIdx.x, nitems, kmajor_csize(a.Hkv));
-  if (item < 0) return;
-  const int J = item / a.Hkv, kvh = item % a.Hkv;
+  int J, kvh, hh_unused;
+  if (!xcd_group_item(blockIdx.x, a.Hkv, a.KB, KMAJOR_BPC, 1, &J, &hh_unused, &kvh)) return;
   const int grp = a.Hq / a.Hkv;
   const int keyoff = wave * 16 + n16;
   const int64_t krow = (int64_t)J * BLK + keyoff;
@@ -449,11 +446,10 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int rh = wave & 1, kh = wave >> 1;
-  const int nitems = a.Hq * a.QB;
-  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
-  if (item < 0) return;
-  const int I = a.QB - 1 - item / a.Hq;
-  const int h = item % a.Hq;
+  int rank_i, hh_i, g_i;
+  if (!xcd_group_item(blockIdx.x, a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv, &rank_i, &hh_i, &g_i)) return;
+  const int I = a.QB - 1 - rank_i;
+  const int h = g_i * (a.Hq / a.Hkv) + hh_i;
   const int kvh = h / (a.Hq / a.Hkv);
   const int64_t u = (int64_t)h * a.QB + I;
   const int64_t row_base = (int64_t)I * BLK + 32 * rh;
@@ -873,10 +869,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   const DmaLane dlane = dma_lane(wave, lane);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int kh = wave >> 1, rh = wave & 1;
-  const int nitems = a.Hkv * a.KB;
-  const int item = xcd_cluster_item(blockIdx.x, nitems, kmajor_csize(a.Hkv));
-  if (item < 0) return;
-  const int J = item / a.Hkv, kvh = item % a.Hkv;
+  int J, kvh, hh_unused;
+  if (!xcd_group_item(blockIdx.x, a.Hkv, a.KB, KMAJOR_BPC, 1, &J, &hh_unused, &kvh)) return;
   const int grp = a.Hq / a.Hkv;
   // The walk is the concatenation of the group's q heads' CSC lists for this
   // key block. Per-head ranges sit in lanes 0 .. grp-1 and are read back with
@@ -1171,9 +1165,9 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
 template <typename T, int D>
 static void launch_bwd_typed(const BwdArgs& a, int parts, hipStream_t stream) {
   if (parts & VS_BWD_DQ)
-    hipLaunchKernelGGL((dq_kernel<T, D>), dim3(xcd_cluster_grid(a.Hq * a.QB, qmajor_csize(a.Hq))), dim3(BWD_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<T, D>), dim3(xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv)), dim3(BWD_THREADS), 0, stream, a);
   if (parts & VS_BWD_DKDV)
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(xcd_cluster_grid(a.Hkv * a.KB, kmajor_csize(a.Hkv))), dim3(BWD_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(xcd_group_grid(a.Hkv, a.KB, KMAJOR_BPC, 1)), dim3(BWD_THREADS), 0, stream, a);
   if (parts & VS_BWD_DKDV_VERT)
     hipLaunchKernelGGL((dkdv_vert_kernel<T, D>), dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
 }
@@ -1200,9 +1194,9 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
       return VS_ERR_UNSUPPORTED;
     if (a.Hq / a.Hkv > 8) return VS_ERR_UNSUPPORTED;
     if (parts & VS_BWD_DQ)
-      hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3(xcd_cluster_grid(a.Hq * a.QB, qmajor_csize(a.Hq))), dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3(xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv)), dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV)
-      hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3(xcd_cluster_grid(a.Hkv * a.KB, kmajor_csize(a.Hkv))), dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3(xcd_group_grid(a.Hkv, a.KB, KMAJOR_BPC, 1)), dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV_VERT)
       hipLaunchKernelGGL(dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
   }

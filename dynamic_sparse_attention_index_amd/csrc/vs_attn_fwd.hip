@@ -61,12 +61,11 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
-  // work item: heavy (late) query blocks first, clustered per XCD
-  const int nitems = a.Hq * a.QB;
-  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
-  if (item < 0) return;
-  const int I = a.QB - 1 - item / a.Hq;
-  const int h = item % a.Hq;
+  // work item: heavy (late) query blocks first, clustered per XCD and kv group
+  int rank_i, hh_i, g_i;
+  if (!xcd_group_item(blockIdx.x, a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv, &rank_i, &hh_i, &g_i)) return;
+  const int I = a.QB - 1 - rank_i;
+  const int h = g_i * (a.Hq / a.Hkv) + hh_i;
   const int kvh = h / (a.Hq / a.Hkv);
   const int64_t u = (int64_t)h * a.QB + I;
   const int rowoff = wave * 16 + n16;  // this lane's query row within the block
@@ -314,11 +313,10 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int rh = wave & 1, kh = wave >> 1;   // row half, key half
-  const int nitems = a.Hq * a.QB;
-  const int item = xcd_cluster_item(blockIdx.x, nitems, qmajor_csize(a.Hq));
-  if (item < 0) return;
-  const int I = a.QB - 1 - item / a.Hq;
-  const int h = item % a.Hq;
+  int rank_i, hh_i, g_i;
+  if (!xcd_group_item(blockIdx.x, a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv, &rank_i, &hh_i, &g_i)) return;
+  const int I = a.QB - 1 - rank_i;
+  const int h = g_i * (a.Hq / a.Hkv) + hh_i;
   const int kvh = h / (a.Hq / a.Hkv);
   const int64_t u = (int64_t)h * a.QB + I;
   const int64_t row_base = (int64_t)I * BLK + 32 * rh;   // this wave's first query row
@@ -602,7 +600,7 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
-  const dim3 grid(xcd_cluster_grid(m->Hq * m->QB, qmajor_csize(m->Hq))), block(FWD_THREADS);
+  const dim3 grid(xcd_group_grid(m->Hkv, m->QB, QMAJOR_BPC, m->Hq / m->Hkv)), block(FWD_THREADS);
   if (dtype == VS_BF16 && D == 128) {
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     const int64_t krows = (int64_t)m->KB * BLK;

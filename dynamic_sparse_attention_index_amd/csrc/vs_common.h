@@ -55,26 +55,35 @@ __device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
 }
 
 // --- work order across XCDs ---------------------------------------------------
-// Callers number their work items heavy-first (causal work shrinks along the
-// item order). Items are taken in clusters of `csize` consecutive items and
-// cluster k runs on XCD k % 8 (the dispatcher deals blocks to the 8 XCDs
-// round-robin), so every XCD gets an even share of heavy and light clusters and
-// the blocks resident on one XCD at a time work on neighbouring items, whose
-// tiles its L2 then serves more than once. The grid is rounded up to whole
-// rounds of 8 clusters; blocks past the last item get -1 and return at once.
-__device__ __forceinline__ int xcd_cluster_item(int b, int nitems, int csize) {
-  const int x = b & 7, j = b >> 3;
-  const int item = ((j / csize) * 8 + x) * csize + j % csize;
-  return item < nitems ? item : -1;
+// A work item is (block rank, head within its kv group, kv group); block rank
+// 0 is the heaviest (causal work shrinks along the rank). Items are taken in
+// clusters of `bpc` consecutive block ranks x the `hpg` heads of ONE kv group,
+// and cluster c runs on XCD c % 8 (the dispatcher deals workgroups to the 8
+// XCDs in turn). Round r = c / 8 gives all 8 XCDs the same kv group
+// (r % G) and 8 neighbouring block groups, so the workgroups resident on an
+// XCD at a time work on one kv head's K/V (or one group's Q/dO) and on
+// neighbouring blocks whose tiles its L2 serves more than once, while over
+// the rounds every XCD gets an even share of every group and of heavy and
+// light blocks. The grid is rounded up to whole rounds; workgroups past the
+// last block return false and exit at once.
+__device__ __forceinline__ bool xcd_group_item(int b, int G, int nblk, int bpc, int hpg, int* blk, int* hh,
+                                               int* g) {
+  const int csize = bpc * hpg;
+  const int x = b & 7, r = (b >> 3) / csize, k = (b >> 3) % csize;
+  *g = r % G;
+  *blk = ((r / G) * 8 + x) * bpc + k / hpg;
+  *hh = k % hpg;
+  return *blk < nblk;
 }
-__host__ inline unsigned xcd_cluster_grid(int nitems, int csize) {
-  const int nclusters = (nitems + csize - 1) / csize;
-  return (unsigned)(((nclusters + 7) / 8) * 8 * csize);
+__host__ inline unsigned xcd_group_grid(int G, int nblk, int bpc, int hpg) {
+  const int nbg = (nblk + bpc - 1) / bpc;
+  return (unsigned)(G * ((nbg + 7) / 8) * 8 * bpc * hpg);
 }
-// Query-major kernels: 8 query blocks x all heads per cluster.
-__host__ __device__ __forceinline__ int qmajor_csize(int Hq) { return 8 * Hq; }
-// Key-major kernels: 8 key blocks x all kv heads per cluster.
-__host__ __device__ __forceinline__ int kmajor_csize(int Hkv) { return 8 * Hkv; }
+// Query-major kernels (two workgroups per CU, 64 per XCD): clusters of 8
+// query blocks x the group's q heads. Key-major kernels (one workgroup per CU,
+// 32 per XCD): clusters of 32 key blocks of one kv head.
+constexpr int QMAJOR_BPC = 8;
+constexpr int KMAJOR_BPC = 32;
 
 // --- layout maps -------------------------------------------------------------
 // Global 64-block of local block J of rank `rank` (NB = local blocks per shard).
