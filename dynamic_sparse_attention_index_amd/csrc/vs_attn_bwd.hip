@@ -559,17 +559,31 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
         }
       split8(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
     }
-    // dQ^T += K^T dS^T over this wave's 32 keys
+    // dQ^T += K^T dS^T over this wave's 32 keys; the transposed K operand of
+    // block dt + 1 is read after the first MFMA of block dt
     const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
+    bf16x8 ka[2];
+    auto rdk = [&](int dt, int b) {
+      const int lc = 2 * dt + ((n16 & 3) >> 1);
+      ka[b] = lds_read_tr16_x2(Ks + tile_off(vr, lc) + 4 * (n16 & 1), D);
+    };
+    rdk(0, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int lc = 2 * dt + ((n16 & 3) >> 1);
-      const bf16x8 ka = lds_read_tr16_x2(Ks + tile_off(vr, lc) + 4 * (n16 & 1), D);
+      if (dt + 1 < 8) rdk(dt + 1, (dt + 1) & 1);
+      const int b = dt & 1;
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
-        acc[rs][dt] = mfma_bf16(ka, dsh[rs], acc[rs][dt]);
-        acc[rs][dt] = mfma_bf16(ka, dsl[rs], acc[rs][dt]);
+        acc[rs][dt] = mfma_bf16(ka[b], dsh[rs], acc[rs][dt]);
+        acc[rs][dt] = mfma_bf16(ka[b], dsl[rs], acc[rs][dt]);
       }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     }
   };
 
@@ -606,6 +620,9 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   }
 }
 
+__device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf16x8* ph, const bf16x8* pl,
+                                        const bf16x8* dh, const bf16x8* dl, int rh, int g4, int n16,
+                                        f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8]);
 // Key-major core: wave (kh, rh) holds keys 32 kh + 16 kt + n (kt = 0, 1) as
 // K/V fragments and processes rows 32 rh .. 32 rh + 31 of a staged query block
 // (Q, dO tiles; per-row lse in log2 units and delta). thr[kt]: rows with
@@ -659,20 +676,7 @@ __device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const f
     split8(ds[0], ds[1], dh[kt], dl[kt]);
   }
   // dV^T += dO^T P, dK^T += Q^T dS over the wave's 32 rows
-  const int rr = 32 * rh + 8 * g4 + (n16 >> 2);
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const int lc = 2 * dt + ((n16 & 3) >> 1);
-    const bf16x8 oT = lds_read_tr16_x2(Os + tile_off(rr, lc) + 4 * (n16 & 1), D);
-    const bf16x8 qT = lds_read_tr16_x2(Qs + tile_off(rr, lc) + 4 * (n16 & 1), D);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      acc_dv[kt][dt] = mfma_bf16(oT, ph[kt], acc_dv[kt][dt]);
-      acc_dv[kt][dt] = mfma_bf16(oT, pl[kt], acc_dv[kt][dt]);
-      acc_dk[kt][dt] = mfma_bf16(qT, dh[kt], acc_dk[kt][dt]);
-      acc_dk[kt][dt] = mfma_bf16(qT, dl[kt], acc_dk[kt][dt]);
-    }
-  }
+  kv_grad(Qs, Os, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
 }
 
 // The two halves of kv_block, for the software-pipelined dK/dV kernel:
@@ -754,18 +758,36 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
                                         f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8]) {
   constexpr int D = TD;
   const int rr = 32 * rh + 8 * g4 + (n16 >> 2);
+  // The transposed operands of column block dt + 1 are read while the eight
+  // MFMAs of block dt run (two register sets, order pinned below); with one
+  // set every block would wait out a full LDS round trip.
+  bf16x8 oT[2], qT[2];
+  auto rd = [&](int dt, int b) {
+    const int lc = 2 * dt + ((n16 & 3) >> 1);
+    oT[b] = lds_read_tr16_x2(Os + tile_off(rr, lc) + 4 * (n16 & 1), D);
+    qT[b] = lds_read_tr16_x2(Qs + tile_off(rr, lc) + 4 * (n16 & 1), D);
+  };
+  rd(0, 0);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const int lc = 2 * dt + ((n16 & 3) >> 1);
-    const bf16x8 oT = lds_read_tr16_x2(Os + tile_off(rr, lc) + 4 * (n16 & 1), D);
-    const bf16x8 qT = lds_read_tr16_x2(Qs + tile_off(rr, lc) + 4 * (n16 & 1), D);
+    if (dt + 1 < 8) rd(dt + 1, (dt + 1) & 1);
+    const int b = dt & 1;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      acc_dv[kt][dt] = mfma_bf16(oT, ph[kt], acc_dv[kt][dt]);
-      acc_dv[kt][dt] = mfma_bf16(oT, pl[kt], acc_dv[kt][dt]);
-      acc_dk[kt][dt] = mfma_bf16(qT, dh[kt], acc_dk[kt][dt]);
-      acc_dk[kt][dt] = mfma_bf16(qT, dl[kt], acc_dk[kt][dt]);
+      acc_dv[kt][dt] = mfma_bf16(oT[b], ph[kt], acc_dv[kt][dt]);
+      acc_dv[kt][dt] = mfma_bf16(oT[b], pl[kt], acc_dv[kt][dt]);
+      acc_dk[kt][dt] = mfma_bf16(qT[b], dh[kt], acc_dk[kt][dt]);
+      acc_dk[kt][dt] = mfma_bf16(qT[b], dl[kt], acc_dk[kt][dt]);
     }
+  }
+  // reads of block dt + 1 go out after the first MFMA of block dt, so the
+  // wait in front of that MFMA covers block dt's reads only
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 7, 0);
   }
 }
 

@@ -471,21 +471,31 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T by 16-column blocks dt of V; the transposed V operand of
+    // block dt + 1 is read after the first MFMA of block dt (two register
+    // sets, order pinned below), so only block 0 waits out an LDS round trip
     const bf16* Vs = Vst.template operator()<p>();
     const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
     const int vb = (n16 & 3) >> 1, vo = 4 * (n16 & 1);
+    bf16x8 va[2];
+    auto rdv = [&](int dt, int b) { va[b] = lds_read_tr16_x2(Vs + tile_off(vr, 2 * dt + vb) + vo, D); };
+    rdv(0, 0);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      bf16x8 va[4];
-      lds_read_tr16_x2_4(Vs + tile_off(vr, 8 * q + vb) + vo, Vs + tile_off(vr, 8 * q + 2 + vb) + vo,
-                         Vs + tile_off(vr, 8 * q + 4 + vb) + vo, Vs + tile_off(vr, 8 * q + 6 + vb) + vo, va);
+    for (int dt = 0; dt < 8; ++dt) {
+      if (dt + 1 < 8) rdv(dt + 1, (dt + 1) & 1);
 #pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
+      for (int rs = 0; rs < 2; ++rs) {
+        acc[rs][dt] = mfma_bf16(va[dt & 1], pf[rs], acc[rs][dt]);
+        acc[rs][dt] = mfma_bf16(va[dt & 1], pl[rs], acc[rs][dt]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int rs = 0; rs < 2; ++rs) {
-          acc[rs][4 * q + d4] = mfma_bf16(va[d4], pf[rs], acc[rs][4 * q + d4]);
-          acc[rs][4 * q + d4] = mfma_bf16(va[d4], pl[rs], acc[rs][4 * q + d4]);
-        }
+    for (int dt = 0; dt < 8; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     }
   };
 
