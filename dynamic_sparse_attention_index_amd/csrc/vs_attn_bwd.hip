@@ -419,15 +419,6 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 // copies, two stages, one barrier per tile; each wave covers 32 rows x 32 keys.
 
 // Split 8 fp32 weights into a bf16 hi/lo pair of MFMA operands.
-__device__ __forceinline__ void split8(const f32x4& w0, const f32x4& w1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16 h0, l0, h1, l1;
-    split_bf16(w0[i], h0, l0);
-    split_bf16(w1[i], h1, l1);
-    hi[i] = h0; lo[i] = l0; hi[4 + i] = h1; lo[4 + i] = l1;
-  }
-}
 
 // dQ, query-major. Wave (rh, kh) = rows 32 rh.. of the block, keys 32 kh.. of
 // every tile; the two key halves' partial dQ are added through LDS at the end.

@@ -450,17 +450,15 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
       float psum = 0.f;
+      f32x4 pr[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -m_use[rs]));
-          psum += pr;
-          bf16 hi, lo;
-          split_bf16(pr, hi, lo);
-          pf[rs][4 * t + i] = hi;
-          pl[rs][4 * t + i] = lo;
+          pr[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -m_use[rs]));
+          psum += pr[t][i];
         }
+      split8(pr[0], pr[1], pf[rs], pl[rs]);
       l_run[rs] = l_run[rs] * alpha[rs] + psum;
     }
     qk.template operator()<pk>(s_next);

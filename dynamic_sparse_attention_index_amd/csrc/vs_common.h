@@ -235,9 +235,26 @@ __device__ __forceinline__ float group4_sum(float v) {
 }
 
 // Round 8 fp32 weights to a bf16 pair (hi = bf16(w), lo = bf16(w - hi)).
-__device__ __forceinline__ void split_bf16(float w, bf16& hi, bf16& lo) {
-  hi = (bf16)w;
-  lo = (bf16)(w - (float)hi);
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+// hi = bf16(w) (round to nearest even), lo = bf16(w - hi), for two values at
+// once: one packed convert per pair for each half, and the hi halves widened
+// back to fp32 by a shift and a mask.
+__device__ __forceinline__ void split_pair(float w0, float w1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0, w1}, bf16x2));
+  const float h0 = __builtin_bit_cast(float, hi << 16), h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0 - h0, w1 - h1}, bf16x2));
+}
+// split_pair over eight values: element i of (hi, lo) is w0[i] for i < 4 and
+// w1[i - 4] otherwise.
+__device__ __forceinline__ void split8(const f32x4& w0, const f32x4& w1, bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+  split_pair(w0[0], w0[1], h[0], l[0]);
+  split_pair(w0[2], w0[3], h[1], l[1]);
+  split_pair(w1[0], w1[1], h[2], l[2]);
+  split_pair(w1[2], w1[3], h[3], l[3]);
+  hi = __builtin_bit_cast(bf16x8, i32x4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
+  lo = __builtin_bit_cast(bf16x8, i32x4{(int)l[0], (int)l[1], (int)l[2], (int)l[3]});
 }
 
 }  // namespace vs
