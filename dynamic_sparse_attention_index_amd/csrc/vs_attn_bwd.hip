@@ -611,64 +611,6 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   }
 }
 
-__device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf16x8* ph, const bf16x8* pl,
-                                        const bf16x8* dh, const bf16x8* dl, int rh, int g4, int n16,
-                                        f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8]);
-// Key-major core: wave (kh, rh) holds keys 32 kh + 16 kt + n (kt = 0, 1) as
-// K/V fragments and processes rows 32 rh .. 32 rh + 31 of a staged query block
-// (Q, dO tiles; per-row lse in log2 units and delta). thr[kt]: rows with
-// offset below it are inactive for key kt of this lane.
-__device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const float* lsh, const float* dsh_,
-                                         const bf16x8 (*kf)[4], const bf16x8 (*vf)[4], const int* thr,
-                                         int kh, int rh, int g4, int n16, float sl2, f32x4 (*acc_dk)[8],
-                                         f32x4 (*acc_dv)[8]) {
-  (void)kh;
-  constexpr int D = TD;
-  // S and dP, rows 32 rh + 8 g + 4 t + i (lane's column = key n)
-  f32x4 s[2][2], dp[2][2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int qr = 32 * rh + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) s[kt][t] = dp[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 qa = *(const bf16x8*)(Qs + tile_off(qr, 4 * ks + g4));
-      const bf16x8 oa = *(const bf16x8*)(Os + tile_off(qr, 4 * ks + g4));
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[kt][t] = mfma_bf16(qa, kf[kt][ks], s[kt][t]);
-        dp[kt][t] = mfma_bf16(oa, vf[kt][ks], dp[kt][t]);
-      }
-    }
-  }
-  const int r0 = 32 * rh + 8 * g4;
-  f32x4 l2[2] = {*(const f32x4*)(lsh + r0), *(const f32x4*)(lsh + r0 + 4)};   // natural log
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) l2[t][i] *= LOG2E;
-  const f32x4 dd[2] = {*(const f32x4*)(dsh_ + r0), *(const f32x4*)(dsh_ + r0 + 4)};
-  bf16x8 ph[2], pl[2], dh[2], dl[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    f32x4 ds[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + 4 * t + i;
-        const bool act = r >= thr[kt] && l2[t][i] > -INFINITY;
-        const float p = act ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][t][i], sl2, -l2[t][i])) : 0.f;
-        s[kt][t][i] = p;
-        ds[t][i] = p * (dp[kt][t][i] - dd[t][i]);
-      }
-    split8(s[kt][0], s[kt][1], ph[kt], pl[kt]);
-    split8(ds[0], ds[1], dh[kt], dl[kt]);
-  }
-  // dV^T += dO^T P, dK^T += Q^T dS over the wave's 32 rows
-  kv_grad(Qs, Os, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
-}
 
 // The two halves of kv_block, for the software-pipelined dK/dV kernel:
 // kv_sdp computes S and dP of a staged tile (MFMA only); kv_grad turns them
@@ -700,16 +642,27 @@ __device__ __forceinline__ void kv_sdp(const bf16x8 (*qa)[4], const bf16x8 (*oa)
       }
   }
 }
-// per-row lse (log2 units) and delta of the wave's rows 32 rh + 8 g + 4 t + i
+// The staged row LSE in log2 units, +inf for an empty row (so exp2(S * scale
+// - LSE) is 0 there without a per-element select); one wave converts a
+// staged tile's 64 values in place.
+__device__ __forceinline__ void lse_to_log2(float* lsh, int lane) {
+  const float v = lsh[lane];
+  lsh[lane] = v == -INFINITY ? INFINITY : v * LOG2E;
+}
+// per-row lse and delta of the wave's rows 32 rh + 8 g + 4 t + i; LOG2 says
+// whether the staged LSE was already converted by lse_to_log2
+template <bool LOG2>
 __device__ __forceinline__ void kv_rowstats(const float* lsh, const float* dsh_, int rh, int g4, f32x4* l2,
                                             f32x4* dd) {
   const int r0 = 32 * rh + 8 * g4;
   l2[0] = *(const f32x4*)(lsh + r0);
   l2[1] = *(const f32x4*)(lsh + r0 + 4);
+  if constexpr (!LOG2) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l2[t][i] = l2[t][i] == -INFINITY ? INFINITY : l2[t][i] * LOG2E;
+      for (int i = 0; i < 4; ++i) l2[t][i] = l2[t][i] == -INFINITY ? INFINITY : l2[t][i] * LOG2E;
+  }
   dd[0] = *(const f32x4*)(dsh_ + r0);
   dd[1] = *(const f32x4*)(dsh_ + r0 + 4);
 }
@@ -780,6 +733,27 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
     if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 7, 0);
   }
+}
+
+// One staged query block against the wave's keys, without pipelining (the
+// vertical-column kernel): thr[kt] = rows of the block with offset below it
+// are inactive for key kt of this lane (BLK: the whole block); the LSE is
+// staged in natural-log units.
+__device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const float* lsh, const float* dsh_,
+                                         const bf16x8 (*kf)[4], const bf16x8 (*vf)[4], const int* thr,
+                                         int rh, int g4, int n16, float sl2, f32x4 (*acc_dk)[8],
+                                         f32x4 (*acc_dv)[8]) {
+  bf16x8 qa[2][4], oa[2][4];
+  kv_frag(Qs, Os, rh, g4, n16, qa, oa);
+  f32x4 s[2][2], dp[2][2];
+  kv_sdp(qa, oa, kf, vf, s, dp);
+  f32x4 l2[2], dd[2];
+  kv_rowstats<false>(lsh, dsh_, rh, g4, l2, dd);
+  // thresholds apply under a wave-uniform branch: most blocks have none
+  const int masked = __builtin_amdgcn_ballot_w64(thr[0] != 0 || thr[1] != 0) != 0ull ? 1 : 0;
+  bf16x8 ph[2], pl[2], dh[2], dl[2];
+  kv_pds(s, dp, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl);
+  kv_grad(Qs, Os, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
 }
 
 // Copy the Q and dO rows of query block I of head h and its lse/delta.
@@ -985,9 +959,11 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
     const bf16* Qn = QOst.template operator()<p1>();
     bf16x8 qa[2][4], oa[2][4];
     kv_frag(Qn, Qn + TILE_ELEMS, rh, g4, n16, qa, oa);
+    // tile i + 1's LSE has landed: wave 0 converts it for step i + 1
+    if (wave == 0) lse_to_log2(Lst.template operator()<p1>(), lane);
     f32x4 l2[2], dd[2];
     const float* Lc = Lst.template operator()<p>();
-    kv_rowstats(Lc, Lc + BLK, rh, g4, l2, dd);
+    kv_rowstats<true>(Lc, Lc + BLK, rh, g4, l2, dd);
     int thr[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) thr[kt] = 32 * kh + 16 * kt + n16;
@@ -1024,6 +1000,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   if (total > 1) diag_n1 = issue.template operator()<1>(1);
   wait_all_mem();
   __syncthreads();
+  if (wave == 0) lse_to_log2(L0, lane);   // tile 0's LSE, seen after step 0's barrier
   {
     bf16x8 qa[2][4], oa[2][4];
     kv_frag(QO0, QO0 + TILE_ELEMS, rh, g4, n16, qa, oa);
@@ -1125,7 +1102,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
         thr[kt] = BLK;
         if (valid[kt] && j >= 0 && !((sbits[j >> 5] >> (j & 31)) & 1u)) thr[kt] = (j == 0) ? (m[kt] % BLK) : 0;
       }
-      kv_block(Qs, Os, Ls, Ls + BLK, kf, vf, thr, kh, rh, g4, n16, sl2, acc_dk, acc_dv);
+      kv_block(Qs, Os, Ls, Ls + BLK, kf, vf, thr, rh, g4, n16, sl2, acc_dk, acc_dv);
     };
     stage_qblock(Q0, O0, L0, a, h, I_lo, wave, lane, dlane);
     for (int it = 0; it < total; it += 2) {
