@@ -107,3 +107,93 @@ def build_index(q_last, k, scale, n_global, top_p):
     vert = [select_top_p(v[h], top_p) for h in range(v.shape[0])]
     slash = [select_top_p(s[h], top_p) for h in range(s.shape[0])]
     return {"v": v, "s": s, "lse": lse, "vert": vert, "slash": slash}
+
+
+def rank_row_stats(q_last, k_shard, pos, scale, n_global):
+    """One rank's partial row statistics over the keys it holds.
+
+    The distributed index of the same section (三.2, item 1): the scored
+    queries are broadcast, every rank scores them against its local keys only
+    and keeps, per scored row, the running maximum and the sum of exponentials
+    relative to it (the two numbers an exchange needs to rebuild the row's
+    log-sum-exp).
+
+    k_shard: [Hkv, n_local, D] the rank's keys, at global positions ``pos``.
+    Returns (m [Hq, L], l [Hq, L]): m = max logit over the rank's causal keys
+    (-inf if none), l = sum exp(z - m) (0 if none).
+    """
+    Hq, L, _ = q_last.shape
+    Hkv = k_shard.shape[0]
+    rows = np.arange(n_global - L, n_global)
+    causal = pos[None, :] <= rows[:, None]
+    m = np.full((Hq, L), -np.inf)
+    l = np.zeros((Hq, L))
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        z = (q_last[h].astype(np.float64) @ k_shard[g].astype(np.float64).T) * scale
+        z = np.where(causal, z, -np.inf)
+        mh = z.max(axis=1) if z.shape[1] else np.full(L, -np.inf)
+        ok = mh > -np.inf
+        m[h] = mh
+        l[h, ok] = np.exp(z[ok] - mh[ok, None]).sum(axis=1)
+    return m, l
+
+
+def merge_row_stats(parts):
+    """Row log-sum-exp from every rank's (m, l): M = max m, LSE = M + log sum
+    l_r exp(m_r - M); -inf for a row no rank saw."""
+    ms = np.stack([p[0] for p in parts])
+    ls = np.stack([p[1] for p in parts])
+    M = ms.max(axis=0)
+    ok = M > -np.inf
+    lse = np.full(M.shape, -np.inf)
+    w = np.where(ms > -np.inf, np.exp(ms - np.where(ok, M, 0.0)[None]), 0.0)
+    lse[ok] = M[ok] + np.log((ls * w).sum(axis=0)[ok])
+    return lse
+
+
+def rank_mass(q_last, k_shard, pos, scale, n_global, lse):
+    """One rank's share of the vertical and slash mass: v(m) for its keys and
+    the slash mass of the 64-blocks it holds (with the scored rows in the last
+    block, block-diagonal j collects exactly key block T-1-j). Returns
+    (v_local [Hq, n_local], s_part [Hq, T]) in fp64; s_part is zero outside
+    the rank's blocks."""
+    Hq, L, _ = q_last.shape
+    Hkv = k_shard.shape[0]
+    T = n_global // BLOCK
+    rows = np.arange(n_global - L, n_global)
+    causal = pos[None, :] <= rows[:, None]
+    diag = rows[:, None] // BLOCK - pos[None, :] // BLOCK
+    v = np.zeros((Hq, pos.shape[0]))
+    s = np.zeros((Hq, T))
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        z = (q_last[h].astype(np.float64) @ k_shard[g].astype(np.float64).T) * scale
+        ok = np.isfinite(lse[h])[:, None] & causal
+        a = np.where(ok, np.exp(np.where(ok, z - lse[h][:, None], 0.0)), 0.0)
+        v[h] = a.sum(axis=0) / L
+        s[h] = np.bincount(diag[ok], weights=a[ok], minlength=T)[:T] / L
+    return v, s
+
+
+def build_index_distributed(q_last, k, scale, n_global, top_p, kind, P):
+    """The index built the distributed way: per-rank partial statistics, an
+    all-gather of (m, l), the merged row LSE, per-rank mass, then an
+    all-gather of v and a sum of the slash parts, and the same top-p on the
+    gathered scores. k is [Hkv, N, D] in global order; each rank is handed
+    the keys at its shard positions."""
+    from .layout import shard_positions
+    shards = [shard_positions(kind, n_global, P, r) for r in range(P)]
+    parts = [rank_row_stats(q_last, k[:, pos], pos, scale, n_global) for pos in shards]
+    lse = merge_row_stats(parts)
+    Hq = q_last.shape[0]
+    v = np.zeros((Hq, n_global))
+    s = np.zeros((Hq, n_global // BLOCK))
+    for pos in shards:
+        v_r, s_r = rank_mass(q_last, k[:, pos], pos, scale, n_global, lse)
+        v[:, pos] = v_r
+        s += s_r
+    v, s = v.astype(np.float32), s.astype(np.float32)
+    vert = [select_top_p(v[h], top_p) for h in range(Hq)]
+    slash = [select_top_p(s[h], top_p) for h in range(Hq)]
+    return {"v": v, "s": s, "lse": lse, "vert": vert, "slash": slash}

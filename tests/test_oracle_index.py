@@ -171,3 +171,31 @@ def test_negative_control_no_structure():
     idx, _ = _index_for(cfg)
     # with no mean and no outliers the mass is spread: most columns are needed
     assert len(idx["vert"][0]) > 0.5 * cfg.N
+
+
+@pytest.mark.parametrize("kind,P", [("contig", 4), ("striped", 4), ("zigzag", 2), ("striped", 8)])
+def test_distributed_index_equals_global(kind, P):
+    """Per-rank partial statistics, merged, give the global index (the same
+    scores up to fp64 rounding and the same selections)."""
+    rng = np.random.default_rng(7 + P)
+    Hq, Hkv, L, D, N = 4, 2, 64, 16, 1024
+    q = rng.standard_normal((Hq, L, D))
+    k = rng.standard_normal((Hkv, N, D))
+    k[:, rng.choice(N, 6, replace=False)] *= 5.0
+    g = oi.build_index(q, k, 0.25, N, 0.9)
+    d = oi.build_index_distributed(q, k, 0.25, N, 0.9, kind, P)
+    np.testing.assert_allclose(d["lse"], g["lse"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(d["v"], g["v"], rtol=1e-6, atol=0)
+    np.testing.assert_allclose(d["s"], g["s"], rtol=1e-6, atol=0)
+    for h in range(Hq):
+        assert np.array_equal(d["vert"][h], g["vert"][h])
+        assert np.array_equal(d["slash"][h], g["slash"][h])
+
+
+def test_merge_row_stats_handles_empty_ranks():
+    """A rank that holds no causal key of a row contributes (-inf, 0)."""
+    m = [np.array([[1.0, -np.inf]]), np.array([[-np.inf, -np.inf]]), np.array([[3.0, -np.inf]])]
+    l = [np.array([[2.0, 0.0]]), np.array([[0.0, 0.0]]), np.array([[1.5, 0.0]])]
+    lse = oi.merge_row_stats(list(zip(m, l)))
+    assert lse[0, 1] == -np.inf
+    np.testing.assert_allclose(lse[0, 0], np.log(2.0 * np.exp(1.0) + 1.5 * np.exp(3.0)), rtol=1e-15)
