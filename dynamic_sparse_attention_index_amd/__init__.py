@@ -26,7 +26,8 @@ TILE_DIAG = 0x40000000
 TILE_MASK = 0x3FFFFFFF
 
 EXPORTED = [
-    "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_mask_bytes", "vs_mask_init",
+    "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_index_rank_stats", "vs_index_rank_mass",
+    "vs_index_select", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL = 1, 2, 4, 7
@@ -79,6 +80,12 @@ def lib():
         L.vs_index_workspace_size.argtypes = [i32, i32, i64, i32, i32]
         L.vs_index_build.restype = i32
         L.vs_index_build.argtypes = [VsTensor, VsTensor, VsLayout, f32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.vs_index_rank_stats.restype = i32
+        L.vs_index_rank_stats.argtypes = [VsTensor, VsTensor, VsLayout, i32, f32, vp, vp, sz, vp]
+        L.vs_index_rank_mass.restype = i32
+        L.vs_index_rank_mass.argtypes = [VsTensor, VsTensor, VsLayout, i32, f32, vp, vp, vp, vp, sz, vp]
+        L.vs_index_select.restype = i32
+        L.vs_index_select.argtypes = [vp, vp, i32, i64, f32, vp, vp, vp, vp, vp]
         L.vs_mask_bytes.restype = sz
         L.vs_mask_bytes.argtypes = [i32, i32, VsLayout, i64]
         L.vs_mask_init.restype = i32
@@ -158,6 +165,27 @@ def vs_index_build(q_last, k, lay: VsLayout, scale, top_p, vert_score, slash_sco
                                 _ptr(slash_score), _ptr(vert_idx), _ptr(vert_cnt), _ptr(slash_idx),
                                 _ptr(slash_cnt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "vs_index_build")
+
+
+def vs_index_rank_stats(q_last, k_local, lay: VsLayout, rank, scale, stats, ws, stream=None):
+    _check(lib().vs_index_rank_stats(as_vs_tensor(q_last), as_vs_tensor(k_local), lay, rank, scale, _cptr(stats),
+                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "vs_index_rank_stats")
+
+
+def vs_index_rank_mass(q_last, k_local, lay: VsLayout, rank, scale, all_stats, vert_score, slash_score, ws,
+                       stream=None):
+    _check(lib().vs_index_rank_mass(as_vs_tensor(q_last), as_vs_tensor(k_local), lay, rank, scale,
+                                    _cptr(all_stats), _cptr(vert_score), _cptr(slash_score), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)),
+           "vs_index_rank_mass")
+
+
+def vs_index_select(vert_score, slash_score, Hq, n_global, top_p, vert_idx, vert_cnt, slash_idx, slash_cnt,
+                    stream=None):
+    _check(lib().vs_index_select(_cptr(vert_score), _cptr(slash_score), Hq, n_global, top_p, _ptr(vert_idx),
+                                 _ptr(vert_cnt), _ptr(slash_idx), _ptr(slash_cnt), _stream(stream)),
+           "vs_index_select")
 
 
 class Mask:

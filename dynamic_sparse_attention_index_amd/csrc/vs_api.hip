@@ -111,6 +111,55 @@ int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, fl
                             (hipStream_t)stream);
 }
 
+// Checks shared by the per-rank index calls; on success sets the dims.
+static int check_rank_index(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int rank, float scale, void* ws,
+                            size_t ws_bytes, int* Hq, int* Hkv, int* D, int* last_q) {
+  int st;
+  if ((st = check_layout(lay)) != VS_OK) return st;
+  if (rank < 0 || rank >= lay.P) return VS_ERR_ARG;
+  *Hq = q_last.H; *Hkv = k_local.H; *D = q_last.D; *last_q = (int)q_last.N;
+  if (*Hq <= 0 || *Hkv <= 0 || *Hq % *Hkv) return VS_ERR_ARG;
+  if (*Hq / *Hkv > 8) return VS_ERR_UNSUPPORTED;
+  if (*last_q < 1 || *last_q > 64) return VS_ERR_UNSUPPORTED;
+  if ((st = check_tensor(q_last, *Hq, *last_q, *D)) != VS_OK) return st;
+  if ((st = check_tensor(k_local, *Hkv, lay.n_global / lay.P, *D)) != VS_OK) return st;
+  if (q_last.dtype != k_local.dtype || !supported_dtype_dim(k_local.dtype, *D)) return VS_ERR_UNSUPPORTED;
+  if (!ws || !(scale > 0.f)) return VS_ERR_ARG;
+  if (ws_bytes < vs_index_workspace_size(*Hq, *Hkv, lay.n_global, *D, *last_q)) return VS_ERR_WORKSPACE;
+  return VS_OK;
+}
+
+int vs_index_rank_stats(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int rank, float scale,
+                        float* stats, void* ws, size_t ws_bytes, void* stream) {
+  int Hq, Hkv, D, last_q, st;
+  if ((st = check_rank_index(q_last, k_local, lay, rank, scale, ws, ws_bytes, &Hq, &Hkv, &D, &last_q)) != VS_OK)
+    return st;
+  if (!stats) return VS_ERR_ARG;
+  return launch_index_rank_stats(k_local.dtype, D, view(q_last), Hq, last_q, view(k_local), Hkv, lay, rank, scale,
+                                 stats, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int vs_index_rank_mass(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int rank, float scale,
+                       const float* all_stats, float* vert_score, float* slash_score,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int Hq, Hkv, D, last_q, st;
+  if ((st = check_rank_index(q_last, k_local, lay, rank, scale, ws, ws_bytes, &Hq, &Hkv, &D, &last_q)) != VS_OK)
+    return st;
+  if (!all_stats || !vert_score || !slash_score) return VS_ERR_ARG;
+  return launch_index_rank_mass(k_local.dtype, D, view(q_last), Hq, last_q, view(k_local), Hkv, lay, rank, scale,
+                                all_stats, vert_score, slash_score, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int vs_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
+                    int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
+                    void* stream) {
+  if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || Hq <= 0) return VS_ERR_ARG;
+  if (top_p != top_p || n_global <= 0) return VS_ERR_ARG;
+  if (n_global % 64 || n_global / 64 > ((int64_t)1 << 24)) return VS_ERR_UNSUPPORTED;
+  return launch_index_select(vert_score, slash_score, Hq, n_global, top_p, vert_idx, vert_cnt, slash_idx, slash_cnt,
+                             (hipStream_t)stream);
+}
+
 size_t vs_mask_bytes(int Hq, int Hkv, vs_layout lay, int64_t tile_cap) {
   if (Hq <= 0 || Hkv <= 0 || tile_cap < 0 || check_layout(lay) != VS_OK) return 0;
   return mask_layout(Hq, lay, tile_cap).total;

@@ -32,11 +32,20 @@ struct IndexArgs {
   const void* q; const void* k;
   int64_t qsh, qsn, ksh, ksn;
   int Hq, Hkv, last_q, kind, P, NB, T, nsplit, tiles_per;
+  // tiles walked by passes 1 and 3: all T (k holds every shard, storage
+  // order) or, for one rank's share, the NB tiles of rank `rank_fixed`
+  // (k holds that shard only); rank_fixed < 0 for the first case
+  int ntiles, rank_fixed;
   int64_t n_global;
   float scale_log2;
   float* part;       // [Hq, 64, nsplit, 2]
   float* lse2;       // [Hq, 64] (log2 domain)
   float* vert; float* slash;
+  // combine pass: partial (max, sum) pair s of row t at
+  // cmb_in[(t * cmb_tstride + s * cmb_sstride) * 2], s < cmb_n; writes lse2,
+  // or (max, sum) of the row to cmb_stats when that is set
+  const float* cmb_in; int cmb_n; int64_t cmb_tstride, cmb_sstride;
+  float* cmb_stats;
 };
 
 template <typename T, int D>
@@ -105,6 +114,7 @@ __device__ __forceinline__ int64_t stage_key_tile(T* Ks, const IndexArgs& a, int
     const int r = ch / CPR, col = (ch % CPR) * (16 / (int)sizeof(T));
     *(i32x4*)(Ks + r * KP + col) = *(const i32x4*)(kb + (int64_t)r * a.ksn + col);
   }
+  if (a.rank_fixed >= 0) return global_block(a.kind, a.P, a.NB, a.rank_fixed, tau);
   return global_block(a.kind, a.P, a.NB, tau / a.NB, tau % a.NB);
 }
 
@@ -125,7 +135,7 @@ __global__ void __launch_bounds__(512) index_rowstat_kernel(IndexArgs a) {
     #pragma unroll
     for (int i = 0; i < 4; ++i) { m[rs][i] = -INFINITY; l[rs][i] = 0.f; }
   const int tau0 = blockIdx.x * a.tiles_per;
-  const int tau1 = min(a.T, tau0 + a.tiles_per);
+  const int tau1 = min(a.ntiles, tau0 + a.tiles_per);
   for (int tau = tau0; tau < tau1; ++tau) {
     const int64_t G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
     __syncthreads();
@@ -178,23 +188,32 @@ __global__ void __launch_bounds__(512) index_rowstat_kernel(IndexArgs a) {
     }
 }
 
-// Pass 2: one wave per (q head, row); lanes stride over the key-range splits.
+// Pass 2: one wave per (q head, row); lanes stride over the partial pairs
+// (key-range splits, or ranks).
 constexpr int COMB_THREADS = 256;
 __global__ void __launch_bounds__(COMB_THREADS) index_combine_kernel(IndexArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (COMB_THREADS / 64) + (threadIdx.x >> 6);
   if (t >= a.Hq * BLK) return;
-  const float* p = a.part + (int64_t)t * a.nsplit * 2;
+  const float* p = a.cmb_in + (int64_t)t * a.cmb_tstride * 2;
+  const int64_t ss = a.cmb_sstride * 2;
   float mm = -INFINITY;
-  for (int s = lane; s < a.nsplit; s += 64) mm = fmaxf(mm, p[2 * s]);
+  for (int s = lane; s < a.cmb_n; s += 64) mm = fmaxf(mm, p[s * ss]);
   #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
   float ll = 0.f;
   if (mm > -INFINITY)
-    for (int s = lane; s < a.nsplit; s += 64) ll += p[2 * s + 1] * __builtin_amdgcn_exp2f(p[2 * s] - mm);
+    for (int s = lane; s < a.cmb_n; s += 64) ll += p[s * ss + 1] * __builtin_amdgcn_exp2f(p[s * ss] - mm);
   #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ll += __shfl_xor(ll, off, 64);
-  if (lane == 0) a.lse2[t] = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+  if (lane == 0) {
+    if (a.cmb_stats) {
+      a.cmb_stats[2 * t] = mm;
+      a.cmb_stats[2 * t + 1] = ll;
+    } else {
+      a.lse2[t] = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+    }
+  }
 }
 
 // Pass 3: grid (nsplit, Hkv); vertical mass per key and slash mass per block.
@@ -218,7 +237,7 @@ __global__ void __launch_bounds__(512) index_colsum_kernel(IndexArgs a) {
   const int row0 = BLK - a.last_q;
   const float inv_rows = 1.f / (float)a.last_q;
   const int tau0 = blockIdx.x * a.tiles_per;
-  const int tau1 = min(a.T, tau0 + a.tiles_per);
+  const int tau1 = min(a.ntiles, tau0 + a.tiles_per);
   for (int tau = tau0; tau < tau1; ++tau) {
     const int64_t G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
     __syncthreads();
@@ -482,45 +501,98 @@ size_t index_workspace_bytes(int Hq, int Hkv, int64_t n_global, int D, int last_
   return (size_t)(Hq * BLK * nsplit * 2 + Hq * BLK) * sizeof(float) + 256;
 }
 
-int launch_index_build(int dtype, int D, TView q_last, int Hq, int last_q, TView k, int Hkv,
-                       const vs_layout& lay, float scale, float top_p, float* vert_score,
-                       float* slash_score, int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx,
-                       int32_t* slash_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
-  IndexArgs a;
+// Shared set-up: the tiles walked (all T, or the NB tiles of rank_fixed) and
+// their split over workgroups; the workspace holds the split partials and
+// the row LSE.
+static IndexArgs index_args(TView q_last, int Hq, int last_q, TView k, int Hkv, const vs_layout& lay, float scale,
+                            int rank_fixed, void* ws) {
+  IndexArgs a{};
   a.q = q_last.ptr; a.k = k.ptr;
   a.qsh = q_last.sh; a.qsn = q_last.sn; a.ksh = k.sh; a.ksn = k.sn;
   a.Hq = Hq; a.Hkv = Hkv; a.last_q = last_q; a.kind = lay.kind; a.P = lay.P;
   a.n_global = lay.n_global;
   a.T = (int)(lay.n_global / BLK);
   a.NB = a.T / lay.P;
-  a.nsplit = (int)std::min<int64_t>(a.T, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
-  a.tiles_per = (a.T + a.nsplit - 1) / a.nsplit;
-  a.nsplit = (a.T + a.tiles_per - 1) / a.tiles_per;
+  a.rank_fixed = rank_fixed;
+  a.ntiles = rank_fixed >= 0 ? a.NB : a.T;
+  a.nsplit = (int)std::min<int64_t>(a.ntiles, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
+  a.tiles_per = (a.ntiles + a.nsplit - 1) / a.nsplit;
+  a.nsplit = (a.ntiles + a.tiles_per - 1) / a.tiles_per;
   a.scale_log2 = scale * LOG2E;
-  if (ws_bytes < index_workspace_bytes(Hq, Hkv, lay.n_global, D, last_q)) return VS_ERR_WORKSPACE;
   a.part = (float*)ws;
   a.lse2 = a.part + (int64_t)Hq * BLK * a.nsplit * 2;
-  a.vert = vert_score; a.slash = slash_score;
-  const int grp = Hq / Hkv;
-  const dim3 grid(a.nsplit, Hkv), block(64 * grp);
-  if (dtype == VS_BF16 && D == 128) {
-    hipLaunchKernelGGL((index_rowstat_kernel<bf16, 128>), grid, block, 0, stream, a);
-  } else if (dtype == VS_BF16 && D == 64) {
-    hipLaunchKernelGGL((index_rowstat_kernel<bf16, 64>), grid, block, 0, stream, a);
-  } else if (dtype == VS_F32 && D == 64) {
-    hipLaunchKernelGGL((index_rowstat_kernel<float, 64>), grid, block, 0, stream, a);
-  } else {
-    return VS_ERR_UNSUPPORTED;
-  }
-  hipLaunchKernelGGL(index_combine_kernel, dim3((Hq * BLK + COMB_THREADS / 64 - 1) / (COMB_THREADS / 64)),
-                     dim3(COMB_THREADS), 0, stream, a);
+  return a;
+}
+
+static bool launch_rowstat(int dtype, int D, const IndexArgs& a, hipStream_t stream) {
+  const dim3 grid(a.nsplit, a.Hkv), block(64 * (a.Hq / a.Hkv));
+  if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL((index_rowstat_kernel<bf16, 128>), grid, block, 0, stream, a);
+  else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((index_rowstat_kernel<bf16, 64>), grid, block, 0, stream, a);
+  else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((index_rowstat_kernel<float, 64>), grid, block, 0, stream, a);
+  else return false;
+  return true;
+}
+
+static bool launch_colsum(int dtype, int D, const IndexArgs& a, hipStream_t stream) {
+  const dim3 grid(a.nsplit, a.Hkv), block(64 * (a.Hq / a.Hkv));
   if (dtype == VS_BF16 && D == 128) hipLaunchKernelGGL((index_colsum_kernel<bf16, 128>), grid, block, 0, stream, a);
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((index_colsum_kernel<bf16, 64>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((index_colsum_kernel<float, 64>), grid, block, 0, stream, a);
+  else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((index_colsum_kernel<float, 64>), grid, block, 0, stream, a);
+  else return false;
+  return true;
+}
+
+static void launch_combine(IndexArgs a, const float* in, int n, int64_t tstride, int64_t sstride, float* stats,
+                           hipStream_t stream) {
+  a.cmb_in = in; a.cmb_n = n; a.cmb_tstride = tstride; a.cmb_sstride = sstride; a.cmb_stats = stats;
+  hipLaunchKernelGGL(index_combine_kernel, dim3((a.Hq * BLK + COMB_THREADS / 64 - 1) / (COMB_THREADS / 64)),
+                     dim3(COMB_THREADS), 0, stream, a);
+}
+
+int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
+                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
+                        hipStream_t stream) {
   SelectArgs s;
   s.vert = vert_score; s.slash = slash_score; s.vert_idx = vert_idx; s.vert_cnt = vert_cnt;
-  s.slash_idx = slash_idx; s.slash_cnt = slash_cnt; s.n_vert = lay.n_global; s.n_slash = a.T; s.top_p = top_p;
+  s.slash_idx = slash_idx; s.slash_cnt = slash_cnt; s.n_vert = n_global; s.n_slash = (int)(n_global / BLK);
+  s.top_p = top_p;
   hipLaunchKernelGGL(topp_select_kernel, dim3(Hq, 2), dim3(SEL_THREADS), 0, stream, s);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+int launch_index_build(int dtype, int D, TView q_last, int Hq, int last_q, TView k, int Hkv,
+                       const vs_layout& lay, float scale, float top_p, float* vert_score,
+                       float* slash_score, int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx,
+                       int32_t* slash_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes < index_workspace_bytes(Hq, Hkv, lay.n_global, D, last_q)) return VS_ERR_WORKSPACE;
+  IndexArgs a = index_args(q_last, Hq, last_q, k, Hkv, lay, scale, -1, ws);
+  a.vert = vert_score; a.slash = slash_score;
+  if (!launch_rowstat(dtype, D, a, stream)) return VS_ERR_UNSUPPORTED;
+  launch_combine(a, a.part, a.nsplit, a.nsplit, 1, nullptr, stream);
+  launch_colsum(dtype, D, a, stream);
+  return launch_index_select(vert_score, slash_score, Hq, lay.n_global, top_p, vert_idx, vert_cnt, slash_idx,
+                             slash_cnt, stream);
+}
+
+int launch_index_rank_stats(int dtype, int D, TView q_last, int Hq, int last_q, TView k_local, int Hkv,
+                            const vs_layout& lay, int rank, float scale, float* stats, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (ws_bytes < index_workspace_bytes(Hq, Hkv, lay.n_global, D, last_q)) return VS_ERR_WORKSPACE;
+  IndexArgs a = index_args(q_last, Hq, last_q, k_local, Hkv, lay, scale, rank, ws);
+  if (!launch_rowstat(dtype, D, a, stream)) return VS_ERR_UNSUPPORTED;
+  launch_combine(a, a.part, a.nsplit, a.nsplit, 1, stats, stream);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+int launch_index_rank_mass(int dtype, int D, TView q_last, int Hq, int last_q, TView k_local, int Hkv,
+                           const vs_layout& lay, int rank, float scale, const float* all_stats, float* vert_score,
+                           float* slash_score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes < index_workspace_bytes(Hq, Hkv, lay.n_global, D, last_q)) return VS_ERR_WORKSPACE;
+  IndexArgs a = index_args(q_last, Hq, last_q, k_local, Hkv, lay, scale, rank, ws);
+  a.vert = vert_score; a.slash = slash_score;
+  // the gathered stats are [P][Hq * 64][2]: row t of rank s at (s * Hq * 64 + t) * 2
+  launch_combine(a, all_stats, lay.P, 1, (int64_t)Hq * BLK, nullptr, stream);
+  if (!launch_colsum(dtype, D, a, stream)) return VS_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 

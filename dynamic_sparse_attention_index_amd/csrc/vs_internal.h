@@ -38,4 +38,16 @@ int launch_index_build(int dtype, int D, TView q_last, int Hq, int last_q, TView
                        float* slash_score, int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx,
                        int32_t* slash_cnt, void* ws, size_t ws_bytes, hipStream_t stream);
 
+int launch_index_rank_stats(int dtype, int D, TView q_last, int Hq, int last_q, TView k_local, int Hkv,
+                            const vs_layout& lay, int rank, float scale, float* stats, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+int launch_index_rank_mass(int dtype, int D, TView q_last, int Hq, int last_q, TView k_local, int Hkv,
+                           const vs_layout& lay, int rank, float scale, const float* all_stats, float* vert_score,
+                           float* slash_score, void* ws, size_t ws_bytes, hipStream_t stream);
+
+int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
+                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
+                        hipStream_t stream);
+
 }  // namespace vs

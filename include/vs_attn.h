@@ -157,6 +157,53 @@ int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, fl
                    int32_t* slash_idx, int32_t* slash_cnt,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* The same index built the distributed way (review page 1, section 三.2
+ * item 1: the scored queries are broadcast and every rank scores them
+ * against the keys it holds). Per rank r, with exchanges between the calls:
+ *   1. vs_index_rank_stats: the rank's partial row statistics;
+ *   2. all-gather of the P slots into all_stats[P][Hq][64][2];
+ *   3. vs_index_rank_mass: merged row LSE, then the rank's entries of the
+ *      vertical and slash scores;
+ *   4. all-gather of the score entries (ranks write disjoint entries);
+ *   5. vs_index_select on the gathered scores (the same on every rank).
+ * On one GPU the ranks run one after another and the exchange buffers are
+ * shared. The scores equal vs_index_build's up to fp32 rounding of the
+ * merge (the summation order differs), and the selection follows from them
+ * by the same rule.
+ *
+ * vs_index_rank_stats:
+ *   q_last:  [Hq, last_q, D], as for vs_index_build;
+ *   k_local: [Hkv, n_global / P, D], rank `rank`'s keys in storage order
+ *            under `lay`;
+ *   stats:   [Hq, 64, 2] fp32 (device, caller-owned; rows >= last_q are
+ *            unused): per scored row, the largest logit over the rank's
+ *            causal keys in log2 units (logit * log2 e) and the sum of
+ *            2^(logit * log2 e - largest); (-inf, 0) when the rank holds no
+ *            causal key of the row;
+ *   ws:      vs_index_workspace_size(Hq, Hkv, n_global, D, last_q) bytes.
+ * Errors: as vs_index_build; VS_ERR_ARG for rank outside [0, P). */
+int vs_index_rank_stats(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int rank, float scale,
+                        float* stats, void* ws, size_t ws_bytes, void* stream);
+
+/* vs_index_rank_mass:
+ *   all_stats: [P, Hq, 64, 2] fp32, every rank's stats slot (read-only);
+ *   vert_score [Hq, n_global], slash_score [Hq, n_global / 64]: written only
+ *     at the global positions of the rank's keys and at the diagonals of its
+ *     key blocks (block-diagonal T-1-G for key block G), other entries are
+ *     left as they are;
+ *   other arguments and errors as vs_index_rank_stats. */
+int vs_index_rank_mass(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int rank, float scale,
+                       const float* all_stats, float* vert_score, float* slash_score,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* vs_index_select: the top-p selection of vs_index_build on given scores
+ * (vert_score [Hq, n_global], slash_score [Hq, n_global / 64], non-negative
+ * fp32); outputs as for vs_index_build. VS_ERR_ARG for null pointers or
+ * Hq <= 0; VS_ERR_UNSUPPORTED if n_global is not a multiple of 64. */
+int vs_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
+                    int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
+                    void* stream);
+
 /* ---- 2. active region ------------------------------------------------- */
 
 /* Device bytes of one mask buffer able to hold `tile_cap` (h, I, J) tiles. */

@@ -119,6 +119,26 @@ def test_block_mask_and_index_validation(L):
     assert L.vs_index_build(q, kshort, lay, 0.1, 0.9, *args, p, ws, None) == vs.VS_ERR_ARG
 
 
+def test_rank_index_validation(L):
+    """Per-rank index calls: host checks return before any device work."""
+    p = ctypes.c_void_p(0x60000000)
+    q = _fake_tensor(0x20000000, 16, 64, 128)
+    lay = vs.layout("striped", 4, 4096)
+    k_local = _fake_tensor(0x30000000, 2, 1024, 128)
+    ws = L.vs_index_workspace_size(16, 2, 4096, 128, 64)
+    assert L.vs_index_rank_stats(q, k_local, lay, 4, 0.1, p, p, ws, None) == vs.VS_ERR_ARG      # rank >= P
+    assert L.vs_index_rank_stats(q, k_local, lay, -1, 0.1, p, p, ws, None) == vs.VS_ERR_ARG
+    assert L.vs_index_rank_stats(q, k_local, lay, 0, 0.1, None, p, ws, None) == vs.VS_ERR_ARG   # no stats
+    assert L.vs_index_rank_stats(q, k_local, lay, 0, 0.1, p, p, ws - 1, None) == vs.VS_ERR_WORKSPACE
+    k_global = _fake_tensor(0x30000000, 2, 4096, 128)                                           # not a shard
+    assert L.vs_index_rank_stats(q, k_global, lay, 0, 0.1, p, p, ws, None) == vs.VS_ERR_ARG
+    assert L.vs_index_rank_mass(q, k_local, lay, 1, 0.1, None, p, p, p, ws, None) == vs.VS_ERR_ARG
+    assert L.vs_index_rank_mass(q, k_local, lay, 1, 0.0, p, p, p, p, ws, None) == vs.VS_ERR_ARG  # scale
+    assert L.vs_index_select(p, p, 16, 4096, 0.9, p, p, p, None, None) == vs.VS_ERR_ARG
+    assert L.vs_index_select(p, p, 0, 4096, 0.9, p, p, p, p, None) == vs.VS_ERR_ARG
+    assert L.vs_index_select(p, p, 16, 4000, 0.9, p, p, p, p, None) == vs.VS_ERR_UNSUPPORTED
+
+
 def test_bwd_and_merge_validation(L):
     m, lay, _, _ = _mask(L)
     m.rank = m.src = 0

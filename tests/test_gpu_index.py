@@ -74,3 +74,46 @@ def test_index_ties_at_cutoff(p):
     sel = set(vert[0].tolist())
     inside = [i for i in range(300, 420) if i in sel]
     assert inside == list(range(300, 300 + len(inside)))   # a prefix of the tie group
+
+
+@pytest.mark.parametrize("kind,P,dtype_cfg", [("striped", 4, "qwen32k"), ("zigzag", 2, "qwen32k"),
+                                              ("contig", 4, "qwen32k"), ("striped", 8, "tiny")])
+def test_index_distributed_ranks(kind, P, dtype_cfg):
+    """The distributed index simulated on one GPU: each rank's pass 1 on its
+    own shard, an all-gather of the (max, sum) slots, each rank's pass 2
+    writing its score entries, then the selection. Checked against the
+    oracle's distributed build (which its CPU tests pin to the global index)
+    and against the library's one-pass build on the same device."""
+    import torch
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    if dtype_cfg == "tiny":
+        cfg = config_by_name("tiny")
+    else:
+        cfg = config_by_name("qwen32k", N=8192, Hq=8, Hkv=2, c=5.0)
+    t = generate(cfg, tensors=("q", "k"), rows=None)
+    N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    q_last = H.to_dev(t["q"][:, N - 64:], cfg.dtype)
+    lay = vs.layout(kind, P, N)
+    ws = torch.empty(vs.index_workspace_size(Hq, Hkv, N, D, 64), dtype=torch.uint8, device="cuda")
+    shards = [H.to_dev(H.shard(t["k"], kind, P, r), cfg.dtype) for r in range(P)]
+    all_stats = torch.full((P, Hq, 64, 2), float("nan"), device="cuda")
+    for r in range(P):
+        vs.vs_index_rank_stats(q_last, shards[r], lay, r, cfg.scale, all_stats[r], ws)
+    v = torch.full((Hq, N), float("nan"), device="cuda")
+    s = torch.full((Hq, N // 64), float("nan"), device="cuda")
+    for r in range(P):
+        vs.vs_index_rank_mass(q_last, shards[r], lay, r, cfg.scale, all_stats, v, s, ws)
+    out = {"v": v, "s": s,
+           "vidx": torch.full((Hq, N), -7, dtype=torch.int32, device="cuda"),
+           "vcnt": torch.empty(Hq, dtype=torch.int32, device="cuda"),
+           "sidx": torch.full((Hq, N // 64), -7, dtype=torch.int32, device="cuda"),
+           "scnt": torch.empty(Hq, dtype=torch.int32, device="cuda")}
+    vs.vs_index_select(v, s, Hq, N, cfg.top_p, out["vidx"], out["vcnt"], out["sidx"], out["scnt"])
+    torch.cuda.synchronize()
+    assert not torch.isnan(v).any() and not torch.isnan(s).any()    # every entry written by some rank
+    ref = oi.build_index_distributed(t["q"][:, N - 64:], t["k"], cfg.scale, N, cfg.top_p, kind, P)
+    H.check_index(out, ref, cfg.top_p)
+    one = H.gpu_index(q_last, H.to_dev(H.storage_order(t["k"], kind, P), cfg.dtype), lay, cfg.scale, cfg.top_p)
+    for a, b in ((v, one["v"]), (s, one["s"])):
+        assert torch.allclose(a, b, rtol=1e-5, atol=1e-9), (a - b).abs().max().item()
