@@ -304,6 +304,33 @@ def ring_report(args, cfg):
             ev = timed(index)
             torch.cuda.synchronize()
             t_index.append(ev[0].elapsed_time(ev[1]))
+        # the same index built the distributed way: every rank's two passes on
+        # its own shard (a slice of the storage order), the gathered (max, sum)
+        # slots between them, then the selection (exchanges excluded)
+        all_stats = torch.empty(P, Hq, 64, 2, device=dev)
+        vert_d, slash_d = torch.empty_like(vert_s), torch.empty_like(slash_s)
+        vidx_d, vcnt_d = torch.empty_like(vidx), torch.empty_like(vcnt)
+        sidx_d, scnt_d = torch.empty_like(sidx), torch.empty_like(scnt)
+        nl = N // P
+        t_d1, t_d2, t_d3 = [], [], []
+        for rep in range(-1, args.ring_reps):
+            e1 = [timed(lambda: vs.vs_index_rank_stats(q_last, k[:, r * nl:(r + 1) * nl], lay, r, cfg.scale,
+                                                       all_stats[r], ws, stream)) for r in range(P)]
+            e2 = [timed(lambda: vs.vs_index_rank_mass(q_last, k[:, r * nl:(r + 1) * nl], lay, r, cfg.scale,
+                                                      all_stats, vert_d, slash_d, ws, stream)) for r in range(P)]
+            e3 = timed(lambda: vs.vs_index_select(vert_d, slash_d, Hq, N, cfg.top_p, vidx_d, vcnt_d, sidx_d,
+                                                  scnt_d, stream))
+            torch.cuda.synchronize()
+            if rep >= 0:
+                t_d1.append(max(a.elapsed_time(b) for a, b in e1))
+                t_d2.append(max(a.elapsed_time(b) for a, b in e2))
+                t_d3.append(e3[0].elapsed_time(e3[1]))
+        same_sel = bool(torch.equal(vcnt_d, vcnt) and torch.equal(scnt_d, scnt))
+        if same_sel:
+            for h in range(Hq):
+                same_sel = same_sel and torch.equal(vidx_d[h, :int(vcnt[h])], vidx[h, :int(vcnt[h])]) and \
+                    torch.equal(sidx_d[h, :int(scnt[h])], sidx[h, :int(scnt[h])])
+        score_rel = float(((vert_d - vert_s).abs() / vert_s.abs().clamp_min(1e-30)).max().item())
         cap = Hq * QB * (int(scnt.max().item()) + 1)
         t_mask = np.zeros((args.ring_reps, P, P))
         t_fwd = np.zeros((args.ring_reps, P, P))
@@ -381,6 +408,12 @@ def ring_report(args, cfg):
             del m
         out["layouts"][kind] = {
             "index_ms": round(float(np.median(t_index)), 4),
+            "index_distributed_pass1_ms_max_rank": round(float(np.median(t_d1)), 4),
+            "index_distributed_pass2_ms_max_rank": round(float(np.median(t_d2)), 4),
+            "index_distributed_select_ms": round(float(np.median(t_d3)), 4),
+            "index_distributed_exchange_bytes": P * Hq * 64 * 2 * 4 + Hq * (N + T) * 4,
+            "index_distributed_same_selection": same_sel,
+            "index_distributed_max_rel_score_diff": float(f"{score_rel:.3e}"),
             "mask_ms_per_step_mean": round(float(tm.mean()), 4),
             "fwd_ms_per_step_mean": round(float(tf.mean()), 4),
             "bwd_ms_per_step_mean": round(float(tb.mean()), 4),
