@@ -312,6 +312,7 @@ def ring_report(args, cfg):
         vidx_d, vcnt_d = torch.empty_like(vidx), torch.empty_like(vcnt)
         sidx_d, scnt_d = torch.empty_like(sidx), torch.empty_like(scnt)
         nl = N // P
+        sws = torch.empty(vs.index_select_workspace_size(Hq, N), dtype=torch.uint8, device=dev)
         t_d1, t_d2, t_d3 = [], [], []
         for rep in range(-1, args.ring_reps):
             e1 = [timed(lambda: vs.vs_index_rank_stats(q_last, k[:, r * nl:(r + 1) * nl], lay, r, cfg.scale,
@@ -319,7 +320,7 @@ def ring_report(args, cfg):
             e2 = [timed(lambda: vs.vs_index_rank_mass(q_last, k[:, r * nl:(r + 1) * nl], lay, r, cfg.scale,
                                                       all_stats, vert_d, slash_d, ws, stream)) for r in range(P)]
             e3 = timed(lambda: vs.vs_index_select(vert_d, slash_d, Hq, N, cfg.top_p, vidx_d, vcnt_d, sidx_d,
-                                                  scnt_d, stream))
+                                                  scnt_d, sws, stream))
             torch.cuda.synchronize()
             if rep >= 0:
                 t_d1.append(max(a.elapsed_time(b) for a, b in e1))

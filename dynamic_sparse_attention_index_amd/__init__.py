@@ -27,7 +27,7 @@ TILE_MASK = 0x3FFFFFFF
 
 EXPORTED = [
     "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_index_rank_stats", "vs_index_rank_mass",
-    "vs_index_select", "vs_mask_bytes", "vs_mask_init",
+    "vs_index_select_workspace_size", "vs_index_select", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL = 1, 2, 4, 7
@@ -85,7 +85,9 @@ def lib():
         L.vs_index_rank_mass.restype = i32
         L.vs_index_rank_mass.argtypes = [VsTensor, VsTensor, VsLayout, i32, f32, vp, vp, vp, vp, sz, vp]
         L.vs_index_select.restype = i32
-        L.vs_index_select.argtypes = [vp, vp, i32, i64, f32, vp, vp, vp, vp, vp]
+        L.vs_index_select.argtypes = [vp, vp, i32, i64, f32, vp, vp, vp, vp, vp, sz, vp]
+        L.vs_index_select_workspace_size.restype = sz
+        L.vs_index_select_workspace_size.argtypes = [i32, i64]
         L.vs_mask_bytes.restype = sz
         L.vs_mask_bytes.argtypes = [i32, i32, VsLayout, i64]
         L.vs_mask_init.restype = i32
@@ -181,10 +183,15 @@ def vs_index_rank_mass(q_last, k_local, lay: VsLayout, rank, scale, all_stats, v
            "vs_index_rank_mass")
 
 
-def vs_index_select(vert_score, slash_score, Hq, n_global, top_p, vert_idx, vert_cnt, slash_idx, slash_cnt,
+def index_select_workspace_size(Hq, n_global) -> int:
+    return int(lib().vs_index_select_workspace_size(Hq, n_global))
+
+
+def vs_index_select(vert_score, slash_score, Hq, n_global, top_p, vert_idx, vert_cnt, slash_idx, slash_cnt, ws,
                     stream=None):
     _check(lib().vs_index_select(_cptr(vert_score), _cptr(slash_score), Hq, n_global, top_p, _ptr(vert_idx),
-                                 _ptr(vert_cnt), _ptr(slash_idx), _ptr(slash_cnt), _stream(stream)),
+                                 _ptr(vert_cnt), _ptr(slash_idx), _ptr(slash_cnt), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)),
            "vs_index_select")
 
 

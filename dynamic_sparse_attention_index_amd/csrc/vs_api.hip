@@ -150,14 +150,21 @@ int vs_index_rank_mass(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int r
                                 all_stats, vert_score, slash_score, ws, ws_bytes, (hipStream_t)stream);
 }
 
+size_t vs_index_select_workspace_size(int Hq, int64_t n_global) {
+  if (Hq <= 0 || n_global <= 0) return 0;
+  return select_workspace_bytes(Hq, n_global);
+}
+
 int vs_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
                     int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
-                    void* stream) {
-  if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || Hq <= 0) return VS_ERR_ARG;
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || Hq <= 0 || !ws)
+    return VS_ERR_ARG;
   if (top_p != top_p || n_global <= 0) return VS_ERR_ARG;
   if (n_global % 64 || n_global / 64 > ((int64_t)1 << 24)) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < select_workspace_bytes(Hq, n_global)) return VS_ERR_WORKSPACE;
   return launch_index_select(vert_score, slash_score, Hq, n_global, top_p, vert_idx, vert_cnt, slash_idx, slash_cnt,
-                             (hipStream_t)stream);
+                             ws, ws_bytes, (hipStream_t)stream);
 }
 
 size_t vs_mask_bytes(int Hq, int Hkv, vs_layout lay, int64_t tile_cap) {

@@ -272,15 +272,36 @@ __global__ void __launch_bounds__(512) index_colsum_kernel(IndexArgs a) {
 }
 
 // ---- exact top-p selection ---------------------------------------------------
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int SEL_UNROLL = 8;   // loads in flight per thread in each sweep
+// Radix select on the fp32 bit patterns of one (head, direction)'s scores
+// (non-negative: bit order = value order), each digit weighted by its
+// fixed-point mass, spread over many workgroups: a pass is one launch of
+// per-chunk histograms (LDS, then merged into a global histogram with 64-bit
+// atomics) and one launch that scans the global histogram and fixes the
+// digit. Digits: bits 31-20, 19-8, 7-0. Then a count launch and a write
+// launch compact the kept indices in ascending order.
+constexpr int SEL_CHUNK = 4096;              // scores per workgroup
+constexpr int SEL_WG = 256;                  // threads of the chunk kernels
+constexpr int SEL_PER = SEL_CHUNK / SEL_WG;  // scores per thread
+constexpr int SEL_BINS = 4096;               // 12-bit digits
+constexpr int SCAN_THREADS = 1024;           // one thread per 4 bins
+
+struct SelState {
+  unsigned long long rem;     // mass still to collect at or below the fixed prefix
+  unsigned long long k_tie;   // after the last pass: ties at the cutoff to keep
+  uint32_t prefix;            // fixed high bits of the cutoff pattern
+  int mode;                   // 0: selecting, 1: keep every index, 2: keep none
+  int pad[2];
+};
 
 struct SelectArgs {
   const float* vert; const float* slash;
   int32_t *vert_idx, *vert_cnt, *slash_idx, *slash_cnt;
   int64_t n_vert; int n_slash;
   float top_p;
+  unsigned long long* hist;   // [Hq][2][SEL_BINS]
+  SelState* state;            // [Hq][2]
+  int* counts;                // [Hq][2][max_chunks][2]: (above the cutoff, at it)
+  int max_chunks;
 };
 
 // round_half_even(x * 2^40) for a non-negative fp32 x <= 2^23, in integers:
@@ -312,193 +333,276 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 
-// One wave over a 256-digit mass histogram h (lane l holds digits 4l..4l+3).
-// With the suffix mass S(b) = sum of h[b'] for b' >= b, returns the digit
-// b* = the largest b >= 1 with S(b) >= rem (0 when there is none) and stores
-// S(b* + 1), the mass of the digits above it, in *above. The histogram total
-// goes to *total.
-__device__ __forceinline__ int sel_digit(const unsigned long long* h, unsigned long long rem, int lane,
-                                         unsigned long long* above, unsigned long long* total) {
+// the scores of (h, dir), their count and outputs
+struct SelView {
+  const float* x; int32_t* out; int32_t* cnt; int n;
+};
+__device__ __forceinline__ SelView sel_view(const SelectArgs& a, int h, int dir) {
+  SelView v;
+  if (dir == 0) {
+    v.x = a.vert + h * a.n_vert; v.out = a.vert_idx + h * a.n_vert; v.cnt = a.vert_cnt + h; v.n = (int)a.n_vert;
+  } else {
+    v.x = a.slash + (int64_t)h * a.n_slash; v.out = a.slash_idx + (int64_t)h * a.n_slash; v.cnt = a.slash_cnt + h;
+    v.n = a.n_slash;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void sel_digit_bits(int pass, int& shift, int& width) {
+  shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+  width = pass == 2 ? 8 : 12;
+}
+
+// grid (Hq, 2): clear the global histogram, set the mode
+__global__ void __launch_bounds__(SEL_WG) sel_init_kernel(SelectArgs a) {
+  const int hd = blockIdx.x * 2 + blockIdx.y;
+  unsigned long long* gh = a.hist + (int64_t)hd * SEL_BINS;
+  for (int b = threadIdx.x; b < SEL_BINS; b += SEL_WG) gh[b] = 0;
+  if (threadIdx.x == 0) {
+    SelState s{};
+    s.mode = a.top_p >= 1.f ? 1 : (a.top_p > 0.f ? 0 : 2);
+    a.state[hd] = s;
+  }
+}
+
+// grid (max_chunks, Hq, 2): histogram of one chunk's scores that carry the
+// fixed prefix, by the pass's digit, merged into the global histogram
+__global__ void __launch_bounds__(SEL_WG) sel_hist_kernel(SelectArgs a, int pass) {
+  __shared__ unsigned long long lh[SEL_BINS];
+  const int h = blockIdx.y, dir = blockIdx.z, hd = h * 2 + dir;
+  const SelView v = sel_view(a, h, dir);
+  const int c0 = blockIdx.x * SEL_CHUNK;
+  if (c0 >= v.n) return;
+  const SelState st = a.state[hd];
+  if (st.mode != 0) return;
+  int shift, width;
+  sel_digit_bits(pass, shift, width);
+  const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + width));
+  const uint32_t dmask = (1u << width) - 1u;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < SEL_BINS; b += SEL_WG) lh[b] = 0;
+  uint32_t bits[SEL_PER];
+  #pragma unroll
+  for (int k = 0; k < SEL_PER; ++k) {
+    const int i = c0 + tid + k * SEL_WG;
+    bits[k] = i < v.n ? __float_as_uint(v.x[i]) : 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  #pragma unroll
+  for (int k = 0; k < SEL_PER; ++k) {
+    const int i = c0 + tid + k * SEL_WG;
+    if (i < v.n && (bits[k] & hi_mask) == st.prefix)
+      atomicAdd(&lh[(bits[k] >> shift) & dmask], (unsigned long long)fixed_mass(__uint_as_float(bits[k])));
+  }
+  __syncthreads();
+  unsigned long long* gh = a.hist + (int64_t)hd * SEL_BINS;
+  for (int b = tid; b < SEL_BINS; b += SEL_WG)
+    if (lh[b]) atomicAdd(&gh[b], lh[b]);
+}
+
+// grid (Hq, 2): scan the global histogram for the pass's digit. With the
+// suffix mass S(b) = sum of bins b' >= b, the digit is the largest b >= 1
+// with S(b) >= rem (0 if none) and the mass above it leaves the budget. The
+// histogram is cleared for the next pass (and the next call).
+__global__ void __launch_bounds__(SCAN_THREADS) sel_scan_kernel(SelectArgs a, int pass) {
+  __shared__ unsigned long long wsum[SCAN_THREADS / 64];
+  __shared__ int wcnt[SCAN_THREADS / 64];
+  __shared__ unsigned long long wab[SCAN_THREADS / 64];
+  const int hd = blockIdx.x * 2 + blockIdx.y;
+  const SelState st = a.state[hd];
+  if (st.mode != 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = SCAN_THREADS / 64;
+  int shift, width;
+  sel_digit_bits(pass, shift, width);
+  const int nbins = 1 << width;
+  unsigned long long* gh = a.hist + (int64_t)hd * SEL_BINS;
+  // thread t holds bins 4t .. 4t + 3
   unsigned long long v[4];
   #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = h[4 * lane + j];
+  for (int j = 0; j < 4; ++j) {
+    const int b = 4 * tid + j;
+    v[j] = b < nbins ? gh[b] : 0ull;
+  }
+  #pragma unroll
+  for (int j = 0; j < 4; ++j) gh[4 * tid + j] = 0;
   const unsigned long long loc = v[0] + v[1] + v[2] + v[3];
-  unsigned long long suf = loc;   // inclusive suffix over lanes
+  // suffix sums over threads: within the wave, then across waves
+  unsigned long long suf = loc;
   #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const unsigned long long t = __shfl_down(suf, off, 64);
     if (lane + off < 64) suf += t;
   }
-  *total = __shfl(suf, 0, 64);
-  unsigned long long s = suf - loc;
-  int cnt = 0;
+  if (lane == 0) wsum[wave] = suf;
+  __syncthreads();
+  unsigned long long above_waves = 0, total = 0;
   #pragma unroll
-  for (int j = 3; j >= 0; --j) {
-    s += v[j];   // S(4 lane + j)
-    cnt += (4 * lane + j >= 1 && s >= rem) ? 1 : 0;
+  for (int w = 0; w < NW; ++w) {
+    total += wsum[w];
+    if (w > wave) above_waves += wsum[w];
   }
-  const int b = wave_sum_i32(cnt);
-  unsigned long long ab = 0;
-  #pragma unroll
-  for (int j = 0; j < 4; ++j) ab += (4 * lane + j > b) ? v[j] : 0ull;
-  *above = wave_sum_u64(ab);
-  return b;
-}
-
-// grid (Hq, 2): y = 0 vertical scores, y = 1 slash scores.
-__global__ void __launch_bounds__(SEL_THREADS) topp_select_kernel(SelectArgs a) {
-  __shared__ unsigned long long hist[SEL_WAVES][256];
-  __shared__ unsigned long long sel_rem;
-  __shared__ uint32_t sel_prefix;
-  __shared__ int sel_empty;
-  const int h = blockIdx.x;
-  const bool is_vert = blockIdx.y == 0;
-  const int n = is_vert ? (int)a.n_vert : a.n_slash;
-  const float* x = is_vert ? a.vert + h * a.n_vert : a.slash + (int64_t)h * a.n_slash;
-  int32_t* out = is_vert ? a.vert_idx + h * a.n_vert : a.slash_idx + (int64_t)h * a.n_slash;
-  int32_t* cnt = is_vert ? a.vert_cnt + h : a.slash_cnt + h;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  if (a.top_p >= 1.f) {
-    for (int i = tid; i < n; i += SEL_THREADS) out[i] = i;
-    if (tid == 0) *cnt = n;
-    return;
-  }
-  if (!(a.top_p > 0.f)) {
-    if (tid == 0) *cnt = 0;
-    return;
-  }
-  // Radix select on the fp32 bit pattern (non-negative: bit order = value
-  // order), 8 bits a pass, each digit weighted by its fixed-point mass. The
-  // first pass sees every score, so its histogram total is the whole mass
-  // and sets the target ceil(p * total).
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    const uint32_t prefix = pass == 0 ? 0u : sel_prefix;
-    unsigned long long* hw = hist[wave];
-    #pragma unroll
-    for (int j = 0; j < 4; ++j) hw[lane + 64 * j] = 0;
-    for (int c0 = 0; c0 < n; c0 += SEL_THREADS * SEL_UNROLL) {
-      uint32_t bits[SEL_UNROLL];
-      #pragma unroll
-      for (int k = 0; k < SEL_UNROLL; ++k) {
-        const int i = c0 + tid + k * SEL_THREADS;
-        bits[k] = i < n ? __float_as_uint(x[i]) : 0u;
-      }
-      #pragma unroll
-      for (int k = 0; k < SEL_UNROLL; ++k) {
-        const int i = c0 + tid + k * SEL_THREADS;
-        if (i < n && (bits[k] & hi_mask) == prefix)
-          atomicAdd(&hw[(bits[k] >> shift) & 255u], fixed_mass(__uint_as_float(bits[k])));
-      }
-    }
-    __syncthreads();
-    if (tid < 256) {
-      unsigned long long t = 0;
-      #pragma unroll
-      for (int w = 0; w < SEL_WAVES; ++w) t += hist[w][tid];
-      hist[0][tid] = t;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      unsigned long long rem = pass == 0 ? 0ull : sel_rem, above, total;
-      if (pass == 0) {
-        // the target needs the total first: a second wave-wide sum
-        unsigned long long loc = 0;
-        #pragma unroll
-        for (int j = 0; j < 4; ++j) loc += hist[0][4 * lane + j];
-        const unsigned long long tot = wave_sum_u64(loc);
-        const unsigned long long pq = (unsigned long long)__builtin_rint((double)a.top_p * 4294967296.0);
-        const unsigned __int128 prod = (unsigned __int128)pq * tot;
-        rem = (unsigned long long)((prod + 0xFFFFFFFFull) >> 32);   // ceil(pq * tot / 2^32)
-      }
-      const int b = sel_digit(hist[0], rem, lane, &above, &total);
-      if (lane == 0) {
-        sel_empty = rem == 0;
-        sel_rem = rem - above;
-        sel_prefix = prefix | ((uint32_t)b << shift);
-      }
-    }
-    __syncthreads();
-    if (sel_empty) {
-      if (tid == 0) *cnt = 0;
+  unsigned long long rem = st.rem;
+  if (pass == 0) {
+    const unsigned long long pq = (unsigned long long)__builtin_rint((double)a.top_p * 4294967296.0);
+    const unsigned __int128 prod = (unsigned __int128)pq * total;
+    rem = (unsigned long long)((prod + 0xFFFFFFFFull) >> 32);   // ceil(pq * total / 2^32)
+    if (rem == 0) {
+      if (tid == 0) a.state[hd].mode = 2;
       return;
     }
   }
-  const uint32_t xstar = sel_prefix;
-  const unsigned long long qstar = fixed_mass(__uint_as_float(xstar));
-  const unsigned long long k_tie = qstar ? (sel_rem + qstar - 1) / qstar : 0;
-  // ascending compaction: x > x*, or x == x* among the first k_tie ties (in
-  // index order). Each wave owns a contiguous index range; pass A counts its
-  // keeps and ties, one barrier, then pass B writes positions from ballots.
-  __shared__ int wave_gt[SEL_WAVES], wave_tie[SEL_WAVES];
-  const int per = (n + SEL_WAVES - 1) / SEL_WAVES;
-  const int w0 = min(n, wave * per), w1 = min(n, w0 + per);
-  int n_gt = 0, n_tie = 0;
-  for (int c0 = w0; c0 < w1; c0 += 64 * SEL_UNROLL) {
-    uint32_t bits[SEL_UNROLL];
-    #pragma unroll
-    for (int k = 0; k < SEL_UNROLL; ++k) {
-      const int i = c0 + lane + 64 * k;
-      bits[k] = i < w1 ? __float_as_uint(x[i]) : 0u;
+  unsigned long long s = above_waves + suf - loc;   // mass of the bins above this thread's
+  int c = 0;
+  #pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    s += v[j];   // S(4 t + j)
+    c += (4 * tid + j >= 1 && s >= rem) ? 1 : 0;
+  }
+  c = wave_sum_i32(c);
+  if (lane == 0) wcnt[wave] = c;
+  __syncthreads();
+  int bstar = 0;
+  #pragma unroll
+  for (int w = 0; w < NW; ++w) bstar += wcnt[w];
+  unsigned long long ab = 0;
+  #pragma unroll
+  for (int j = 0; j < 4; ++j) ab += (4 * tid + j > bstar) ? v[j] : 0ull;
+  ab = wave_sum_u64(ab);
+  if (lane == 0) wab[wave] = ab;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long above = 0;
+    for (int w = 0; w < NW; ++w) above += wab[w];
+    SelState ns = st;
+    ns.rem = rem - above;
+    ns.prefix = st.prefix | ((uint32_t)bstar << shift);
+    if (pass == 2) {
+      const unsigned long long qstar = fixed_mass(__uint_as_float(ns.prefix));
+      ns.k_tie = qstar ? (ns.rem + qstar - 1) / qstar : 0;
     }
+    a.state[hd] = ns;
+  }
+}
+
+// grid (max_chunks, Hq, 2): per chunk, the scores above the cutoff and at it
+__global__ void __launch_bounds__(SEL_WG) sel_count_kernel(SelectArgs a) {
+  __shared__ int red[2][SEL_WG / 64];
+  const int h = blockIdx.y, dir = blockIdx.z, hd = h * 2 + dir;
+  const SelView v = sel_view(a, h, dir);
+  const int c0 = blockIdx.x * SEL_CHUNK;
+  if (c0 >= v.n) return;
+  const SelState st = a.state[hd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int n_gt = 0, n_tie = 0;
+  if (st.mode == 0) {
     #pragma unroll
-    for (int k = 0; k < SEL_UNROLL; ++k) {
-      const bool ok = c0 + lane + 64 * k < w1;
-      n_gt += (ok && bits[k] > xstar) ? 1 : 0;
-      n_tie += (ok && bits[k] == xstar) ? 1 : 0;
+    for (int k = 0; k < SEL_PER; ++k) {
+      const int i = c0 + tid + k * SEL_WG;
+      if (i < v.n) {
+        const uint32_t b = __float_as_uint(v.x[i]);
+        n_gt += b > st.prefix ? 1 : 0;
+        n_tie += b == st.prefix ? 1 : 0;
+      }
     }
   }
   n_gt = wave_sum_i32(n_gt);
   n_tie = wave_sum_i32(n_tie);
-  if (lane == 0) {
-    wave_gt[wave] = n_gt;
-    wave_tie[wave] = n_tie;
-  }
+  if (lane == 0) { red[0][wave] = n_gt; red[1][wave] = n_tie; }
   __syncthreads();
-  // this wave's output base, and the ties before its range
-  unsigned long long ties_before = 0, run_ties = 0;
-  int base = 0, total_kept = 0;
-  for (int w = 0; w < SEL_WAVES; ++w) {
-    const unsigned long long room = k_tie > run_ties ? k_tie - run_ties : 0;
-    const int kept_w = wave_gt[w] + (int)min((unsigned long long)wave_tie[w], room);
-    if (w < wave) base += kept_w;
-    if (w == wave) ties_before = run_ties;
-    total_kept += kept_w;
-    run_ties += (unsigned long long)wave_tie[w];
+  if (tid == 0) {
+    int g = 0, t = 0;
+    for (int w = 0; w < SEL_WG / 64; ++w) { g += red[0][w]; t += red[1][w]; }
+    int* cc = a.counts + ((int64_t)hd * a.max_chunks + blockIdx.x) * 2;
+    cc[0] = g;
+    cc[1] = t;
   }
-  unsigned long long ties_seen = ties_before;
+}
+
+// grid (max_chunks, Hq, 2): write the chunk's kept indices in ascending order:
+// scores above the cutoff, and the ties at it up to k_tie in index order.
+// Each wave owns a contiguous quarter of the chunk; ballots give positions.
+__global__ void __launch_bounds__(SEL_WG) sel_write_kernel(SelectArgs a) {
+  constexpr int NW = SEL_WG / 64, QUART = SEL_CHUNK / NW;
+  __shared__ int wgt[NW], wtie[NW];
+  const int h = blockIdx.y, dir = blockIdx.z, hd = h * 2 + dir;
+  const SelView v = sel_view(a, h, dir);
+  const int chunk = blockIdx.x, c0 = chunk * SEL_CHUNK;
+  if (c0 >= v.n) return;
+  const SelState st = a.state[hd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunks = (v.n + SEL_CHUNK - 1) / SEL_CHUNK;
+  if (st.mode == 1) {
+    for (int i = c0 + tid; i < min(v.n, c0 + SEL_CHUNK); i += SEL_WG) v.out[i] = i;
+    if (chunk == 0 && tid == 0) *v.cnt = v.n;
+    return;
+  }
+  if (st.mode == 2) {
+    if (chunk == 0 && tid == 0) *v.cnt = 0;
+    return;
+  }
+  // above-cutoff and tie counts of the chunks before this one, and of all
+  const int* cc = a.counts + (int64_t)hd * a.max_chunks * 2;
+  int g_before = 0, t_before = 0, g_all = 0, t_all = 0;
+  for (int c = lane; c < nchunks; c += 64) {
+    const int g = cc[2 * c], t = cc[2 * c + 1];
+    g_all += g; t_all += t;
+    if (c < chunk) { g_before += g; t_before += t; }
+  }
+  g_before = wave_sum_i32(g_before); t_before = wave_sum_i32(t_before);
+  g_all = wave_sum_i32(g_all); t_all = wave_sum_i32(t_all);
+  const unsigned long long k_tie = st.k_tie;
+  const uint32_t xstar = st.prefix;
+  if (chunk == 0 && tid == 0)
+    *v.cnt = g_all + (int)min((unsigned long long)t_all, k_tie);
+  // this wave's quarter: counts, then the waves before it
+  const int w0 = min(v.n, c0 + wave * QUART), w1 = min(v.n, w0 + QUART);
+  int n_gt = 0, n_tie = 0;
+  for (int i = w0 + lane; i < w1; i += 64) {
+    const uint32_t b = __float_as_uint(v.x[i]);
+    n_gt += b > xstar ? 1 : 0;
+    n_tie += b == xstar ? 1 : 0;
+  }
+  n_gt = wave_sum_i32(n_gt);
+  n_tie = wave_sum_i32(n_tie);
+  if (lane == 0) { wgt[wave] = n_gt; wtie[wave] = n_tie; }
+  __syncthreads();
+  unsigned long long ties_seen = (unsigned long long)t_before;
+  int gt_before = g_before;
+  for (int w = 0; w < wave; ++w) { gt_before += wgt[w]; ties_seen += (unsigned long long)wtie[w]; }
+  // kept before this wave: every above-cutoff score, and min(ties, k_tie)
+  int base = gt_before + (int)min(ties_seen, k_tie);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = w0; c0 < w1; c0 += 64 * SEL_UNROLL) {
-    uint32_t bits[SEL_UNROLL];
-    #pragma unroll
-    for (int k = 0; k < SEL_UNROLL; ++k) {
-      const int i = c0 + lane + 64 * k;
-      bits[k] = i < w1 ? __float_as_uint(x[i]) : 0u;
-    }
-    #pragma unroll
-    for (int k = 0; k < SEL_UNROLL; ++k) {
-      const int i = c0 + lane + 64 * k;
-      const bool ok = i < w1;
-      const bool is_tie = ok && bits[k] == xstar;
-      const unsigned long long tmask = __ballot(is_tie);
-      const unsigned long long tie_rank = ties_seen + __popcll(tmask & below);
-      const bool keep = ok && (bits[k] > xstar || (is_tie && tie_rank < k_tie));
-      const unsigned long long kmask = __ballot(keep);
-      if (keep) out[base + __popcll(kmask & below)] = i;
-      base += __popcll(kmask);
-      ties_seen += __popcll(tmask);
-    }
+  for (int cs = w0; cs < w1; cs += 64) {
+    const int i = cs + lane;
+    const bool ok = i < w1;
+    const uint32_t b = ok ? __float_as_uint(v.x[i]) : 0u;
+    const bool is_tie = ok && b == xstar;
+    const unsigned long long tmask = __ballot(is_tie);
+    const unsigned long long tie_rank = ties_seen + __popcll(tmask & below);
+    const bool keep = ok && (b > xstar || (is_tie && tie_rank < k_tie));
+    const unsigned long long kmask = __ballot(keep);
+    if (keep) v.out[base + __popcll(kmask & below)] = i;
+    base += __popcll(kmask);
+    ties_seen += __popcll(tmask);
   }
-  if (tid == 0) *cnt = total_kept;
+}
+
+size_t select_workspace_bytes(int Hq, int64_t n_global) {
+  const int64_t chunks = (n_global + SEL_CHUNK - 1) / SEL_CHUNK;
+  return (size_t)Hq * 2 * (SEL_BINS * sizeof(unsigned long long) + sizeof(SelState) + chunks * 2 * sizeof(int)) + 256;
+}
+
+// the passes' partials and row LSE, then (256-byte aligned) the selection's
+static size_t index_pass_bytes(int Hq, int Hkv, int64_t n_global) {
+  const int64_t T = n_global / BLK;
+  const int64_t nsplit = std::min<int64_t>(T, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
+  return ((size_t)(Hq * BLK * nsplit * 2 + Hq * BLK) * sizeof(float) + 255) & ~(size_t)255;
 }
 
 size_t index_workspace_bytes(int Hq, int Hkv, int64_t n_global, int D, int last_q) {
   (void)D; (void)last_q;
-  const int64_t T = n_global / BLK;
-  const int64_t nsplit = std::min<int64_t>(T, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
-  return (size_t)(Hq * BLK * nsplit * 2 + Hq * BLK) * sizeof(float) + 256;
+  return index_pass_bytes(Hq, Hkv, n_global) + select_workspace_bytes(Hq, n_global);
 }
 
 // Shared set-up: the tiles walked (all T, or the NB tiles of rank_fixed) and
@@ -550,13 +654,28 @@ static void launch_combine(IndexArgs a, const float* in, int n, int64_t tstride,
 }
 
 int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
-                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
-                        hipStream_t stream) {
+                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes < select_workspace_bytes(Hq, n_global)) return VS_ERR_WORKSPACE;
   SelectArgs s;
   s.vert = vert_score; s.slash = slash_score; s.vert_idx = vert_idx; s.vert_cnt = vert_cnt;
   s.slash_idx = slash_idx; s.slash_cnt = slash_cnt; s.n_vert = n_global; s.n_slash = (int)(n_global / BLK);
   s.top_p = top_p;
-  hipLaunchKernelGGL(topp_select_kernel, dim3(Hq, 2), dim3(SEL_THREADS), 0, stream, s);
+  s.max_chunks = (int)((n_global + SEL_CHUNK - 1) / SEL_CHUNK);
+  char* w = (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  s.hist = (unsigned long long*)w;
+  w += (size_t)Hq * 2 * SEL_BINS * sizeof(unsigned long long);
+  s.state = (SelState*)w;
+  w += (size_t)Hq * 2 * sizeof(SelState);
+  s.counts = (int*)w;
+  const dim3 heads(Hq, 2), chunks(s.max_chunks, Hq, 2);
+  hipLaunchKernelGGL(sel_init_kernel, heads, dim3(SEL_WG), 0, stream, s);
+  for (int pass = 0; pass < 3; ++pass) {
+    hipLaunchKernelGGL(sel_hist_kernel, chunks, dim3(SEL_WG), 0, stream, s, pass);
+    hipLaunchKernelGGL(sel_scan_kernel, heads, dim3(SCAN_THREADS), 0, stream, s, pass);
+  }
+  hipLaunchKernelGGL(sel_count_kernel, chunks, dim3(SEL_WG), 0, stream, s);
+  hipLaunchKernelGGL(sel_write_kernel, chunks, dim3(SEL_WG), 0, stream, s);
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 
@@ -570,8 +689,9 @@ int launch_index_build(int dtype, int D, TView q_last, int Hq, int last_q, TView
   if (!launch_rowstat(dtype, D, a, stream)) return VS_ERR_UNSUPPORTED;
   launch_combine(a, a.part, a.nsplit, a.nsplit, 1, nullptr, stream);
   launch_colsum(dtype, D, a, stream);
+  const size_t off = index_pass_bytes(Hq, Hkv, lay.n_global);
   return launch_index_select(vert_score, slash_score, Hq, lay.n_global, top_p, vert_idx, vert_cnt, slash_idx,
-                             slash_cnt, stream);
+                             slash_cnt, (char*)ws + off, ws_bytes - off, stream);
 }
 
 int launch_index_rank_stats(int dtype, int D, TView q_last, int Hq, int last_q, TView k_local, int Hkv,

@@ -46,8 +46,10 @@ int launch_index_rank_mass(int dtype, int D, TView q_last, int Hq, int last_q, T
                            const vs_layout& lay, int rank, float scale, const float* all_stats, float* vert_score,
                            float* slash_score, void* ws, size_t ws_bytes, hipStream_t stream);
 
+size_t select_workspace_bytes(int Hq, int64_t n_global);
+
 int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
-                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
-                        hipStream_t stream);
+                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 }  // namespace vs

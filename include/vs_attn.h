@@ -196,13 +196,19 @@ int vs_index_rank_mass(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int r
                        const float* all_stats, float* vert_score, float* slash_score,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes vs_index_select needs (device memory; 0 for Hq <= 0 or
+ * n_global <= 0). */
+size_t vs_index_select_workspace_size(int Hq, int64_t n_global);
+
 /* vs_index_select: the top-p selection of vs_index_build on given scores
  * (vert_score [Hq, n_global], slash_score [Hq, n_global / 64], non-negative
- * fp32); outputs as for vs_index_build. VS_ERR_ARG for null pointers or
- * Hq <= 0; VS_ERR_UNSUPPORTED if n_global is not a multiple of 64. */
+ * fp32); outputs as for vs_index_build; ws: caller-owned scratch of
+ * vs_index_select_workspace_size bytes (contents need no initialisation).
+ * VS_ERR_ARG for null pointers or Hq <= 0; VS_ERR_UNSUPPORTED if n_global is
+ * not a multiple of 64; VS_ERR_WORKSPACE if ws_bytes is too small. */
 int vs_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
                     int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
-                    void* stream);
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---- 2. active region ------------------------------------------------- */
 

@@ -109,7 +109,8 @@ def test_index_distributed_ranks(kind, P, dtype_cfg):
            "vcnt": torch.empty(Hq, dtype=torch.int32, device="cuda"),
            "sidx": torch.full((Hq, N // 64), -7, dtype=torch.int32, device="cuda"),
            "scnt": torch.empty(Hq, dtype=torch.int32, device="cuda")}
-    vs.vs_index_select(v, s, Hq, N, cfg.top_p, out["vidx"], out["vcnt"], out["sidx"], out["scnt"])
+    sws = torch.empty(vs.index_select_workspace_size(Hq, N), dtype=torch.uint8, device="cuda")
+    vs.vs_index_select(v, s, Hq, N, cfg.top_p, out["vidx"], out["vcnt"], out["sidx"], out["scnt"], sws)
     torch.cuda.synchronize()
     assert not torch.isnan(v).any() and not torch.isnan(s).any()    # every entry written by some rank
     ref = oi.build_index_distributed(t["q"][:, N - 64:], t["k"], cfg.scale, N, cfg.top_p, kind, P)
