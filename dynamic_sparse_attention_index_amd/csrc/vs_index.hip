@@ -26,7 +26,7 @@
 
 namespace vs {
 
-constexpr int IDX_SPLIT_TARGET = 1024;   // workgroups per pass (over all kv heads)
+constexpr int IDX_SPLIT_TARGET = 256;    // workgroups per pass (over all kv heads)
 
 struct IndexArgs {
   const void* q; const void* k;
@@ -118,6 +118,38 @@ __device__ __forceinline__ int64_t stage_key_tile(T* Ks, const IndexArgs& a, int
   return global_block(a.kind, a.P, a.NB, tau / a.NB, tau % a.NB);
 }
 
+// The same copy split in two, for workgroups of at least BLK * CPR / KPF_N
+// threads: key_tile_load issues the global loads of tile `tau` into
+// registers (they stay in flight while the current tile is scored), and
+// key_tile_store writes them to LDS.
+constexpr int KPF_N = 4;
+template <typename T, int D>
+__device__ __forceinline__ void key_tile_load(i32x4* r, const IndexArgs& a, int kvh, int tau, int tid, int nthr) {
+  constexpr int CPR = IdxTile<T, D>::CPR;
+  const T* kb = (const T*)a.k + kvh * a.ksh + (int64_t)tau * BLK * a.ksn;
+#pragma unroll
+  for (int j = 0; j < KPF_N; ++j) {
+    const int ch = tid + j * nthr;
+    if (ch < BLK * CPR) {
+      const int row = ch / CPR, col = (ch % CPR) * (16 / (int)sizeof(T));
+      r[j] = *(const i32x4*)(kb + (int64_t)row * a.ksn + col);
+    }
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void key_tile_store(T* Ks, const i32x4* r, int tid, int nthr) {
+  constexpr int KP = IdxTile<T, D>::KP, CPR = IdxTile<T, D>::CPR;
+#pragma unroll
+  for (int j = 0; j < KPF_N; ++j) {
+    const int ch = tid + j * nthr;
+    if (ch < BLK * CPR) *(i32x4*)(Ks + (ch / CPR) * KP + (ch % CPR) * (16 / (int)sizeof(T))) = r[j];
+  }
+}
+__device__ __forceinline__ int64_t key_tile_block(const IndexArgs& a, int tau) {
+  if (a.rank_fixed >= 0) return global_block(a.kind, a.P, a.NB, a.rank_fixed, tau);
+  return global_block(a.kind, a.P, a.NB, tau / a.NB, tau % a.NB);
+}
+
 // Pass 1: grid (nsplit, Hkv), 64 * group threads (one wave per q head).
 template <typename T, int D>
 __global__ void __launch_bounds__(512) index_rowstat_kernel(IndexArgs a) {
@@ -136,9 +168,21 @@ __global__ void __launch_bounds__(512) index_rowstat_kernel(IndexArgs a) {
     for (int i = 0; i < 4; ++i) { m[rs][i] = -INFINITY; l[rs][i] = 0.f; }
   const int tau0 = blockIdx.x * a.tiles_per;
   const int tau1 = min(a.ntiles, tau0 + a.tiles_per);
+  // with enough threads, the next tile's loads are issued before this tile
+  // is scored (wave-uniform choice)
+  const bool pf = nthr * KPF_N >= BLK * Tl::CPR;
+  i32x4 kreg[KPF_N];
+  if (pf && tau0 < tau1) key_tile_load<T, D>(kreg, a, kvh, tau0, tid, nthr);
   for (int tau = tau0; tau < tau1; ++tau) {
-    const int64_t G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
+    int64_t G;
+    if (pf) {
+      key_tile_store<T, D>(Ks, kreg, tid, nthr);
+      G = key_tile_block(a, tau);
+    } else {
+      G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
+    }
     __syncthreads();
+    if (pf && tau + 1 < tau1) key_tile_load<T, D>(kreg, a, kvh, tau + 1, tid, nthr);
     f32x4 acc[4][4];
     score_tile<T, D>(Ks, qa, n16, g4, acc);
     const bool last = G == a.T - 1;
@@ -238,9 +282,21 @@ __global__ void __launch_bounds__(512) index_colsum_kernel(IndexArgs a) {
   const float inv_rows = 1.f / (float)a.last_q;
   const int tau0 = blockIdx.x * a.tiles_per;
   const int tau1 = min(a.ntiles, tau0 + a.tiles_per);
+  // with enough threads, the next tile's loads are issued before this tile
+  // is scored (wave-uniform choice)
+  const bool pf = nthr * KPF_N >= BLK * Tl::CPR;
+  i32x4 kreg[KPF_N];
+  if (pf && tau0 < tau1) key_tile_load<T, D>(kreg, a, kvh, tau0, tid, nthr);
   for (int tau = tau0; tau < tau1; ++tau) {
-    const int64_t G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
+    int64_t G;
+    if (pf) {
+      key_tile_store<T, D>(Ks, kreg, tid, nthr);
+      G = key_tile_block(a, tau);
+    } else {
+      G = stage_key_tile<T, D>(Ks, a, kvh, tau, tid, nthr);
+    }
     __syncthreads();
+    if (pf && tau + 1 < tau1) key_tile_load<T, D>(kreg, a, kvh, tau + 1, tid, nthr);
     f32x4 acc[4][4];
     score_tile<T, D>(Ks, qa, n16, g4, acc);
     const bool last = G == a.T - 1;
