@@ -103,12 +103,12 @@ def main():
     o = torch.empty(Hq, N, D, device=dev)
     lse = torch.empty(Hq, N, device=dev)
     delta = torch.empty(Hq, N, device=dev)
-    dq = torch.zeros(Hq, N, D, device=dev)
-    dk = torch.zeros(Hkv, N, D, device=dev)
-    dv = torch.zeros(Hkv, N, D, device=dev)
+    dq = torch.empty(Hq, N, D, device=dev)     # written whole by the backward step
+    dk = torch.empty(Hkv, N, D, device=dev)
+    dv = torch.empty(Hkv, N, D, device=dev)
     stream = torch.cuda.current_stream()
 
-    stages = ("index", "mask", "fwd", "bwd_prep_zero", "dq", "dkdv", "dkdv_vert")
+    stages = ("index", "mask", "fwd", "bwd_prep", "dq", "dkdv", "dkdv_vert")
     ev = {name: [] for name in stages}
 
     def step(record):
@@ -126,13 +126,13 @@ def main():
         mark(3)
         if cfg.backward:
             vs.vs_attn_bwd_prep(o, do, delta, stream)
-            dq.zero_()
-            dk.zero_()
-            dv.zero_()
             mark(4)
-            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DQ, stream)
+            # dq and the slash dk/dv write their outputs whole; the vertical part adds after them
+            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv,
+                                 vs.VS_BWD_DQ | vs.VS_BWD_OVERWRITE, stream)
             mark(5)
-            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DKDV, stream)
+            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv,
+                                 vs.VS_BWD_DKDV | vs.VS_BWD_OVERWRITE, stream)
             mark(6)
             vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DKDV_VERT, stream)
         else:
@@ -169,7 +169,7 @@ def main():
     sparsity = 1.0 - A / total_causal
     eff_flops = (4 + (10 if cfg.backward else 0)) * D * A
     tflops = eff_flops / (ms_per_step * 1e-3) / 1e12
-    attn_ms = sum(stage_ms[x] for x in ("fwd", "bwd_prep_zero", "dq", "dkdv", "dkdv_vert"))
+    attn_ms = sum(stage_ms[x] for x in ("fwd", "bwd_prep", "dq", "dkdv", "dkdv_vert"))
     attn_tflops = eff_flops / (attn_ms * 1e-3) / 1e12
 
     # Roofline of the dominant kernel. Each timed stage below is exactly one

@@ -268,7 +268,7 @@ int vs_attn_bwd_parts(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, con
   if ((st = check_attn(q, k, v, m)) != VS_OK) return st;
   if ((st = check_tensor(dout, m->Hq, (int64_t)m->QB * 64, q.D)) != VS_OK) return st;
   if (dout.dtype != q.dtype) return VS_ERR_ARG;
-  if (parts <= 0 || (parts & ~VS_BWD_ALL)) return VS_ERR_ARG;
+  if ((parts & VS_BWD_ALL) == 0 || (parts & ~(VS_BWD_ALL | VS_BWD_OVERWRITE))) return VS_ERR_ARG;
   if (!lse || !delta || !dq || !dk || !dv) return VS_ERR_ARG;
   if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return VS_ERR_UNSUPPORTED;
   if (!(scale > 0.f)) return VS_ERR_ARG;

@@ -38,7 +38,16 @@ struct BwdArgs {
   float *dq, *dk, *dv;
   int Hq, Hkv, QB, KB, W, kind, P, rank, src;
   float scale, scale_log2;
+  int overwrite;   // dq and slash dk/dv written, not added (VS_BWD_OVERWRITE)
 };
+
+// Zero 64 rows of D = TD floats at `rows` with a workgroup of BWD_THREADS
+// (an overwriting part's rows that receive no contribution).
+__device__ __forceinline__ void zero_rows64(float* rows, int tid) {
+#pragma unroll
+  for (int j = 0; j < BLK * TD / 4 / BWD_THREADS; ++j)
+    *(f32x4*)(rows + 4 * (tid + j * BWD_THREADS)) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
 
 // Row/key permutation inside a 64-wide tile (see the forward kernel): value i
 // of subtile t in lane group g is position 32*(t/2) + 8*g + 4*(t%2) + i.
@@ -451,7 +460,10 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
   bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
   bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
   const int total = bt.total;
-  if (total == 0) return;
+  if (total == 0) {
+    if (a.overwrite) zero_rows64(a.dq + ((int64_t)h * a.QB * BLK + (int64_t)I * BLK) * TD, tid);
+    return;
+  }
   const uint32_t* sbg = a.slash_bits + (int64_t)h * a.W;
   for (int w = tid; w < a.W; w += BWD_THREADS) sbits[w] = sbg[w];
 
@@ -603,7 +615,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const f32x4 o1 = *(const f32x4*)(xo + ((rs * 8 + dt) * 64 + lane) * 4);
-      f32x4 r = *(f32x4*)(out + 16 * dt + 4 * g4);
+      f32x4 r = a.overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *(f32x4*)(out + 16 * dt + 4 * g4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] += (acc[rs][dt][i] + o1[i]) * a.scale;
       *(f32x4*)(out + 16 * dt + 4 * g4) = r;
@@ -774,10 +786,11 @@ __device__ __forceinline__ void stage_qblock(bf16* Qn, bf16* On, float* ln, cons
 
 // Combine the two row halves' dK/dV partials (rh = 1 -> rh = 0 through LDS)
 // and add them to dk/dv (plain stores when `atomic` is 0, fp32 atomics
-// otherwise). keys[kt]: output row of this lane's key kt (-1 = none).
+// otherwise; with `overwrite` the plain stores replace the old values).
+// keys[kt]: output row of this lane's key kt (-1 = none).
 __device__ __forceinline__ void kv_finish(float* xbuf_dk, float* xbuf_dv, f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8],
                                           float* dk, float* dv, const int64_t* keys, int kh, int rh, int lane, int g4,
-                                          float scale, bool atomic) {
+                                          float scale, bool atomic, bool overwrite) {
   constexpr int D = TD;
   float* xk = xbuf_dk + kh * (2 * 8 * 64 * 4);
   float* xv = xbuf_dv + kh * (2 * 8 * 64 * 4);
@@ -809,8 +822,8 @@ __device__ __forceinline__ void kv_finish(float* xbuf_dk, float* xbuf_dv, f32x4 
           atomicAdd(vr + 16 * dt + 4 * g4 + i, acc_dv[kt][dt][i] + v1[i]);
         }
       } else {
-        f32x4 x = *(f32x4*)(kr + 16 * dt + 4 * g4);
-        f32x4 y = *(f32x4*)(vr + 16 * dt + 4 * g4);
+        f32x4 x = overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *(f32x4*)(kr + 16 * dt + 4 * g4);
+        f32x4 y = overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *(f32x4*)(vr + 16 * dt + 4 * g4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x[i] += (acc_dk[kt][dt][i] + k1[i]) * scale;
@@ -871,7 +884,14 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   }
   int total = 0;
   for (int hh = 0; hh < grp; ++hh) total += __builtin_amdgcn_readlane(cnt_l, hh);
-  if (total == 0) return;
+  if (total == 0) {
+    if (a.overwrite) {
+      const int64_t r0 = ((int64_t)kvh * a.KB * BLK + (int64_t)J * BLK) * TD;
+      zero_rows64(a.dk + r0, tid);
+      zero_rows64(a.dv + r0, tid);
+    }
+    return;
+  }
   // per-head row-0 offsets (bytes) of Q and dO, and of the head's lse / delta rows
   const int64_t q_off_l = lane < grp ? (int64_t)(kvh * grp + lane) * a.qsh * 2 : 0;
   const int64_t o_off_l = lane < grp ? (int64_t)(kvh * grp + lane) * a.dsh * 2 : 0;
@@ -1015,7 +1035,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) keys[kt] = (int64_t)kvh * a.KB * BLK + (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
   wait_all_mem();
-  kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, false);
+  kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, false,
+            a.overwrite != 0);
 }
 
 // dK/dV of vertical columns: work items (head, 64-column chunk of the shard's
@@ -1112,7 +1133,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
     int64_t keys[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) keys[kt] = valid[kt] ? (int64_t)kvh * a.KB * BLK + m[kt] : -1;
-    kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, true);
+    kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, true, false);
   }
 }
 
@@ -1152,8 +1173,22 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 
+// n floats (a multiple of 4) set to zero
+__global__ void zero_f32_kernel(float* p, int64_t n) {
+  for (int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x); i < n; i += 4 * (int64_t)gridDim.x * blockDim.x)
+    *(f32x4*)(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 template <typename T, int D>
 static void launch_bwd_typed(const BwdArgs& a, int parts, hipStream_t stream) {
+  if (parts & VS_BWD_OVERWRITE) {   // these kernels add: clear their outputs first
+    const int64_t nq = (int64_t)a.Hq * a.QB * BLK * D, nk = (int64_t)a.Hkv * a.KB * BLK * D;
+    if (parts & VS_BWD_DQ) hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, stream, a.dq, nq);
+    if (parts & VS_BWD_DKDV) {
+      hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, stream, a.dk, nk);
+      hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, stream, a.dv, nk);
+    }
+  }
   if (parts & VS_BWD_DQ)
     hipLaunchKernelGGL((dq_kernel<T, D>), dim3(xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv)), dim3(BWD_THREADS), 0, stream, a);
   if (parts & VS_BWD_DKDV)
@@ -1176,7 +1211,9 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src;
   a.scale = scale; a.scale_log2 = scale * LOG2E;
+  a.overwrite = 0;
   if (dtype == VS_BF16 && D == 128) {
+    a.overwrite = (parts & VS_BWD_OVERWRITE) ? 1 : 0;
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     const int64_t krows = (int64_t)m->KB * BLK, qrows = (int64_t)m->QB * BLK;
     if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn) || !dma_offsets_fit(qrows, q.sn) ||

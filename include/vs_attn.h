@@ -272,11 +272,17 @@ int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout,
  *                   over the CSC lists; plain read-modify-write);
  *   VS_BWD_DKDV_VERT -- dk/dv of the vertical columns (fp32 atomics).
  * `parts` is an OR of these; VS_BWD_ALL is vs_attn_bwd. Parts that write the
- * same array (the two dk/dv parts) must not run concurrently. */
+ * same array (the two dk/dv parts) must not run concurrently.
+ * With VS_BWD_OVERWRITE also set, the VS_BWD_DQ and VS_BWD_DKDV parts write
+ * their arrays instead of adding to them (every row of dq and every key row
+ * of dk/dv gets a value, zero where the step has no active entry), so the
+ * caller need not zero them for the first ring step; VS_BWD_DKDV_VERT always
+ * adds and must then run after VS_BWD_DKDV. */
 #define VS_BWD_DQ 1
 #define VS_BWD_DKDV 2
 #define VS_BWD_DKDV_VERT 4
 #define VS_BWD_ALL 7
+#define VS_BWD_OVERWRITE 8
 int vs_attn_bwd_parts(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout,
                       const float* lse, const float* delta, const vs_mask* m, float scale,
                       float* dq, float* dk, float* dv, int parts, void* stream);

@@ -203,3 +203,50 @@ def test_merge_kernel_matches_formula():
     fin = np.isfinite(ref_l)
     assert np.abs(tl.cpu().numpy()[fin] - ref_l[fin]).max() < 1e-5
     assert (tl.cpu().numpy()[~fin] == -np.inf).all()
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_bwd_overwrite_matches_accumulate(dtype, D):
+    """VS_BWD_OVERWRITE on NaN-filled outputs gives what the adding parts give
+    on zeroed ones: dq and the slash dk/dv bit for bit (rows without a
+    contribution become zero), and after the vertical part (fp32 atomics in
+    both runs) to 1e-6. One ring step that leaves many blocks empty."""
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    rng = np.random.default_rng(11)
+    kind, P, rank, step = "striped", 4, 1, 2
+    cfg = config_by_name("qwen32k", N=64 * 32, Hq=4, Hkv=2, D=D, dtype=dtype, n_out=4, c=2.0)
+    vert, slash = _index(rng, cfg.N, cfg.Hq, 40, 3, band=0)
+    t = generate(cfg)
+    N, Hq, Hkv = cfg.N, cfg.Hq, cfg.Hkv
+    lay = vs.layout(kind, P, N)
+    QB = N // 64 // P
+    lists = H.upload_lists(vert, slash, N)
+    cap = H.tile_cap_for(slash, Hq, QB)
+    src = ol.ring_source(rank, step, P)
+    q = H.to_dev(H.shard(t["q"], kind, P, rank), cfg.dtype)
+    do = H.to_dev(H.shard(t["do"], kind, P, rank), cfg.dtype)
+    k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
+    v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+    m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+    o = torch.zeros(Hq, QB * 64, D, device="cuda")
+    lse = torch.full((Hq, QB * 64), -math.inf, device="cuda")
+    vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse, accumulate=1)
+    delta = torch.empty(Hq, QB * 64, device="cuda")
+    vs.vs_attn_bwd_prep(o, do, delta)
+    shapes = ((Hq, QB * 64, D), (Hkv, QB * 64, D), (Hkv, QB * 64, D))
+    ref = [torch.zeros(sh, device="cuda") for sh in shapes]
+    got = [torch.full(sh, float("nan"), device="cuda") for sh in shapes]
+    vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, m, cfg.scale, *ref, vs.VS_BWD_DQ | vs.VS_BWD_DKDV)
+    vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, m, cfg.scale, *got,
+                         vs.VS_BWD_DQ | vs.VS_BWD_DKDV | vs.VS_BWD_OVERWRITE)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+    n_zero_rows = int((ref[1].abs().sum(dim=2) == 0).sum().item())
+    assert n_zero_rows > 0            # the case has key rows without any contribution
+    vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, m, cfg.scale, *ref, vs.VS_BWD_DKDV_VERT)
+    vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, m, cfg.scale, *got, vs.VS_BWD_DKDV_VERT)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.allclose(a, b, rtol=1e-6, atol=1e-7)
