@@ -19,6 +19,10 @@ Readings (the pages leave these open):
     index, with exact fixed-point sums (q_i = round(x_i * 2^40),
     target = ceil(round(p * 2^32) * sum q / 2^32));
   * p >= 1 keeps everything, p <= 0 keeps nothing.
+
+Two other budgets on the same scores: a fixed count per head (select_top_k)
+and one top-p over the pooled vertical and slash candidates
+(select_joint_top_p).
 """
 import numpy as np
 
@@ -95,6 +99,43 @@ def select_top_p(x: np.ndarray, p: float) -> np.ndarray:
     cum = np.cumsum(q[order])
     k = int(np.searchsorted(cum, tgt, side="left")) + 1
     return np.sort(order[:k])
+
+
+def select_top_k(x: np.ndarray, k: int) -> np.ndarray:
+    """Fixed-count budget: the min(k, n) largest scores, ties to the lower
+    index (ascending output); k <= 0 keeps nothing.
+
+    The review (page 1, section 八, item 4) reports that its experiments fix
+    the sparsity at 95% by hand instead of adapting it; a fixed count of
+    verticals and slashes per head is the plain form of such a budget, the
+    caller choosing the counts that give the sparsity it wants.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    n = x.shape[0]
+    k = max(0, min(int(k), n))
+    order = np.lexsort((np.arange(n), -x.astype(np.float64)))      # x desc, index asc
+    return np.sort(order[:k])
+
+
+def select_joint_top_p(v: np.ndarray, s: np.ndarray, p: float):
+    """Joint budget: one top-p over the pooled vertical and slash scores.
+
+    Page 1, section 三.2 item 1 asks for the fewest verticals and slashes that
+    recall the target mass; read jointly, the count that is minimised is the
+    number of verticals plus slashes. The candidates of one head are its n
+    verticals followed by its T slashes; the fewest of them in descending
+    score order (ties: verticals before slashes, then the lower index) whose
+    fixed-point mass reaches p of the pooled total are kept, with the same
+    integer rule as select_top_p. Each attention entry is counted once in its
+    column and once in its diagonal; the overlap of a chosen column and a
+    chosen diagonal is not deducted (the pages give no rule for it).
+    Returns (vertical indices, slash indices), each ascending.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    s = np.asarray(s, dtype=np.float32)
+    n = v.shape[0]
+    kept = select_top_p(np.concatenate([v, s]), p)
+    return kept[kept < n], kept[kept >= n] - n
 
 
 def build_index(q_last, k, scale, n_global, top_p):

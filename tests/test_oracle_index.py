@@ -141,6 +141,86 @@ def test_select_edges_and_monotone():
         prev = cur
 
 
+def _golden_lines(name):
+    for line in open(os.path.join(GOLDEN, name)):
+        if not line.startswith("#") and line.strip():
+            yield [f.split() for f in line.split(";")]
+
+
+@pytest.mark.parametrize("x,k,expected", [
+    (np.array(xs, dtype=np.float32), int(k[0]), [int(t) for t in sel])
+    for xs, k, sel in _golden_lines("select_top_k.txt")])
+def test_select_top_k_golden(x, k, expected):
+    assert list(oi.select_top_k(x, k)) == expected
+
+
+def _brute_top_k(x_units, k):
+    """Largest-mass subset of size min(k, n), then the lexicographically
+    smallest sorted indices."""
+    n = len(x_units)
+    k = max(0, min(k, n))
+    best = None
+    for comb in itertools.combinations(range(n), k):
+        key = (-sum(x_units[i] for i in comb), comb)
+        if best is None or key < best:
+            best = key
+    return list(best[1])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_select_top_k_bruteforce(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 10))
+    units = rng.integers(0, 5, size=n)
+    x = (units * 2.0 ** -20).astype(np.float32)
+    k = int(rng.integers(-1, n + 2))
+    assert list(oi.select_top_k(x, k)) == _brute_top_k([int(u) for u in units], k)
+
+
+@pytest.mark.parametrize("v,s,p,ev,es", [
+    (np.array(v, dtype=np.float32), np.array(s, dtype=np.float32), float(p[0]), [int(t) for t in ev],
+     [int(t) for t in es]) for v, s, p, ev, es in _golden_lines("select_joint.txt")])
+def test_select_joint_golden(v, s, p, ev, es):
+    gv, gs = oi.select_joint_top_p(v, s, p)
+    assert (list(gv), list(gs)) == (ev, es)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_select_joint_bruteforce(seed):
+    """Fewest pooled candidates reaching p of the pooled mass (exact rationals;
+    candidate order: verticals, then slashes)."""
+    rng = np.random.default_rng(200 + seed)
+    nv, ns = int(rng.integers(1, 7)), int(rng.integers(1, 5))
+    uv, us = rng.integers(0, 6, size=nv), rng.integers(0, 9, size=ns)
+    if uv.sum() + us.sum() == 0:
+        uv[0] = 1
+    v = (uv * 2.0 ** -20).astype(np.float32)
+    s = (us * 2.0 ** -20).astype(np.float32)
+    p_num = int(rng.integers(1, 256))
+    gv, gs = oi.select_joint_top_p(v, s, p_num / 256.0)
+    want = _brute_select([int(u) for u in uv] + [int(u) for u in us], p_num, 256)
+    assert list(gv) == [i for i in want if i < nv]
+    assert list(gs) == [i - nv for i in want if i >= nv]
+
+
+def test_select_joint_properties():
+    rng = np.random.default_rng(5)
+    v = rng.random(3000).astype(np.float32) ** 8
+    s = rng.random(47).astype(np.float32) ** 4
+    for p in (0.3, 0.8, 0.95):
+        gv, gs = oi.select_joint_top_p(v, s, p)
+        # the separate selections together also reach p of the pooled mass,
+        # so the joint count can be no larger than theirs
+        assert len(gv) + len(gs) <= len(oi.select_top_p(v, p)) + len(oi.select_top_p(s, p))
+        # no slash candidates: the joint budget is the vertical top-p
+        jv, js = oi.select_joint_top_p(v, np.zeros_like(s), p)
+        assert list(jv) == list(oi.select_top_p(v, p)) and len(js) == 0
+    gv, gs = oi.select_joint_top_p(v, s, 1.0)
+    assert len(gv) == 3000 and len(gs) == 47
+    gv, gs = oi.select_joint_top_p(v, s, 0.0)
+    assert len(gv) == 0 and len(gs) == 0
+
+
 def _index_for(cfg):
     t = generate(cfg, tensors=("q", "k"), rows=None)
     q_last = t["q"][:, cfg.N - cfg.last_q:]
