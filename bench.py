@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--workload", default="qwen128k")
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-budgets", action="store_true", help="skip the budget-rule report (after the timed steps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-probe", action="store_true", help="run only a 1 GiB device copy (counter scaling)")
     ap.add_argument("--layouts", default="striped,zigzag", help="ring simulation: layouts to compare")
@@ -214,6 +215,9 @@ def main():
                   "frac_mfma_peak": round(idx_flops / (stage_ms["index"] * 1e-3) / 1e12 / peak, 4)}
     strict_tflops = (4 + (8 if cfg.backward else 0)) * D * A / (ms_per_step * 1e-3) / 1e12
 
+    budgets = None if args.no_budgets else budget_report(vs, torch, Hq, Hkv, N, lay, vert_s, slash_s, cfg.top_p,
+                                                         stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, host, vidx, vcnt, sidx, scnt, args.cpu_seconds, tflops_unit=True)
@@ -232,9 +236,64 @@ def main():
         "active_entries": A, "active_slash_tiles": A_slash, "active_vertical": A_vert,
         "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
         "strict_algorithmic_tflops": round(strict_tflops, 3), "index_pass": index_pass,
-        "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(gen_s, 1),
+        "roofline": roofline, "cpu_baseline": cpu, "budgets": budgets, "gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def budget_report(vs, torch, Hq, Hkv, N, lay, vert_s, slash_s, top_p, stream, target=0.95, reps=20):
+    """The three budget rules on the workload's own scores: selection time
+    (one launch sequence, mean over `reps`), mean kept counts and the
+    sparsity of the mask they give. The fixed-count budget is sized for
+    `target` sparsity (the pages' hand-fixed 95%): counts proportional to the
+    top-p means, scaled by bisection until the mask just reaches it."""
+    dev = vert_s.device
+    T = N // 64
+    vidx = torch.empty(Hq, N, dtype=torch.int32, device=dev)
+    vcnt = torch.empty(Hq, dtype=torch.int32, device=dev)
+    sidx = torch.empty(Hq, T, dtype=torch.int32, device=dev)
+    scnt = torch.empty(Hq, dtype=torch.int32, device=dev)
+    sws = torch.empty(vs.index_select_workspace_size(Hq, N), dtype=torch.uint8, device=dev)
+    total_causal = Hq * N * (N + 1) // 2
+
+    def run(budget, p, kv, ks):
+        vs.vs_index_select_budget(vert_s, slash_s, Hq, N, budget, p, kv, ks, vidx, vcnt, sidx, scnt, sws, stream)
+
+    def sparsity():
+        torch.cuda.synchronize()
+        m = vs.Mask(Hq, Hkv, lay, tile_cap=Hq * T * (int(scnt.max().item()) + 1))
+        vs.vs_block_mask(vidx, vcnt, sidx, scnt, 0, 0, m, stream)
+        torch.cuda.synchronize()
+        arr = m.arrays()
+        if int(arr["status"].item()) != 0:
+            raise RuntimeError("mask status in budget report")
+        return 1.0 - int(arr["n_active"].sum().item()) / total_causal
+
+    def entry(budget, p, kv, ks):
+        run(budget, p, kv, ks)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run(budget, p, kv, ks)
+        e1.record(stream)
+        sp = sparsity()
+        return {"select_ms": round(e0.elapsed_time(e1) / reps, 4), "mean_verticals": round(float(vcnt.float().mean()), 1),
+                "mean_slashes": round(float(scnt.float().mean()), 1), "sparsity": round(sp, 5)}
+
+    out = {"top_p": dict(entry(vs.VS_BUDGET_TOP_P, top_p, 0, 0), p=top_p)}
+    mv, ms = out["top_p"]["mean_verticals"], out["top_p"]["mean_slashes"]
+    lo, hi = 0.0, 4.0                               # scale of the counts; sparsity falls as it grows
+    for _ in range(16):
+        mid = 0.5 * (lo + hi)
+        run(vs.VS_BUDGET_TOP_K, 0.0, max(1, round(mid * mv)), max(1, round(mid * ms)))
+        if sparsity() >= target:
+            lo = mid
+        else:
+            hi = mid
+    kv, ks = max(1, round(lo * mv)), max(1, round(lo * ms))
+    out["top_k"] = dict(entry(vs.VS_BUDGET_TOP_K, 0.0, kv, ks), k_vert=kv, k_slash=ks, target_sparsity=target)
+    out["joint_top_p"] = dict(entry(vs.VS_BUDGET_JOINT_TOP_P, top_p, 0, 0), p=top_p)
+    return out
 
 
 def ring_report(args, cfg):

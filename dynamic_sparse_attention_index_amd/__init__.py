@@ -27,7 +27,7 @@ TILE_MASK = 0x3FFFFFFF
 
 EXPORTED = [
     "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_index_rank_stats", "vs_index_rank_mass",
-    "vs_index_select_workspace_size", "vs_index_select", "vs_mask_bytes", "vs_mask_init",
+    "vs_index_select_workspace_size", "vs_index_select", "vs_index_select_budget", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
@@ -86,6 +86,8 @@ def lib():
         L.vs_index_rank_mass.argtypes = [VsTensor, VsTensor, VsLayout, i32, f32, vp, vp, vp, vp, sz, vp]
         L.vs_index_select.restype = i32
         L.vs_index_select.argtypes = [vp, vp, i32, i64, f32, vp, vp, vp, vp, vp, sz, vp]
+        L.vs_index_select_budget.restype = i32
+        L.vs_index_select_budget.argtypes = [vp, vp, i32, i64, i32, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.vs_index_select_workspace_size.restype = sz
         L.vs_index_select_workspace_size.argtypes = [i32, i64]
         L.vs_mask_bytes.restype = sz
@@ -193,6 +195,19 @@ def vs_index_select(vert_score, slash_score, Hq, n_global, top_p, vert_idx, vert
                                  _ptr(vert_cnt), _ptr(slash_idx), _ptr(slash_cnt), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)),
            "vs_index_select")
+
+
+VS_BUDGET_TOP_P = 0
+VS_BUDGET_TOP_K = 1
+VS_BUDGET_JOINT_TOP_P = 2
+
+
+def vs_index_select_budget(vert_score, slash_score, Hq, n_global, budget, top_p, k_vert, k_slash, vert_idx, vert_cnt,
+                           slash_idx, slash_cnt, ws, stream=None):
+    _check(lib().vs_index_select_budget(_cptr(vert_score), _cptr(slash_score), Hq, n_global, int(budget), top_p,
+                                        int(k_vert), int(k_slash), _ptr(vert_idx), _ptr(vert_cnt), _ptr(slash_idx),
+                                        _ptr(slash_cnt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "vs_index_select_budget")
 
 
 class Mask:

@@ -11,6 +11,12 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Float classification on the bit pattern: the library is built without NaN
+// semantics, under which x != x and comparisons with NaN fold away.
+uint32_t float_bits(float x) { uint32_t b; memcpy(&b, &x, 4); return b; }
+bool is_nan(float x) { return (float_bits(x) & 0x7FFFFFFFu) > 0x7F800000u; }
+bool finite_positive(float x) { const uint32_t b = float_bits(x); return b > 0u && b < 0x7F800000u; }
+
 int elem_bytes(int dtype) { return dtype == VS_BF16 ? 2 : 4; }
 
 // Checks every property the kernels rely on for a [H, N, D] view.
@@ -104,7 +110,7 @@ int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, fl
   if (q_last.dtype != k.dtype || !supported_dtype_dim(k.dtype, D)) return VS_ERR_UNSUPPORTED;
   if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || !ws)
     return VS_ERR_ARG;
-  if (!(scale > 0.f) || top_p != top_p) return VS_ERR_ARG;
+  if (!finite_positive(scale) || is_nan(top_p)) return VS_ERR_ARG;
   if (ws_bytes < vs_index_workspace_size(Hq, Hkv, lay.n_global, D, last_q)) return VS_ERR_WORKSPACE;
   return launch_index_build(k.dtype, D, view(q_last), Hq, last_q, view(k), Hkv, lay, scale, top_p, vert_score,
                             slash_score, vert_idx, vert_cnt, slash_idx, slash_cnt, ws, ws_bytes,
@@ -124,7 +130,7 @@ static int check_rank_index(vs_tensor q_last, vs_tensor k_local, vs_layout lay, 
   if ((st = check_tensor(q_last, *Hq, *last_q, *D)) != VS_OK) return st;
   if ((st = check_tensor(k_local, *Hkv, lay.n_global / lay.P, *D)) != VS_OK) return st;
   if (q_last.dtype != k_local.dtype || !supported_dtype_dim(k_local.dtype, *D)) return VS_ERR_UNSUPPORTED;
-  if (!ws || !(scale > 0.f)) return VS_ERR_ARG;
+  if (!ws || !finite_positive(scale)) return VS_ERR_ARG;
   if (ws_bytes < vs_index_workspace_size(*Hq, *Hkv, lay.n_global, *D, *last_q)) return VS_ERR_WORKSPACE;
   return VS_OK;
 }
@@ -155,16 +161,24 @@ size_t vs_index_select_workspace_size(int Hq, int64_t n_global) {
   return select_workspace_bytes(Hq, n_global);
 }
 
+int vs_index_select_budget(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, int budget,
+                           float top_p, int k_vert, int k_slash, int32_t* vert_idx, int32_t* vert_cnt,
+                           int32_t* slash_idx, int32_t* slash_cnt, void* ws, size_t ws_bytes, void* stream) {
+  if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || Hq <= 0 || !ws)
+    return VS_ERR_ARG;
+  if (budget != VS_BUDGET_TOP_P && budget != VS_BUDGET_TOP_K && budget != VS_BUDGET_JOINT_TOP_P) return VS_ERR_ARG;
+  if (is_nan(top_p) || n_global <= 0) return VS_ERR_ARG;
+  if (n_global % 64 || n_global > ((int64_t)1 << 30)) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < select_workspace_bytes(Hq, n_global)) return VS_ERR_WORKSPACE;
+  return launch_index_select(vert_score, slash_score, Hq, n_global, budget, top_p, k_vert, k_slash, vert_idx,
+                             vert_cnt, slash_idx, slash_cnt, ws, ws_bytes, (hipStream_t)stream);
+}
+
 int vs_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
                     int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
                     void* ws, size_t ws_bytes, void* stream) {
-  if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || Hq <= 0 || !ws)
-    return VS_ERR_ARG;
-  if (top_p != top_p || n_global <= 0) return VS_ERR_ARG;
-  if (n_global % 64 || n_global / 64 > ((int64_t)1 << 24)) return VS_ERR_UNSUPPORTED;
-  if (ws_bytes < select_workspace_bytes(Hq, n_global)) return VS_ERR_WORKSPACE;
-  return launch_index_select(vert_score, slash_score, Hq, n_global, top_p, vert_idx, vert_cnt, slash_idx, slash_cnt,
-                             ws, ws_bytes, (hipStream_t)stream);
+  return vs_index_select_budget(vert_score, slash_score, Hq, n_global, VS_BUDGET_TOP_P, top_p, 0, 0, vert_idx,
+                                vert_cnt, slash_idx, slash_cnt, ws, ws_bytes, stream);
 }
 
 size_t vs_mask_bytes(int Hq, int Hkv, vs_layout lay, int64_t tile_cap) {
@@ -238,7 +252,7 @@ int vs_attn_fwd(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float s
   if ((st = check_attn(q, k, v, m)) != VS_OK) return st;
   if (!o || !lse || !aligned16(o)) return VS_ERR_ARG;
   if (accumulate != 0 && accumulate != 1) return VS_ERR_ARG;
-  if (!(scale > 0.f)) return VS_ERR_ARG;
+  if (!finite_positive(scale)) return VS_ERR_ARG;
   return launch_attn_fwd(q.dtype, q.D, view(q), view(k), view(v), m, scale, o, lse, accumulate,
                          (hipStream_t)stream);
 }
@@ -271,7 +285,7 @@ int vs_attn_bwd_parts(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, con
   if ((parts & VS_BWD_ALL) == 0 || (parts & ~(VS_BWD_ALL | VS_BWD_OVERWRITE))) return VS_ERR_ARG;
   if (!lse || !delta || !dq || !dk || !dv) return VS_ERR_ARG;
   if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return VS_ERR_UNSUPPORTED;
-  if (!(scale > 0.f)) return VS_ERR_ARG;
+  if (!finite_positive(scale)) return VS_ERR_ARG;
   return launch_attn_bwd(q.dtype, q.D, view(q), view(k), view(v), view(dout), lse, delta, m, scale, dq, dk, dv,
                          parts, (hipStream_t)stream);
 }

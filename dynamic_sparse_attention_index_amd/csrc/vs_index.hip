@@ -327,14 +327,17 @@ __global__ void __launch_bounds__(512) index_colsum_kernel(IndexArgs a) {
   }
 }
 
-// ---- exact top-p selection ---------------------------------------------------
+// ---- exact budget selection -------------------------------------------------
 // Radix select on the fp32 bit patterns of one (head, direction)'s scores
 // (non-negative: bit order = value order), each digit weighted by its
-// fixed-point mass, spread over many workgroups: a pass is one launch of
-// per-chunk histograms (LDS, then merged into a global histogram with 64-bit
-// atomics) and one launch that scans the global histogram and fixes the
-// digit. Digits: bits 31-20, 19-8, 7-0. Then a count launch and a write
-// launch compact the kept indices in ascending order.
+// fixed-point mass (top-p) or by one (fixed count), spread over many
+// workgroups: a pass is one launch of per-chunk histograms (LDS, then merged
+// into a global histogram with 64-bit atomics) and one launch that scans the
+// global histogram and fixes the digit. Digits: bits 31-20, 19-8, 7-0. Then a
+// count launch and a write launch compact the kept indices in ascending
+// order. The joint budget runs one selection per head over both directions:
+// they share the histogram and state of direction 0, and in the pooled order
+// the vertical ties come before the slash ties.
 constexpr int SEL_CHUNK = 4096;              // scores per workgroup
 constexpr int SEL_WG = 256;                  // threads of the chunk kernels
 constexpr int SEL_PER = SEL_CHUNK / SEL_WG;  // scores per thread
@@ -349,11 +352,15 @@ struct SelState {
   int pad[2];
 };
 
+enum { BUDGET_TOP_P = 0, BUDGET_TOP_K = 1, BUDGET_JOINT = 2 };
+
 struct SelectArgs {
   const float* vert; const float* slash;
   int32_t *vert_idx, *vert_cnt, *slash_idx, *slash_cnt;
   int64_t n_vert; int n_slash;
   float top_p;
+  int budget;                 // BUDGET_*
+  int k_vert, k_slash;        // counts of the fixed-count budget
   unsigned long long* hist;   // [Hq][2][SEL_BINS]
   SelState* state;            // [Hq][2]
   int* counts;                // [Hq][2][max_chunks][2]: (above the cutoff, at it)
@@ -404,6 +411,11 @@ __device__ __forceinline__ SelView sel_view(const SelectArgs& a, int h, int dir)
   return v;
 }
 
+// the histogram / state slot a (head, direction) selects with
+__device__ __forceinline__ int sel_slot(const SelectArgs& a, int h, int dir) {
+  return a.budget == BUDGET_JOINT ? 2 * h : 2 * h + dir;
+}
+
 __device__ __forceinline__ void sel_digit_bits(int pass, int& shift, int& width) {
   shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
   width = pass == 2 ? 8 : 12;
@@ -416,7 +428,14 @@ __global__ void __launch_bounds__(SEL_WG) sel_init_kernel(SelectArgs a) {
   for (int b = threadIdx.x; b < SEL_BINS; b += SEL_WG) gh[b] = 0;
   if (threadIdx.x == 0) {
     SelState s{};
-    s.mode = a.top_p >= 1.f ? 1 : (a.top_p > 0.f ? 0 : 2);
+    if (a.budget == BUDGET_TOP_K) {
+      const int64_t n = blockIdx.y ? a.n_slash : a.n_vert;
+      const int k = blockIdx.y ? a.k_slash : a.k_vert;
+      s.mode = k >= n ? 1 : (k > 0 ? 0 : 2);
+      s.rem = k > 0 ? (unsigned long long)k : 0ull;
+    } else {
+      s.mode = a.top_p >= 1.f ? 1 : (a.top_p > 0.f ? 0 : 2);
+    }
     a.state[hd] = s;
   }
 }
@@ -425,12 +444,13 @@ __global__ void __launch_bounds__(SEL_WG) sel_init_kernel(SelectArgs a) {
 // fixed prefix, by the pass's digit, merged into the global histogram
 __global__ void __launch_bounds__(SEL_WG) sel_hist_kernel(SelectArgs a, int pass) {
   __shared__ unsigned long long lh[SEL_BINS];
-  const int h = blockIdx.y, dir = blockIdx.z, hd = h * 2 + dir;
+  const int h = blockIdx.y, dir = blockIdx.z, hd = sel_slot(a, h, dir);
   const SelView v = sel_view(a, h, dir);
   const int c0 = blockIdx.x * SEL_CHUNK;
   if (c0 >= v.n) return;
   const SelState st = a.state[hd];
   if (st.mode != 0) return;
+  const bool by_count = a.budget == BUDGET_TOP_K;
   int shift, width;
   sel_digit_bits(pass, shift, width);
   const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + width));
@@ -448,7 +468,8 @@ __global__ void __launch_bounds__(SEL_WG) sel_hist_kernel(SelectArgs a, int pass
   for (int k = 0; k < SEL_PER; ++k) {
     const int i = c0 + tid + k * SEL_WG;
     if (i < v.n && (bits[k] & hi_mask) == st.prefix)
-      atomicAdd(&lh[(bits[k] >> shift) & dmask], (unsigned long long)fixed_mass(__uint_as_float(bits[k])));
+      atomicAdd(&lh[(bits[k] >> shift) & dmask],
+                by_count ? 1ull : (unsigned long long)fixed_mass(__uint_as_float(bits[k])));
   }
   __syncthreads();
   unsigned long long* gh = a.hist + (int64_t)hd * SEL_BINS;
@@ -464,6 +485,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) sel_scan_kernel(SelectArgs a, in
   __shared__ unsigned long long wsum[SCAN_THREADS / 64];
   __shared__ int wcnt[SCAN_THREADS / 64];
   __shared__ unsigned long long wab[SCAN_THREADS / 64];
+  if (a.budget == BUDGET_JOINT && blockIdx.y) return;
   const int hd = blockIdx.x * 2 + blockIdx.y;
   const SelState st = a.state[hd];
   if (st.mode != 0) return;
@@ -498,8 +520,8 @@ __global__ void __launch_bounds__(SCAN_THREADS) sel_scan_kernel(SelectArgs a, in
     total += wsum[w];
     if (w > wave) above_waves += wsum[w];
   }
-  unsigned long long rem = st.rem;
-  if (pass == 0) {
+  unsigned long long rem = st.rem;   // the fixed-count budget sets it at init
+  if (pass == 0 && a.budget != BUDGET_TOP_K) {
     const unsigned long long pq = (unsigned long long)__builtin_rint((double)a.top_p * 4294967296.0);
     const unsigned __int128 prod = (unsigned __int128)pq * total;
     rem = (unsigned long long)((prod + 0xFFFFFFFFull) >> 32);   // ceil(pq * total / 2^32)
@@ -534,8 +556,12 @@ __global__ void __launch_bounds__(SCAN_THREADS) sel_scan_kernel(SelectArgs a, in
     ns.rem = rem - above;
     ns.prefix = st.prefix | ((uint32_t)bstar << shift);
     if (pass == 2) {
-      const unsigned long long qstar = fixed_mass(__uint_as_float(ns.prefix));
-      ns.k_tie = qstar ? (ns.rem + qstar - 1) / qstar : 0;
+      if (a.budget == BUDGET_TOP_K) {
+        ns.k_tie = ns.rem;
+      } else {
+        const unsigned long long qstar = fixed_mass(__uint_as_float(ns.prefix));
+        ns.k_tie = qstar ? (ns.rem + qstar - 1) / qstar : 0;
+      }
     }
     a.state[hd] = ns;
   }
@@ -548,7 +574,7 @@ __global__ void __launch_bounds__(SEL_WG) sel_count_kernel(SelectArgs a) {
   const SelView v = sel_view(a, h, dir);
   const int c0 = blockIdx.x * SEL_CHUNK;
   if (c0 >= v.n) return;
-  const SelState st = a.state[hd];
+  const SelState st = a.state[sel_slot(a, h, dir)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int n_gt = 0, n_tie = 0;
   if (st.mode == 0) {
@@ -585,7 +611,7 @@ __global__ void __launch_bounds__(SEL_WG) sel_write_kernel(SelectArgs a) {
   const SelView v = sel_view(a, h, dir);
   const int chunk = blockIdx.x, c0 = chunk * SEL_CHUNK;
   if (c0 >= v.n) return;
-  const SelState st = a.state[hd];
+  const SelState st = a.state[sel_slot(a, h, dir)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunks = (v.n + SEL_CHUNK - 1) / SEL_CHUNK;
   if (st.mode == 1) {
@@ -607,10 +633,19 @@ __global__ void __launch_bounds__(SEL_WG) sel_write_kernel(SelectArgs a) {
   }
   g_before = wave_sum_i32(g_before); t_before = wave_sum_i32(t_before);
   g_all = wave_sum_i32(g_all); t_all = wave_sum_i32(t_all);
+  // joint budget, slashes: the vertical ties come first in the pooled order
+  int t_off = 0;
+  if (a.budget == BUDGET_JOINT && dir == 1) {
+    const int* cv = a.counts + (int64_t)(h * 2) * a.max_chunks * 2;
+    const int nch_v = (int)((a.n_vert + SEL_CHUNK - 1) / SEL_CHUNK);
+    for (int c = lane; c < nch_v; c += 64) t_off += cv[2 * c + 1];
+    t_off = wave_sum_i32(t_off);
+  }
   const unsigned long long k_tie = st.k_tie;
+  const unsigned long long kept_off = min((unsigned long long)t_off, k_tie);   // ties the verticals took
   const uint32_t xstar = st.prefix;
   if (chunk == 0 && tid == 0)
-    *v.cnt = g_all + (int)min((unsigned long long)t_all, k_tie);
+    *v.cnt = g_all + (int)(min((unsigned long long)(t_off + t_all), k_tie) - kept_off);
   // this wave's quarter: counts, then the waves before it
   const int w0 = min(v.n, c0 + wave * QUART), w1 = min(v.n, w0 + QUART);
   int n_gt = 0, n_tie = 0;
@@ -623,11 +658,12 @@ __global__ void __launch_bounds__(SEL_WG) sel_write_kernel(SelectArgs a) {
   n_tie = wave_sum_i32(n_tie);
   if (lane == 0) { wgt[wave] = n_gt; wtie[wave] = n_tie; }
   __syncthreads();
-  unsigned long long ties_seen = (unsigned long long)t_before;
+  unsigned long long ties_seen = (unsigned long long)(t_off + t_before);   // in the pooled order
   int gt_before = g_before;
   for (int w = 0; w < wave; ++w) { gt_before += wgt[w]; ties_seen += (unsigned long long)wtie[w]; }
-  // kept before this wave: every above-cutoff score, and min(ties, k_tie)
-  int base = gt_before + (int)min(ties_seen, k_tie);
+  // kept before this wave: every above-cutoff score, and this direction's
+  // share of the first k_tie ties
+  int base = gt_before + (int)(min(ties_seen, k_tie) - kept_off);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int cs = w0; cs < w1; cs += 64) {
     const int i = cs + lane;
@@ -709,14 +745,15 @@ static void launch_combine(IndexArgs a, const float* in, int n, int64_t tstride,
                      dim3(COMB_THREADS), 0, stream, a);
 }
 
-int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
-                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, int budget,
+                        float top_p, int k_vert, int k_slash, int32_t* vert_idx, int32_t* vert_cnt,
+                        int32_t* slash_idx, int32_t* slash_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (ws_bytes < select_workspace_bytes(Hq, n_global)) return VS_ERR_WORKSPACE;
   SelectArgs s;
   s.vert = vert_score; s.slash = slash_score; s.vert_idx = vert_idx; s.vert_cnt = vert_cnt;
   s.slash_idx = slash_idx; s.slash_cnt = slash_cnt; s.n_vert = n_global; s.n_slash = (int)(n_global / BLK);
   s.top_p = top_p;
+  s.budget = budget; s.k_vert = k_vert; s.k_slash = k_slash;
   s.max_chunks = (int)((n_global + SEL_CHUNK - 1) / SEL_CHUNK);
   char* w = (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   s.hist = (unsigned long long*)w;
@@ -746,8 +783,8 @@ int launch_index_build(int dtype, int D, TView q_last, int Hq, int last_q, TView
   launch_combine(a, a.part, a.nsplit, a.nsplit, 1, nullptr, stream);
   launch_colsum(dtype, D, a, stream);
   const size_t off = index_pass_bytes(Hq, Hkv, lay.n_global);
-  return launch_index_select(vert_score, slash_score, Hq, lay.n_global, top_p, vert_idx, vert_cnt, slash_idx,
-                             slash_cnt, (char*)ws + off, ws_bytes - off, stream);
+  return launch_index_select(vert_score, slash_score, Hq, lay.n_global, BUDGET_TOP_P, top_p, 0, 0, vert_idx, vert_cnt,
+                             slash_idx, slash_cnt, (char*)ws + off, ws_bytes - off, stream);
 }
 
 int launch_index_rank_stats(int dtype, int D, TView q_last, int Hq, int last_q, TView k_local, int Hkv,

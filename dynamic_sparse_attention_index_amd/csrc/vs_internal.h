@@ -48,8 +48,9 @@ int launch_index_rank_mass(int dtype, int D, TView q_last, int Hq, int last_q, T
 
 size_t select_workspace_bytes(int Hq, int64_t n_global);
 
-int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
-                        int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt, void* ws,
-                        size_t ws_bytes, hipStream_t stream);
+// budget: VS_BUDGET_TOP_P / VS_BUDGET_TOP_K / VS_BUDGET_JOINT_TOP_P (0 / 1 / 2)
+int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, int budget,
+                        float top_p, int k_vert, int k_slash, int32_t* vert_idx, int32_t* vert_cnt,
+                        int32_t* slash_idx, int32_t* slash_cnt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace vs

@@ -30,6 +30,7 @@
  *     status word that the caller reads after synchronising the stream.
  *   - A token position is "global" when it indexes the whole sequence and
  *     "local" when it indexes one rank's shard in storage order.
+ *   - Every `scale` argument must be finite and positive, else VS_ERR_ARG.
  *   - Attention uses natural-log LSE, logits q.k * scale (scale = 1/sqrt(D)),
  *     query head h reads kv head h / (Hq / Hkv). Empty rows give O = 0 and
  *     LSE = -inf and contribute no gradient.
@@ -204,11 +205,38 @@ size_t vs_index_select_workspace_size(int Hq, int64_t n_global);
  * (vert_score [Hq, n_global], slash_score [Hq, n_global / 64], non-negative
  * fp32); outputs as for vs_index_build; ws: caller-owned scratch of
  * vs_index_select_workspace_size bytes (contents need no initialisation).
- * VS_ERR_ARG for null pointers or Hq <= 0; VS_ERR_UNSUPPORTED if n_global is
- * not a multiple of 64; VS_ERR_WORKSPACE if ws_bytes is too small. */
+ * VS_ERR_ARG for null pointers, Hq <= 0 or a NaN top_p; VS_ERR_UNSUPPORTED if
+ * n_global is not a multiple of 64; VS_ERR_WORKSPACE if ws_bytes is too
+ * small. */
 int vs_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, float top_p,
                     int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* Budget kinds of vs_index_select_budget. */
+#define VS_BUDGET_TOP_P 0        /* separate top-p on v and on s (vs_index_select) */
+#define VS_BUDGET_TOP_K 1        /* a fixed count per head */
+#define VS_BUDGET_JOINT_TOP_P 2  /* one top-p over the pooled v and s candidates */
+
+/* vs_index_select_budget: vs_index_select with a choice of budget rule, on
+ * the same scores, outputs, workspace and errors (VS_ERR_ARG also for an
+ * unknown `budget`).
+ *   VS_BUDGET_TOP_P: as vs_index_select; k_vert, k_slash unused.
+ *   VS_BUDGET_TOP_K: a fixed count, the form of the budget behind the review's
+ *     hand-fixed 95% sparsity (page 1, section 八 item 4): per head the
+ *     min(k_vert, n_global) largest vertical scores and the
+ *     min(k_slash, n_global / 64) largest slash scores, ties to the lower
+ *     index; a count <= 0 keeps none of that direction. top_p unused.
+ *   VS_BUDGET_JOINT_TOP_P: the fewest verticals plus slashes of section 三.2
+ *     item 1 read as one count: per head the n_global verticals followed by
+ *     the n_global / 64 slashes form one candidate list, and the fewest in
+ *     descending score order (ties: verticals first, then the lower index)
+ *     whose fixed-point mass reaches ceil(round(p * 2^32) * total / 2^32) of
+ *     the pooled total are kept (p >= 1: all, p <= 0: none). k_vert, k_slash
+ *     unused.
+ * Each output list is ascending, with its count in vert_cnt / slash_cnt. */
+int vs_index_select_budget(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, int budget,
+                           float top_p, int k_vert, int k_slash, int32_t* vert_idx, int32_t* vert_cnt,
+                           int32_t* slash_idx, int32_t* slash_cnt, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- 2. active region ------------------------------------------------- */
 

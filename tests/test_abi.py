@@ -134,6 +134,8 @@ def test_rank_index_validation(L):
     assert L.vs_index_rank_stats(q, k_global, lay, 0, 0.1, p, p, ws, None) == vs.VS_ERR_ARG
     assert L.vs_index_rank_mass(q, k_local, lay, 1, 0.1, None, p, p, p, ws, None) == vs.VS_ERR_ARG
     assert L.vs_index_rank_mass(q, k_local, lay, 1, 0.0, p, p, p, p, ws, None) == vs.VS_ERR_ARG  # scale
+    for bad in (float("nan"), float("inf"), -0.5):
+        assert L.vs_index_rank_mass(q, k_local, lay, 1, bad, p, p, p, p, ws, None) == vs.VS_ERR_ARG
     sws = L.vs_index_select_workspace_size(16, 4096)
     assert sws > 0 and L.vs_index_select_workspace_size(0, 4096) == 0
     assert L.vs_index_select(p, p, 16, 4096, 0.9, p, p, p, None, p, sws, None) == vs.VS_ERR_ARG
@@ -141,6 +143,13 @@ def test_rank_index_validation(L):
     assert L.vs_index_select(p, p, 16, 4096, 0.9, p, p, p, p, None, sws, None) == vs.VS_ERR_ARG
     assert L.vs_index_select(p, p, 16, 4000, 0.9, p, p, p, p, p, sws, None) == vs.VS_ERR_UNSUPPORTED
     assert L.vs_index_select(p, p, 16, 4096, 0.9, p, p, p, p, p, sws - 1, None) == vs.VS_ERR_WORKSPACE
+    B = L.vs_index_select_budget
+    assert B(p, p, 16, 4096, 3, 0.9, 1, 1, p, p, p, p, p, sws, None) == vs.VS_ERR_ARG            # unknown budget
+    assert B(p, p, 16, 4096, -1, 0.9, 1, 1, p, p, p, p, p, sws, None) == vs.VS_ERR_ARG
+    assert B(p, p, 16, 4096, vs.VS_BUDGET_TOP_K, 0.9, 8, 8, p, None, p, p, p, sws, None) == vs.VS_ERR_ARG
+    assert B(p, p, 16, 4000, vs.VS_BUDGET_TOP_K, 0.9, 8, 8, p, p, p, p, p, sws, None) == vs.VS_ERR_UNSUPPORTED
+    assert B(p, p, 16, 4096, vs.VS_BUDGET_JOINT_TOP_P, float("nan"), 0, 0, p, p, p, p, p, sws, None) == vs.VS_ERR_ARG
+    assert B(p, p, 16, 4096, vs.VS_BUDGET_JOINT_TOP_P, 0.9, 0, 0, p, p, p, p, p, sws - 1, None) == vs.VS_ERR_WORKSPACE
 
 
 def test_bwd_and_merge_validation(L):

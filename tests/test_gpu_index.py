@@ -118,3 +118,93 @@ def test_index_distributed_ranks(kind, P, dtype_cfg):
     one = H.gpu_index(q_last, H.to_dev(H.storage_order(t["k"], kind, P), cfg.dtype), lay, cfg.scale, cfg.top_p)
     for a, b in ((v, one["v"]), (s, one["s"])):
         assert torch.allclose(a, b, rtol=1e-5, atol=1e-9), (a - b).abs().max().item()
+
+
+def _budget_scores(rng, Hq, N, ties):
+    """Seeded score rows shaped like the index's: a heavy-tailed vertical row
+    normalised to one, the slash row its 64-wide tile sums (fp32). With
+    `ties`, the values are rounded to multiples of 2^-22 so that many are
+    equal, zeros included."""
+    v = rng.random((Hq, N)) ** 12
+    v[:, rng.choice(N, 40, replace=False)] += 0.02
+    v /= v.sum(axis=1, keepdims=True)
+    if ties:
+        v = np.round(v * 2.0 ** 22) / 2.0 ** 22
+    s = v.reshape(Hq, N // 64, 64).sum(axis=2)[:, ::-1].copy()   # diagonal j = key tile T-1-j
+    return v.astype(np.float32), s.astype(np.float32)
+
+
+def _run_budget(v, s, budget, p, kv, ks):
+    import torch
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    Hq, N = v.shape
+    dv, ds = torch.tensor(v, device="cuda"), torch.tensor(s, device="cuda")
+    out = {"vidx": torch.full((Hq, N), -7, dtype=torch.int32, device="cuda"),
+           "vcnt": torch.full((Hq,), -7, dtype=torch.int32, device="cuda"),
+           "sidx": torch.full((Hq, N // 64), -7, dtype=torch.int32, device="cuda"),
+           "scnt": torch.full((Hq,), -7, dtype=torch.int32, device="cuda")}
+    ws = torch.full((vs.index_select_workspace_size(Hq, N),), 0xAB, dtype=torch.uint8, device="cuda")
+    vs.vs_index_select_budget(dv, ds, Hq, N, budget, p, kv, ks, out["vidx"], out["vcnt"], out["sidx"], out["scnt"],
+                              ws)
+    torch.cuda.synchronize()
+    return H.lists_from_gpu(out)
+
+
+@pytest.mark.parametrize("N,ties", [(32768, True), (131072, False), (4096, True)])
+def test_select_budget_top_k(N, ties):
+    """Fixed-count budget: bit-exact index lists against the oracle for counts
+    from none to more than every element."""
+    import dynamic_sparse_attention_index_amd as vs
+    rng = np.random.default_rng(N + ties)
+    Hq, T = 4, N // 64
+    v, s = _budget_scores(rng, Hq, N, ties)
+    for kv, ks in ((0, 0), (1, 1), (257, 7), (N // 20, T // 20), (N - 1, T - 1), (N, T), (N + 5, T + 9), (-3, 5)):
+        gv, gs = _run_budget(v, s, vs.VS_BUDGET_TOP_K, 0.0, kv, ks)
+        for h in range(Hq):
+            assert np.array_equal(gv[h], oi.select_top_k(v[h], kv)), (kv, h)
+            assert np.array_equal(gs[h], oi.select_top_k(s[h], ks)), (ks, h)
+
+
+@pytest.mark.parametrize("N,ties", [(32768, True), (131072, False), (4096, True)])
+def test_select_budget_joint(N, ties):
+    """Joint top-p over the pooled vertical and slash candidates: bit-exact
+    against the oracle; the separate top-p through the same entry point equals
+    vs_index_select's rule."""
+    import dynamic_sparse_attention_index_amd as vs
+    rng = np.random.default_rng(7 * N + ties)
+    Hq = 4
+    v, s = _budget_scores(rng, Hq, N, ties)
+    for p in (0.0, 0.05, 0.3, 0.9, 0.95, 0.999, 1.0):
+        gv, gs = _run_budget(v, s, vs.VS_BUDGET_JOINT_TOP_P, p, 0, 0)
+        for h in range(Hq):
+            rv, rs = oi.select_joint_top_p(v[h], s[h], p)
+            assert np.array_equal(gv[h], rv) and np.array_equal(gs[h], rs), (p, h)
+    gv, gs = _run_budget(v, s, vs.VS_BUDGET_TOP_P, 0.95, 0, 0)
+    for h in range(Hq):
+        assert np.array_equal(gv[h], oi.select_top_p(v[h], 0.95))
+        assert np.array_equal(gs[h], oi.select_top_p(s[h], 0.95))
+
+
+def test_select_budget_joint_ties_across_directions():
+    """Ties at the joint cutoff shared by verticals and slashes: the verticals
+    are kept first (in every chunk), then the slashes with the lowest indices."""
+    import dynamic_sparse_attention_index_amd as vs
+    rng = np.random.default_rng(3)
+    Hq, N = 2, 32768
+    T = N // 64
+    x = np.float32(2.0 ** -12)
+    v = np.zeros((Hq, N), dtype=np.float32)
+    s = np.zeros((Hq, T), dtype=np.float32)
+    for h in range(Hq):
+        v[h, rng.choice(N, 100, replace=False)] = x      # spread over every chunk
+        s[h, rng.choice(T, 50, replace=False)] = x
+        s[h, rng.choice(T, 3, replace=False)] = 4 * x     # above the cutoff
+    for p in (0.5, 0.8, 0.9, 0.97):
+        gv, gs = _run_budget(v, s, vs.VS_BUDGET_JOINT_TOP_P, p, 0, 0)
+        for h in range(Hq):
+            rv, rs = oi.select_joint_top_p(v[h], s[h], p)
+            assert np.array_equal(gv[h], rv) and np.array_equal(gs[h], rs), (p, h)
+    # p = 0.8 of 162 x: 3 big slashes (12 x) then 118 ties -> 100 verticals, 18 slashes
+    rv, rs = oi.select_joint_top_p(v[0], s[0], 0.8)
+    assert len(rv) == 100 and len(rs) == 3 + 18
