@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen128k")
     ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--operands", choices=("f16", "bf16"), default="f16",
+                    help="attention operand format for bf16 workloads: exact fp16 copies (converted inside the "
+                         "timed step, single fp16 P/dS) or the bf16 inputs (hi + lo bf16 P/dS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-budgets", action="store_true", help="skip the budget-rule report (after the timed steps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -109,7 +112,17 @@ def main():
     dv = torch.empty(Hkv, N, D, device=dev)
     stream = torch.cuda.current_stream()
 
-    stages = ("index", "mask", "fwd", "bwd_prep", "dq", "dkdv", "dkdv_vert")
+    # fp16 operands: exact copies of the bf16 inputs, made inside every timed
+    # step (q, k, v before the forward; dO before the backward)
+    f16 = args.operands == "f16" and cfg.dtype == "bf16" and D == 128
+    conv_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    if f16:
+        q16, k16, v16, do16 = (torch.empty(x.shape, dtype=torch.float16, device=dev) for x in (q, k, v, do))
+        aq, ak, av, ado = q16, k16, v16, do16
+    else:
+        aq, ak, av, ado = q, k, v, do
+
+    stages = ("index", "mask", "convert_qkv", "fwd", "convert_do", "bwd_prep", "dq", "dkdv", "dkdv_vert")
     ev = {name: [] for name in stages}
 
     def step(record):
@@ -123,23 +136,31 @@ def main():
         mark(1)
         vs.vs_block_mask(vidx, vcnt, sidx, scnt, 0, 0, mask, stream)
         mark(2)
-        vs.vs_attn_fwd(q, k, v, mask, cfg.scale, o, lse, 0, stream)
+        if f16:
+            for src, dst in ((q, q16), (k, k16), (v, v16)):
+                vs.vs_convert_f16(src, dst, conv_status, stream)
         mark(3)
+        vs.vs_attn_fwd(aq, ak, av, mask, cfg.scale, o, lse, 0, stream)
+        mark(4)
         if cfg.backward:
-            vs.vs_attn_bwd_prep(o, do, delta, stream)
-            mark(4)
-            # dq and the slash dk/dv write their outputs whole; the vertical part adds after them
-            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv,
-                                 vs.VS_BWD_DQ | vs.VS_BWD_OVERWRITE, stream)
+            if f16:
+                vs.vs_convert_f16(do, do16, conv_status, stream)
             mark(5)
-            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv,
-                                 vs.VS_BWD_DKDV | vs.VS_BWD_OVERWRITE, stream)
+            vs.vs_attn_bwd_prep(o, ado, delta, stream)
             mark(6)
-            vs.vs_attn_bwd_parts(q, k, v, do, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DKDV_VERT, stream)
+            # dq and the slash dk/dv write their outputs whole; the vertical part adds after them
+            vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
+                                 vs.VS_BWD_DQ | vs.VS_BWD_OVERWRITE, stream)
+            mark(7)
+            vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
+                                 vs.VS_BWD_DKDV | vs.VS_BWD_OVERWRITE, stream)
+            mark(8)
+            vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DKDV_VERT,
+                                 stream)
         else:
-            for i in (4, 5, 6):
+            for i in (5, 6, 7, 8):
                 mark(i)
-        mark(7)
+        mark(9)
         if record:
             for i, name in enumerate(stages):
                 ev[name].append((marks[i], marks[i + 1]))
@@ -150,11 +171,15 @@ def main():
     status = int(mask.arrays()["status"].item())
     if status != 0:
         raise RuntimeError(f"mask status {status}")
+    if int(conv_status.item()) != 0:
+        raise RuntimeError("an input is outside the fp16 range: run with --operands bf16")
     t_start = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    if int(conv_status.item()) != 0:
+        raise RuntimeError("fp16 conversion range error in the timed steps")
     ms_per_step = wall * 1e3 / args.steps
     stage_ms = {kname: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for kname, pairs in ev.items()}
 
@@ -170,17 +195,18 @@ def main():
     sparsity = 1.0 - A / total_causal
     eff_flops = (4 + (10 if cfg.backward else 0)) * D * A
     tflops = eff_flops / (ms_per_step * 1e-3) / 1e12
-    attn_ms = sum(stage_ms[x] for x in ("fwd", "bwd_prep", "dq", "dkdv", "dkdv_vert"))
+    attn_ms = sum(stage_ms[x] for x in ("convert_qkv", "fwd", "convert_do", "bwd_prep", "dq", "dkdv", "dkdv_vert"))
     attn_tflops = eff_flops / (attn_ms * 1e-3) / 1e12
 
-    # Roofline of the dominant kernel. Each timed stage below is exactly one
-    # kernel launch. Algorithmic FLOPs per active entry (FlashAttention-2
+    # Roofline of the dominant kernel. Each timed kernel stage below is exactly
+    # one kernel launch (convert_qkv is three). Algorithmic FLOPs per active entry (FlashAttention-2
     # convention, 14 d in total): forward 4 d; dK/dV kernels 8 d (recompute S,
     # dP, dV, dK) over their entries; dQ kernel 2 d.
     peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     if cfg.dtype == "bf16" and D == 128:
-        kn = {"fwd": "attn_fwd_bf16_d128_kernel", "dq": "dq_bf16_d128_kernel",
-              "dkdv": "dkdv_bf16_d128_kernel", "dkdv_vert": "dkdv_vert_bf16_d128_kernel"}
+        op = "f16" if f16 else "bf16"
+        kn = {"fwd": f"attn_fwd_{op}_d128_kernel", "dq": f"dq_{op}_d128_kernel",
+              "dkdv": f"dkdv_{op}_d128_kernel", "dkdv_vert": f"dkdv_vert_{op}_d128_kernel"}
     else:
         tn = "bf16" if cfg.dtype == "bf16" else "float"
         kn = {"fwd": f"attn_fwd_kernel<{tn}, {D}>", "dq": f"dq_kernel<{tn}, {D}>",
@@ -225,7 +251,10 @@ def main():
     line = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "vs_baseline": None, "dtype": "f16" if f16 else cfg.dtype, "data": "synthetic",
+        "inputs": cfg.dtype,
+        "operands": ("fp16 copies of the bf16 inputs (exact; converted inside the step), single fp16 P/dS, "
+                     "fp32 accumulation") if f16 else f"{cfg.dtype} inputs as given",
         "config": {"workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "seq_len": N, "head_dim": D,
                    "top_p": cfg.top_p, "last_q": cfg.last_q, "backward": cfg.backward, "mean_c": cfg.c,
                    "seed": cfg.seed},
@@ -306,7 +335,11 @@ def ring_report(args, cfg):
     the merge fused into its epilogue, and after the forward of all steps the
     backward of every step. Each (r, s) kernel group is timed alone with HIP
     events on the launch stream; reported times are medians over repetitions.
-    Communication between ranks is not part of it (one GPU).
+    Communication between ranks is not part of it (one GPU). With fp16
+    operands every rank's q, k, v, dO shard is converted once before its ring
+    (the shard a rank sends round the ring is then already fp16); that
+    one-time conversion is timed over all shards at once and reported per
+    rank (total / P) beside the steps.
     """
     import torch
     import dynamic_sparse_attention_index_amd as vs
@@ -332,6 +365,7 @@ def ring_report(args, cfg):
     out = {"metric": f"ring simulation: one rank's sparse fwd+bwd ring steps, {N} tokens at P={P}, 1 MI355X",
            "unit": "ms", "workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "seq_len": N, "P": P, "head_dim": D,
            "dtype": cfg.dtype, "data": "synthetic", "reps": args.ring_reps, "gen_s": round(gen_s, 1),
+           "operands": args.operands if cfg.dtype == "bf16" and D == 128 else cfg.dtype,
            "communication": "excluded (one GPU; every rank's steps run in turn)", "layouts": {}}
     for kind in args.layouts.split(","):
         perm = np.concatenate([layout_permutation(kind, N, P, r) for r in range(P)])
@@ -340,6 +374,23 @@ def ring_report(args, cfg):
         v = torch.tensor(host["v"][:, perm]).to(dev, tdt)
         do = torch.tensor(host["do"][:, perm]).to(dev, tdt)
         lay = vs.layout(kind, P, N)
+        f16 = args.operands == "f16" and cfg.dtype == "bf16" and D == 128
+        t_conv = None
+        if f16:
+            conv_status = torch.zeros(1, dtype=torch.int32, device=dev)
+            aq, ak, av, ado = (torch.empty(x.shape, dtype=torch.float16, device=dev) for x in (q, k, v, do))
+            # all P shards at once (bandwidth-bound, linear in size): per rank = total / P
+            t_conv = []
+            for rep in range(-1, args.ring_reps):
+                e = timed(lambda: [vs.vs_convert_f16(x, y, conv_status, stream)
+                                   for x, y in ((q, aq), (k, ak), (v, av), (do, ado))])
+                torch.cuda.synchronize()
+                if rep >= 0:
+                    t_conv.append(e[0].elapsed_time(e[1]) / P)
+            if int(conv_status.item()) != 0:
+                raise RuntimeError("an input is outside the fp16 range: run with --operands bf16")
+        else:
+            aq, ak, av, ado = q, k, v, do
         # global index over the storage-order keys; the last rows are global
         # rows N - last_q .. N - 1, wherever they are stored
         last_rows = np.nonzero(np.isin(perm, np.arange(N - cfg.last_q, N)))[0]
@@ -407,7 +458,7 @@ def ring_report(args, cfg):
             dv.zero_()
             for r in range(P):
                 rows = slice(r * QB * 64, (r + 1) * QB * 64)
-                qr, dor = q[:, rows], do[:, rows]
+                qr, dor = aq[:, rows], ado[:, rows]
                 o.zero_()
                 lse.fill_(-math.inf)
                 dq.zero_()
@@ -417,7 +468,7 @@ def ring_report(args, cfg):
                     cols = slice(src * QB * 64, (src + 1) * QB * 64)
                     m = vs.Mask(Hq, Hkv, lay, cap)
                     e_m = timed(lambda: vs.vs_block_mask(vidx, vcnt, sidx, scnt, r, st, m, stream))
-                    e_f = timed(lambda: vs.vs_attn_fwd(qr, k[:, cols], v[:, cols], m, cfg.scale, o, lse, 1, stream))
+                    e_f = timed(lambda: vs.vs_attn_fwd(qr, ak[:, cols], av[:, cols], m, cfg.scale, o, lse, 1, stream))
                     masks.append(m)
                     evs.append((e_m, e_f))
                 vs.vs_attn_bwd_prep(o, dor, delta, stream)
@@ -425,7 +476,7 @@ def ring_report(args, cfg):
                 for st in range(P):
                     src = (r - st) % P
                     cols = slice(src * QB * 64, (src + 1) * QB * 64)
-                    ebs.append(timed(lambda: vs.vs_attn_bwd(qr, k[:, cols], v[:, cols], dor, lse, delta, masks[st],
+                    ebs.append(timed(lambda: vs.vs_attn_bwd(qr, ak[:, cols], av[:, cols], dor, lse, delta, masks[st],
                                                             cfg.scale, dq, dk[src], dv[src], stream)))
                 torch.cuda.synchronize()
                 if rep >= 0:
@@ -453,14 +504,14 @@ def ring_report(args, cfg):
         l_step = torch.empty_like(lse)
         fused, split = [], []
         r = 0
-        qr = q[:, 0:QB * 64]
+        qr = aq[:, 0:QB * 64]
         for st in range(P):
             src = (r - st) % P
             cols = slice(src * QB * 64, (src + 1) * QB * 64)
             m = vs.Mask(Hq, Hkv, lay, cap)
             vs.vs_block_mask(vidx, vcnt, sidx, scnt, r, st, m, stream)
-            ef = timed(lambda: vs.vs_attn_fwd(qr, k[:, cols], v[:, cols], m, cfg.scale, o, lse, 1, stream))
-            es1 = timed(lambda: vs.vs_attn_fwd(qr, k[:, cols], v[:, cols], m, cfg.scale, o_step, l_step, 0, stream))
+            ef = timed(lambda: vs.vs_attn_fwd(qr, ak[:, cols], av[:, cols], m, cfg.scale, o, lse, 1, stream))
+            es1 = timed(lambda: vs.vs_attn_fwd(qr, ak[:, cols], av[:, cols], m, cfg.scale, o_step, l_step, 0, stream))
             es2 = timed(lambda: vs.vs_merge_lse(o, lse, o_step, l_step, stream))
             torch.cuda.synchronize()
             fused.append(ef[0].elapsed_time(ef[1]))
@@ -468,6 +519,7 @@ def ring_report(args, cfg):
             del m
         out["layouts"][kind] = {
             "index_ms": round(float(np.median(t_index)), 4),
+            "convert_f16_ms_per_rank": round(float(np.median(t_conv)), 4) if t_conv else None,
             "index_distributed_pass1_ms_max_rank": round(float(np.median(t_d1)), 4),
             "index_distributed_pass2_ms_max_rank": round(float(np.median(t_d2)), 4),
             "index_distributed_select_ms": round(float(np.median(t_d3)), 4),
@@ -490,7 +542,7 @@ def ring_report(args, cfg):
             "merge_fused_ms_per_step": round(float(np.mean(fused)), 4),
             "merge_separate_ms_per_step": round(float(np.mean(split)), 4),
         }
-        del q, k, v, do, dk, dv
+        del q, k, v, do, dk, dv, aq, ak, av, ado
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
     if args.report_md:

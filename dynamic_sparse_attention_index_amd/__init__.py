@@ -7,7 +7,7 @@ raises; there is no fallback implementation.
 
 Entry points (same names and meaning as the C ABI):
     vs_index_build, vs_block_mask, vs_attn_fwd, vs_merge_lse,
-    vs_attn_bwd_prep, vs_attn_bwd
+    vs_attn_bwd_prep, vs_attn_bwd, vs_convert_f16
 plus helpers to size workspaces and hold a mask buffer (``Mask``).
 """
 import ctypes
@@ -20,7 +20,8 @@ from . import _build
 LIB_PATH = _build.LIB
 
 VS_OK, VS_ERR_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_CAPACITY, VS_ERR_HIP = 0, -1, -2, -3, -4, -5
-VS_F32, VS_BF16 = 0, 1
+VS_ERR_RANGE = -6
+VS_F32, VS_BF16, VS_F16 = 0, 1, 2
 LAYOUTS = {"contig": 0, "striped": 1, "zigzag": 2}
 TILE_DIAG = 0x40000000
 TILE_MASK = 0x3FFFFFFF
@@ -29,6 +30,7 @@ EXPORTED = [
     "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_index_rank_stats", "vs_index_rank_mass",
     "vs_index_select_workspace_size", "vs_index_select", "vs_index_select_budget", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
+    "vs_convert_f16",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
 
@@ -100,6 +102,8 @@ def lib():
         L.vs_attn_fwd.argtypes = [VsTensor, VsTensor, VsTensor, ctypes.POINTER(VsMask), f32, vp, vp, i32, vp]
         L.vs_merge_lse.restype = i32
         L.vs_merge_lse.argtypes = [vp, vp, vp, vp, i32, i64, i32, vp]
+        L.vs_convert_f16.restype = i32
+        L.vs_convert_f16.argtypes = [vp, vp, i64, vp, vp]
         L.vs_attn_bwd_prep.restype = i32
         L.vs_attn_bwd_prep.argtypes = [vp, VsTensor, vp, vp]
         L.vs_attn_bwd.restype = i32
@@ -148,6 +152,8 @@ def as_vs_tensor(t: torch.Tensor) -> VsTensor:
         raise ValueError("expected a [H, N, D] tensor with contiguous D")
     if t.dtype == torch.bfloat16:
         dt = VS_BF16
+    elif t.dtype == torch.float16:
+        dt = VS_F16
     elif t.dtype == torch.float32:
         dt = VS_F32
     else:
@@ -260,6 +266,18 @@ def vs_merge_lse(o_acc, lse_acc, o_step, lse_step, stream=None):
     Hq, Nq, D = o_acc.shape
     _check(lib().vs_merge_lse(_cptr(o_acc), _cptr(lse_acc), _cptr(o_step), _cptr(lse_step), Hq, Nq, D,
                               _stream(stream)), "vs_merge_lse")
+
+
+def vs_convert_f16(src, dst, status, stream=None):
+    """dst (float16) = exact fp16 copy of src (bfloat16), both dense with the
+    same number of elements; status: one int32 device word the caller set to
+    VS_OK, which receives VS_ERR_RANGE if a value is outside fp16's range."""
+    if src.dtype != torch.bfloat16 or dst.dtype != torch.float16 or status.dtype != torch.int32:
+        raise ValueError("vs_convert_f16 takes bfloat16 src, float16 dst and an int32 status word")
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst differ in size")
+    _check(lib().vs_convert_f16(_cptr(src), _cptr(dst), src.numel(), _cptr(status), _stream(stream)),
+           "vs_convert_f16")
 
 
 def vs_attn_bwd_prep(o, dout, delta, stream=None):

@@ -17,12 +17,12 @@ uint32_t float_bits(float x) { uint32_t b; memcpy(&b, &x, 4); return b; }
 bool is_nan(float x) { return (float_bits(x) & 0x7FFFFFFFu) > 0x7F800000u; }
 bool finite_positive(float x) { const uint32_t b = float_bits(x); return b > 0u && b < 0x7F800000u; }
 
-int elem_bytes(int dtype) { return dtype == VS_BF16 ? 2 : 4; }
+int elem_bytes(int dtype) { return dtype == VS_F32 ? 4 : 2; }
 
 // Checks every property the kernels rely on for a [H, N, D] view.
 int check_tensor(const vs_tensor& t, int H, int64_t N, int D) {
   if (!t.ptr) return VS_ERR_ARG;
-  if (t.dtype != VS_F32 && t.dtype != VS_BF16) return VS_ERR_ARG;
+  if (t.dtype != VS_F32 && t.dtype != VS_BF16 && t.dtype != VS_F16) return VS_ERR_ARG;
   if (t.H != H || t.N != N || t.D != D) return VS_ERR_ARG;
   if (t.stride_n < D || t.stride_h < 0) return VS_ERR_ARG;
   const int eb = elem_bytes(t.dtype);
@@ -39,8 +39,13 @@ int check_layout(const vs_layout& lay) {
   return VS_OK;
 }
 
+// index kernels: bf16 (D 64, 128) and f32 (D 64)
 bool supported_dtype_dim(int dtype, int D) {
   return (dtype == VS_BF16 && (D == 64 || D == 128)) || (dtype == VS_F32 && D == 64);
+}
+// attention kernels: also fp16 at D = 128
+bool supported_attn_dtype_dim(int dtype, int D) {
+  return supported_dtype_dim(dtype, D) || (dtype == VS_F16 && D == 128);
 }
 
 TView view(const vs_tensor& t) { return TView{t.ptr, t.stride_h, t.stride_n}; }
@@ -87,6 +92,7 @@ const char* vs_status_string(int s) {
     case VS_ERR_WORKSPACE: return "workspace or buffer too small";
     case VS_ERR_CAPACITY: return "tile list capacity exceeded";
     case VS_ERR_HIP: return "HIP runtime error";
+    case VS_ERR_RANGE: return "value outside the range of the target type";
     default: return "unknown status";
   }
 }
@@ -242,7 +248,7 @@ static int check_attn(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v
   if ((st = check_tensor(k, m->Hkv, Nk, D)) != VS_OK) return st;
   if ((st = check_tensor(v, m->Hkv, Nk, D)) != VS_OK) return st;
   if (q.dtype != k.dtype || q.dtype != v.dtype) return VS_ERR_ARG;
-  if (!supported_dtype_dim(q.dtype, D)) return VS_ERR_UNSUPPORTED;
+  if (!supported_attn_dtype_dim(q.dtype, D)) return VS_ERR_UNSUPPORTED;
   return VS_OK;
 }
 
@@ -266,11 +272,18 @@ int vs_merge_lse(float* o_acc, float* lse_acc, const float* o_step, const float*
   return launch_merge(o_acc, lse_acc, o_step, lse_step, Hq, Nq, D, (hipStream_t)stream);
 }
 
+int vs_convert_f16(const void* src, void* dst, int64_t n, int32_t* status, void* stream) {
+  if (!src || !dst || !status || n < 0) return VS_ERR_ARG;
+  if (!aligned16(src) || !aligned16(dst) || n % 8) return VS_ERR_UNSUPPORTED;
+  if (n == 0) return VS_OK;
+  return launch_convert_f16(src, dst, n, status, (hipStream_t)stream);
+}
+
 int vs_attn_bwd_prep(const float* o, vs_tensor dout, float* delta, void* stream) {
   if (!o || !delta || !dout.ptr) return VS_ERR_ARG;
   int st;
   if ((st = check_tensor(dout, dout.H, dout.N, dout.D)) != VS_OK) return st;
-  if (dout.D != 64 && dout.D != 128) return VS_ERR_UNSUPPORTED;
+  if (!supported_attn_dtype_dim(dout.dtype, dout.D)) return VS_ERR_UNSUPPORTED;
   if (!aligned16(o)) return VS_ERR_UNSUPPORTED;
   if (dout.H <= 0 || dout.N <= 0) return VS_ERR_ARG;
   return launch_bwd_prep(o, dout.dtype, view(dout), dout.H, dout.N, dout.D, delta, (hipStream_t)stream);

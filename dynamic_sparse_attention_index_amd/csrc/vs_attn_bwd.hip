@@ -427,11 +427,12 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 // query blocks and 64-key tiles staged in swizzled LDS tiles by asynchronous
 // copies, two stages, one barrier per tile; each wave covers 32 rows x 32 keys.
 
-// Split 8 fp32 weights into a bf16 hi/lo pair of MFMA operands.
 
 // dQ, query-major. Wave (rh, kh) = rows 32 rh.. of the block, keys 32 kh.. of
 // every tile; the two key halves' partial dQ are added through LDS at the end.
-__global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a) {
+// F16: fp16 inputs, dS as one fp16 operand (one MFMA per product).
+template <bool F16>
+__device__ __forceinline__ void dq_d128(const BwdArgs& a) {
   constexpr int D = TD;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
@@ -533,8 +534,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
         const bf16x8 vf = *(const bf16x8*)(Vs + tile_off(kr, 4 * ks + g4));
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
-          s[rs][t] = mfma_bf16(kf, qf[rs][ks], s[rs][t]);
-          dp[rs][t] = mfma_bf16(vf, df[rs][ks], dp[rs][t]);
+          s[rs][t] = mma16<F16>(kf, qf[rs][ks], s[rs][t]);
+          dp[rs][t] = mma16<F16>(vf, df[rs][ks], dp[rs][t]);
         }
       }
     }
@@ -560,7 +561,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs]));
           s[rs][t][i] = p * (dp[rs][t][i] - dl[rs]);
         }
-      split8(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
+      weights8<F16>(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
     }
     // dQ^T += K^T dS^T over this wave's 32 keys; the transposed K operand of
     // block dt + 1 is read after the first MFMA of block dt
@@ -577,16 +578,17 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
       const int b = dt & 1;
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
-        acc[rs][dt] = mfma_bf16(ka[b], dsh[rs], acc[rs][dt]);
-        acc[rs][dt] = mfma_bf16(ka[b], dsl[rs], acc[rs][dt]);
+        acc[rs][dt] = mma16<F16>(ka[b], dsh[rs], acc[rs][dt]);
+        if constexpr (!F16) acc[rs][dt] = mma16<F16>(ka[b], dsl[rs], acc[rs][dt]);
       }
     }
+    constexpr int MPB = F16 ? 2 : 4;   // MFMAs per column block
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
     }
   };
 
@@ -622,6 +624,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a)
     }
   }
 }
+__global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a) { dq_d128<false>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 2) dq_f16_d128_kernel(BwdArgs a) { dq_d128<true>(a); }
 
 
 // The two halves of kv_block, for the software-pipelined dK/dV kernel:
@@ -639,6 +643,7 @@ __device__ __forceinline__ void kv_frag(const bf16* Qs, const bf16* Os, int rh, 
     }
   }
 }
+template <bool F16>
 __device__ __forceinline__ void kv_sdp(const bf16x8 (*qa)[4], const bf16x8 (*oa)[4], const bf16x8 (*kf)[4],
                                        const bf16x8 (*vf)[4], f32x4 (*s)[2], f32x4 (*dp)[2]) {
 #pragma unroll
@@ -649,8 +654,8 @@ __device__ __forceinline__ void kv_sdp(const bf16x8 (*qa)[4], const bf16x8 (*oa)
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        s[kt][t] = mfma_bf16(qa[t][ks], kf[kt][ks], s[kt][t]);
-        dp[kt][t] = mfma_bf16(oa[t][ks], vf[kt][ks], dp[kt][t]);
+        s[kt][t] = mma16<F16>(qa[t][ks], kf[kt][ks], s[kt][t]);
+        dp[kt][t] = mma16<F16>(oa[t][ks], vf[kt][ks], dp[kt][t]);
       }
   }
 }
@@ -681,6 +686,7 @@ __device__ __forceinline__ void kv_rowstats(const float* lsh, const float* dsh_,
 // l2: row LSE in log2 units, +inf for an empty row (kv_rowstats); on the
 // diagonal tile (wave-uniform `diag`) key kt of this lane is active for rows
 // >= thr[kt].
+template <bool F16>
 __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], const f32x4* l2, const f32x4* dd,
                                        int diag, const int* thr, int rh, int g4, float sl2, bf16x8* ph,
                                        bf16x8* pl, bf16x8* dh, bf16x8* dl) {
@@ -705,10 +711,11 @@ __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], cons
         s[kt][t][i] = pr;
         ds[t][i] = pr * (dp[kt][t][i] - dd[t][i]);
       }
-    split8(s[kt][0], s[kt][1], ph[kt], pl[kt]);
-    split8(ds[0], ds[1], dh[kt], dl[kt]);
+    weights8<F16>(s[kt][0], s[kt][1], ph[kt], pl[kt]);
+    weights8<F16>(ds[0], ds[1], dh[kt], dl[kt]);
   }
 }
+template <bool F16>
 __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf16x8* ph, const bf16x8* pl,
                                         const bf16x8* dh, const bf16x8* dl, int rh, int g4, int n16,
                                         f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8]) {
@@ -730,12 +737,13 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
     const int b = dt & 1;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      acc_dv[kt][dt] = mfma_bf16(oT[b], ph[kt], acc_dv[kt][dt]);
-      acc_dv[kt][dt] = mfma_bf16(oT[b], pl[kt], acc_dv[kt][dt]);
-      acc_dk[kt][dt] = mfma_bf16(qT[b], dh[kt], acc_dk[kt][dt]);
-      acc_dk[kt][dt] = mfma_bf16(qT[b], dl[kt], acc_dk[kt][dt]);
+      acc_dv[kt][dt] = mma16<F16>(oT[b], ph[kt], acc_dv[kt][dt]);
+      if constexpr (!F16) acc_dv[kt][dt] = mma16<F16>(oT[b], pl[kt], acc_dv[kt][dt]);
+      acc_dk[kt][dt] = mma16<F16>(qT[b], dh[kt], acc_dk[kt][dt]);
+      if constexpr (!F16) acc_dk[kt][dt] = mma16<F16>(qT[b], dl[kt], acc_dk[kt][dt]);
     }
   }
+  constexpr int MPB = F16 ? 4 : 8;   // MFMAs per column block
   // reads of block dt + 1 go out after the first MFMA of block dt, so the
   // wait in front of that MFMA covers block dt's reads only
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -743,7 +751,7 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
   for (int dt = 0; dt < 8; ++dt) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 7, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
   }
 }
 
@@ -751,6 +759,7 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
 // vertical-column kernel): thr[kt] = rows of the block with offset below it
 // are inactive for key kt of this lane (BLK: the whole block); the LSE is
 // staged in natural-log units.
+template <bool F16>
 __device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const float* lsh, const float* dsh_,
                                          const bf16x8 (*kf)[4], const bf16x8 (*vf)[4], const int* thr,
                                          int rh, int g4, int n16, float sl2, f32x4 (*acc_dk)[8],
@@ -758,14 +767,14 @@ __device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const f
   bf16x8 qa[2][4], oa[2][4];
   kv_frag(Qs, Os, rh, g4, n16, qa, oa);
   f32x4 s[2][2], dp[2][2];
-  kv_sdp(qa, oa, kf, vf, s, dp);
+  kv_sdp<F16>(qa, oa, kf, vf, s, dp);
   f32x4 l2[2], dd[2];
   kv_rowstats<false>(lsh, dsh_, rh, g4, l2, dd);
   // thresholds apply under a wave-uniform branch: most blocks have none
   const int masked = __builtin_amdgcn_ballot_w64(thr[0] != 0 || thr[1] != 0) != 0ull ? 1 : 0;
   bf16x8 ph[2], pl[2], dh[2], dl[2];
-  kv_pds(s, dp, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl);
-  kv_grad(Qs, Os, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
+  kv_pds<F16>(s, dp, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl);
+  kv_grad<F16>(Qs, Os, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
 }
 
 // Copy the Q and dO rows of query block I of head h and its lse/delta.
@@ -844,7 +853,8 @@ __device__ __forceinline__ void kv_finish(float* xbuf_dk, float* xbuf_dv, f32x4 
 // (Q, dO) stages: tile i (gradient products), tile i + 1 (S, dP), tile i + 2
 // (being copied). One workgroup per CU (the accumulators and K/V fragments
 // take more than half the registers), so LDS has room for the third stage.
-__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs a) {
+template <bool F16>
+__device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO2[2 * TILE_ELEMS];
@@ -989,17 +999,18 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
     for (int kt = 0; kt < 2; ++kt) thr[kt] = 32 * kh + 16 * kt + n16;
     __builtin_amdgcn_sched_barrier(0);
     f32x4 s_n[2][2], dp_n[2][2];
-    kv_sdp(qa, oa, kf, vf, s_n, dp_n);
+    kv_sdp<F16>(qa, oa, kf, vf, s_n, dp_n);
     bf16x8 ph[2], pl[2], dh[2], dl[2];
-    kv_pds(s_c, dp_c, l2, dd, diag_i, thr, rh, g4, sl2, ph, pl, dh, dl);
+    kv_pds<F16>(s_c, dp_c, l2, dd, diag_i, thr, rh, g4, sl2, ph, pl, dh, dl);
+    constexpr int VPM = F16 ? 4 : 6;   // vector ops per MFMA (fp16 weights need one convert per pair)
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     const bf16* Qc = QOst.template operator()<p>();
-    kv_grad(Qc, Qc + TILE_ELEMS, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
+    kv_grad<F16>(Qc, Qc + TILE_ELEMS, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -1024,7 +1035,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   {
     bf16x8 qa[2][4], oa[2][4];
     kv_frag(QO0, QO0 + TILE_ELEMS, rh, g4, n16, qa, oa);
-    kv_sdp(qa, oa, kf, vf, s_c, dp_c);
+    kv_sdp<F16>(qa, oa, kf, vf, s_c, dp_c);
   }
   for (int i0 = 0; i0 < total; i0 += 3) {
     step.template operator()<0>(i0);
@@ -1038,6 +1049,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
   kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, false,
             a.overwrite != 0);
 }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs a) { dkdv_d128<false>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_f16_d128_kernel(BwdArgs a) { dkdv_d128<true>(a); }
 
 // dK/dV of vertical columns: work items (head, 64-column chunk of the shard's
 // verticals, range of VERT_SEG query blocks) enumerated from the device-side
@@ -1046,7 +1059,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs 
 // per-key thresholds (causal edge, columns covered by a listed tile).
 // Results are added with fp32 atomics (a column can be a vertical of several
 // q heads of the group).
-__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(BwdArgs a) {
+template <bool F16>
+__device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) float L0[2 * BLK];
@@ -1123,7 +1137,7 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
         thr[kt] = BLK;
         if (valid[kt] && j >= 0 && !((sbits[j >> 5] >> (j & 31)) & 1u)) thr[kt] = (j == 0) ? (m[kt] % BLK) : 0;
       }
-      kv_block(Qs, Os, Ls, Ls + BLK, kf, vf, thr, rh, g4, n16, sl2, acc_dk, acc_dv);
+      kv_block<F16>(Qs, Os, Ls, Ls + BLK, kf, vf, thr, rh, g4, n16, sl2, acc_dk, acc_dv);
     };
     stage_qblock(Q0, O0, L0, a, h, I_lo, wave, lane, dlane);
     for (int it = 0; it < total; it += 2) {
@@ -1136,6 +1150,8 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(Bwd
     kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, true, false);
   }
 }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(BwdArgs a) { dkdv_vert_d128<false>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_f16_d128_kernel(BwdArgs a) { dkdv_vert_d128<true>(a); }
 
 // ---------------------------------------------------------------------------
 // delta[row] = dO[row] . O[row]; D/4 threads per row.
@@ -1164,7 +1180,10 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
   const int64_t n = rows * (D / 4);
   const int tpb = 256;
   const dim3 grid((unsigned)((n + tpb - 1) / tpb));
-  if (dtype == VS_BF16)
+  if (dtype == VS_F16)
+    hipLaunchKernelGGL(bwd_prep_kernel<_Float16>, grid, dim3(tpb), 0, stream, o, (const _Float16*)dout.ptr, dout.sh,
+                       dout.sn, Nq, rows, D, delta);
+  else if (dtype == VS_BF16)
     hipLaunchKernelGGL(bwd_prep_kernel<bf16>, grid, dim3(tpb), 0, stream, o, (const bf16*)dout.ptr, dout.sh, dout.sn,
                        Nq, rows, D, delta);
   else
@@ -1212,7 +1231,8 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src;
   a.scale = scale; a.scale_log2 = scale * LOG2E;
   a.overwrite = 0;
-  if (dtype == VS_BF16 && D == 128) {
+  if ((dtype == VS_BF16 || dtype == VS_F16) && D == 128) {
+    const bool f16 = dtype == VS_F16;
     a.overwrite = (parts & VS_BWD_OVERWRITE) ? 1 : 0;
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     const int64_t krows = (int64_t)m->KB * BLK, qrows = (int64_t)m->QB * BLK;
@@ -1220,12 +1240,14 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
         !dma_offsets_fit(qrows, dout.sn))
       return VS_ERR_UNSUPPORTED;
     if (a.Hq / a.Hkv > 8) return VS_ERR_UNSUPPORTED;
+    const dim3 qgrid(xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv)), kgrid(xcd_group_grid(a.Hkv, a.KB, KMAJOR_BPC, 1));
     if (parts & VS_BWD_DQ)
-      hipLaunchKernelGGL(dq_bf16_d128_kernel, dim3(xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv)), dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(f16 ? dq_f16_d128_kernel : dq_bf16_d128_kernel, qgrid, dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV)
-      hipLaunchKernelGGL(dkdv_bf16_d128_kernel, dim3(xcd_group_grid(a.Hkv, a.KB, KMAJOR_BPC, 1)), dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(f16 ? dkdv_f16_d128_kernel : dkdv_bf16_d128_kernel, kgrid, dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV_VERT)
-      hipLaunchKernelGGL(dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(f16 ? dkdv_vert_f16_d128_kernel : dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID),
+                         dim3(BWD_THREADS), 0, stream, a);
   }
   else if (dtype == VS_BF16 && D == 64) launch_bwd_typed<bf16, 64>(a, parts, stream);
   else if (dtype == VS_F32 && D == 64) launch_bwd_typed<float, 64>(a, parts, stream);

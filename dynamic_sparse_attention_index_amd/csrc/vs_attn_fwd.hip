@@ -286,7 +286,11 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 // two workgroups per CU). Descriptors (list entries or gathered vertical
 // rows) arrive one step before the K copy that needs them; what the V copy
 // needs (the same descriptor, read again) stays in LDS in between.
-__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
+//
+// F16: the inputs are fp16 (exact copies of bf16 data, see vs_convert_f16)
+// and P is one fp16 operand, so P.V takes one MFMA instead of the hi + lo pair.
+template <bool F16>
+__device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   constexpr int D = TD;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
@@ -397,7 +401,7 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 kf = *(const bf16x8*)(Ks + tile_off(kr, 4 * ks + g4));
 #pragma unroll
-        for (int rs = 0; rs < 2; ++rs) s[rs][t] = mfma_bf16(kf, qf[rs][ks], s[rs][t]);
+        for (int rs = 0; rs < 2; ++rs) s[rs][t] = mma16<F16>(kf, qf[rs][ks], s[rs][t]);
       }
     }
   };
@@ -417,7 +421,8 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
             if (th > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
         }
     }
-    // P as a hi + lo bf16 pair (two MFMAs per product): with bf16 P alone the
+    // P as a hi + lo bf16 pair (two MFMAs per product), or one fp16 operand
+    // (F16; 8x finer rounding than bf16): with bf16 P alone the
     // O error (a few 1e-3) passes into delta = rowsum(dO * O) and from there,
     // scaled by large outlier keys, into dQ beyond the 2e-2 bound
     bf16x8 pf[2], pl[2];
@@ -458,7 +463,7 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
           pr[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -m_use[rs]));
           psum += pr[t][i];
         }
-      split8(pr[0], pr[1], pf[rs], pl[rs]);
+      weights8<F16>(pr[0], pr[1], pf[rs], pl[rs]);
       l_run[rs] = l_run[rs] * alpha[rs] + psum;
     }
     qk.template operator()<pk>(s_next);
@@ -484,16 +489,17 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
       if (dt + 1 < 8) rdv(dt + 1, (dt + 1) & 1);
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
-        acc[rs][dt] = mfma_bf16(va[dt & 1], pf[rs], acc[rs][dt]);
-        acc[rs][dt] = mfma_bf16(va[dt & 1], pl[rs], acc[rs][dt]);
+        acc[rs][dt] = mma16<F16>(va[dt & 1], pf[rs], acc[rs][dt]);
+        if constexpr (!F16) acc[rs][dt] = mma16<F16>(va[dt & 1], pl[rs], acc[rs][dt]);
       }
     }
+    constexpr int MPB = F16 ? 2 : 4;   // MFMAs per column block
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
     }
   };
 
@@ -597,6 +603,8 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
     }
   }
 }
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) { attn_fwd_d128<false>(a); }
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_f16_d128_kernel(FwdArgs a) { attn_fwd_d128<true>(a); }
 
 int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* m, float scale,
                     float* o, float* lse, int accumulate, hipStream_t stream) {
@@ -609,11 +617,12 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
   const dim3 grid(xcd_group_grid(m->Hkv, m->QB, QMAJOR_BPC, m->Hq / m->Hkv)), block(FWD_THREADS);
-  if (dtype == VS_BF16 && D == 128) {
+  if ((dtype == VS_BF16 || dtype == VS_F16) && D == 128) {
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     const int64_t krows = (int64_t)m->KB * BLK;
     if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
+    if (dtype == VS_F16) hipLaunchKernelGGL(attn_fwd_f16_d128_kernel, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
   }
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);

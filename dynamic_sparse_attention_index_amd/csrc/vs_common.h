@@ -22,12 +22,26 @@ constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
 
 // --- MFMA wrappers (lane layouts verified on gfx950) ------------------------
 // 16x16x32 bf16: lane l supplies A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16]
 // (j=0..7) and receives C[4*(l/16)+i][l%16] (i=0..3).
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// The same shape on fp16 operands (identical lane layout).
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+__device__ __forceinline__ f32x4 mfma_f16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
+}
+// 16-bit MFMA operands travel in bf16x8 containers; F16 says the bits are
+// fp16 (tiles and fragments are only moved, never converted, on the way).
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (F16) return mfma_f16(a, b, c);
+  else return mfma_bf16(a, b, c);
 }
 // 16x16x4 f32: lane l supplies A[l%16][l/16], B[l/16][l%16]; C as above.
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
@@ -255,6 +269,22 @@ __device__ __forceinline__ void split8(const f32x4& w0, const f32x4& w1, bf16x8&
   split_pair(w1[2], w1[3], h[3], l[3]);
   hi = __builtin_bit_cast(bf16x8, i32x4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
   lo = __builtin_bit_cast(bf16x8, i32x4{(int)l[0], (int)l[1], (int)l[2], (int)l[3]});
+}
+// Eight fp32 weights (P or dS) as MFMA operands. bf16: the hi + lo pair of
+// split8 (two MFMAs per product). fp16: one operand rounded to nearest even
+// (11 significant bits); lo is left untouched and not used.
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+template <bool F16>
+__device__ __forceinline__ void weights8(const f32x4& w0, const f32x4& w1, bf16x8& hi, bf16x8& lo) {
+  if constexpr (F16) {
+    const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0[0], w0[1]}, f16x2));
+    const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0[2], w0[3]}, f16x2));
+    const uint32_t h2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w1[0], w1[1]}, f16x2));
+    const uint32_t h3 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w1[2], w1[3]}, f16x2));
+    hi = __builtin_bit_cast(bf16x8, i32x4{(int)h0, (int)h1, (int)h2, (int)h3});
+  } else {
+    split8(w0, w1, hi, lo);
+  }
 }
 
 }  // namespace vs

@@ -24,6 +24,8 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
 int launch_merge(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
                  int Hq, int64_t Nq, int D, hipStream_t stream);
 
+int launch_convert_f16(const void* src, void* dst, int64_t n, int32_t* status, hipStream_t stream);
+
 int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, int D, float* delta,
                     hipStream_t stream);
 

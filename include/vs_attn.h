@@ -39,6 +39,10 @@
  *       M_h[n, m] = [m <= n] and ([m in V_h] or [n/64 - m/64 in S_h]).
  * Supported: D in {64, 128}; dtype f32 or bf16 (q, k, v, dout alike); every
  * local length a multiple of 64; Hq a multiple of Hkv; last_q in [1, 64].
+ * The attention calls (vs_attn_fwd, vs_attn_bwd_prep, vs_attn_bwd*) also take
+ * fp16 at D = 128: exact copies of bf16 data made by vs_convert_f16, on
+ * which the attention weights P and dS enter their products as single fp16
+ * operands (11 significant bits) instead of hi + lo bf16 pairs.
  */
 #ifndef VS_ATTN_H
 #define VS_ATTN_H
@@ -56,10 +60,11 @@ typedef enum {
   VS_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head dim, alignment) */
   VS_ERR_WORKSPACE = -3,    /* workspace or mask buffer too small              */
   VS_ERR_CAPACITY = -4,     /* device-side list capacity exceeded (status word) */
-  VS_ERR_HIP = -5           /* a HIP runtime call or kernel launch failed      */
+  VS_ERR_HIP = -5,          /* a HIP runtime call or kernel launch failed      */
+  VS_ERR_RANGE = -6         /* a value outside the target type (status word)   */
 } vs_status;
 
-typedef enum { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
+typedef enum { VS_F32 = 0, VS_BF16 = 1, VS_F16 = 2 } vs_dtype;
 
 /* How global positions are dealt to the P ranks of the context-parallel ring
  * (review page 1, section 三.3):
@@ -275,6 +280,23 @@ int vs_attn_fwd(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float s
  * o_acc/o_step: [Hq, Nq, D] fp32 contiguous; lse_acc/lse_step: [Hq, Nq]. */
 int vs_merge_lse(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
                  int Hq, int64_t Nq, int D, void* stream);
+
+/* ---- 16-bit operand format -------------------------------------------- */
+
+/* dst[i] = fp16(src[i]) for n contiguous bf16 values (src, dst 16-byte
+ * aligned device buffers of n * 2 bytes, n a multiple of 8, not overlapping).
+ * Not a step of the pages' method: it changes only the bit format the
+ * attention kernels read. bf16 keeps 8 significant bits, fp16 11, so the
+ * conversion is exact for 2^-17 <= |x| < 65536 and for 0; smaller magnitudes
+ * are rounded to fp16's 2^-24 spacing (absolute error <= 2^-25). A value
+ * with |x| >= 65536 (including inf) or a NaN is a range error: the kernel
+ * writes VS_ERR_RANGE to the device word *status (which the caller sets to
+ * VS_OK beforehand and reads after synchronising) and dst is then
+ * unspecified. Inputs of larger range are pre-scaled by the caller by a power
+ * of two (exact), with the scale folded into `scale` or the outputs.
+ * Errors: VS_ERR_ARG for null pointers or n < 0; VS_ERR_UNSUPPORTED for
+ * misaligned buffers or n % 8 != 0. */
+int vs_convert_f16(const void* src, void* dst, int64_t n, int32_t* status, void* stream);
 
 /* ---- 5. backward ------------------------------------------------------ */
 

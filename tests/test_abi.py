@@ -35,7 +35,7 @@ def test_header_symbols_exported(L):
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert vs.status_string(code) and vs.status_string(code) != "unknown status"
     assert vs.status_string(123) == "unknown status"
 
@@ -173,3 +173,36 @@ def test_dense_buffer_arguments_must_be_contiguous():
     with pytest.raises(vs.VsError):
         vs._cptr(torch.zeros(4, 8)[:, :4])
     assert vs._cptr(torch.zeros(4, 8)).value is not None
+
+
+def test_f16_validation_before_device_work(L):
+    """fp16 operands: attention at D = 128 only, never mixed with bf16, never
+    for the index; the conversion call checks its buffers on the host."""
+    m, lay, _, _ = _mask(L)
+    m.rank = m.src = 0
+    q16 = _fake_tensor(0x20000000, 4, 1024, 128, vs.VS_F16)
+    k16 = _fake_tensor(0x30000000, 2, 1024, 128, vs.VS_F16)
+    kb = _fake_tensor(0x30000000, 2, 1024, 128)
+    o, lse = ctypes.c_void_p(0x40000000), ctypes.c_void_p(0x50000000)
+    assert L.vs_attn_fwd(q16, kb, kb, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_ARG
+    q64 = _fake_tensor(0x20000000, 4, 1024, 64, vs.VS_F16)
+    k64 = _fake_tensor(0x30000000, 2, 1024, 64, vs.VS_F16)
+    assert L.vs_attn_fwd(q64, k64, k64, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_UNSUPPORTED
+    p = ctypes.c_void_p(0x40000000)
+    assert L.vs_attn_bwd(q16, k16, k16, _fake_tensor(0x20000000, 4, 1024, 128), p, p, ctypes.byref(m), 0.1,
+                         p, p, p, None) == vs.VS_ERR_ARG
+    assert L.vs_attn_bwd_prep(p, q64, p, None) == vs.VS_ERR_UNSUPPORTED
+    bad = _fake_tensor(0x20000000, 4, 1024, 128, 7)
+    assert L.vs_attn_fwd(bad, bad, bad, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_ARG
+    # the index has no fp16 kernels
+    ws = ctypes.c_void_p(0x60000000)
+    ql = _fake_tensor(0x20000000, 4, 64, 128, vs.VS_F16)
+    assert L.vs_index_build(ql, _fake_tensor(0x30000000, 2, 1024, 128, vs.VS_F16), vs.layout("contig", 1, 1024),
+                            0.1, 0.9, p, p, p, p, p, p, ws, 1 << 30, None) == vs.VS_ERR_UNSUPPORTED
+    a, b, st = ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000)
+    assert L.vs_convert_f16(None, b, 64, st, None) == vs.VS_ERR_ARG
+    assert L.vs_convert_f16(a, b, 64, None, None) == vs.VS_ERR_ARG
+    assert L.vs_convert_f16(a, b, -8, st, None) == vs.VS_ERR_ARG
+    assert L.vs_convert_f16(a, b, 12, st, None) == vs.VS_ERR_UNSUPPORTED
+    assert L.vs_convert_f16(ctypes.c_void_p(0x20000002), b, 64, st, None) == vs.VS_ERR_UNSUPPORTED
+    assert L.vs_convert_f16(a, b, 0, st, None) == vs.VS_OK                 # nothing to do

@@ -12,7 +12,13 @@ from synth import config_by_name, generate
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "f32": 1e-4}
+TOL = {"bf16": 2e-2, "f32": 1e-4, "f16": 2e-2}
+
+
+def _cfg(dtype, **kw):
+    """Config whose inputs are `dtype` values; "f16" (fp16 operands) runs on
+    bf16 inputs converted exactly by the library."""
+    return config_by_name("qwen32k", dtype="bf16" if dtype == "f16" else dtype, **kw)
 
 
 def _index(rng, N, Hq, nv, ns, band=3):
@@ -23,9 +29,10 @@ def _index(rng, N, Hq, nv, ns, band=3):
     return vert, slash
 
 
-def _fwd_case(cfg, vert, slash, kind="contig", P=1, accumulate_steps=False):
+def _fwd_case(cfg, vert, slash, kind="contig", P=1, accumulate_steps=False, comp=None):
     import dynamic_sparse_attention_index_amd as vs
     from tests import vs_harness as H
+    comp = comp or cfg.dtype
     t = generate(cfg, tensors=("q", "k", "v"))
     N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
     lay = vs.layout(kind, P, N)
@@ -34,15 +41,15 @@ def _fwd_case(cfg, vert, slash, kind="contig", P=1, accumulate_steps=False):
     cap = H.tile_cap_for(slash, Hq, QB)
     worst = 0.0
     for rank in range(P):
-        q = H.to_dev(H.shard(t["q"], kind, P, rank), cfg.dtype)
+        q = H.to_dev_comp(H.shard(t["q"], kind, P, rank), comp)
         o_acc = torch.zeros(Hq, QB * 64, D, device="cuda")
         l_acc = torch.full((Hq, QB * 64), -math.inf, device="cuda")
         ref_o = np.zeros((Hq, QB * 64, D))
         ref_l = np.full((Hq, QB * 64), -np.inf)
         for step in range(P):
             src = ol.ring_source(rank, step, P)
-            k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
-            v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+            k = H.to_dev_comp(H.shard(t["k"], kind, P, src), comp)
+            v = H.to_dev_comp(H.shard(t["v"], kind, P, src), comp)
             m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
             if accumulate_steps:
                 vs.vs_attn_fwd(q, k, v, m, cfg.scale, o_acc, l_acc, accumulate=1)
@@ -62,28 +69,29 @@ def _fwd_case(cfg, vert, slash, kind="contig", P=1, accumulate_steps=False):
         assert (gl[~fin] == -np.inf).all() and (go[~fin] == 0).all()
         lerr = np.abs(gl[fin] - ref_l[fin]).max() if fin.any() else 0.0
         worst = max(worst, err, lerr)
-        print(f"fwd {cfg.dtype} D={cfg.D} {kind} P={P} rank={rank}: max|dO|={err:.3e} max|dLSE|={lerr:.3e}")
-        assert err <= TOL[cfg.dtype] and lerr <= TOL[cfg.dtype], (rank, err, lerr)
+        print(f"fwd {comp} D={cfg.D} {kind} P={P} rank={rank}: max|dO|={err:.3e} max|dLSE|={lerr:.3e}")
+        assert err <= TOL[comp] and lerr <= TOL[comp], (rank, err, lerr)
     return worst
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f32", 64)])
 def test_fwd_random_index_contig(dtype, D):
     rng = np.random.default_rng(1)
-    cfg = config_by_name("qwen32k", N=64 * 24, Hq=4, Hkv=2, D=D, dtype=dtype, n_out=5, c=2.0)
+    cfg = _cfg(dtype, N=64 * 24, Hq=4, Hkv=2, D=D, n_out=5, c=2.0)
     vert, slash = _index(rng, cfg.N, cfg.Hq, 150, 5)
     slash[1] = slash[1][slash[1] != 0]        # a head without the diagonal block: causal verticals + empty rows
     vert[2] = np.zeros(0, dtype=np.int64)     # a head without verticals
-    _fwd_case(cfg, vert, slash)
+    _fwd_case(cfg, vert, slash, comp=dtype)
 
 
-@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2), ("contig", 2)])
-def test_fwd_ring_merge(kind, P):
+@pytest.mark.parametrize("kind,P,comp", [("striped", 4, "bf16"), ("zigzag", 2, "bf16"), ("contig", 2, "bf16"),
+                                         ("striped", 4, "f16")])
+def test_fwd_ring_merge(kind, P, comp):
     rng = np.random.default_rng(2)
     cfg = config_by_name("qwen32k", N=64 * 32, Hq=4, Hkv=1, n_out=4, c=2.0)
     vert, slash = _index(rng, cfg.N, cfg.Hq, 100, 6)
-    _fwd_case(cfg, vert, slash, kind, P, accumulate_steps=False)
-    _fwd_case(cfg, vert, slash, kind, P, accumulate_steps=True)
+    _fwd_case(cfg, vert, slash, kind, P, accumulate_steps=False, comp=comp)
+    _fwd_case(cfg, vert, slash, kind, P, accumulate_steps=True, comp=comp)
 
 
 def test_fwd_full_budget_is_dense_causal_sdpa():
@@ -108,9 +116,10 @@ def test_fwd_full_budget_is_dense_causal_sdpa():
     assert (o - ref).abs().max().item() < 2e-2
 
 
-def _bwd_case(cfg, vert, slash, kind="contig", P=1):
+def _bwd_case(cfg, vert, slash, kind="contig", P=1, comp=None):
     import dynamic_sparse_attention_index_amd as vs
     from tests import vs_harness as H
+    comp = comp or cfg.dtype
     t = generate(cfg)
     N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
     lay = vs.layout(kind, P, N)
@@ -133,14 +142,14 @@ def _bwd_case(cfg, vert, slash, kind="contig", P=1):
     dv_all = {r: torch.zeros(Hkv, QB * 64, D, device="cuda") for r in range(P)}
     errs = []
     for rank in range(P):
-        q = H.to_dev(H.shard(t["q"], kind, P, rank), cfg.dtype)
-        do = H.to_dev(H.shard(t["do"], kind, P, rank), cfg.dtype)
+        q = H.to_dev_comp(H.shard(t["q"], kind, P, rank), comp)
+        do = H.to_dev_comp(H.shard(t["do"], kind, P, rank), comp)
         o = torch.zeros(Hq, QB * 64, D, device="cuda")
         lse = torch.full((Hq, QB * 64), -math.inf, device="cuda")
         for step in range(P):
             src = ol.ring_source(rank, step, P)
-            k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
-            v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+            k = H.to_dev_comp(H.shard(t["k"], kind, P, src), comp)
+            v = H.to_dev_comp(H.shard(t["v"], kind, P, src), comp)
             m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
             vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse, accumulate=1)
         delta = torch.empty(Hq, QB * 64, device="cuda")
@@ -148,8 +157,8 @@ def _bwd_case(cfg, vert, slash, kind="contig", P=1):
         dq = torch.zeros(Hq, QB * 64, D, device="cuda")
         for step in range(P):
             src = ol.ring_source(rank, step, P)
-            k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
-            v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+            k = H.to_dev_comp(H.shard(t["k"], kind, P, src), comp)
+            v = H.to_dev_comp(H.shard(t["v"], kind, P, src), comp)
             m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
             vs.vs_attn_bwd(q, k, v, do, lse, delta, m, cfg.scale, dq, dk_all[src], dv_all[src])
         torch.cuda.synchronize()
@@ -159,26 +168,26 @@ def _bwd_case(cfg, vert, slash, kind="contig", P=1):
         cols = ol.shard_positions(kind, N, P, r)
         errs.append(np.abs(dk_all[r].cpu().numpy() - ref_dk[:, cols]).max())
         errs.append(np.abs(dv_all[r].cpu().numpy() - ref_dv[:, cols]).max())
-    print(f"bwd {cfg.dtype} D={cfg.D} {kind} P={P}: max errors (dq per rank, then dk, dv per shard) {errs}")
-    assert max(errs) <= TOL[cfg.dtype], errs
+    print(f"bwd {comp} D={cfg.D} {kind} P={P}: max errors (dq per rank, then dk, dv per shard) {errs}")
+    assert max(errs) <= TOL[comp], errs
     return errs
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("f32", 64), ("bf16", 64)])
 def test_bwd_random_index(dtype, D):
     rng = np.random.default_rng(3)
-    cfg = config_by_name("qwen32k", N=64 * 16, Hq=4, Hkv=2, D=D, dtype=dtype, n_out=4, c=2.0)
+    cfg = _cfg(dtype, N=64 * 16, Hq=4, Hkv=2, D=D, n_out=4, c=2.0)
     vert, slash = _index(rng, cfg.N, cfg.Hq, 90, 4)
     slash[3] = slash[3][slash[3] != 0]
-    _bwd_case(cfg, vert, slash)
+    _bwd_case(cfg, vert, slash, comp=dtype)
 
 
-@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2)])
-def test_bwd_ring(kind, P):
+@pytest.mark.parametrize("kind,P,comp", [("striped", 4, "bf16"), ("zigzag", 2, "bf16"), ("zigzag", 2, "f16")])
+def test_bwd_ring(kind, P, comp):
     rng = np.random.default_rng(4)
     cfg = config_by_name("qwen32k", N=64 * 16, Hq=2, Hkv=1, n_out=4, c=2.0)
     vert, slash = _index(rng, cfg.N, cfg.Hq, 60, 4)
-    _bwd_case(cfg, vert, slash, kind, P)
+    _bwd_case(cfg, vert, slash, kind, P, comp=comp)
 
 
 def test_merge_kernel_matches_formula():
@@ -205,7 +214,7 @@ def test_merge_kernel_matches_formula():
     assert (tl.cpu().numpy()[~fin] == -np.inf).all()
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("f32", 64)])
 def test_bwd_overwrite_matches_accumulate(dtype, D):
     """VS_BWD_OVERWRITE on NaN-filled outputs gives what the adding parts give
     on zeroed ones: dq and the slash dk/dv bit for bit (rows without a
@@ -215,7 +224,7 @@ def test_bwd_overwrite_matches_accumulate(dtype, D):
     from tests import vs_harness as H
     rng = np.random.default_rng(11)
     kind, P, rank, step = "striped", 4, 1, 2
-    cfg = config_by_name("qwen32k", N=64 * 32, Hq=4, Hkv=2, D=D, dtype=dtype, n_out=4, c=2.0)
+    cfg = _cfg(dtype, N=64 * 32, Hq=4, Hkv=2, D=D, n_out=4, c=2.0)
     vert, slash = _index(rng, cfg.N, cfg.Hq, 40, 3, band=0)
     t = generate(cfg)
     N, Hq, Hkv = cfg.N, cfg.Hq, cfg.Hkv
@@ -224,10 +233,10 @@ def test_bwd_overwrite_matches_accumulate(dtype, D):
     lists = H.upload_lists(vert, slash, N)
     cap = H.tile_cap_for(slash, Hq, QB)
     src = ol.ring_source(rank, step, P)
-    q = H.to_dev(H.shard(t["q"], kind, P, rank), cfg.dtype)
-    do = H.to_dev(H.shard(t["do"], kind, P, rank), cfg.dtype)
-    k = H.to_dev(H.shard(t["k"], kind, P, src), cfg.dtype)
-    v = H.to_dev(H.shard(t["v"], kind, P, src), cfg.dtype)
+    q = H.to_dev_comp(H.shard(t["q"], kind, P, rank), dtype)
+    do = H.to_dev_comp(H.shard(t["do"], kind, P, rank), dtype)
+    k = H.to_dev_comp(H.shard(t["k"], kind, P, src), dtype)
+    v = H.to_dev_comp(H.shard(t["v"], kind, P, src), dtype)
     m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
     o = torch.zeros(Hq, QB * 64, D, device="cuda")
     lse = torch.full((Hq, QB * 64), -math.inf, device="cuda")
@@ -250,3 +259,34 @@ def test_bwd_overwrite_matches_accumulate(dtype, D):
     torch.cuda.synchronize()
     for a, b in zip(got, ref):
         assert torch.allclose(a, b, rtol=1e-6, atol=1e-7)
+
+
+def test_convert_f16_exact_and_range():
+    """vs_convert_f16: bit-exact with round-to-nearest-even (torch's cast), the
+    value unchanged wherever fp16 can hold it (2^-17 <= |x| < 65536, and 0),
+    and VS_ERR_RANGE in the status word for |x| >= 65536, inf and NaN."""
+    import dynamic_sparse_attention_index_amd as vs
+    rng = np.random.default_rng(21)
+    n = 1 << 20
+    mag = np.exp2(rng.uniform(-30, 15.99, n)) * rng.choice([-1.0, 1.0], n)
+    mag[:16] = [0.0, -0.0, 65280.0, -65280.0, 2.0 ** -17, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                1.0, -1.0, 2.0 ** -14, 1e-3, 6e4, -6e4, 2.0 ** -18, 2.0 ** -30]
+    x = torch.tensor(mag, dtype=torch.float32).to(torch.bfloat16).cuda()
+    out = torch.empty(n, dtype=torch.float16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    vs.vs_convert_f16(x, out, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == vs.VS_OK
+    ref = x.to(torch.float16)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    xf = x.float()
+    held = (xf.abs() >= 2.0 ** -17) | (xf == 0)
+    assert torch.equal(out.float()[held], xf[held])
+    assert ((out.float() - xf).abs()[~held] <= 2.0 ** -25).all()
+    for bad in (65536.0, -1e6, float("inf"), float("nan")):
+        y = x.clone()
+        y[n // 2 + 3] = bad
+        status.zero_()
+        vs.vs_convert_f16(y, out, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == vs.VS_ERR_RANGE, bad

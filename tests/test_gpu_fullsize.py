@@ -54,9 +54,17 @@ def _candidate_cols(rows, vert_h, slash_h):
 
 
 def _rows_check(t, cfg, vert, slash, rows_of, got, heads, blocks):
-    """O / LSE / dQ of query blocks `blocks` (rows_of(I) -> global rows) of `heads`."""
+    """O / LSE / dQ of query blocks `blocks` (rows_of(I) -> global rows) of `heads`.
+    `got` is one result dict, or a dict of them by name (the oracle rows are
+    then computed once and every result is checked against them)."""
+    if "o" not in got:
+        return _rows_check_many(t, cfg, vert, slash, rows_of, got, heads, blocks)
+    return _rows_check_many(t, cfg, vert, slash, rows_of, {"": got}, heads, blocks)[""]
+
+
+def _rows_check_many(t, cfg, vert, slash, rows_of, gots, heads, blocks):
     Hq, Hkv = cfg.Hq, cfg.Hkv
-    worst = {"o": 0.0, "lse": 0.0, "dq": 0.0}
+    worsts = {name: {"o": 0.0, "lse": 0.0, "dq": 0.0} for name in gots}
     for h in heads:
         g = h * Hkv // Hq
         for I in blocks:
@@ -71,10 +79,13 @@ def _rows_check(t, cfg, vert, slash, rows_of, got, heads, blocks):
             dq, _, _ = oa.backward_rows(q, k, v, M, cfg.scale, do)
             fin = np.isfinite(lse)
             sl = slice(64 * I, 64 * I + 64)
-            worst["o"] = max(worst["o"], float(np.abs(got["o"][h, sl] - o).max()))
-            worst["lse"] = max(worst["lse"], float(np.abs(got["lse"][h, sl][fin] - lse[fin]).max()) if fin.any() else 0.0)
-            worst["dq"] = max(worst["dq"], float(np.abs(got["dq"][h, sl] - dq).max()))
-    return worst
+            for name, got in gots.items():
+                worst = worsts[name]
+                worst["o"] = max(worst["o"], float(np.abs(got["o"][h, sl] - o).max()))
+                worst["lse"] = max(worst["lse"],
+                                   float(np.abs(got["lse"][h, sl][fin] - lse[fin]).max()) if fin.any() else 0.0)
+                worst["dq"] = max(worst["dq"], float(np.abs(got["dq"][h, sl] - dq).max()))
+    return worsts
 
 
 def _tail_active(cfg, vert, slash, row_lo, rows_filter=None):
@@ -119,7 +130,9 @@ def _tail_start(cfg, vert, slash, first_blocks, rows_filter=None, need=4096, max
 
 def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None):
     """dK / dV of keys at global positions >= row_lo: exact contributions of the
-    rows at or after row_lo (optionally only those passing rows_filter)."""
+    rows at or after row_lo (optionally only those passing rows_filter).
+    dk_of / dv_of may be lists (several results checked against one oracle
+    computation); the errors are then lists too."""
     Hq, Hkv, N = cfg.Hq, cfg.Hkv, cfg.N
     rows = np.arange(row_lo, N)
     if rows_filter is not None:
@@ -139,10 +152,16 @@ def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None):
         sel = used >= row_lo
         ref_dk[g, used[sel] - row_lo] += dk[sel]
         ref_dv[g, used[sel] - row_lo] += dv[sel]
+    if isinstance(dk_of, (list, tuple)):
+        return ([float(np.abs(f(keys) - ref_dk).max()) for f in dk_of],
+                [float(np.abs(f(keys) - ref_dv).max()) for f in dv_of])
     return (float(np.abs(dk_of(keys) - ref_dk).max()), float(np.abs(dv_of(keys) - ref_dv).max()))
 
 
-def _contig_case(name):
+def _contig_case(name, comps=("bf16",)):
+    """comps: operand formats of the attention kernels checked on the same
+    index and oracle rows: "bf16" (the inputs as given, hi + lo weights) and
+    "f16" (exact fp16 copies made by vs_convert_f16, single fp16 weights)."""
     import dynamic_sparse_attention_index_amd as vs
     from tests import vs_harness as H
     cfg = config_by_name(name)
@@ -158,44 +177,57 @@ def _contig_case(name):
     _log(f"{name}: GPU index vs oracle index")
     H.check_index(H.gpu_index(q[:, N - cfg.last_q:], k, lay, cfg.scale, cfg.top_p), ref, cfg.top_p)
     vert, slash = ref["vert"], ref["slash"]
-    _log(f"{name}: GPU mask + forward + backward (oracle index)")
     m = H.gpu_mask(H.upload_lists(vert, slash, N), Hq, Hkv, lay, 0, 0, H.tile_cap_for(slash, Hq, T))
     assert int(m.arrays()["status"].item()) == 0
-    o = torch.empty(Hq, N, D, device=dev)
-    lse = torch.empty(Hq, N, device=dev)
-    delta = torch.empty(Hq, N, device=dev)
-    dq = torch.zeros(Hq, N, D, device=dev)
-    dk = torch.zeros(Hkv, N, D, device=dev)
-    dv = torch.zeros(Hkv, N, D, device=dev)
-    vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse)
-    vs.vs_attn_bwd_prep(o, do, delta)
-    vs.vs_attn_bwd(q, k, v, do, lse, delta, m, cfg.scale, dq, dk, dv)
-    torch.cuda.synchronize()
+    gots, dks, dvs = {}, [], []
+    for comp in comps:
+        _log(f"{name}: GPU mask + forward + backward (oracle index), {comp} operands")
+        ops = [H.as_f16(x) for x in (q, k, v, do)] if comp == "f16" else [q, k, v, do]
+        o = torch.empty(Hq, N, D, device=dev)
+        lse = torch.empty(Hq, N, device=dev)
+        delta = torch.empty(Hq, N, device=dev)
+        dq = torch.zeros(Hq, N, D, device=dev)
+        dk = torch.zeros(Hkv, N, D, device=dev)
+        dv = torch.zeros(Hkv, N, D, device=dev)
+        vs.vs_attn_fwd(ops[0], ops[1], ops[2], m, cfg.scale, o, lse)
+        vs.vs_attn_bwd_prep(o, ops[3], delta)
+        vs.vs_attn_bwd(*ops, lse, delta, m, cfg.scale, dq, dk, dv)
+        torch.cuda.synchronize()
+        del ops
+        gots[comp] = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
+        dk_h, dv_h = dk.cpu().numpy(), dv.cpu().numpy()
+        dks.append(lambda keys, a=dk_h: a[:, keys])
+        dvs.append(lambda keys, a=dv_h: a[:, keys])
+        del o, lse, delta, dq, dk, dv
     rng = np.random.default_rng(cfg.seed + 77)
     heads = sorted(set([0, Hq - 1] + rng.choice(Hq, 2, replace=False).tolist()))
     blocks = sorted(set([0, T - 1, T // 2] + rng.choice(T, 3, replace=False).tolist()))
     _log(f"{name}: oracle rows heads={heads} blocks={blocks}")
-    got = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
-    w = _rows_check(t, cfg, vert, slash, lambda I: np.arange(64 * I, 64 * I + 64), got, heads, blocks)
+    ws = _rows_check(t, cfg, vert, slash, lambda I: np.arange(64 * I, 64 * I + 64), gots, heads, blocks)
     row_lo, n_tail = _tail_start(cfg, vert, slash, 3)
     _log(f"{name}: oracle dK/dV of the last {(N - row_lo) // 64} key blocks ({n_tail} active entries)")
     assert n_tail > 0
-    dk_h, dv_h = dk.cpu().numpy(), dv.cpu().numpy()
-    ek, ev = _tail_kv_check(t, cfg, vert, slash, row_lo, lambda keys: dk_h[:, keys], lambda keys: dv_h[:, keys])
-    _log(f"{name}: max errors O {w['o']:.3e} LSE {w['lse']:.3e} dQ {w['dq']:.3e} dK {ek:.3e} dV {ev:.3e}")
-    assert max(w["o"], w["lse"], w["dq"], ek, ev) <= TOL, (w, ek, ev)
+    eks, evs = _tail_kv_check(t, cfg, vert, slash, row_lo, dks, dvs)
+    for comp, ek, ev in zip(comps, eks, evs):
+        w = ws[comp]
+        _log(f"{name} [{comp}]: max errors O {w['o']:.3e} LSE {w['lse']:.3e} dQ {w['dq']:.3e} "
+             f"dK {ek:.3e} dV {ev:.3e}")
+    for comp, ek, ev in zip(comps, eks, evs):
+        w = ws[comp]
+        assert max(w["o"], w["lse"], w["dq"], ek, ev) <= TOL, (comp, w, ek, ev)
 
 
 @pytest.mark.timeout(600)
 def test_fullsize_qwen128k_step():
-    """The benchmarked step: 16/2 heads, 131072 tokens, d 128, bf16, fwd + bwd."""
-    _contig_case("qwen128k")
+    """The benchmarked step: 16/2 heads, 131072 tokens, d 128, bf16 inputs,
+    fwd + bwd, with bf16 and with fp16 operands."""
+    _contig_case("qwen128k", comps=("bf16", "f16"))
 
 
 @pytest.mark.timeout(900)
 def test_fullsize_llama256k_step():
     """32/8 heads, 262144 tokens with Yarn x32 positions, fwd + bwd."""
-    _contig_case("llama256k")
+    _contig_case("llama256k", comps=("bf16", "f16"))
 
 
 @pytest.mark.timeout(900)
@@ -224,36 +256,43 @@ def test_fullsize_qwen512k_ring_rank(kind, rank):
     cap = H.tile_cap_for(slash, Hq, QB)
     dev = "cuda"
     rows_r = ol.shard_positions(kind, N, P, rank)
-    q = H.to_dev(t["q"][:, rows_r], cfg.dtype)
-    do = H.to_dev(t["do"][:, rows_r], cfg.dtype)
-    o = torch.zeros(Hq, QB * 64, D, device=dev)
-    lse = torch.full((Hq, QB * 64), -math.inf, device=dev)
-    _log("512k: forward over 32 ring steps")
-    kv = {}
-    for step in range(P):
-        src = ol.ring_source(rank, step, P)
-        cols = ol.shard_positions(kind, N, P, src)
-        kv[src] = (H.to_dev(t["k"][:, cols], cfg.dtype), H.to_dev(t["v"][:, cols], cfg.dtype))
-        m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
-        assert int(m.arrays()["status"].item()) == 0
-        vs.vs_attn_fwd(q, kv[src][0], kv[src][1], m, cfg.scale, o, lse, accumulate=1)
-    delta = torch.empty(Hq, QB * 64, device=dev)
-    vs.vs_attn_bwd_prep(o, do, delta)
-    dq = torch.zeros(Hq, QB * 64, D, device=dev)
-    dk = {s: torch.zeros(Hkv, QB * 64, D, device=dev) for s in range(P)}
-    dv = {s: torch.zeros(Hkv, QB * 64, D, device=dev) for s in range(P)}
-    _log("512k: backward over 32 ring steps")
-    for step in range(P):
-        src = ol.ring_source(rank, step, P)
-        m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
-        vs.vs_attn_bwd(q, kv[src][0], kv[src][1], do, lse, delta, m, cfg.scale, dq, dk[src], dv[src])
-    torch.cuda.synchronize()
     rng = np.random.default_rng(cfg.seed + 11 * rank)
     heads = sorted(set([0, Hq - 1] + rng.choice(Hq, 1).tolist()))
     blocks = sorted(set([0, QB - 1] + rng.choice(QB, 3, replace=False).tolist()))
+    comps = ("bf16", "f16")
+    gots, dk_hs, dv_hs = {}, {}, {}
+    for comp in comps:
+        conv = H.as_f16 if comp == "f16" else (lambda x: x)
+        q = conv(H.to_dev(t["q"][:, rows_r], cfg.dtype))
+        do = conv(H.to_dev(t["do"][:, rows_r], cfg.dtype))
+        o = torch.zeros(Hq, QB * 64, D, device=dev)
+        lse = torch.full((Hq, QB * 64), -math.inf, device=dev)
+        _log(f"512k [{comp}]: forward over 32 ring steps")
+        kv = {}
+        for step in range(P):
+            src = ol.ring_source(rank, step, P)
+            cols = ol.shard_positions(kind, N, P, src)
+            kv[src] = (conv(H.to_dev(t["k"][:, cols], cfg.dtype)), conv(H.to_dev(t["v"][:, cols], cfg.dtype)))
+            m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+            assert int(m.arrays()["status"].item()) == 0
+            vs.vs_attn_fwd(q, kv[src][0], kv[src][1], m, cfg.scale, o, lse, accumulate=1)
+        delta = torch.empty(Hq, QB * 64, device=dev)
+        vs.vs_attn_bwd_prep(o, do, delta)
+        dq = torch.zeros(Hq, QB * 64, D, device=dev)
+        dk = {s: torch.zeros(Hkv, QB * 64, D, device=dev) for s in range(P)}
+        dv = {s: torch.zeros(Hkv, QB * 64, D, device=dev) for s in range(P)}
+        _log(f"512k [{comp}]: backward over 32 ring steps")
+        for step in range(P):
+            src = ol.ring_source(rank, step, P)
+            m = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+            vs.vs_attn_bwd(q, kv[src][0], kv[src][1], do, lse, delta, m, cfg.scale, dq, dk[src], dv[src])
+        torch.cuda.synchronize()
+        gots[comp] = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
+        dk_hs[comp] = {s: dk[s].cpu().numpy() for s in range(P)}
+        dv_hs[comp] = {s: dv[s].cpu().numpy() for s in range(P)}
+        del q, do, o, lse, delta, dq, dk, dv, kv
     _log(f"512k: oracle rows heads={heads} local blocks={blocks}")
-    got = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
-    w = _rows_check(t, cfg, vert, slash, lambda I: rows_r[64 * I:64 * I + 64], got, heads, blocks)
+    ws = _rows_check(t, cfg, vert, slash, lambda I: rows_r[64 * I:64 * I + 64], gots, heads, blocks)
     # dK/dV of the key blocks from 64 (or more) blocks before this rank's last
     # row to the end, from this rank's rows only (keys past its last row get
     # nothing from it)
@@ -263,9 +302,6 @@ def test_fullsize_qwen512k_ring_rank(kind, rank):
         c = ol.shard_positions(kind, N, P, s)
         owner[c] = s
         local[c] = np.arange(len(c))
-    dk_h = {s: dk[s].cpu().numpy() for s in range(P)}
-    dv_h = {s: dv[s].cpu().numpy() for s in range(P)}
-
     def gather(store, keys):
         out = np.empty((Hkv, len(keys), D), dtype=np.float32)
         for s in np.unique(owner[keys]):
@@ -280,8 +316,14 @@ def test_fullsize_qwen512k_ring_rank(kind, rank):
                                  end_row=int(rows_r.max()) + 1)
     _log(f"512k: oracle dK/dV of the last {(N - row_lo) // 64} key blocks, this rank's rows ({n_tail} active)")
     assert n_tail > 0
-    ek, ev = _tail_kv_check(t, cfg, vert, slash, row_lo, lambda keys: gather(dk_h, keys),
-                            lambda keys: gather(dv_h, keys), rows_filter=lambda rows: mine[rows])
-    _log(f"512k {kind} rank {rank}: max errors O {w['o']:.3e} LSE {w['lse']:.3e} dQ {w['dq']:.3e} "
-         f"dK {ek:.3e} dV {ev:.3e}")
-    assert max(w["o"], w["lse"], w["dq"], ek, ev) <= TOL, (w, ek, ev)
+    eks, evs = _tail_kv_check(t, cfg, vert, slash, row_lo,
+                              [lambda keys, c=c: gather(dk_hs[c], keys) for c in comps],
+                              [lambda keys, c=c: gather(dv_hs[c], keys) for c in comps],
+                              rows_filter=lambda rows: mine[rows])
+    for comp, ek, ev in zip(comps, eks, evs):
+        w = ws[comp]
+        _log(f"512k {kind} rank {rank} [{comp}]: max errors O {w['o']:.3e} LSE {w['lse']:.3e} dQ {w['dq']:.3e} "
+             f"dK {ek:.3e} dV {ev:.3e}")
+    for comp, ek, ev in zip(comps, eks, evs):
+        w = ws[comp]
+        assert max(w["o"], w["lse"], w["dq"], ek, ev) <= TOL, (comp, w, ek, ev)

@@ -16,6 +16,25 @@ def to_dev(x, dtype):
     return t.to(device=DEV, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
+def as_f16(x):
+    """Exact fp16 copy of a bf16 device tensor, made by the library's own
+    conversion (vs_convert_f16); fails on a range error."""
+    out = torch.empty(x.shape, dtype=torch.float16, device=x.device)
+    status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    vs.vs_convert_f16(x.contiguous(), out, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == vs.VS_OK
+    return out
+
+
+def to_dev_comp(x, comp):
+    """Device operands for compute format comp: "bf16", "f32", or "f16" (the
+    bf16 values converted exactly by the library)."""
+    if comp == "f16":
+        return as_f16(to_dev(x, "bf16"))
+    return to_dev(x, comp)
+
+
 def gpu_index(q_last, k, lay, scale, top_p):
     """q_last [Hq, L, D], k [Hkv, N, D] device tensors (k in layout storage order)."""
     Hq, Hkv, D, N = q_last.shape[0], k.shape[0], k.shape[2], lay.n_global
