@@ -380,15 +380,17 @@ def ring_report(args, cfg):
             conv_status = torch.zeros(1, dtype=torch.int32, device=dev)
             aq, ak, av, ado = (torch.empty(x.shape, dtype=torch.float16, device=dev) for x in (q, k, v, do))
             # all P shards at once (bandwidth-bound, linear in size): per rank = total / P
+            qc, kc, vc, doc = (x.contiguous() for x in (q, k, v, do))
             t_conv = []
             for rep in range(-1, args.ring_reps):
                 e = timed(lambda: [vs.vs_convert_f16(x, y, conv_status, stream)
-                                   for x, y in ((q, aq), (k, ak), (v, av), (do, ado))])
+                                   for x, y in ((qc, aq), (kc, ak), (vc, av), (doc, ado))])
                 torch.cuda.synchronize()
                 if rep >= 0:
                     t_conv.append(e[0].elapsed_time(e[1]) / P)
             if int(conv_status.item()) != 0:
                 raise RuntimeError("an input is outside the fp16 range: run with --operands bf16")
+            del qc, kc, vc, doc
         else:
             aq, ak, av, ado = q, k, v, do
         # global index over the storage-order keys; the last rows are global
