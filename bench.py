@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--operands", choices=("f16", "bf16"), default="f16",
                     help="attention operand format for bf16 workloads: exact fp16 copies (converted inside the "
                          "timed step, single fp16 P/dS) or the bf16 inputs (hi + lo bf16 P/dS)")
+    ap.add_argument("--bwd-streams", type=int, choices=(1, 2), default=1,
+                    help="2: run the dQ part on a second stream, concurrently with the dK/dV parts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-budgets", action="store_true", help="skip the budget-rule report (after the timed steps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -124,9 +126,12 @@ def main():
 
     stages = ("index", "mask", "convert_qkv", "fwd", "convert_do", "bwd_prep", "dq", "dkdv", "dkdv_vert")
     ev = {name: [] for name in stages}
+    two = args.bwd_streams == 2 and cfg.backward
+    side = torch.cuda.Stream(device=dev) if two else None    # default priority, like every stream here
 
     def step(record):
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
+        dq_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if record else None
 
         def mark(i):
             if record:
@@ -149,8 +154,21 @@ def main():
             vs.vs_attn_bwd_prep(o, ado, delta, stream)
             mark(6)
             # dq and the slash dk/dv write their outputs whole; the vertical part adds after them
-            vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
-                                 vs.VS_BWD_DQ | vs.VS_BWD_OVERWRITE, stream)
+            if two:
+                # dq (writes dq only) on the side stream, dk/dv parts on the launch stream
+                fork, join = torch.cuda.Event(), torch.cuda.Event()
+                fork.record(stream)
+                side.wait_event(fork)
+                if record:
+                    dq_ev[0].record(side)
+                vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
+                                     vs.VS_BWD_DQ | vs.VS_BWD_OVERWRITE, side)
+                if record:
+                    dq_ev[1].record(side)
+                join.record(side)
+            else:
+                vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
+                                     vs.VS_BWD_DQ | vs.VS_BWD_OVERWRITE, stream)
             mark(7)
             vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
                                  vs.VS_BWD_DKDV | vs.VS_BWD_OVERWRITE, stream)
@@ -161,9 +179,11 @@ def main():
             for i in (5, 6, 7, 8):
                 mark(i)
         mark(9)
+        if two:
+            stream.wait_event(join)
         if record:
             for i, name in enumerate(stages):
-                ev[name].append((marks[i], marks[i + 1]))
+                ev[name].append(dq_ev if (two and name == "dq") else (marks[i], marks[i + 1]))
 
     for _ in range(args.warmup):
         step(False)
@@ -195,7 +215,11 @@ def main():
     sparsity = 1.0 - A / total_causal
     eff_flops = (4 + (10 if cfg.backward else 0)) * D * A
     tflops = eff_flops / (ms_per_step * 1e-3) / 1e12
-    attn_ms = sum(stage_ms[x] for x in ("convert_qkv", "fwd", "convert_do", "bwd_prep", "dq", "dkdv", "dkdv_vert"))
+    attn_ms = sum(stage_ms[x] for x in ("convert_qkv", "fwd", "convert_do", "bwd_prep"))
+    if two:   # dq overlaps the dk/dv parts
+        attn_ms += max(stage_ms["dq"], stage_ms["dkdv"] + stage_ms["dkdv_vert"])
+    else:
+        attn_ms += stage_ms["dq"] + stage_ms["dkdv"] + stage_ms["dkdv_vert"]
     attn_tflops = eff_flops / (attn_ms * 1e-3) / 1e12
 
     # Roofline of the dominant kernel. Each timed kernel stage below is exactly
@@ -255,6 +279,7 @@ def main():
         "inputs": cfg.dtype,
         "operands": ("fp16 copies of the bf16 inputs (exact; converted inside the step), single fp16 P/dS, "
                      "fp32 accumulation") if f16 else f"{cfg.dtype} inputs as given",
+        "bwd_streams": args.bwd_streams,
         "config": {"workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "seq_len": N, "head_dim": D,
                    "top_p": cfg.top_p, "last_q": cfg.last_q, "backward": cfg.backward, "mean_c": cfg.c,
                    "seed": cfg.seed},
@@ -366,6 +391,7 @@ def ring_report(args, cfg):
            "unit": "ms", "workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "seq_len": N, "P": P, "head_dim": D,
            "dtype": cfg.dtype, "data": "synthetic", "reps": args.ring_reps, "gen_s": round(gen_s, 1),
            "operands": args.operands if cfg.dtype == "bf16" and D == 128 else cfg.dtype,
+           "bwd_streams": args.bwd_streams,
            "communication": "excluded (one GPU; every rank's steps run in turn)", "layouts": {}}
     for kind in args.layouts.split(","):
         perm = np.concatenate([layout_permutation(kind, N, P, r) for r in range(P)])
@@ -455,6 +481,24 @@ def ring_report(args, cfg):
         dq = torch.empty(Hq, QB * 64, D, device=dev)
         dk = torch.zeros(P, Hkv, QB * 64, D, device=dev)   # per source shard
         dv = torch.zeros(P, Hkv, QB * 64, D, device=dev)
+        side = torch.cuda.Stream(device=dev) if args.bwd_streams == 2 else None   # default priority
+
+        def bwd_step(qr, kc, vc, dor, m, dks, dvs):
+            """One step's backward: one launch sequence, or with two streams dQ on
+            the side stream concurrently with the dK/dV parts (the step's end
+            event on the launch stream waits for both)."""
+            if side is None:
+                vs.vs_attn_bwd(qr, kc, vc, dor, lse, delta, m, cfg.scale, dq, dks, dvs, stream)
+                return
+            fork, join = torch.cuda.Event(), torch.cuda.Event()
+            fork.record(stream)
+            side.wait_event(fork)
+            vs.vs_attn_bwd_parts(qr, kc, vc, dor, lse, delta, m, cfg.scale, dq, dks, dvs, vs.VS_BWD_DQ, side)
+            join.record(side)
+            vs.vs_attn_bwd_parts(qr, kc, vc, dor, lse, delta, m, cfg.scale, dq, dks, dvs,
+                                 vs.VS_BWD_DKDV | vs.VS_BWD_DKDV_VERT, stream)
+            stream.wait_event(join)
+
         for rep in range(-1, args.ring_reps):       # rep -1: warm-up
             dk.zero_()
             dv.zero_()
@@ -478,8 +522,8 @@ def ring_report(args, cfg):
                 for st in range(P):
                     src = (r - st) % P
                     cols = slice(src * QB * 64, (src + 1) * QB * 64)
-                    ebs.append(timed(lambda: vs.vs_attn_bwd(qr, ak[:, cols], av[:, cols], dor, lse, delta, masks[st],
-                                                            cfg.scale, dq, dk[src], dv[src], stream)))
+                    ebs.append(timed(lambda: bwd_step(qr, ak[:, cols], av[:, cols], dor, masks[st], dk[src],
+                                                      dv[src])))
                 torch.cuda.synchronize()
                 if rep >= 0:
                     for st in range(P):
