@@ -52,6 +52,8 @@ def parse():
                     help="2: run the dQ part on a second stream, concurrently with the dK/dV parts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-budgets", action="store_true", help="skip the budget-rule report (after the timed steps)")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the per-kv-head index / head-pair forward report (after the timed steps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-probe", action="store_true", help="run only a 1 GiB device copy (counter scaling)")
     ap.add_argument("--layouts", default="striped,zigzag", help="ring simulation: layouts to compare")
@@ -268,6 +270,10 @@ def main():
     budgets = None if args.no_budgets else budget_report(vs, torch, Hq, Hkv, N, lay, vert_s, slash_s, cfg.top_p,
                                                          stream)
 
+    packed = None
+    if not args.no_packed and D == 128 and (Hq // Hkv) % 2 == 0 and cfg.dtype == "bf16":
+        packed = packed_report(vs, torch, cfg, lay, vert_s, slash_s, aq, ak, av, o, lse, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, host, vidx, vcnt, sidx, scnt, args.cpu_seconds, tflops_unit=True)
@@ -290,9 +296,57 @@ def main():
         "active_entries": A, "active_slash_tiles": A_slash, "active_vertical": A_vert,
         "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
         "strict_algorithmic_tflops": round(strict_tflops, 3), "index_pass": index_pass,
-        "roofline": roofline, "cpu_baseline": cpu, "budgets": budgets, "gen_s": round(gen_s, 1),
+        "roofline": roofline, "cpu_baseline": cpu, "budgets": budgets, "gqa_packed": packed,
+        "gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def packed_report(vs, torch, cfg, lay, vert_s, slash_s, q, k, v, o, lse, stream, reps=10):
+    """The per-kv-head index (one top-p per kv head on its q heads' mean
+    scores) on the workload's own scores, and the sparse forward on it run
+    two ways: one q head per workgroup (vs_attn_fwd) and two q heads of a kv
+    group per workgroup sharing the K/V tile copies (vs_attn_fwd_packed).
+    Mean kernel time over `reps` launches each."""
+    dev = vert_s.device
+    N, Hq, Hkv = cfg.N, cfg.Hq, cfg.Hkv
+    T = N // 64
+    vidx = torch.empty(Hq, N, dtype=torch.int32, device=dev)
+    sidx = torch.empty(Hq, T, dtype=torch.int32, device=dev)
+    vcnt, scnt = (torch.empty(Hq, dtype=torch.int32, device=dev) for _ in range(2))
+    gws = torch.empty(vs.index_select_group_workspace_size(Hq, Hkv, N), dtype=torch.uint8, device=dev)
+    vs.vs_index_select_group(vert_s, slash_s, Hq, Hkv, N, cfg.top_p, vidx, vcnt, sidx, scnt, gws, stream)
+    torch.cuda.synchronize()
+    m = vs.Mask(Hq, Hkv, lay, tile_cap=Hq * T * (int(scnt.max().item()) + 1))
+    vs.vs_block_mask(vidx, vcnt, sidx, scnt, 0, 0, m, stream)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    t_sel = timed(lambda: vs.vs_index_select_group(vert_s, slash_s, Hq, Hkv, N, cfg.top_p, vidx, vcnt, sidx, scnt,
+                                                   gws, stream))
+    t1 = timed(lambda: vs.vs_attn_fwd(q, k, v, m, cfg.scale, o, lse, 0, stream))
+    o1 = o.clone()
+    t2 = timed(lambda: vs.vs_attn_fwd_packed(q, k, v, m, cfg.scale, o, lse, status, 0, stream))
+    arr = m.arrays()
+    if int(arr["status"].item()) != 0 or int(status.item()) != 0:
+        raise RuntimeError("packed report: mask or pair status")
+    same = bool(torch.equal(o1, o))
+    A = int(arr["n_active"].sum().item())
+    f = 4 * cfg.D * A
+    return {"select_ms": round(t_sel, 4), "mean_verticals": round(float(vcnt.float().mean()), 1),
+            "mean_slashes": round(float(scnt.float().mean()), 1),
+            "sparsity": round(1.0 - A / (Hq * N * (N + 1) // 2), 5),
+            "fwd_ms": round(t1, 4), "fwd_packed_ms": round(t2, 4),
+            "fwd_tflops": round(f / (t1 * 1e-3) / 1e12, 2), "fwd_packed_tflops": round(f / (t2 * 1e-3) / 1e12, 2),
+            "packed_equals_unpacked": same}
 
 
 def budget_report(vs, torch, Hq, Hkv, N, lay, vert_s, slash_s, top_p, stream, target=0.95, reps=20):

@@ -30,7 +30,7 @@ EXPORTED = [
     "vs_status_string", "vs_index_workspace_size", "vs_index_build", "vs_index_rank_stats", "vs_index_rank_mass",
     "vs_index_select_workspace_size", "vs_index_select", "vs_index_select_budget", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
-    "vs_convert_f16",
+    "vs_convert_f16", "vs_index_select_group_workspace_size", "vs_index_select_group", "vs_attn_fwd_packed",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
 
@@ -102,6 +102,13 @@ def lib():
         L.vs_attn_fwd.argtypes = [VsTensor, VsTensor, VsTensor, ctypes.POINTER(VsMask), f32, vp, vp, i32, vp]
         L.vs_merge_lse.restype = i32
         L.vs_merge_lse.argtypes = [vp, vp, vp, vp, i32, i64, i32, vp]
+        L.vs_index_select_group_workspace_size.restype = sz
+        L.vs_index_select_group_workspace_size.argtypes = [i32, i32, i64]
+        L.vs_index_select_group.restype = i32
+        L.vs_index_select_group.argtypes = [vp, vp, i32, i32, i64, f32, vp, vp, vp, vp, vp, sz, vp]
+        L.vs_attn_fwd_packed.restype = i32
+        L.vs_attn_fwd_packed.argtypes = [VsTensor, VsTensor, VsTensor, ctypes.POINTER(VsMask), f32, vp, vp, i32, vp,
+                                         vp]
         L.vs_convert_f16.restype = i32
         L.vs_convert_f16.argtypes = [vp, vp, i64, vp, vp]
         L.vs_attn_bwd_prep.restype = i32
@@ -260,6 +267,23 @@ def vs_block_mask(vert_idx, vert_cnt, slash_idx, slash_cnt, rank, step, mask: Ma
 def vs_attn_fwd(q, k, v, mask: Mask, scale, o, lse, accumulate=0, stream=None):
     _check(lib().vs_attn_fwd(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), ctypes.byref(mask.desc), scale,
                              _cptr(o), _cptr(lse), int(accumulate), _stream(stream)), "vs_attn_fwd")
+
+
+def vs_attn_fwd_packed(q, k, v, mask: Mask, scale, o, lse, status, accumulate=0, stream=None):
+    _check(lib().vs_attn_fwd_packed(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), ctypes.byref(mask.desc),
+                                    scale, _cptr(o), _cptr(lse), int(accumulate), _cptr(status), _stream(stream)),
+           "vs_attn_fwd_packed")
+
+
+def index_select_group_workspace_size(Hq, Hkv, n_global):
+    return lib().vs_index_select_group_workspace_size(Hq, Hkv, n_global)
+
+
+def vs_index_select_group(vert_score, slash_score, Hq, Hkv, n_global, top_p, vert_idx, vert_cnt, slash_idx,
+                          slash_cnt, ws, stream=None):
+    _check(lib().vs_index_select_group(_cptr(vert_score), _cptr(slash_score), Hq, Hkv, n_global, top_p,
+                                       _cptr(vert_idx), _cptr(vert_cnt), _cptr(slash_idx), _cptr(slash_cnt),
+                                       _cptr(ws), ws.numel(), _stream(stream)), "vs_index_select_group")
 
 
 def vs_merge_lse(o_acc, lse_acc, o_step, lse_step, stream=None):

@@ -187,6 +187,22 @@ int vs_index_select(const float* vert_score, const float* slash_score, int Hq, i
                                 vert_cnt, slash_idx, slash_cnt, ws, ws_bytes, stream);
 }
 
+size_t vs_index_select_group_workspace_size(int Hq, int Hkv, int64_t n_global) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_global <= 0 || n_global % 64) return 0;
+  return group_select_workspace_bytes(Hkv, n_global);
+}
+
+int vs_index_select_group(const float* vert_score, const float* slash_score, int Hq, int Hkv, int64_t n_global,
+                          float top_p, int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!vert_score || !slash_score || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt || !ws) return VS_ERR_ARG;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || is_nan(top_p) || n_global <= 0) return VS_ERR_ARG;
+  if (n_global % 64 || n_global > ((int64_t)1 << 30)) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < group_select_workspace_bytes(Hkv, n_global)) return VS_ERR_WORKSPACE;
+  return launch_index_select_group(vert_score, slash_score, Hq, Hkv, n_global, top_p, vert_idx, vert_cnt, slash_idx,
+                                   slash_cnt, ws, ws_bytes, (hipStream_t)stream);
+}
+
 size_t vs_mask_bytes(int Hq, int Hkv, vs_layout lay, int64_t tile_cap) {
   if (Hq <= 0 || Hkv <= 0 || tile_cap < 0 || check_layout(lay) != VS_OK) return 0;
   return mask_layout(Hq, lay, tile_cap).total;
@@ -261,6 +277,18 @@ int vs_attn_fwd(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float s
   if (!finite_positive(scale)) return VS_ERR_ARG;
   return launch_attn_fwd(q.dtype, q.D, view(q), view(k), view(v), m, scale, o, lse, accumulate,
                          (hipStream_t)stream);
+}
+
+int vs_attn_fwd_packed(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float scale, float* o, float* lse,
+                       int accumulate, int32_t* status, void* stream) {
+  int st;
+  if ((st = check_attn(q, k, v, m)) != VS_OK) return st;
+  if (!o || !lse || !status || !aligned16(o)) return VS_ERR_ARG;
+  if (accumulate != 0 && accumulate != 1) return VS_ERR_ARG;
+  if (!finite_positive(scale)) return VS_ERR_ARG;
+  if ((q.dtype != VS_BF16 && q.dtype != VS_F16) || q.D != 128 || (m->Hq / m->Hkv) % 2) return VS_ERR_UNSUPPORTED;
+  return launch_attn_fwd_packed(q.dtype, view(q), view(k), view(v), m, scale, o, lse, accumulate, status,
+                                (hipStream_t)stream);
 }
 
 int vs_merge_lse(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step, int Hq, int64_t Nq,

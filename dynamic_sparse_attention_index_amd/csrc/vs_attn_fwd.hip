@@ -32,6 +32,7 @@ struct FwdArgs {
   const int32_t* tile_ptr; const int32_t* tile_col;
   const int32_t* vloc; const int32_t* vert_end; const uint32_t* slash_bits;
   float* o; float* lse;
+  int32_t* status;   // head-pair kernel: written VS_ERR_ARG if a pair's active sets differ
   int Hq, Hkv, QB, KB, W, kind, P, rank, src, accumulate;
   float scale_log2;
 };
@@ -289,14 +290,20 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 //
 // F16: the inputs are fp16 (exact copies of bf16 data, see vs_convert_f16)
 // and P is one fp16 operand, so P.V takes one MFMA instead of the hi + lo pair.
-template <bool F16>
+//
+// HP = 2 (grouped-query packing): two q heads of one kv group share the
+// workgroup (eight waves, four per head) and every K/V tile copy, which the
+// first head's waves issue. Valid when the two heads have the same active
+// set (an index selected per kv head); each workgroup checks that its pair's
+// lists agree and otherwise writes VS_ERR_ARG to a.status and returns.
+template <bool F16, int HP>
 __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   constexpr int D = TD;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 V1[TILE_ELEMS];
-  __shared__ float xs[2 * 2 * 64 * 2];
+  __shared__ float xs[HP * 2 * 2 * 64 * 2];
   // descriptor and row thresholds of tile t live in slot t % 3 from the
   // descriptor copy (step t - 3) to the softmax (step t)
   __shared__ int thr_sh[3][BLK];
@@ -314,16 +321,34 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hs = wave8 >> 2;                 // head slot in the workgroup (0 unless HP = 2)
+  const int wave = wave8 & 3;                // wave among its head's four
   const int g4 = lane >> 4, n16 = lane & 15;
   const int rh = wave & 1, kh = wave >> 1;   // row half, key half
   int rank_i, hh_i, g_i;
-  if (!xcd_group_item(blockIdx.x, a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv, &rank_i, &hh_i, &g_i)) return;
+  if (!xcd_group_item(blockIdx.x, a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv / HP, &rank_i, &hh_i, &g_i)) return;
   const int I = a.QB - 1 - rank_i;
-  const int h = g_i * (a.Hq / a.Hkv) + hh_i;
-  const int kvh = h / (a.Hq / a.Hkv);
-  const int64_t u = (int64_t)h * a.QB + I;
+  const int h0 = g_i * (a.Hq / a.Hkv) + HP * hh_i;   // the workgroup's first head: its lists drive the walk
+  const int h = h0 + hs;
+  const int kvh = g_i;
+  const int64_t u = (int64_t)h0 * a.QB + I;
   const int64_t row_base = (int64_t)I * BLK + 32 * rh;   // this wave's first query row
+  if constexpr (HP == 2) {
+    const int64_t u1 = u + a.QB;
+    const int t0 = a.tile_ptr[u], nt0 = a.tile_ptr[u + 1] - t0, ve0 = a.vert_end[u];
+    const int t1 = a.tile_ptr[u1], nt1 = a.tile_ptr[u1 + 1] - t1, ve1 = a.vert_end[u1];
+    int mism = (nt0 != nt1 || ve0 != ve1) ? 1 : 0;
+    if (!mism) {
+      for (int i = tid; i < nt0; i += HP * FWD_THREADS) mism |= a.tile_col[t0 + i] != a.tile_col[t1 + i];
+      const int32_t* v0 = a.vloc + (int64_t)h0 * a.KB * BLK;
+      for (int i = tid; i < ve0; i += HP * FWD_THREADS) mism |= v0[i] != v0[(int64_t)a.KB * BLK + i];
+    }
+    if (__syncthreads_or(mism)) {
+      if (tid == 0) *a.status = VS_ERR_ARG;
+      return;
+    }
+  }
 
   const bf16* qb = (const bf16*)a.q + h * a.qsh;
   const char* kbase = (const char*)((const bf16*)a.k + kvh * a.ksh);
@@ -332,13 +357,13 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   const DmaLane dl = dma_lane(wave, lane);
 
   BlockTiles bt;
-  bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
+  bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h0 * a.KB * BLK; bt.sbits = sbits;
   bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
   bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
   bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
   const int total = bt.total;
-  const uint32_t* sbg = a.slash_bits + (int64_t)h * a.W;
-  for (int w = tid; w < a.W; w += FWD_THREADS) sbits[w] = sbg[w];
+  const uint32_t* sbg = a.slash_bits + (int64_t)h0 * a.W;
+  for (int w = tid; w < a.W; w += HP * FWD_THREADS) sbits[w] = sbg[w];
 
   bf16x8 qf[2][4];
 #pragma unroll
@@ -365,11 +390,11 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
     if (!bt.vert(t)) {
       int mode;
       const int r0 = bt.tile_row(slot, mode);
-      dma_tile_rows(ks, kbase + (int64_t)r0 * krb, krb, dl, wave);
+      if (hs == 0) dma_tile_rows(ks, kbase + (int64_t)r0 * krb, krb, dl, wave);
     } else {
       int rows[4];
       bt.vert_rows(t, slot, rows, thr, wave, lane, tid);
-      dma_tile_gather(ks, kbase, rows, krb, dl, wave);
+      if (hs == 0) dma_tile_gather(ks, kbase, rows, krb, dl, wave);
     }
     if (tid < BLK) thr_sh[t % 3][tid] = thr;
   };
@@ -379,12 +404,14 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
     const int* slot = desc_sh[t % 3];
     if (!bt.vert(t)) {
       const int r0 = bt.tile_row(slot, mode_pend);
-      dma_tile_rows(vs_, vbase + (int64_t)r0 * vrb, vrb, dl, wave);
+      if (hs == 0) dma_tile_rows(vs_, vbase + (int64_t)r0 * vrb, vrb, dl, wave);
     } else {
-      int rows[4];
+      if (hs == 0) {
+        int rows[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
-      dma_tile_gather(vs_, vbase, rows, vrb, dl, wave);
+        for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+        dma_tile_gather(vs_, vbase, rows, vrb, dl, wave);
+      }
       mode_pend = 1;
     }
   };
@@ -513,7 +540,7 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
     const int mode_i = mode_pend;
     if (i + 1 < total) issue_v.template operator()<q>(i + 1);
     if (i + 2 < total) issue_k.template operator()<p>(i + 2);
-    if (i + 3 < total) bt.desc_copy(i + 3, desc_sh[i % 3], wave, lane);
+    if (i + 3 < total) bt.desc_copy(i + 3, desc_sh[i % 3], wave8, lane);
     // (the last step computes a next S from a stale stage and drops it)
     f32x4 s_next[2][2];
     softmax_pv.template operator()<p, q>(s_cur, mode_i, thr_sh[i % 3], s_next);
@@ -526,7 +553,7 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   if (total > 0) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
-      if (t < total) bt.desc_copy(t, desc_sh[t], wave, lane);
+      if (t < total) bt.desc_copy(t, desc_sh[t], wave8, lane);
     wait_all_mem();
     __syncthreads();
     issue_k.template operator()<0>(0);
@@ -546,22 +573,22 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   for (int rs = 0; rs < 2; ++rs) l_run[rs] = group4_sum(l_run[rs]);
   __syncthreads();  // every wave is past its last read of the stages
   // [2 rs][8 dt][64 lanes] f32x4 = 16 KiB per row half: K stage 0 / V stage 0
-  float* xo = (float*)(rh == 0 ? K0 : V0);
+  float* xo = (float*)(hs == 0 ? (rh == 0 ? K0 : V0) : (rh == 0 ? K1 : V1));
   if (kh == 1) {
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) *(f32x4*)(xo + ((rs * 8 + dt) * 64 + lane) * 4) = acc[rs][dt];
-      xs[((rh * 2 + rs) * 64 + lane) * 2 + 0] = m_run[rs];
-      xs[((rh * 2 + rs) * 64 + lane) * 2 + 1] = l_run[rs];
+      xs[(((hs * 2 + rh) * 2 + rs) * 64 + lane) * 2 + 0] = m_run[rs];
+      xs[(((hs * 2 + rh) * 2 + rs) * 64 + lane) * 2 + 1] = l_run[rs];
     }
   }
   __syncthreads();
   if (kh == 1) return;
 #pragma unroll
   for (int rs = 0; rs < 2; ++rs) {
-    const float m1 = xs[((rh * 2 + rs) * 64 + lane) * 2 + 0];
-    const float l1 = xs[((rh * 2 + rs) * 64 + lane) * 2 + 1];
+    const float m1 = xs[(((hs * 2 + rh) * 2 + rs) * 64 + lane) * 2 + 0];
+    const float l1 = xs[(((hs * 2 + rh) * 2 + rs) * 64 + lane) * 2 + 1];
     const float m0 = m_run[rs];
     const float mm = fmaxf(m0, m1);
     const float mb = (mm == -INFINITY) ? 0.f : mm;
@@ -603,8 +630,16 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
     }
   }
 }
-__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) { attn_fwd_d128<false>(a); }
-__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_f16_d128_kernel(FwdArgs a) { attn_fwd_d128<true>(a); }
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdArgs a) {
+  attn_fwd_d128<false, 1>(a);
+}
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_f16_d128_kernel(FwdArgs a) { attn_fwd_d128<true, 1>(a); }
+__global__ void __launch_bounds__(2 * FWD_THREADS, 1) attn_fwd_pair_bf16_d128_kernel(FwdArgs a) {
+  attn_fwd_d128<false, 2>(a);
+}
+__global__ void __launch_bounds__(2 * FWD_THREADS, 1) attn_fwd_pair_f16_d128_kernel(FwdArgs a) {
+  attn_fwd_d128<true, 2>(a);
+}
 
 int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* m, float scale,
                     float* o, float* lse, int accumulate, hipStream_t stream) {
@@ -612,7 +647,7 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.q = q.ptr; a.k = k.ptr; a.v = v.ptr;
   a.qsh = q.sh; a.qsn = q.sn; a.ksh = k.sh; a.ksn = k.sn; a.vsh = v.sh; a.vsn = v.sn;
   a.tile_ptr = m->tile_ptr; a.tile_col = m->tile_col; a.vloc = m->vloc; a.vert_end = m->vert_end;
-  a.slash_bits = m->slash_bits; a.o = o; a.lse = lse;
+  a.slash_bits = m->slash_bits; a.o = o; a.lse = lse; a.status = nullptr;
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
@@ -627,6 +662,27 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);
   else return VS_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+// Two q heads per workgroup sharing the K/V tile copies (requires equal active
+// sets within each head pair; checked per workgroup, reported in *status).
+int launch_attn_fwd_packed(int dtype, TView q, TView k, TView v, const vs_mask* m, float scale, float* o,
+                           float* lse, int accumulate, int32_t* status, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr;
+  a.qsh = q.sh; a.qsn = q.sn; a.ksh = k.sh; a.ksn = k.sn; a.vsh = v.sh; a.vsn = v.sn;
+  a.tile_ptr = m->tile_ptr; a.tile_col = m->tile_col; a.vloc = m->vloc; a.vert_end = m->vert_end;
+  a.slash_bits = m->slash_bits; a.o = o; a.lse = lse; a.status = status;
+  a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
+  a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
+  a.scale_log2 = scale * LOG2E;
+  if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
+  const int64_t krows = (int64_t)m->KB * BLK;
+  if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
+  const dim3 grid(xcd_group_grid(m->Hkv, m->QB, QMAJOR_BPC, m->Hq / m->Hkv / 2)), block(2 * FWD_THREADS);
+  if (dtype == VS_F16) hipLaunchKernelGGL(attn_fwd_pair_f16_d128_kernel, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(attn_fwd_pair_bf16_d128_kernel, grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 

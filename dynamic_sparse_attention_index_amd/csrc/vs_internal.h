@@ -21,6 +21,9 @@ int launch_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t 
 int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* m, float scale,
                     float* o, float* lse, int accumulate, hipStream_t stream);
 
+int launch_attn_fwd_packed(int dtype, TView q, TView k, TView v, const vs_mask* m, float scale, float* o,
+                           float* lse, int accumulate, int32_t* status, hipStream_t stream);
+
 int launch_merge(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
                  int Hq, int64_t Nq, int D, hipStream_t stream);
 
@@ -49,6 +52,12 @@ int launch_index_rank_mass(int dtype, int D, TView q_last, int Hq, int last_q, T
                            float* slash_score, void* ws, size_t ws_bytes, hipStream_t stream);
 
 size_t select_workspace_bytes(int Hq, int64_t n_global);
+
+size_t group_select_workspace_bytes(int Hkv, int64_t n_global);
+
+int launch_index_select_group(const float* vert_score, const float* slash_score, int Hq, int Hkv, int64_t N,
+                              float top_p, int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx,
+                              int32_t* slash_cnt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // budget: VS_BUDGET_TOP_P / VS_BUDGET_TOP_K / VS_BUDGET_JOINT_TOP_P (0 / 1 / 2)
 int launch_index_select(const float* vert_score, const float* slash_score, int Hq, int64_t n_global, int budget,

@@ -217,6 +217,22 @@ int vs_index_select(const float* vert_score, const float* slash_score, int Hq, i
                     int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx, int32_t* slash_cnt,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Per-kv-head variant of the selection (grouped-query attention; the review
+ * fixes one index per attention head, page 1, section 三.2 item 1, and this
+ * variant takes the head to be the kv head): for every kv group g of R =
+ * Hq / Hkv consecutive q heads, v_g = (1/R) sum_{h in g} v_h and likewise
+ * s_g (fp32, heads added in ascending order, then scaled by 1/R); the top-p
+ * rule of vs_index_select is applied once per group; every q head of the
+ * group receives the group's lists. Outputs as vs_index_select ([Hq, ...]).
+ * All q heads of a group then share one active set, which is what
+ * vs_attn_fwd_packed requires. ws: vs_index_select_group_workspace_size
+ * bytes. Errors as vs_index_select, plus VS_ERR_ARG if Hkv <= 0 or
+ * Hq % Hkv != 0. */
+size_t vs_index_select_group_workspace_size(int Hq, int Hkv, int64_t n_global);
+int vs_index_select_group(const float* vert_score, const float* slash_score, int Hq, int Hkv, int64_t n_global,
+                          float top_p, int32_t* vert_idx, int32_t* vert_cnt, int32_t* slash_idx,
+                          int32_t* slash_cnt, void* ws, size_t ws_bytes, void* stream);
+
 /* Budget kinds of vs_index_select_budget. */
 #define VS_BUDGET_TOP_P 0        /* separate top-p on v and on s (vs_index_select) */
 #define VS_BUDGET_TOP_K 1        /* a fixed count per head */
@@ -274,6 +290,18 @@ int vs_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert
  *   vs_merge_lse), without writing the step's own output. */
 int vs_attn_fwd(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float scale,
                 float* o, float* lse, int accumulate, void* stream);
+
+/* vs_attn_fwd with two q heads per workgroup: q heads 2i and 2i + 1 of
+ * every kv group share the workgroup and every K/V tile copy (half the tile
+ * traffic of vs_attn_fwd). Same arguments, outputs and results as
+ * vs_attn_fwd, for masks whose two heads of each such pair have identical
+ * active sets (built from vs_index_select_group lists). Each workgroup
+ * compares its pair's tile list and vertical columns and, if they differ,
+ * writes VS_ERR_ARG to the device word *status (set to VS_OK by the caller)
+ * and leaves its rows of o / lse unwritten. Supported: bf16 or fp16 operands,
+ * D = 128, Hq / Hkv even (else VS_ERR_UNSUPPORTED). */
+int vs_attn_fwd_packed(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, float scale,
+                       float* o, float* lse, int accumulate, int32_t* status, void* stream);
 
 /* In-place log-sum-exp merge (Ring Attention overview, section 2.1):
  *   L = log(e^La + e^Lb), O = e^(La-L) Oa + e^(Lb-L) Ob, (0, -inf) = identity.

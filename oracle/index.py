@@ -22,7 +22,8 @@ Readings (the pages leave these open):
 
 Two other budgets on the same scores: a fixed count per head (select_top_k)
 and one top-p over the pooled vertical and slash candidates
-(select_joint_top_p).
+(select_joint_top_p). select_group_top_p selects once per kv head, on the
+mean scores of its q heads (group_scores).
 """
 import numpy as np
 
@@ -136,6 +137,33 @@ def select_joint_top_p(v: np.ndarray, s: np.ndarray, p: float):
     n = v.shape[0]
     kept = select_top_p(np.concatenate([v, s]), p)
     return kept[kept < n], kept[kept >= n] - n
+
+
+def group_scores(x: np.ndarray, Hkv: int) -> np.ndarray:
+    """Per-kv-head scores for grouped-query attention: the mean over the
+    R = Hq / Hkv consecutive q heads that share kv head g (fp64).
+
+    The review fixes one sparse index per attention head (page 1, section
+    三.2 item 1); this variant takes the head to be the kv head, so every q
+    head of a group attends the same positions."""
+    x = np.asarray(x, dtype=np.float64)
+    Hq = x.shape[0]
+    assert Hq % Hkv == 0
+    return x.reshape(Hkv, Hq // Hkv, -1).mean(axis=1)
+
+
+def select_group_top_p(v: np.ndarray, s: np.ndarray, Hkv: int, p: float):
+    """Top-p (select_top_p) on the per-kv-head scores, the lists handed to
+    every q head of the group: returns (vert, slash), one list per q head.
+    v, s: [Hq, N] and [Hq, T] scores; the group scores are rounded to fp32
+    before the selection (the selection rule takes fp32 scores)."""
+    Hq = v.shape[0]
+    R = Hq // Hkv
+    gv = group_scores(v, Hkv).astype(np.float32)
+    gs = group_scores(s, Hkv).astype(np.float32)
+    vg = [select_top_p(gv[g], p) for g in range(Hkv)]
+    sg = [select_top_p(gs[g], p) for g in range(Hkv)]
+    return [vg[h // R] for h in range(Hq)], [sg[h // R] for h in range(Hq)]
 
 
 def build_index(q_last, k, scale, n_global, top_p):

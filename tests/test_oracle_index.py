@@ -279,3 +279,46 @@ def test_merge_row_stats_handles_empty_ranks():
     lse = oi.merge_row_stats(list(zip(m, l)))
     assert lse[0, 1] == -np.inf
     np.testing.assert_allclose(lse[0, 0], np.log(2.0 * np.exp(1.0) + 1.5 * np.exp(3.0)), rtol=1e-15)
+
+
+def test_select_group_hand_case():
+    """Per-kv-head selection, hand-derived: q heads 0, 1 share kv head 0 and
+    q heads 2, 3 kv head 1 (consecutive q heads form a group). Group means:
+    [0.4, 0.4, 0.1, 0.1] and [0.1, 0.1, 0.4, 0.4]; at p = 0.75 the two 0.4
+    columns (0.8) are the fewest that reach it. Grouping heads h % Hkv
+    instead would pair heads 0 and 2 and give other lists."""
+    v = np.array([[0.7, 0.1, 0.1, 0.1], [0.1, 0.7, 0.1, 0.1],
+                  [0.1, 0.1, 0.1, 0.7], [0.1, 0.1, 0.7, 0.1]], dtype=np.float32)
+    s = v.copy()
+    vert, slash = oi.select_group_top_p(v, s, 2, 0.75)
+    for h, exp in enumerate([[0, 1], [0, 1], [2, 3], [2, 3]]):
+        assert vert[h].tolist() == exp and slash[h].tolist() == exp
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_group_reductions(seed):
+    """One q head per kv head is the per-head rule; with dyadic scores (exact
+    means) the group lists equal the top-p of the group's summed scores, and
+    every q head of a group gets the same list."""
+    rng = np.random.default_rng(500 + seed)
+    Hq, N = 8, 256
+    v = (rng.integers(0, 64, (Hq, N)) * rng.integers(0, 2, (Hq, N))).astype(np.float32) / 1024
+    s = rng.integers(0, 64, (Hq, N // 4)).astype(np.float32) / 1024
+    p = float(rng.uniform(0.3, 0.99))
+    vert, slash = oi.select_group_top_p(v, s, Hq, p)
+    for h in range(Hq):
+        assert np.array_equal(vert[h], oi.select_top_p(v[h], p))
+        assert np.array_equal(slash[h], oi.select_top_p(s[h], p))
+    for Hkv in (1, 2, 4):
+        R = Hq // Hkv
+        vert, slash = oi.select_group_top_p(v, s, Hkv, p)
+        for g in range(Hkv):
+            sv = v[g * R:(g + 1) * R].astype(np.float64).sum(axis=0) / R * (R // 2 if R > 1 else 1)
+            # R is a power of two and the scores dyadic: the mean, and the sum
+            # scaled by 2^k, are exact in fp32 and select the same set
+            sel = oi.select_top_p(np.float32(1.0) * (v[g * R:(g + 1) * R].astype(np.float64).mean(axis=0))
+                                  .astype(np.float32), p)
+            assert np.array_equal(sel, oi.select_top_p(sv.astype(np.float32), p))
+            for h in range(g * R, (g + 1) * R):
+                assert np.array_equal(vert[h], sel)
+                assert np.array_equal(slash[h], slash[g * R])
