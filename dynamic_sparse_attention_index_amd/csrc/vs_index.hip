@@ -26,7 +26,14 @@
 
 namespace vs {
 
-constexpr int IDX_SPLIT_TARGET = 256;    // workgroups per pass (over all kv heads)
+// Key-range splits per pass: about IDX_WAVE_TARGET waves over all q heads
+// (one wave per q head and split), i.e. two waves per SIMD on 256 CUs
+// whatever the group size (one wave per SIMD leaves the exponentials and the
+// scoring MFMAs of a wave to run back to back).
+constexpr int IDX_WAVE_TARGET = 2048;
+__host__ inline int64_t idx_nsplit(int Hq, int64_t ntiles) {
+  return std::min<int64_t>(ntiles, std::max<int64_t>(1, IDX_WAVE_TARGET / Hq));
+}
 
 struct IndexArgs {
   const void* q; const void* k;
@@ -688,7 +695,7 @@ size_t select_workspace_bytes(int Hq, int64_t n_global) {
 // the passes' partials and row LSE, then (256-byte aligned) the selection's
 static size_t index_pass_bytes(int Hq, int Hkv, int64_t n_global) {
   const int64_t T = n_global / BLK;
-  const int64_t nsplit = std::min<int64_t>(T, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
+  const int64_t nsplit = idx_nsplit(Hq, T);
   return ((size_t)(Hq * BLK * nsplit * 2 + Hq * BLK) * sizeof(float) + 255) & ~(size_t)255;
 }
 
@@ -711,7 +718,7 @@ static IndexArgs index_args(TView q_last, int Hq, int last_q, TView k, int Hkv, 
   a.NB = a.T / lay.P;
   a.rank_fixed = rank_fixed;
   a.ntiles = rank_fixed >= 0 ? a.NB : a.T;
-  a.nsplit = (int)std::min<int64_t>(a.ntiles, std::max<int64_t>(1, IDX_SPLIT_TARGET / Hkv));
+  a.nsplit = (int)idx_nsplit(Hq, a.ntiles);
   a.tiles_per = (a.ntiles + a.nsplit - 1) / a.nsplit;
   a.nsplit = (a.ntiles + a.tiles_per - 1) / a.tiles_per;
   a.scale_log2 = scale * LOG2E;
