@@ -126,7 +126,7 @@ def main():
     else:
         aq, ak, av, ado = q, k, v, do
 
-    stages = ("index", "mask", "convert_qkv", "fwd", "convert_do", "bwd_prep", "dq", "dkdv", "dkdv_vert")
+    stages = ("index", "mask", "convert_qkv", "fwd", "bwd_prep", "dq", "dkdv", "dkdv_vert")
     ev = {name: [] for name in stages}
     two = args.bwd_streams == 2 and cfg.backward
     side = torch.cuda.Stream(device=dev) if two else None    # default priority, like every stream here
@@ -150,11 +150,11 @@ def main():
         vs.vs_attn_fwd(aq, ak, av, mask, cfg.scale, o, lse, 0, stream)
         mark(4)
         if cfg.backward:
-            if f16:
-                vs.vs_convert_f16(do, do16, conv_status, stream)
+            if f16:     # delta and the fp16 copy of dO in one pass over dO
+                vs.vs_attn_bwd_prep_f16(o, do, do16, delta, conv_status, stream)
+            else:
+                vs.vs_attn_bwd_prep(o, ado, delta, stream)
             mark(5)
-            vs.vs_attn_bwd_prep(o, ado, delta, stream)
-            mark(6)
             # dq and the slash dk/dv write their outputs whole; the vertical part adds after them
             if two:
                 # dq (writes dq only) on the side stream, dk/dv parts on the launch stream
@@ -171,16 +171,16 @@ def main():
             else:
                 vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
                                      vs.VS_BWD_DQ | vs.VS_BWD_OVERWRITE, stream)
-            mark(7)
+            mark(6)
             vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv,
                                  vs.VS_BWD_DKDV | vs.VS_BWD_OVERWRITE, stream)
-            mark(8)
+            mark(7)
             vs.vs_attn_bwd_parts(aq, ak, av, ado, lse, delta, mask, cfg.scale, dq, dk, dv, vs.VS_BWD_DKDV_VERT,
                                  stream)
         else:
-            for i in (5, 6, 7, 8):
+            for i in (5, 6, 7):
                 mark(i)
-        mark(9)
+        mark(8)
         if two:
             stream.wait_event(join)
         if record:
@@ -217,7 +217,7 @@ def main():
     sparsity = 1.0 - A / total_causal
     eff_flops = (4 + (10 if cfg.backward else 0)) * D * A
     tflops = eff_flops / (ms_per_step * 1e-3) / 1e12
-    attn_ms = sum(stage_ms[x] for x in ("convert_qkv", "fwd", "convert_do", "bwd_prep"))
+    attn_ms = sum(stage_ms[x] for x in ("convert_qkv", "fwd", "bwd_prep"))
     if two:   # dq overlaps the dk/dv parts
         attn_ms += max(stage_ms["dq"], stage_ms["dkdv"] + stage_ms["dkdv_vert"])
     else:

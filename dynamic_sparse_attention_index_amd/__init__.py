@@ -31,6 +31,7 @@ EXPORTED = [
     "vs_index_select_workspace_size", "vs_index_select", "vs_index_select_budget", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
     "vs_convert_f16", "vs_index_select_group_workspace_size", "vs_index_select_group", "vs_attn_fwd_packed",
+    "vs_attn_bwd_prep_f16",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
 
@@ -109,6 +110,8 @@ def lib():
         L.vs_attn_fwd_packed.restype = i32
         L.vs_attn_fwd_packed.argtypes = [VsTensor, VsTensor, VsTensor, ctypes.POINTER(VsMask), f32, vp, vp, i32, vp,
                                          vp]
+        L.vs_attn_bwd_prep_f16.restype = i32
+        L.vs_attn_bwd_prep_f16.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, vp]
         L.vs_convert_f16.restype = i32
         L.vs_convert_f16.argtypes = [vp, vp, i64, vp, vp]
         L.vs_attn_bwd_prep.restype = i32
@@ -302,6 +305,15 @@ def vs_convert_f16(src, dst, status, stream=None):
         raise ValueError("src and dst differ in size")
     _check(lib().vs_convert_f16(_cptr(src), _cptr(dst), src.numel(), _cptr(status), _stream(stream)),
            "vs_convert_f16")
+
+
+def vs_attn_bwd_prep_f16(o, dout, dout_f16, delta, status, stream=None):
+    """delta from bf16 dout [Hq, Nq, D] (dense), writing its fp16 copy dout_f16."""
+    if dout.dtype != torch.bfloat16 or dout_f16.dtype != torch.float16 or dout.shape != dout_f16.shape:
+        raise ValueError("vs_attn_bwd_prep_f16 takes bfloat16 dout and a float16 dout_f16 of the same shape")
+    Hq, Nq, D = dout.shape
+    _check(lib().vs_attn_bwd_prep_f16(_cptr(o), _cptr(dout), _cptr(dout_f16), Hq, Nq, D, _cptr(delta),
+                                      _cptr(status), _stream(stream)), "vs_attn_bwd_prep_f16")
 
 
 def vs_attn_bwd_prep(o, dout, delta, stream=None):

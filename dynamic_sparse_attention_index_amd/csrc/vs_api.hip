@@ -317,6 +317,14 @@ int vs_attn_bwd_prep(const float* o, vs_tensor dout, float* delta, void* stream)
   return launch_bwd_prep(o, dout.dtype, view(dout), dout.H, dout.N, dout.D, delta, (hipStream_t)stream);
 }
 
+int vs_attn_bwd_prep_f16(const float* o, const void* dout, void* dout_f16, int Hq, int64_t Nq, int D, float* delta,
+                         int32_t* status, void* stream) {
+  if (!o || !dout || !dout_f16 || !delta || !status || Hq <= 0 || Nq <= 0) return VS_ERR_ARG;
+  if (D != 128 && D != 64) return VS_ERR_UNSUPPORTED;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dout_f16)) return VS_ERR_UNSUPPORTED;
+  return launch_bwd_prep_f16(o, dout, dout_f16, Hq, Nq, D, delta, status, (hipStream_t)stream);
+}
+
 int vs_attn_bwd_parts(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, const float* lse, const float* delta,
                       const vs_mask* m, float scale, float* dq, float* dk, float* dv, int parts, void* stream) {
   int st;

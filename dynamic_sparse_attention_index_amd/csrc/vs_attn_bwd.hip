@@ -1192,6 +1192,49 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 
+// delta[row] = dO[row] . O[row] from bf16 dO, writing the fp16 copy of dO
+// on the way (one read of dO instead of one for the copy and one for delta).
+// A value with a biased bf16 exponent >= 127 + 16 (|x| >= 65536, inf, NaN)
+// sets *status = VS_ERR_RANGE.
+__global__ void bwd_prep_f16_kernel(const float* o, const uint16_t* dout, uint16_t* dout16, int64_t rows, int D,
+                                    float* delta, int32_t* status) {
+  const int per = D / 4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = t / per;
+  const int c = (int)(t % per) * 4;
+  float x = 0.f;
+  bool bad = false;
+  if (r < rows) {
+    const f32x4 ov = *(const f32x4*)(o + r * D + c);
+    typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+    const u32x2 w = *(const u32x2*)(dout + r * D + c);
+    u32x2 h;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t e0 = (w[j] >> 7) & 0xffu, e1 = (w[j] >> 23) & 0xffu;
+      bad |= (e0 >= 143u) | (e1 >= 143u);
+      const float f0 = __builtin_bit_cast(float, w[j] << 16), f1 = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+      x += ov[2 * j] * f0;       // same accumulation order as bwd_prep_kernel
+      x += ov[2 * j + 1] * f1;
+      h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{f0, f1}, f16x2));
+    }
+    *(u32x2*)(dout16 + r * D + c) = h;
+  }
+  for (int off = per / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  if (r < rows && c == 0) delta[r] = x;
+  if (bad) *status = VS_ERR_RANGE;
+}
+
+int launch_bwd_prep_f16(const float* o, const void* dout, void* dout16, int Hq, int64_t Nq, int D, float* delta,
+                        int32_t* status, hipStream_t stream) {
+  const int64_t rows = (int64_t)Hq * Nq;
+  const int64_t n = rows * (D / 4);
+  const int tpb = 256;
+  hipLaunchKernelGGL(bwd_prep_f16_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0, stream, o,
+                     (const uint16_t*)dout, (uint16_t*)dout16, rows, D, delta, status);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
 // n floats (a multiple of 4) set to zero
 __global__ void zero_f32_kernel(float* p, int64_t n) {
   for (int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x); i < n; i += 4 * (int64_t)gridDim.x * blockDim.x)

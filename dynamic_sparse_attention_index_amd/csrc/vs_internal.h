@@ -29,6 +29,9 @@ int launch_merge(float* o_acc, float* lse_acc, const float* o_step, const float*
 
 int launch_convert_f16(const void* src, void* dst, int64_t n, int32_t* status, hipStream_t stream);
 
+int launch_bwd_prep_f16(const float* o, const void* dout, void* dout16, int Hq, int64_t Nq, int D, float* delta,
+                        int32_t* status, hipStream_t stream);
+
 int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, int D, float* delta,
                     hipStream_t stream);
 

@@ -332,6 +332,16 @@ int vs_convert_f16(const void* src, void* dst, int64_t n, int32_t* status, void*
  * softmax gradient), from the FINAL output o [Hq, Nq, D] fp32 contiguous. */
 int vs_attn_bwd_prep(const float* o, vs_tensor dout, float* delta, void* stream);
 
+/* vs_attn_bwd_prep for bf16 dO that also writes its fp16 copy (the operand
+ * of the fp16 backward kernels), reading dO once: dout [Hq, Nq, D] bf16
+ * contiguous (read), dout_f16 [Hq, Nq, D] fp16 contiguous (written, as
+ * vs_convert_f16 would), delta as vs_attn_bwd_prep (bit for bit the same as
+ * vs_attn_bwd_prep on either copy). Range errors as vs_convert_f16, in the
+ * device word *status. VS_ERR_ARG for null pointers or Hq, Nq <= 0;
+ * VS_ERR_UNSUPPORTED for D not in {64, 128} or misaligned buffers. */
+int vs_attn_bwd_prep_f16(const float* o, const void* dout, void* dout_f16, int Hq, int64_t Nq, int D,
+                         float* delta, int32_t* status, void* stream);
+
 /* Gradient contribution of the active entries of `m` (one ring step), using
  * the final lse [Hq, Nq] and delta [Hq, Nq] of the rank's rows:
  *   P = exp(q.k*scale - lse), dV += P^T dO, dS = P (dO.v - delta),

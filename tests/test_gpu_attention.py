@@ -290,3 +290,30 @@ def test_convert_f16_exact_and_range():
         vs.vs_convert_f16(y, out, status)
         torch.cuda.synchronize()
         assert int(status.item()) == vs.VS_ERR_RANGE, bad
+
+
+def test_bwd_prep_f16_matches_separate_calls():
+    """vs_attn_bwd_prep_f16 (delta and the fp16 dO copy in one pass) equals
+    vs_convert_f16 followed by vs_attn_bwd_prep, bit for bit; range errors
+    reach the status word."""
+    import dynamic_sparse_attention_index_amd as vs
+    rng = np.random.default_rng(17)
+    Hq, Nq, D = 3, 64 * 5, 128
+    o = torch.tensor(rng.standard_normal((Hq, Nq, D)), dtype=torch.float32, device="cuda")
+    do = torch.tensor(rng.standard_normal((Hq, Nq, D)) * 3, dtype=torch.float32).to(torch.bfloat16).cuda()
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    do16a = torch.empty(Hq, Nq, D, dtype=torch.float16, device="cuda")
+    do16b = torch.empty_like(do16a)
+    da, db = torch.empty(Hq, Nq, device="cuda"), torch.empty(Hq, Nq, device="cuda")
+    vs.vs_convert_f16(do, do16a, st)
+    vs.vs_attn_bwd_prep(o, do16a, da)
+    vs.vs_attn_bwd_prep_f16(o, do, do16b, db, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == vs.VS_OK
+    assert torch.equal(do16a.view(torch.int16), do16b.view(torch.int16)) and torch.equal(da, db)
+    ref = (o.double() * do.double()).sum(-1)
+    assert (da.double() - ref).abs().max().item() < 1e-3
+    do[1, 7, 5] = 1e6
+    vs.vs_attn_bwd_prep_f16(o, do, do16b, db, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == vs.VS_ERR_RANGE
