@@ -26,7 +26,9 @@
 namespace vs {
 
 constexpr int BWD_THREADS = 256;
-constexpr int VERT_SEG = 128;          // query blocks per vertical work item
+constexpr int VERT_SEG = 128;          // query blocks per vertical work item (at most)
+constexpr int VERT_SEG_MIN = 8;        // ... and at least, when the range is shortened
+constexpr int VERT_ITEMS_MIN = 2048;   // shorten the range until there are this many items
 constexpr int VERT_GRID = 2048;        // persistent workgroups for vertical columns
 
 struct BwdArgs {
@@ -1075,9 +1077,17 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
   const DmaLane dlane = dma_lane(wave, lane);
   const int g4 = lane >> 4, n16 = lane & 15;
   const int kh = wave >> 1, rh = wave & 1;
-  const int nseg = (a.QB + VERT_SEG - 1) / VERT_SEG;
-  int64_t nwork = 0;
-  for (int h = 0; h < a.Hq; ++h) nwork += (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+  // Query-block range per item: VERT_SEG blocks, halved (down to
+  // VERT_SEG_MIN) while there are fewer than VERT_ITEMS_MIN items, so a ring
+  // step with few vertical columns still spreads over the whole GPU instead
+  // of walking long ranges in a few workgroups. Every workgroup derives the
+  // same partition from the device-side counts.
+  int64_t nchunks = 0;
+  for (int h = 0; h < a.Hq; ++h) nchunks += (a.vloc_cnt[h] + BLK - 1) / BLK;
+  int seg_len = VERT_SEG;
+  while (seg_len > VERT_SEG_MIN && nchunks * ((a.QB + seg_len - 1) / seg_len) < VERT_ITEMS_MIN) seg_len >>= 1;
+  const int nseg = (a.QB + seg_len - 1) / seg_len;
+  const int64_t nwork = nchunks * nseg;
   const int grp = a.Hq / a.Hkv;
   const float sl2 = a.scale_log2;
   for (int64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
@@ -1096,8 +1106,8 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
     const int cnt = a.vloc_cnt[h];
     const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
     const int64_t gb_min = global_block(a.kind, a.P, a.KB, a.src, vl[chunk * BLK] / BLK);
-    const int I_lo = max(seg * VERT_SEG, blocks_upto(a.kind, a.P, a.QB, a.rank, gb_min - 1));
-    const int I_hi = min(a.QB, (seg + 1) * VERT_SEG);
+    const int I_lo = max(seg * seg_len, blocks_upto(a.kind, a.P, a.QB, a.rank, gb_min - 1));
+    const int I_hi = min(a.QB, (seg + 1) * seg_len);
     const int total = I_hi - I_lo;
     if (total <= 0) continue;
     __syncthreads();  // the previous item's exchange has been read
