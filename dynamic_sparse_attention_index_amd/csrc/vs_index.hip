@@ -193,6 +193,27 @@ __global__ void __launch_bounds__(512) index_rowstat_kernel(IndexArgs a) {
     f32x4 acc[4][4];
     score_tile<T, D>(Ks, qa, n16, g4, acc);
     const bool last = G == a.T - 1;
+    if (!last && a.last_q == BLK) {
+      // no masked entry in this tile (wave-uniform): the running maximum is
+      // taken on the raw scores (scale > 0 keeps their order) and every
+      // exponential is one fused multiply-add away from its score
+      #pragma unroll
+      for (int rs = 0; rs < 4; ++rs)
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float tmax = fmaxf(fmaxf(acc[rs][0][i], acc[rs][1][i]), fmaxf(acc[rs][2][i], acc[rs][3][i])) *
+                             a.scale_log2;
+          if (tmax > m[rs][i]) {
+            l[rs][i] *= __builtin_amdgcn_exp2f(m[rs][i] - tmax);
+            m[rs][i] = tmax;
+          }
+          #pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            l[rs][i] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[rs][kt][i], a.scale_log2, -m[rs][i]));
+        }
+      __syncthreads();
+      continue;
+    }
     #pragma unroll
     for (int rs = 0; rs < 4; ++rs)
       #pragma unroll
@@ -307,18 +328,29 @@ __global__ void __launch_bounds__(512) index_colsum_kernel(IndexArgs a) {
     f32x4 acc[4][4];
     score_tile<T, D>(Ks, qa, n16, g4, acc);
     const bool last = G == a.T - 1;
+    // no masked entry in this tile (wave-uniform): every scored row is live
+    // (its LSE is finite) and no key lies beyond it
+    const bool plain = !last && a.last_q == BLK;
     float col[4];
     #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       float c = 0.f;
-      #pragma unroll
-      for (int rs = 0; rs < 4; ++rs)
+      if (plain) {
         #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rs + 4 * g4 + i;
-          const bool act = lse[rs][i] > -INFINITY && !(last && 16 * kt + n16 > row0 + r);
-          if (act) c += __builtin_amdgcn_exp2f(acc[rs][kt][i] * a.scale_log2 - lse[rs][i]);
-        }
+        for (int rs = 0; rs < 4; ++rs)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i)
+            c += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[rs][kt][i], a.scale_log2, -lse[rs][i]));
+      } else {
+        #pragma unroll
+        for (int rs = 0; rs < 4; ++rs)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rs + 4 * g4 + i;
+            const bool act = lse[rs][i] > -INFINITY && !(last && 16 * kt + n16 > row0 + r);
+            if (act) c += __builtin_amdgcn_exp2f(acc[rs][kt][i] * a.scale_log2 - lse[rs][i]);
+          }
+      }
       c += __shfl_xor(c, 16, 64);
       c += __shfl_xor(c, 32, 64);
       col[kt] = c * inv_rows;
