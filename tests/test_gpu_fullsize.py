@@ -13,6 +13,7 @@ the small index tests). Checked per workload:
 The ring case runs one rank's full ring (every step) at P = 32.
 """
 import math
+import sys
 import time
 
 import numpy as np
@@ -31,7 +32,10 @@ TOL = 2e-2   # bf16 inputs, fp32 outputs (absolute)
 
 
 def _log(msg):
-    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    """Progress lines go to the process's own stderr, past pytest's output
+    capture, so a long full-size case keeps reporting its steps."""
+    sys.__stderr__.write(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}\n")
+    sys.__stderr__.flush()
 
 
 def _oracle_index(t, cfg):
@@ -128,11 +132,12 @@ def _tail_start(cfg, vert, slash, first_blocks, rows_filter=None, need=4096, max
         nb *= 2
 
 
-def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None):
+def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None, kv_heads=None):
     """dK / dV of keys at global positions >= row_lo: exact contributions of the
     rows at or after row_lo (optionally only those passing rows_filter).
     dk_of / dv_of may be lists (several results checked against one oracle
-    computation); the errors are then lists too."""
+    computation); the errors are then lists too. kv_heads: check only these
+    kv heads (the q heads of their groups), else all."""
     Hq, Hkv, N = cfg.Hq, cfg.Hkv, cfg.N
     rows = np.arange(row_lo, N)
     if rows_filter is not None:
@@ -140,10 +145,13 @@ def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None):
     keys = np.arange(row_lo, N)
     ref_dk = np.zeros((Hkv, len(keys), cfg.D))
     ref_dv = np.zeros((Hkv, len(keys), cfg.D))
+    kv_sel = list(range(Hkv)) if kv_heads is None else sorted(kv_heads)
     for h in range(Hq):
         g = h * Hkv // Hq
-        if len(rows) == 0:
+        if len(rows) == 0 or g not in kv_sel:
             continue
+        if h % 4 == 0:
+            _log(f"  oracle dK/dV: q head {h} of {Hq}")
         cand = _candidate_cols(rows, vert[h], slash[h])
         M, _, _ = om.active(rows, cand, vert[h], slash[h])
         used = cand[M.any(axis=0)]
@@ -152,10 +160,11 @@ def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None):
         sel = used >= row_lo
         ref_dk[g, used[sel] - row_lo] += dk[sel]
         ref_dv[g, used[sel] - row_lo] += dv[sel]
+    ks = np.asarray(kv_sel)
     if isinstance(dk_of, (list, tuple)):
-        return ([float(np.abs(f(keys) - ref_dk).max()) for f in dk_of],
-                [float(np.abs(f(keys) - ref_dv).max()) for f in dv_of])
-    return (float(np.abs(dk_of(keys) - ref_dk).max()), float(np.abs(dv_of(keys) - ref_dv).max()))
+        return ([float(np.abs(f(keys)[ks] - ref_dk[ks]).max()) for f in dk_of],
+                [float(np.abs(f(keys)[ks] - ref_dv[ks]).max()) for f in dv_of])
+    return (float(np.abs(dk_of(keys)[ks] - ref_dk[ks]).max()), float(np.abs(dv_of(keys)[ks] - ref_dv[ks]).max()))
 
 
 def _contig_case(name, comps=("bf16",)):
@@ -205,9 +214,11 @@ def _contig_case(name, comps=("bf16",)):
     _log(f"{name}: oracle rows heads={heads} blocks={blocks}")
     ws = _rows_check(t, cfg, vert, slash, lambda I: np.arange(64 * I, 64 * I + 64), gots, heads, blocks)
     row_lo, n_tail = _tail_start(cfg, vert, slash, 3)
-    _log(f"{name}: oracle dK/dV of the last {(N - row_lo) // 64} key blocks ({n_tail} active entries)")
+    _log(f"{name}: oracle dK/dV of the last {(N - row_lo) // 64} key blocks ({n_tail} active entries over "
+         f"all heads)")
     assert n_tail > 0
-    eks, evs = _tail_kv_check(t, cfg, vert, slash, row_lo, dks, dvs)
+    kv_heads = None if Hkv <= 2 else [0, Hkv - 1]     # the first and last kv groups of a wide layer
+    eks, evs = _tail_kv_check(t, cfg, vert, slash, row_lo, dks, dvs, kv_heads=kv_heads)
     for comp, ek, ev in zip(comps, eks, evs):
         w = ws[comp]
         _log(f"{name} [{comp}]: max errors O {w['o']:.3e} LSE {w['lse']:.3e} dQ {w['dq']:.3e} "
