@@ -292,13 +292,14 @@ def test_convert_f16_exact_and_range():
         assert int(status.item()) == vs.VS_ERR_RANGE, bad
 
 
-def test_bwd_prep_f16_matches_separate_calls():
-    """vs_attn_bwd_prep_f16 (delta and the fp16 dO copy in one pass) equals
-    vs_convert_f16 followed by vs_attn_bwd_prep, bit for bit; range errors
-    reach the status word."""
+@pytest.mark.parametrize("D", [128, 64])
+def test_bwd_prep_f16_matches_separate_calls(D):
+    """vs_attn_bwd_prep_f16 (delta and the fp16 dO copy in one pass): its
+    copy equals vs_convert_f16's and its delta vs_attn_bwd_prep's on the same
+    dO, bit for bit; range errors reach the status word."""
     import dynamic_sparse_attention_index_amd as vs
     rng = np.random.default_rng(17)
-    Hq, Nq, D = 3, 64 * 5, 128
+    Hq, Nq = 3, 64 * 5
     o = torch.tensor(rng.standard_normal((Hq, Nq, D)), dtype=torch.float32, device="cuda")
     do = torch.tensor(rng.standard_normal((Hq, Nq, D)) * 3, dtype=torch.float32).to(torch.bfloat16).cuda()
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -306,7 +307,7 @@ def test_bwd_prep_f16_matches_separate_calls():
     do16b = torch.empty_like(do16a)
     da, db = torch.empty(Hq, Nq, device="cuda"), torch.empty(Hq, Nq, device="cuda")
     vs.vs_convert_f16(do, do16a, st)
-    vs.vs_attn_bwd_prep(o, do16a, da)
+    vs.vs_attn_bwd_prep(o, do, da)              # delta from the bf16 values (the same numbers)
     vs.vs_attn_bwd_prep_f16(o, do, do16b, db, st)
     torch.cuda.synchronize()
     assert int(st.item()) == vs.VS_OK

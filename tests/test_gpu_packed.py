@@ -134,3 +134,56 @@ def test_packed_forward_ring_accumulate():
         assert int(status.item()) == vs.VS_OK
         outs.append((o, lse))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_group_select_one_head_per_group_is_per_head_select():
+    """With one q head per kv head the per-kv-head selection is the per-head
+    selection, bit for bit (the group mean of one head is that head)."""
+    import dynamic_sparse_attention_index_amd as vs
+    rng = np.random.default_rng(31)
+    Hq, N = 3, 64 * 48
+    T = N // 64
+    v = torch.tensor(rng.exponential(1.0, (Hq, N)) ** 3, dtype=torch.float32, device="cuda")
+    s = torch.tensor(rng.exponential(1.0, (Hq, T)) ** 3, dtype=torch.float32, device="cuda")
+    outs = []
+    for group in (False, True):
+        vi = torch.full((Hq, N), -1, dtype=torch.int32, device="cuda")
+        si = torch.full((Hq, T), -1, dtype=torch.int32, device="cuda")
+        vc, sc = (torch.empty(Hq, dtype=torch.int32, device="cuda") for _ in range(2))
+        if group:
+            ws = torch.empty(vs.index_select_group_workspace_size(Hq, Hq, N), dtype=torch.uint8, device="cuda")
+            vs.vs_index_select_group(v, s, Hq, Hq, N, 0.9, vi, vc, si, sc, ws)
+        else:
+            ws = torch.empty(vs.index_select_workspace_size(Hq, N), dtype=torch.uint8, device="cuda")
+            vs.vs_index_select(v, s, Hq, N, 0.9, vi, vc, si, sc, ws)
+        torch.cuda.synchronize()
+        outs.append((vc.cpu(), sc.cpu(), vi.cpu(), si.cpu()))
+    (vc0, sc0, vi0, si0), (vc1, sc1, vi1, si1) = outs
+    assert torch.equal(vc0, vc1) and torch.equal(sc0, sc1)
+    for h in range(Hq):
+        assert torch.equal(vi0[h, :vc0[h]], vi1[h, :vc1[h]]) and torch.equal(si0[h, :sc0[h]], si1[h, :sc1[h]])
+        assert np.array_equal(vi1[h, :vc1[h]].numpy(), oi.select_top_p(v[h].cpu().numpy(), 0.9))
+
+
+def test_packed_forward_single_pair():
+    """Two q heads sharing one kv head (one pair per group), bf16 operands."""
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    cfg = config_by_name("qwen32k", N=64 * 12, Hq=2, Hkv=1, n_out=3, c=2.0)
+    t = generate(cfg, tensors=("q", "k", "v"))
+    N, Hq, D = cfg.N, cfg.Hq, cfg.D
+    rng = np.random.default_rng(5)
+    vg = np.sort(rng.choice(N, 40, replace=False))
+    sg = np.array([0, 1, 5], dtype=np.int64)
+    lists = H.upload_lists([vg] * Hq, [sg] * Hq, N)
+    lay = vs.layout("contig", 1, N)
+    m = H.gpu_mask(lists, Hq, 1, lay, 0, 0, H.tile_cap_for([sg] * Hq, Hq, N // 64))
+    q, k, v = (H.to_dev(t[x], "bf16") for x in ("q", "k", "v"))
+    o1, l1 = torch.empty(Hq, N, D, device="cuda"), torch.empty(Hq, N, device="cuda")
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    vs.vs_attn_fwd(q, k, v, m, cfg.scale, o1, l1)
+    vs.vs_attn_fwd_packed(q, k, v, m, cfg.scale, o2, l2, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == vs.VS_OK
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
