@@ -97,10 +97,20 @@ __global__ void __launch_bounds__(MASK_THREADS) mask_head_kernel(MaskArgs a) {
     a.vcum[(int64_t)h * (a.NB + 1) + J] = lower_bound_i32(out, base, (int64_t)J * BLK);
 }
 
-// Launch 2: list lengths. Threads [0, Hq*NB) handle (h, I) rows of the CSR,
-// threads [Hq*NB, 2*Hq*NB) handle (h, J) columns of the CSC.
-__global__ void mask_count_kernel(MaskArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Launches 2 and 4 give one wave to each list row: rows [0, Hq*NB) are the
+// (h, I) rows of the CSR, rows [Hq*NB, 2*Hq*NB) the (h, J) columns of the CSC;
+// the lanes stride over the head's slash list 64 entries at a time.
+constexpr int ROW_WAVES = 4;   // waves per workgroup of the row kernels
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Launch 2: list lengths.
+__global__ void __launch_bounds__(64 * ROW_WAVES) mask_count_kernel(MaskArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * ROW_WAVES + (threadIdx.x >> 6);
   const int64_t nrow = (int64_t)a.Hq * a.NB;
   if (t >= 2 * nrow) return;
   const bool csr = t < nrow;
@@ -111,22 +121,22 @@ __global__ void mask_count_kernel(MaskArgs a) {
   int cnt = 0;
   if (csr) {  // key blocks G - j of the visible shard
     const int64_t G = global_block(a.kind, a.P, a.NB, a.rank, B);
-    for (int e = 0; e < ns; ++e) {
+    for (int e = lane; e < ns; e += 64) {
       const int j = S[e];
-      if (j < 0 || j > G) continue;
       int J;
-      if (owner_of_block(a.kind, a.P, a.NB, G - j, &J) == a.src) ++cnt;
+      if (j >= 0 && j <= G && owner_of_block(a.kind, a.P, a.NB, G - j, &J) == a.src) ++cnt;
     }
-    a.tile_ptr[1 + u] = cnt;
+    cnt = wave_sum_i32(cnt);
+    if (lane == 0) a.tile_ptr[1 + u] = cnt;
   } else {    // query blocks G' + j of this rank
     const int64_t Gp = global_block(a.kind, a.P, a.NB, a.src, B);
-    for (int e = 0; e < ns; ++e) {
+    for (int e = lane; e < ns; e += 64) {
       const int j = S[e];
-      if (j < 0 || Gp + j >= a.T) continue;
       int I;
-      if (owner_of_block(a.kind, a.P, a.NB, Gp + j, &I) == a.rank) ++cnt;
+      if (j >= 0 && Gp + j < a.T && owner_of_block(a.kind, a.P, a.NB, Gp + j, &I) == a.rank) ++cnt;
     }
-    a.csc_ptr[1 + u] = cnt;
+    cnt = wave_sum_i32(cnt);
+    if (lane == 0) a.csc_ptr[1 + u] = cnt;
   }
 }
 
@@ -155,8 +165,11 @@ __global__ void __launch_bounds__(MASK_THREADS) mask_scan_kernel(MaskArgs a) {
 }
 
 // Launch 4: fill the lists; the CSR half also writes vert_end and n_active.
-__global__ void mask_fill_kernel(MaskArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Order-preserving compaction per 64-entry chunk: a lane's output position is
+// the running count plus the matches of the lanes below it (ballot).
+__global__ void __launch_bounds__(64 * ROW_WAVES) mask_fill_kernel(MaskArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * ROW_WAVES + (threadIdx.x >> 6);
   const int64_t nrow = (int64_t)a.Hq * a.NB;
   if (t >= 2 * nrow) return;
   const bool csr = t < nrow;
@@ -165,50 +178,70 @@ __global__ void mask_fill_kernel(MaskArgs a) {
   const int32_t* S = a.slash_idx + (int64_t)h * a.slash_stride;
   const int ns = a.slash_cnt[h];
   const bool fits = a.status[0] == VS_OK;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   if (csr) {
     const int64_t G = global_block(a.kind, a.P, a.NB, a.rank, B);
     const int32_t* vc = a.vcum + (int64_t)h * (a.NB + 1);
     int32_t* dst = a.tile_col + a.tile_ptr[u];
     int n = 0;
-    int64_t act = 0, covered = 0;
+    int act = 0, covered = 0;   // this lane's share
     // descending j gives ascending key blocks (same predicate as the count)
-    for (int e = ns - 1; e >= 0; --e) {
-      const int j = S[e];
-      if (j < 0 || j > G) continue;
-      int J;
-      if (owner_of_block(a.kind, a.P, a.NB, G - j, &J) != a.src) continue;
-      if (fits) dst[n] = J | (j == 0 ? VS_TILE_DIAG : 0);
-      ++n;
-      if (j == 0) {
-        act += BLK * (BLK + 1) / 2;
-      } else {
-        act += BLK * BLK;
-        covered += vc[J + 1] - vc[J];
+    for (int c0 = 0; c0 < ns; c0 += 64) {
+      const int e = ns - 1 - (c0 + lane);
+      int J = 0, j = -1;
+      bool ok = false;
+      if (e >= 0) {
+        j = S[e];
+        ok = j >= 0 && j <= G && owner_of_block(a.kind, a.P, a.NB, G - j, &J) == a.src;
       }
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      if (ok) {
+        if (fits) dst[n + __builtin_popcountll(m & below)] = J | (j == 0 ? VS_TILE_DIAG : 0);
+        if (j == 0) {
+          act += BLK * (BLK + 1) / 2;
+        } else {
+          act += BLK * BLK;
+          covered += vc[J + 1] - vc[J];
+        }
+      }
+      n += __builtin_popcountll(m);
     }
     const int J_le = blocks_upto(a.kind, a.P, a.NB, a.src, G);
     const int J_lt = blocks_upto(a.kind, a.P, a.NB, a.src, G - 1);
-    a.vert_end[u] = vc[J_le];
-    act += (int64_t)BLK * (vc[J_lt] - covered);
+    // vertical columns in earlier blocks not covered by a listed tile: full
+    // columns; in the query block's own global block (when its diagonal is
+    // not selected): the causal part of each column
+    int vpart = 0;
     if (J_le > J_lt) {  // the shard holds the query block's own global block
       const bool diag_sel = (a.slash_bits[(int64_t)h * a.W] & 1u) != 0;
       if (!diag_sel) {
         const int32_t* vl = a.vloc + (int64_t)h * a.NB * BLK;
-        for (int e = vc[J_lt]; e < vc[J_le]; ++e) act += BLK - (vl[e] % BLK);
+        for (int e = vc[J_lt] + lane; e < vc[J_le]; e += 64) vpart += BLK - (vl[e] % BLK);
       }
     }
-    a.n_active[u] = act;
+    act = wave_sum_i32(act);
+    covered = wave_sum_i32(covered);
+    vpart = wave_sum_i32(vpart);
+    if (lane == 0) {
+      a.vert_end[u] = vc[J_le];
+      a.n_active[u] = (int64_t)act + (int64_t)BLK * (vc[J_lt] - covered) + vpart;
+    }
   } else {
     if (!fits) return;
     const int64_t Gp = global_block(a.kind, a.P, a.NB, a.src, B);
     int32_t* dst = a.csc_row + a.csc_ptr[u];
     int n = 0;
-    for (int e = 0; e < ns; ++e) {
-      const int j = S[e];
-      if (j < 0 || Gp + j >= a.T) continue;
-      int I;
-      if (owner_of_block(a.kind, a.P, a.NB, Gp + j, &I) != a.rank) continue;
-      dst[n++] = I | (j == 0 ? VS_TILE_DIAG : 0);
+    for (int c0 = 0; c0 < ns; c0 += 64) {
+      const int e = c0 + lane;
+      int I = 0, j = -1;
+      bool ok = false;
+      if (e < ns) {
+        j = S[e];
+        ok = j >= 0 && Gp + j < a.T && owner_of_block(a.kind, a.P, a.NB, Gp + j, &I) == a.rank;
+      }
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      if (ok) dst[n + __builtin_popcountll(m & below)] = I | (j == 0 ? VS_TILE_DIAG : 0);
+      n += __builtin_popcountll(m);
     }
   }
 }
@@ -224,9 +257,9 @@ int launch_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t 
   a.tile_ptr = m->tile_ptr; a.tile_col = m->tile_col; a.csc_ptr = m->csc_ptr; a.csc_row = m->csc_row;
   a.vloc = m->vloc; a.vloc_cnt = m->vloc_cnt; a.vcum = m->vcum; a.vert_end = m->vert_end;
   a.slash_bits = m->slash_bits; a.n_active = m->n_active; a.status = m->status;
-  const int64_t nthr = 2 * (int64_t)m->Hq * m->QB;
-  const int tpb = 256;
-  const unsigned nblk = (unsigned)((nthr + tpb - 1) / tpb);
+  const int64_t nrows = 2 * (int64_t)m->Hq * m->QB;   // one wave per list row
+  const int tpb = 64 * ROW_WAVES;
+  const unsigned nblk = (unsigned)((nrows + ROW_WAVES - 1) / ROW_WAVES);
   hipLaunchKernelGGL(mask_head_kernel, dim3(m->Hq), dim3(MASK_THREADS), 0, stream, a);
   hipLaunchKernelGGL(mask_count_kernel, dim3(nblk), dim3(tpb), 0, stream, a);
   hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(MASK_THREADS), 0, stream, a);
