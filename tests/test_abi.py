@@ -206,3 +206,41 @@ def test_f16_validation_before_device_work(L):
     assert L.vs_convert_f16(a, b, 12, st, None) == vs.VS_ERR_UNSUPPORTED
     assert L.vs_convert_f16(ctypes.c_void_p(0x20000002), b, 64, st, None) == vs.VS_ERR_UNSUPPORTED
     assert L.vs_convert_f16(a, b, 0, st, None) == vs.VS_OK                 # nothing to do
+
+
+def test_group_packed_and_fused_prep_validation(L):
+    """Host checks of the per-kv-head selection, the head-pair forward and the
+    fused delta / fp16 dO copy; nothing reaches the device."""
+    p = ctypes.c_void_p(0x40000000)
+    ws = ctypes.c_void_p(0x60000000)
+    # per-kv-head selection
+    assert L.vs_index_select_group_workspace_size(8, 3, 1024) == 0          # 8 % 3 != 0
+    wsz = L.vs_index_select_group_workspace_size(8, 2, 1024)
+    assert wsz > 0
+    assert L.vs_index_select_group(p, p, 8, 3, 1024, 0.9, p, p, p, p, ws, wsz, None) == vs.VS_ERR_ARG
+    assert L.vs_index_select_group(None, p, 8, 2, 1024, 0.9, p, p, p, p, ws, wsz, None) == vs.VS_ERR_ARG
+    assert L.vs_index_select_group(p, p, 8, 2, 1000, 0.9, p, p, p, p, ws, wsz, None) == vs.VS_ERR_UNSUPPORTED
+    assert L.vs_index_select_group(p, p, 8, 2, 1024, 0.9, p, p, p, p, ws, wsz - 1, None) == vs.VS_ERR_WORKSPACE
+    # head-pair forward
+    m, lay, _, _ = _mask(L, Hq=4, Hkv=2)
+    m.rank = m.src = 0
+    q = _fake_tensor(0x20000000, 4, 1024, 128, vs.VS_F16)
+    k = _fake_tensor(0x30000000, 2, 1024, 128, vs.VS_F16)
+    o, lse, st = ctypes.c_void_p(0x40000000), ctypes.c_void_p(0x50000000), ctypes.c_void_p(0x58000000)
+    assert L.vs_attn_fwd_packed(q, k, k, ctypes.byref(m), 0.1, o, lse, 0, None, None) == vs.VS_ERR_ARG
+    assert L.vs_attn_fwd_packed(q, k, k, ctypes.byref(m), 0.1, o, lse, 2, st, None) == vs.VS_ERR_ARG
+    q32 = _fake_tensor(0x20000000, 4, 1024, 64, vs.VS_F32)
+    k32 = _fake_tensor(0x30000000, 2, 1024, 64, vs.VS_F32)
+    assert L.vs_attn_fwd_packed(q32, k32, k32, ctypes.byref(m), 0.1, o, lse, 0, st, None) == vs.VS_ERR_UNSUPPORTED
+    m3, _, _, _ = _mask(L, Hq=3, Hkv=1)                   # three q heads per kv head: no pairs
+    m3.rank = m3.src = 0
+    q3 = _fake_tensor(0x20000000, 3, 1024, 128, vs.VS_F16)
+    k3 = _fake_tensor(0x30000000, 1, 1024, 128, vs.VS_F16)
+    assert L.vs_attn_fwd_packed(q3, k3, k3, ctypes.byref(m3), 0.1, o, lse, 0, st, None) == vs.VS_ERR_UNSUPPORTED
+    # fused delta and fp16 dO copy
+    a16 = ctypes.c_void_p(0x20000000)
+    assert L.vs_attn_bwd_prep_f16(p, a16, a16, 4, 1024, 128, p, None, None) == vs.VS_ERR_ARG
+    assert L.vs_attn_bwd_prep_f16(p, a16, a16, 0, 1024, 128, p, st, None) == vs.VS_ERR_ARG
+    assert L.vs_attn_bwd_prep_f16(p, a16, a16, 4, 1024, 96, p, st, None) == vs.VS_ERR_UNSUPPORTED
+    assert L.vs_attn_bwd_prep_f16(p, ctypes.c_void_p(0x20000002), a16, 4, 1024, 128, p, st,
+                                  None) == vs.VS_ERR_UNSUPPORTED
