@@ -95,9 +95,11 @@ __host__ inline unsigned xcd_group_grid(int G, int nblk, int bpc, int hpg) {
 }
 // Query-major kernels (two workgroups per CU, 64 per XCD): clusters of 8
 // query blocks x the group's q heads. Key-major kernels (one workgroup per CU,
-// 32 per XCD): clusters of 32 key blocks of one kv head.
+// 32 per XCD): clusters of 8 key blocks of one kv head (measured against 12,
+// 16, 32 and 64: neighbouring key blocks share most of their query tiles, and
+// shorter clusters keep more of an XCD's concurrent blocks adjacent).
 constexpr int QMAJOR_BPC = 8;
-constexpr int KMAJOR_BPC = 32;
+constexpr int KMAJOR_BPC = 8;
 
 // --- layout maps -------------------------------------------------------------
 // Global 64-block of local block J of rank `rank` (NB = local blocks per shard).
