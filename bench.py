@@ -664,7 +664,8 @@ def stored_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (profiles/counters.json: FETCH_SIZE and WRITE_SIZE runs scaled by the
     same counters' reading for a copy of known size), or None when absent or
-    when the kernel's source file has changed since the counters were taken."""
+    when the kernel's source file or the shared kernel headers have changed
+    since the counters were taken (one SHA-256 over all of them)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
@@ -672,8 +673,13 @@ def stored_traffic(kernel):
     rec = json.load(open(path)).get(kernel)
     if not rec:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    h = hashlib.sha256()
+    for rel in [rec["source"]] + rec.get("headers", []):
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
         return None
     return int(rec["hbm_bytes_per_launch"])
 
