@@ -322,3 +322,20 @@ def test_select_group_reductions(seed):
             for h in range(g * R, (g + 1) * R):
                 assert np.array_equal(vert[h], sel)
                 assert np.array_equal(slash[h], slash[g * R])
+
+
+def test_select_group_mean_not_max_or_first():
+    """The group statistic is the mean of the group's q heads, hand-derived on
+    dyadic scores where the mean, the max and the first head disagree:
+      head 0 = [1/2, 1/4, 1/4, 0], head 1 = [0, 1/4, 1/4, 1/2] (one kv group)
+      mean   = [1/4, 1/4, 1/4, 1/4]: p = 1/2 needs two; ties to the lower index -> {0, 1}
+      max    = [1/2, 1/4, 1/4, 1/2]: total 3/2, target 3/4 -> {0, 3}
+      head 0 alone: 1/2 reaches 1/2 -> {0}
+    so only the mean gives {0, 1}."""
+    v = np.array([[0.5, 0.25, 0.25, 0.0], [0.0, 0.25, 0.25, 0.5]], dtype=np.float32)
+    assert oi.group_scores(v, 1).tolist() == [[0.25, 0.25, 0.25, 0.25]]
+    vert, slash = oi.select_group_top_p(v, v.copy(), 1, 0.5)
+    for h in range(2):
+        assert vert[h].tolist() == [0, 1] and slash[h].tolist() == [0, 1]
+    assert oi.select_top_p(v.max(axis=0), 0.5).tolist() == [0, 3]
+    assert oi.select_top_p(v[0], 0.5).tolist() == [0]

@@ -132,3 +132,54 @@ def test_csc_is_transpose():
     pairs_csr = sorted((I, int(J)) for I in range(desc["QB"]) for J in desc["blocks"][(0, I)]["tiles"])
     pairs_csc = sorted((I, J) for J, lst in csc.items() for I, _ in lst)
     assert pairs_csr == pairs_csc
+
+
+def test_golden_two_rank_mask():
+    """Hand-derived descriptions of a 2-rank ring (striped and zigzag): tile
+    lists, LOCAL vertical positions, vertical prefix lengths and counts."""
+    V, S = np.array([10, 100, 150, 200]), np.array([0, 1])
+    cases = []
+    for line in open(os.path.join(GOLDEN, "mask_p2.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        if line.startswith("@"):
+            head, vloc = line[1:].split(";")
+            kind, rank, step = head.split()
+            cases.append((kind, int(rank), int(step), [int(x) for x in vloc.split()], []))
+            continue
+        blk, tiles, vend, nact = [t.strip() for t in line.split(";")]
+        exp_t = [tuple(int(u) for u in t.split(":")) for t in tiles.split()]
+        cases[-1][4].append((int(blk), exp_t, int(vend), int(nact)))
+    assert len(cases) == 5
+    for kind, rank, step, vloc, blocks in cases:
+        desc = om.step_description(kind, 256, 2, rank, step, [V], [S])
+        assert desc["vloc"][0].tolist() == vloc, (kind, rank, step)
+        assert len(blocks) == desc["QB"] == 2
+        for blk, exp_t, vend, nact in blocks:
+            b = desc["blocks"][(0, blk)]
+            assert [(int(J), int(d)) for J, d in zip(b["tiles"], b["diag"])] == exp_t, (kind, rank, step, blk)
+            assert b["vert_end"] == vend, (kind, rank, step, blk)
+            assert b["n_active"] == nact, (kind, rank, step, blk)
+
+
+@pytest.mark.parametrize("kind", ["contig", "striped", "zigzag"])
+@pytest.mark.parametrize("P", [2, 4])
+def test_step_description_verticals_by_enumeration(kind, P):
+    """vloc and vert_end against a direct enumeration: vloc[k] is the storage
+    index of the k-th visible vertical, and vert_end counts the visible
+    verticals with at least one causal row in the query block."""
+    rng = np.random.default_rng(40 + P + len(kind))
+    N = 64 * 16
+    vert = [np.sort(rng.choice(N, 30, replace=False))]
+    slash = [np.array([0, 3])]
+    for r in range(P):
+        rows = ol.shard_positions(kind, N, P, r)
+        for s in range(P):
+            cols = ol.shard_positions(kind, N, P, ol.ring_source(r, s, P))
+            desc = om.step_description(kind, N, P, r, s, vert, slash)
+            exp_vloc = [b for b, m in enumerate(cols.tolist()) if m in set(vert[0].tolist())]
+            assert desc["vloc"][0].tolist() == exp_vloc
+            for I in range(desc["QB"]):
+                last_row = int(rows[64 * I + 63])
+                exp_end = sum(1 for b in exp_vloc if int(cols[b]) <= last_row)
+                assert desc["blocks"][(0, I)]["vert_end"] == exp_end
