@@ -141,27 +141,42 @@ __global__ void __launch_bounds__(64 * ROW_WAVES) mask_count_kernel(MaskArgs a) 
 }
 
 // Launch 3: one workgroup; in-place inclusive scan of both length arrays.
-__device__ void scan_inplace(int32_t* p, int64_t n, int* sh) {
-  int run = 0;
+// The running total is kept in 64 bits, so a list larger than the int32
+// entries can hold is still seen to exceed the capacity (tile_cap < 2^31);
+// the stored prefix values are then wrong, but they are overwritten below.
+__device__ int64_t scan_inplace(int32_t* p, int64_t n, int* sh) {
+  int64_t run = 0;
   if (threadIdx.x == 0) p[0] = 0;
   for (int64_t c0 = 0; c0 < n; c0 += MASK_THREADS) {
     const int64_t e = c0 + threadIdx.x;
-    const int x = e < n ? p[1 + e] : 0;
+    const int x = e < n ? p[1 + e] : 0;   // one row's count: at most T
     int tot;
     const int pos = block_exclusive_scan(x, &tot, sh);
-    if (e < n) p[1 + e] = run + pos + x;
+    if (e < n) p[1 + e] = (int32_t)(run + pos + x);
     run += tot;
   }
+  return run;
 }
 
+// On overflow every list is made empty before any consumer runs: both
+// pointer arrays become all zeros and the per-head vertical counts zero
+// (vert_end is zeroed by the fill launch), so attention calls queued behind
+// this mask on the stream read no list entry and compute nothing for the
+// step; only the status word and n_active (exact counts) are meaningful.
 __global__ void __launch_bounds__(MASK_THREADS) mask_scan_kernel(MaskArgs a) {
   __shared__ int sh[MASK_THREADS / 64 + 1];
   const int64_t n = (int64_t)a.Hq * a.NB;
-  scan_inplace(a.tile_ptr, n, sh);
-  scan_inplace(a.csc_ptr, n, sh);
+  const int64_t tiles = scan_inplace(a.tile_ptr, n, sh);
+  const int64_t cols = scan_inplace(a.csc_ptr, n, sh);
   __syncthreads();
-  if (threadIdx.x == 0 && ((int64_t)a.tile_ptr[n] > a.tile_cap || (int64_t)a.csc_ptr[n] > a.tile_cap))
-    a.status[0] = VS_ERR_CAPACITY;
+  if (tiles > a.tile_cap || cols > a.tile_cap) {
+    for (int64_t e = threadIdx.x; e <= n; e += MASK_THREADS) {
+      a.tile_ptr[e] = 0;
+      a.csc_ptr[e] = 0;
+    }
+    for (int h = threadIdx.x; h < a.Hq; h += MASK_THREADS) a.vloc_cnt[h] = 0;
+    if (threadIdx.x == 0) a.status[0] = VS_ERR_CAPACITY;
+  }
 }
 
 // Launch 4: fill the lists; the CSR half also writes vert_end and n_active.
@@ -223,7 +238,7 @@ __global__ void __launch_bounds__(64 * ROW_WAVES) mask_fill_kernel(MaskArgs a) {
     covered = wave_sum_i32(covered);
     vpart = wave_sum_i32(vpart);
     if (lane == 0) {
-      a.vert_end[u] = vc[J_le];
+      a.vert_end[u] = fits ? vc[J_le] : 0;
       a.n_active[u] = (int64_t)act + (int64_t)BLK * (vc[J_lt] - covered) + vpart;
     }
   } else {

@@ -1,5 +1,6 @@
 """GPU active-region compaction vs the oracle's definition (bit-exact)."""
 import numpy as np
+import torch
 import pytest
 
 from oracle import layout as ol
@@ -85,8 +86,33 @@ def test_mask_capacity_overflow_reported():
     N, Hq = 64 * 16, 2
     vert = [np.arange(0, N, 5)] * Hq
     slash = [np.arange(N // 64)] * Hq
-    m = H.gpu_mask(H.upload_lists(vert, slash, N), Hq, 1, vs.layout("contig", 1, N), 0, 0, tile_cap=10)
-    assert H.mask_to_numpy(m)["status"][0] == vs.VS_ERR_CAPACITY
+    lay = vs.layout("contig", 1, N)
+    m = H.gpu_mask(H.upload_lists(vert, slash, N), Hq, 1, lay, 0, 0, tile_cap=10)
+    a = H.mask_to_numpy(m)
+    assert a["status"][0] == vs.VS_ERR_CAPACITY
+    # every list reads as empty, so consumers queued behind the mask do nothing
+    assert (a["tile_ptr"] == 0).all() and (a["csc_ptr"] == 0).all()
+    assert (a["vloc_cnt"] == 0).all() and (a["vert_end"] == 0).all()
+    # the exact active counts survive
+    for h in range(Hq):
+        assert a["n_active"][h * 16:(h + 1) * 16].sum() == om.active_count(N, vert[h], slash[h])
+    # a forward and a backward queued behind the overflowed mask compute nothing
+    rng = np.random.default_rng(9)
+    q = H.to_dev(rng.standard_normal((Hq, N, 128)), "bf16")
+    k = H.to_dev(rng.standard_normal((1, N, 128)), "bf16")
+    v = H.to_dev(rng.standard_normal((1, N, 128)), "bf16")
+    do = H.to_dev(rng.standard_normal((Hq, N, 128)), "bf16")
+    o = torch.full((Hq, N, 128), 7.0, device="cuda")
+    lse = torch.full((Hq, N), 7.0, device="cuda")
+    vs.vs_attn_fwd(q, k, v, m, 0.088, o, lse)
+    dq = torch.zeros(Hq, N, 128, device="cuda")
+    dk = torch.zeros(1, N, 128, device="cuda")
+    dv = torch.zeros(1, N, 128, device="cuda")
+    delta = torch.zeros(Hq, N, device="cuda")
+    vs.vs_attn_bwd(q, k, v, do, torch.zeros(Hq, N, device="cuda"), delta, m, 0.088, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert (o == 0).all() and torch.isneginf(lse).all()
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
 
 
 def test_mask_full_size_striped_rank_share():
