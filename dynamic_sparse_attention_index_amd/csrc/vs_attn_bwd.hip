@@ -35,7 +35,7 @@ struct BwdArgs {
   const void *q, *k, *v, *dout;
   int64_t qsh, qsn, ksh, ksn, vsh, vsn, dsh, dsn;
   const float *lse, *delta;
-  const int32_t *tile_ptr, *tile_col, *csc_ptr, *csc_row, *vloc, *vloc_cnt, *vert_end;
+  const int32_t *tile_ptr, *tile_col, *csc_ptr, *csc_row, *vloc, *vloc_cnt, *vcum, *vert_end;
   const uint32_t* slash_bits;
   float *dq, *dk, *dv;
   int Hq, Hkv, QB, KB, W, kind, P, rank, src;
@@ -432,7 +432,10 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 
 // dQ, query-major. Wave (rh, kh) = rows 32 rh.. of the block, keys 32 kh.. of
 // every tile; the two key halves' partial dQ are added through LDS at the end.
-// F16: fp16 inputs, dS as one fp16 operand (one MFMA per product).
+// dS enters the dQ product as a hi + lo pair in both operand formats (bf16
+// pair, or fp16 pair on fp16 inputs): dQ_n sums dS over every active key of
+// the row, and the large outlier keys scale each weight's rounding error, so
+// a single fp16 dS put dQ at 1.9e-2 of the oracle at 262144 tokens.
 template <bool F16>
 __device__ __forceinline__ void dq_d128(const BwdArgs& a) {
   constexpr int D = TD;
@@ -563,7 +566,7 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs]));
           s[rs][t][i] = p * (dp[rs][t][i] - dl[rs]);
         }
-      weights8<F16>(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
+      weights8<F16, true>(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
     }
     // dQ^T += K^T dS^T over this wave's 32 keys; the transposed K operand of
     // block dt + 1 is read after the first MFMA of block dt
@@ -581,10 +584,10 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a) {
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
         acc[rs][dt] = mma16<F16>(ka[b], dsh[rs], acc[rs][dt]);
-        if constexpr (!F16) acc[rs][dt] = mma16<F16>(ka[b], dsl[rs], acc[rs][dt]);
+        acc[rs][dt] = mma16<F16>(ka[b], dsl[rs], acc[rs][dt]);
       }
     }
-    constexpr int MPB = F16 ? 2 : 4;   // MFMAs per column block
+    constexpr int MPB = 4;   // MFMAs per column block
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -688,7 +691,7 @@ __device__ __forceinline__ void kv_rowstats(const float* lsh, const float* dsh_,
 // l2: row LSE in log2 units, +inf for an empty row (kv_rowstats); on the
 // diagonal tile (wave-uniform `diag`) key kt of this lane is active for rows
 // >= thr[kt].
-template <bool F16>
+template <bool F16, bool PAIR = !F16>
 __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], const f32x4* l2, const f32x4* dd,
                                        int diag, const int* thr, int rh, int g4, float sl2, bf16x8* ph,
                                        bf16x8* pl, bf16x8* dh, bf16x8* dl) {
@@ -713,11 +716,11 @@ __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], cons
         s[kt][t][i] = pr;
         ds[t][i] = pr * (dp[kt][t][i] - dd[t][i]);
       }
-    weights8<F16>(s[kt][0], s[kt][1], ph[kt], pl[kt]);
-    weights8<F16>(ds[0], ds[1], dh[kt], dl[kt]);
+    weights8<F16, PAIR>(s[kt][0], s[kt][1], ph[kt], pl[kt]);
+    weights8<F16, PAIR>(ds[0], ds[1], dh[kt], dl[kt]);
   }
 }
-template <bool F16>
+template <bool F16, bool PAIR = !F16>
 __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf16x8* ph, const bf16x8* pl,
                                         const bf16x8* dh, const bf16x8* dl, int rh, int g4, int n16,
                                         f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8]) {
@@ -740,12 +743,12 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       acc_dv[kt][dt] = mma16<F16>(oT[b], ph[kt], acc_dv[kt][dt]);
-      if constexpr (!F16) acc_dv[kt][dt] = mma16<F16>(oT[b], pl[kt], acc_dv[kt][dt]);
+      if constexpr (PAIR) acc_dv[kt][dt] = mma16<F16>(oT[b], pl[kt], acc_dv[kt][dt]);
       acc_dk[kt][dt] = mma16<F16>(qT[b], dh[kt], acc_dk[kt][dt]);
-      if constexpr (!F16) acc_dk[kt][dt] = mma16<F16>(qT[b], dl[kt], acc_dk[kt][dt]);
+      if constexpr (PAIR) acc_dk[kt][dt] = mma16<F16>(qT[b], dl[kt], acc_dk[kt][dt]);
     }
   }
-  constexpr int MPB = F16 ? 4 : 8;   // MFMAs per column block
+  constexpr int MPB = PAIR ? 8 : 4;   // MFMAs per column block
   // reads of block dt + 1 go out after the first MFMA of block dt, so the
   // wait in front of that MFMA covers block dt's reads only
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -761,7 +764,7 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
 // vertical-column kernel): thr[kt] = rows of the block with offset below it
 // are inactive for key kt of this lane (BLK: the whole block); the LSE is
 // staged in natural-log units.
-template <bool F16>
+template <bool F16, bool PAIR = !F16>
 __device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const float* lsh, const float* dsh_,
                                          const bf16x8 (*kf)[4], const bf16x8 (*vf)[4], const int* thr,
                                          int rh, int g4, int n16, float sl2, f32x4 (*acc_dk)[8],
@@ -775,8 +778,8 @@ __device__ __forceinline__ void kv_block(const bf16* Qs, const bf16* Os, const f
   // thresholds apply under a wave-uniform branch: most blocks have none
   const int masked = __builtin_amdgcn_ballot_w64(thr[0] != 0 || thr[1] != 0) != 0ull ? 1 : 0;
   bf16x8 ph[2], pl[2], dh[2], dl[2];
-  kv_pds<F16>(s, dp, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl);
-  kv_grad<F16>(Qs, Os, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
+  kv_pds<F16, PAIR>(s, dp, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl);
+  kv_grad<F16, PAIR>(Qs, Os, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
 }
 
 // Copy the Q and dO rows of query block I of head h and its lse/delta.
@@ -896,6 +899,21 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
   }
   int total = 0;
   for (int hh = 0; hh < grp; ++hh) total += __builtin_amdgcn_readlane(cnt_l, hh);
+  // Vertical columns are left to the vertical-column kernel over every query
+  // block (with hi + lo weights there), so this kernel drops them from its
+  // tiles: lane hh < grp holds the 64-bit set of key block J's columns that
+  // are verticals of the group's q head hh.
+  uint32_t vm_lo_l = 0, vm_hi_l = 0;
+  if (lane < grp) {
+    const int64_t hq = kvh * grp + lane;
+    const int32_t* vc = a.vcum + hq * (a.KB + 1);
+    const int32_t* vl = a.vloc + hq * a.KB * BLK;
+    for (int e = vc[J]; e < vc[J + 1]; ++e) {
+      const int b = vl[e] & (BLK - 1);
+      if (b < 32) vm_lo_l |= 1u << b;
+      else vm_hi_l |= 1u << (b - 32);
+    }
+  }
   if (total == 0) {
     if (a.overwrite) {
       const int64_t r0 = ((int64_t)kvh * a.KB * BLK + (int64_t)J * BLK) * TD;
@@ -934,7 +952,8 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
     ++cur_p;
     cur_skip();
   };
-  // start the copy of tile t into stage p; returns its diagonal flag
+  // start the copy of tile t into stage p; returns its diagonal flag (bit 0)
+  // and its q head within the group (bits 1..)
   auto issue = [&]<int p>(int t) -> int {
     const int e = __builtin_amdgcn_readfirstlane(desc_sh[t % 3][0]);
     const int hh = __builtin_amdgcn_readfirstlane(head_sh[t % 3]);
@@ -952,7 +971,7 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
                                            (__attribute__((address_space(3))) float*)(ls + wave * BLK)),
                                        4, 0, 0);
     }
-    return (e & VS_TILE_DIAG) ? 1 : 0;
+    return ((e & VS_TILE_DIAG) ? 1 : 0) | (hh << 1);
   };
 
   bf16x8 kf[2][4], vf[2][4];
@@ -996,14 +1015,23 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
     f32x4 l2[2], dd[2];
     const float* Lc = Lst.template operator()<p>();
     kv_rowstats<true>(Lc, Lc + BLK, rh, g4, l2, dd);
+    // key kt of this lane is active for rows >= thr[kt]: its index on the
+    // diagonal tile, 0 elsewhere, and never (BLK) for a vertical of the head
+    const int hh_i = diag_i >> 1;
+    const uint32_t vlo = __builtin_amdgcn_readlane(vm_lo_l, hh_i), vhi = __builtin_amdgcn_readlane(vm_hi_l, hh_i);
     int thr[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) thr[kt] = 32 * kh + 16 * kt + n16;
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = 32 * kh + 16 * kt + n16;
+      const bool vert = ((kh ? vhi : vlo) >> (16 * kt + n16)) & 1u;
+      thr[kt] = vert ? BLK : ((diag_i & 1) ? key : 0);
+    }
+    const int masked = ((diag_i & 1) || vlo || vhi) ? 1 : 0;
     __builtin_amdgcn_sched_barrier(0);
     f32x4 s_n[2][2], dp_n[2][2];
     kv_sdp<F16>(qa, oa, kf, vf, s_n, dp_n);
     bf16x8 ph[2], pl[2], dh[2], dl[2];
-    kv_pds<F16>(s_c, dp_c, l2, dd, diag_i, thr, rh, g4, sl2, ph, pl, dh, dl);
+    kv_pds<F16>(s_c, dp_c, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl);
     constexpr int VPM = F16 ? 4 : 6;   // vector ops per MFMA (fp16 weights need one convert per pair)
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
@@ -1060,14 +1088,17 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_f16_d128_kernel(BwdArgs a
 // first column are skipped; within the range every block is processed with
 // per-key thresholds (causal edge, columns covered by a listed tile).
 // Results are added with fp32 atomics (a column can be a vertical of several
-// q heads of the group).
+// q heads of the group). A vertical column sums P and dS over up to every row
+// of the sequence and of the group's q heads, so the weights always enter as
+// hi + lo pairs (fp16 pairs on fp16 operands): one rounding of each weight
+// to fp16 leaves an error that grows with the square root of that count and
+// reached 0.1 in dV on the outlier columns of the 131072-token layer.
 template <bool F16>
 __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) float L0[2 * BLK];
   __shared__ __attribute__((aligned(16))) float L1[2 * BLK];
-  __shared__ uint32_t sbits[MAX_LDS_W];
   bf16* Q0 = QO0;
   bf16* O0 = QO0 + TILE_ELEMS;
   bf16* Q1 = QO1;
@@ -1111,8 +1142,6 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
     const int total = I_hi - I_lo;
     if (total <= 0) continue;
     __syncthreads();  // the previous item's exchange has been read
-    const uint32_t* sbg = a.slash_bits + (int64_t)h * a.W;
-    for (int x = tid; x < a.W; x += BWD_THREADS) sbits[x] = sbg[x];
     int m[2];
     int64_t gbk[2];
     bool valid[2];
@@ -1143,11 +1172,13 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
       int thr[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        // every causal row of the column, inside listed tiles too (the slash
+        // kernel leaves vertical columns out of its tiles)
         const int64_t j = G - gbk[kt];
         thr[kt] = BLK;
-        if (valid[kt] && j >= 0 && !((sbits[j >> 5] >> (j & 31)) & 1u)) thr[kt] = (j == 0) ? (m[kt] % BLK) : 0;
+        if (valid[kt] && j >= 0) thr[kt] = (j == 0) ? (m[kt] % BLK) : 0;
       }
-      kv_block<F16>(Qs, Os, Ls, Ls + BLK, kf, vf, thr, rh, g4, n16, sl2, acc_dk, acc_dv);
+      kv_block<F16, true>(Qs, Os, Ls, Ls + BLK, kf, vf, thr, rh, g4, n16, sl2, acc_dk, acc_dv);
     };
     stage_qblock(Q0, O0, L0, a, h, I_lo, wave, lane, dlane);
     for (int it = 0; it < total; it += 2) {
@@ -1278,7 +1309,8 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   a.dsh = dout.sh; a.dsn = dout.sn;
   a.lse = lse; a.delta = delta;
   a.tile_ptr = m->tile_ptr; a.tile_col = m->tile_col; a.csc_ptr = m->csc_ptr; a.csc_row = m->csc_row;
-  a.vloc = m->vloc; a.vloc_cnt = m->vloc_cnt; a.vert_end = m->vert_end; a.slash_bits = m->slash_bits;
+  a.vloc = m->vloc; a.vloc_cnt = m->vloc_cnt; a.vcum = m->vcum; a.vert_end = m->vert_end;
+  a.slash_bits = m->slash_bits;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src;

@@ -274,16 +274,29 @@ __device__ __forceinline__ void split8(const f32x4& w0, const f32x4& w1, bf16x8&
 }
 // Eight fp32 weights (P or dS) as MFMA operands. bf16: the hi + lo pair of
 // split8 (two MFMAs per product). fp16: one operand rounded to nearest even
-// (11 significant bits); lo is left untouched and not used.
+// (11 significant bits; lo is left untouched and not used), or with PAIR an
+// fp16 hi + lo pair (hi = fp16(w), lo = fp16(w - hi): 22 significant bits
+// down to fp16's 2^-24 spacing), for products that sum very many weights.
 typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
-template <bool F16>
+__device__ __forceinline__ uint32_t f16_pair_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+template <bool F16, bool PAIR = !F16>
 __device__ __forceinline__ void weights8(const f32x4& w0, const f32x4& w1, bf16x8& hi, bf16x8& lo) {
   if constexpr (F16) {
-    const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0[0], w0[1]}, f16x2));
-    const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0[2], w0[3]}, f16x2));
-    const uint32_t h2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w1[0], w1[1]}, f16x2));
-    const uint32_t h3 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w1[2], w1[3]}, f16x2));
+    const uint32_t h0 = f16_pair_bits(w0[0], w0[1]);
+    const uint32_t h1 = f16_pair_bits(w0[2], w0[3]);
+    const uint32_t h2 = f16_pair_bits(w1[0], w1[1]);
+    const uint32_t h3 = f16_pair_bits(w1[2], w1[3]);
     hi = __builtin_bit_cast(bf16x8, i32x4{(int)h0, (int)h1, (int)h2, (int)h3});
+    if constexpr (PAIR) {
+      const f16x8 hv = __builtin_bit_cast(f16x8, hi);
+      const uint32_t l0 = f16_pair_bits(w0[0] - (float)hv[0], w0[1] - (float)hv[1]);
+      const uint32_t l1 = f16_pair_bits(w0[2] - (float)hv[2], w0[3] - (float)hv[3]);
+      const uint32_t l2 = f16_pair_bits(w1[0] - (float)hv[4], w1[1] - (float)hv[5]);
+      const uint32_t l3 = f16_pair_bits(w1[2] - (float)hv[6], w1[3] - (float)hv[7]);
+      lo = __builtin_bit_cast(bf16x8, i32x4{(int)l0, (int)l1, (int)l2, (int)l3});
+    }
   } else {
     split8(w0, w1, hi, lo);
   }

@@ -272,8 +272,14 @@ int vs_mask_init(vs_mask* m, void* buf, size_t bytes, int Hq, int Hkv, vs_layout
  * shard src = (rank - step) mod P) from the shared index (review page 1,
  * section 三.2 item 3). vert_idx/slash_idx rows have strides vert_stride /
  * slash_stride (elements) and hold vert_cnt[h] / slash_cnt[h] ascending
- * entries. Fills every array of `m`; on tile-list overflow writes
- * VS_ERR_CAPACITY to m->status and leaves the lists unspecified. */
+ * entries. Fills every array of `m`. If the tile lists need more than
+ * m->tile_cap entries, the device writes VS_ERR_CAPACITY to m->status and
+ * leaves every list empty (tile_ptr and csc_ptr all zero, vloc_cnt and
+ * vert_end zero; n_active still holds the exact counts), so attention calls
+ * queued behind it on the stream read no list entry and compute nothing for
+ * the step (vs_attn_fwd then writes O = 0, LSE = -inf, or leaves an
+ * accumulating merge unchanged). The caller reads the status word after
+ * synchronising. */
 int vs_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
                   const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
                   int rank, int step, vs_mask* m, void* stream);
@@ -359,6 +365,12 @@ int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout,
  *   VS_BWD_DKDV  -- dk/dv of the keys inside listed slash tiles (key-major
  *                   over the CSC lists; plain read-modify-write);
  *   VS_BWD_DKDV_VERT -- dk/dv of the vertical columns (fp32 atomics).
+ * At D = 128 (bf16 and fp16 operands) a head's vertical columns belong to
+ * VS_BWD_DKDV_VERT over every causal row, also inside that head's listed
+ * tiles, which VS_BWD_DKDV then leaves out: a vertical column sums its
+ * weights over up to the whole sequence, and that part forms the products
+ * with hi + lo weight pairs. (D = 64 and fp32 keep such entries in the tile
+ * part.) The sum of the two parts is the same gradient either way.
  * `parts` is an OR of these; VS_BWD_ALL is vs_attn_bwd. Parts that write the
  * same array (the two dk/dv parts) must not run concurrently.
  * With VS_BWD_OVERWRITE also set, the VS_BWD_DQ and VS_BWD_DKDV parts write

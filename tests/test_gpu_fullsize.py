@@ -9,7 +9,12 @@ the small index tests). Checked per workload:
     oracle's attention over each row's whole active key set;
   * dK and dV of the last key blocks: keys there are attended only by rows
     at or after them, so the oracle gets their exact gradients from those
-    few rows (slash tiles and vertical columns both contribute).
+    few rows (slash tiles and vertical columns both contribute);
+  * for one whole kv group (the contiguous workloads): O, LSE and dQ of every
+    row of its q heads and dK, dV of every key, from the oracle run block by
+    block in worker processes, and the planted outlier keys plus the
+    most-attended vertical columns once more in column order with the
+    componentwise bound of rounding P and dS beside the error.
 The ring case runs one rank's full ring (every step) at P = 32.
 """
 import math
@@ -25,6 +30,7 @@ from oracle import index as oi
 from oracle import layout as ol
 from oracle import mask as om
 from synth import config_by_name, generate
+from tests import fullsize_group as fg
 
 pytestmark = pytest.mark.gpu
 
@@ -44,17 +50,7 @@ def _oracle_index(t, cfg):
     return ref
 
 
-def _candidate_cols(rows, vert_h, slash_h):
-    """A superset of the keys the rows can attend (their verticals and the key
-    blocks on their selected block diagonals, up to the last row); the oracle's
-    active() is then evaluated on these columns only (exact: every other
-    column is inactive by definition)."""
-    qb = np.unique(rows // 64)
-    kb = np.unique((qb[:, None] - np.asarray(slash_h, dtype=np.int64)[None, :]).ravel())
-    kb = kb[kb >= 0]
-    cols = np.concatenate([np.asarray(vert_h, dtype=np.int64), (kb[:, None] * 64 + np.arange(64)[None, :]).ravel()])
-    cols = np.unique(cols)
-    return cols[cols <= rows.max()]
+_candidate_cols = fg.candidate_cols
 
 
 def _rows_check(t, cfg, vert, slash, rows_of, got, heads, blocks):
@@ -167,19 +163,42 @@ def _tail_kv_check(t, cfg, vert, slash, row_lo, dk_of, dv_of, rows_filter=None, 
     return (float(np.abs(dk_of(keys)[ks] - ref_dk[ks]).max()), float(np.abs(dv_of(keys)[ks] - ref_dv[ks]).max()))
 
 
-def _contig_case(name, comps=("bf16",)):
+_CACHE = {}
+
+
+def _inputs_and_scores(name):
+    """The workload's inputs and the oracle's index scores (which do not
+    depend on the budget), kept for the next case of the same workload."""
+    if name not in _CACHE:
+        _CACHE.clear()
+        cfg = config_by_name(name)
+        _log(f"{name}: generating N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv}")
+        t = generate(cfg)
+        _log(f"{name}: oracle index scores")
+        _CACHE[name] = (t, _oracle_index(t, cfg))
+    return _CACHE[name]
+
+
+def _contig_case(name, comps=("bf16",), top_p=None, whole_group=True, mask_heads=None):
     """comps: operand formats of the attention kernels checked on the same
     index and oracle rows: "bf16" (the inputs as given, hi + lo weights) and
-    "f16" (exact fp16 copies made by vs_convert_f16, single fp16 weights)."""
+    "f16" (exact fp16 copies made by vs_convert_f16, single fp16 weights).
+    top_p: another budget than the workload's (the oracle selection is
+    re-run on the same scores). mask_heads: also compare the GPU's tile
+    lists, vertical columns and counts of sampled query blocks of these heads
+    bit for bit with the oracle's description. whole_group: run the
+    whole-group check."""
     import dynamic_sparse_attention_index_amd as vs
     from tests import vs_harness as H
-    cfg = config_by_name(name)
+    cfg = config_by_name(name) if top_p is None else config_by_name(name, top_p=top_p)
     N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
     T = N // 64
-    _log(f"{name}: generating N={N} Hq={Hq} Hkv={Hkv}")
-    t = generate(cfg)
-    _log(f"{name}: oracle index")
-    ref = _oracle_index(t, cfg)
+    t, scores = _inputs_and_scores(name)
+    ref = dict(scores)
+    if top_p is not None:
+        ref["vert"] = [oi.select_top_p(ref["v"][h], top_p) for h in range(Hq)]
+        ref["slash"] = [oi.select_top_p(ref["s"][h], top_p) for h in range(Hq)]
+    _log(f"{name}: p = {cfg.top_p}, oracle sparsity {float(om.sparsity(N, ref['vert'], ref['slash']).mean()):.4f}")
     dev = "cuda"
     q, k, v, do = (H.to_dev(t[x], cfg.dtype) for x in ("q", "k", "v", "do"))
     lay = vs.layout("contig", 1, N)
@@ -188,7 +207,23 @@ def _contig_case(name, comps=("bf16",)):
     vert, slash = ref["vert"], ref["slash"]
     m = H.gpu_mask(H.upload_lists(vert, slash, N), Hq, Hkv, lay, 0, 0, H.tile_cap_for(slash, Hq, T))
     assert int(m.arrays()["status"].item()) == 0
-    gots, dks, dvs = {}, [], []
+    if mask_heads is not None:
+        rng = np.random.default_rng(cfg.seed + 5)
+        mblocks = sorted(set([0, T - 1] + rng.choice(T, 4, replace=False).tolist()))
+        _log(f"{name}: GPU mask vs oracle description, heads {mask_heads}, blocks {mblocks}")
+        a = H.mask_to_numpy(m)
+        desc = om.step_description("contig", N, 1, 0, 0, vert, slash, heads=mask_heads, blocks=mblocks)
+        for h in mask_heads:
+            assert np.array_equal(a["vloc"][h * T * 64:h * T * 64 + a["vloc_cnt"][h]], desc["vloc"][h])
+            for I in mblocks:
+                b = desc["blocks"][(h, I)]
+                u = h * T + I
+                got = a["tile_col"][a["tile_ptr"][u]:a["tile_ptr"][u + 1]]
+                assert got.tolist() == [J | (0x40000000 if d else 0) for J, d in zip(b["tiles"], b["diag"])]
+                assert a["vert_end"][u] == b["vert_end"] and a["n_active"][u] == b["n_active"]
+        assert int(a["n_active"].sum()) == sum(om.active_count(N, vert[h], slash[h]) for h in range(Hq))
+    gots, dks, dvs, group = {}, [], [], {}
+    R = Hq // Hkv
     for comp in comps:
         _log(f"{name}: GPU mask + forward + backward (oracle index), {comp} operands")
         ops = [H.as_f16(x) for x in (q, k, v, do)] if comp == "f16" else [q, k, v, do]
@@ -207,6 +242,9 @@ def _contig_case(name, comps=("bf16",)):
         dk_h, dv_h = dk.cpu().numpy(), dv.cpu().numpy()
         dks.append(lambda keys, a=dk_h: a[:, keys])
         dvs.append(lambda keys, a=dv_h: a[:, keys])
+        hs = slice(GROUP * R, (GROUP + 1) * R)
+        group[comp] = {"o": gots[comp]["o"][hs], "lse": gots[comp]["lse"][hs], "dq": gots[comp]["dq"][hs],
+                       "dk": dk_h[GROUP], "dv": dv_h[GROUP]}
         del o, lse, delta, dq, dk, dv
     rng = np.random.default_rng(cfg.seed + 77)
     heads = sorted(set([0, Hq - 1] + rng.choice(Hq, 2, replace=False).tolist()))
@@ -226,19 +264,69 @@ def _contig_case(name, comps=("bf16",)):
     for comp, ek, ev in zip(comps, eks, evs):
         w = ws[comp]
         assert max(w["o"], w["lse"], w["dq"], ek, ev) <= TOL, (comp, w, ek, ev)
+    if whole_group:
+        _whole_group_check(name, t, cfg, ref, group)
 
 
-@pytest.mark.timeout(600)
+GROUP = 0   # the kv group checked whole
+
+
+def _whole_group_check(name, t, cfg, ref, group):
+    """Every row of kv group GROUP's q heads and every key of the group, then
+    the outlier and most-attended vertical columns with their bounds."""
+    Hq, Hkv, N = cfg.Hq, cfg.Hkv, cfg.N
+    R = Hq // Hkv
+    hs = list(range(GROUP * R, (GROUP + 1) * R))
+    vert, slash = ref["vert"], ref["slash"]
+    _log(f"{name}: whole-group oracle, kv group {GROUP} ({R} q heads x {N} rows, every key)")
+    err, lse, delta, dk_ref, dv_ref = fg.whole_group(t, GROUP, Hq, Hkv, vert, slash, cfg.scale, group, log=_log)
+    for comp, e in err.items():
+        _log(f"{name} [{comp}] whole group: max errors O {e['o']:.3e} LSE {e['lse']:.3e} dQ {e['dq']:.3e} "
+             f"dK {e['dk']:.3e} dV {e['dv']:.3e}")
+    # the planted outlier keys and the group's 16 most-attended vertical columns
+    top = np.argsort(-ref["v"][hs].astype(np.float64).sum(axis=0), kind="stable")[:16]
+    cols = np.unique(np.concatenate([t["outliers"], top])).astype(np.int64)
+    q, do = t["q"][hs], t["do"][hs]
+    ck, cv, abs_k, abs_v = fg.column_sums(q, t["k"][GROUP], t["v"][GROUP], do, [vert[h] for h in hs],
+                                          [slash[h] for h in hs], lse, delta, cols, cfg.scale)
+    # the two oracle summation orders (row blocks vs columns) agree
+    assert np.abs(ck - dk_ref[cols]).max() <= 1e-9 * max(1.0, np.abs(ck).max())
+    assert np.abs(cv - dv_ref[cols]).max() <= 1e-9 * max(1.0, np.abs(cv).max())
+    for comp, e in err.items():
+        for what, got, ref_c, bnd in (("dK", group[comp]["dk"][cols], ck, abs_k),
+                                      ("dV", group[comp]["dv"][cols], cv, abs_v)):
+            d = np.abs(got - ref_c)
+            i = np.unravel_index(np.argmax(d), d.shape)
+            b8 = 2.0 ** -8 * bnd
+            ratio = float((d / np.maximum(b8, 1e-30)).max())
+            _log(f"{name} [{comp}] {what} on {len(cols)} outlier/vertical columns: max err {d.max():.3e} "
+                 f"(column {cols[i[0]]}, bound 2^-8 sum|terms| there {b8[i]:.3e}); "
+                 f"max err / 2^-8 sum|terms| = {ratio:.3e}; largest sum|terms| {bnd.max():.3e}")
+            e[f"{what.lower()}_cols"] = float(d.max())
+    for comp, e in err.items():
+        assert max(e["o"], e["lse"], e["dq"], e["dk"], e["dv"]) <= TOL, (comp, e)
+
+
+@pytest.mark.timeout(1500)
 def test_fullsize_qwen128k_step():
     """The benchmarked step: 16/2 heads, 131072 tokens, d 128, bf16 inputs,
     fwd + bwd, with bf16 and with fp16 operands."""
     _contig_case("qwen128k", comps=("bf16", "f16"))
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1800)
 def test_fullsize_llama256k_step():
     """32/8 heads, 262144 tokens with Yarn x32 positions, fwd + bwd."""
     _contig_case("llama256k", comps=("bf16", "f16"))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("p", [0.8, 0.99])
+def test_fullsize_llama256k_budget_sweep(p):
+    """The same layer at the other budgets of the sweep (fp16 operands, the
+    benchmarked path): index, sampled mask blocks bit for bit, O / LSE / dQ of
+    sampled rows and the tail dK / dV."""
+    _contig_case("llama256k", comps=("f16",), top_p=p, whole_group=False, mask_heads=[0, 31])
 
 
 @pytest.mark.timeout(900)
@@ -252,6 +340,7 @@ def test_fullsize_qwen512k_ring_rank(kind, rank):
     N, Hq, Hkv, D, P = cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P
     T = N // 64
     QB = T // P
+    _CACHE.clear()
     _log(f"512k {kind} rank {rank}: generating")
     t = generate(cfg)
     _log("512k: oracle index")
