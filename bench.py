@@ -213,6 +213,18 @@ def main():
     n_diag = int(((tcol & vs.TILE_DIAG) != 0).sum())
     A_slash = 4096 * (len(tcol) - n_diag) + 2080 * n_diag     # entries inside listed slash tiles
     A_vert = A - A_slash                                       # vertical entries outside them
+    # entries the kernels compute: every listed tile whole (the diagonal
+    # tile's upper half is masked), and the vertical columns of a query block
+    # gathered 64 at a time into whole 64 x 64 tiles
+    vend = arrs["vert_end"].cpu().numpy().astype(np.int64)
+    computed_slash = 4096 * len(tcol)
+    computed_vert = 4096 * int(((vend + 63) // 64).sum())
+    tile_fill = {"slash_tiles": round(A_slash / max(computed_slash, 1), 4),
+                 "vertical_chunks": round(A_vert / max(computed_vert, 1), 4),
+                 "all": round(A / max(computed_slash + computed_vert, 1), 4),
+                 "computed_entries": computed_slash + computed_vert,
+                 "note": "active entries / entries the forward and dQ kernels compute (whole 64x64 tiles: "
+                         "listed slash tiles, and vertical columns gathered 64 per tile)"}
     total_causal = Hq * N * (N + 1) // 2
     sparsity = 1.0 - A / total_causal
     eff_flops = (4 + (10 if cfg.backward else 0)) * D * A
@@ -249,9 +261,17 @@ def main():
                           "frac_mfma_peak": round(tf / peak, 4)}
     dom = max(per_kernel, key=lambda x: per_kernel[x]["ms"])
     dk_name, dk_flops = kernels[dom]
+    # strict count (no recomputation credited): forward 4 d, dK/dV 6 d (dP, dV,
+    # dK), dQ 2 d, vertical dK/dV 6 d
+    strict_per = {"fwd": 4, "dq": 2, "dkdv": 6, "dkdv_vert": 6}
+    strict_flops = strict_per[dom] * D * (A_slash if dom == "dkdv" else A_vert if dom == "dkdv_vert" else A)
     roofline = {"kernel": dk_name, "bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": peak,
                 "unit": "TFLOP/s", "frac": per_kernel[dom]["frac_mfma_peak"],
-                "traffic": stored_traffic(dk_name), "algorithmic_flops_per_launch": dk_flops,
+                "traffic": stored_traffic(dk_name),
+                "traffic_kind": "bytes per launch between L2 and the data fabric (FETCH_SIZE + WRITE_SIZE, "
+                                "scaled by a copy of known size): HBM plus Infinity Cache hits",
+                "algorithmic_flops_per_launch": dk_flops,
+                "frac_strict": round(strict_flops / (stage_ms[dom] * 1e-3) / 1e12 / peak, 4),
                 "mean_launch_ms": round(stage_ms[dom], 4)}
 
     # Index pass (scores + top-p): algorithmic bytes = K read once + the last
@@ -283,7 +303,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16" if f16 else cfg.dtype, "data": "synthetic",
         "inputs": cfg.dtype,
-        "operands": ("fp16 copies of the bf16 inputs (exact; converted inside the step), single fp16 P/dS, "
+        "operands": ("fp16 copies of the bf16 inputs (exact for 2^-17 <= |x| < 65536, smaller magnitudes "
+                     "rounded to 2^-24 spacing; converted inside the step), single fp16 P/dS, "
                      "fp32 accumulation") if f16 else f"{cfg.dtype} inputs as given",
         "bwd_streams": args.bwd_streams,
         "config": {"workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "seq_len": N, "head_dim": D,
@@ -293,7 +314,7 @@ def main():
         "attn_only_tflops": round(attn_tflops, 3),
         "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
         "kernels": per_kernel,
-        "active_entries": A, "active_slash_tiles": A_slash, "active_vertical": A_vert,
+        "active_entries": A, "active_slash_tiles": A_slash, "active_vertical": A_vert, "tile_fill": tile_fill,
         "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
         "strict_algorithmic_tflops": round(strict_tflops, 3), "index_pass": index_pass,
         "roofline": roofline, "cpu_baseline": cpu, "budgets": budgets, "gqa_packed": packed,
@@ -528,6 +549,7 @@ def ring_report(args, cfg):
         t_mask = np.zeros((args.ring_reps, P, P))
         t_fwd = np.zeros((args.ring_reps, P, P))
         t_bwd = np.zeros((args.ring_reps, P, P))
+        t_prep = np.zeros((args.ring_reps, P))
         act = np.zeros((P, P), dtype=np.int64)
         o = torch.empty(Hq, QB * 64, D, device=dev)
         lse = torch.empty(Hq, QB * 64, device=dev)
@@ -571,7 +593,7 @@ def ring_report(args, cfg):
                     e_f = timed(lambda: vs.vs_attn_fwd(qr, ak[:, cols], av[:, cols], m, cfg.scale, o, lse, 1, stream))
                     masks.append(m)
                     evs.append((e_m, e_f))
-                vs.vs_attn_bwd_prep(o, dor, delta, stream)
+                e_p = timed(lambda: vs.vs_attn_bwd_prep(o, dor, delta, stream))
                 ebs = []
                 for st in range(P):
                     src = (r - st) % P
@@ -580,6 +602,7 @@ def ring_report(args, cfg):
                                                       dv[src])))
                 torch.cuda.synchronize()
                 if rep >= 0:
+                    t_prep[rep, r] = e_p[0].elapsed_time(e_p[1])
                     for st in range(P):
                         (a, b), (c, d) = evs[st]
                         t_mask[rep, r, st] = a.elapsed_time(b)
@@ -593,11 +616,16 @@ def ring_report(args, cfg):
                         act[r, st] = int(arr["n_active"].sum().item())
                 del masks
         tm, tf, tb = (np.median(x, axis=0) for x in (t_mask, t_fwd, t_bwd))
+        tp = np.median(t_prep, axis=0)                 # per rank, once per ring
         t = tf + tb                                    # attention time of step s on rank r
         mean_r = t.mean(axis=0)
         max_r = t.max(axis=0)
         cmean, cmax = act.mean(axis=0), act.max(axis=0)
         ring_ms = float(max_r.sum())                   # the ring waits for the slowest rank each step
+        # the whole ring of a rank: every step's active region, forward and
+        # backward (slowest rank per step) plus the rank's one delta pass
+        tall = tm + tf + tb
+        ring_all_ms = float(tall.max(axis=0).sum() + tp.max())
         A_total = int(act.sum())
         # merge: separate kernel vs fused into the forward, rank 0's steps
         o_step = torch.empty_like(o)
@@ -636,8 +664,11 @@ def ring_report(args, cfg):
             "ring_time_imbalance": round(float(max_r.sum() / mean_r.sum()), 4),
             "worker_total_imbalance": round(float(t.sum(axis=1).max() / t.sum(axis=1).mean()), 4),
             "ring_ms_fwd_bwd": round(ring_ms, 3),
-            "per_gpu_tokens_per_s": round((N / P) / (ring_ms * 1e-3), 1),
-            "per_gpu_effective_tflops": round(14 * D * A_total / P / (ring_ms * 1e-3) / 1e12, 2),
+            "ring_ms_with_mask_and_prep": round(ring_all_ms, 3),
+            "bwd_prep_ms_per_rank": round(float(tp.mean()), 4),
+            "per_gpu_tokens_per_s": round((N / P) / (ring_all_ms * 1e-3), 1),
+            "per_gpu_effective_tflops": round(14 * D * A_total / P / (ring_all_ms * 1e-3) / 1e12, 2),
+            "per_gpu_effective_tflops_attention_only": round(14 * D * A_total / P / (ring_ms * 1e-3) / 1e12, 2),
             "active_entries": A_total,
             "merge_fused_ms_per_step": round(float(np.mean(fused)), 4),
             "merge_separate_ms_per_step": round(float(np.mean(split)), 4),
@@ -661,9 +692,10 @@ def ring_report(args, cfg):
 
 
 def stored_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/counters.json: FETCH_SIZE and WRITE_SIZE runs scaled by the
-    same counters' reading for a copy of known size), or None when absent or
+    """L2-to-fabric bytes per launch of `kernel` (HBM traffic plus Infinity
+    Cache hits) from the committed counter summary (profiles/counters.json:
+    FETCH_SIZE and WRITE_SIZE runs scaled by the same counters' reading for a
+    copy of known size), or None when absent or
     when the kernel's source file or the shared kernel headers have changed
     since the counters were taken (one SHA-256 over all of them)."""
     import hashlib
@@ -681,7 +713,7 @@ def stored_traffic(kernel):
         h.update(open(path, "rb").read())
     if h.hexdigest() != rec["source_sha256"]:
         return None
-    return int(rec["hbm_bytes_per_launch"])
+    return int(rec["l2_miss_bytes_per_launch"])
 
 
 def copy_probe():
@@ -699,55 +731,95 @@ def copy_probe():
 
 
 def cpu_baseline(cfg, host, vidx, vcnt, sidx, scnt, seconds, tflops_unit=True):
-    """Time the fp64 oracle on a bounded sample of the same workload on host cores.
+    """Time the fp64 oracle on the host cores on the same workload.
 
-    Sample: the index step for a subset of q heads, and forward+backward of a
-    seeded set of (head, query block) items, extrapolated linearly to the whole
-    step by head count and by active entries.
+    Index: the oracle's index step over every q head, in full. Active region:
+    the oracle's per-block description (tile list, vertical prefix, active
+    count) of a seeded sample of (head, query block) items, extrapolated by
+    item count. Attention: forward (+ backward) of random (head, 64-row block)
+    items for about `seconds`, extrapolated linearly in active entries. The
+    attention sample runs again with BLAS limited to one thread (a third of
+    the time budget) for a single-thread figure.
     """
     import torch  # noqa: F401  (for .cpu())
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import index as oi
     from oracle import attention as oa
     from oracle import mask as om
 
     N, Hq, Hkv, D = cfg.N, cfg.Hq, cfg.Hkv, cfg.D
     cores = len(os.sched_getaffinity(0))
+    blas = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+    blas_threads = max((int(x["num_threads"]) for x in blas), default=None)
     vc, sc = vcnt.cpu().numpy(), scnt.cpu().numpy()
     vert = [vidx[h, :vc[h]].cpu().numpy().astype(np.int64) for h in range(Hq)]
     slash = [sidx[h, :sc[h]].cpu().numpy().astype(np.int64) for h in range(Hq)]
-    # index: one head
+    QB = N // 64
+    # index, every head
     t0 = time.perf_counter()
-    oi.build_index(host["q"][:1, N - cfg.last_q:], host["k"][:1], cfg.scale, N, cfg.top_p)
-    t_index = (time.perf_counter() - t0) * Hq
-    # attention fwd+bwd on random blocks until the time budget is used
-    rng = np.random.default_rng(0)
-    pos = np.arange(N)
-    done_active, t_attn = 0, 0.0
-    items = 0
-    while t_attn < seconds and items < 4096:
-        h = int(rng.integers(Hq))
-        I = int(rng.integers(N // 64))
-        g = h * Hkv // Hq
-        rows = pos[64 * I:64 * I + 64]
+    oi.build_index(host["q"][:, N - cfg.last_q:], host["k"], cfg.scale, N, cfg.top_p)
+    t_index = time.perf_counter() - t0
+    # active region, sampled blocks
+    rng = np.random.default_rng(1)
+    n_mask = 0
+    t_mask = 0.0
+    while t_mask < seconds / 6 and n_mask < 256:
+        h, I = int(rng.integers(Hq)), int(rng.integers(QB))
         t0 = time.perf_counter()
-        M, _, _ = om.active(rows, pos, vert[h], slash[h])
-        used = M.any(axis=0)
-        kk, vv = host["k"][g, used], host["v"][g, used]
-        oa.forward_rows(host["q"][h, rows], kk, vv, M[:, used], cfg.scale)
-        if cfg.backward:
-            oa.backward_rows(host["q"][h, rows], kk, vv, M[:, used], cfg.scale, host["do"][h, rows])
-        t_attn += time.perf_counter() - t0
-        done_active += int(M.sum())
-        items += 1
+        om.step_description("contig", N, 1, 0, 0, vert, slash, heads=[h], blocks=[I])
+        t_mask += time.perf_counter() - t0
+        n_mask += 1
+    t_mask_full = t_mask * Hq * QB / max(n_mask, 1)
+    pos = np.arange(N)
+
+    def attn_sample(budget, seed):
+        rng = np.random.default_rng(seed)
+        done_active, t_attn, items = 0, 0.0, 0
+        while t_attn < budget and items < 4096:
+            h = int(rng.integers(Hq))
+            I = int(rng.integers(QB))
+            g = h * Hkv // Hq
+            rows = pos[64 * I:64 * I + 64]
+            t0 = time.perf_counter()
+            M, _, _ = om.active(rows, pos, vert[h], slash[h])
+            used = M.any(axis=0)
+            kk, vv = host["k"][g, used], host["v"][g, used]
+            oa.forward_rows(host["q"][h, rows], kk, vv, M[:, used], cfg.scale)
+            if cfg.backward:
+                oa.backward_rows(host["q"][h, rows], kk, vv, M[:, used], cfg.scale, host["do"][h, rows])
+            t_attn += time.perf_counter() - t0
+            done_active += int(M.sum())
+            items += 1
+        return t_attn, done_active, items
+
     A_total = sum(om.active_count(N, vert[h], slash[h]) for h in range(Hq))
+    t_attn, done_active, items = attn_sample(seconds, 0)
     t_attn_full = t_attn * A_total / max(done_active, 1)
-    t_total = t_index + t_attn_full
+    with threadpool_limits(1):
+        t1, done1, items1 = attn_sample(seconds / 3, 2)
+        t0 = time.perf_counter()
+        oi.build_index(host["q"][:1, N - cfg.last_q:], host["k"][:1], cfg.scale, N, cfg.top_p)
+        t_index1 = (time.perf_counter() - t0) * Hq
+    t_attn1_full = t1 * A_total / max(done1, 1)
+    t_total = t_index + t_mask_full + t_attn_full
+    t_total1 = t_index1 + t_mask_full + t_attn1_full
     eff = (4 + (10 if cfg.backward else 0)) * D * A_total
-    return {"value": round(eff / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "tokens_per_s": round(N / t_total, 3), "seconds_measured": round(t_attn + t_index / Hq, 1),
-            "sample": f"index step of 1 of {Hq} q heads (x{Hq}); fwd+bwd of {items} random (head, 64-row "
-                      f"block) items = {done_active} of {A_total} active entries, extrapolated linearly "
-                      f"in active entries; numpy fp64"}
+    return {"value": round(eff / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "blas_threads": blas_threads, "kind": "oracle",
+            "tokens_per_s": round(N / t_total, 3),
+            "stage_s": {"index": round(t_index, 2), "mask_extrapolated": round(t_mask_full, 1),
+                        "attention_extrapolated": round(t_attn_full, 1)},
+            "seconds_measured": round(t_index + t_mask + t_attn + t1 + t_index1 / Hq, 1),
+            "single_thread": {"value": round(eff / t_total1 / 1e12, 6), "unit": "TFLOP/s", "blas_threads": 1,
+                              "stage_s": {"index_extrapolated": round(t_index1, 2),
+                                          "attention_extrapolated": round(t_attn1_full, 1)},
+                              "sample": f"index step of 1 of {Hq} q heads (x{Hq}); fwd+bwd of {items1} random "
+                                        f"items = {done1} active entries, extrapolated; the active-region "
+                                        f"time of the threaded run"},
+            "sample": f"index step of all {Hq} q heads in full; active-region description of {n_mask} random "
+                      f"(head, 64-row block) items of {Hq * QB}, extrapolated by item count; fwd+bwd of {items} "
+                      f"random (head, block) items = {done_active} of {A_total} active entries, extrapolated "
+                      f"linearly in active entries; numpy fp64, BLAS threads {blas_threads}"}
 
 
 if __name__ == "__main__":

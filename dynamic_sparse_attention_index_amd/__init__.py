@@ -17,7 +17,9 @@ import torch
 
 from . import _build
 
-LIB_PATH = _build.LIB
+# VS_ATTN_LIB names another build of the same library (the host-sanitizer
+# build of the ABI checks); by default the in-tree libvsattn.so is loaded.
+LIB_PATH = os.environ.get("VS_ATTN_LIB", _build.LIB)
 
 VS_OK, VS_ERR_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_CAPACITY, VS_ERR_HIP = 0, -1, -2, -3, -4, -5
 VS_ERR_RANGE = -6
