@@ -33,7 +33,7 @@ EXPORTED = [
     "vs_index_select_workspace_size", "vs_index_select", "vs_index_select_budget", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
     "vs_convert_f16", "vs_index_select_group_workspace_size", "vs_index_select_group", "vs_attn_fwd_packed",
-    "vs_attn_bwd_prep_f16",
+    "vs_attn_bwd_prep_f16", "vs_index_build_noalloc",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
 
@@ -85,6 +85,8 @@ def lib():
         L.vs_index_workspace_size.argtypes = [i32, i32, i64, i32, i32]
         L.vs_index_build.restype = i32
         L.vs_index_build.argtypes = [VsTensor, VsTensor, VsLayout, f32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.vs_index_build_noalloc.restype = i32
+        L.vs_index_build_noalloc.argtypes = [VsTensor, VsTensor, VsLayout, f32, f32, vp, vp, vp, vp, vp, vp, vp]
         L.vs_index_rank_stats.restype = i32
         L.vs_index_rank_stats.argtypes = [VsTensor, VsTensor, VsLayout, i32, f32, vp, vp, sz, vp]
         L.vs_index_rank_mass.restype = i32
@@ -187,6 +189,16 @@ def vs_index_build(q_last, k, lay: VsLayout, scale, top_p, vert_score, slash_sco
                                 _ptr(slash_score), _ptr(vert_idx), _ptr(vert_cnt), _ptr(slash_idx),
                                 _ptr(slash_cnt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "vs_index_build")
+
+
+def vs_index_build_noalloc(q_last, k, lay: VsLayout, scale, top_p, vert_score, slash_score, vert_idx, vert_cnt,
+                           slash_idx, slash_cnt, stream=None):
+    """vs_index_build with the library's own per-GPU scratch instead of a
+    caller workspace (no allocation in the call)."""
+    _check(lib().vs_index_build_noalloc(as_vs_tensor(q_last), as_vs_tensor(k), lay, scale, top_p, _ptr(vert_score),
+                                        _ptr(slash_score), _ptr(vert_idx), _ptr(vert_cnt), _ptr(slash_idx),
+                                        _ptr(slash_cnt), _stream(stream)),
+           "vs_index_build_noalloc")
 
 
 def vs_index_rank_stats(q_last, k_local, lay: VsLayout, rank, scale, stats, ws, stream=None):

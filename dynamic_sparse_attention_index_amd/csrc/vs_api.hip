@@ -2,6 +2,8 @@
 // No device memory is allocated here; every buffer comes from the caller.
 #include <string.h>
 
+#include <mutex>
+
 #include "vs_common.h"
 #include "vs_internal.h"
 
@@ -121,6 +123,48 @@ int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, fl
   return launch_index_build(k.dtype, D, view(q_last), Hq, last_q, view(k), Hkv, lay, scale, top_p, vert_score,
                             slash_score, vert_idx, vert_cnt, slash_idx, slash_cnt, ws, ws_bytes,
                             (hipStream_t)stream);
+}
+
+// ---- the index build without a caller workspace ---------------------------
+// Scratch of vs_index_build_noalloc: one copy per GPU the library runs on,
+// held until the process ends. Host code never uses the array's name as an
+// address (that is a host-side stand-in): each device's address is looked up
+// once with hipGetSymbolAddress, with that device current, and kept.
+static __device__ __align__(256) char scratch[VS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// This device's scratch address (looked up on its first use), or null.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+int vs_index_build_noalloc(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, float top_p,
+                           float* vert_score, float* slash_score, int32_t* vert_idx, int32_t* vert_cnt,
+                           int32_t* slash_idx, int32_t* slash_cnt, void* stream) {
+  int st;
+  if ((st = check_layout(lay)) != VS_OK) return st;
+  const int Hq = q_last.H, Hkv = k.H, D = q_last.D, last_q = (int)q_last.N;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return VS_ERR_ARG;
+  // the size check comes first so that it needs no device
+  if (vs_index_workspace_size(Hq, Hkv, lay.n_global, D, last_q) > (size_t)VS_NOALLOC_SCRATCH_BYTES)
+    return VS_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return VS_ERR_HIP;
+  return vs_index_build(q_last, k, lay, scale, top_p, vert_score, slash_score, vert_idx, vert_cnt, slash_idx,
+                        slash_cnt, ws, (size_t)VS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // Checks shared by the per-rank index calls; on success sets the dims.

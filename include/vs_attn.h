@@ -163,6 +163,24 @@ int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, fl
                    int32_t* slash_idx, int32_t* slash_cnt,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* vs_index_build for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, whose role a scratch array
+ * inside the library takes: VS_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held
+ * from the first call on that GPU until the process ends. The call itself
+ * allocates nothing. Calls whose vs_index_workspace_size exceeds the scratch
+ * return VS_ERR_WORKSPACE before any device work (it holds Hq = 128 q heads
+ * at 2^20 tokens). Every call on one GPU uses that GPU's one scratch array:
+ * calls that overlap on a GPU (concurrent streams or host threads) race and
+ * must be serialised by the caller; consecutive calls on one stream are
+ * safe (nothing in the scratch needs to start at zero: every pass writes
+ * what it reads). VS_ERR_HIP if the device's scratch address cannot be
+ * looked up. Results equal vs_index_build's bit for bit. */
+#define VS_NOALLOC_SCRATCH_BYTES (16 << 20)
+int vs_index_build_noalloc(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, float top_p,
+                           float* vert_score, float* slash_score, int32_t* vert_idx, int32_t* vert_cnt,
+                           int32_t* slash_idx, int32_t* slash_cnt, void* stream);
+
 /* The same index built the distributed way (review page 1, section 三.2
  * item 1: the scored queries are broadcast and every rank scores them
  * against the keys it holds). Per rank r, with exchanges between the calls:

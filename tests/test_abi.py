@@ -244,3 +244,18 @@ def test_group_packed_and_fused_prep_validation(L):
     assert L.vs_attn_bwd_prep_f16(p, a16, a16, 4, 1024, 96, p, st, None) == vs.VS_ERR_UNSUPPORTED
     assert L.vs_attn_bwd_prep_f16(p, ctypes.c_void_p(0x20000002), a16, 4, 1024, 128, p, st,
                                   None) == vs.VS_ERR_UNSUPPORTED
+
+
+def test_index_noalloc_rejects_beyond_scratch(L):
+    """The entry point without a workspace refuses an index whose workspace
+    would exceed its 16 MiB per-GPU scratch, before any device work."""
+    N, Hq, Hkv, D = 1 << 20, 512, 64, 128
+    assert vs.index_workspace_size(Hq, Hkv, N, D) > 16 << 20
+    lay = vs.layout("contig", 1, N)
+    fake = 0x10000000   # never dereferenced: the size check returns first
+    q = _fake_tensor(fake, Hq, 64, D)
+    k = _fake_tensor(fake, Hkv, N, D)
+    assert L.vs_index_build_noalloc(q, k, lay, 0.088, 0.9, fake, fake, fake, fake, fake, fake, None) == \
+        vs.VS_ERR_WORKSPACE
+    # and the largest supported shape fits
+    assert vs.index_workspace_size(128, 16, N, D) <= 16 << 20
