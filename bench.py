@@ -627,6 +627,33 @@ def ring_report(args, cfg):
         tall = tm + tf + tb
         ring_all_ms = float(tall.max(axis=0).sum() + tp.max())
         A_total = int(act.sum())
+        # resident mode: a rank's masks of every step built up front, then the
+        # forward of all its steps in one launch (the online softmax carried
+        # across the steps in the kernel: no per-step merge) and the backward
+        # of all its steps in one call; k/v hold every shard in storage order
+        res_masks = [vs.Mask(Hq, Hkv, lay, cap) for _ in range(P)]
+        dk_res = torch.empty(Hkv, N, D, device=dev)
+        dv_res = torch.empty(Hkv, N, D, device=dev)
+        t_res = np.zeros((args.ring_reps, P, 4))      # mask, fwd, prep, bwd per rank
+        for rep in range(-1, args.ring_reps):
+            for r in range(P):
+                rows = slice(r * QB * 64, (r + 1) * QB * 64)
+                qr, dor = aq[:, rows], ado[:, rows]
+                e_m = timed(lambda: [vs.vs_block_mask(vidx, vcnt, sidx, scnt, r, st, res_masks[st], stream)
+                                     for st in range(P)])
+                e_f = timed(lambda: vs.vs_attn_fwd_ring(qr, ak, av, res_masks, cfg.scale, o, lse, 0, stream))
+                e_p = timed(lambda: vs.vs_attn_bwd_prep(o, dor, delta, stream))
+                e_b = timed(lambda: vs.vs_attn_bwd_ring(qr, ak, av, dor, lse, delta, res_masks, cfg.scale, dq, dk_res,
+                                                        dv_res, vs.VS_BWD_ALL | vs.VS_BWD_OVERWRITE, stream))
+                torch.cuda.synchronize()
+                if rep >= 0:
+                    for i, (a_, b_) in enumerate((e_m, e_f, e_p, e_b)):
+                        t_res[rep, r, i] = a_.elapsed_time(b_)
+        tr = np.median(t_res, axis=0)                 # [rank, part]
+        rank_ms = tr.sum(axis=1)
+        res_ms = float(rank_ms.max())
+        A_rank = act.sum(axis=1)
+        del res_masks, dk_res, dv_res
         # merge: separate kernel vs fused into the forward, rank 0's steps
         o_step = torch.empty_like(o)
         l_step = torch.empty_like(lse)
@@ -672,6 +699,14 @@ def ring_report(args, cfg):
             "active_entries": A_total,
             "merge_fused_ms_per_step": round(float(np.mean(fused)), 4),
             "merge_separate_ms_per_step": round(float(np.mean(split)), 4),
+            "resident_ring_ms_max_rank": round(res_ms, 3),
+            "resident_parts_ms_max_rank": {k_: round(float(tr[int(np.argmax(rank_ms)), i]), 3)
+                                           for i, k_ in enumerate(("masks", "fwd", "bwd_prep", "bwd"))},
+            "resident_rank_imbalance": round(float(rank_ms.max() / rank_ms.mean()), 4),
+            "resident_per_gpu_tokens_per_s": round((N / P) / (res_ms * 1e-3), 1),
+            "resident_per_gpu_effective_tflops": round(14 * D * float(A_rank[int(np.argmax(rank_ms))]) /
+                                                       (res_ms * 1e-3) / 1e12, 2),
+            "resident_effective_tflops_mean_rank": round(float(np.mean(14 * D * A_rank / (rank_ms * 1e-3) / 1e12)), 2),
         }
         del q, k, v, do, dk, dv, aq, ak, av, ado
         torch.cuda.empty_cache()
@@ -684,7 +719,13 @@ def ring_report(args, cfg):
                     f" --layouts {args.layouts} --ring-reps {args.ring_reps}"
                     f" --report-md <path>`\n\n")
             f.write("Every rank's ring steps run one after another on the one GPU (communication excluded); "
-                    "times are medians over repetitions of each (rank, step) kernel group timed alone.\n\n")
+                    "times are medians over repetitions of each (rank, step) kernel group timed alone. "
+                    "Per-step mode: one active-region build, one forward (merge fused) and one backward call per "
+                    "step. Resident mode (`resident_*`): a rank's masks of all steps built up front, then one "
+                    "forward launch over all its steps (vs_attn_fwd_ring: the online softmax carried across the "
+                    "steps, O written once) and one backward call (vs_attn_bwd_ring: dQ accumulated across the "
+                    "steps, the key-major parts over every step's shard in one grid); its time per rank is "
+                    "masks + forward + delta + backward.\n\n")
             keys = list(next(iter(out["layouts"].values())).keys())
             f.write("| quantity | " + " | ".join(out["layouts"]) + " |\n|---|" + "---|" * len(out["layouts"]) + "\n")
             for kk in keys:

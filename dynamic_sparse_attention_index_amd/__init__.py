@@ -33,7 +33,7 @@ EXPORTED = [
     "vs_index_select_workspace_size", "vs_index_select", "vs_index_select_budget", "vs_mask_bytes", "vs_mask_init",
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
     "vs_convert_f16", "vs_index_select_group_workspace_size", "vs_index_select_group", "vs_attn_fwd_packed",
-    "vs_attn_bwd_prep_f16", "vs_index_build_noalloc",
+    "vs_attn_bwd_prep_f16", "vs_index_build_noalloc", "vs_attn_fwd_ring", "vs_attn_bwd_ring",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
 
@@ -123,6 +123,12 @@ def lib():
         L.vs_attn_bwd.restype = i32
         L.vs_attn_bwd.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask), f32,
                                   vp, vp, vp, vp]
+        L.vs_attn_fwd_ring.restype = i32
+        L.vs_attn_fwd_ring.argtypes = [VsTensor, VsTensor, VsTensor, ctypes.POINTER(VsMask), i32, f32, vp, vp, i32,
+                                       vp]
+        L.vs_attn_bwd_ring.restype = i32
+        L.vs_attn_bwd_ring.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask), i32,
+                                       f32, vp, vp, vp, i32, vp]
         L.vs_attn_bwd_parts.restype = i32
         L.vs_attn_bwd_parts.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask),
                                         f32, vp, vp, vp, i32, vp]
@@ -344,3 +350,26 @@ def vs_attn_bwd_parts(q, k, v, dout, lse, delta, mask: Mask, scale, dq, dk, dv, 
     _check(lib().vs_attn_bwd_parts(as_vs_tensor(q), as_vs_tensor(k), as_vs_tensor(v), as_vs_tensor(dout),
                                    _cptr(lse), _cptr(delta), ctypes.byref(mask.desc), scale, _cptr(dq), _cptr(dk),
                                    _cptr(dv), int(parts), _stream(stream)), "vs_attn_bwd_parts")
+
+
+def _mask_array(masks):
+    arr = (VsMask * len(masks))()
+    for i, m in enumerate(masks):
+        arr[i] = m.desc
+    return arr
+
+
+def vs_attn_fwd_ring(q, k_all, v_all, masks, scale, o, lse, accumulate=0, stream=None):
+    """One rank's ring steps (`masks`: one Mask per step, filled by
+    vs_block_mask) in one launch; k_all/v_all hold every shard in storage order."""
+    arr = _mask_array(masks)
+    _check(lib().vs_attn_fwd_ring(as_vs_tensor(q), as_vs_tensor(k_all), as_vs_tensor(v_all), arr, len(masks), scale,
+                                  _cptr(o), _cptr(lse), int(accumulate), _stream(stream)), "vs_attn_fwd_ring")
+
+
+def vs_attn_bwd_ring(q, k_all, v_all, dout, lse, delta, masks, scale, dq, dk_all, dv_all, parts=VS_BWD_ALL,
+                     stream=None):
+    arr = _mask_array(masks)
+    _check(lib().vs_attn_bwd_ring(as_vs_tensor(q), as_vs_tensor(k_all), as_vs_tensor(v_all), as_vs_tensor(dout),
+                                  _cptr(lse), _cptr(delta), arr, len(masks), scale, _cptr(dq), _cptr(dk_all),
+                                  _cptr(dv_all), int(parts), _stream(stream)), "vs_attn_bwd_ring")

@@ -388,4 +388,63 @@ int vs_attn_bwd(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout, const flo
   return vs_attn_bwd_parts(q, k, v, dout, lse, delta, m, scale, dq, dk, dv, VS_BWD_ALL, stream);
 }
 
+// One rank's ring steps: every mask describes the same rank and layout, the
+// steps see distinct shards, and K/V hold every shard in storage order.
+static int check_ring(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v, const vs_mask* ms, int nsteps) {
+  int st;
+  if (!ms || nsteps < 1) return VS_ERR_ARG;
+  const vs_mask& m = ms[0];
+  if (!m.tile_ptr || m.rank < 0) return VS_ERR_ARG;
+  const int P = m.lay.P;
+  if (nsteps > P) return VS_ERR_ARG;
+  uint64_t seen[64] = {};
+  if (P > 64 * 64) return VS_ERR_UNSUPPORTED;
+  for (int s = 0; s < nsteps; ++s) {
+    const vs_mask& x = ms[s];
+    if (!x.tile_ptr || !x.tile_col || !x.csc_ptr || !x.csc_row || !x.vloc || !x.vloc_cnt || !x.vcum ||
+        !x.vert_end || !x.slash_bits)
+      return VS_ERR_ARG;
+    if (x.Hq != m.Hq || x.Hkv != m.Hkv || x.QB != m.QB || x.KB != m.KB || x.T != m.T || x.W != m.W ||
+        x.lay.kind != m.lay.kind || x.lay.P != P || x.lay.n_global != m.lay.n_global || x.rank != m.rank)
+      return VS_ERR_ARG;
+    if (x.src < 0 || x.src >= P) return VS_ERR_ARG;
+    if (seen[x.src >> 6] & (1ull << (x.src & 63))) return VS_ERR_ARG;   // each shard once
+    seen[x.src >> 6] |= 1ull << (x.src & 63);
+  }
+  const int D = q.D;
+  const int64_t Nq = (int64_t)m.QB * 64, Nall = (int64_t)P * m.KB * 64;
+  if ((st = check_tensor(q, m.Hq, Nq, D)) != VS_OK) return st;
+  if ((st = check_tensor(k, m.Hkv, Nall, D)) != VS_OK) return st;
+  if ((st = check_tensor(v, m.Hkv, Nall, D)) != VS_OK) return st;
+  if (q.dtype != k.dtype || q.dtype != v.dtype) return VS_ERR_ARG;
+  if ((q.dtype != VS_BF16 && q.dtype != VS_F16) || D != 128) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
+int vs_attn_fwd_ring(vs_tensor q, vs_tensor k_all, vs_tensor v_all, const vs_mask* masks, int nsteps, float scale,
+                     float* o, float* lse, int accumulate, void* stream) {
+  int st;
+  if ((st = check_ring(q, k_all, v_all, masks, nsteps)) != VS_OK) return st;
+  if (!o || !lse || !aligned16(o)) return VS_ERR_ARG;
+  if (accumulate != 0 && accumulate != 1) return VS_ERR_ARG;
+  if (!finite_positive(scale)) return VS_ERR_ARG;
+  return launch_attn_fwd_ring(q.dtype, view(q), view(k_all), view(v_all), masks, nsteps, scale, o, lse, accumulate,
+                              (hipStream_t)stream);
+}
+
+int vs_attn_bwd_ring(vs_tensor q, vs_tensor k_all, vs_tensor v_all, vs_tensor dout, const float* lse,
+                     const float* delta, const vs_mask* masks, int nsteps, float scale, float* dq, float* dk_all,
+                     float* dv_all, int parts, void* stream) {
+  int st;
+  if ((st = check_ring(q, k_all, v_all, masks, nsteps)) != VS_OK) return st;
+  if ((st = check_tensor(dout, masks[0].Hq, (int64_t)masks[0].QB * 64, q.D)) != VS_OK) return st;
+  if (dout.dtype != q.dtype) return VS_ERR_ARG;
+  if ((parts & VS_BWD_ALL) == 0 || (parts & ~(VS_BWD_ALL | VS_BWD_OVERWRITE))) return VS_ERR_ARG;
+  if (!lse || !delta || !dq || !dk_all || !dv_all) return VS_ERR_ARG;
+  if (!aligned16(dq) || !aligned16(dk_all) || !aligned16(dv_all)) return VS_ERR_UNSUPPORTED;
+  if (!finite_positive(scale)) return VS_ERR_ARG;
+  return launch_attn_bwd_ring(q.dtype, view(q), view(k_all), view(v_all), view(dout), lse, delta, masks, nsteps,
+                              scale, dq, dk_all, dv_all, parts, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -436,8 +436,10 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 // pair, or fp16 pair on fp16 inputs): dQ_n sums dS over every active key of
 // the row, and the large outlier keys scale each weight's rounding error, so
 // a single fp16 dS put dQ at 1.9e-2 of the oracle at 262144 tokens.
-template <bool F16>
-__device__ __forceinline__ void dq_d128(const BwdArgs& a) {
+// RING: the tile sequence runs over several ring steps (RingTiles, `rs`; K/V
+// hold every shard in storage order) and dQ accumulates across them.
+template <bool F16, bool RING = false>
+__device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = nullptr) {
   constexpr int D = TD;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE_ELEMS];
@@ -460,11 +462,21 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a) {
   const int64_t u = (int64_t)h * a.QB + I;
   const int64_t row_base = (int64_t)I * BLK + 32 * rh;
 
-  BlockTiles bt;
-  bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
-  bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
-  bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
-  bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+  typename std::conditional<RING, RingTiles, BlockTiles>::type bt;
+  if constexpr (RING) {
+    __shared__ RingTable rtab;
+    bt.rs = rs; bt.tb = &rtab; bt.sbits = sbits; bt.vl_off = (int64_t)h * a.KB * BLK;
+    bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB;
+    bt.fill(u, wave, lane);
+    __syncthreads();
+    bt.start();
+  } else {
+    bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
+    bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
+    bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+  }
   const int total = bt.total;
   if (total == 0) {
     if (a.overwrite) zero_rows64(a.dq + ((int64_t)h * a.QB * BLK + (int64_t)I * BLK) * TD, tid);
@@ -480,15 +492,18 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a) {
   // start the copy of tile t into (Kn, Vn); its row thresholds go to thn
   auto issue = [&](int t, const int* slot, bf16* Kn, bf16* Vn, int* thn) -> int {
     int thr = tid, mode = 1;
-    if (!bt.vert(t)) {
+    const int64_t sr0 = bt.row0(t, 1);   // the tile's shard
+    const char* kb = kbase + sr0 * krb;
+    const char* vb = vbase + sr0 * vrb;
+    if (!bt.vert(t, 1)) {
       const int r0 = bt.tile_row(slot, mode);
-      dma_tile_rows(Kn, kbase + (int64_t)r0 * krb, krb, dlane, wave);
-      dma_tile_rows(Vn, vbase + (int64_t)r0 * vrb, vrb, dlane, wave);
+      dma_tile_rows(Kn, kb + (int64_t)r0 * krb, krb, dlane, wave);
+      dma_tile_rows(Vn, vb + (int64_t)r0 * vrb, vrb, dlane, wave);
     } else {
       int rows[4];
-      bt.vert_rows(t, slot, rows, thr, wave, lane, tid);
-      dma_tile_gather(Kn, kbase, rows, krb, dlane, wave);
-      dma_tile_gather(Vn, vbase, rows, vrb, dlane, wave);
+      bt.vert_rows(t, slot, rows, thr, wave, lane, tid, 1);
+      dma_tile_gather(Kn, kb, rows, krb, dlane, wave);
+      dma_tile_gather(Vn, vb, rows, vrb, dlane, wave);
     }
     if (tid < BLK) thn[tid] = thr;
     return mode;
@@ -631,6 +646,12 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a) {
 }
 __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a) { dq_d128<false>(a); }
 __global__ void __launch_bounds__(BWD_THREADS, 2) dq_f16_d128_kernel(BwdArgs a) { dq_d128<true>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 2) dq_ring_bf16_d128_kernel(BwdArgs a, RingSteps rs) {
+  dq_d128<false, true>(a, &rs);
+}
+__global__ void __launch_bounds__(BWD_THREADS, 2) dq_ring_f16_d128_kernel(BwdArgs a, RingSteps rs) {
+  dq_d128<true, true>(a, &rs);
+}
 
 
 // The two halves of kv_block, for the software-pipelined dK/dV kernel:
@@ -858,8 +879,25 @@ __device__ __forceinline__ void kv_finish(float* xbuf_dk, float* xbuf_dv, f32x4 
 // (Q, dO) stages: tile i (gradient products), tile i + 1 (S, dP), tile i + 2
 // (being copied). One workgroup per CU (the accumulators and K/V fragments
 // take more than half the registers), so LDS has room for the third stage.
-template <bool F16>
-__device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
+//
+// RING: one launch covers several ring steps: workgroup b belongs to step
+// b / (gridDim.x / nsteps) (a whole number of XCD rounds per step), reads
+// that step's CSC lists and writes the dK/dV rows of its visible shard in
+// tensors that hold every shard in storage order (as K/V do).
+template <bool F16, bool RING = false>
+__device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* rk = nullptr) {
+  BwdArgs a = a0;
+  int b = blockIdx.x;
+  int64_t srow0 = 0, kv_hrows = (int64_t)a0.KB * BLK;   // shard's first row; rows per kv head
+  if constexpr (RING) {
+    const int per = gridDim.x / rk->nsteps;
+    const int st = b / per;
+    b -= st * per;
+    a.csc_ptr = rk->csc_ptr[st]; a.csc_row = rk->csc_row[st]; a.vloc = rk->vloc[st]; a.vcum = rk->vcum[st];
+    a.src = rk->src[st];
+    srow0 = (int64_t)a.src * a.KB * BLK;
+    kv_hrows = (int64_t)a.P * a.KB * BLK;
+  }
   __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO2[2 * TILE_ELEMS];
@@ -885,7 +923,7 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
   const int g4 = lane >> 4, n16 = lane & 15;
   const int kh = wave >> 1, rh = wave & 1;
   int J, kvh, hh_unused;
-  if (!xcd_group_item(blockIdx.x, a.Hkv, a.KB, KMAJOR_BPC, 1, &J, &hh_unused, &kvh)) return;
+  if (!xcd_group_item(b, a.Hkv, a.KB, KMAJOR_BPC, 1, &J, &hh_unused, &kvh)) return;
   const int grp = a.Hq / a.Hkv;
   // The walk is the concatenation of the group's q heads' CSC lists for this
   // key block. Per-head ranges sit in lanes 0 .. grp-1 and are read back with
@@ -916,7 +954,7 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
   }
   if (total == 0) {
     if (a.overwrite) {
-      const int64_t r0 = ((int64_t)kvh * a.KB * BLK + (int64_t)J * BLK) * TD;
+      const int64_t r0 = ((int64_t)kvh * kv_hrows + srow0 + (int64_t)J * BLK) * TD;
       zero_rows64(a.dk + r0, tid);
       zero_rows64(a.dv + r0, tid);
     }
@@ -977,7 +1015,7 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
   bf16x8 kf[2][4], vf[2][4];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const int64_t krow = (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
+    const int64_t krow = srow0 + (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       kf[kt][ks] = *(const bf16x8*)((const bf16*)a.k + kvh * a.ksh + krow * a.ksn + 32 * ks + 8 * g4);
@@ -1074,13 +1112,20 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a) {
   }
   int64_t keys[2];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) keys[kt] = (int64_t)kvh * a.KB * BLK + (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
+  for (int kt = 0; kt < 2; ++kt)
+    keys[kt] = (int64_t)kvh * kv_hrows + srow0 + (int64_t)J * BLK + 32 * kh + 16 * kt + n16;
   wait_all_mem();
   kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, false,
             a.overwrite != 0);
 }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs a) { dkdv_d128<false>(a); }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_f16_d128_kernel(BwdArgs a) { dkdv_d128<true>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_ring_bf16_d128_kernel(BwdArgs a, RingStepsKV rk) {
+  dkdv_d128<false, true>(a, &rk);
+}
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_ring_f16_d128_kernel(BwdArgs a, RingStepsKV rk) {
+  dkdv_d128<true, true>(a, &rk);
+}
 
 // dK/dV of vertical columns: work items (head, 64-column chunk of the shard's
 // verticals, range of VERT_SEG query blocks) enumerated from the device-side
@@ -1093,8 +1138,11 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_f16_d128_kernel(BwdArgs a
 // hi + lo pairs (fp16 pairs on fp16 operands): one rounding of each weight
 // to fp16 leaves an error that grows with the square root of that count and
 // reached 0.1 in dV on the outlier columns of the 131072-token layer.
-template <bool F16>
-__device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
+//
+// RING: the work items of several ring steps in one launch (each step's
+// verticals in its visible shard, written to tensors holding every shard).
+template <bool F16, bool RING = false>
+__device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingStepsKV* rk = nullptr) {
   __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) float L0[2 * BLK];
@@ -1113,19 +1161,47 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
   // step with few vertical columns still spreads over the whole GPU instead
   // of walking long ranges in a few workgroups. Every workgroup derives the
   // same partition from the device-side counts.
+  // per step: its chunks of 64 verticals over all heads (steps in LDS)
+  __shared__ int step_chunks[RING ? MAX_RING_STEPS : 1];
+  const int nst = RING ? rk->nsteps : 1;
+  auto vcnt_of = [&](int st) -> const int32_t* {
+    if constexpr (RING) return rk->vloc_cnt[st];
+    else return a.vloc_cnt;
+  };
+  if (tid < nst) {
+    int c = 0;
+    for (int h = 0; h < a.Hq; ++h) c += (vcnt_of(tid)[h] + BLK - 1) / BLK;
+    step_chunks[tid] = c;
+  }
+  __syncthreads();
   int64_t nchunks = 0;
-  for (int h = 0; h < a.Hq; ++h) nchunks += (a.vloc_cnt[h] + BLK - 1) / BLK;
+  for (int st = 0; st < nst; ++st) nchunks += step_chunks[st];
   int seg_len = VERT_SEG;
   while (seg_len > VERT_SEG_MIN && nchunks * ((a.QB + seg_len - 1) / seg_len) < VERT_ITEMS_MIN) seg_len >>= 1;
   const int nseg = (a.QB + seg_len - 1) / seg_len;
   const int64_t nwork = nchunks * nseg;
   const int grp = a.Hq / a.Hkv;
   const float sl2 = a.scale_log2;
+  const int64_t kv_hrows = (int64_t)(RING ? a.P : 1) * a.KB * BLK;   // rows per kv head of k, v, dk, dv
   for (int64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
     int64_t r = w;
+    int st = 0;
+    for (; st + 1 < nst; ++st) {
+      const int64_t n = (int64_t)step_chunks[st] * nseg;
+      if (r < n) break;
+      r -= n;
+    }
+    const int32_t* vloc_cnt = vcnt_of(st);
+    const int32_t* vloc = a.vloc;
+    int src = a.src;
+    if constexpr (RING) {
+      vloc = rk->vloc[st];
+      src = rk->src[st];
+    }
+    const int64_t srow0 = RING ? (int64_t)src * a.KB * BLK : 0;
     int h = 0;
     for (; h < a.Hq; ++h) {
-      const int64_t n = (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+      const int64_t n = (int64_t)((vloc_cnt[h] + BLK - 1) / BLK) * nseg;
       if (r < n) break;
       r -= n;
     }
@@ -1134,9 +1210,9 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
     // chunk's last (always full) segment
     const int chunk = (int)(r / nseg), seg = (int)((r % nseg + chunk) % nseg);
     const int kvh = h / grp;
-    const int cnt = a.vloc_cnt[h];
-    const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
-    const int64_t gb_min = global_block(a.kind, a.P, a.KB, a.src, vl[chunk * BLK] / BLK);
+    const int cnt = vloc_cnt[h];
+    const int32_t* vl = vloc + (int64_t)h * a.KB * BLK;
+    const int64_t gb_min = global_block(a.kind, a.P, a.KB, src, vl[chunk * BLK] / BLK);
     const int I_lo = max(seg * seg_len, blocks_upto(a.kind, a.P, a.QB, a.rank, gb_min - 1));
     const int I_hi = min(a.QB, (seg + 1) * seg_len);
     const int total = I_hi - I_lo;
@@ -1151,11 +1227,11 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
       const int slot = chunk * BLK + 32 * kh + 16 * kt + n16;
       valid[kt] = slot < cnt;
       m[kt] = vl[valid[kt] ? slot : chunk * BLK];
-      gbk[kt] = global_block(a.kind, a.P, a.KB, a.src, m[kt] / BLK);
+      gbk[kt] = global_block(a.kind, a.P, a.KB, src, m[kt] / BLK);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        kf[kt][ks] = *(const bf16x8*)((const bf16*)a.k + kvh * a.ksh + (int64_t)m[kt] * a.ksn + 32 * ks + 8 * g4);
-        vf[kt][ks] = *(const bf16x8*)((const bf16*)a.v + kvh * a.vsh + (int64_t)m[kt] * a.vsn + 32 * ks + 8 * g4);
+        kf[kt][ks] = *(const bf16x8*)((const bf16*)a.k + kvh * a.ksh + (srow0 + m[kt]) * a.ksn + 32 * ks + 8 * g4);
+        vf[kt][ks] = *(const bf16x8*)((const bf16*)a.v + kvh * a.vsh + (srow0 + m[kt]) * a.vsn + 32 * ks + 8 * g4);
       }
     }
     f32x4 acc_dk[2][8], acc_dv[2][8];
@@ -1187,12 +1263,18 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a) {
     }
     int64_t keys[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) keys[kt] = valid[kt] ? (int64_t)kvh * a.KB * BLK + m[kt] : -1;
+    for (int kt = 0; kt < 2; ++kt) keys[kt] = valid[kt] ? (int64_t)kvh * kv_hrows + srow0 + m[kt] : -1;
     kv_finish((float*)QO0, (float*)QO1, acc_dk, acc_dv, a.dk, a.dv, keys, kh, rh, lane, g4, a.scale, true, false);
   }
 }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(BwdArgs a) { dkdv_vert_d128<false>(a); }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_f16_d128_kernel(BwdArgs a) { dkdv_vert_d128<true>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_ring_bf16_d128_kernel(BwdArgs a, RingStepsKV rk) {
+  dkdv_vert_d128<false, true>(a, &rk);
+}
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_ring_f16_d128_kernel(BwdArgs a, RingStepsKV rk) {
+  dkdv_vert_d128<true, true>(a, &rk);
+}
 
 // ---------------------------------------------------------------------------
 // delta[row] = dO[row] . O[row]; D/4 threads per row.
@@ -1337,6 +1419,67 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   else if (dtype == VS_BF16 && D == 64) launch_bwd_typed<bf16, 64>(a, parts, stream);
   else if (dtype == VS_F32 && D == 64) launch_bwd_typed<float, 64>(a, parts, stream);
   else return VS_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+// Several ring steps of one rank per launch (groups of up to MAX_RING_STEPS):
+// k, v, dk, dv hold every shard in storage order (shard r at rows
+// r * KB * 64). dQ accumulates over the steps of a group; with
+// VS_BWD_OVERWRITE the first group writes dq (later groups add to it) and
+// every group writes its visible shards' dk/dv rows (the vertical part then
+// adds to them).
+int launch_attn_bwd_ring(int dtype, TView q, TView k, TView v, TView dout, const float* lse, const float* delta,
+                         const vs_mask* ms, int nsteps, float scale, float* dq, float* dk, float* dv, int parts,
+                         hipStream_t stream) {
+  const vs_mask* m = &ms[0];
+  if (dtype != VS_BF16 && dtype != VS_F16) return VS_ERR_UNSUPPORTED;
+  if (m->W > MAX_LDS_W || m->Hq / m->Hkv > 8) return VS_ERR_UNSUPPORTED;
+  const int64_t krows = (int64_t)m->KB * BLK, qrows = (int64_t)m->QB * BLK;   // 32-bit offsets per shard
+  if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn) || !dma_offsets_fit(qrows, q.sn) ||
+      !dma_offsets_fit(qrows, dout.sn))
+    return VS_ERR_UNSUPPORTED;
+  BwdArgs a;
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.dout = dout.ptr;
+  a.qsh = q.sh; a.qsn = q.sn; a.ksh = k.sh; a.ksn = k.sn; a.vsh = v.sh; a.vsn = v.sn;
+  a.dsh = dout.sh; a.dsn = dout.sn;
+  a.lse = lse; a.delta = delta;
+  a.tile_ptr = nullptr; a.tile_col = nullptr; a.csc_ptr = nullptr; a.csc_row = nullptr;
+  a.vloc = nullptr; a.vloc_cnt = nullptr; a.vcum = nullptr; a.vert_end = nullptr;
+  a.slash_bits = m->slash_bits;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
+  a.P = m->lay.P; a.rank = m->rank; a.src = -1;
+  a.scale = scale; a.scale_log2 = scale * LOG2E;
+  const bool f16 = dtype == VS_F16;
+  const unsigned qgrid = xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv);
+  const unsigned kgrid = xcd_group_grid(a.Hkv, a.KB, KMAJOR_BPC, 1);
+  for (int s0 = 0; s0 < nsteps; s0 += MAX_RING_STEPS) {
+    const int ns = nsteps - s0 < MAX_RING_STEPS ? nsteps - s0 : MAX_RING_STEPS;
+    RingSteps rs{};
+    RingStepsKV rk{};
+    rs.nsteps = rk.nsteps = ns;
+    for (int s = 0; s < ns; ++s) {
+      const vs_mask& x = ms[s0 + s];
+      rs.tile_ptr[s] = x.tile_ptr; rs.tile_col[s] = x.tile_col; rs.vloc[s] = x.vloc; rs.vert_end[s] = x.vert_end;
+      rs.src[s] = x.src;
+      rk.csc_ptr[s] = x.csc_ptr; rk.csc_row[s] = x.csc_row; rk.vloc[s] = x.vloc; rk.vloc_cnt[s] = x.vloc_cnt;
+      rk.vcum[s] = x.vcum; rk.src[s] = x.src;
+    }
+    // dq: the first group may overwrite, later groups add; dk/dv: every
+    // group's shards are its own (a rank sees each shard at one step), so
+    // the overwrite holds for every group
+    a.overwrite = (s0 == 0 && (parts & VS_BWD_OVERWRITE)) ? 1 : 0;
+    if (parts & VS_BWD_DQ)
+      hipLaunchKernelGGL(f16 ? dq_ring_f16_d128_kernel : dq_ring_bf16_d128_kernel, dim3(qgrid), dim3(BWD_THREADS), 0,
+                         stream, a, rs);
+    a.overwrite = (parts & VS_BWD_OVERWRITE) ? 1 : 0;
+    if (parts & VS_BWD_DKDV)
+      hipLaunchKernelGGL(f16 ? dkdv_ring_f16_d128_kernel : dkdv_ring_bf16_d128_kernel, dim3(kgrid * ns),
+                         dim3(BWD_THREADS), 0, stream, a, rk);
+    if (parts & VS_BWD_DKDV_VERT)
+      hipLaunchKernelGGL(f16 ? dkdv_vert_ring_f16_d128_kernel : dkdv_vert_ring_bf16_d128_kernel, dim3(VERT_GRID),
+                         dim3(BWD_THREADS), 0, stream, a, rk);
+  }
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 

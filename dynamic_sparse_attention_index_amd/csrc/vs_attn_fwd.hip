@@ -296,8 +296,12 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 // first head's waves issue. Valid when the two heads have the same active
 // set (an index selected per kv head); each workgroup checks that its pair's
 // lists agree and otherwise writes VS_ERR_ARG to a.status and returns.
-template <bool F16, int HP>
-__device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
+//
+// RING: the tile sequence runs over several ring steps (RingTiles, `rs`):
+// K/V hold every shard in storage order and each tile's copy starts at its
+// step's shard; the online-softmax state carries across the steps.
+template <bool F16, int HP, bool RING = false>
+__device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps* rs = nullptr) {
   constexpr int D = TD;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE_ELEMS];
@@ -356,11 +360,21 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   const uint32_t krb = (uint32_t)a.ksn * 2, vrb = (uint32_t)a.vsn * 2;   // row pitch in bytes
   const DmaLane dl = dma_lane(wave, lane);
 
-  BlockTiles bt;
-  bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h0 * a.KB * BLK; bt.sbits = sbits;
-  bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
-  bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
-  bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+  typename std::conditional<RING, RingTiles, BlockTiles>::type bt;
+  if constexpr (RING) {
+    __shared__ RingTable rtab;
+    bt.rs = rs; bt.tb = &rtab; bt.sbits = sbits; bt.vl_off = (int64_t)h0 * a.KB * BLK;
+    bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB;
+    bt.fill(u, wave8, lane);
+    __syncthreads();
+    bt.start();
+  } else {
+    bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h0 * a.KB * BLK; bt.sbits = sbits;
+    bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
+    bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+  }
   const int total = bt.total;
   const uint32_t* sbg = a.slash_bits + (int64_t)h0 * a.W;
   for (int w = tid; w < a.W; w += HP * FWD_THREADS) sbits[w] = sbg[w];
@@ -387,14 +401,15 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
     bf16* ks = Kst.template operator()<p>();
     const int* slot = desc_sh[t % 3];
     int thr = tid;
-    if (!bt.vert(t)) {
+    const char* kb = kbase + bt.row0(t, 1) * krb;   // the tile's shard
+    if (!bt.vert(t, 1)) {
       int mode;
       const int r0 = bt.tile_row(slot, mode);
-      if (hs == 0) dma_tile_rows(ks, kbase + (int64_t)r0 * krb, krb, dl, wave);
+      if (hs == 0) dma_tile_rows(ks, kb + (int64_t)r0 * krb, krb, dl, wave);
     } else {
       int rows[4];
-      bt.vert_rows(t, slot, rows, thr, wave, lane, tid);
-      if (hs == 0) dma_tile_gather(ks, kbase, rows, krb, dl, wave);
+      bt.vert_rows(t, slot, rows, thr, wave, lane, tid, 1);
+      if (hs == 0) dma_tile_gather(ks, kb, rows, krb, dl, wave);
     }
     if (tid < BLK) thr_sh[t % 3][tid] = thr;
   };
@@ -402,15 +417,16 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a) {
   auto issue_v = [&]<int p>(int t) {
     bf16* vs_ = Vst.template operator()<p>();
     const int* slot = desc_sh[t % 3];
-    if (!bt.vert(t)) {
+    const char* vb = vbase + bt.row0(t, 2) * vrb;   // the tile's shard
+    if (!bt.vert(t, 2)) {
       const int r0 = bt.tile_row(slot, mode_pend);
-      if (hs == 0) dma_tile_rows(vs_, vbase + (int64_t)r0 * vrb, vrb, dl, wave);
+      if (hs == 0) dma_tile_rows(vs_, vb + (int64_t)r0 * vrb, vrb, dl, wave);
     } else {
       if (hs == 0) {
         int rows[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
-        dma_tile_gather(vs_, vbase, rows, vrb, dl, wave);
+        dma_tile_gather(vs_, vb, rows, vrb, dl, wave);
       }
       mode_pend = 1;
     }
@@ -634,6 +650,12 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_bf16_d128_kernel(FwdA
   attn_fwd_d128<false, 1>(a);
 }
 __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_f16_d128_kernel(FwdArgs a) { attn_fwd_d128<true, 1>(a); }
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_ring_bf16_d128_kernel(FwdArgs a, RingSteps rs) {
+  attn_fwd_d128<false, 1, true>(a, &rs);
+}
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_ring_f16_d128_kernel(FwdArgs a, RingSteps rs) {
+  attn_fwd_d128<true, 1, true>(a, &rs);
+}
 __global__ void __launch_bounds__(2 * FWD_THREADS, 1) attn_fwd_pair_bf16_d128_kernel(FwdArgs a) {
   attn_fwd_d128<false, 2>(a);
 }
@@ -683,6 +705,41 @@ int launch_attn_fwd_packed(int dtype, TView q, TView k, TView v, const vs_mask* 
   const dim3 grid(xcd_group_grid(m->Hkv, m->QB, QMAJOR_BPC, m->Hq / m->Hkv / 2)), block(2 * FWD_THREADS);
   if (dtype == VS_F16) hipLaunchKernelGGL(attn_fwd_pair_f16_d128_kernel, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(attn_fwd_pair_bf16_d128_kernel, grid, block, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+// Several ring steps of one rank in one launch per group of up to
+// MAX_RING_STEPS steps: k, v hold every shard in storage order (shard r at
+// rows r * KB * 64); the first group honours `accumulate`, later groups merge
+// into its result.
+int launch_attn_fwd_ring(int dtype, TView q, TView k, TView v, const vs_mask* ms, int nsteps, float scale, float* o,
+                         float* lse, int accumulate, hipStream_t stream) {
+  const vs_mask* m = &ms[0];
+  FwdArgs a;
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr;
+  a.qsh = q.sh; a.qsn = q.sn; a.ksh = k.sh; a.ksn = k.sn; a.vsh = v.sh; a.vsn = v.sn;
+  a.tile_ptr = nullptr; a.tile_col = nullptr; a.vloc = nullptr; a.vert_end = nullptr;
+  a.slash_bits = m->slash_bits; a.o = o; a.lse = lse; a.status = nullptr;
+  a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
+  a.P = m->lay.P; a.rank = m->rank; a.src = -1;
+  a.scale_log2 = scale * LOG2E;
+  if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
+  const int64_t krows = (int64_t)m->KB * BLK;   // 32-bit copy offsets within one shard
+  if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
+  const dim3 grid(xcd_group_grid(m->Hkv, m->QB, QMAJOR_BPC, m->Hq / m->Hkv)), block(FWD_THREADS);
+  for (int s0 = 0; s0 < nsteps; s0 += MAX_RING_STEPS) {
+    RingSteps rs{};
+    rs.nsteps = nsteps - s0 < MAX_RING_STEPS ? nsteps - s0 : MAX_RING_STEPS;
+    for (int s = 0; s < rs.nsteps; ++s) {
+      const vs_mask& ms_s = ms[s0 + s];
+      rs.tile_ptr[s] = ms_s.tile_ptr; rs.tile_col[s] = ms_s.tile_col; rs.vloc[s] = ms_s.vloc;
+      rs.vert_end[s] = ms_s.vert_end; rs.src[s] = ms_s.src;
+    }
+    a.accumulate = s0 == 0 ? accumulate : 1;
+    if (dtype == VS_F16) hipLaunchKernelGGL(attn_fwd_ring_f16_d128_kernel, grid, block, 0, stream, a, rs);
+    else if (dtype == VS_BF16) hipLaunchKernelGGL(attn_fwd_ring_bf16_d128_kernel, grid, block, 0, stream, a, rs);
+    else return VS_ERR_UNSUPPORTED;
+  }
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 

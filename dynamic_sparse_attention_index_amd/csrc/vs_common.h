@@ -365,6 +365,137 @@ struct BlockTiles {
       if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
     }
   }
+  // The same calls as RingTiles (one visible shard at local row 0; the call
+  // site's cursor `c` is not needed).
+  __device__ __forceinline__ bool vert(int it, int) const { return vert(it); }
+  __device__ __forceinline__ void vert_rows(int it, const int* slot, int* rows, int& thr, int wave, int lane, int tid,
+                                            int) const {
+    vert_rows(it, slot, rows, thr, wave, lane, tid);
+  }
+  __device__ __forceinline__ int64_t row0(int, int) const { return 0; }
+};
+
+// ---- several ring steps in one launch ----------------------------------------
+// One rank's ring steps walked by one launch with every visible shard
+// resident: the tile sequence of a (q head, query block) is the
+// concatenation of its sequences in the steps' masks (each step: its
+// vertical chunks, then its listed tiles), and the online-softmax state (or
+// the dQ accumulator) carries across the steps, so the output is written
+// once instead of being merged step by step.
+constexpr int MAX_RING_STEPS = 32;
+
+// Per-step mask arrays and visible shard (kernel argument).
+struct RingSteps {
+  const int32_t* tile_ptr[MAX_RING_STEPS];
+  const int32_t* tile_col[MAX_RING_STEPS];
+  const int32_t* vloc[MAX_RING_STEPS];
+  const int32_t* vert_end[MAX_RING_STEPS];
+  int32_t src[MAX_RING_STEPS];
+  int32_t nsteps;
+};
+
+// Per-step arrays of the key-major gradient parts (kernel argument): one
+// launch covers the key blocks of every step's visible shard.
+struct RingStepsKV {
+  const int32_t* csc_ptr[MAX_RING_STEPS];
+  const int32_t* csc_row[MAX_RING_STEPS];
+  const int32_t* vloc[MAX_RING_STEPS];
+  const int32_t* vloc_cnt[MAX_RING_STEPS];
+  const int32_t* vcum[MAX_RING_STEPS];
+  int32_t src[MAX_RING_STEPS];
+  int32_t nsteps;
+};
+
+// LDS table of one list row across the steps.
+struct RingTable {
+  int cum[MAX_RING_STEPS + 1];   // tiles of the steps before step s
+  int t0[MAX_RING_STEPS], nt[MAX_RING_STEPS], ve[MAX_RING_STEPS];
+};
+
+__device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Tile sequence over the steps, with the calls of BlockTiles. Tile t lies in
+// step s with cum[s] <= t < cum[s + 1]; each call site walks its tiles in
+// increasing order and keeps its own step cursor (c = 0: descriptor copies,
+// 1 and 2: the kernel's two copy sites), so finding the step is a short
+// forward scan. Key rows of step s's shard start at row0 = src[s] * KB * 64
+// of the tensors that hold every shard in storage order.
+struct RingTiles {
+  const RingSteps* rs;
+  RingTable* tb;
+  const uint32_t* sbits;      // LDS copy of the head's slash bitmap (the same in every step)
+  int64_t vl_off;             // the head's first entry in each step's vloc
+  int64_t G;                  // global block of the query block
+  int kind, P, KB, total;
+  int cur[3];
+
+  // Wave 0 fills the table of list row u (= h * QB + I); the caller
+  // synchronises the workgroup before start().
+  __device__ __forceinline__ void fill(int64_t u, int wave, int lane) {
+    if (wave != 0) return;
+    const int n = rs->nsteps;
+    int tot = 0;
+    if (lane < n) {
+      const int a0 = rs->tile_ptr[lane][u], a1 = rs->tile_ptr[lane][u + 1];
+      const int ve = rs->vert_end[lane][u];
+      tb->t0[lane] = a0;
+      tb->nt[lane] = a1 - a0;
+      tb->ve[lane] = ve;
+      tot = (a1 - a0) + (ve + BLK - 1) / BLK;
+    }
+    int incl = tot;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane < n) tb->cum[lane + 1] = incl;
+    if (lane == 0) tb->cum[0] = 0;
+  }
+  __device__ __forceinline__ void start() {
+    total = rfl(tb->cum[rs->nsteps]);
+    cur[0] = cur[1] = cur[2] = 0;
+  }
+  __device__ __forceinline__ int step_of(int t, int c) {
+    int s = cur[c];
+    while (s + 1 < rs->nsteps && t >= rfl(tb->cum[s + 1])) ++s;
+    cur[c] = s;
+    return s;
+  }
+  __device__ __forceinline__ int nvc(int s) const { return (rfl(tb->ve[s]) + BLK - 1) / BLK; }
+  __device__ __forceinline__ bool vert(int t, int c) {
+    const int s = step_of(t, c);
+    return t - rfl(tb->cum[s]) < nvc(s);
+  }
+  __device__ __forceinline__ void desc_copy(int t, int* slot, int wave, int lane) {
+    const int s = step_of(t, 0);
+    if (wave != 0) return;
+    const int it = t - rfl(tb->cum[s]), nv = nvc(s), ve = rfl(tb->ve[s]);
+    const int32_t* p = it < nv ? rs->vloc[s] + vl_off + min(it * BLK + lane, ve - 1)
+                               : rs->tile_col[s] + rfl(tb->t0[s]) + (rfl(tb->nt[s]) - 1 - (it - nv));
+    __builtin_amdgcn_global_load_lds((const void*)p,
+                                     (__attribute__((address_space(3))) void*)(
+                                         (__attribute__((address_space(3))) int*)(slot)),
+                                     4, 0, 0);
+  }
+  __device__ __forceinline__ int tile_row(const int* slot, int& mode) const {
+    const int e = __builtin_amdgcn_readfirstlane(slot[0]);
+    mode = (e & VS_TILE_DIAG) ? 1 : 0;
+    return (e & VS_TILE_MASK) * BLK;
+  }
+  __device__ __forceinline__ void vert_rows(int t, const int* slot, int* rows, int& thr, int wave, int lane, int tid,
+                                            int c) {
+    const int s = step_of(t, c);
+    const int it = t - rfl(tb->cum[s]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rows[k] = slot[dma_local_row(wave, k, lane)];
+    thr = BLK;
+    if (tid < BLK && it * BLK + tid < rfl(tb->ve[s])) {
+      const int m = slot[tid];
+      const int64_t j = G - global_block(kind, P, KB, rs->src[s], m / BLK);
+      if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
+    }
+  }
+  __device__ __forceinline__ int64_t row0(int t, int c) { return (int64_t)rs->src[step_of(t, c)] * KB * BLK; }
 };
 
 }  // namespace vs

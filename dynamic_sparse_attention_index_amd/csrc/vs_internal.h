@@ -21,6 +21,9 @@ int launch_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t 
 int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* m, float scale,
                     float* o, float* lse, int accumulate, hipStream_t stream);
 
+int launch_attn_fwd_ring(int dtype, TView q, TView k, TView v, const vs_mask* ms, int nsteps, float scale, float* o,
+                         float* lse, int accumulate, hipStream_t stream);
+
 int launch_attn_fwd_packed(int dtype, TView q, TView k, TView v, const vs_mask* m, float scale, float* o,
                            float* lse, int accumulate, int32_t* status, hipStream_t stream);
 
@@ -38,6 +41,10 @@ int launch_bwd_prep(const float* o, int dtype, TView dout, int Hq, int64_t Nq, i
 int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, const float* lse,
                     const float* delta, const vs_mask* m, float scale, float* dq, float* dk, float* dv,
                     int parts, hipStream_t stream);
+
+int launch_attn_bwd_ring(int dtype, TView q, TView k, TView v, TView dout, const float* lse, const float* delta,
+                         const vs_mask* ms, int nsteps, float scale, float* dq, float* dk, float* dv, int parts,
+                         hipStream_t stream);
 
 size_t index_workspace_bytes(int Hq, int Hkv, int64_t n_global, int D, int last_q);
 

@@ -405,6 +405,40 @@ int vs_attn_bwd_parts(vs_tensor q, vs_tensor k, vs_tensor v, vs_tensor dout,
                       const float* lse, const float* delta, const vs_mask* m, float scale,
                       float* dq, float* dk, float* dv, int parts, void* stream);
 
+/* ---- a rank's whole ring in one launch --------------------------------- */
+
+/* The ring steps of one rank run as one launch (per group of up to 32 steps)
+ * instead of one call per step, with every visible shard resident: the
+ * incremental softmax of the Ring Attention overview (section 2.1) is carried
+ * inside the kernel across the steps, so O and LSE are written once, and the
+ * backward accumulates dQ across the steps and covers the key blocks of
+ * every step's shard in one grid.
+ *   q:       [Hq, QB*64, D], the rank's queries;
+ *   k_all, v_all: [Hkv, P*KB*64, D], every rank's shard in storage order
+ *            (shard r at rows r*KB*64 .. (r+1)*KB*64 - 1);
+ *   masks:   host array of `nsteps` descriptors (1 <= nsteps <= P), each
+ *            filled by vs_block_mask for the same rank and layout at one step
+ *            (masks[i].src is the shard it reads); no shard twice;
+ *   o, lse:  as vs_attn_fwd; accumulate = 0 writes the result of all the
+ *            steps, 1 merges it into (o, lse).
+ * Results equal the step-by-step calls (vs_attn_fwd with accumulate = 1 per
+ * step) up to fp32 rounding order. Supported: bf16 or fp16 operands at D =
+ * 128 (else VS_ERR_UNSUPPORTED); VS_ERR_ARG for inconsistent masks, a shard
+ * seen twice or nsteps outside [1, P]. */
+int vs_attn_fwd_ring(vs_tensor q, vs_tensor k_all, vs_tensor v_all, const vs_mask* masks, int nsteps, float scale,
+                     float* o, float* lse, int accumulate, void* stream);
+
+/* The gradient of the same steps (review page 1, section 三.2 item 3, with
+ * the final lse and delta of the rank's rows): dq [Hq, QB*64, D], dk_all,
+ * dv_all [Hkv, P*KB*64, D] (shard r's key rows at r*KB*64, as k_all), fp32.
+ * `parts` as vs_attn_bwd_parts. Without VS_BWD_OVERWRITE every output adds;
+ * with it dq is written (then added to by steps beyond the first 32) and the
+ * dk/dv rows of every visible shard are written before the vertical part
+ * adds to them (rows of shards no step sees are left alone). */
+int vs_attn_bwd_ring(vs_tensor q, vs_tensor k_all, vs_tensor v_all, vs_tensor dout, const float* lse,
+                     const float* delta, const vs_mask* masks, int nsteps, float scale, float* dq, float* dk_all,
+                     float* dv_all, int parts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
