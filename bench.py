@@ -627,7 +627,8 @@ def ring_report(args, cfg):
         tall = tm + tf + tb
         ring_all_ms = float(tall.max(axis=0).sum() + tp.max())
         A_total = int(act.sum())
-        # resident mode: a rank's masks of every step built up front, then the
+        # resident mode: a rank's masks of every step built up front (one
+        # launch sequence for all steps, vs_block_mask_ring), then the
         # forward of all its steps in one launch (the online softmax carried
         # across the steps in the kernel: no per-step merge) and the backward
         # of all its steps in one call; k/v hold every shard in storage order
@@ -639,8 +640,7 @@ def ring_report(args, cfg):
             for r in range(P):
                 rows = slice(r * QB * 64, (r + 1) * QB * 64)
                 qr, dor = aq[:, rows], ado[:, rows]
-                e_m = timed(lambda: [vs.vs_block_mask(vidx, vcnt, sidx, scnt, r, st, res_masks[st], stream)
-                                     for st in range(P)])
+                e_m = timed(lambda: vs.vs_block_mask_ring(vidx, vcnt, sidx, scnt, r, res_masks, stream))
                 e_f = timed(lambda: vs.vs_attn_fwd_ring(qr, ak, av, res_masks, cfg.scale, o, lse, 0, stream))
                 e_p = timed(lambda: vs.vs_attn_bwd_prep(o, dor, delta, stream))
                 e_b = timed(lambda: vs.vs_attn_bwd_ring(qr, ak, av, dor, lse, delta, res_masks, cfg.scale, dq, dk_res,
@@ -721,7 +721,8 @@ def ring_report(args, cfg):
             f.write("Every rank's ring steps run one after another on the one GPU (communication excluded); "
                     "times are medians over repetitions of each (rank, step) kernel group timed alone. "
                     "Per-step mode: one active-region build, one forward (merge fused) and one backward call per "
-                    "step. Resident mode (`resident_*`): a rank's masks of all steps built up front, then one "
+                    "step. Resident mode (`resident_*`): a rank's masks of all steps built up front by one launch "
+                    "sequence (vs_block_mask_ring), then one "
                     "forward launch over all its steps (vs_attn_fwd_ring: the online softmax carried across the "
                     "steps, O written once) and one backward call (vs_attn_bwd_ring: dQ accumulated across the "
                     "steps, the key-major parts over every step's shard in one grid); its time per rank is "

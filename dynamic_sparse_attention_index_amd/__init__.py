@@ -34,6 +34,7 @@ EXPORTED = [
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
     "vs_convert_f16", "vs_index_select_group_workspace_size", "vs_index_select_group", "vs_attn_fwd_packed",
     "vs_attn_bwd_prep_f16", "vs_index_build_noalloc", "vs_attn_fwd_ring", "vs_attn_bwd_ring",
+    "vs_block_mask_ring",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
 
@@ -123,6 +124,8 @@ def lib():
         L.vs_attn_bwd.restype = i32
         L.vs_attn_bwd.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask), f32,
                                   vp, vp, vp, vp]
+        L.vs_block_mask_ring.restype = i32
+        L.vs_block_mask_ring.argtypes = [vp, vp, i64, vp, vp, i64, i32, ctypes.POINTER(VsMask), i32, vp]
         L.vs_attn_fwd_ring.restype = i32
         L.vs_attn_fwd_ring.argtypes = [VsTensor, VsTensor, VsTensor, ctypes.POINTER(VsMask), i32, f32, vp, vp, i32,
                                        vp]
@@ -373,3 +376,13 @@ def vs_attn_bwd_ring(q, k_all, v_all, dout, lse, delta, masks, scale, dq, dk_all
     _check(lib().vs_attn_bwd_ring(as_vs_tensor(q), as_vs_tensor(k_all), as_vs_tensor(v_all), as_vs_tensor(dout),
                                   _cptr(lse), _cptr(delta), arr, len(masks), scale, _cptr(dq), _cptr(dk_all),
                                   _cptr(dv_all), int(parts), _stream(stream)), "vs_attn_bwd_ring")
+
+
+def vs_block_mask_ring(vert_idx, vert_cnt, slash_idx, slash_cnt, rank, masks, stream=None):
+    """Steps 0 .. len(masks)-1 of `rank` into `masks` (Mask objects of one shape)."""
+    arr = _mask_array(masks)
+    _check(lib().vs_block_mask_ring(_ptr(vert_idx), _ptr(vert_cnt), vert_idx.stride(0), _ptr(slash_idx),
+                                    _ptr(slash_cnt), slash_idx.stride(0), rank, arr, len(masks), _stream(stream)),
+           "vs_block_mask_ring")
+    for m, d in zip(masks, arr):     # the library set each descriptor's rank and visible shard
+        m.desc = d

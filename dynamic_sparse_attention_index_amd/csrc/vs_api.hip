@@ -299,6 +299,28 @@ int vs_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert
                            (hipStream_t)stream);
 }
 
+int vs_block_mask_ring(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
+                       const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
+                       int rank, vs_mask* masks, int nsteps, void* stream) {
+  if (!masks || nsteps < 1 || !vert_idx || !vert_cnt || !slash_idx || !slash_cnt) return VS_ERR_ARG;
+  if (vert_stride < 0 || slash_stride < 0) return VS_ERR_ARG;
+  const vs_mask& m = masks[0];
+  if (check_layout(m.lay) != VS_OK) return VS_ERR_ARG;
+  const int P = m.lay.P;
+  if (rank < 0 || rank >= P || nsteps > P) return VS_ERR_ARG;
+  for (int s = 0; s < nsteps; ++s) {
+    const vs_mask& x = masks[s];
+    if (!x.tile_ptr || !x.tile_col || !x.csc_ptr || !x.csc_row || !x.vloc || !x.vloc_cnt || !x.vcum ||
+        !x.vert_end || !x.slash_bits || !x.n_active || !x.status)
+      return VS_ERR_ARG;
+    if (x.Hq != m.Hq || x.Hkv != m.Hkv || x.QB != m.QB || x.KB != m.KB || x.T != m.T || x.W != m.W ||
+        x.lay.kind != m.lay.kind || x.lay.P != P || x.lay.n_global != m.lay.n_global || x.tile_cap != m.tile_cap)
+      return VS_ERR_ARG;
+  }
+  return launch_block_mask_ring(vert_idx, vert_cnt, vert_stride, slash_idx, slash_cnt, slash_stride, rank, masks,
+                                nsteps, (hipStream_t)stream);
+}
+
 static int check_attn(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v, const vs_mask* m) {
   int st;
   if (!m || !m->tile_ptr || m->rank < 0) return VS_ERR_ARG;

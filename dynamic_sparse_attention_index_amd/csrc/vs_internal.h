@@ -18,6 +18,10 @@ int launch_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t 
                       const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
                       int rank, int src, vs_mask* m, hipStream_t stream);
 
+int launch_block_mask_ring(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
+                           const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
+                           int rank, vs_mask* ms, int nsteps, hipStream_t stream);
+
 int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* m, float scale,
                     float* o, float* lse, int accumulate, hipStream_t stream);
 

@@ -28,6 +28,29 @@ struct MaskArgs {
 
 constexpr int MASK_THREADS = 1024;
 
+// Several ring steps of one rank built by the same four launches (grid.y =
+// step): the fields that differ per step (visible shard, output arrays).
+constexpr int MAX_MASK_STEPS = 32;
+struct MaskRing {
+  int32_t src[MAX_MASK_STEPS];
+  int32_t *tile_ptr[MAX_MASK_STEPS], *tile_col[MAX_MASK_STEPS], *csc_ptr[MAX_MASK_STEPS], *csc_row[MAX_MASK_STEPS];
+  int32_t *vloc[MAX_MASK_STEPS], *vloc_cnt[MAX_MASK_STEPS], *vcum[MAX_MASK_STEPS], *vert_end[MAX_MASK_STEPS];
+  uint32_t* slash_bits[MAX_MASK_STEPS];
+  int64_t* n_active[MAX_MASK_STEPS];
+  int32_t* status[MAX_MASK_STEPS];
+};
+// The arguments of this workgroup's step (the shared ones from `a`).
+__device__ __forceinline__ MaskArgs step_args(const MaskArgs& a, const MaskRing* rg) {
+  if (!rg) return a;
+  const int s = blockIdx.y;
+  MaskArgs b = a;
+  b.src = rg->src[s];
+  b.tile_ptr = rg->tile_ptr[s]; b.tile_col = rg->tile_col[s]; b.csc_ptr = rg->csc_ptr[s]; b.csc_row = rg->csc_row[s];
+  b.vloc = rg->vloc[s]; b.vloc_cnt = rg->vloc_cnt[s]; b.vcum = rg->vcum[s]; b.vert_end = rg->vert_end[s];
+  b.slash_bits = rg->slash_bits[s]; b.n_active = rg->n_active[s]; b.status = rg->status[s];
+  return b;
+}
+
 // Block-wide exclusive scan of one int per thread (1024 threads = 16 waves).
 __device__ __forceinline__ int block_exclusive_scan(int x, int* total, int* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -51,7 +74,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* total, int* sh) 
 }
 
 // Launch 1: grid = Hq, one workgroup per head.
-__global__ void __launch_bounds__(MASK_THREADS) mask_head_kernel(MaskArgs a) {
+__device__ __forceinline__ void mask_head_body(const MaskArgs& a) {
   __shared__ int sh[MASK_THREADS / 64 + 1];
   const int h = blockIdx.x;
   const int32_t* S = a.slash_idx + (int64_t)h * a.slash_stride;
@@ -108,7 +131,7 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
 }
 
 // Launch 2: list lengths.
-__global__ void __launch_bounds__(64 * ROW_WAVES) mask_count_kernel(MaskArgs a) {
+__device__ __forceinline__ void mask_count_body(const MaskArgs& a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * ROW_WAVES + (threadIdx.x >> 6);
   const int64_t nrow = (int64_t)a.Hq * a.NB;
@@ -163,7 +186,7 @@ __device__ int64_t scan_inplace(int32_t* p, int64_t n, int* sh) {
 // (vert_end is zeroed by the fill launch), so attention calls queued behind
 // this mask on the stream read no list entry and compute nothing for the
 // step; only the status word and n_active (exact counts) are meaningful.
-__global__ void __launch_bounds__(MASK_THREADS) mask_scan_kernel(MaskArgs a) {
+__device__ __forceinline__ void mask_scan_body(const MaskArgs& a) {
   __shared__ int sh[MASK_THREADS / 64 + 1];
   const int64_t n = (int64_t)a.Hq * a.NB;
   const int64_t tiles = scan_inplace(a.tile_ptr, n, sh);
@@ -182,7 +205,7 @@ __global__ void __launch_bounds__(MASK_THREADS) mask_scan_kernel(MaskArgs a) {
 // Launch 4: fill the lists; the CSR half also writes vert_end and n_active.
 // Order-preserving compaction per 64-entry chunk: a lane's output position is
 // the running count plus the matches of the lanes below it (ballot).
-__global__ void __launch_bounds__(64 * ROW_WAVES) mask_fill_kernel(MaskArgs a) {
+__device__ __forceinline__ void mask_fill_body(const MaskArgs& a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * ROW_WAVES + (threadIdx.x >> 6);
   const int64_t nrow = (int64_t)a.Hq * a.NB;
@@ -261,6 +284,23 @@ __global__ void __launch_bounds__(64 * ROW_WAVES) mask_fill_kernel(MaskArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(MASK_THREADS) mask_head_kernel(MaskArgs a) { mask_head_body(a); }
+__global__ void __launch_bounds__(64 * ROW_WAVES) mask_count_kernel(MaskArgs a) { mask_count_body(a); }
+__global__ void __launch_bounds__(MASK_THREADS) mask_scan_kernel(MaskArgs a) { mask_scan_body(a); }
+__global__ void __launch_bounds__(64 * ROW_WAVES) mask_fill_kernel(MaskArgs a) { mask_fill_body(a); }
+__global__ void __launch_bounds__(MASK_THREADS) mask_head_ring_kernel(MaskArgs a, MaskRing rg) {
+  mask_head_body(step_args(a, &rg));
+}
+__global__ void __launch_bounds__(64 * ROW_WAVES) mask_count_ring_kernel(MaskArgs a, MaskRing rg) {
+  mask_count_body(step_args(a, &rg));
+}
+__global__ void __launch_bounds__(MASK_THREADS) mask_scan_ring_kernel(MaskArgs a, MaskRing rg) {
+  mask_scan_body(step_args(a, &rg));
+}
+__global__ void __launch_bounds__(64 * ROW_WAVES) mask_fill_ring_kernel(MaskArgs a, MaskRing rg) {
+  mask_fill_body(step_args(a, &rg));
+}
+
 int launch_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
                       const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
                       int rank, int src, vs_mask* m, hipStream_t stream) {
@@ -279,6 +319,42 @@ int launch_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t 
   hipLaunchKernelGGL(mask_count_kernel, dim3(nblk), dim3(tpb), 0, stream, a);
   hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(MASK_THREADS), 0, stream, a);
   hipLaunchKernelGGL(mask_fill_kernel, dim3(nblk), dim3(tpb), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+// Steps 0 .. nsteps-1 of rank `rank` into ms[0 .. nsteps-1] (every mask
+// carved for the same shape and layout), the four launches shared by up to
+// MAX_MASK_STEPS steps.
+int launch_block_mask_ring(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
+                           const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
+                           int rank, vs_mask* ms, int nsteps, hipStream_t stream) {
+  const vs_mask* m = &ms[0];
+  MaskArgs a;
+  a.vert_idx = vert_idx; a.vert_cnt = vert_cnt; a.vert_stride = vert_stride;
+  a.slash_idx = slash_idx; a.slash_cnt = slash_cnt; a.slash_stride = slash_stride;
+  a.kind = m->lay.kind; a.P = m->lay.P; a.NB = m->QB; a.T = m->T; a.W = m->W; a.Hq = m->Hq;
+  a.rank = rank; a.src = -1; a.tile_cap = m->tile_cap;
+  const int64_t nrows = 2 * (int64_t)m->Hq * m->QB;
+  const int tpb = 64 * ROW_WAVES;
+  const unsigned nblk = (unsigned)((nrows + ROW_WAVES - 1) / ROW_WAVES);
+  for (int s0 = 0; s0 < nsteps; s0 += MAX_MASK_STEPS) {
+    const int ns = nsteps - s0 < MAX_MASK_STEPS ? nsteps - s0 : MAX_MASK_STEPS;
+    MaskRing rg{};
+    for (int i = 0; i < ns; ++i) {
+      vs_mask& x = ms[s0 + i];
+      const int src = ((rank - (s0 + i)) % a.P + a.P) % a.P;
+      x.rank = rank;
+      x.src = src;
+      rg.src[i] = src;
+      rg.tile_ptr[i] = x.tile_ptr; rg.tile_col[i] = x.tile_col; rg.csc_ptr[i] = x.csc_ptr; rg.csc_row[i] = x.csc_row;
+      rg.vloc[i] = x.vloc; rg.vloc_cnt[i] = x.vloc_cnt; rg.vcum[i] = x.vcum; rg.vert_end[i] = x.vert_end;
+      rg.slash_bits[i] = x.slash_bits; rg.n_active[i] = x.n_active; rg.status[i] = x.status;
+    }
+    hipLaunchKernelGGL(mask_head_ring_kernel, dim3(m->Hq, ns), dim3(MASK_THREADS), 0, stream, a, rg);
+    hipLaunchKernelGGL(mask_count_ring_kernel, dim3(nblk, ns), dim3(tpb), 0, stream, a, rg);
+    hipLaunchKernelGGL(mask_scan_ring_kernel, dim3(1, ns), dim3(MASK_THREADS), 0, stream, a, rg);
+    hipLaunchKernelGGL(mask_fill_ring_kernel, dim3(nblk, ns), dim3(tpb), 0, stream, a, rg);
+  }
   return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 

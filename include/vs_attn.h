@@ -302,6 +302,17 @@ int vs_block_mask(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert
                   const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
                   int rank, int step, vs_mask* m, void* stream);
 
+/* The active regions of steps 0 .. nsteps-1 of rank `rank` (1 <= nsteps <=
+ * P), written to masks[0 .. nsteps-1] (host array of descriptors carved by
+ * vs_mask_init for the same shape, layout and tile_cap), each exactly as
+ * vs_block_mask(..., rank, step, &masks[step], ...) writes it, by the same
+ * four launches for up to 32 steps at a time (the masks a rank's resident
+ * ring consumes). Errors as vs_block_mask, plus VS_ERR_ARG for masks of
+ * different shapes; overflow is reported in each mask's own status word. */
+int vs_block_mask_ring(const int32_t* vert_idx, const int32_t* vert_cnt, int64_t vert_stride,
+                       const int32_t* slash_idx, const int32_t* slash_cnt, int64_t slash_stride,
+                       int rank, vs_mask* masks, int nsteps, void* stream);
+
 /* ---- 3./4. forward and merge ----------------------------------------- */
 
 /* Sparse attention of the rank's queries against one visible KV shard,

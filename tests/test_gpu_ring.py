@@ -62,7 +62,9 @@ def _ring_case(kind, P, comp, N, Hq=4, Hkv=2, seed=0):
         rows = ol.shard_positions(kind, N, P, rank)
         q = H.to_dev_comp(t["q"][:, rows], comp)
         do = H.to_dev_comp(t["do"][:, rows], comp)
-        masks = [H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap) for step in range(P)]
+        masks = [vs.Mask(Hq, Hkv, lay, cap) for _ in range(P)]
+        vs.vs_block_mask_ring(*lists, rank, masks)
+        torch.cuda.synchronize()
         for m in masks:
             assert int(m.arrays()["status"].item()) == 0
         # ring: one launch per group of steps
@@ -142,3 +144,35 @@ def test_ring_launch_more_steps_than_one_group():
     """40 steps: the launcher splits them into groups of at most 32, the
     later group merging into (forward) or adding to (backward) the first."""
     _ring_case("striped", 40, "f16", N=64 * 80, Hq=2, Hkv=1, seed=5)
+
+
+@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2), ("contig", 4), ("striped", 40)])
+def test_block_mask_ring_equals_per_step(kind, P):
+    """vs_block_mask_ring writes every step's active region exactly as one
+    vs_block_mask call per step does (every array, bit for bit, over the
+    filled lengths), also past one group of 32 steps."""
+    import dynamic_sparse_attention_index_amd as vs
+    from tests import vs_harness as H
+    rng = np.random.default_rng(P)
+    N, Hq, Hkv = 64 * 2 * P * (2 if P > 8 else 8), 4, 2
+    vert, slash = _index(rng, N, Hq, 50, 5)
+    lay = vs.layout(kind, P, N)
+    QB = N // 64 // P
+    lists = H.upload_lists(vert, slash, N)
+    cap = H.tile_cap_for(slash, Hq, QB)
+    for rank in sorted({0, P - 1, P // 2}):
+        masks = [vs.Mask(Hq, Hkv, lay, cap) for _ in range(P)]
+        vs.vs_block_mask_ring(*lists, rank, masks)
+        torch.cuda.synchronize()
+        for step in range(P):
+            ref = H.gpu_mask(lists, Hq, Hkv, lay, rank, step, cap)
+            a, b = H.mask_to_numpy(masks[step]), H.mask_to_numpy(ref)
+            assert masks[step].desc.src == ref.desc.src == ol.ring_source(rank, step, P)
+            for name in ("tile_ptr", "csc_ptr", "vloc_cnt", "vcum", "vert_end", "slash_bits", "n_active", "status"):
+                assert np.array_equal(a[name], b[name]), (rank, step, name)
+            n = int(b["tile_ptr"][-1])
+            assert np.array_equal(a["tile_col"][:n], b["tile_col"][:n]) and \
+                np.array_equal(a["csc_row"][:n], b["csc_row"][:n]), (rank, step)
+            for h in range(Hq):
+                c = int(b["vloc_cnt"][h])
+                assert np.array_equal(a["vloc"][h * QB * 64:h * QB * 64 + c], b["vloc"][h * QB * 64:h * QB * 64 + c])
