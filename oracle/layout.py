@@ -7,6 +7,8 @@ stripes dealt round-robin).
 
 Readings where the pages leave the detail open:
   * stripe width = one 64-token tile (rank r owns global 64-blocks G = r mod P);
+    the variant "striped1" deals single positions (rank r owns n = r mod P),
+    the plainest reading of "fine-grained stripes dealt round-robin";
   * zigzag = 2P equal chunks, rank r owns chunks r and 2P-1-r;
   * at ring step s, rank r holds the KV shard of rank (r - s) mod P.
 """
@@ -22,6 +24,8 @@ def shard_positions(kind: str, n_global: int, P: int, rank: int) -> np.ndarray:
         owner = pos // (n_global // P)
     elif kind == "striped":
         owner = (pos // BLOCK) % P
+    elif kind == "striped1":
+        owner = pos % P
     elif kind == "zigzag":
         chunk = pos // (n_global // (2 * P))
         owner = np.where(chunk < P, chunk, 2 * P - 1 - chunk)

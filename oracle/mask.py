@@ -15,7 +15,13 @@ M is defined on global positions, so every layout describes the same set.
 The per-(rank, step) description mirrors what the attention kernels consume:
   tiles[h][I]  -- ascending local key blocks J of the visible shard whose 64x64
                   block holds at least one slash-active entry of local query
-                  block I, each flagged DIAG when it is the same global block;
+                  block I, each flagged when not all of its 4096 entries are
+                  active (so a per-entry predicate applies inside it). Under
+                  64-token layouts a local tile is a global tile and the
+                  flagged tile is exactly the query block's own diagonal tile;
+                  under the one-position stripes of "striped1" a tile spans P
+                  global blocks on each side and most listed tiles are
+                  partial;
   vloc[h]      -- ascending local positions of the shard's vertical columns;
   vert_end[h][I] -- how many leading vloc entries have an active entry in
                   query block I (they always form a prefix of vloc);
@@ -47,7 +53,7 @@ def block_description(rows_g, cols_g, vert_h, slash_h):
     for J in range(kb):
         if m_slash[:, J * BLOCK:(J + 1) * BLOCK].any():
             tiles.append(J)
-            diag.append(bool(cols_g[J * BLOCK] // BLOCK == qgb))
+            diag.append(not bool(M[:, J * BLOCK:(J + 1) * BLOCK].all()))
     is_vert_col = np.isin(cols_g, vert_h)
     vloc = np.nonzero(is_vert_col)[0]
     used = m_vert.any(axis=0)[vloc]

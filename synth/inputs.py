@@ -190,6 +190,9 @@ def layout_permutation(kind: str, N: int, P: int, rank: int) -> np.ndarray:
     striped: 64-token stripes dealt round-robin; rank r owns global 64-blocks
              G with G mod P == r (the balanced layout of the review, page 1,
              section 三.3).
+    striped1: single positions dealt round-robin; rank r owns positions n with
+             n mod P == r (the fine-grained stripes of the Ring Attention
+             overview, section 3.1).
     zigzag: 2P equal chunks; rank r owns chunks r and 2P-1-r (same section).
     """
     if kind == "contig":
@@ -199,6 +202,8 @@ def layout_permutation(kind: str, N: int, P: int, rank: int) -> np.ndarray:
         T = N // 64
         blocks = np.arange(rank, T, P, dtype=np.int64)
         return (blocks[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+    if kind == "striped1":
+        return np.arange(rank, N, P, dtype=np.int64)
     if kind == "zigzag":
         c = N // (2 * P)
         a = np.arange(rank * c, (rank + 1) * c, dtype=np.int64)

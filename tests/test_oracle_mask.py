@@ -11,7 +11,7 @@ from synth import layout_permutation
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-@pytest.mark.parametrize("kind", ["contig", "striped", "zigzag"])
+@pytest.mark.parametrize("kind", ["contig", "striped", "zigzag", "striped1"])
 @pytest.mark.parametrize("P", [1, 2, 4, 8])
 def test_layout_partition_and_agreement(kind, P):
     N = 64 * 32
@@ -23,6 +23,8 @@ def test_layout_partition_and_agreement(kind, P):
         assert len(parts[r]) == N // P
         if kind == "striped":
             assert ((parts[r] // 64) % P == r).all()
+        if kind == "striped1":
+            assert (parts[r] % P == r).all()
         if kind == "zigzag":
             ch = parts[r] // (N // (2 * P))
             assert set(ch.tolist()) == {r, 2 * P - 1 - r}
@@ -134,12 +136,9 @@ def test_csc_is_transpose():
     assert pairs_csr == pairs_csc
 
 
-def test_golden_two_rank_mask():
-    """Hand-derived descriptions of a 2-rank ring (striped and zigzag): tile
-    lists, LOCAL vertical positions, vertical prefix lengths and counts."""
-    V, S = np.array([10, 100, 150, 200]), np.array([0, 1])
+def _golden_cases(fname):
     cases = []
-    for line in open(os.path.join(GOLDEN, "mask_p2.txt")):
+    for line in open(os.path.join(GOLDEN, fname)):
         if line.startswith("#") or not line.strip():
             continue
         if line.startswith("@"):
@@ -150,7 +149,10 @@ def test_golden_two_rank_mask():
         blk, tiles, vend, nact = [t.strip() for t in line.split(";")]
         exp_t = [tuple(int(u) for u in t.split(":")) for t in tiles.split()]
         cases[-1][4].append((int(blk), exp_t, int(vend), int(nact)))
-    assert len(cases) == 5
+    return cases
+
+
+def _check_golden(cases, V, S):
     for kind, rank, step, vloc, blocks in cases:
         desc = om.step_description(kind, 256, 2, rank, step, [V], [S])
         assert desc["vloc"][0].tolist() == vloc, (kind, rank, step)
@@ -162,7 +164,55 @@ def test_golden_two_rank_mask():
             assert b["n_active"] == nact, (kind, rank, step, blk)
 
 
-@pytest.mark.parametrize("kind", ["contig", "striped", "zigzag"])
+def test_golden_two_rank_mask():
+    """Hand-derived descriptions of a 2-rank ring (striped and zigzag): tile
+    lists, LOCAL vertical positions, vertical prefix lengths and counts."""
+    cases = _golden_cases("mask_p2.txt")
+    assert len(cases) == 5
+    _check_golden(cases, np.array([10, 100, 150, 200]), np.array([0, 1]))
+
+
+def test_golden_one_position_stripes():
+    """Hand-derived descriptions under one-position stripes (P = 2): every
+    listed tile is partial, counts per query block."""
+    cases = _golden_cases("mask_stripe1.txt")
+    assert len(cases) == 4
+    _check_golden(cases, np.array([10, 77]), np.array([0]))
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_stripe1_description_by_enumeration(P):
+    """Under one-position stripes, for every (rank, step): a tile is listed
+    iff the brute-force active set holds a slash entry in it, flagged iff not
+    all of it is active, counts per block, and the partition of the causal
+    square over all (rank, step)."""
+    rng = np.random.default_rng(70 + P)
+    N = 64 * 4 * P
+    vert = [np.sort(rng.choice(N, 25, replace=False))]
+    slash = [np.array([0, 1, 5])]
+    total = 0
+    for r in range(P):
+        rows = ol.shard_positions("striped1", N, P, r)
+        for s_ in range(P):
+            cols = ol.shard_positions("striped1", N, P, ol.ring_source(r, s_, P))
+            desc = om.step_description("striped1", N, P, r, s_, vert, slash)
+            for I in range(desc["QB"]):
+                rb = rows[64 * I:64 * I + 64]
+                Mb = _brute_mask(rb, cols, vert[0], slash[0])
+                Sb = np.zeros_like(Mb)
+                for a, n in enumerate(rb):
+                    for bb, m in enumerate(cols):
+                        Sb[a, bb] = m <= n and (n // 64 - m // 64) in set(slash[0].tolist())
+                exp = [(J, bool(not Mb[:, 64 * J:64 * J + 64].all())) for J in range(len(cols) // 64)
+                       if Sb[:, 64 * J:64 * J + 64].any()]
+                b = desc["blocks"][(0, I)]
+                assert [(int(J), bool(d)) for J, d in zip(b["tiles"], b["diag"])] == exp
+                assert b["n_active"] == int(Mb.sum())
+                total += b["n_active"]
+    assert total == om.active_count(N, vert[0], slash[0])
+
+
+@pytest.mark.parametrize("kind", ["contig", "striped", "zigzag", "striped1"])
 @pytest.mark.parametrize("P", [2, 4])
 def test_step_description_verticals_by_enumeration(kind, P):
     """vloc and vert_end against a direct enumeration: vloc[k] is the storage
