@@ -16,7 +16,8 @@ The per-(rank, step) description mirrors what the attention kernels consume:
   tiles[h][I]  -- ascending local key blocks J of the visible shard whose 64x64
                   block holds at least one slash-active entry of local query
                   block I, each flagged when not all of its 4096 entries are
-                  active (so a per-entry predicate applies inside it). Under
+                  slash-active (so the slash predicate applies inside it;
+                  vertical columns are accounted separately, below). Under
                   64-token layouts a local tile is a global tile and the
                   flagged tile is exactly the query block's own diagonal tile;
                   under the one-position stripes of "striped1" a tile spans P
@@ -53,7 +54,7 @@ def block_description(rows_g, cols_g, vert_h, slash_h):
     for J in range(kb):
         if m_slash[:, J * BLOCK:(J + 1) * BLOCK].any():
             tiles.append(J)
-            diag.append(not bool(M[:, J * BLOCK:(J + 1) * BLOCK].all()))
+            diag.append(not bool(m_slash[:, J * BLOCK:(J + 1) * BLOCK].all()))
     is_vert_col = np.isin(cols_g, vert_h)
     vloc = np.nonzero(is_vert_col)[0]
     used = m_vert.any(axis=0)[vloc]

@@ -180,16 +180,20 @@ def test_golden_one_position_stripes():
     _check_golden(cases, np.array([10, 77]), np.array([0]))
 
 
-@pytest.mark.parametrize("P", [2, 4])
-def test_stripe1_description_by_enumeration(P):
+@pytest.mark.parametrize("P,slash_set", [(2, (0, 1, 5)), (4, (0, 1, 5)),
+                                         (2, (0, 1, 2, 3, 4, 5, 9)), (4, tuple(range(12)) + (20,))])
+def test_stripe1_description_by_enumeration(P, slash_set):
     """Under one-position stripes, for every (rank, step): a tile is listed
     iff the brute-force active set holds a slash entry in it, flagged iff not
-    all of it is active, counts per block, and the partition of the causal
-    square over all (rank, step)."""
+    all of its entries are slash entries, counts per block, and the partition
+    of the causal square over all (rank, step). The last two slash sets hold
+    whole windows of 2P - 1 consecutive diagonals, so some off-diagonal tiles
+    are full (unflagged) and the rest partial."""
     rng = np.random.default_rng(70 + P)
-    N = 64 * 4 * P
+    N = 64 * 8 * P
     vert = [np.sort(rng.choice(N, 25, replace=False))]
-    slash = [np.array([0, 1, 5])]
+    slash = [np.array(slash_set)]
+    n_full = 0
     total = 0
     for r in range(P):
         rows = ol.shard_positions("striped1", N, P, r)
@@ -199,17 +203,16 @@ def test_stripe1_description_by_enumeration(P):
             for I in range(desc["QB"]):
                 rb = rows[64 * I:64 * I + 64]
                 Mb = _brute_mask(rb, cols, vert[0], slash[0])
-                Sb = np.zeros_like(Mb)
-                for a, n in enumerate(rb):
-                    for bb, m in enumerate(cols):
-                        Sb[a, bb] = m <= n and (n // 64 - m // 64) in set(slash[0].tolist())
-                exp = [(J, bool(not Mb[:, 64 * J:64 * J + 64].all())) for J in range(len(cols) // 64)
+                Sb = (cols[None, :] <= rb[:, None]) & np.isin(rb[:, None] // 64 - cols[None, :] // 64, slash[0])
+                exp = [(J, bool(not Sb[:, 64 * J:64 * J + 64].all())) for J in range(len(cols) // 64)
                        if Sb[:, 64 * J:64 * J + 64].any()]
                 b = desc["blocks"][(0, I)]
                 assert [(int(J), bool(d)) for J, d in zip(b["tiles"], b["diag"])] == exp
                 assert b["n_active"] == int(Mb.sum())
                 total += b["n_active"]
+                n_full += sum(1 for _, d in exp if not d)
     assert total == om.active_count(N, vert[0], slash[0])
+    assert (n_full > 0) == (len(slash_set) > 3)
 
 
 @pytest.mark.parametrize("kind", ["contig", "striped", "zigzag", "striped1"])
