@@ -24,7 +24,7 @@ LIB_PATH = os.environ.get("VS_ATTN_LIB", _build.LIB)
 VS_OK, VS_ERR_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_CAPACITY, VS_ERR_HIP = 0, -1, -2, -3, -4, -5
 VS_ERR_RANGE = -6
 VS_F32, VS_BF16, VS_F16 = 0, 1, 2
-LAYOUTS = {"contig": 0, "striped": 1, "zigzag": 2}
+LAYOUTS = {"contig": 0, "striped": 1, "zigzag": 2, "striped1": 3}
 TILE_DIAG = 0x40000000
 TILE_MASK = 0x3FFFFFFF
 

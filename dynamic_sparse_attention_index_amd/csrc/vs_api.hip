@@ -34,7 +34,9 @@ int check_tensor(const vs_tensor& t, int H, int64_t N, int D) {
 
 int check_layout(const vs_layout& lay) {
   if (lay.P < 1 || lay.n_global <= 0) return VS_ERR_ARG;
-  if (lay.kind != VS_CONTIG && lay.kind != VS_STRIPED && lay.kind != VS_ZIGZAG) return VS_ERR_ARG;
+  if (lay.kind != VS_CONTIG && lay.kind != VS_STRIPED && lay.kind != VS_ZIGZAG && lay.kind != VS_STRIPED1)
+    return VS_ERR_ARG;
+  if (lay.kind == VS_STRIPED1 && lay.P > 32) return VS_ERR_UNSUPPORTED;
   const int64_t unit = (lay.kind == VS_ZIGZAG ? 128 : 64) * (int64_t)lay.P;
   if (lay.n_global % unit) return VS_ERR_UNSUPPORTED;
   if (lay.n_global / 64 > (int64_t)1 << 24) return VS_ERR_UNSUPPORTED;
@@ -109,6 +111,7 @@ int vs_index_build(vs_tensor q_last, vs_tensor k, vs_layout lay, float scale, fl
                    int32_t* slash_idx, int32_t* slash_cnt, void* ws, size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_layout(lay)) != VS_OK) return st;
+  if (lay.kind == VS_STRIPED1 && lay.P > 1) return VS_ERR_UNSUPPORTED;   // keys in global order only
   const int Hq = q_last.H, Hkv = k.H, D = q_last.D, last_q = (int)q_last.N;
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return VS_ERR_ARG;
   if (Hq / Hkv > 8) return VS_ERR_UNSUPPORTED;
@@ -172,6 +175,7 @@ static int check_rank_index(vs_tensor q_last, vs_tensor k_local, vs_layout lay, 
                             size_t ws_bytes, int* Hq, int* Hkv, int* D, int* last_q) {
   int st;
   if ((st = check_layout(lay)) != VS_OK) return st;
+  if (lay.kind == VS_STRIPED1 && lay.P > 1) return VS_ERR_UNSUPPORTED;   // per-rank tiles span P blocks
   if (rank < 0 || rank >= lay.P) return VS_ERR_ARG;
   *Hq = q_last.H; *Hkv = k_local.H; *D = q_last.D; *last_q = (int)q_last.N;
   if (*Hq <= 0 || *Hkv <= 0 || *Hq % *Hkv) return VS_ERR_ARG;
@@ -331,6 +335,7 @@ static int check_attn(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v
   if ((st = check_tensor(v, m->Hkv, Nk, D)) != VS_OK) return st;
   if (q.dtype != k.dtype || q.dtype != v.dtype) return VS_ERR_ARG;
   if (!supported_attn_dtype_dim(q.dtype, D)) return VS_ERR_UNSUPPORTED;
+  if (m->lay.kind == VS_STRIPED1) return VS_ERR_UNSUPPORTED;
   return VS_OK;
 }
 
@@ -440,6 +445,7 @@ static int check_ring(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v
   if ((st = check_tensor(v, m.Hkv, Nall, D)) != VS_OK) return st;
   if (q.dtype != k.dtype || q.dtype != v.dtype) return VS_ERR_ARG;
   if ((q.dtype != VS_BF16 && q.dtype != VS_F16) || D != 128) return VS_ERR_UNSUPPORTED;
+  if (m.lay.kind == VS_STRIPED1) return VS_ERR_UNSUPPORTED;
   return VS_OK;
 }
 

@@ -102,9 +102,14 @@ __device__ __forceinline__ void mask_head_body(const MaskArgs& a) {
     if (e < nv) {
       const int64_t m = V[e];
       if (m >= 0 && m < (int64_t)a.T * BLK) {
-        int J;
-        keep = owner_of_block(a.kind, a.P, a.NB, m / BLK, &J) == a.src;
-        local = J * BLK + (int)(m % BLK);
+        if (a.kind == VS_STRIPED1) {
+          keep = (int)(m % a.P) == a.src;
+          local = (int)(m / a.P);
+        } else {
+          int J;
+          keep = owner_of_block(a.kind, a.P, a.NB, m / BLK, &J) == a.src;
+          local = J * BLK + (int)(m % BLK);
+        }
       }
     }
     int tot;
@@ -130,6 +135,100 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
   return x;
 }
 
+// ---- one-position stripes (VS_STRIPED1) ---------------------------------------
+// Local position l of rank r is global position l P + r, so local query block
+// I (rank r) spans global blocks I P .. I P + P - 1 and local key block J
+// (shard s) global blocks J P .. J P + P - 1 (P <= 32). Row a of the query
+// block lies in global block I P + qa(a), qa(a) = (a P + r) >> 6, and key b in
+// J P + kb(b), kb(b) = (b P + s) >> 6. An entry of tile (I, J) lies on global
+// block-diagonal o P + qa - kb with o = I - J, and every (qa, kb) pair occurs,
+// so with o >= 1 the tile meets diagonals o P - P + 1 .. o P + P - 1 (all of
+// them causal). With o = 0 it meets 0 .. P - 1 causally (diagonal 0 partly:
+// b P + s <= a P + r); negative ones lie above the rows.
+
+// Bits lo .. lo + len - 1 (len <= 64) of a head's slash bitmap of W words;
+// bits outside the bitmap read as 0.
+__device__ __forceinline__ uint64_t sbit_window(const uint32_t* sb, int W, int64_t lo, int len) {
+  const int64_t w0 = lo >> 5;                 // floor(lo / 32), also for lo < 0
+  const int sh = (int)(lo - w0 * 32);
+  auto word = [&](int64_t i) -> uint64_t { return (i >= 0 && i < W) ? (uint64_t)sb[i] : 0ull; };
+  const uint64_t lo64 = word(w0) | (word(w0 + 1) << 32);
+  uint64_t x = lo64 >> sh;
+  if (sh) x |= word(w0 + 2) << (64 - sh);
+  return len >= 64 ? x : (x & ((1ull << len) - 1ull));
+}
+// Selected diagonals a stripe-1 tile at block offset o meets (bit i: diagonal
+// o P - P + 1 + i for o >= 1; diagonal i for o = 0).
+__device__ __forceinline__ uint64_t s1_window(const uint32_t* sb, int W, int P, int o) {
+  return o == 0 ? sbit_window(sb, W, 0, P) : sbit_window(sb, W, (int64_t)o * P - P + 1, 2 * P - 1);
+}
+// A listed tile is full (unflagged) when every diagonal it meets is selected.
+__device__ __forceinline__ bool s1_full(uint64_t win, int P, int o) {
+  return o > 0 && win == ((2 * P - 1 >= 64) ? ~0ull : ((1ull << (2 * P - 1)) - 1ull));
+}
+// First row a of the query block with qa(a) >= x (x in 0 .. P): rows with
+// qa = x are [first(x), first(x + 1)).
+__device__ __forceinline__ int s1_first(int x, int r, int P) {
+  return x == 0 ? 0 : min(BLK, (BLK * x - r + P - 1) / P);
+}
+
+// Per-workgroup tables of the stripe-1 counts for one (rank r, shard s):
+//   fq[x]  first row with qa >= x (x = 0 .. P), fk[y] the same for keys;
+//   cd[d + P - 1] = entries with qa - kb = d (d = -(P-1) .. P-1);
+//   cd0 = causal entries with qa == kb (b P + s <= a P + r).
+struct S1Tables {
+  int fq[33], fk[33];
+  int cd[63];
+  int cd0;
+};
+__device__ void s1_tables(S1Tables& t, int r, int s, int P) {
+  const int tid = threadIdx.x;
+  if (tid <= P) {
+    t.fq[tid] = s1_first(tid, r, P);
+    t.fk[tid] = s1_first(tid, s, P);
+  }
+  __syncthreads();
+  if (tid < 2 * P - 1) {
+    const int d = tid - (P - 1);
+    int c = 0;
+    for (int x = 0; x < P; ++x) {
+      const int y = x - d;
+      if (y >= 0 && y < P) c += (t.fq[x + 1] - t.fq[x]) * (t.fk[y + 1] - t.fk[y]);
+    }
+    t.cd[tid] = c;
+  }
+  if (tid == 0) {
+    int c = 0;
+    for (int aa = 0; aa < BLK; ++aa) {
+      const int x = ((aa * P + r) >> 6);
+      const int hi = min(t.fk[x + 1] - 1, aa - (r < s ? 1 : 0));   // b <= a (r >= s) or b < a
+      c += max(0, hi - t.fk[x] + 1);
+    }
+    t.cd0 = c;
+  }
+  __syncthreads();
+}
+// Slash-active entries of a listed tile at offset o with window `win`.
+__device__ __forceinline__ int s1_tile_count(const S1Tables& t, uint64_t win, int P, int o) {
+  int c = 0;
+  if (o > 0) {
+    while (win) {
+      const int i = __builtin_ctzll(win);
+      win &= win - 1;
+      c += t.cd[i];               // diagonal o P - P + 1 + i: qa - kb = i - (P - 1)
+    }
+  } else {
+    if (win & 1ull) c += t.cd0;
+    win &= ~1ull;
+    while (win) {
+      const int i = __builtin_ctzll(win);
+      win &= win - 1;
+      c += t.cd[i + P - 1];
+    }
+  }
+  return c;
+}
+
 // Launch 2: list lengths.
 __device__ __forceinline__ void mask_count_body(const MaskArgs& a) {
   const int lane = threadIdx.x & 63;
@@ -142,6 +241,14 @@ __device__ __forceinline__ void mask_count_body(const MaskArgs& a) {
   const int32_t* S = a.slash_idx + (int64_t)h * a.slash_stride;
   const int ns = a.slash_cnt[h];
   int cnt = 0;
+  if (a.kind == VS_STRIPED1) {   // block offsets o = I - J with a selected diagonal in the tile's window
+    const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
+    const int n_o = csr ? B + 1 : a.NB - B;   // CSR row I: J = 0 .. I; CSC column J: I = J .. NB - 1
+    for (int o = lane; o < n_o; o += 64) cnt += s1_window(sb, a.W, a.P, o) != 0ull;
+    cnt = wave_sum_i32(cnt);
+    if (lane == 0) (csr ? a.tile_ptr : a.csc_ptr)[1 + u] = cnt;
+    return;
+  }
   if (csr) {  // key blocks G - j of the visible shard
     const int64_t G = global_block(a.kind, a.P, a.NB, a.rank, B);
     for (int e = lane; e < ns; e += 64) {
@@ -205,10 +312,21 @@ __device__ __forceinline__ void mask_scan_body(const MaskArgs& a) {
 // Launch 4: fill the lists; the CSR half also writes vert_end and n_active.
 // Order-preserving compaction per 64-entry chunk: a lane's output position is
 // the running count plus the matches of the lanes below it (ballot).
+__device__ void mask_fill_s1(const MaskArgs& a, const S1Tables& tb, bool csr, int64_t u, int h, int B);
+
 __device__ __forceinline__ void mask_fill_body(const MaskArgs& a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * ROW_WAVES + (threadIdx.x >> 6);
   const int64_t nrow = (int64_t)a.Hq * a.NB;
+  if (a.kind == VS_STRIPED1) {
+    __shared__ S1Tables tb;
+    s1_tables(tb, a.rank, a.src, a.P);
+    if (t >= 2 * nrow) return;
+    const bool csr = t < nrow;
+    const int64_t u = csr ? t : t - nrow;
+    mask_fill_s1(a, tb, csr, u, (int)(u / a.NB), (int)(u % a.NB));
+    return;
+  }
   if (t >= 2 * nrow) return;
   const bool csr = t < nrow;
   const int64_t u = csr ? t : t - nrow;
@@ -279,6 +397,72 @@ __device__ __forceinline__ void mask_fill_body(const MaskArgs& a) {
       }
       const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
       if (ok) dst[n + __builtin_popcountll(m & below)] = I | (j == 0 ? VS_TILE_DIAG : 0);
+      n += __builtin_popcountll(m);
+    }
+  }
+}
+
+// Launch 4 under one-position stripes. CSR row (h, I): key blocks J = I - o
+// ascending with a selected diagonal in the window, flagged unless the window
+// is wholly selected; n_active adds each listed tile's slash entries and, per
+// vertical column of the shard, its causal rows on unselected diagonals.
+// vert_end: the columns at or before the block's last row,
+// l P + s <= (64 I + 63) P + r, i.e. l < 64 I + 64 - [r < s].
+// CSC column (h, J): query blocks I = J + o ascending, the same flags.
+__device__ void mask_fill_s1(const MaskArgs& a, const S1Tables& tb, bool csr, int64_t u, int h, int B) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
+  const bool fits = a.status[0] == VS_OK;
+  const int P = a.P;
+  if (csr) {
+    const int I = B;
+    int32_t* dst = a.tile_col + a.tile_ptr[u];
+    int n = 0, act = 0;
+    for (int c0 = 0; c0 <= I; c0 += 64) {
+      const int J = c0 + lane, o = I - J;
+      uint64_t win = 0;
+      if (J <= I) win = s1_window(sb, a.W, P, o);
+      const bool ok = win != 0ull;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      if (ok) {
+        if (fits) dst[n + __builtin_popcountll(m & below)] = J | (s1_full(win, P, o) ? 0 : VS_TILE_DIAG);
+        act += s1_tile_count(tb, win, P, o);
+      }
+      n += __builtin_popcountll(m);
+    }
+    const int32_t* vl = a.vloc + (int64_t)h * a.NB * BLK;
+    const int nv = a.vloc_cnt[h];
+    const int ve = lower_bound_i32(vl, nv, (int64_t)BLK * I + BLK - (a.rank < a.src ? 1 : 0));
+    int vpart = 0;
+    for (int e = lane; e < ve; e += 64) {
+      const int64_t mg = (int64_t)vl[e] * P + a.src;          // global column
+      // first causal row: (64 I + c) P + r >= mg
+      const int64_t num = mg - a.rank - (int64_t)BLK * I * P;
+      const int c = num <= 0 ? 0 : (int)min<int64_t>(BLK, (num + P - 1) / P);
+      // bit x: diagonal I P + x - floor(mg / 64) selected (negative ones: rows above the column)
+      const uint64_t win = sbit_window(sb, a.W, (int64_t)I * P - (mg >> 6), P);
+      for (int x = 0; x < P; ++x)
+        if (!((win >> x) & 1ull)) vpart += max(0, tb.fq[x + 1] - max(tb.fq[x], c));
+    }
+    act = wave_sum_i32(act);
+    vpart = wave_sum_i32(vpart);
+    if (lane == 0) {
+      a.vert_end[u] = fits ? ve : 0;
+      a.n_active[u] = (int64_t)act + vpart;
+    }
+  } else {
+    if (!fits) return;
+    const int J = B;
+    int32_t* dst = a.csc_row + a.csc_ptr[u];
+    int n = 0;
+    for (int c0 = 0; J + c0 < a.NB; c0 += 64) {
+      const int o = c0 + lane, I = J + o;
+      uint64_t win = 0;
+      if (I < a.NB) win = s1_window(sb, a.W, P, o);
+      const bool ok = win != 0ull;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      if (ok) dst[n + __builtin_popcountll(m & below)] = I | (s1_full(win, P, o) ? 0 : VS_TILE_DIAG);
       n += __builtin_popcountll(m);
     }
   }

@@ -71,9 +71,19 @@ typedef enum { VS_F32 = 0, VS_BF16 = 1, VS_F16 = 2 } vs_dtype;
  *   VS_CONTIG  -- rank r holds [r*N/P, (r+1)*N/P);
  *   VS_STRIPED -- 64-token stripes round-robin: rank r holds global blocks
  *                 G with G mod P == r (the balanced layout);
- *   VS_ZIGZAG  -- 2P equal chunks, rank r holds chunks r and 2P-1-r.
+ *   VS_ZIGZAG  -- 2P equal chunks, rank r holds chunks r and 2P-1-r;
+ *   VS_STRIPED1 -- single positions dealt round-robin: rank r holds the
+ *                 positions n with n mod P == r (the fine-grained stripes of
+ *                 the Ring Attention overview, section 3.1); P <= 32. A
+ *                 local 64-row tile then spans P global blocks, so listed
+ *                 tiles are mostly partial (VS_TILE_DIAG marks them) and the
+ *                 attention kernels evaluate the active set entry by entry in
+ *                 them. The index calls refuse this kind for P > 1
+ *                 (VS_ERR_UNSUPPORTED): build the index on the keys in global
+ *                 order (VS_CONTIG, P = 1); the lists are global positions
+ *                 and diagonals, the same under every layout.
  * A shard is stored in ascending global order. P = 1 is the plain sequence. */
-typedef enum { VS_CONTIG = 0, VS_STRIPED = 1, VS_ZIGZAG = 2 } vs_layout_kind;
+typedef enum { VS_CONTIG = 0, VS_STRIPED = 1, VS_ZIGZAG = 2, VS_STRIPED1 = 3 } vs_layout_kind;
 
 typedef struct {
   int32_t kind;      /* vs_layout_kind */
@@ -92,8 +102,10 @@ typedef struct {
   int64_t stride_n;
 } vs_tensor;
 
-/* Flag bit on tile_col / csc_row entries: the tile is the query block's own
- * global block, so the causal predicate applies inside it. */
+/* Flag bit on tile_col / csc_row entries: not every entry of the tile is
+ * active, so a predicate applies inside it. Under the 64-token layouts that
+ * is exactly the query block's own global block (the causal cut); under
+ * VS_STRIPED1 any tile not wholly covered by selected diagonals. */
 #define VS_TILE_DIAG 0x40000000
 #define VS_TILE_MASK 0x3FFFFFFF
 

@@ -69,6 +69,9 @@ def test_layout_validation(L):
     assert L.vs_mask_bytes(4, 2, vs.layout("striped", 3, 64 * 10), 10) == 0      # N % (64 P) != 0
     assert L.vs_mask_bytes(4, 2, vs.layout("zigzag", 2, 64 * 6), 10) == 0        # N % (128 P) != 0
     assert L.vs_mask_bytes(4, 2, vs.layout("zigzag", 2, 64 * 8), 10) > 0
+    assert L.vs_mask_bytes(4, 2, vs.layout("striped1", 4, 64 * 8), 10) > 0
+    assert L.vs_mask_bytes(4, 2, vs.layout("striped1", 4, 64 * 6), 10) == 0      # N % (64 P) != 0
+    assert L.vs_mask_bytes(4, 2, vs.layout("striped1", 33, 64 * 33), 10) == 0    # one-position stripes: P <= 32
     m = vs.VsMask()
     assert L.vs_mask_init(ctypes.byref(m), 0x10000000, 1 << 20, 3, 2, vs.layout("contig", 1, 1024), 10) \
         == vs.VS_ERR_ARG                                                           # Hq % Hkv != 0
@@ -117,6 +120,11 @@ def test_block_mask_and_index_validation(L):
     assert L.vs_index_build(q, k3, lay, 0.1, 0.9, *args, p, ws, None) == vs.VS_ERR_ARG
     kshort = _fake_tensor(0x30000000, 2, 2048, 128)
     assert L.vs_index_build(q, kshort, lay, 0.1, 0.9, *args, p, ws, None) == vs.VS_ERR_ARG
+    # one-position stripes: the index takes the keys in global order
+    s1 = vs.layout("striped1", 4, 4096)
+    assert L.vs_index_build(q, k, s1, 0.1, 0.9, *args, p, ws, None) == vs.VS_ERR_UNSUPPORTED
+    k_local = _fake_tensor(0x30000000, 2, 1024, 128)
+    assert L.vs_index_rank_stats(q, k_local, s1, 0, 0.1, p, p, ws, None) == vs.VS_ERR_UNSUPPORTED
 
 
 def test_rank_index_validation(L):

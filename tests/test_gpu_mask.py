@@ -71,6 +71,25 @@ def test_mask_bitexact_layouts(kind, P):
             _check_mask(vert, slash, Hq, Hkv, kind, P, rank, step, N)
 
 
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8, 32])
+def test_mask_bitexact_stripe1(P):
+    """One-position stripes: every (rank, step) of small rings, and sampled
+    (rank, step) pairs at P = 8 and 32, against the oracle's description.
+    Slash sets mix sparse diagonals with whole windows of 2P - 1 consecutive
+    diagonals (full tiles) and heads without diagonal 0."""
+    rng = np.random.default_rng(300 + P)
+    N, Hq, Hkv = 64 * P * (24 if P <= 4 else 6), 4, 2
+    T = N // 64
+    vert, slash = _random_index(rng, N, Hq, 150, 10, force_diag=[1, 0, 1, 0])
+    run = min(T - 1, 3 * P)
+    slash[2] = np.union1d(slash[2], np.arange(1, run)).astype(np.int64)
+    slash[3] = np.union1d(slash[3], np.arange(T - run, T)).astype(np.int64)
+    pairs = [(r, s) for r in range(P) for s in range(P)] if P <= 4 else \
+        [(0, 0), (P - 1, 0), (1, P - 1), (P // 2, 3), (P - 1, P - 1)]
+    for rank, step in pairs:
+        _check_mask(vert, slash, Hq, Hkv, "striped1", P, rank, step, N)
+
+
 def test_mask_edge_cases():
     N, Hq = 64 * 8, 3
     # empty index, full index, and only the diagonal
@@ -78,6 +97,8 @@ def test_mask_edge_cases():
     slash = [np.zeros(0, dtype=np.int64), np.arange(N // 64), np.array([0])]
     _check_mask(vert, slash, Hq, 1, "contig", 1, 0, 0, N)
     _check_mask(vert, slash, Hq, 1, "striped", 2, 1, 1, N)
+    _check_mask(vert, slash, Hq, 1, "striped1", 2, 1, 1, N)
+    _check_mask(vert, slash, Hq, 1, "striped1", 4, 0, 3, N)
 
 
 def test_mask_capacity_overflow_reported():

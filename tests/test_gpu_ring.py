@@ -146,7 +146,8 @@ def test_ring_launch_more_steps_than_one_group():
     _ring_case("striped", 40, "f16", N=64 * 80, Hq=2, Hkv=1, seed=5)
 
 
-@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2), ("contig", 4), ("striped", 40)])
+@pytest.mark.parametrize("kind,P", [("striped", 4), ("zigzag", 2), ("contig", 4), ("striped", 40),
+                                    ("striped1", 4), ("striped1", 32)])
 def test_block_mask_ring_equals_per_step(kind, P):
     """vs_block_mask_ring writes every step's active region exactly as one
     vs_block_mask call per step does (every array, bit for bit, over the

@@ -74,7 +74,10 @@ def upload_lists(vert, slash, N):
 
 
 def tile_cap_for(slash, Hq, QB):
-    return max(1, Hq * QB * (max(len(s) for s in slash) + 1))
+    """Tiles a mask can list: per query block at most one per selected diagonal
+    under 64-token layouts and at most two per diagonal under one-position
+    stripes (a diagonal j meets block offsets floor(j / P) and ceil(j / P))."""
+    return max(1, Hq * QB * (2 * max(len(s) for s in slash) + 1))
 
 
 def gpu_mask(lists_dev, Hq, Hkv, lay, rank, step, tile_cap):
