@@ -335,7 +335,8 @@ static int check_attn(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v
   if ((st = check_tensor(v, m->Hkv, Nk, D)) != VS_OK) return st;
   if (q.dtype != k.dtype || q.dtype != v.dtype) return VS_ERR_ARG;
   if (!supported_attn_dtype_dim(q.dtype, D)) return VS_ERR_UNSUPPORTED;
-  if (m->lay.kind == VS_STRIPED1) return VS_ERR_UNSUPPORTED;
+  // one-position stripes: the per-entry path of the head-dim-128 kernels
+  if (m->lay.kind == VS_STRIPED1 && (D != 128 || q.dtype == VS_F32)) return VS_ERR_UNSUPPORTED;
   return VS_OK;
 }
 
@@ -358,6 +359,7 @@ int vs_attn_fwd_packed(vs_tensor q, vs_tensor k, vs_tensor v, const vs_mask* m, 
   if (accumulate != 0 && accumulate != 1) return VS_ERR_ARG;
   if (!finite_positive(scale)) return VS_ERR_ARG;
   if ((q.dtype != VS_BF16 && q.dtype != VS_F16) || q.D != 128 || (m->Hq / m->Hkv) % 2) return VS_ERR_UNSUPPORTED;
+  if (m->lay.kind == VS_STRIPED1) return VS_ERR_UNSUPPORTED;
   return launch_attn_fwd_packed(q.dtype, view(q), view(k), view(v), m, scale, o, lse, accumulate, status,
                                 (hipStream_t)stream);
 }

@@ -438,7 +438,9 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 // a single fp16 dS put dQ at 1.9e-2 of the oracle at 262144 tokens.
 // RING: the tile sequence runs over several ring steps (RingTiles, `rs`; K/V
 // hold every shard in storage order) and dQ accumulates across them.
-template <bool F16, bool RING = false>
+// S1 (one-position stripes): per-key thresholds and diagonal windows, as in
+// the forward.
+template <bool F16, bool RING = false, bool S1 = false>
 __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = nullptr) {
   constexpr int D = TD;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
@@ -447,6 +449,7 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
   __shared__ __attribute__((aligned(16))) bf16 V1[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) int thr0_sh[BLK];
   __shared__ __attribute__((aligned(16))) int thr1_sh[BLK];
+  __shared__ __attribute__((aligned(16))) uint32_t win_sh[2][S1 ? BLK : 4];
   __shared__ int desc0_sh[BLK], desc1_sh[BLK];
   __shared__ uint32_t sbits[MAX_LDS_W];
 
@@ -490,22 +493,35 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
   const uint32_t krb = (uint32_t)a.ksn * 2, vrb = (uint32_t)a.vsn * 2;   // row pitch in bytes
   const DmaLane dlane = dma_lane(wave, lane);
   // start the copy of tile t into (Kn, Vn); its row thresholds go to thn
-  auto issue = [&](int t, const int* slot, bf16* Kn, bf16* Vn, int* thn) -> int {
+  // (S1: its diagonal windows to wn)
+  auto issue = [&](int t, const int* slot, bf16* Kn, bf16* Vn, int* thn, uint32_t* wn) -> int {
     int thr = tid, mode = 1;
+    uint32_t win = ~0u;
     const int64_t sr0 = bt.row0(t, 1);   // the tile's shard
     const char* kb = kbase + sr0 * krb;
     const char* vb = vbase + sr0 * vrb;
     if (!bt.vert(t, 1)) {
       const int r0 = bt.tile_row(slot, mode);
+      if constexpr (S1) {
+        if (tid < BLK) {
+          const int o = I - r0 / BLK;
+          win = s1_key_window(s1_tile_window(sbits, a.W, a.P, o), a.P, a.src, tid);
+          thr = s1_key_threshold(o, a.rank, a.src, tid);
+        }
+      }
       dma_tile_rows(Kn, kb + (int64_t)r0 * krb, krb, dlane, wave);
       dma_tile_rows(Vn, vb + (int64_t)r0 * vrb, vrb, dlane, wave);
     } else {
       int rows[4];
-      bt.vert_rows(t, slot, rows, thr, wave, lane, tid, 1);
+      if constexpr (S1) bt.vert_rows_s1(t, slot, rows, thr, win, wave, lane, tid, I, a.rank, a.W);
+      else bt.vert_rows(t, slot, rows, thr, wave, lane, tid, 1);
       dma_tile_gather(Kn, kb, rows, krb, dlane, wave);
       dma_tile_gather(Vn, vb, rows, vrb, dlane, wave);
     }
-    if (tid < BLK) thn[tid] = thr;
+    if (tid < BLK) {
+      thn[tid] = thr;
+      if constexpr (S1) wn[tid] = win;
+    }
     return mode;
   };
   bf16x8 qf[2][4], df[2][4];
@@ -531,14 +547,19 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
     for (int dt = 0; dt < 8; ++dt) acc[rs][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale_log2;
   int mode_c = 0;
+  int qa_l[2] = {0, 0};   // S1: global-block offset qa of this lane's two rows
+  if constexpr (S1) {
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) qa_l[rs] = ((32 * rh + 16 * rs + n16) * a.P + a.rank) >> 6;
+  }
 
-  auto step = [&](int it, const bf16* Ks, const bf16* Vs, const int* thc, bf16* Kn, bf16* Vn, int* thn,
-                  int* dn_next, const int* dn_cur) {
+  auto step = [&](int it, const bf16* Ks, const bf16* Vs, const int* thc, const uint32_t* wc, bf16* Kn, bf16* Vn,
+                  int* thn, uint32_t* wn, int* dn_next, const int* dn_cur) {
     wait_all_mem();
     __syncthreads();
     const int mode = mode_c;
     if (it + 1 < total) {
-      mode_c = issue(it + 1, dn_cur, Kn, Vn, thn);
+      mode_c = issue(it + 1, dn_cur, Kn, Vn, thn, wn);
       if (it + 2 < total) bt.desc_copy(it + 2, dn_next, wave, lane);
     }
     // S^T and dP^T for keys 32 kh + 8 g + 4 t + i, rows 16 rs + n of the wave
@@ -564,13 +585,21 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
       // row thresholds of this lane's 8 keys (two 16-byte reads)
       const i32x4 th0 = *(const i32x4*)(thc + 32 * kh + 8 * g4);
       const i32x4 th1 = *(const i32x4*)(thc + 32 * kh + 8 * g4 + 4);
+      i32x4 w0 = i32x4{-1, -1, -1, -1}, w1 = w0;
+      if constexpr (S1) {
+        w0 = *(const i32x4*)(wc + 32 * kh + 8 * g4);
+        w1 = *(const i32x4*)(wc + 32 * kh + 8 * g4 + 4);
+      }
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((t == 0 ? th0[i] : th1[i]) > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            bool off = (t == 0 ? th0[i] : th1[i]) > 32 * rh + 16 * rs + n16;
+            if constexpr (S1) off = off || !(((uint32_t)(t == 0 ? w0[i] : w1[i]) >> qa_l[rs]) & 1u);
+            if (off) s[rs][t][i] = -INFINITY;
+          }
     }
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
@@ -616,10 +645,10 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
   if (total > 1) bt.desc_copy(1, desc1_sh, wave, lane);
   wait_all_mem();
   __syncthreads();
-  mode_c = issue(0, desc0_sh, K0, V0, thr0_sh);
+  mode_c = issue(0, desc0_sh, K0, V0, thr0_sh, win_sh[0]);
   for (int it = 0; it < total; it += 2) {
-    step(it, K0, V0, thr0_sh, K1, V1, thr1_sh, desc0_sh, desc1_sh);
-    if (it + 1 < total) step(it + 1, K1, V1, thr1_sh, K0, V0, thr0_sh, desc1_sh, desc0_sh);
+    step(it, K0, V0, thr0_sh, win_sh[0], K1, V1, thr1_sh, win_sh[1], desc0_sh, desc1_sh);
+    if (it + 1 < total) step(it + 1, K1, V1, thr1_sh, win_sh[1], K0, V0, thr0_sh, win_sh[0], desc1_sh, desc0_sh);
   }
   __syncthreads();
   float* xo = (float*)(rh == 0 ? K0 : V0);   // [2 rs][8 dt][64 lanes] f32x4 per row half
@@ -646,6 +675,10 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
 }
 __global__ void __launch_bounds__(BWD_THREADS, 2) dq_bf16_d128_kernel(BwdArgs a) { dq_d128<false>(a); }
 __global__ void __launch_bounds__(BWD_THREADS, 2) dq_f16_d128_kernel(BwdArgs a) { dq_d128<true>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 2) dq_s1_bf16_d128_kernel(BwdArgs a) {
+  dq_d128<false, false, true>(a);
+}
+__global__ void __launch_bounds__(BWD_THREADS, 2) dq_s1_f16_d128_kernel(BwdArgs a) { dq_d128<true, false, true>(a); }
 __global__ void __launch_bounds__(BWD_THREADS, 2) dq_ring_bf16_d128_kernel(BwdArgs a, RingSteps rs) {
   dq_d128<false, true>(a, &rs);
 }
@@ -711,11 +744,13 @@ __device__ __forceinline__ void kv_rowstats(const float* lsh, const float* dsh_,
 }
 // l2: row LSE in log2 units, +inf for an empty row (kv_rowstats); on the
 // diagonal tile (wave-uniform `diag`) key kt of this lane is active for rows
-// >= thr[kt].
-template <bool F16, bool PAIR = !F16>
+// >= thr[kt]. S1: and only for the rows 4 t + i of this lane whose
+// global-block offset qa[4 t + i] is a set bit of win[kt].
+template <bool F16, bool PAIR = !F16, bool S1 = false>
 __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], const f32x4* l2, const f32x4* dd,
                                        int diag, const int* thr, int rh, int g4, float sl2, bf16x8* ph,
-                                       bf16x8* pl, bf16x8* dh, bf16x8* dl) {
+                                       bf16x8* pl, bf16x8* dh, bf16x8* dl, const uint32_t* win = nullptr,
+                                       const int* qa = nullptr) {
   const int r0 = 32 * rh + 8 * g4;
   if (diag) {
 #pragma unroll
@@ -723,8 +758,11 @@ __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], cons
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r0 + 4 * t + i < thr[kt]) s[kt][t][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          bool off = r0 + 4 * t + i < thr[kt];
+          if constexpr (S1) off = off || !((win[kt] >> qa[4 * t + i]) & 1u);
+          if (off) s[kt][t][i] = -INFINITY;
+        }
   }
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -884,7 +922,11 @@ __device__ __forceinline__ void kv_finish(float* xbuf_dk, float* xbuf_dv, f32x4 
 // b / (gridDim.x / nsteps) (a whole number of XCD rounds per step), reads
 // that step's CSC lists and writes the dK/dV rows of its visible shard in
 // tensors that hold every shard in storage order (as K/V do).
-template <bool F16, bool RING = false>
+//
+// S1 (one-position stripes): keys of a flagged tile carry a causal threshold
+// and a window of diagonals (as in the forward), built per tile from the
+// tile's q head's slash bitmap.
+template <bool F16, bool RING = false, bool S1 = false>
 __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* rk = nullptr) {
   BwdArgs a = a0;
   int b = blockIdx.x;
@@ -990,8 +1032,8 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
     ++cur_p;
     cur_skip();
   };
-  // start the copy of tile t into stage p; returns its diagonal flag (bit 0)
-  // and its q head within the group (bits 1..)
+  // start the copy of tile t into stage p; returns its diagonal flag (bit 0),
+  // its q head within the group (bits 1..3) and, S1, its query block (bits 4..)
   auto issue = [&]<int p>(int t) -> int {
     const int e = __builtin_amdgcn_readfirstlane(desc_sh[t % 3][0]);
     const int hh = __builtin_amdgcn_readfirstlane(head_sh[t % 3]);
@@ -1009,8 +1051,13 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
                                            (__attribute__((address_space(3))) float*)(ls + wave * BLK)),
                                        4, 0, 0);
     }
-    return ((e & VS_TILE_DIAG) ? 1 : 0) | (hh << 1);
+    return ((e & VS_TILE_DIAG) ? 1 : 0) | (hh << 1) | (S1 ? (I << 4) : 0);
   };
+  int qa_r[8] = {};   // S1: global-block offset qa of this lane's eight rows
+  if constexpr (S1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qa_r[j] = ((32 * rh + 8 * g4 + j) * a.P + a.rank) >> 6;
+  }
 
   bf16x8 kf[2][4], vf[2][4];
 #pragma unroll
@@ -1055,21 +1102,34 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
     kv_rowstats<true>(Lc, Lc + BLK, rh, g4, l2, dd);
     // key kt of this lane is active for rows >= thr[kt]: its index on the
     // diagonal tile, 0 elsewhere, and never (BLK) for a vertical of the head
-    const int hh_i = diag_i >> 1;
+    const int hh_i = S1 ? (diag_i >> 1) & 7 : diag_i >> 1;
     const uint32_t vlo = __builtin_amdgcn_readlane(vm_lo_l, hh_i), vhi = __builtin_amdgcn_readlane(vm_hi_l, hh_i);
     int thr[2];
+    uint32_t win[2] = {~0u, ~0u};
+    if constexpr (S1) {
+      const int o = (diag_i >> 4) - J;
+      const uint64_t tw = s1_tile_window(a.slash_bits + (int64_t)(kvh * grp + hh_i) * a.W, a.W, a.P, o);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = 32 * kh + 16 * kt + n16;
-      const bool vert = ((kh ? vhi : vlo) >> (16 * kt + n16)) & 1u;
-      thr[kt] = vert ? BLK : ((diag_i & 1) ? key : 0);
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = 32 * kh + 16 * kt + n16;
+        const bool vert = ((kh ? vhi : vlo) >> (16 * kt + n16)) & 1u;
+        win[kt] = s1_key_window(tw, a.P, a.src, key);
+        thr[kt] = vert ? BLK : s1_key_threshold(o, a.rank, a.src, key);
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = 32 * kh + 16 * kt + n16;
+        const bool vert = ((kh ? vhi : vlo) >> (16 * kt + n16)) & 1u;
+        thr[kt] = vert ? BLK : ((diag_i & 1) ? key : 0);
+      }
     }
     const int masked = ((diag_i & 1) || vlo || vhi) ? 1 : 0;
     __builtin_amdgcn_sched_barrier(0);
     f32x4 s_n[2][2], dp_n[2][2];
     kv_sdp<F16>(qa, oa, kf, vf, s_n, dp_n);
     bf16x8 ph[2], pl[2], dh[2], dl[2];
-    kv_pds<F16>(s_c, dp_c, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl);
+    kv_pds<F16, !F16, S1>(s_c, dp_c, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl, win, qa_r);
     constexpr int VPM = F16 ? 4 : 6;   // vector ops per MFMA (fp16 weights need one convert per pair)
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
@@ -1120,6 +1180,12 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
 }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_bf16_d128_kernel(BwdArgs a) { dkdv_d128<false>(a); }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_f16_d128_kernel(BwdArgs a) { dkdv_d128<true>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_s1_bf16_d128_kernel(BwdArgs a) {
+  dkdv_d128<false, false, true>(a);
+}
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_s1_f16_d128_kernel(BwdArgs a) {
+  dkdv_d128<true, false, true>(a);
+}
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_ring_bf16_d128_kernel(BwdArgs a, RingStepsKV rk) {
   dkdv_d128<false, true>(a, &rk);
 }
@@ -1141,7 +1207,9 @@ __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_ring_f16_d128_kernel(BwdA
 //
 // RING: the work items of several ring steps in one launch (each step's
 // verticals in its visible shard, written to tensors holding every shard).
-template <bool F16, bool RING = false>
+// S1 (one-position stripes): the causal rows of a column follow from its
+// global position l P + src.
+template <bool F16, bool RING = false, bool S1 = false>
 __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingStepsKV* rk = nullptr) {
   __shared__ __attribute__((aligned(16))) bf16 QO0[2 * TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 QO1[2 * TILE_ELEMS];
@@ -1212,8 +1280,14 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
     const int kvh = h / grp;
     const int cnt = vloc_cnt[h];
     const int32_t* vl = vloc + (int64_t)h * a.KB * BLK;
-    const int64_t gb_min = global_block(a.kind, a.P, a.KB, src, vl[chunk * BLK] / BLK);
-    const int I_lo = max(seg * seg_len, blocks_upto(a.kind, a.P, a.QB, a.rank, gb_min - 1));
+    int I_first;   // the first query block with a row at or below the chunk's first column
+    if constexpr (S1) {
+      I_first = s1_first_qblock((int64_t)vl[chunk * BLK] * a.P + src, a.rank, a.P);
+    } else {
+      const int64_t gb_min = global_block(a.kind, a.P, a.KB, src, vl[chunk * BLK] / BLK);
+      I_first = blocks_upto(a.kind, a.P, a.QB, a.rank, gb_min - 1);
+    }
+    const int I_lo = max(seg * seg_len, I_first);
     const int I_hi = min(a.QB, (seg + 1) * seg_len);
     const int total = I_hi - I_lo;
     if (total <= 0) continue;
@@ -1227,7 +1301,7 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
       const int slot = chunk * BLK + 32 * kh + 16 * kt + n16;
       valid[kt] = slot < cnt;
       m[kt] = vl[valid[kt] ? slot : chunk * BLK];
-      gbk[kt] = global_block(a.kind, a.P, a.KB, src, m[kt] / BLK);
+      gbk[kt] = S1 ? (int64_t)m[kt] * a.P + src : global_block(a.kind, a.P, a.KB, src, m[kt] / BLK);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         kf[kt][ks] = *(const bf16x8*)((const bf16*)a.k + kvh * a.ksh + (srow0 + m[kt]) * a.ksn + 32 * ks + 8 * g4);
@@ -1244,15 +1318,20 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
       wait_all_mem();
       __syncthreads();
       if (it + 1 < total) stage_qblock(Qn, On, Ln, a, h, I_lo + it + 1, wave, lane, dlane);
-      const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I_lo + it);
       int thr[2];
+      if constexpr (S1) {   // gbk: the column's global position
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        // every causal row of the column, inside listed tiles too (the slash
-        // kernel leaves vertical columns out of its tiles)
-        const int64_t j = G - gbk[kt];
-        thr[kt] = BLK;
-        if (valid[kt] && j >= 0) thr[kt] = (j == 0) ? (m[kt] % BLK) : 0;
+        for (int kt = 0; kt < 2; ++kt) thr[kt] = valid[kt] ? s1_causal_row(gbk[kt], a.rank, a.P, I_lo + it) : BLK;
+      } else {
+        const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I_lo + it);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          // every causal row of the column, inside listed tiles too (the slash
+          // kernel leaves vertical columns out of its tiles)
+          const int64_t j = G - gbk[kt];
+          thr[kt] = BLK;
+          if (valid[kt] && j >= 0) thr[kt] = (j == 0) ? (m[kt] % BLK) : 0;
+        }
       }
       kv_block<F16, true>(Qs, Os, Ls, Ls + BLK, kf, vf, thr, rh, g4, n16, sl2, acc_dk, acc_dv);
     };
@@ -1269,6 +1348,12 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
 }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_bf16_d128_kernel(BwdArgs a) { dkdv_vert_d128<false>(a); }
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_f16_d128_kernel(BwdArgs a) { dkdv_vert_d128<true>(a); }
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_s1_bf16_d128_kernel(BwdArgs a) {
+  dkdv_vert_d128<false, false, true>(a);
+}
+__global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_s1_f16_d128_kernel(BwdArgs a) {
+  dkdv_vert_d128<true, false, true>(a);
+}
 __global__ void __launch_bounds__(BWD_THREADS, 1) dkdv_vert_ring_bf16_d128_kernel(BwdArgs a, RingStepsKV rk) {
   dkdv_vert_d128<false, true>(a, &rk);
 }
@@ -1408,14 +1493,21 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
       return VS_ERR_UNSUPPORTED;
     if (a.Hq / a.Hkv > 8) return VS_ERR_UNSUPPORTED;
     const dim3 qgrid(xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv)), kgrid(xcd_group_grid(a.Hkv, a.KB, KMAJOR_BPC, 1));
+    const bool s1 = m->lay.kind == VS_STRIPED1;
     if (parts & VS_BWD_DQ)
-      hipLaunchKernelGGL(f16 ? dq_f16_d128_kernel : dq_bf16_d128_kernel, qgrid, dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(s1 ? (f16 ? dq_s1_f16_d128_kernel : dq_s1_bf16_d128_kernel)
+                            : (f16 ? dq_f16_d128_kernel : dq_bf16_d128_kernel),
+                         qgrid, dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV)
-      hipLaunchKernelGGL(f16 ? dkdv_f16_d128_kernel : dkdv_bf16_d128_kernel, kgrid, dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(s1 ? (f16 ? dkdv_s1_f16_d128_kernel : dkdv_s1_bf16_d128_kernel)
+                            : (f16 ? dkdv_f16_d128_kernel : dkdv_bf16_d128_kernel),
+                         kgrid, dim3(BWD_THREADS), 0, stream, a);
     if (parts & VS_BWD_DKDV_VERT)
-      hipLaunchKernelGGL(f16 ? dkdv_vert_f16_d128_kernel : dkdv_vert_bf16_d128_kernel, dim3(VERT_GRID),
-                         dim3(BWD_THREADS), 0, stream, a);
+      hipLaunchKernelGGL(s1 ? (f16 ? dkdv_vert_s1_f16_d128_kernel : dkdv_vert_s1_bf16_d128_kernel)
+                            : (f16 ? dkdv_vert_f16_d128_kernel : dkdv_vert_bf16_d128_kernel),
+                         dim3(VERT_GRID), dim3(BWD_THREADS), 0, stream, a);
   }
+  else if (m->lay.kind == VS_STRIPED1) return VS_ERR_UNSUPPORTED;   // one-position stripes: D = 128 only
   else if (dtype == VS_BF16 && D == 64) launch_bwd_typed<bf16, 64>(a, parts, stream);
   else if (dtype == VS_F32 && D == 64) launch_bwd_typed<float, 64>(a, parts, stream);
   else return VS_ERR_UNSUPPORTED;

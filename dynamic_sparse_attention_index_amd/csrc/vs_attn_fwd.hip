@@ -300,7 +300,12 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 // RING: the tile sequence runs over several ring steps (RingTiles, `rs`):
 // K/V hold every shard in storage order and each tile's copy starts at its
 // step's shard; the online-softmax state carries across the steps.
-template <bool F16, int HP, bool RING = false>
+//
+// S1 (one-position stripes): a flagged tile's keys carry a causal threshold
+// and a window of diagonals, entry (a, b) active when a >= thr[b] and bit
+// qa(a) of win[b] is set; vertical chunks keep each column's causal rows on
+// unselected diagonals (the rest lies in listed tiles).
+template <bool F16, int HP, bool RING = false, bool S1 = false>
 __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps* rs = nullptr) {
   constexpr int D = TD;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE_ELEMS];
@@ -311,6 +316,7 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
   // descriptor and row thresholds of tile t live in slot t % 3 from the
   // descriptor copy (step t - 3) to the softmax (step t)
   __shared__ int thr_sh[3][BLK];
+  __shared__ uint32_t win_sh[S1 ? 3 : 1][BLK];
   __shared__ int desc_sh[3][BLK];
   __shared__ uint32_t sbits[MAX_LDS_W];
   // stages are chosen at compile time (the loop is unrolled by two) so the
@@ -395,23 +401,40 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
   const float sl2 = a.scale_log2;
 
   int mode_pend = 0;   // mode of the tile whose V copy was started last
+  int qa_l[2] = {0, 0};   // S1: global-block offset qa of this lane's two rows
+  if constexpr (S1) {
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) qa_l[rs] = ((32 * rh + 16 * rs + n16) * a.P + a.rank) >> 6;
+  }
 
   // start the K copy of tile t into K stage p and record its row thresholds
   auto issue_k = [&]<int p>(int t) {
     bf16* ks = Kst.template operator()<p>();
     const int* slot = desc_sh[t % 3];
     int thr = tid;
+    uint32_t win = ~0u;
     const char* kb = kbase + bt.row0(t, 1) * krb;   // the tile's shard
     if (!bt.vert(t, 1)) {
       int mode;
       const int r0 = bt.tile_row(slot, mode);
+      if constexpr (S1) {
+        if (tid < BLK) {
+          const int o = I - r0 / BLK;
+          win = s1_key_window(s1_tile_window(sbits, a.W, a.P, o), a.P, a.src, tid);
+          thr = s1_key_threshold(o, a.rank, a.src, tid);
+        }
+      }
       if (hs == 0) dma_tile_rows(ks, kb + (int64_t)r0 * krb, krb, dl, wave);
     } else {
       int rows[4];
-      bt.vert_rows(t, slot, rows, thr, wave, lane, tid, 1);
+      if constexpr (S1) bt.vert_rows_s1(t, slot, rows, thr, win, wave, lane, tid, I, a.rank, a.W);
+      else bt.vert_rows(t, slot, rows, thr, wave, lane, tid, 1);
       if (hs == 0) dma_tile_gather(ks, kb, rows, krb, dl, wave);
     }
-    if (tid < BLK) thr_sh[t % 3][tid] = thr;
+    if (tid < BLK) {
+      thr_sh[t % 3][tid] = thr;
+      if constexpr (S1) win_sh[t % 3][tid] = win;
+    }
   };
   // start the V copy of tile t into V stage p (descriptor read again)
   auto issue_v = [&]<int p>(int t) {
@@ -452,16 +475,23 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
   // O^T += V^T P^T from V stage p
   // S of the next tile (from K stage pk) is computed inside the branch-free
   // exponential section so its MFMAs interleave with the vector work.
-  auto softmax_pv = [&]<int p, int pk>(f32x4 (&s)[2][2], int mode, const int* thr, f32x4 (&s_next)[2][2]) {
+  auto softmax_pv = [&]<int p, int pk>(f32x4 (&s)[2][2], int mode, const int* thr, const uint32_t* win,
+                                        f32x4 (&s_next)[2][2]) {
     if (mode) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int th = thr[32 * kh + 8 * g4 + 4 * t + i];
+          const int key = 32 * kh + 8 * g4 + 4 * t + i;
+          const int th = thr[key];
+          uint32_t wk = ~0u;
+          if constexpr (S1) wk = win[key];
 #pragma unroll
-          for (int rs = 0; rs < 2; ++rs)
-            if (th > 32 * rh + 16 * rs + n16) s[rs][t][i] = -INFINITY;
+          for (int rs = 0; rs < 2; ++rs) {
+            bool off = th > 32 * rh + 16 * rs + n16;
+            if constexpr (S1) off = off || !((wk >> qa_l[rs]) & 1u);
+            if (off) s[rs][t][i] = -INFINITY;
+          }
         }
     }
     // P as a hi + lo bf16 pair (two MFMAs per product), or one fp16 operand
@@ -559,7 +589,7 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
     if (i + 3 < total) bt.desc_copy(i + 3, desc_sh[i % 3], wave8, lane);
     // (the last step computes a next S from a stale stage and drops it)
     f32x4 s_next[2][2];
-    softmax_pv.template operator()<p, q>(s_cur, mode_i, thr_sh[i % 3], s_next);
+    softmax_pv.template operator()<p, q>(s_cur, mode_i, thr_sh[i % 3], win_sh[S1 ? i % 3 : 0], s_next);
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
@@ -656,6 +686,12 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_ring_bf16_d128_kernel
 __global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_ring_f16_d128_kernel(FwdArgs a, RingSteps rs) {
   attn_fwd_d128<true, 1, true>(a, &rs);
 }
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_s1_bf16_d128_kernel(FwdArgs a) {
+  attn_fwd_d128<false, 1, false, true>(a);
+}
+__global__ void __launch_bounds__(FWD_THREADS, 2) attn_fwd_s1_f16_d128_kernel(FwdArgs a) {
+  attn_fwd_d128<true, 1, false, true>(a);
+}
 __global__ void __launch_bounds__(2 * FWD_THREADS, 1) attn_fwd_pair_bf16_d128_kernel(FwdArgs a) {
   attn_fwd_d128<false, 2>(a);
 }
@@ -678,9 +714,16 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
     const int64_t krows = (int64_t)m->KB * BLK;
     if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
-    if (dtype == VS_F16) hipLaunchKernelGGL(attn_fwd_f16_d128_kernel, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
+    const bool s1 = m->lay.kind == VS_STRIPED1;
+    if (dtype == VS_F16) {
+      if (s1) hipLaunchKernelGGL(attn_fwd_s1_f16_d128_kernel, grid, block, 0, stream, a);
+      else hipLaunchKernelGGL(attn_fwd_f16_d128_kernel, grid, block, 0, stream, a);
+    } else {
+      if (s1) hipLaunchKernelGGL(attn_fwd_s1_bf16_d128_kernel, grid, block, 0, stream, a);
+      else hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, grid, block, 0, stream, a);
+    }
   }
+  else if (m->lay.kind == VS_STRIPED1) return VS_ERR_UNSUPPORTED;   // one-position stripes: D = 128 only
   else if (dtype == VS_BF16 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == VS_F32 && D == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);
   else return VS_ERR_UNSUPPORTED;

@@ -142,6 +142,58 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int64_t 
   return lo;
 }
 
+// ---- one-position stripes (VS_STRIPED1) ---------------------------------------
+// Local position l of rank r is global position l P + r (P <= 32), so local
+// query block I spans global blocks I P .. I P + P - 1: row a of it lies in
+// global block I P + qa(a), qa(a) = (a P + r) >> 6, and key b of local block
+// J of shard s in J P + kb(b), kb(b) = (b P + s) >> 6. An entry of tile
+// (I, J) lies on global block-diagonal o P + qa - kb, o = I - J.
+
+// Bits lo .. lo + len - 1 (len <= 64) of a slash bitmap of W words; bits
+// outside the bitmap read as 0.
+__device__ __forceinline__ uint64_t sbit_window(const uint32_t* sb, int W, int64_t lo, int len) {
+  const int64_t w0 = lo >> 5;                 // floor(lo / 32), also for lo < 0
+  const int sh = (int)(lo - w0 * 32);
+  auto word = [&](int64_t i) -> uint64_t { return (i >= 0 && i < W) ? (uint64_t)sb[i] : 0ull; };
+  const uint64_t lo64 = word(w0) | (word(w0 + 1) << 32);
+  uint64_t x = lo64 >> sh;
+  if (sh) x |= word(w0 + 2) << (64 - sh);
+  return len >= 64 ? x : (x & ((1ull << len) - 1ull));
+}
+// The selected diagonals a tile at block offset o meets: bit i is diagonal
+// o P - P + 1 + i (i < 2P - 1; negative diagonals read 0).
+__device__ __forceinline__ uint64_t s1_tile_window(const uint32_t* sb, int W, int P, int o) {
+  return sbit_window(sb, W, (int64_t)o * P - P + 1, 2 * P - 1);
+}
+// Key b of such a tile: bit x of the result says whether rows with qa = x
+// lie on a selected diagonal (o P + x - kb(b) = o P - P + 1 + (x + P - 1 - kb)),
+// and rows below the returned threshold are above the causal edge (o = 0:
+// b P + s <= a P + r).
+__device__ __forceinline__ uint32_t s1_key_window(uint64_t tile_win, int P, int s, int b) {
+  const int kb = (b * P + s) >> 6;
+  return (uint32_t)(tile_win >> (P - 1 - kb));
+}
+__device__ __forceinline__ int s1_key_threshold(int o, int r, int s, int b) {
+  return o == 0 ? b + (s > r ? 1 : 0) : 0;
+}
+// First row of local query block I (rank r) at or below global column mg:
+// rows a >= the result have (64 I + a) P + r >= mg (BLK: none).
+__device__ __forceinline__ int s1_causal_row(int64_t mg, int r, int P, int I) {
+  const int64_t num = mg - r - (int64_t)BLK * I * P;
+  return num <= 0 ? 0 : (int)(num >= (int64_t)BLK * P ? BLK : (num + P - 1) / P);
+}
+// First local query block of rank r with a row at or below global column mg.
+__device__ __forceinline__ int s1_first_qblock(int64_t mg, int r, int P) {
+  const int64_t num = mg - r - (int64_t)(BLK - 1) * P;
+  return num <= 0 ? 0 : (int)((num + (int64_t)BLK * P - 1) / ((int64_t)BLK * P));
+}
+// A vertical column (global mg) in query block I: the rows it is active for
+// outside the listed tiles are its causal rows (threshold) whose diagonal
+// I P + qa - floor(mg / 64) is not selected (bit qa of the window).
+__device__ __forceinline__ uint32_t s1_vert_window(const uint32_t* sb, int W, int P, int I, int64_t mg) {
+  return ~(uint32_t)sbit_window(sb, W, (int64_t)I * P - (mg >> 6), P);
+}
+
 }  // namespace vs
 
 namespace vs {
@@ -366,6 +418,21 @@ struct BlockTiles {
       const int m = slot[tid];
       const int64_t j = G - global_block(kind, P, KB, src, m / BLK);
       if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
+    }
+  }
+  // The same under one-position stripes: key tid's causal threshold and the
+  // window of diagonals (bit qa) on which its rows are not already covered by
+  // a listed tile of query block I (rank `rank`); W words of sbits.
+  __device__ __forceinline__ void vert_rows_s1(int it, const int* slot, int* rows, int& thr, uint32_t& win, int wave,
+                                               int lane, int tid, int I, int rank, int W) const {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+    thr = BLK;
+    win = 0;
+    if (tid < BLK && it * BLK + tid < ve) {
+      const int64_t mg = (int64_t)slot[tid] * P + src;
+      thr = s1_causal_row(mg, rank, P, I);
+      win = s1_vert_window(sbits, W, P, I, mg);
     }
   }
   // The same calls as RingTiles (one visible shard at local row 0; the call

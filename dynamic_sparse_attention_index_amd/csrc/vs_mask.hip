@@ -146,19 +146,9 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
 // them causal). With o = 0 it meets 0 .. P - 1 causally (diagonal 0 partly:
 // b P + s <= a P + r); negative ones lie above the rows.
 
-// Bits lo .. lo + len - 1 (len <= 64) of a head's slash bitmap of W words;
-// bits outside the bitmap read as 0.
-__device__ __forceinline__ uint64_t sbit_window(const uint32_t* sb, int W, int64_t lo, int len) {
-  const int64_t w0 = lo >> 5;                 // floor(lo / 32), also for lo < 0
-  const int sh = (int)(lo - w0 * 32);
-  auto word = [&](int64_t i) -> uint64_t { return (i >= 0 && i < W) ? (uint64_t)sb[i] : 0ull; };
-  const uint64_t lo64 = word(w0) | (word(w0 + 1) << 32);
-  uint64_t x = lo64 >> sh;
-  if (sh) x |= word(w0 + 2) << (64 - sh);
-  return len >= 64 ? x : (x & ((1ull << len) - 1ull));
-}
-// Selected diagonals a stripe-1 tile at block offset o meets (bit i: diagonal
-// o P - P + 1 + i for o >= 1; diagonal i for o = 0).
+// Selected diagonals a stripe-1 tile at block offset o meets, as the mask
+// kernels read them (bit i: diagonal o P - P + 1 + i for o >= 1; diagonal i
+// for o = 0).
 __device__ __forceinline__ uint64_t s1_window(const uint32_t* sb, int W, int P, int o) {
   return o == 0 ? sbit_window(sb, W, 0, P) : sbit_window(sb, W, (int64_t)o * P - P + 1, 2 * P - 1);
 }

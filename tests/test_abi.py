@@ -101,6 +101,23 @@ def test_fwd_validation_before_device_work(L):
     assert L.vs_attn_fwd(q, k, k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_ARG
 
 
+def test_stripe1_attention_validation(L):
+    """One-position stripes run on the head-dim-128 bf16/fp16 kernels only; the
+    head-pair and resident-ring forms refuse the layout before device work."""
+    m, lay, _, _ = _mask(L, kind="striped1", P=4, N=1024)
+    m.rank = 0
+    m.src = 0
+    q64 = _fake_tensor(0x20000000, 4, 256, 64)
+    k64 = _fake_tensor(0x30000000, 2, 256, 64)
+    o, lse, st = ctypes.c_void_p(0x40000000), ctypes.c_void_p(0x50000000), ctypes.c_void_p(0x60000000)
+    assert L.vs_attn_fwd(q64, k64, k64, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_UNSUPPORTED
+    q = _fake_tensor(0x20000000, 4, 256, 128)
+    k = _fake_tensor(0x30000000, 2, 256, 128)
+    assert L.vs_attn_fwd_packed(q, k, k, ctypes.byref(m), 0.1, o, lse, 0, st, None) == vs.VS_ERR_UNSUPPORTED
+    k_all = _fake_tensor(0x30000000, 2, 1024, 128)
+    assert L.vs_attn_fwd_ring(q, k_all, k_all, ctypes.byref(m), 1, 0.1, o, lse, 0, None) == vs.VS_ERR_UNSUPPORTED
+
+
 def test_block_mask_and_index_validation(L):
     m, lay, _, _ = _mask(L, kind="striped", P=4, N=1024)
     p = ctypes.c_void_p(0x60000000)

@@ -94,6 +94,28 @@ def test_fwd_ring_merge(kind, P, comp):
     _fwd_case(cfg, vert, slash, kind, P, accumulate_steps=True, comp=comp)
 
 
+def _stripe1_index(rng, N, Hq, P):
+    """Random lists plus the cases one-position stripes single out: a head
+    whose diagonals 1 .. 3P + 1 are all selected (whole windows: full tiles)
+    and diagonal 0 is not, and a head without verticals."""
+    vert, slash = _index(rng, N, Hq, 100, 6)
+    run = min(N // 64, 3 * P + 2)
+    slash[1] = np.union1d(slash[1][slash[1] != 0], np.arange(1, run)).astype(np.int64)
+    vert[2] = np.zeros(0, dtype=np.int64)
+    return vert, slash
+
+
+@pytest.mark.parametrize("P,comp", [(2, "bf16"), (2, "f16"), (3, "f16"), (4, "bf16"), (8, "f16"), (32, "f16")])
+def test_fwd_stripe1(P, comp):
+    """One-position stripes: every (rank, step) of the ring, merged per rank,
+    against the oracle (per-entry predicate in partial tiles, vertical
+    columns outside the listed tiles' selected diagonals)."""
+    rng = np.random.default_rng(20 + P)
+    cfg = config_by_name("qwen32k", N=64 * P * (2 if P > 8 else 32 // P * 2), Hq=4, Hkv=2, n_out=4, c=2.0)
+    vert, slash = _stripe1_index(rng, cfg.N, cfg.Hq, P)
+    _fwd_case(cfg, vert, slash, "striped1", P, accumulate_steps=P % 2 == 0, comp=comp)
+
+
 def test_fwd_full_budget_is_dense_causal_sdpa():
     """All verticals and slashes selected -> dense causal attention (torch SDPA on the GPU, fp32)."""
     import dynamic_sparse_attention_index_amd as vs
@@ -188,6 +210,14 @@ def test_bwd_ring(kind, P, comp):
     cfg = config_by_name("qwen32k", N=64 * 16, Hq=2, Hkv=1, n_out=4, c=2.0)
     vert, slash = _index(rng, cfg.N, cfg.Hq, 60, 4)
     _bwd_case(cfg, vert, slash, kind, P, comp=comp)
+
+
+@pytest.mark.parametrize("P,comp", [(2, "bf16"), (4, "f16"), (8, "f16"), (8, "bf16")])
+def test_bwd_stripe1(P, comp):
+    rng = np.random.default_rng(40 + P)
+    cfg = config_by_name("qwen32k", N=64 * 16 if P <= 4 else 64 * 2 * P, Hq=4, Hkv=2, n_out=4, c=2.0)
+    vert, slash = _stripe1_index(rng, cfg.N, cfg.Hq, P)
+    _bwd_case(cfg, vert, slash, "striped1", P, comp=comp)
 
 
 def test_merge_kernel_matches_formula():
