@@ -495,10 +495,17 @@ def ring_report(args, cfg):
         else:
             aq, ak, av, ado = q, k, v, do
         # global index over the storage-order keys; the last rows are global
-        # rows N - last_q .. N - 1, wherever they are stored
+        # rows N - last_q .. N - 1, wherever they are stored. One-position
+        # stripes: the index takes the keys in global order (the lists are
+        # global either way), and the per-rank passes are not offered.
         last_rows = np.nonzero(np.isin(perm, np.arange(N - cfg.last_q, N)))[0]
         order = np.argsort(perm[last_rows])
         q_last = q[:, torch.tensor(last_rows[order], device=dev)].contiguous()
+        s1 = kind == "striped1"
+        idx_lay, k_idx = lay, k
+        if s1:
+            idx_lay = vs.layout("contig", 1, N)
+            k_idx = torch.tensor(host["k"]).to(dev, tdt)
         vert_s = torch.empty(Hq, N, device=dev)
         slash_s = torch.empty(Hq, T, device=dev)
         vidx = torch.empty(Hq, N, dtype=torch.int32, device=dev)
@@ -508,8 +515,8 @@ def ring_report(args, cfg):
         ws = torch.empty(vs.index_workspace_size(Hq, Hkv, N, D), dtype=torch.uint8, device=dev)
 
         def index():
-            vs.vs_index_build(q_last, k, lay, cfg.scale, cfg.top_p, vert_s, slash_s, vidx, vcnt, sidx, scnt, ws,
-                              stream)
+            vs.vs_index_build(q_last, k_idx, idx_lay, cfg.scale, cfg.top_p, vert_s, slash_s, vidx, vcnt, sidx, scnt,
+                              ws, stream)
         index()
         torch.cuda.synchronize()
         t_index = []
@@ -527,7 +534,9 @@ def ring_report(args, cfg):
         nl = N // P
         sws = torch.empty(vs.index_select_workspace_size(Hq, N), dtype=torch.uint8, device=dev)
         t_d1, t_d2, t_d3 = [], [], []
-        for rep in range(-1, args.ring_reps):
+        for rep in range(-1, 0 if s1 else args.ring_reps):
+            if s1:
+                break
             e1 = [timed(lambda: vs.vs_index_rank_stats(q_last, k[:, r * nl:(r + 1) * nl], lay, r, cfg.scale,
                                                        all_stats[r], ws, stream)) for r in range(P)]
             e2 = [timed(lambda: vs.vs_index_rank_mass(q_last, k[:, r * nl:(r + 1) * nl], lay, r, cfg.scale,
@@ -539,18 +548,20 @@ def ring_report(args, cfg):
                 t_d1.append(max(a.elapsed_time(b) for a, b in e1))
                 t_d2.append(max(a.elapsed_time(b) for a, b in e2))
                 t_d3.append(e3[0].elapsed_time(e3[1]))
-        same_sel = bool(torch.equal(vcnt_d, vcnt) and torch.equal(scnt_d, scnt))
+        same_sel = bool(torch.equal(vcnt_d, vcnt) and torch.equal(scnt_d, scnt)) if not s1 else None
         if same_sel:
             for h in range(Hq):
                 same_sel = same_sel and torch.equal(vidx_d[h, :int(vcnt[h])], vidx[h, :int(vcnt[h])]) and \
                     torch.equal(sidx_d[h, :int(scnt[h])], sidx[h, :int(scnt[h])])
-        score_rel = float(((vert_d - vert_s).abs() / vert_s.abs().clamp_min(1e-30)).max().item())
-        cap = Hq * QB * (int(scnt.max().item()) + 1)
+        score_rel = None if s1 else float(((vert_d - vert_s).abs() / vert_s.abs().clamp_min(1e-30)).max().item())
+        # tiles per query block: one per selected diagonal, two under one-position stripes
+        cap = Hq * QB * ((2 if s1 else 1) * int(scnt.max().item()) + 1)
         t_mask = np.zeros((args.ring_reps, P, P))
         t_fwd = np.zeros((args.ring_reps, P, P))
         t_bwd = np.zeros((args.ring_reps, P, P))
         t_prep = np.zeros((args.ring_reps, P))
         act = np.zeros((P, P), dtype=np.int64)
+        computed = np.zeros((P, P), dtype=np.int64)   # entries the forward computes (whole 64x64 tiles)
         o = torch.empty(Hq, QB * 64, D, device=dev)
         lse = torch.empty(Hq, QB * 64, device=dev)
         delta = torch.empty(Hq, QB * 64, device=dev)
@@ -614,6 +625,8 @@ def ring_report(args, cfg):
                         if int(arr["status"].item()) != 0:
                             raise RuntimeError(f"mask status {int(arr['status'].item())} at rank {r} step {st}")
                         act[r, st] = int(arr["n_active"].sum().item())
+                        chunks = int(((arr["vert_end"].long() + 63) // 64).sum().item())
+                        computed[r, st] = 4096 * (int(arr["tile_ptr"][-1].item()) + chunks)
                 del masks
         tm, tf, tb = (np.median(x, axis=0) for x in (t_mask, t_fwd, t_bwd))
         tp = np.median(t_prep, axis=0)                 # per rank, once per ring
@@ -632,11 +645,12 @@ def ring_report(args, cfg):
         # forward of all its steps in one launch (the online softmax carried
         # across the steps in the kernel: no per-step merge) and the backward
         # of all its steps in one call; k/v hold every shard in storage order
+        # (not offered under one-position stripes)
         res_masks = [vs.Mask(Hq, Hkv, lay, cap) for _ in range(P)]
         dk_res = torch.empty(Hkv, N, D, device=dev)
         dv_res = torch.empty(Hkv, N, D, device=dev)
         t_res = np.zeros((args.ring_reps, P, 4))      # mask, fwd, prep, bwd per rank
-        for rep in range(-1, args.ring_reps):
+        for rep in range(-1, -1 if s1 else args.ring_reps):
             for r in range(P):
                 rows = slice(r * QB * 64, (r + 1) * QB * 64)
                 qr, dor = aq[:, rows], ado[:, rows]
@@ -650,9 +664,11 @@ def ring_report(args, cfg):
                     for i, (a_, b_) in enumerate((e_m, e_f, e_p, e_b)):
                         t_res[rep, r, i] = a_.elapsed_time(b_)
         tr = np.median(t_res, axis=0)                 # [rank, part]
-        rank_ms = tr.sum(axis=1)
+        rank_ms = np.maximum(tr.sum(axis=1), 1e-9)
         res_ms = float(rank_ms.max())
         A_rank = act.sum(axis=1)
+        r3 = (lambda x: None) if s1 else (lambda x: round(x, 3))
+        r2 = (lambda x: None) if s1 else (lambda x: round(x, 2))
         del res_masks, dk_res, dv_res
         # merge: separate kernel vs fused into the forward, rank 0's steps
         o_step = torch.empty_like(o)
@@ -675,12 +691,12 @@ def ring_report(args, cfg):
         out["layouts"][kind] = {
             "index_ms": round(float(np.median(t_index)), 4),
             "convert_f16_ms_per_rank": round(float(np.median(t_conv)), 4) if t_conv else None,
-            "index_distributed_pass1_ms_max_rank": round(float(np.median(t_d1)), 4),
-            "index_distributed_pass2_ms_max_rank": round(float(np.median(t_d2)), 4),
-            "index_distributed_select_ms": round(float(np.median(t_d3)), 4),
-            "index_distributed_exchange_bytes": P * Hq * 64 * 2 * 4 + Hq * (N + T) * 4,
+            "index_distributed_pass1_ms_max_rank": round(float(np.median(t_d1)), 4) if t_d1 else None,
+            "index_distributed_pass2_ms_max_rank": round(float(np.median(t_d2)), 4) if t_d2 else None,
+            "index_distributed_select_ms": round(float(np.median(t_d3)), 4) if t_d3 else None,
+            "index_distributed_exchange_bytes": None if s1 else P * Hq * 64 * 2 * 4 + Hq * (N + T) * 4,
             "index_distributed_same_selection": same_sel,
-            "index_distributed_max_rel_score_diff": float(f"{score_rel:.3e}"),
+            "index_distributed_max_rel_score_diff": None if s1 else float(f"{score_rel:.3e}"),
             "mask_ms_per_step_mean": round(float(tm.mean()), 4),
             "fwd_ms_per_step_mean": round(float(tf.mean()), 4),
             "bwd_ms_per_step_mean": round(float(tb.mean()), 4),
@@ -697,18 +713,20 @@ def ring_report(args, cfg):
             "per_gpu_effective_tflops": round(14 * D * A_total / P / (ring_all_ms * 1e-3) / 1e12, 2),
             "per_gpu_effective_tflops_attention_only": round(14 * D * A_total / P / (ring_ms * 1e-3) / 1e12, 2),
             "active_entries": A_total,
+            "tile_fill_fwd": round(A_total / max(int(computed.sum()), 1), 4),
             "merge_fused_ms_per_step": round(float(np.mean(fused)), 4),
             "merge_separate_ms_per_step": round(float(np.mean(split)), 4),
-            "resident_ring_ms_max_rank": round(res_ms, 3),
-            "resident_parts_ms_max_rank": {k_: round(float(tr[int(np.argmax(rank_ms)), i]), 3)
-                                           for i, k_ in enumerate(("masks", "fwd", "bwd_prep", "bwd"))},
-            "resident_rank_imbalance": round(float(rank_ms.max() / rank_ms.mean()), 4),
-            "resident_per_gpu_tokens_per_s": round((N / P) / (res_ms * 1e-3), 1),
-            "resident_per_gpu_effective_tflops": round(14 * D * float(A_rank[int(np.argmax(rank_ms))]) /
-                                                       (res_ms * 1e-3) / 1e12, 2),
-            "resident_effective_tflops_mean_rank": round(float(np.mean(14 * D * A_rank / (rank_ms * 1e-3) / 1e12)), 2),
+            "resident_ring_ms_max_rank": r3(res_ms),
+            "resident_parts_ms_max_rank": None if s1 else
+            {k_: round(float(tr[int(np.argmax(rank_ms)), i]), 3)
+             for i, k_ in enumerate(("masks", "fwd", "bwd_prep", "bwd"))},
+            "resident_rank_imbalance": None if s1 else round(float(rank_ms.max() / rank_ms.mean()), 4),
+            "resident_per_gpu_tokens_per_s": None if s1 else round((N / P) / (res_ms * 1e-3), 1),
+            "resident_per_gpu_effective_tflops": r2(14 * D * float(A_rank[int(np.argmax(rank_ms))]) /
+                                                    (res_ms * 1e-3) / 1e12),
+            "resident_effective_tflops_mean_rank": r2(float(np.mean(14 * D * A_rank / (rank_ms * 1e-3) / 1e12))),
         }
-        del q, k, v, do, dk, dv, aq, ak, av, ado
+        del q, k, v, do, dk, dv, aq, ak, av, ado, k_idx
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
     if args.report_md:
@@ -726,11 +744,16 @@ def ring_report(args, cfg):
                     "forward launch over all its steps (vs_attn_fwd_ring: the online softmax carried across the "
                     "steps, O written once) and one backward call (vs_attn_bwd_ring: dQ accumulated across the "
                     "steps, the key-major parts over every step's shard in one grid); its time per rank is "
-                    "masks + forward + delta + backward.\n\n")
+                    "masks + forward + delta + backward. Under one-position stripes (`striped1`: rank r holds "
+                    "the positions n with n mod P = r) the index is built on the keys in global order, the "
+                    "per-rank index passes and the resident mode are not offered (empty cells), and "
+                    "`tile_fill_fwd` (active entries / entries of the listed tiles and vertical chunks the "
+                    "forward computes) shows how thin a selected diagonal becomes inside a local tile.\n\n")
             keys = list(next(iter(out["layouts"].values())).keys())
             f.write("| quantity | " + " | ".join(out["layouts"]) + " |\n|---|" + "---|" * len(out["layouts"]) + "\n")
             for kk in keys:
-                f.write(f"| {kk} | " + " | ".join(str(out["layouts"][L][kk]) for L in out["layouts"]) + " |\n")
+                f.write(f"| {kk} | " + " | ".join("—" if out["layouts"][L][kk] is None else str(out["layouts"][L][kk])
+                                                  for L in out["layouts"]) + " |\n")
 
 
 def stored_traffic(kernel):
