@@ -10,6 +10,7 @@ Entry points (same names and meaning as the C ABI):
     vs_attn_bwd_prep, vs_attn_bwd, vs_convert_f16
 plus helpers to size workspaces and hold a mask buffer (``Mask``).
 """
+import contextlib
 import ctypes
 import os
 
@@ -20,6 +21,9 @@ from . import _build
 # VS_ATTN_LIB names another build of the same library (the host-sanitizer
 # build of the ABI checks); by default the in-tree libvsattn.so is loaded.
 LIB_PATH = os.environ.get("VS_ATTN_LIB", _build.LIB)
+# The same library with bounds checks on every mask value the attention
+# kernels turn into an address (built beside it; see vs_debug_bounds_count).
+DEBUG_LIB_PATH = _build.DEBUG_LIB
 
 VS_OK, VS_ERR_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_CAPACITY, VS_ERR_HIP = 0, -1, -2, -3, -4, -5
 VS_ERR_RANGE = -6
@@ -34,7 +38,7 @@ EXPORTED = [
     "vs_block_mask", "vs_attn_fwd", "vs_merge_lse", "vs_attn_bwd_prep", "vs_attn_bwd", "vs_attn_bwd_parts",
     "vs_convert_f16", "vs_index_select_group_workspace_size", "vs_index_select_group", "vs_attn_fwd_packed",
     "vs_attn_bwd_prep_f16", "vs_index_build_noalloc", "vs_attn_fwd_ring", "vs_attn_bwd_ring",
-    "vs_block_mask_ring",
+    "vs_block_mask_ring", "vs_debug_bounds_enabled", "vs_debug_bounds_count",
 ]
 VS_BWD_DQ, VS_BWD_DKDV, VS_BWD_DKDV_VERT, VS_BWD_ALL, VS_BWD_OVERWRITE = 1, 2, 4, 7, 8
 
@@ -69,16 +73,38 @@ class VsError(RuntimeError):
 
 
 _lib = None
+_loaded = {}
 
 
 def lib():
     """Load libvsattn.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -c 'import __graft_entry__ as g; g.build()'`")
-        L = ctypes.CDLL(LIB_PATH)
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path):
+    """Route every entry point through another build of the library at `path`
+    (the bounds-checked debug build, DEBUG_LIB_PATH) inside the block."""
+    global _lib
+    prev = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _load(path):
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    if True:
+        L = ctypes.CDLL(path)
         vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         L.vs_status_string.restype = ctypes.c_char_p
         L.vs_status_string.argtypes = [i32]
@@ -135,8 +161,12 @@ def lib():
         L.vs_attn_bwd_parts.restype = i32
         L.vs_attn_bwd_parts.argtypes = [VsTensor, VsTensor, VsTensor, VsTensor, vp, vp, ctypes.POINTER(VsMask),
                                         f32, vp, vp, vp, i32, vp]
-        _lib = L
-    return _lib
+        L.vs_debug_bounds_enabled.restype = i32
+        L.vs_debug_bounds_enabled.argtypes = []
+        L.vs_debug_bounds_count.restype = i32
+        L.vs_debug_bounds_count.argtypes = [vp, i32, vp]
+    _loaded[path] = L
+    return L
 
 
 def status_string(code):
@@ -386,3 +416,15 @@ def vs_block_mask_ring(vert_idx, vert_cnt, slash_idx, slash_cnt, rank, masks, st
            "vs_block_mask_ring")
     for m, d in zip(masks, arr):     # the library set each descriptor's rank and visible shard
         m.desc = d
+
+
+def debug_bounds_enabled() -> bool:
+    return bool(lib().vs_debug_bounds_enabled())
+
+
+def debug_bounds_count(reset: bool = True, stream=None) -> int:
+    """Out-of-range mask values the attention kernels met since the last reset
+    (always 0 for the release build, which has no checks)."""
+    n = ctypes.c_int32(0)
+    _check(lib().vs_debug_bounds_count(ctypes.byref(n), 1 if reset else 0, _stream(stream)), "vs_debug_bounds_count")
+    return int(n.value)

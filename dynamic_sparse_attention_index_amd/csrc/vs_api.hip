@@ -170,6 +170,63 @@ int vs_index_build_noalloc(vs_tensor q_last, vs_tensor k, vs_layout lay, float s
                         slash_cnt, ws, (size_t)VS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+// ---- debug builds: bounds-violation counter ---------------------------------
+// The bounds-checked build (VS_DEBUG_BOUNDS) counts, in one word per GPU, every
+// mask value an attention kernel met outside the range its use allows (and
+// replaced by an in-range one). Looked up per device like the scratch array.
+}  // extern "C"
+
+#ifdef VS_DEBUG_BOUNDS
+static __device__ int32_t debug_count;
+namespace {
+int32_t* debug_ptr[MAX_DEVICES] = {};
+}  // namespace
+#endif
+
+namespace vs {
+int32_t* debug_word() {
+#ifdef VS_DEBUG_BOUNDS
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!debug_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(debug_count)) != hipSuccess || !p) return nullptr;
+    debug_ptr[dev] = (int32_t*)p;
+  }
+  return debug_ptr[dev];
+#else
+  return nullptr;
+#endif
+}
+}  // namespace vs
+
+extern "C" {
+
+int vs_debug_bounds_enabled(void) {
+#ifdef VS_DEBUG_BOUNDS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+int vs_debug_bounds_count(int32_t* count, int reset, void* stream) {
+  if (!count || (reset != 0 && reset != 1)) return VS_ERR_ARG;
+  *count = 0;
+#ifdef VS_DEBUG_BOUNDS
+  int32_t* w = debug_word();
+  if (!w) return VS_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(count, w, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return VS_ERR_HIP;
+  if (reset && hipMemsetAsync(w, 0, sizeof(int32_t), s) != hipSuccess) return VS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return VS_ERR_HIP;
+#else
+  (void)stream;
+#endif
+  return VS_OK;
+}
+
 // Checks shared by the per-rank index calls; on success sets the dims.
 static int check_rank_index(vs_tensor q_last, vs_tensor k_local, vs_layout lay, int rank, float scale, void* ws,
                             size_t ws_bytes, int* Hq, int* Hkv, int* D, int* last_q) {
@@ -434,7 +491,8 @@ static int check_ring(const vs_tensor& q, const vs_tensor& k, const vs_tensor& v
         !x.vert_end || !x.slash_bits)
       return VS_ERR_ARG;
     if (x.Hq != m.Hq || x.Hkv != m.Hkv || x.QB != m.QB || x.KB != m.KB || x.T != m.T || x.W != m.W ||
-        x.lay.kind != m.lay.kind || x.lay.P != P || x.lay.n_global != m.lay.n_global || x.rank != m.rank)
+        x.lay.kind != m.lay.kind || x.lay.P != P || x.lay.n_global != m.lay.n_global || x.rank != m.rank ||
+        x.tile_cap != m.tile_cap)
       return VS_ERR_ARG;
     if (x.src < 0 || x.src >= P) return VS_ERR_ARG;
     if (seen[x.src >> 6] & (1ull << (x.src & 63))) return VS_ERR_ARG;   // each shard once

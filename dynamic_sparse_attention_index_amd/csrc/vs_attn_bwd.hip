@@ -41,6 +41,8 @@ struct BwdArgs {
   int Hq, Hkv, QB, KB, W, kind, P, rank, src;
   float scale, scale_log2;
   int overwrite;   // dq and slash dk/dv written, not added (VS_BWD_OVERWRITE)
+  int32_t* dbg;    // debug builds: bounds-violation counter (null otherwise)
+  int64_t cap;     // capacity of tile_col / csc_row (debug-build checks)
 };
 
 // Zero 64 rows of D = TD floats at `rows` with a workgroup of BWD_THREADS
@@ -170,9 +172,9 @@ __global__ void __launch_bounds__(BWD_THREADS) dq_kernel(BwdArgs a) {
   const int64_t u = (int64_t)h * a.QB + I;
   const int rowoff = wave * 16 + n16;
   const int64_t grow = (int64_t)I * BLK + rowoff;
-  const int t0 = a.tile_ptr[u];
-  const int nt = a.tile_ptr[u + 1] - t0;
-  const int ve = a.vert_end[u];
+  const int t0 = dbg_clamp(a.tile_ptr[u], 0, (int)a.cap + 1, a.dbg);
+  const int nt = dbg_clamp(a.tile_ptr[u + 1] - t0, 0, min(a.KB, (int)a.cap - t0) + 1, a.dbg);
+  const int ve = dbg_clamp(a.vert_end[u], 0, a.KB * BLK + 1, a.dbg);
   const int total = nt + (ve + BLK - 1) / BLK;
   if (total == 0) return;
 
@@ -197,7 +199,7 @@ __global__ void __launch_bounds__(BWD_THREADS) dq_kernel(BwdArgs a) {
     int mode;
     if (it < nt) {
       const int e = a.tile_col[t0 + it];
-      const int J = e & VS_TILE_MASK;
+      const int J = dbg_clamp(e & VS_TILE_MASK, 0, a.KB, a.dbg);
       mode = (e & VS_TILE_DIAG) ? 1 : 0;
       #pragma unroll
       for (int c = 0; c < CPT; ++c) rows[c] = J * BLK + (tid + c * BWD_THREADS) / CPR;
@@ -208,13 +210,13 @@ __global__ void __launch_bounds__(BWD_THREADS) dq_kernel(BwdArgs a) {
       #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = base + (tid + c * BWD_THREADS) / CPR;
-        rows[c] = idx < ve ? vl[idx] : vl[base];
+        rows[c] = dbg_clamp(idx < ve ? vl[idx] : vl[base], 0, a.KB * BLK, a.dbg);
       }
       if (tid < BLK) {
         const int idx = base + tid;
         int thr = BLK;
         if (idx < ve) {
-          const int m = vl[idx];
+          const int m = dbg_clamp(vl[idx], 0, a.KB * BLK, a.dbg);
           const int64_t j = G - global_block(a.kind, a.P, a.KB, a.src, m / BLK);
           if (!((sb[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
         }
@@ -318,10 +320,11 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_kernel(BwdArgs a) {
   for (int hh = 0; hh < grp; ++hh) {
     const int h = kvh * grp + hh;
     const int64_t cu = (int64_t)h * a.KB + J;
-    const int c0 = a.csc_ptr[cu], c1 = a.csc_ptr[cu + 1];
+    const int c0 = dbg_clamp(a.csc_ptr[cu], 0, (int)a.cap + 1, a.dbg);
+    const int c1 = c0 + dbg_clamp(a.csc_ptr[cu + 1] - c0, 0, min(a.QB, (int)a.cap - c0) + 1, a.dbg);
     for (int e = c0; e < c1; ++e) {
       const int ent = a.csc_row[e];
-      const int I = ent & VS_TILE_MASK;
+      const int I = dbg_clamp(ent & VS_TILE_MASK, 0, a.QB, a.dbg);
       stage_query_block<T, D>(Qs, dOs, lse_sh, dl_sh, a, h, I, tid);
       __syncthreads();
       // diagonal tile: key k is active for rows >= k
@@ -362,15 +365,16 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, n16 = lane & 15;
   const int nseg = (a.QB + VERT_SEG - 1) / VERT_SEG;
+  auto vcnt = [&](int h) { return dbg_clamp(a.vloc_cnt[h], 0, a.KB * BLK + 1, a.dbg); };
   int64_t total = 0;
-  for (int h = 0; h < a.Hq; ++h) total += (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+  for (int h = 0; h < a.Hq; ++h) total += (int64_t)((vcnt(h) + BLK - 1) / BLK) * nseg;
   const int grp = a.Hq / a.Hkv;
   for (int64_t w = blockIdx.x; w < total; w += gridDim.x) {
     // decode (h, chunk, seg)
     int64_t r = w;
     int h = 0;
     for (; h < a.Hq; ++h) {
-      const int64_t n = (int64_t)((a.vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+      const int64_t n = (int64_t)((vcnt(h) + BLK - 1) / BLK) * nseg;
       if (r < n) break;
       r -= n;
     }
@@ -379,12 +383,12 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
     // chunk's last (always full) segment
     const int chunk = (int)(r / nseg), seg = (int)((r % nseg + chunk) % nseg);
     const int kvh = h / grp;
-    const int cnt = a.vloc_cnt[h];
+    const int cnt = vcnt(h);
     const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
     const uint32_t* sb = a.slash_bits + (int64_t)h * a.W;
     const int slot = chunk * BLK + wave * 16 + n16;
     const bool valid = slot < cnt;
-    const int m = vl[valid ? slot : chunk * BLK];
+    const int m = dbg_clamp(vl[valid ? slot : chunk * BLK], 0, a.KB * BLK, a.dbg);
     const int64_t gb = global_block(a.kind, a.P, a.KB, a.src, m / BLK);
     typename Tl::Frag kf[NK], vf[NK];
     load_row_frag<T, D>((const T*)a.k + kvh * a.ksh + (int64_t)m * a.ksn, g4, kf);
@@ -470,15 +474,15 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
     __shared__ RingTable rtab;
     bt.rs = rs; bt.tb = &rtab; bt.sbits = sbits; bt.vl_off = (int64_t)h * a.KB * BLK;
     bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
-    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB;
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.dbg = a.dbg;
     bt.fill(u, wave, lane);
     __syncthreads();
     bt.start();
   } else {
     bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h * a.KB * BLK; bt.sbits = sbits;
-    bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
     bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
-    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src; bt.dbg = a.dbg; bt.cap = a.cap;
+    bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
   }
   const int total = bt.total;
   if (total == 0) {
@@ -974,8 +978,8 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
   int cst_l = 0, cnt_l = 0;
   if (lane < grp) {
     const int64_t cu = (int64_t)(kvh * grp + lane) * a.KB + J;
-    cst_l = a.csc_ptr[cu];
-    cnt_l = a.csc_ptr[cu + 1] - cst_l;
+    cst_l = dbg_clamp(a.csc_ptr[cu], 0, (int)a.cap + 1, a.dbg);
+    cnt_l = dbg_clamp(a.csc_ptr[cu + 1] - cst_l, 0, min(a.QB, (int)a.cap - cst_l) + 1, a.dbg);
   }
   int total = 0;
   for (int hh = 0; hh < grp; ++hh) total += __builtin_amdgcn_readlane(cnt_l, hh);
@@ -988,7 +992,9 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
     const int64_t hq = kvh * grp + lane;
     const int32_t* vc = a.vcum + hq * (a.KB + 1);
     const int32_t* vl = a.vloc + hq * a.KB * BLK;
-    for (int e = vc[J]; e < vc[J + 1]; ++e) {
+    const int e0 = dbg_clamp(vc[J], 0, a.KB * BLK + 1, a.dbg);
+    const int e1 = e0 + dbg_clamp(vc[J + 1] - e0, 0, a.KB * BLK - e0 + 1, a.dbg);
+    for (int e = e0; e < e1; ++e) {
       const int b = vl[e] & (BLK - 1);
       if (b < 32) vm_lo_l |= 1u << b;
       else vm_hi_l |= 1u << (b - 32);
@@ -1037,7 +1043,7 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
   auto issue = [&]<int p>(int t) -> int {
     const int e = __builtin_amdgcn_readfirstlane(desc_sh[t % 3][0]);
     const int hh = __builtin_amdgcn_readfirstlane(head_sh[t % 3]);
-    const int I = e & VS_TILE_MASK;
+    const int I = dbg_clamp(e & VS_TILE_MASK, 0, a.QB, a.dbg);
     bf16* qo = QOst.template operator()<p>();
     float* ls = Lst.template operator()<p>();
     const int64_t r0 = (int64_t)I * BLK;
@@ -1238,7 +1244,7 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
   };
   if (tid < nst) {
     int c = 0;
-    for (int h = 0; h < a.Hq; ++h) c += (vcnt_of(tid)[h] + BLK - 1) / BLK;
+    for (int h = 0; h < a.Hq; ++h) c += (dbg_clamp(vcnt_of(tid)[h], 0, a.KB * BLK + 1, a.dbg) + BLK - 1) / BLK;
     step_chunks[tid] = c;
   }
   __syncthreads();
@@ -1267,9 +1273,10 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
       src = rk->src[st];
     }
     const int64_t srow0 = RING ? (int64_t)src * a.KB * BLK : 0;
+    auto vcnt = [&](int hq) { return dbg_clamp(vloc_cnt[hq], 0, a.KB * BLK + 1, a.dbg); };
     int h = 0;
     for (; h < a.Hq; ++h) {
-      const int64_t n = (int64_t)((vloc_cnt[h] + BLK - 1) / BLK) * nseg;
+      const int64_t n = (int64_t)((vcnt(h) + BLK - 1) / BLK) * nseg;
       if (r < n) break;
       r -= n;
     }
@@ -1278,13 +1285,13 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
     // chunk's last (always full) segment
     const int chunk = (int)(r / nseg), seg = (int)((r % nseg + chunk) % nseg);
     const int kvh = h / grp;
-    const int cnt = vloc_cnt[h];
+    const int cnt = vcnt(h);
     const int32_t* vl = vloc + (int64_t)h * a.KB * BLK;
     int I_first;   // the first query block with a row at or below the chunk's first column
     if constexpr (S1) {
-      I_first = s1_first_qblock((int64_t)vl[chunk * BLK] * a.P + src, a.rank, a.P);
+      I_first = s1_first_qblock((int64_t)dbg_clamp(vl[chunk * BLK], 0, a.KB * BLK, a.dbg) * a.P + src, a.rank, a.P);
     } else {
-      const int64_t gb_min = global_block(a.kind, a.P, a.KB, src, vl[chunk * BLK] / BLK);
+      const int64_t gb_min = global_block(a.kind, a.P, a.KB, src, dbg_clamp(vl[chunk * BLK], 0, a.KB * BLK, a.dbg) / BLK);
       I_first = blocks_upto(a.kind, a.P, a.QB, a.rank, gb_min - 1);
     }
     const int I_lo = max(seg * seg_len, I_first);
@@ -1300,7 +1307,7 @@ __device__ __forceinline__ void dkdv_vert_d128(const BwdArgs& a, const RingSteps
     for (int kt = 0; kt < 2; ++kt) {
       const int slot = chunk * BLK + 32 * kh + 16 * kt + n16;
       valid[kt] = slot < cnt;
-      m[kt] = vl[valid[kt] ? slot : chunk * BLK];
+      m[kt] = dbg_clamp(vl[valid[kt] ? slot : chunk * BLK], 0, a.KB * BLK, a.dbg);
       gbk[kt] = S1 ? (int64_t)m[kt] * a.P + src : global_block(a.kind, a.P, a.KB, src, m[kt] / BLK);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -1482,6 +1489,7 @@ int launch_attn_bwd(int dtype, int D, TView q, TView k, TView v, TView dout, con
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src;
   a.scale = scale; a.scale_log2 = scale * LOG2E;
+  a.dbg = debug_word(); a.cap = m->tile_cap;
   a.overwrite = 0;
   if ((dtype == VS_BF16 || dtype == VS_F16) && D == 128) {
     const bool f16 = dtype == VS_F16;
@@ -1542,6 +1550,7 @@ int launch_attn_bwd_ring(int dtype, TView q, TView k, TView v, TView dout, const
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = -1;
   a.scale = scale; a.scale_log2 = scale * LOG2E;
+  a.dbg = debug_word(); a.cap = m->tile_cap;
   const bool f16 = dtype == VS_F16;
   const unsigned qgrid = xcd_group_grid(a.Hkv, a.QB, QMAJOR_BPC, a.Hq / a.Hkv);
   const unsigned kgrid = xcd_group_grid(a.Hkv, a.KB, KMAJOR_BPC, 1);
@@ -1550,6 +1559,7 @@ int launch_attn_bwd_ring(int dtype, TView q, TView k, TView v, TView dout, const
     RingSteps rs{};
     RingStepsKV rk{};
     rs.nsteps = rk.nsteps = ns;
+    rs.cap = m->tile_cap;
     for (int s = 0; s < ns; ++s) {
       const vs_mask& x = ms[s0 + s];
       rs.tile_ptr[s] = x.tile_ptr; rs.tile_col[s] = x.tile_col; rs.vloc[s] = x.vloc; rs.vert_end[s] = x.vert_end;

@@ -35,6 +35,8 @@ struct FwdArgs {
   int32_t* status;   // head-pair kernel: written VS_ERR_ARG if a pair's active sets differ
   int Hq, Hkv, QB, KB, W, kind, P, rank, src, accumulate;
   float scale_log2;
+  int32_t* dbg;      // debug builds: bounds-violation counter (null otherwise)
+  int64_t cap;       // capacity of tile_col (debug-build checks)
 };
 
 // Physical key (0..63) held by S^T output value i of 16-key subtile t in lane
@@ -88,9 +90,9 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
     for (int ks = 0; ks < NQ; ++ks) qf[ks] = qrow[4 * ks + g4];
   }
 
-  const int t0 = a.tile_ptr[u];
-  const int nt = a.tile_ptr[u + 1] - t0;
-  const int ve = a.vert_end[u];
+  const int t0 = dbg_clamp(a.tile_ptr[u], 0, (int)a.cap + 1, a.dbg);
+  const int nt = dbg_clamp(a.tile_ptr[u + 1] - t0, 0, min(a.KB, (int)a.cap - t0) + 1, a.dbg);
+  const int ve = dbg_clamp(a.vert_end[u], 0, a.KB * BLK + 1, a.dbg);
   const int total = nt + (ve + BLK - 1) / BLK;
   const int64_t G = global_block(a.kind, a.P, a.QB, a.rank, I);
   const int32_t* vl = a.vloc + (int64_t)h * a.KB * BLK;
@@ -109,7 +111,7 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
     int src_rows[CPT];
     if (it < nt) {
       const int e = a.tile_col[t0 + it];
-      const int J = e & VS_TILE_MASK;
+      const int J = dbg_clamp(e & VS_TILE_MASK, 0, a.KB, a.dbg);
       mode_next = (e & VS_TILE_DIAG) ? 1 : 0;
       #pragma unroll
       for (int c = 0; c < CPT; ++c) src_rows[c] = J * BLK + (tid + c * FWD_THREADS) / CPR;
@@ -121,13 +123,13 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
       for (int c = 0; c < CPT; ++c) {
         const int slot = (tid + c * FWD_THREADS) / CPR;
         const int idx = base + slot;
-        src_rows[c] = idx < ve ? vl[idx] : vl[base];
+        src_rows[c] = dbg_clamp(idx < ve ? vl[idx] : vl[base], 0, a.KB * BLK, a.dbg);
       }
       if (tid < BLK) {
         const int idx = base + tid;
         int thr = BLK;  // never active
         if (idx < ve) {
-          const int m = vl[idx];
+          const int m = dbg_clamp(vl[idx], 0, a.KB * BLK, a.dbg);
           const int64_t gb = global_block(a.kind, a.P, a.KB, a.src, m / BLK);
           const int64_t j = G - gb;
           const bool covered = (sb[j >> 5] >> (j & 31)) & 1u;
@@ -346,8 +348,12 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
   const int64_t row_base = (int64_t)I * BLK + 32 * rh;   // this wave's first query row
   if constexpr (HP == 2) {
     const int64_t u1 = u + a.QB;
-    const int t0 = a.tile_ptr[u], nt0 = a.tile_ptr[u + 1] - t0, ve0 = a.vert_end[u];
-    const int t1 = a.tile_ptr[u1], nt1 = a.tile_ptr[u1 + 1] - t1, ve1 = a.vert_end[u1];
+    const int t0 = dbg_clamp(a.tile_ptr[u], 0, (int)a.cap + 1, a.dbg);
+    const int nt0 = dbg_clamp(a.tile_ptr[u + 1] - t0, 0, min(a.KB, (int)a.cap - t0) + 1, a.dbg);
+    const int ve0 = dbg_clamp(a.vert_end[u], 0, a.KB * BLK + 1, a.dbg);
+    const int t1 = dbg_clamp(a.tile_ptr[u1], 0, (int)a.cap + 1, a.dbg);
+    const int nt1 = dbg_clamp(a.tile_ptr[u1 + 1] - t1, 0, min(a.KB, (int)a.cap - t1) + 1, a.dbg);
+    const int ve1 = dbg_clamp(a.vert_end[u1], 0, a.KB * BLK + 1, a.dbg);
     int mism = (nt0 != nt1 || ve0 != ve1) ? 1 : 0;
     if (!mism) {
       for (int i = tid; i < nt0; i += HP * FWD_THREADS) mism |= a.tile_col[t0 + i] != a.tile_col[t1 + i];
@@ -371,15 +377,15 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
     __shared__ RingTable rtab;
     bt.rs = rs; bt.tb = &rtab; bt.sbits = sbits; bt.vl_off = (int64_t)h0 * a.KB * BLK;
     bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
-    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB;
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.dbg = a.dbg;
     bt.fill(u, wave8, lane);
     __syncthreads();
     bt.start();
   } else {
     bt.tile_col = a.tile_col; bt.vl = a.vloc + (int64_t)h0 * a.KB * BLK; bt.sbits = sbits;
-    bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
     bt.G = global_block(a.kind, a.P, a.QB, a.rank, I);
-    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src;
+    bt.kind = a.kind; bt.P = a.P; bt.KB = a.KB; bt.src = a.src; bt.dbg = a.dbg; bt.cap = a.cap;
+    bt.init(a.tile_ptr[u], a.tile_ptr[u + 1], a.vert_end[u]);
   }
   const int total = bt.total;
   const uint32_t* sbg = a.slash_bits + (int64_t)h0 * a.W;
@@ -709,6 +715,7 @@ int launch_attn_fwd(int dtype, int D, TView q, TView k, TView v, const vs_mask* 
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
+  a.dbg = debug_word(); a.cap = m->tile_cap;
   const dim3 grid(xcd_group_grid(m->Hkv, m->QB, QMAJOR_BPC, m->Hq / m->Hkv)), block(FWD_THREADS);
   if ((dtype == VS_BF16 || dtype == VS_F16) && D == 128) {
     if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
@@ -742,6 +749,7 @@ int launch_attn_fwd_packed(int dtype, TView q, TView k, TView v, const vs_mask* 
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = m->src; a.accumulate = accumulate;
   a.scale_log2 = scale * LOG2E;
+  a.dbg = debug_word(); a.cap = m->tile_cap;
   if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
   const int64_t krows = (int64_t)m->KB * BLK;
   if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
@@ -766,6 +774,7 @@ int launch_attn_fwd_ring(int dtype, TView q, TView k, TView v, const vs_mask* ms
   a.Hq = m->Hq; a.Hkv = m->Hkv; a.QB = m->QB; a.KB = m->KB; a.W = m->W; a.kind = m->lay.kind;
   a.P = m->lay.P; a.rank = m->rank; a.src = -1;
   a.scale_log2 = scale * LOG2E;
+  a.dbg = debug_word(); a.cap = m->tile_cap;
   if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
   const int64_t krows = (int64_t)m->KB * BLK;   // 32-bit copy offsets within one shard
   if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
@@ -773,6 +782,7 @@ int launch_attn_fwd_ring(int dtype, TView q, TView k, TView v, const vs_mask* ms
   for (int s0 = 0; s0 < nsteps; s0 += MAX_RING_STEPS) {
     RingSteps rs{};
     rs.nsteps = nsteps - s0 < MAX_RING_STEPS ? nsteps - s0 : MAX_RING_STEPS;
+    rs.cap = m->tile_cap;
     for (int s = 0; s < rs.nsteps; ++s) {
       const vs_mask& ms_s = ms[s0 + s];
       rs.tile_ptr[s] = ms_s.tile_ptr; rs.tile_col[s] = ms_s.tile_col; rs.vloc[s] = ms_s.vloc;

@@ -133,6 +133,20 @@ __device__ __forceinline__ int blocks_upto(int kind, int P, int NB, int rank, in
   return lo;
 }
 
+// Debug builds (VS_DEBUG_BOUNDS): a value read from a mask that becomes part
+// of an address must lie in [lo, hi); one that does not is counted in *dbg
+// and replaced by lo, so the kernel still touches only valid memory and
+// finishes. Release builds return v unchecked.
+__device__ __forceinline__ int dbg_clamp(int v, int lo, int hi, int32_t* dbg) {
+#ifdef VS_DEBUG_BOUNDS
+  if (v < lo || v >= hi) {
+    if (dbg) atomicAdd(dbg, 1);
+    return lo;
+  }
+#endif
+  return v;
+}
+
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int64_t x) {
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -379,6 +393,8 @@ struct BlockTiles {
   int t0, nt, ve, nvc, total;
   int64_t G;                  // global block of the query block
   int kind, P, KB, src;
+  int32_t* dbg = nullptr;     // debug builds: bounds-violation counter
+  int64_t cap = 0;            // debug builds: capacity of tile_col
 
   // Tile order: the nvc vertical chunks first, then the listed tiles from the
   // query block's own diagonal outwards (the list holds them far to near).
@@ -387,6 +403,11 @@ struct BlockTiles {
   // tiles and the O rescale is rarely needed afterwards.
   __device__ __forceinline__ void init(int t0_, int t1_, int ve_) {
     t0 = t0_; nt = t1_ - t0_; ve = ve_;
+#ifdef VS_DEBUG_BOUNDS
+    t0 = dbg_clamp(t0, 0, (int)cap + 1, dbg);
+    nt = dbg_clamp(nt, 0, min(KB, (int)cap - t0) + 1, dbg);
+    ve = dbg_clamp(ve, 0, KB * BLK + 1, dbg);
+#endif
     nvc = (ve + BLK - 1) / BLK;
     total = nt + nvc;
   }
@@ -404,7 +425,7 @@ struct BlockTiles {
   __device__ __forceinline__ int tile_row(const int* slot, int& mode) const {
     const int e = __builtin_amdgcn_readfirstlane(slot[0]);
     mode = (e & VS_TILE_DIAG) ? 1 : 0;
-    return (e & VS_TILE_MASK) * BLK;
+    return dbg_clamp(e & VS_TILE_MASK, 0, KB, dbg) * BLK;
   }
   // Vertical chunk `it`: the key rows of this lane's copy pieces and, for
   // tid < BLK, the key's row threshold (rows below it are inactive: the causal
@@ -412,10 +433,10 @@ struct BlockTiles {
   __device__ __forceinline__ void vert_rows(int it, const int* slot, int* rows, int& thr, int wave, int lane,
                                             int tid) const {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+    for (int c = 0; c < 4; ++c) rows[c] = dbg_clamp(slot[dma_local_row(wave, c, lane)], 0, KB * BLK, dbg);
     thr = BLK;
     if (tid < BLK && it * BLK + tid < ve) {
-      const int m = slot[tid];
+      const int m = dbg_clamp(slot[tid], 0, KB * BLK, dbg);
       const int64_t j = G - global_block(kind, P, KB, src, m / BLK);
       if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
     }
@@ -426,11 +447,11 @@ struct BlockTiles {
   __device__ __forceinline__ void vert_rows_s1(int it, const int* slot, int* rows, int& thr, uint32_t& win, int wave,
                                                int lane, int tid, int I, int rank, int W) const {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+    for (int c = 0; c < 4; ++c) rows[c] = dbg_clamp(slot[dma_local_row(wave, c, lane)], 0, KB * BLK, dbg);
     thr = BLK;
     win = 0;
     if (tid < BLK && it * BLK + tid < ve) {
-      const int64_t mg = (int64_t)slot[tid] * P + src;
+      const int64_t mg = (int64_t)dbg_clamp(slot[tid], 0, KB * BLK, dbg) * P + src;
       thr = s1_causal_row(mg, rank, P, I);
       win = s1_vert_window(sbits, W, P, I, mg);
     }
@@ -462,6 +483,7 @@ struct RingSteps {
   const int32_t* vert_end[MAX_RING_STEPS];
   int32_t src[MAX_RING_STEPS];
   int32_t nsteps;
+  int64_t cap;   // capacity of every step's tile_col (debug-build checks)
 };
 
 // Per-step arrays of the key-major gradient parts (kernel argument): one
@@ -498,6 +520,7 @@ struct RingTiles {
   int64_t G;                  // global block of the query block
   int kind, P, KB, total;
   int cur[3];
+  int32_t* dbg = nullptr;     // debug builds: bounds-violation counter
 
   // Wave 0 fills the table of list row u (= h * QB + I); the caller
   // synchronises the workgroup before start().
@@ -506,8 +529,13 @@ struct RingTiles {
     const int n = rs->nsteps;
     int tot = 0;
     if (lane < n) {
-      const int a0 = rs->tile_ptr[lane][u], a1 = rs->tile_ptr[lane][u + 1];
-      const int ve = rs->vert_end[lane][u];
+      int a0 = rs->tile_ptr[lane][u], a1 = rs->tile_ptr[lane][u + 1];
+      int ve = rs->vert_end[lane][u];
+#ifdef VS_DEBUG_BOUNDS
+      a0 = dbg_clamp(a0, 0, (int)rs->cap + 1, dbg);
+      a1 = a0 + dbg_clamp(a1 - a0, 0, min(KB, (int)rs->cap - a0) + 1, dbg);
+      ve = dbg_clamp(ve, 0, KB * BLK + 1, dbg);
+#endif
       tb->t0[lane] = a0;
       tb->nt[lane] = a1 - a0;
       tb->ve[lane] = ve;
@@ -550,17 +578,17 @@ struct RingTiles {
   __device__ __forceinline__ int tile_row(const int* slot, int& mode) const {
     const int e = __builtin_amdgcn_readfirstlane(slot[0]);
     mode = (e & VS_TILE_DIAG) ? 1 : 0;
-    return (e & VS_TILE_MASK) * BLK;
+    return dbg_clamp(e & VS_TILE_MASK, 0, KB, dbg) * BLK;
   }
   __device__ __forceinline__ void vert_rows(int t, const int* slot, int* rows, int& thr, int wave, int lane, int tid,
                                             int c) {
     const int s = step_of(t, c);
     const int it = t - rfl(tb->cum[s]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) rows[k] = slot[dma_local_row(wave, k, lane)];
+    for (int k = 0; k < 4; ++k) rows[k] = dbg_clamp(slot[dma_local_row(wave, k, lane)], 0, KB * BLK, dbg);
     thr = BLK;
     if (tid < BLK && it * BLK + tid < rfl(tb->ve[s])) {
-      const int m = slot[tid];
+      const int m = dbg_clamp(slot[tid], 0, KB * BLK, dbg);
       const int64_t j = G - global_block(kind, P, KB, rs->src[s], m / BLK);
       if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
     }

@@ -8,6 +8,10 @@
 
 namespace vs {
 
+// Device address of the debug build's bounds-violation counter on the current
+// device (looked up once per device); null in the release build.
+int32_t* debug_word();
+
 // A device view of a [H, N, D] tensor as the kernels use it.
 struct TView {
   const void* ptr;

@@ -462,6 +462,22 @@ int vs_attn_bwd_ring(vs_tensor q, vs_tensor k_all, vs_tensor v_all, vs_tensor do
                      const float* delta, const vs_mask* masks, int nsteps, float scale, float* dq, float* dk_all,
                      float* dv_all, int parts, void* stream);
 
+/* ---- bounds-checked debug build --------------------------------------------
+ * The library also builds as libvsattn_debug.so (macro VS_DEBUG_BOUNDS): there
+ * every value an attention kernel reads from a mask and turns into an address
+ * (list ranges, tile and query-block numbers, vertical column positions) is
+ * checked against the range its use allows; a value outside it is counted in
+ * a per-GPU word and replaced by an in-range one, so a corrupted mask gives a
+ * count instead of an out-of-bounds access. The release build has no checks.
+ *
+ * vs_debug_bounds_enabled: 1 in the debug build, 0 in the release build.
+ * vs_debug_bounds_count: after the work queued on `stream` so far, *count
+ *   (host) receives the number of violations counted on the current GPU since
+ *   the last reset (release build: always 0, no device work); reset = 1 clears
+ *   the word. Synchronises `stream`. VS_ERR_ARG on a null count. */
+int vs_debug_bounds_enabled(void);
+int vs_debug_bounds_count(int32_t* count, int reset, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,23 @@ def test_header_symbols_exported(L):
         assert hasattr(L, n), n
 
 
+def test_debug_build_exports_and_reports(L):
+    """The bounds-checked build exports the same symbols and says so; the
+    release build reports no checks and no count without touching a device."""
+    assert L.vs_debug_bounds_enabled() == 0
+    n = ctypes.c_int32(7)
+    assert L.vs_debug_bounds_count(ctypes.byref(n), 1, None) == 0 and n.value == 0
+    assert L.vs_debug_bounds_count(None, 0, None) == vs.VS_ERR_ARG
+    if not os.path.exists(vs.DEBUG_LIB_PATH):
+        pytest.skip("debug library not built")
+    with vs.use_library(vs.DEBUG_LIB_PATH) as D:
+        for name in _declared():
+            assert hasattr(D, name), name
+        assert D.vs_debug_bounds_enabled() == 1
+        assert vs.lib() is D
+    assert vs.lib() is L
+
+
 def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert vs.status_string(code) and vs.status_string(code) != "unknown status"
