@@ -617,18 +617,20 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
       weights8<F16, true>(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
     }
     // dQ^T += K^T dS^T over this wave's 32 keys; the transposed K operand of
-    // block dt + 1 is read after the first MFMA of block dt
+    // block dt + 2 is read after the first MFMA of block dt (three register
+    // sets), so a read has seven MFMAs to land
     const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
-    bf16x8 ka[2];
+    bf16x8 ka[3];
     auto rdk = [&](int dt, int b) {
       const int lc = 2 * dt + ((n16 & 3) >> 1);
       ka[b] = lds_read_tr16_x2(Ks + tile_off(vr, lc) + 4 * (n16 & 1), D);
     };
     rdk(0, 0);
+    rdk(1, 1);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      if (dt + 1 < 8) rdk(dt + 1, (dt + 1) & 1);
-      const int b = dt & 1;
+      if (dt + 2 < 8) rdk(dt + 2, (dt + 2) % 3);
+      const int b = dt % 3;
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
         acc[rs][dt] = mma16<F16>(ka[b], dsh[rs], acc[rs][dt]);
@@ -636,11 +638,11 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
       }
     }
     constexpr int MPB = 4;   // MFMAs per column block
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
     }
   };
@@ -789,20 +791,21 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
                                         f32x4 (*acc_dk)[8], f32x4 (*acc_dv)[8]) {
   constexpr int D = TD;
   const int rr = 32 * rh + 8 * g4 + (n16 >> 2);
-  // The transposed operands of column block dt + 1 are read while the eight
-  // MFMAs of block dt run (two register sets, order pinned below); with one
-  // set every block would wait out a full LDS round trip.
-  bf16x8 oT[2], qT[2];
+  // The transposed operands of column block dt + 2 are read while the MFMAs
+  // of block dt run (three register sets, order pinned below); with one set
+  // every block would wait out a full LDS round trip.
+  bf16x8 oT[3], qT[3];
   auto rd = [&](int dt, int b) {
     const int lc = 2 * dt + ((n16 & 3) >> 1);
     oT[b] = lds_read_tr16_x2(Os + tile_off(rr, lc) + 4 * (n16 & 1), D);
     qT[b] = lds_read_tr16_x2(Qs + tile_off(rr, lc) + 4 * (n16 & 1), D);
   };
   rd(0, 0);
+  rd(1, 1);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    if (dt + 1 < 8) rd(dt + 1, (dt + 1) & 1);
-    const int b = dt & 1;
+    if (dt + 2 < 8) rd(dt + 2, (dt + 2) % 3);
+    const int b = dt % 3;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       acc_dv[kt][dt] = mma16<F16>(oT[b], ph[kt], acc_dv[kt][dt]);
@@ -812,13 +815,12 @@ __device__ __forceinline__ void kv_grad(const bf16* Qs, const bf16* Os, const bf
     }
   }
   constexpr int MPB = PAIR ? 8 : 4;   // MFMAs per column block
-  // reads of block dt + 1 go out after the first MFMA of block dt, so the
-  // wait in front of that MFMA covers block dt's reads only
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  // reads of block dt + 2 go out after the first MFMA of block dt
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
   }
 }

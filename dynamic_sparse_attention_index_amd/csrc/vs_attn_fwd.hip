@@ -555,29 +555,31 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
     }
     __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T P^T by 16-column blocks dt of V; the transposed V operand of
-    // block dt + 1 is read after the first MFMA of block dt (two register
-    // sets, order pinned below), so only block 0 waits out an LDS round trip
+    // block dt + 2 is read after the first MFMA of block dt (three register
+    // sets, order pinned below), so a read has three MFMAs (fp16; seven with
+    // bf16 pairs) to land and only blocks 0 and 1 wait out an LDS round trip
     const bf16* Vs = Vst.template operator()<p>();
     const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
     const int vb = (n16 & 3) >> 1, vo = 4 * (n16 & 1);
-    bf16x8 va[2];
+    bf16x8 va[3];
     auto rdv = [&](int dt, int b) { va[b] = lds_read_tr16_x2(Vs + tile_off(vr, 2 * dt + vb) + vo, D); };
     rdv(0, 0);
+    rdv(1, 1);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      if (dt + 1 < 8) rdv(dt + 1, (dt + 1) & 1);
+      if (dt + 2 < 8) rdv(dt + 2, (dt + 2) % 3);
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
-        acc[rs][dt] = mma16<F16>(va[dt & 1], pf[rs], acc[rs][dt]);
-        if constexpr (!F16) acc[rs][dt] = mma16<F16>(va[dt & 1], pl[rs], acc[rs][dt]);
+        acc[rs][dt] = mma16<F16>(va[dt % 3], pf[rs], acc[rs][dt]);
+        if constexpr (!F16) acc[rs][dt] = mma16<F16>(va[dt % 3], pl[rs], acc[rs][dt]);
       }
     }
     constexpr int MPB = F16 ? 2 : 4;   // MFMAs per column block
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
     }
   };
