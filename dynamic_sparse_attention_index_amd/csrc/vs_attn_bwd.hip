@@ -436,10 +436,12 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 
 // dQ, query-major. Wave (rh, kh) = rows 32 rh.. of the block, keys 32 kh.. of
 // every tile; the two key halves' partial dQ are added through LDS at the end.
-// dS enters the dQ product as a hi + lo pair in both operand formats (bf16
-// pair, or fp16 pair on fp16 inputs): dQ_n sums dS over every active key of
-// the row, and the large outlier keys scale each weight's rounding error, so
-// a single fp16 dS put dQ at 1.9e-2 of the oracle at 262144 tokens.
+// dS enters the dQ product of a vertical chunk as a hi + lo pair in both
+// operand formats (bf16 pair, or fp16 pair on fp16 inputs): dQ_n sums dS k_m
+// over every active key of the row, and the vertical columns hold the large
+// outlier keys whose terms dominate that sum (a single fp16 dS everywhere
+// put dQ at 1.9e-2 of the oracle at 262144 tokens). Listed slash tiles take
+// dS as one fp16 operand (bf16 inputs keep the pair everywhere).
 // RING: the tile sequence runs over several ring steps (RingTiles, `rs`; K/V
 // hold every shard in storage order) and dQ accumulates across them.
 // S1 (one-position stripes): per-key thresholds and diagonal windows, as in
@@ -557,8 +559,9 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
     for (int rs = 0; rs < 2; ++rs) qa_l[rs] = ((32 * rh + 16 * rs + n16) * a.P + a.rank) >> 6;
   }
 
-  auto step = [&](int it, const bf16* Ks, const bf16* Vs, const int* thc, const uint32_t* wc, bf16* Kn, bf16* Vn,
-                  int* thn, uint32_t* wn, int* dn_next, const int* dn_cur) {
+  // VCH: the tile is a vertical chunk (dS as a hi + lo pair in the dQ product)
+  auto step = [&]<bool VCH>(int it, const bf16* Ks, const bf16* Vs, const int* thc, const uint32_t* wc, bf16* Kn,
+                            bf16* Vn, int* thn, uint32_t* wn, int* dn_next, const int* dn_cur) {
     wait_all_mem();
     __syncthreads();
     const int mode = mode_c;
@@ -584,7 +587,6 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
         }
       }
     }
-    bf16x8 dsh[2], dsl[2];
     if (mode) {   // wave-uniform: diagonal tile or vertical chunk
       // row thresholds of this lane's 8 keys (two 16-byte reads)
       const i32x4 th0 = *(const i32x4*)(thc + 32 * kh + 8 * g4);
@@ -606,7 +608,7 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
           }
     }
 #pragma unroll
-    for (int rs = 0; rs < 2; ++rs) {
+    for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -614,37 +616,40 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rs][t][i], sl2, -lse2[rs]));
           s[rs][t][i] = p * (dp[rs][t][i] - dl[rs]);
         }
-      weights8<F16, true>(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
-    }
-    // dQ^T += K^T dS^T over this wave's 32 keys; the transposed K operand of
-    // block dt + 2 is read after the first MFMA of block dt (three register
-    // sets), so a read has seven MFMAs to land
-    const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
-    bf16x8 ka[3];
-    auto rdk = [&](int dt, int b) {
-      const int lc = 2 * dt + ((n16 & 3) >> 1);
-      ka[b] = lds_read_tr16_x2(Ks + tile_off(vr, lc) + 4 * (n16 & 1), D);
-    };
-    rdk(0, 0);
-    rdk(1, 1);
+    // dQ^T += K^T dS^T over this wave's 32 keys (PR: dS as a hi + lo pair);
+    // the transposed K operand of block dt + 1 is read after the first MFMA
+    // of block dt (two register sets: a third spills registers here)
+    auto dq_product = [&]<bool PR>() {
+      bf16x8 dsh[2], dsl[2];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      if (dt + 2 < 8) rdk(dt + 2, (dt + 2) % 3);
-      const int b = dt % 3;
+      for (int rs = 0; rs < 2; ++rs) weights8<F16, PR>(s[rs][0], s[rs][1], dsh[rs], dsl[rs]);
+      const int vr = 32 * kh + 8 * g4 + (n16 >> 2);
+      bf16x8 ka[2];
+      auto rdk = [&](int dt, int b) {
+        const int lc = 2 * dt + ((n16 & 3) >> 1);
+        ka[b] = lds_read_tr16_x2(Ks + tile_off(vr, lc) + 4 * (n16 & 1), D);
+      };
+      rdk(0, 0);
 #pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        acc[rs][dt] = mma16<F16>(ka[b], dsh[rs], acc[rs][dt]);
-        acc[rs][dt] = mma16<F16>(ka[b], dsl[rs], acc[rs][dt]);
+      for (int dt = 0; dt < 8; ++dt) {
+        if (dt + 1 < 8) rdk(dt + 1, (dt + 1) & 1);
+        const int b = dt & 1;
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          acc[rs][dt] = mma16<F16>(ka[b], dsh[rs], acc[rs][dt]);
+          if constexpr (PR) acc[rs][dt] = mma16<F16>(ka[b], dsl[rs], acc[rs][dt]);
+        }
       }
-    }
-    constexpr int MPB = 4;   // MFMAs per column block
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      constexpr int MPB = PR ? 4 : 2;   // MFMAs per column block
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
-    }
+      for (int dt = 0; dt < 8; ++dt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (dt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MPB - 1, 0);
+      }
+    };
+    dq_product.template operator()<VCH || !F16>();
   };
 
   bt.desc_copy(0, desc0_sh, wave, lane);
@@ -652,10 +657,20 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
   wait_all_mem();
   __syncthreads();
   mode_c = issue(0, desc0_sh, K0, V0, thr0_sh, win_sh[0]);
-  for (int it = 0; it < total; it += 2) {
-    step(it, K0, V0, thr0_sh, win_sh[0], K1, V1, thr1_sh, win_sh[1], desc0_sh, desc1_sh);
-    if (it + 1 < total) step(it + 1, K1, V1, thr1_sh, win_sh[1], K0, V0, thr0_sh, win_sh[0], desc1_sh, desc0_sh);
-  }
+  // tiles [0, npr) take the pair: the vertical chunks, which lead the
+  // sequence (every tile under RING, whose steps interleave chunks and tiles)
+  auto walk = [&]<bool PR>(int it0, int it1) {
+    for (int it = it0; it < it1; ++it) {
+      const bool o = it & 1;   // stage parity
+      step.template operator()<PR>(it, o ? K1 : K0, o ? V1 : V0, o ? thr1_sh : thr0_sh, win_sh[o ? 1 : 0],
+                                   o ? K0 : K1, o ? V0 : V1, o ? thr0_sh : thr1_sh, win_sh[o ? 0 : 1],
+                                   o ? desc1_sh : desc0_sh, o ? desc0_sh : desc1_sh);
+    }
+  };
+  int npr = total;
+  if constexpr (!RING) npr = bt.nvc;
+  walk.template operator()<true>(0, npr);
+  walk.template operator()<false>(npr, total);
   __syncthreads();
   float* xo = (float*)(rh == 0 ? K0 : V0);   // [2 rs][8 dt][64 lanes] f32x4 per row half
   if (kh == 1) {
