@@ -441,7 +441,7 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 // over every active key of the row, and the vertical columns hold the large
 // outlier keys whose terms dominate that sum (a single fp16 dS everywhere
 // put dQ at 1.9e-2 of the oracle at 262144 tokens). Listed slash tiles take
-// dS as one fp16 operand (bf16 inputs keep the pair everywhere).
+// dS as one fp16 operand on the one-step fp16 path.
 // RING: the tile sequence runs over several ring steps (RingTiles, `rs`; K/V
 // hold every shard in storage order) and dQ accumulates across them.
 // S1 (one-position stripes): per-key thresholds and diagonal windows, as in
@@ -657,20 +657,36 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
   wait_all_mem();
   __syncthreads();
   mode_c = issue(0, desc0_sh, K0, V0, thr0_sh, win_sh[0]);
-  // tiles [0, npr) take the pair: the vertical chunks, which lead the
-  // sequence (every tile under RING, whose steps interleave chunks and tiles)
+  // With fp16 operands the vertical chunks, which lead the sequence, take the
+  // pair and the listed tiles one operand; the resident ring (whose steps
+  // interleave chunks and tiles) and one-position stripes keep the pair on
+  // every tile, as does the bf16 operand format.
+  // Stages are fixed per call site (tile parity) so the compiler can tell the
+  // stage being read from the one being filled and keeps its copy wait at
+  // the step's barrier.
+  auto even = [&]<bool PR>(int it) {
+    step.template operator()<PR>(it, K0, V0, thr0_sh, win_sh[0], K1, V1, thr1_sh, win_sh[1], desc0_sh, desc1_sh);
+  };
+  auto odd = [&]<bool PR>(int it) {
+    step.template operator()<PR>(it, K1, V1, thr1_sh, win_sh[1], K0, V0, thr0_sh, win_sh[0], desc1_sh, desc0_sh);
+  };
   auto walk = [&]<bool PR>(int it0, int it1) {
-    for (int it = it0; it < it1; ++it) {
-      const bool o = it & 1;   // stage parity
-      step.template operator()<PR>(it, o ? K1 : K0, o ? V1 : V0, o ? thr1_sh : thr0_sh, win_sh[o ? 1 : 0],
-                                   o ? K0 : K1, o ? V0 : V1, o ? thr0_sh : thr1_sh, win_sh[o ? 0 : 1],
-                                   o ? desc1_sh : desc0_sh, o ? desc0_sh : desc1_sh);
+    int it = it0;
+    if ((it & 1) && it < it1) odd.template operator()<PR>(it++);
+    for (; it < it1; it += 2) {
+      even.template operator()<PR>(it);
+      if (it + 1 < it1) odd.template operator()<PR>(it + 1);
     }
   };
-  int npr = total;
-  if constexpr (!RING) npr = bt.nvc;
-  walk.template operator()<true>(0, npr);
-  walk.template operator()<false>(npr, total);
+  if constexpr (F16 && !RING && !S1) {
+    walk.template operator()<true>(0, bt.nvc);
+    walk.template operator()<false>(bt.nvc, total);
+  } else {   // pairs throughout (bf16 operands, the ring, one-position stripes)
+    for (int it = 0; it < total; it += 2) {
+      even.template operator()<true>(it);
+      if (it + 1 < total) odd.template operator()<true>(it + 1);
+    }
+  }
   __syncthreads();
   float* xo = (float*)(rh == 0 ? K0 : V0);   // [2 rs][8 dt][64 lanes] f32x4 per row half
   if (kh == 1) {
