@@ -468,7 +468,11 @@ def ring_report(args, cfg):
            "operands": args.operands if cfg.dtype == "bf16" and D == 128 else cfg.dtype,
            "bwd_streams": args.bwd_streams,
            "communication": "excluded (one GPU; every rank's steps run in turn)", "layouts": {}}
+    def progress(msg):
+        print(f"[ring {time.time() - t0:6.1f}s] {msg}", file=sys.stderr, flush=True)
+
     for kind in args.layouts.split(","):
+        progress(f"{kind}: inputs")
         perm = np.concatenate([layout_permutation(kind, N, P, r) for r in range(P)])
         q = torch.tensor(host["q"][:, perm]).to(dev, tdt)
         k = torch.tensor(host["k"][:, perm]).to(dev, tdt)
@@ -587,6 +591,7 @@ def ring_report(args, cfg):
             stream.wait_event(join)
 
         for rep in range(-1, args.ring_reps):       # rep -1: warm-up
+            progress(f"{kind}: per-step mode, repetition {rep + 1} of {args.ring_reps} (first: warm-up)")
             dk.zero_()
             dv.zero_()
             for r in range(P):
@@ -651,6 +656,7 @@ def ring_report(args, cfg):
         dv_res = torch.empty(Hkv, N, D, device=dev)
         t_res = np.zeros((args.ring_reps, P, 4))      # mask, fwd, prep, bwd per rank
         for rep in range(-1, -1 if s1 else args.ring_reps):
+            progress(f"{kind}: resident mode, repetition {rep + 1} of {args.ring_reps} (first: warm-up)")
             for r in range(P):
                 rows = slice(r * QB * 64, (r + 1) * QB * 64)
                 qr, dor = aq[:, rows], ado[:, rows]
