@@ -441,7 +441,7 @@ __global__ void __launch_bounds__(BWD_THREADS) dkdv_vert_kernel(BwdArgs a) {
 // over every active key of the row, and the vertical columns hold the large
 // outlier keys whose terms dominate that sum (a single fp16 dS everywhere
 // put dQ at 1.9e-2 of the oracle at 262144 tokens). Listed slash tiles take
-// dS as one fp16 operand on the one-step fp16 path.
+// dS as one fp16 operand on the fp16 path.
 // RING: the tile sequence runs over several ring steps (RingTiles, `rs`; K/V
 // hold every shard in storage order) and dQ accumulates across them.
 // S1 (one-position stripes): per-key thresholds and diagonal windows, as in
@@ -657,10 +657,10 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
   wait_all_mem();
   __syncthreads();
   mode_c = issue(0, desc0_sh, K0, V0, thr0_sh, win_sh[0]);
-  // With fp16 operands the vertical chunks, which lead the sequence, take the
-  // pair and the listed tiles one operand; the resident ring (whose steps
-  // interleave chunks and tiles) and one-position stripes keep the pair on
-  // every tile, as does the bf16 operand format.
+  // With fp16 operands the vertical chunks, which lead the sequence (in the
+  // resident ring those of every step), take the pair and the listed tiles
+  // one operand; one-position stripes keep the pair on every tile, as does
+  // the bf16 operand format.
   // Stages are fixed per call site (tile parity) so the compiler can tell the
   // stage being read from the one being filled and keeps its copy wait at
   // the step's barrier.
@@ -678,10 +678,10 @@ __device__ __forceinline__ void dq_d128(const BwdArgs& a, const RingSteps* rs = 
       if (it + 1 < it1) odd.template operator()<PR>(it + 1);
     }
   };
-  if constexpr (F16 && !RING && !S1) {
-    walk.template operator()<true>(0, bt.nvc);
-    walk.template operator()<false>(bt.nvc, total);
-  } else {   // pairs throughout (bf16 operands, the ring, one-position stripes)
+  if constexpr (F16 && !S1) {
+    walk.template operator()<true>(0, bt.nvert());
+    walk.template operator()<false>(bt.nvert(), total);
+  } else {   // pairs throughout (bf16 operands, one-position stripes)
     for (int it = 0; it < total; it += 2) {
       even.template operator()<true>(it);
       if (it + 1 < total) odd.template operator()<true>(it + 1);
@@ -1567,7 +1567,9 @@ int launch_attn_bwd_ring(int dtype, TView q, TView k, TView v, TView dout, const
   const vs_mask* m = &ms[0];
   if (dtype != VS_BF16 && dtype != VS_F16) return VS_ERR_UNSUPPORTED;
   if (m->W > MAX_LDS_W || m->Hq / m->Hkv > 8) return VS_ERR_UNSUPPORTED;
-  const int64_t krows = (int64_t)m->KB * BLK, qrows = (int64_t)m->QB * BLK;   // 32-bit offsets per shard
+  // 32-bit copy offsets: over every shard for K/V (the dQ kernel's vertical
+  // chunks gather storage rows), over the rank's rows for Q/dO
+  const int64_t krows = (int64_t)m->lay.P * m->KB * BLK, qrows = (int64_t)m->QB * BLK;
   if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn) || !dma_offsets_fit(qrows, q.sn) ||
       !dma_offsets_fit(qrows, dout.sn))
     return VS_ERR_UNSUPPORTED;

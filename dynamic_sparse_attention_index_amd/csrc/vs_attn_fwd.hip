@@ -453,8 +453,7 @@ __device__ __forceinline__ void attn_fwd_d128(const FwdArgs& a, const RingSteps*
     } else {
       if (hs == 0) {
         int rows[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) rows[c] = slot[dma_local_row(wave, c, lane)];
+        bt.gather_rows(t, slot, rows, wave, lane, 2);
         dma_tile_gather(vs_, vb, rows, vrb, dl, wave);
       }
       mode_pend = 1;
@@ -778,7 +777,8 @@ int launch_attn_fwd_ring(int dtype, TView q, TView k, TView v, const vs_mask* ms
   a.scale_log2 = scale * LOG2E;
   a.dbg = debug_word(); a.cap = m->tile_cap;
   if (m->W > MAX_LDS_W) return VS_ERR_UNSUPPORTED;
-  const int64_t krows = (int64_t)m->KB * BLK;   // 32-bit copy offsets within one shard
+  // 32-bit copy offsets over every shard (vertical chunks gather storage rows)
+  const int64_t krows = (int64_t)m->lay.P * m->KB * BLK;
   if (!dma_offsets_fit(krows, k.sn) || !dma_offsets_fit(krows, v.sn)) return VS_ERR_UNSUPPORTED;
   const dim3 grid(xcd_group_grid(m->Hkv, m->QB, QMAJOR_BPC, m->Hq / m->Hkv)), block(FWD_THREADS);
   for (int s0 = 0; s0 < nsteps; s0 += MAX_RING_STEPS) {

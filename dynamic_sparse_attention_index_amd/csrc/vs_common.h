@@ -458,7 +458,12 @@ struct BlockTiles {
   }
   // The same calls as RingTiles (one visible shard at local row 0; the call
   // site's cursor `c` is not needed).
+  __device__ __forceinline__ void gather_rows(int, const int* slot, int* rows, int wave, int lane, int) const {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rows[c] = dbg_clamp(slot[dma_local_row(wave, c, lane)], 0, KB * BLK, dbg);
+  }
   __device__ __forceinline__ bool vert(int it, int) const { return vert(it); }
+  __device__ __forceinline__ int nvert() const { return nvc; }
   __device__ __forceinline__ void vert_rows(int it, const int* slot, int* rows, int& thr, int wave, int lane, int tid,
                                             int) const {
     vert_rows(it, slot, rows, thr, wave, lane, tid);
@@ -468,11 +473,11 @@ struct BlockTiles {
 
 // ---- several ring steps in one launch ----------------------------------------
 // One rank's ring steps walked by one launch with every visible shard
-// resident: the tile sequence of a (q head, query block) is the
-// concatenation of its sequences in the steps' masks (each step: its
-// vertical chunks, then its listed tiles), and the online-softmax state (or
-// the dQ accumulator) carries across the steps, so the output is written
-// once instead of being merged step by step.
+// resident: the tile sequence of a (q head, query block) takes the vertical
+// columns of all steps, gathered 64 at a time across the steps' shards,
+// then every step's listed tiles; the online-softmax state (or the dQ
+// accumulator) carries across the steps, so the output is written once
+// instead of being merged step by step.
 constexpr int MAX_RING_STEPS = 32;
 
 // Per-step mask arrays and visible shard (kernel argument).
@@ -500,8 +505,10 @@ struct RingStepsKV {
 
 // LDS table of one list row across the steps.
 struct RingTable {
-  int cum[MAX_RING_STEPS + 1];   // tiles of the steps before step s
-  int t0[MAX_RING_STEPS], nt[MAX_RING_STEPS], ve[MAX_RING_STEPS];
+  int vcum[MAX_RING_STEPS + 1];  // vertical columns of the steps before step s
+  int tcum[MAX_RING_STEPS + 1];  // listed tiles of the steps before step s
+  int t0[MAX_RING_STEPS], nt[MAX_RING_STEPS];
+  int src[MAX_RING_STEPS];       // visible shard of step s
 };
 
 __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -512,13 +519,24 @@ __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlan
 // 1 and 2: the kernel's two copy sites), so finding the step is a short
 // forward scan. Key rows of step s's shard start at row0 = src[s] * KB * 64
 // of the tensors that hold every shard in storage order.
+// Tile sequence over the steps, with the calls of BlockTiles. Tiles
+// 0 .. nv - 1 are vertical chunks: chunk t holds the columns at positions
+// 64 t .. 64 t + 63 of the steps' vertical lists laid end to end (step s's
+// columns at vcum[s] .. vcum[s + 1] - 1), so a chunk can gather rows of
+// several shards and its copy rows are storage rows of the tensors that hold
+// every shard (shard src at row src * KB * 64). Tile nv + u is listed tile u
+// of the steps' lists laid end to end: step s with tcum[s] <= u < tcum[s + 1],
+// its rows from row0 = src[s] * KB * 64. Each call site walks its tiles in
+// increasing order and keeps its own step cursor (c = 0: descriptor copies,
+// 1 and 2: the kernel's two copy sites), so finding the step of a listed
+// tile is a short forward scan.
 struct RingTiles {
   const RingSteps* rs;
   RingTable* tb;
   const uint32_t* sbits;      // LDS copy of the head's slash bitmap (the same in every step)
   int64_t vl_off;             // the head's first entry in each step's vloc
   int64_t G;                  // global block of the query block
-  int kind, P, KB, total;
+  int kind, P, KB, total, nv, vt;
   int cur[3];
   int32_t* dbg = nullptr;     // debug builds: bounds-violation counter
 
@@ -527,10 +545,10 @@ struct RingTiles {
   __device__ __forceinline__ void fill(int64_t u, int wave, int lane) {
     if (wave != 0) return;
     const int n = rs->nsteps;
-    int tot = 0;
+    int nt = 0, ve = 0;
     if (lane < n) {
       int a0 = rs->tile_ptr[lane][u], a1 = rs->tile_ptr[lane][u + 1];
-      int ve = rs->vert_end[lane][u];
+      ve = rs->vert_end[lane][u];
 #ifdef VS_DEBUG_BOUNDS
       a0 = dbg_clamp(a0, 0, (int)rs->cap + 1, dbg);
       a1 = a0 + dbg_clamp(a1 - a0, 0, min(KB, (int)rs->cap - a0) + 1, dbg);
@@ -538,38 +556,61 @@ struct RingTiles {
 #endif
       tb->t0[lane] = a0;
       tb->nt[lane] = a1 - a0;
-      tb->ve[lane] = ve;
-      tot = (a1 - a0) + (ve + BLK - 1) / BLK;
+      tb->src[lane] = rs->src[lane];
+      nt = a1 - a0;
     }
-    int incl = tot;
+    int ti = nt, vi = ve;   // inclusive scans over the steps
     for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
+      const int y = __shfl_up(ti, off, 64), z = __shfl_up(vi, off, 64);
+      if (lane >= off) {
+        ti += y;
+        vi += z;
+      }
     }
-    if (lane < n) tb->cum[lane + 1] = incl;
-    if (lane == 0) tb->cum[0] = 0;
+    if (lane < n) {
+      tb->tcum[lane + 1] = ti;
+      tb->vcum[lane + 1] = vi;
+    }
+    if (lane == 0) tb->tcum[0] = tb->vcum[0] = 0;
   }
   __device__ __forceinline__ void start() {
-    total = rfl(tb->cum[rs->nsteps]);
+    vt = rfl(tb->vcum[rs->nsteps]);
+    nv = (vt + BLK - 1) / BLK;
+    total = nv + rfl(tb->tcum[rs->nsteps]);
     cur[0] = cur[1] = cur[2] = 0;
   }
+  // step of listed tile t (t >= nv)
   __device__ __forceinline__ int step_of(int t, int c) {
+    const int u = t - nv;
     int s = cur[c];
-    while (s + 1 < rs->nsteps && t >= rfl(tb->cum[s + 1])) ++s;
+    while (s + 1 < rs->nsteps && u >= rfl(tb->tcum[s + 1])) ++s;
     cur[c] = s;
     return s;
   }
-  __device__ __forceinline__ int nvc(int s) const { return (rfl(tb->ve[s]) + BLK - 1) / BLK; }
-  __device__ __forceinline__ bool vert(int t, int c) {
-    const int s = step_of(t, c);
-    return t - rfl(tb->cum[s]) < nvc(s);
+  // step holding vertical position pos (< vt): the last s with vcum[s] <= pos
+  __device__ __forceinline__ int vstep(int pos) const {
+    int lo = 0, hi = rs->nsteps - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tb->vcum[mid] <= pos) lo = mid; else hi = mid - 1;
+    }
+    return lo;
   }
+  __device__ __forceinline__ bool vert(int t, int) const { return t < nv; }
+  __device__ __forceinline__ int nvert() const { return nv; }
   __device__ __forceinline__ void desc_copy(int t, int* slot, int wave, int lane) {
-    const int s = step_of(t, 0);
+    if (t >= nv) step_of(t, 0);
     if (wave != 0) return;
-    const int it = t - rfl(tb->cum[s]), nv = nvc(s), ve = rfl(tb->ve[s]);
-    const int32_t* p = it < nv ? rs->vloc[s] + vl_off + min(it * BLK + lane, ve - 1)
-                               : rs->tile_col[s] + rfl(tb->t0[s]) + (rfl(tb->nt[s]) - 1 - (it - nv));
+    const int32_t* p;
+    if (t < nv) {
+      const int pos = min(t * BLK + lane, vt - 1);
+      const int s = vstep(pos);
+      p = rs->vloc[s] + vl_off + (pos - tb->vcum[s]);
+    } else {
+      const int s = cur[0];
+      const int it = t - nv - rfl(tb->tcum[s]);
+      p = rs->tile_col[s] + rfl(tb->t0[s]) + (rfl(tb->nt[s]) - 1 - it);
+    }
     __builtin_amdgcn_global_load_lds((const void*)p,
                                      (__attribute__((address_space(3))) void*)(
                                          (__attribute__((address_space(3))) int*)(slot)),
@@ -580,20 +621,31 @@ struct RingTiles {
     mode = (e & VS_TILE_DIAG) ? 1 : 0;
     return dbg_clamp(e & VS_TILE_MASK, 0, KB, dbg) * BLK;
   }
+  // storage row of the column at chunk position r of vertical chunk t
+  __device__ __forceinline__ int vrow(int t, const int* slot, int r) const {
+    const int s = vstep(min(t * BLK + r, vt - 1));
+    return tb->src[s] * KB * BLK + dbg_clamp(slot[r], 0, KB * BLK, dbg);
+  }
+  // copy rows of this lane's four pieces of vertical chunk t
+  __device__ __forceinline__ void gather_rows(int t, const int* slot, int* rows, int wave, int lane, int) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rows[k] = vrow(t, slot, dma_local_row(wave, k, lane));
+  }
   __device__ __forceinline__ void vert_rows(int t, const int* slot, int* rows, int& thr, int wave, int lane, int tid,
                                             int c) {
-    const int s = step_of(t, c);
-    const int it = t - rfl(tb->cum[s]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) rows[k] = dbg_clamp(slot[dma_local_row(wave, k, lane)], 0, KB * BLK, dbg);
+    gather_rows(t, slot, rows, wave, lane, c);
     thr = BLK;
-    if (tid < BLK && it * BLK + tid < rfl(tb->ve[s])) {
+    if (tid < BLK && t * BLK + tid < vt) {
+      const int s = vstep(t * BLK + tid);
       const int m = dbg_clamp(slot[tid], 0, KB * BLK, dbg);
-      const int64_t j = G - global_block(kind, P, KB, rs->src[s], m / BLK);
+      const int64_t j = G - global_block(kind, P, KB, tb->src[s], m / BLK);
       if (!((sbits[j >> 5] >> (j & 31)) & 1u)) thr = (j == 0) ? (m % BLK) : 0;
     }
   }
-  __device__ __forceinline__ int64_t row0(int t, int c) { return (int64_t)rs->src[step_of(t, c)] * KB * BLK; }
+  // first storage row of tile t's shard (vertical chunks: rows are storage rows)
+  __device__ __forceinline__ int64_t row0(int t, int c) {
+    return t < nv ? 0 : (int64_t)rs->src[step_of(t, c)] * KB * BLK;
+  }
 };
 
 }  // namespace vs

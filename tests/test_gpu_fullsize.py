@@ -391,6 +391,35 @@ def test_fullsize_qwen512k_ring_rank(kind, rank):
         dk_hs[comp] = {s: dk[s].cpu().numpy() for s in range(P)}
         dv_hs[comp] = {s: dv[s].cpu().numpy() for s in range(P)}
         del q, do, o, lse, delta, dq, dk, dv, kv
+    # the resident calls, as the ring report times them: every shard in
+    # storage order, the masks of all steps from one call, one forward and
+    # one backward call over the whole ring (fp16 operands)
+    _log("512k [f16 resident]: masks, forward and backward over the ring in one call each")
+    store = np.concatenate([ol.shard_positions(kind, N, P, s) for s in range(P)])
+    k_all = H.as_f16(H.to_dev(t["k"][:, store], cfg.dtype))
+    v_all = H.as_f16(H.to_dev(t["v"][:, store], cfg.dtype))
+    q = H.as_f16(H.to_dev(t["q"][:, rows_r], cfg.dtype))
+    do = H.as_f16(H.to_dev(t["do"][:, rows_r], cfg.dtype))
+    masks = [vs.Mask(Hq, Hkv, lay, cap) for _ in range(P)]
+    vs.vs_block_mask_ring(*lists, rank, masks)
+    o = torch.full((Hq, QB * 64, D), float("nan"), device=dev)
+    lse = torch.full((Hq, QB * 64), float("nan"), device=dev)
+    vs.vs_attn_fwd_ring(q, k_all, v_all, masks, cfg.scale, o, lse, accumulate=0)
+    delta = torch.empty(Hq, QB * 64, device=dev)
+    vs.vs_attn_bwd_prep(o, do, delta)
+    dq = torch.full((Hq, QB * 64, D), float("nan"), device=dev)
+    dk_all = torch.full((Hkv, N, D), float("nan"), device=dev)
+    dv_all = torch.full((Hkv, N, D), float("nan"), device=dev)
+    vs.vs_attn_bwd_ring(q, k_all, v_all, do, lse, delta, masks, cfg.scale, dq, dk_all, dv_all,
+                        vs.VS_BWD_ALL | vs.VS_BWD_OVERWRITE)
+    torch.cuda.synchronize()
+    for m in masks:
+        assert int(m.arrays()["status"].item()) == 0
+    gots["f16 resident"] = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy()}
+    dk_hs["f16 resident"] = {s: dk_all[:, s * QB * 64:(s + 1) * QB * 64].cpu().numpy() for s in range(P)}
+    dv_hs["f16 resident"] = {s: dv_all[:, s * QB * 64:(s + 1) * QB * 64].cpu().numpy() for s in range(P)}
+    del k_all, v_all, q, do, o, lse, delta, dq, dk_all, dv_all, masks
+    comps = comps + ("f16 resident",)
     _log(f"512k: oracle rows heads={heads} local blocks={blocks}")
     ws = _rows_check(t, cfg, vert, slash, lambda I: rows_r[64 * I:64 * I + 64], gots, heads, blocks)
     # dK/dV of the key blocks from 64 (or more) blocks before this rank's last
