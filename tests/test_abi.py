@@ -135,6 +135,22 @@ def test_stripe1_attention_validation(L):
     assert L.vs_attn_fwd_ring(q, k_all, k_all, ctypes.byref(m), 1, 0.1, o, lse, 0, None) == vs.VS_ERR_UNSUPPORTED
 
 
+def test_sequence_beyond_the_lds_bitmap_refused(L):
+    """2^20 tokens is the longest sequence the head-dim-128 attention kernels
+    take (a head's slash bitmap, 512 words, lives in LDS); one block more is
+    refused before device work."""
+    N = (1 << 20) + 64
+    m, lay, _, _ = _mask(L, Hq=2, Hkv=1, N=N)
+    m.rank = 0
+    m.src = 0
+    q = _fake_tensor(0x20000000, 2, N, 128)
+    k = _fake_tensor(0x30000000, 1, N, 128)
+    o, lse = ctypes.c_void_p(0x40000000), ctypes.c_void_p(0x50000000)
+    assert L.vs_attn_fwd(q, k, k, ctypes.byref(m), 0.1, o, lse, 0, None) == vs.VS_ERR_UNSUPPORTED
+    p = ctypes.c_void_p(0x60000000)
+    assert L.vs_attn_bwd(q, k, k, q, p, p, ctypes.byref(m), 0.1, p, p, p, None) == vs.VS_ERR_UNSUPPORTED
+
+
 def test_block_mask_and_index_validation(L):
     m, lay, _, _ = _mask(L, kind="striped", P=4, N=1024)
     p = ctypes.c_void_p(0x60000000)
