@@ -779,17 +779,19 @@ __device__ __forceinline__ void kv_rowstats(const float* lsh, const float* dsh_,
   dd[0] = *(const f32x4*)(dsh_ + r0);
   dd[1] = *(const f32x4*)(dsh_ + r0 + 4);
 }
-// l2: row LSE in log2 units, +inf for an empty row (kv_rowstats); on the
-// diagonal tile (wave-uniform `diag`) key kt of this lane is active for rows
-// >= thr[kt]. S1: and only for the rows 4 t + i of this lane whose
-// global-block offset qa[4 t + i] is a set bit of win[kt].
-template <bool F16, bool PAIR = !F16, bool S1 = false>
+// l2: row LSE in log2 units, +inf for an empty row (kv_rowstats); on a
+// masked tile key kt of this lane is active for rows >= thr[kt]. S1: and only
+// for the rows 4 t + i of this lane whose global-block offset qa[4 t + i] is
+// a set bit of win[kt]. MASK = 0 / 1: the tile is known unmasked / masked at
+// compile time (no branch in the caller's scheduling region); MASK = 2: the
+// wave-uniform `diag` decides.
+template <bool F16, bool PAIR = !F16, bool S1 = false, int MASK = 2>
 __device__ __forceinline__ void kv_pds(f32x4 (*s)[2], const f32x4 (*dp)[2], const f32x4* l2, const f32x4* dd,
                                        int diag, const int* thr, int rh, int g4, float sl2, bf16x8* ph,
                                        bf16x8* pl, bf16x8* dh, bf16x8* dl, const uint32_t* win = nullptr,
                                        const int* qa = nullptr) {
   const int r0 = 32 * rh + 8 * g4;
-  if (diag) {
+  if (MASK == 1 || (MASK == 2 && diag)) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -1166,16 +1168,23 @@ __device__ __forceinline__ void dkdv_d128(const BwdArgs& a0, const RingStepsKV* 
     const int masked = ((diag_i & 1) || vlo || vhi) ? 1 : 0;
     __builtin_amdgcn_sched_barrier(0);
     f32x4 s_n[2][2], dp_n[2][2];
-    kv_sdp<F16>(qa, oa, kf, vf, s_n, dp_n);
     bf16x8 ph[2], pl[2], dh[2], dl[2];
-    kv_pds<F16, !F16, S1>(s_c, dp_c, l2, dd, masked, thr, rh, g4, sl2, ph, pl, dh, dl, win, qa_r);
-    constexpr int VPM = F16 ? 4 : 6;   // vector ops per MFMA (fp16 weights need one convert per pair)
+    // the MFMAs of S, dP (tile i + 1) and the vector ops of P, dS (tile i)
+    // form one branch-free region per case (a branch inside it would split
+    // the interleave and leave the MFMAs and the exponentials back to back)
+    auto sdp_pds = [&]<int MASK>() {
+      kv_sdp<F16>(qa, oa, kf, vf, s_n, dp_n);
+      kv_pds<F16, !F16, S1, MASK>(s_c, dp_c, l2, dd, 0, thr, rh, g4, sl2, ph, pl, dh, dl, win, qa_r);
+      constexpr int VPM = F16 ? 4 : 6;   // vector ops per MFMA (fp16 weights need one convert per pair)
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < 32; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (masked) sdp_pds.template operator()<1>();
+    else sdp_pds.template operator()<0>();
     const bf16* Qc = QOst.template operator()<p>();
     kv_grad<F16>(Qc, Qc + TILE_ELEMS, ph, pl, dh, dl, rh, g4, n16, acc_dk, acc_dv);
 #pragma unroll
