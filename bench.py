@@ -118,20 +118,18 @@ def main():
 
     # fp16 operands: exact copies of the bf16 inputs, made inside every timed
     # step (q, k, v before the forward; dO before the backward)
-    f16 = args.operands == "f16" and cfg.dtype == "bf16" and D == 128
+    f16_main = args.operands == "f16" and cfg.dtype == "bf16" and D == 128
     conv_status = torch.zeros(1, dtype=torch.int32, device=dev)
-    if f16:
+    if f16_main:
         q16, k16, v16, do16 = (torch.empty(x.shape, dtype=torch.float16, device=dev) for x in (q, k, v, do))
-        aq, ak, av, ado = q16, k16, v16, do16
-    else:
-        aq, ak, av, ado = q, k, v, do
 
     stages = ("index", "mask", "convert_qkv", "fwd", "bwd_prep", "dq", "dkdv", "dkdv_vert")
     ev = {name: [] for name in stages}
     two = args.bwd_streams == 2 and cfg.backward
     side = torch.cuda.Stream(device=dev) if two else None    # default priority, like every stream here
 
-    def step(record):
+    def step(record, f16=f16_main, ev=ev):
+        aq, ak, av, ado = (q16, k16, v16, do16) if f16 else (q, k, v, do)
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
         dq_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if record else None
 
@@ -204,6 +202,25 @@ def main():
         raise RuntimeError("fp16 conversion range error in the timed steps")
     ms_per_step = wall * 1e3 / args.steps
     stage_ms = {kname: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for kname, pairs in ev.items()}
+    f16 = f16_main
+
+    # The same step with the bf16 inputs as operands (hi + lo bf16 P and dS,
+    # no copies), timed right after on the same inputs and index: the format
+    # the pages train in, beside the fp16 headline.
+    bf16_operands = None
+    if f16_main and cfg.backward:
+        ev_b = {name: [] for name in stages}
+        for _ in range(args.warmup):
+            step(False, f16=False, ev=ev_b)
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        for _ in range(args.steps):
+            step(True, f16=False, ev=ev_b)
+        torch.cuda.synchronize()
+        ms_b = (time.perf_counter() - tb) * 1e3 / args.steps
+        bf16_operands = {"ms_per_step": round(ms_b, 4),
+                         "stage_ms": {kname: round(float(np.mean([a.elapsed_time(b) for a, b in pairs])), 4)
+                                      for kname, pairs in ev_b.items()}}
 
     arrs = mask.arrays()
     n_active = arrs["n_active"]
@@ -292,6 +309,7 @@ def main():
 
     packed = None
     if not args.no_packed and D == 128 and (Hq // Hkv) % 2 == 0 and cfg.dtype == "bf16":
+        aq, ak, av = (q16, k16, v16) if f16 else (q, k, v)   # the headline's operands
         packed = packed_report(vs, torch, cfg, lay, vert_s, slash_s, aq, ak, av, o, lse, stream)
 
     cpu = None
@@ -318,6 +336,10 @@ def main():
         "sparsity": round(sparsity, 5), "effective_flops": eff_flops,
         "strict_algorithmic_tflops": round(strict_tflops, 3), "index_pass": index_pass,
         "roofline": roofline, "cpu_baseline": cpu, "budgets": budgets, "gqa_packed": packed,
+        "bf16_operands": (None if bf16_operands is None else dict(
+            bf16_operands, value=round(eff_flops / (bf16_operands["ms_per_step"] * 1e-3) / 1e12, 3),
+            unit="TFLOP/s", note="the same step on the bf16 inputs as attention operands (hi + lo bf16 P and "
+                                 "dS, no fp16 copies), timed in this run after the headline steps")),
         "gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
