@@ -52,6 +52,8 @@ def parse():
                     help="2: run the dQ part on a second stream, concurrently with the dK/dV parts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-budgets", action="store_true", help="skip the budget-rule report (after the timed steps)")
+    ap.add_argument("--no-bf16-operands", action="store_true",
+                    help="skip the second timing of the step with bf16 operands (kernel traces of the fp16 path)")
     ap.add_argument("--no-packed", action="store_true",
                     help="skip the per-kv-head index / head-pair forward report (after the timed steps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -208,7 +210,7 @@ def main():
     # no copies), timed right after on the same inputs and index: the format
     # the pages train in, beside the fp16 headline.
     bf16_operands = None
-    if f16_main and cfg.backward:
+    if f16_main and cfg.backward and not args.no_bf16_operands:
         ev_b = {name: [] for name in stages}
         for _ in range(args.warmup):
             step(False, f16=False, ev=ev_b)
