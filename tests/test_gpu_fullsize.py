@@ -307,6 +307,15 @@ def _whole_group_check(name, t, cfg, ref, group):
         assert max(e["o"], e["lse"], e["dq"], e["dk"], e["dv"]) <= TOL, (comp, e)
 
 
+@pytest.mark.timeout(900)
+def test_fullsize_qwen32k_step():
+    """The 32768-token workload (16/2 heads, d 128, bf16 inputs) at its full
+    size: GPU index vs the oracle's, masks of sampled blocks bit for bit, then
+    the forward (and the backward beside it) on the oracle's index, sampled
+    rows and the whole kv group, with bf16 and with fp16 operands."""
+    _contig_case("qwen32k", comps=("bf16", "f16"), mask_heads=[0, 15])
+
+
 @pytest.mark.timeout(1500)
 def test_fullsize_qwen128k_step():
     """The benchmarked step: 16/2 heads, 131072 tokens, d 128, bf16 inputs,
