@@ -70,8 +70,8 @@ def main():
         copy_probe()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the sparse path is built and timed on a single "
-              "MI355X; multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: it times one rank's share of the sparse path on a "
+              "single MI355X and has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
